@@ -1,0 +1,15 @@
+"""CPU float64 oracle for the pairwise reductions — test infrastructure, not product code.
+
+Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg may import this
+package. The device library never imports, links or calls it.
+"""
+from .reductions import (  # noqa: F401
+    argkmin,
+    default_workers,
+    gauss_sum,
+    gauss_sum_batched,
+    gauss_sum_grad_x,
+    keys_are_exact,
+    logsumexp_reduction,
+    squared_distances,
+)
