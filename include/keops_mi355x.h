@@ -1,0 +1,135 @@
+/*
+ * keops_mi355x.h — C ABI of the MI355X (gfx950) fused pairwise-reduction library.
+ *
+ * Every entry point evaluates a reduction a_i = Reduction_j F(x_i, y_j, b_j) over all
+ * pairs (i, j) without ever storing the M-by-N table ("Kernel matrix reduction" concept
+ * page, Overview, and eq. 2 of its Implementation sketch). All work is enqueued on the
+ * caller's HIP stream; the call returns as soon as the kernels are queued.
+ *
+ * Conventions shared by all entry points
+ *   - Data pointers are DEVICE pointers to dense, row-major, contiguous arrays, aligned to
+ *     their element size (4 bytes for float32 / int32), to 16 bytes on the fp16 / bf16 path
+ *     and for the workspace. The caller owns every buffer (inputs, outputs, workspace). The
+ *     library never allocates or frees device memory and keeps no state between calls.
+ *   - `workspace` must hold keops_workspace_bytes(...) bytes for the same arguments, queried
+ *     with the same device current; it may be NULL only when that size is 0. Its contents
+ *     on entry are ignored. Two calls in flight at once need two workspaces.
+ *   - Arguments are validated before anything is enqueued; on any error nothing is written
+ *     and the return value says why (keops_last_error() gives the detail, per thread).
+ *     Errors: KEOPS_ERR_INVALID_ARG for NULL / misaligned pointers, negative sizes,
+ *     non-finite or non-positive sigma, K outside [1, N], an output overlapping an input or a
+ *     workspace that is too small; KEOPS_ERR_UNSUPPORTED for dimensions outside the compiled
+ *     families (listed per call); KEOPS_ERR_HIP when a HIP call or launch fails.
+ *   - Kernel-execution faults surface at the caller's next synchronisation, as for any HIP
+ *     launch. No C++ exception crosses this boundary.
+ *   - M = 0 is a no-op. Results are deterministic: the same inputs on the same device give
+ *     bit-identical outputs (every reduction runs in a fixed order; no atomics).
+ *   - sigma is the Gaussian bandwidth: k(x, y) = exp(-||x - y||^2 / (2 sigma^2)). The
+ *     flash-attention page's Phi_tau = exp(-tau/2 ||q - k||^2) is sigma = 1/sqrt(tau).
+ */
+#ifndef KEOPS_MI355X_H
+#define KEOPS_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define KEOPS_API __attribute__((visibility("default")))
+#else
+#define KEOPS_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { KEOPS_F32 = 0, KEOPS_F16 = 1, KEOPS_BF16 = 2 } keops_dtype;
+
+typedef enum {
+  KEOPS_OK = 0,
+  KEOPS_ERR_INVALID_ARG = 1,
+  KEOPS_ERR_UNSUPPORTED = 2,
+  KEOPS_ERR_HIP = 3
+} keops_status;
+
+typedef enum {
+  KEOPS_OP_GAUSS_SUM = 0,
+  KEOPS_OP_LSE = 1,
+  KEOPS_OP_ARGKMIN = 2,
+  KEOPS_OP_GAUSS_SUM_GRAD_X = 3
+} keops_op;
+
+/*
+ * Gaussian kernel sum ("Kernel matrix reduction", Implementation sketch, eq. 1; batched
+ * with signed weights as in "Fast Gauss Sums via Flash Attention", Algorithm 1 Output row):
+ *   out[t][i][c] = sum_j exp(-||x[t][i] - y[t][j]||^2 / (2 sigma^2)) * b[t][j][c]
+ * Shapes: x (B, M, D), y (B, N, D), b (B, N, C), out (B, M, C) float32.
+ * dtype KEOPS_F32: x, y, b are float32; requires B = 1, 1 <= D <= 8, 1 <= C <= 8.
+ * dtype KEOPS_F16 / KEOPS_BF16: x, y, b are fp16 / bf16; requires D = 32 or 64 and
+ * C = 32 or 64 (matrix-core path, fp32 accumulation); any B >= 1.
+ * N = 0 writes zeros.
+ */
+KEOPS_API int keops_gauss_sum(const void* x, const void* y, const void* b, float* out,
+                    int64_t B, int64_t M, int64_t N, int32_t D, int32_t C, float sigma,
+                    keops_dtype dtype, void* workspace, size_t workspace_bytes,
+                    hipStream_t stream);
+
+/*
+ * Log-sum-exp reduction ("Kernel matrix reduction", Overview, list of reductions):
+ *   out[i] = log sum_j exp(-||x_i - y_j||^2 / (2 sigma^2))
+ * Shapes: x (M, D), y (N, D) float32, out (M,) float32. Requires 1 <= D <= 8.
+ * Evaluated with a running row maximum, so rows far from every column stay finite.
+ * N = 0 writes -inf.
+ */
+KEOPS_API int keops_lse(const float* x, const float* y, float* out, int64_t M, int64_t N, int32_t D,
+              float sigma, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * argKmin ("Kernel matrix reduction", Overview: indices of the K smallest entries per row):
+ *   idx[i][0..K-1] = the columns j with the K smallest keys d2_ij, ascending; equal keys
+ *   keep the lower j first.
+ * The key is the float64 evaluation of the squared distance with the differences taken
+ * first and the squares summed in increasing d, each operation rounded (no fused
+ * multiply-add): ((dx0*dx0 + dx1*dx1) + dx2*dx2) + ...; for float32 inputs on a dyadic grid
+ * fine enough (e.g. multiples of 2^-24 in [0,1)^3) this is the exact squared distance.
+ * Shapes: x (M, D), y (N, D) float32; idx (M, K) int32; dist (M, K) float32 or NULL
+ * (the keys rounded to float32). Requires 1 <= D <= 8 and 1 <= K <= min(N, 64)
+ * (K > 64 is KEOPS_ERR_UNSUPPORTED; K > N is KEOPS_ERR_INVALID_ARG). K = 1 is argmin/min.
+ */
+KEOPS_API int keops_argkmin(const float* x, const float* y, int32_t* idx, float* dist, int64_t M,
+                  int64_t N, int32_t D, int32_t K, void* workspace, size_t workspace_bytes,
+                  hipStream_t stream);
+
+/*
+ * Gradient of the Gauss sum with respect to x ("Kernel matrix reduction", Variants:
+ * autodiff through the reduction; the KeOps page's example differentiates sum_i a_i^2),
+ * as a vector-Jacobian product with the upstream gradient g = dL/d out:
+ *   grad[i][:] = -(1/sigma^2) sum_j k_ij (g_i . b_j) (x_i - y_j)
+ * Shapes: x (M, D), y (N, D), b (N, C), g (M, C), grad (M, D), all float32.
+ * Requires 1 <= D <= 8, 1 <= C <= 8. N = 0 writes zeros.
+ */
+KEOPS_API int keops_gauss_sum_grad_x(const float* x, const float* y, const float* b, const float* g,
+                           float* grad, int64_t M, int64_t N, int32_t D, int32_t C,
+                           float sigma, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+
+/* Workspace bytes `op` (a keops_op) needs for these arguments on the current device
+ * (unused arguments are ignored). Returns 0 for unsupported or invalid arguments. */
+KEOPS_API size_t keops_workspace_bytes(int op, int64_t B, int64_t M, int64_t N, int32_t D, int32_t C,
+                             int32_t K, keops_dtype dtype);
+
+/* Static text for a status code. */
+KEOPS_API const char* keops_status_string(int status);
+
+/* Detail of the last failure on the calling thread ("" after a success). */
+KEOPS_API const char* keops_last_error(void);
+
+/* Library version string. */
+KEOPS_API const char* keops_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KEOPS_MI355X_H */

@@ -1,0 +1,141 @@
+"""Fused pairwise kernel reductions on AMD MI355X (gfx950).
+
+Thin Python binding over the C ABI declared in include/keops_mi355x.h. PyTorch supplies
+device memory and the current HIP stream; every arithmetic step runs in the library's HIP
+kernels. Each function takes CUDA (HIP) tensors, allocates its output and workspace from
+PyTorch's allocator (or uses the ones passed in) and enqueues the work on the current stream.
+"""
+from __future__ import annotations
+
+from typing import Optional, Tuple
+
+from . import _lib
+from ._lib import KeopsError  # noqa: F401
+
+__all__ = ["gauss_sum", "lse", "argkmin", "gauss_sum_grad_x", "workspace_bytes", "KeopsError", "version"]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else t.data_ptr()
+
+
+def _stream(device) -> int:
+    torch = _torch()
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _dims(t, rank):
+    if t.dim() != rank:
+        raise ValueError(f"expected a {rank}-D tensor, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.shape
+
+
+def _workspace(nbytes: int, device, workspace=None):
+    torch = _torch()
+    if nbytes == 0:
+        return None, 0
+    if workspace is not None:
+        if workspace.numel() * workspace.element_size() < nbytes:
+            raise ValueError(f"workspace holds {workspace.numel() * workspace.element_size()} bytes, "
+                             f"{nbytes} needed")
+        return workspace, workspace.numel() * workspace.element_size()
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return ws, nbytes
+
+
+def version() -> str:
+    return _lib.load().keops_version().decode()
+
+
+def workspace_bytes(op: int, B: int, M: int, N: int, D: int, C: int = 1, K: int = 0, dtype: int = 0) -> int:
+    return int(_lib.load().keops_workspace_bytes(op, B, M, N, D, C, K, dtype))
+
+
+def gauss_sum(x, y, b, sigma: float, out=None, workspace=None):
+    """s[i, c] = sum_j exp(-|x_i - y_j|^2 / (2 sigma^2)) b[j, c].
+
+    float32: x (M, D), y (N, D), b (N, C) -> (M, C).
+    float16 / bfloat16: x (B, M, D), y (B, N, D), b (B, N, C) -> (B, M, C) float32.
+    """
+    torch = _torch()
+    lib = _lib.load()
+    if x.dtype == torch.float32:
+        M, D = _dims(x, 2)
+        N, _ = _dims(y, 2)
+        _, C = _dims(b, 2)
+        B, dt = 1, _lib.KEOPS_F32
+        shape = (M, C)
+    else:
+        dt = {torch.float16: _lib.KEOPS_F16, torch.bfloat16: _lib.KEOPS_BF16}.get(x.dtype)
+        if dt is None:
+            raise ValueError(f"unsupported dtype {x.dtype}")
+        B, M, D = _dims(x, 3)
+        _, N, _ = _dims(y, 3)
+        _, _, C = _dims(b, 3)
+        shape = (B, M, C)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.float32, device=x.device)
+    nbytes = lib.keops_workspace_bytes(_lib.OP_GAUSS_SUM, B, M, N, D, C, 0, dt)
+    ws, have = _workspace(nbytes, x.device, workspace)
+    st = lib.keops_gauss_sum(_ptr(x), _ptr(y), _ptr(b), _ptr(out), B, M, N, D, C, float(sigma), dt,
+                             _ptr(ws), have, _stream(x.device))
+    _lib.check(st, "keops_gauss_sum")
+    return out
+
+
+def lse(x, y, sigma: float, out=None, workspace=None):
+    """out[i] = log sum_j exp(-|x_i - y_j|^2 / (2 sigma^2)); x (M, D), y (N, D) float32."""
+    torch = _torch()
+    lib = _lib.load()
+    M, D = _dims(x, 2)
+    N, _ = _dims(y, 2)
+    if out is None:
+        out = torch.empty((M,), dtype=torch.float32, device=x.device)
+    nbytes = lib.keops_workspace_bytes(_lib.OP_LSE, 1, M, N, D, 1, 0, _lib.KEOPS_F32)
+    ws, have = _workspace(nbytes, x.device, workspace)
+    st = lib.keops_lse(_ptr(x), _ptr(y), _ptr(out), M, N, D, float(sigma), _ptr(ws), have, _stream(x.device))
+    _lib.check(st, "keops_lse")
+    return out
+
+
+def argkmin(x, y, K: int, with_dist: bool = False, idx=None, dist=None, workspace=None):
+    """Indices (int32) of the K nearest columns per row, ascending, ties to the lower index."""
+    torch = _torch()
+    lib = _lib.load()
+    M, D = _dims(x, 2)
+    N, _ = _dims(y, 2)
+    if idx is None:
+        idx = torch.empty((M, K), dtype=torch.int32, device=x.device)
+    if with_dist and dist is None:
+        dist = torch.empty((M, K), dtype=torch.float32, device=x.device)
+    nbytes = lib.keops_workspace_bytes(_lib.OP_ARGKMIN, 1, M, N, D, 1, K, _lib.KEOPS_F32)
+    ws, have = _workspace(nbytes, x.device, workspace)
+    st = lib.keops_argkmin(_ptr(x), _ptr(y), _ptr(idx), _ptr(dist), M, N, D, int(K), _ptr(ws), have,
+                           _stream(x.device))
+    _lib.check(st, "keops_argkmin")
+    return (idx, dist) if with_dist else idx
+
+
+def gauss_sum_grad_x(x, y, b, g, sigma: float, out=None, workspace=None):
+    """grad[i] = -(1/sigma^2) sum_j k_ij (g_i . b_j)(x_i - y_j); all float32, returns (M, D)."""
+    torch = _torch()
+    lib = _lib.load()
+    M, D = _dims(x, 2)
+    N, _ = _dims(y, 2)
+    _, C = _dims(b, 2)
+    _dims(g, 2)
+    if out is None:
+        out = torch.empty((M, D), dtype=torch.float32, device=x.device)
+    nbytes = lib.keops_workspace_bytes(_lib.OP_GAUSS_SUM_GRAD_X, 1, M, N, D, C, 0, _lib.KEOPS_F32)
+    ws, have = _workspace(nbytes, x.device, workspace)
+    st = lib.keops_gauss_sum_grad_x(_ptr(x), _ptr(y), _ptr(b), _ptr(g), _ptr(out), M, N, D, C, float(sigma),
+                                    _ptr(ws), have, _stream(x.device))
+    _lib.check(st, "keops_gauss_sum_grad_x")
+    return out

@@ -1,0 +1,63 @@
+// Internal declarations shared by the C-ABI layer and the kernel files. Not installed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace keops {
+
+constexpr int kBlock = 256;          // threads per workgroup (4 wave64s) for the low-D family
+constexpr int kMaxLowD = 8;          // largest D of the low-D family
+constexpr int kMaxLowC = 8;          // largest C of the low-D family
+constexpr int kMaxK = 64;            // largest K of argKmin (the per-row list lives in VGPRs)
+constexpr size_t kAlign = 256;       // alignment of workspace sections
+
+// Column record stride (doubles) of the prepared low-D column table: D centred coordinates
+// followed by one per-column exponent term, padded to an even count (16-byte records).
+inline int col_stride(int D) { return (D + 2) & ~1; }
+
+inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+// Launch plan of one low-D reduction: rows per workgroup and the number of column splits.
+struct Plan {
+  int rows_per_block;   // kBlock * R
+  int R;                // rows per lane
+  int64_t row_blocks;   // ceil(M / rows_per_block)
+  int64_t splits;       // S: column ranges reduced independently, then combined in order
+  int64_t cols_per_split;
+};
+
+Plan plan_lowd(int op, int64_t M, int64_t N, int D, int C, int K, int num_cus);
+int device_cus();
+
+// Per-op partial-result bytes per (split, row).
+size_t partial_bytes_per_row(int op, int D, int C, int K);
+
+// ---- launchers (return hipError_t of the launch) ----------------------------------------
+// cols[j] = (y_j - o, -c2 |y_j - o|^2) in float64, o = y_0 when `centre`, else o = 0.
+hipError_t launch_prep_cols(const float* y, double* cols, int64_t N, int D, double c2,
+                            bool centre, hipStream_t s);
+hipError_t launch_gauss_sum_lowd(const float* x, const float* y, const double* cols,
+                                 const float* b, float* out, float* partial, int64_t M,
+                                 int64_t N, int D, int C, double c2, const Plan& p,
+                                 hipStream_t s);
+hipError_t launch_lse_lowd(const float* x, const float* y, const double* cols, float* out,
+                           double* partial, int64_t M, int64_t N, int D, double c2,
+                           const Plan& p, hipStream_t s);
+hipError_t launch_argkmin_lowd(const float* x, const float* y, const double* cols,
+                               int32_t* idx, float* dist, void* partial, int64_t M, int64_t N,
+                               int D, int K, const Plan& p, hipStream_t s);
+hipError_t launch_grad_x_lowd(const float* x, const float* y, const float* b, const float* g,
+                              float* grad, float* partial, int64_t M, int64_t N, int D, int C,
+                              float c2f, float inv_sigma2, const Plan& p, hipStream_t s);
+hipError_t launch_fill(float* out, int64_t n, float value, hipStream_t s);
+
+// Matrix-core (fp16 / bf16) batched Gauss sum.
+bool highd_supported(int D, int C);
+size_t highd_workspace_bytes(int64_t B, int64_t M, int64_t N, int D, int C);
+hipError_t launch_gauss_sum_highd(const void* x, const void* y, const void* b, float* out,
+                                  void* workspace, int64_t B, int64_t M, int64_t N, int D,
+                                  int C, float sigma, bool bf16, hipStream_t s);
+
+}  // namespace keops

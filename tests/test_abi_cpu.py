@@ -1,0 +1,137 @@
+"""The C-ABI library on a host without a GPU: it loads, exports every declared symbol and
+rejects invalid arguments before any HIP call. No compute call is made here."""
+import ctypes
+import math
+import os
+
+import pytest
+
+from pairwise_reductions_amd import _lib
+
+F32, F16 = _lib.KEOPS_F32, _lib.KEOPS_F16
+INVALID, UNSUPPORTED = _lib.KEOPS_ERR_INVALID_ARG, _lib.KEOPS_ERR_UNSUPPORTED
+
+# Fake, never-dereferenced device addresses far apart from each other (validation only).
+X, Y, B, G, OUT, WS, IDX, DIST = (0x10000000 * k for k in range(1, 9))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from pairwise_reductions_amd import build
+        build.build()
+    return _lib.load()
+
+
+def _err(lib):
+    return lib.keops_last_error().decode()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _lib.header_symbols()
+    assert set(names) == {"keops_gauss_sum", "keops_lse", "keops_argkmin", "keops_gauss_sum_grad_x",
+                          "keops_workspace_bytes", "keops_status_string", "keops_last_error", "keops_version"}
+    for name in names:
+        assert hasattr(lib, name), name
+    # the same names, resolved by the dynamic loader straight from the file
+    raw = ctypes.CDLL(_lib.LIB_PATH)
+    for name in names:
+        getattr(raw, name)
+
+
+def test_status_strings_and_version(lib):
+    assert lib.keops_status_string(0) == b"ok"
+    assert lib.keops_status_string(1) == b"invalid argument"
+    assert lib.keops_status_string(2) == b"unsupported configuration"
+    assert lib.keops_status_string(3) == b"HIP runtime error"
+    assert lib.keops_status_string(99) == b"unknown status"
+    assert b"gfx950" in lib.keops_version()
+
+
+def test_workspace_bytes(lib):
+    ws = lib.keops_workspace_bytes
+    n_cols = ws(0, 1, 1_000_000, 1_000_000, 3, 1, 0, F32)
+    assert n_cols >= 1_000_000 * 4 * 8           # float64 column table (4 doubles a column)
+    assert ws(0, 1, 0, 1000, 3, 1, 0, F32) == 0   # M = 0 needs nothing
+    assert ws(0, 1, 10, 0, 3, 1, 0, F32) == 0     # N = 0 needs nothing
+    assert ws(0, 1, 10, 10, 9, 1, 0, F32) == 0    # D out of range
+    assert ws(0, 1, 10, 10, 3, 0, 0, F32) == 0    # C out of range
+    assert ws(0, 2, 10, 10, 3, 1, 0, F32) == 0    # batched float32 unsupported
+    assert ws(2, 1, 10, 10, 3, 1, 11, F32) == 0   # K > N
+    assert ws(2, 1, 10, 100, 3, 1, 65, F32) == 0  # K > 64
+    assert ws(1, 1, -1, 10, 3, 1, 0, F32) == 0    # negative M
+    # small M: the columns are split across workgroups, which needs partial buffers
+    assert ws(0, 1, 100, 100_000, 3, 1, 0, F32) > 100_000 * 32
+    assert ws(3, 1, 100, 100_000, 3, 1, 0, F32) > 0
+
+
+def _gs(lib, x=X, y=Y, b=B, out=OUT, Bt=1, M=100, N=100, D=3, C=1, sigma=0.1, dtype=F32, ws=WS, wsb=1 << 30):
+    return lib.keops_gauss_sum(x, y, b, out, Bt, M, N, D, C, sigma, dtype, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(x=None), INVALID), (dict(y=None), INVALID), (dict(b=None), INVALID), (dict(out=None), INVALID),
+    (dict(M=-1), INVALID), (dict(N=-5), INVALID), (dict(Bt=-1), INVALID),
+    (dict(sigma=0.0), INVALID), (dict(sigma=-1.0), INVALID), (dict(sigma=math.nan), INVALID),
+    (dict(sigma=math.inf), INVALID),
+    (dict(D=9), UNSUPPORTED), (dict(D=0), UNSUPPORTED), (dict(C=0), UNSUPPORTED), (dict(C=9), UNSUPPORTED),
+    (dict(Bt=2), UNSUPPORTED), (dict(dtype=F16, D=3), UNSUPPORTED), (dict(dtype=7), INVALID),
+    (dict(x=X + 2), INVALID), (dict(out=X + 4), INVALID), (dict(M=1 << 31), UNSUPPORTED),
+    (dict(ws=None, wsb=0), INVALID), (dict(wsb=16), INVALID), (dict(ws=WS + 8), INVALID),
+])
+def test_gauss_sum_rejects(lib, kwargs, code):
+    assert _gs(lib, **kwargs) == code
+    assert _err(lib) != ""
+
+
+def test_empty_rows_is_a_noop(lib):
+    assert _gs(lib, M=0) == 0
+    assert _err(lib) == ""
+    assert lib.keops_lse(X, Y, OUT, 0, 10, 3, 0.1, None, 0, None) == 0
+    assert lib.keops_argkmin(X, Y, IDX, None, 0, 10, 3, 4, None, 0, None) == 0
+    assert lib.keops_gauss_sum_grad_x(X, Y, B, G, OUT, 0, 10, 3, 1, 0.1, None, 0, None) == 0
+
+
+def test_lse_rejects(lib):
+    f = lib.keops_lse
+    assert f(None, Y, OUT, 10, 10, 3, 0.1, WS, 1 << 30, None) == INVALID
+    assert f(X, Y, None, 10, 10, 3, 0.1, WS, 1 << 30, None) == INVALID
+    assert f(X, Y, OUT, 10, 10, 0, 0.1, WS, 1 << 30, None) == UNSUPPORTED
+    assert f(X, Y, OUT, 10, 10, 3, -0.1, WS, 1 << 30, None) == INVALID
+    assert f(X, Y, X, 10, 10, 3, 0.1, WS, 1 << 30, None) == INVALID   # out aliases x
+    assert f(X, Y, OUT, 10, 10, 3, 0.1, None, 0, None) == INVALID     # workspace needed
+
+
+def test_argkmin_rejects(lib):
+    f = lib.keops_argkmin
+    assert f(X, Y, IDX, None, 10, 10, 3, 0, WS, 1 << 30, None) == INVALID
+    assert f(X, Y, IDX, None, 10, 10, 3, 11, WS, 1 << 30, None) == INVALID
+    assert f(X, Y, IDX, None, 10, 100, 3, 65, WS, 1 << 30, None) == UNSUPPORTED
+    assert f(X, Y, IDX, None, 10, 0, 3, 1, WS, 1 << 30, None) == INVALID  # N = 0: K > N
+    assert f(X, Y, None, None, 10, 10, 3, 4, WS, 1 << 30, None) == INVALID
+    assert f(X, Y, IDX, DIST + 2, 10, 10, 3, 4, WS, 1 << 30, None) == INVALID
+    assert f(X, Y, IDX, IDX + 8, 10, 10, 3, 4, WS, 1 << 30, None) == INVALID  # idx and dist overlap
+    assert f(X, Y, IDX, None, 10, 10, 9, 4, WS, 1 << 30, None) == UNSUPPORTED
+
+
+def test_grad_rejects(lib):
+    f = lib.keops_gauss_sum_grad_x
+    assert f(X, Y, B, None, OUT, 10, 10, 3, 1, 0.1, WS, 1 << 30, None) == INVALID
+    assert f(X, Y, B, G, OUT, 10, 10, 3, 0, 0.1, WS, 1 << 30, None) == UNSUPPORTED
+    assert f(X, Y, B, G, G, 10, 10, 3, 1, 0.1, WS, 1 << 30, None) == INVALID  # grad aliases g
+    assert f(X, Y, B, G, OUT, 10, 10, 3, 1, 0.0, WS, 1 << 30, None) == INVALID
+
+
+def test_error_is_thread_local(lib):
+    import threading
+    assert _gs(lib, D=9) == UNSUPPORTED
+    seen = []
+
+    def worker():
+        seen.append(_err(lib))
+
+    t = threading.Thread(target=worker)
+    t.start()
+    t.join()
+    assert seen == [""]
+    assert "D=9" in _err(lib)

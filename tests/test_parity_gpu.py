@@ -1,0 +1,211 @@
+"""Parity of the HIP path (through the C ABI) with the float64 oracle on seeded inputs.
+
+Tolerances: Gauss sums and gradients within 1e-4 of the oracle relative to the row normaliser
+sum_j |k_ij b_j| (resp. sum_j |k_ij (g_i.b_j)(x_i - y_j)| / sigma^2); log-sum-exp within 1e-4
+absolute; argKmin indices bit-exact and distances within 1e-6 relative.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from pairwise_reductions_amd import workloads
+
+pytestmark = pytest.mark.gpu
+
+TOL_F32 = 1e-4
+TOL_LSE = 1e-4
+
+
+def _dev(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def _host(t):
+    import torch
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def _announce(name, **kw):
+    print(f"[case] {name} " + " ".join(f"{k}={v}" for k, v in kw.items()), flush=True)
+
+
+def lse_bound(want):
+    """1e-4 absolute, widened to 4 float32 ulps where |lse| is so large that the float32
+    output itself cannot carry 1e-4 (|lse| above about 200)."""
+    return np.maximum(TOL_LSE, 4.0 * np.finfo(np.float32).eps * np.abs(want))
+
+
+def assert_normalised(got, want, norm, tol, what=""):
+    got = np.asarray(got, dtype=np.float64)
+    err = np.abs(got - want)
+    pos = norm > 0
+    if np.any(pos):
+        rel = err[pos] / norm[pos]
+        worst = float(rel.max())
+        assert worst <= tol, f"{what}: max normalised error {worst:.3e} > {tol:.1e}"
+    assert np.all(np.abs(got[~pos]) <= np.finfo(np.float32).tiny), f"{what}: nonzero where the normaliser is 0"
+
+
+def _rand(seed, M, N, D, C, lo=0.0, hi=1.0):
+    rng = np.random.default_rng(seed)
+    x = rng.uniform(lo, hi, (M, D)).astype(np.float32)
+    y = rng.uniform(lo, hi, (N, D)).astype(np.float32)
+    b = rng.standard_normal((N, C)).astype(np.float32)
+    return x, y, b
+
+
+GAUSS_SHAPES = [
+    # (M, N, D, C, sigma): single tile, ragged row/column tails, every D and several C, the
+    # column-split path (small M, large N) and the unsplit path (large M)
+    (1, 1, 3, 1, 0.1), (1, 37, 3, 1, 0.3), (257, 1000, 3, 1, 0.1), (1025, 513, 1, 1, 0.05),
+    (700, 2000, 2, 3, 0.2), (513, 1500, 8, 8, 0.5), (2000, 300, 5, 4, 0.3), (300, 4099, 4, 2, 0.07),
+    (100, 100_003, 3, 2, 0.02), (50_001, 777, 3, 1, 0.1), (1500, 1500, 6, 5, 0.4), (999, 2500, 7, 7, 0.6),
+]
+
+
+@pytest.mark.parametrize("M,N,D,C,sigma", GAUSS_SHAPES)
+def test_gauss_sum_shapes(M, N, D, C, sigma):
+    import pairwise_reductions_amd as pr
+    _announce("gauss_sum", M=M, N=N, D=D, C=C, sigma=sigma)
+    x, y, b = _rand(M * 7 + N, M, N, D, C)
+    sig = float(np.float32(sigma))
+    got = _host(pr.gauss_sum(_dev(x), _dev(y), _dev(b), sig))
+    want, norm = oracle.gauss_sum(x, y, b, sig, workers=8)
+    assert_normalised(got, want, norm, TOL_F32, "gauss_sum")
+
+
+def test_gauss_sum_workload_10k_all_rows():
+    import pairwise_reductions_amd as pr
+    inp = workloads.make_inputs("gauss_sum_10k")
+    _announce("gauss_sum_10k", M=inp["M"], N=inp["N"])
+    sig = float(inp["sigma"])
+    got = _host(pr.gauss_sum(_dev(inp["x"]), _dev(inp["y"]), _dev(inp["b"]), sig))
+    want, norm = oracle.gauss_sum(inp["x"], inp["y"], inp["b"], sig, workers=8)
+    assert_normalised(got, want, norm, TOL_F32, "gauss_sum_10k")
+
+
+def test_gauss_sum_edge_cases():
+    import torch
+    import pairwise_reductions_amd as pr
+    _announce("gauss_sum_edges")
+    x, y, b = _rand(3, 64, 10, 3, 2)
+    # N = 0 writes zeros
+    out = pr.gauss_sum(_dev(x), _dev(y[:0]), _dev(b[:0]), 0.1)
+    assert np.all(_host(out) == 0.0)
+    # M = 0 is a no-op (the output keeps its contents)
+    sentinel = torch.full((0, 2), 7.0, device="cuda")
+    pr.gauss_sum(_dev(x[:0]), _dev(y), _dev(b), 0.1, out=sentinel)
+    # x_i = y_j with every other column far away: the result is exactly b_j
+    y2 = np.array([[0, 0, 0], [50, 0, 0], [0, 60, 0]], np.float32)
+    b2 = np.array([[0.75], [2.0], [-4.0]], np.float32)
+    got = _host(pr.gauss_sum(_dev(y2[[1, 0, 2]]), _dev(y2), _dev(b2), 0.5))
+    assert got[0, 0] == 2.0 and got[1, 0] == 0.75 and got[2, 0] == -4.0
+    # sigma -> infinity: s_i = sum_j b_j
+    x3, y3, b3 = _rand(5, 300, 700, 3, 1)
+    got = _host(pr.gauss_sum(_dev(x3), _dev(y3), _dev(b3), 1e30))
+    assert np.allclose(got[:, 0], b3.astype(np.float64).sum(), rtol=0, atol=1e-4 * np.abs(b3).sum())
+
+
+def test_gauss_sum_deterministic():
+    import pairwise_reductions_amd as pr
+    _announce("gauss_sum_determinism")
+    x, y, b = _rand(11, 3000, 20_000, 3, 1)
+    xd, yd, bd = _dev(x), _dev(y), _dev(b)
+    a = _host(pr.gauss_sum(xd, yd, bd, 0.05))
+    for _ in range(3):
+        assert np.array_equal(a, _host(pr.gauss_sum(xd, yd, bd, 0.05)))
+
+
+LSE_SHAPES = [(1, 1, 3, 0.1), (257, 1000, 3, 0.1), (1025, 513, 1, 0.05), (700, 2000, 2, 0.2),
+              (513, 1500, 8, 0.5), (100, 100_003, 3, 0.02), (50_001, 777, 3, 0.1), (333, 7, 3, 0.01)]
+
+
+@pytest.mark.parametrize("M,N,D,sigma", LSE_SHAPES)
+def test_lse_shapes(M, N, D, sigma):
+    import pairwise_reductions_amd as pr
+    _announce("lse", M=M, N=N, D=D, sigma=sigma)
+    x, y, _ = _rand(M * 3 + N, M, N, D, 1)
+    sig = float(np.float32(sigma))
+    got = _host(pr.lse(_dev(x), _dev(y), sig))
+    want = oracle.logsumexp_reduction(x, y, sig, workers=8)
+    assert np.all(np.abs(got - want) <= lse_bound(want))
+
+
+def test_lse_far_rows_and_empty():
+    import pairwise_reductions_amd as pr
+    _announce("lse_far_and_empty")
+    rng = np.random.default_rng(21)
+    y = rng.random((5000, 3)).astype(np.float32)
+    # rows far from every column: a plain sum of exponentials underflows, the reduction not
+    x = (rng.random((300, 3)) + np.array([3.0, 0.0, 0.0])).astype(np.float32)
+    got = _host(pr.lse(_dev(x), _dev(y), 0.05))
+    want = oracle.logsumexp_reduction(x, y, float(np.float32(0.05)))
+    assert np.all(np.isfinite(got))
+    assert np.all(np.abs(got - want) <= lse_bound(want))
+    got = _host(pr.lse(_dev(x), _dev(y[:0]), 0.1))
+    assert np.all(np.isneginf(got))
+
+
+ARGK_SHAPES = [(1, 1, 3, 1), (257, 1000, 3, 10), (1025, 513, 1, 4), (700, 2000, 2, 16),
+               (513, 1500, 8, 32), (100, 100_003, 3, 10), (50_001, 777, 3, 10), (300, 64, 3, 64),
+               (200, 5000, 3, 64), (333, 20, 5, 20), (1000, 3000, 3, 3)]
+
+
+@pytest.mark.parametrize("M,N,D,K", ARGK_SHAPES)
+def test_argkmin_shapes(M, N, D, K):
+    import pairwise_reductions_amd as pr
+    _announce("argkmin", M=M, N=N, D=D, K=K)
+    rng = np.random.default_rng(M + N + K)
+    x = workloads.grid24(rng, (M, D))
+    y = workloads.grid24(rng, (N, D))
+    idx, dist = pr.argkmin(_dev(x), _dev(y), K, with_dist=True)
+    idx, dist = _host(idx), _host(dist)
+    want_idx, want_d2 = oracle.argkmin(x, y, K, workers=8)
+    assert np.array_equal(idx.astype(np.int64), want_idx)
+    assert np.allclose(dist, want_d2, rtol=1e-6, atol=0)
+
+
+def test_argkmin_ties_lowest_index():
+    import pairwise_reductions_amd as pr
+    _announce("argkmin_ties")
+    rng = np.random.default_rng(5)
+    # a coarse grid makes many exactly equal distances; duplicates are planted on purpose
+    x = (rng.integers(0, 8, size=(2000, 3)) / 8.0).astype(np.float32)
+    y = (rng.integers(0, 8, size=(3000, 3)) / 8.0).astype(np.float32)
+    y[100:200] = y[0]
+    for K in (1, 5, 10, 33):
+        idx = _host(pr.argkmin(_dev(x), _dev(y), K)).astype(np.int64)
+        want, _ = oracle.argkmin(x, y, K, workers=8)
+        assert np.array_equal(idx, want), K
+
+
+GRAD_SHAPES = [(1, 1, 3, 1, 0.1), (257, 1000, 3, 1, 0.1), (1025, 513, 1, 1, 0.05), (700, 2000, 2, 3, 0.2),
+               (513, 1500, 8, 8, 0.5), (100, 100_003, 3, 2, 0.05), (20_001, 777, 3, 1, 0.1)]
+
+
+@pytest.mark.parametrize("M,N,D,C,sigma", GRAD_SHAPES)
+def test_grad_x_shapes(M, N, D, C, sigma):
+    import pairwise_reductions_amd as pr
+    _announce("grad_x", M=M, N=N, D=D, C=C, sigma=sigma)
+    x, y, b = _rand(M * 5 + N, M, N, D, C)
+    g = np.random.default_rng(M).standard_normal((M, C)).astype(np.float32)
+    sig = float(np.float32(sigma))
+    got = _host(pr.gauss_sum_grad_x(_dev(x), _dev(y), _dev(b), _dev(g), sig))
+    want, norm = oracle.gauss_sum_grad_x(x, y, b, g, sig, workers=8)
+    assert_normalised(got, want, norm, TOL_F32, "grad_x")
+
+
+def test_grad_x_of_squared_loss_mixture():
+    """The KeOps example's loss sum_i a_i^2 on the 8-cluster mixture: the upstream gradient
+    is g = 2 s with s the oracle's forward, rounded to float32 for both sides."""
+    import pairwise_reductions_amd as pr
+    inp = workloads.make_inputs("gauss_sum_grad_x_100k_mixture", M=4000, N=6000)
+    _announce("grad_x_loss_mixture", M=4000, N=6000)
+    sig = float(inp["sigma"])
+    s, _ = oracle.gauss_sum(inp["x"], inp["y"], inp["b"], sig, workers=8)
+    g = (2.0 * s).astype(np.float32)
+    got = _host(pr.gauss_sum_grad_x(_dev(inp["x"]), _dev(inp["y"]), _dev(inp["b"]), _dev(g), sig))
+    want, norm = oracle.gauss_sum_grad_x(inp["x"], inp["y"], inp["b"], g, sig, workers=8)
+    assert_normalised(got, want, norm, TOL_F32, "grad_x loss")
