@@ -129,13 +129,88 @@ def cpu_baseline_gauss(inp, rows):
             "seconds": dt}
 
 
+def _resident(inp, keys, dev):
+    import torch
+    return [torch.from_numpy(inp[k]).to(dev) for k in keys]
+
+
+def bench_all(steps, warmup):
+    """Time every workload through the library (inputs resident on the GPU)."""
+    import torch
+
+    import pairwise_reductions_amd as pr
+    from pairwise_reductions_amd import _lib, workloads
+
+    dev = torch.device("cuda:0")
+    rows = {}
+
+    # Gauss sum 10k (small case: launch-dominated)
+    inp = workloads.make_inputs("gauss_sum_10k")
+    x, y, b = _resident(inp, ("x", "y", "b"), dev)
+    sig = float(inp["sigma"])
+    out = torch.empty((inp["M"], inp["C"]), device=dev)
+    ws = torch.empty(max(1, pr.workspace_bytes(0, 1, inp["M"], inp["N"], 3, 1)), dtype=torch.uint8, device=dev)
+    t = _events_time(lambda: pr.gauss_sum(x, y, b, sig, out=out, workspace=ws), max(steps, 100), warmup)
+    pairs = float(inp["M"]) * inp["N"]
+    rows["gauss_sum_10k"] = {"ms": t * 1e3, "pairs_per_s": pairs / t,
+                             "frac_fp32_peak": pairs * 12 / t / 1e12 / PEAK_FP32_VECTOR_TFLOPS}
+
+    # Gauss sum forward + gradient of sum_i s_i^2 (g = 2 s), 100k mixture
+    inp = workloads.make_inputs("gauss_sum_grad_x_100k_mixture")
+    x, y, b = _resident(inp, ("x", "y", "b"), dev)
+    sig = float(inp["sigma"])
+    M, N = inp["M"], inp["N"]
+    out = torch.empty((M, 1), device=dev)
+    g = torch.empty((M, 1), device=dev)
+    grad = torch.empty((M, 3), device=dev)
+    ws = torch.empty(max(pr.workspace_bytes(0, 1, M, N, 3, 1), pr.workspace_bytes(3, 1, M, N, 3, 1), 1),
+                     dtype=torch.uint8, device=dev)
+
+    def fwd_bwd():
+        pr.gauss_sum(x, y, b, sig, out=out, workspace=ws)
+        torch.mul(out, 2.0, out=g)
+        pr.gauss_sum_grad_x(x, y, b, g, sig, out=grad, workspace=ws)
+
+    t = _events_time(fwd_bwd, steps, warmup)
+    tf = _events_time(lambda: pr.gauss_sum(x, y, b, sig, out=out, workspace=ws), steps, warmup)
+    tb = _events_time(lambda: pr.gauss_sum_grad_x(x, y, b, g, sig, out=grad, workspace=ws), steps, warmup)
+    pairs = float(M) * N
+    rows["gauss_sum_grad_x_100k_mixture"] = {
+        "ms": t * 1e3, "fwd_ms": tf * 1e3, "grad_ms": tb * 1e3, "pairs_per_s": 2 * pairs / t,
+        "frac_fp32_peak": pairs * (12 + grad_flops_per_pair(3, 1)) / t / 1e12 / PEAK_FP32_VECTOR_TFLOPS}
+
+    # argKmin (K=10) + log-sum-exp, 100k uniform
+    inp = workloads.make_inputs("argkmin_lse_100k")
+    x, y = _resident(inp, ("x", "y"), dev)
+    M, N, K = inp["M"], inp["N"], inp["K"]
+    sig = float(inp["sigma"])
+    idx = torch.empty((M, K), dtype=torch.int32, device=dev)
+    lse_out = torch.empty((M,), device=dev)
+    ws = torch.empty(max(pr.workspace_bytes(2, 1, M, N, 3, 1, K), pr.workspace_bytes(1, 1, M, N, 3, 1), 1),
+                     dtype=torch.uint8, device=dev)
+
+    def argk_lse():
+        pr.argkmin(x, y, K, idx=idx, workspace=ws)
+        pr.lse(x, y, sig, out=lse_out, workspace=ws)
+
+    t = _events_time(argk_lse, steps, warmup)
+    ta = _events_time(lambda: pr.argkmin(x, y, K, idx=idx, workspace=ws), steps, warmup)
+    tl = _events_time(lambda: pr.lse(x, y, sig, out=lse_out, workspace=ws), steps, warmup)
+    pairs = float(M) * N
+    rows["argkmin_lse_100k"] = {"ms": t * 1e3, "argkmin_ms": ta * 1e3, "lse_ms": tl * 1e3,
+                                "pairs_per_s": 2 * pairs / t}
+    return rows
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--cpu-rows", type=int, default=2048, help="rows of the CPU-oracle sample")
+    ap.add_argument("--cpu-rows", type=int, default=8192, help="rows of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--all", action="store_true", help="also time the other workloads")
+    ap.add_argument("--all-out", default=os.path.join("gpurun_out", "bench_all.json"))
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this engine has no multi-GPU path (asked for --gpus {args.gpus})",
@@ -145,6 +220,13 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.all:
+        rows = bench_all(args.steps, args.warmup)
+        os.makedirs(os.path.dirname(os.path.abspath(args.all_out)), exist_ok=True)
+        with open(args.all_out, "w") as f:
+            json.dump(rows, f, indent=1)
+        for k, v in rows.items():
+            print(f"[all] {k}: " + ", ".join(f"{a}={b:.4g}" for a, b in v.items()), file=sys.stderr, flush=True)
     res = bench_gauss_1m(args.steps, args.warmup, args.cpu_rows, cpu_baseline=not args.no_cpu_baseline)
     print(json.dumps(res), flush=True)
 

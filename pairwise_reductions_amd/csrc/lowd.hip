@@ -486,6 +486,7 @@ constexpr int kRowsSum = 4;
 constexpr int kRowsLse = 4;
 constexpr int kRowsGrad = 2;
 constexpr int kLseTile = 8;
+constexpr int64_t kSplitCols = 65536;
 
 inline int argk_bucket(int K) {
   if (K <= 1) return 1;
@@ -625,12 +626,16 @@ Plan plan_lowd(int op, int64_t M, int64_t N, int D, int C, int K, int num_cus) {
   }
   p.rows_per_block = kBlock * p.R;
   p.row_blocks = M > 0 ? ceil_div(M, p.rows_per_block) : 0;
-  // Aim for about four workgroups (16 wave64s) per compute unit; split the columns when the
-  // rows alone cannot supply that, keeping at least 256 columns per split.
-  const int64_t target = (int64_t)num_cus * 4;
+  // Split the columns so that (a) there are at least eight workgroups (32 wave64s) per compute
+  // unit over the launch, and (b) one split's column table stays within kSplitCols columns,
+  // a working set that fits one XCD's L2 while the resident workgroups (consecutive row
+  // blocks of the same split) stream it together. Every split keeps >= 256 columns.
+  const int64_t target = (int64_t)num_cus * 8;
   int64_t S = 1;
   if (p.row_blocks > 0 && p.row_blocks < target) S = ceil_div(target, p.row_blocks);
-  const int64_t max_split = N / 256 > 1 ? N / 256 : 1;
+  if (S < ceil_div(N, kSplitCols)) S = ceil_div(N, kSplitCols);
+  int64_t max_split = N / 256 > 1 ? N / 256 : 1;
+  if (op == 2 && max_split > 16) max_split = 16;  // argKmin partial lists are K entries per row
   if (S > max_split) S = max_split;
   if (S < 1) S = 1;
   int64_t cps = S > 1 ? ceil_div(N, S) : (N > 0 ? N : 1);
