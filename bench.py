@@ -179,6 +179,21 @@ def bench_all(steps, warmup):
         "ms": t * 1e3, "fwd_ms": tf * 1e3, "grad_ms": tb * 1e3, "pairs_per_s": 2 * pairs / t,
         "frac_fp32_peak": pairs * (12 + grad_flops_per_pair(3, 1)) / t / 1e12 / PEAK_FP32_VECTOR_TFLOPS}
 
+    # Batched Gauss sum, fp16 matrix-core path: B=4, M=N=16384, D=C=32, tau=1
+    inp = workloads.make_inputs("batched_gauss_sum_fp16")
+    q, k, v = _resident(inp, ("x", "y", "b"), dev)
+    Bt, M, N, D, C = inp["B"], inp["M"], inp["N"], inp["D"], inp["C"]
+    out = torch.empty((Bt, M, C), device=dev)
+    ws = torch.empty(max(1, pr.workspace_bytes(0, Bt, M, N, D, C, 0, _lib.KEOPS_F16)), dtype=torch.uint8,
+                     device=dev)
+    t = _events_time(lambda: pr.gauss_sum(q, k, v, float(inp["sigma"]), out=out, workspace=ws),
+                     max(steps, 100), warmup)
+    pairs = float(Bt) * M * N
+    mflops = pairs * 2 * (D + C)
+    rows["batched_gauss_sum_fp16"] = {"ms": t * 1e3, "pairs_per_s": pairs / t,
+                                      "mfma_tflops": mflops / t / 1e12,
+                                      "frac_fp16_mfma_peak": mflops / t / 1e12 / PEAK_FP16_MFMA_TFLOPS}
+
     # argKmin (K=10) + log-sum-exp, 100k uniform
     inp = workloads.make_inputs("argkmin_lse_100k")
     x, y = _resident(inp, ("x", "y"), dev)

@@ -160,7 +160,7 @@ size_t keops_workspace_bytes(int op, int64_t B, int64_t M, int64_t N, int32_t D,
   if (B < 0 || M < 0 || N < 0 || M > kMaxExtent || N > kMaxExtent) return 0;
   switch (op) {
     case KEOPS_OP_GAUSS_SUM:
-      if (dtype == KEOPS_F16 || dtype == KEOPS_BF16) {
+      if (dtype == KEOPS_F16) {
         if (!keops::highd_supported(D, C)) return 0;
         return keops::highd_workspace_bytes(B, M, N, D, C);
       }
@@ -188,6 +188,7 @@ int keops_gauss_sum(const void* x, const void* y, const void* b, float* out, int
   KEOPS_TRY(check_sigma(sigma));
   const bool half = (dtype == KEOPS_F16 || dtype == KEOPS_BF16);
   if (!half && dtype != KEOPS_F32) return fail(KEOPS_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  if (dtype == KEOPS_BF16) return fail(KEOPS_ERR_UNSUPPORTED, "the bf16 matrix-core path is not built (use KEOPS_F16)");
   if (half) {
     if (!keops::highd_supported(D, C))
       return fail(KEOPS_ERR_UNSUPPORTED, "fp16/bf16 path needs D in {32, 64} and C in {32, 64} (got D=%d C=%d)", D, C);

@@ -63,6 +63,10 @@ def test_workspace_bytes(lib):
     # small M: the columns are split across workgroups, which needs partial buffers
     assert ws(0, 1, 100, 100_000, 3, 1, 0, F32) > 100_000 * 32
     assert ws(3, 1, 100, 100_000, 3, 1, 0, F32) > 0
+    # fp16 matrix-core path: key norms (float) and the permuted fp16 copy of v
+    assert ws(0, 4, 16384, 16384, 32, 32, 0, F16) >= 4 * 16384 * (4 + 32 * 2)
+    assert ws(0, 4, 16384, 16384, 48, 32, 0, F16) == 0
+    assert ws(0, 4, 16384, 16384, 32, 32, 0, 2) == 0
 
 
 def _gs(lib, x=X, y=Y, b=B, out=OUT, Bt=1, M=100, N=100, D=3, C=1, sigma=0.1, dtype=F32, ws=WS, wsb=1 << 30):
@@ -76,6 +80,8 @@ def _gs(lib, x=X, y=Y, b=B, out=OUT, Bt=1, M=100, N=100, D=3, C=1, sigma=0.1, dt
     (dict(sigma=math.inf), INVALID),
     (dict(D=9), UNSUPPORTED), (dict(D=0), UNSUPPORTED), (dict(C=0), UNSUPPORTED), (dict(C=9), UNSUPPORTED),
     (dict(Bt=2), UNSUPPORTED), (dict(dtype=F16, D=3), UNSUPPORTED), (dict(dtype=7), INVALID),
+    (dict(dtype=2, D=32, C=32), UNSUPPORTED), (dict(dtype=F16, D=48, C=32), UNSUPPORTED),
+    (dict(dtype=F16, D=32, C=32, x=X + 8), INVALID),
     (dict(x=X + 2), INVALID), (dict(out=X + 4), INVALID), (dict(M=1 << 31), UNSUPPORTED),
     (dict(ws=None, wsb=0), INVALID), (dict(wsb=16), INVALID), (dict(ws=WS + 8), INVALID),
 ])

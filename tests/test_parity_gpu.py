@@ -209,3 +209,64 @@ def test_grad_x_of_squared_loss_mixture():
     got = _host(pr.gauss_sum_grad_x(_dev(inp["x"]), _dev(inp["y"]), _dev(inp["b"]), _dev(g), sig))
     want, norm = oracle.gauss_sum_grad_x(inp["x"], inp["y"], inp["b"], g, sig, workers=8)
     assert_normalised(got, want, norm, TOL_F32, "grad_x loss")
+
+
+# ------------------------------------------------------------------ fp16 matrix-core path
+TOL_F16 = 2e-3
+
+HIGHD_SHAPES = [
+    # (B, M, N, D, C, sigma)
+    (1, 1, 1, 32, 32, 1.0), (1, 100, 77, 32, 32, 1.0), (2, 300, 1000, 32, 32, 0.7),
+    (4, 513, 2049, 32, 32, 1.0), (1, 1024, 4096, 64, 32, 1.5), (1, 257, 300, 32, 64, 1.0),
+    (2, 700, 5000, 64, 64, 2.0), (3, 4097, 8191, 32, 32, 1.0),
+]
+
+
+def _highd_inputs(seed, B, M, N, D, C, shift=0.0):
+    rng = np.random.default_rng(seed)
+    q = (rng.standard_normal((B, M, D)) / np.sqrt(D) + shift).astype(np.float16)
+    k = (rng.standard_normal((B, N, D)) / np.sqrt(D)).astype(np.float16)
+    v = rng.standard_normal((B, N, C)).astype(np.float16)
+    return q, k, v
+
+
+def _check_highd(q, k, v, sigma):
+    import pairwise_reductions_amd as pr
+    sig = float(np.float32(sigma))
+    got = _host(pr.gauss_sum(_dev(q), _dev(k), _dev(v), sig))
+    tau = 1.0 / (sig * sig)
+    want, norm = oracle.gauss_sum_batched(q, k, v, tau, workers=8)
+    assert_normalised(got, want, norm, TOL_F16, "gauss_sum fp16")
+
+
+@pytest.mark.parametrize("B,M,N,D,C,sigma", HIGHD_SHAPES)
+def test_gauss_sum_fp16_shapes(B, M, N, D, C, sigma):
+    _announce("gauss_sum_fp16", B=B, M=M, N=N, D=D, C=C, sigma=sigma)
+    q, k, v = _highd_inputs(B * 13 + M + N, B, M, N, D, C)
+    _check_highd(q, k, v, sigma)
+
+
+def test_gauss_sum_fp16_far_rows_and_rescale():
+    """Rows far from every key (all kernel values below the fp16 normal range without the
+    running shift), and keys ordered far-to-near so the shift must rise mid-sweep."""
+    _announce("gauss_sum_fp16_far")
+    q, k, v = _highd_inputs(77, 2, 600, 3000, 32, 32, shift=1.0)
+    _check_highd(q, k, v, 1.0)
+    rng = np.random.default_rng(78)
+    qn = (rng.standard_normal((1, 300, 32)) / np.sqrt(32)).astype(np.float16)
+    kn = (rng.standard_normal((1, 4000, 32)) / np.sqrt(32)).astype(np.float16)
+    d2 = ((qn[0, :1].astype(np.float64) - kn[0].astype(np.float64)) ** 2).sum(axis=1)
+    kn = kn[:, np.argsort(-d2)]          # farthest keys first for row 0
+    vn = rng.standard_normal((1, 4000, 32)).astype(np.float16)
+    _check_highd(qn, kn, vn, 0.25)
+
+
+def test_gauss_sum_fp16_workload_sampled():
+    """The B=4, M=N=16384, D=C=32 workload at full size, checked on sampled rows."""
+    import pairwise_reductions_amd as pr
+    inp = workloads.make_inputs("batched_gauss_sum_fp16")
+    _announce("gauss_sum_fp16_workload", B=inp["B"], M=inp["M"], N=inp["N"])
+    got = _host(pr.gauss_sum(_dev(inp["x"]), _dev(inp["y"]), _dev(inp["b"]), float(inp["sigma"])))
+    rows = workloads.sample_rows(inp["M"], 256, seed=3)
+    want, norm = oracle.gauss_sum_batched(inp["x"][:, rows], inp["y"], inp["b"], 1.0, workers=8)
+    assert_normalised(got[:, rows], want, norm, TOL_F16, "fp16 workload")
