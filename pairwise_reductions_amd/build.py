@@ -17,6 +17,10 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libkeops_mi355x.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 SOURCES = ["abi.hip", "lowd.hip", "highd.hip"]
+# Per-source extras. highd.hip keeps matrix-core accumulators in ordinary VGPRs (the
+# exponent and max steps read every accumulator value, so AGPR copies would cost a VALU op
+# each) and runs with IEEE mode off, so max needs no NaN quieting.
+EXTRA_FLAGS = {"highd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mno-amdgpu-ieee", "-fno-honor-nans"]}
 ARCH = os.environ.get("KEOPS_OFFLOAD_ARCH", "gfx950")
 
 # Packed-FP32 instruction selection is switched off: every float32 op is a plain VALU op.
@@ -50,7 +54,7 @@ def build(verbose: bool = False) -> str:
     jobs = []
     for src in SOURCES:
         obj = os.path.join(objdir, src.replace(".hip", ".o"))
-        jobs.append((obj, [hipcc, *COMMON_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]))
+        jobs.append((obj, [hipcc, *COMMON_FLAGS, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]))
     with cf.ThreadPoolExecutor(max_workers=min(len(jobs), os.cpu_count() or 1)) as ex:
         outs = list(ex.map(lambda j: _run(j[1]), jobs))
     tmp = LIB_PATH + ".tmp"
