@@ -36,6 +36,24 @@ def grad_flops_per_pair(D, C):
     return 5 * D + 2 * C + 1
 
 
+# HBM bytes per launch of the dominant kernel on the 1M workload, from rocprofv3 --pmc
+# FETCH_SIZE and WRITE_SIZE (each scaled by what it reads for a 256 MiB copy: x2.0 and x1.0).
+# Reported only while the kernel source is byte-identical to the one that was measured.
+MEASURED_TRAFFIC = {"bytes": 851386226, "source": "pairwise_reductions_amd/csrc/lowd.hip",
+                    "sha256_prefix": "d9b71c3ac747c558"}
+
+
+def measured_traffic():
+    import hashlib
+    path = os.path.join(ROOT, MEASURED_TRAFFIC["source"])
+    try:
+        with open(path, "rb") as f:
+            digest = hashlib.sha256(f.read()).hexdigest()
+    except OSError:
+        return None
+    return MEASURED_TRAFFIC["bytes"] if digest.startswith(MEASURED_TRAFFIC["sha256_prefix"]) else None
+
+
 def _events_time(fn, steps, warmup):
     import torch
     for _ in range(warmup):
@@ -98,7 +116,8 @@ def bench_gauss_1m(steps, warmup, cpu_rows, cpu_baseline=True):
             "peak": PEAK_FP32_VECTOR_TFLOPS,
             "unit": "TFLOP/s",
             "frac": achieved / PEAK_FP32_VECTOR_TFLOPS,
-            "traffic": None,
+            "traffic": measured_traffic(),
+            "traffic_unit": "bytes per launch",
             "kernel": "gauss_sum_kernel<3,1,4>",
             "flop_per_pair": gauss_flops_per_pair(D, C),
             "kernel_ms": t * 1e3,
