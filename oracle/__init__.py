@@ -8,7 +8,9 @@ from .reductions import (  # noqa: F401
     default_workers,
     gauss_sum,
     gauss_sum_batched,
+    gauss_sum_grad_b,
     gauss_sum_grad_x,
+    gauss_sum_grad_y,
     keys_are_exact,
     logsumexp_reduction,
     squared_distances,

@@ -255,6 +255,69 @@ def gauss_sum_grad_x(x, y, b, g, sigma: float, workers: Optional[int] = None) ->
     return grad, n
 
 
+def gauss_sum_grad_y(x, y, b, g, sigma: float, workers: Optional[int] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """Gradient of the Gauss sum with respect to the columns y, contracted with g.
+
+    [KMR, Variants: each partial derivative is its own reduction]: d k_ij / d y_j =
+    +k_ij (x_i - y_j) / sigma^2, so
+        grad_y[j, :] = (1/sigma^2) sum_i k_ij (g_i . b_j) (x_i - y_j),
+    a reduction over the rows i for every column j.
+    Returns (grad_y (N, D), n (N, D)) with n[j, d] = (1/sigma^2) sum_i |k_ij (g_i . b_j)(x_id - y_jd)|.
+    """
+    x = _f64(x)
+    y = _f64(y)
+    b = _f64(b)
+    g = _f64(g)
+    if b.ndim == 1:
+        b = b[:, None]
+    if g.ndim == 1:
+        g = g[:, None]
+    M, N, D = x.shape[0], y.shape[0], y.shape[1]
+    grad = np.zeros((N, D))
+    n = np.zeros((N, D))
+    sigma2 = float(sigma) * float(sigma)
+
+    def block(sl):  # a block of columns j
+        k = np.exp(-squared_distances(y[sl], x) / (2.0 * sigma2))   # (cols, M)
+        w = k * (b[sl] @ g.T)
+        for d in range(D):
+            diff = x[:, d][None, :] - y[sl, d][:, None]
+            term = w * diff
+            grad[sl, d] = term.sum(axis=1) / sigma2
+            n[sl, d] = np.abs(term).sum(axis=1) / sigma2
+
+    if M > 0:
+        _parallel_rows(block, N, M, workers)
+    return grad, n
+
+
+def gauss_sum_grad_b(x, y, g, sigma: float, workers: Optional[int] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """Gradient of the Gauss sum with respect to the weights b, contracted with g.
+
+    s_ic = sum_j k_ij b_jc is linear in b, so grad_b[j, c] = sum_i k_ij g_ic: the Gauss sum
+    with the roles of rows and columns exchanged. Returns (grad_b (N, C), n = sum_i |k_ij g_ic|).
+    """
+    x = _f64(x)
+    y = _f64(y)
+    g = _f64(g)
+    if g.ndim == 1:
+        g = g[:, None]
+    M, N, C = x.shape[0], y.shape[0], g.shape[1]
+    grad = np.zeros((N, C))
+    n = np.zeros((N, C))
+    two_sigma2 = 2.0 * float(sigma) * float(sigma)
+    absg = np.abs(g)
+
+    def block(sl):
+        k = np.exp(-squared_distances(y[sl], x) / two_sigma2)         # (cols, M)
+        grad[sl] = k @ g
+        n[sl] = k @ absg
+
+    if M > 0:
+        _parallel_rows(block, N, M, workers)
+    return grad, n
+
+
 def default_workers() -> int:
     """Host threads the oracle uses when asked to run in parallel."""
     return max(1, os.cpu_count() or 1)

@@ -111,6 +111,11 @@ def make_inputs(key: str, M: Optional[int] = None, N: Optional[int] = None,
     return out
 
 
+def upstream_gradient(M: int, C: int, seed: int = 2) -> np.ndarray:
+    """A seeded upstream gradient g = dL/ds of shape (M, C), float32 ~ N(0,1)."""
+    return np.random.default_rng(seed).standard_normal((M, C)).astype(np.float32)
+
+
 def sample_rows(M: int, count: int, seed: int = 1, edge: int = 64) -> np.ndarray:
     """Sorted row indices for sampled checks: ``count`` seeded rows plus the first and
     last ``edge`` rows (so the tail of the last tile is always covered)."""

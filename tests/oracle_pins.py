@@ -428,6 +428,55 @@ def check_grad_limits(o):
     assert np.allclose(g1, g2, rtol=1e-9, atol=1e-12)
 
 
+def check_grad_yb_vs_autograd(o):
+    """torch.autograd of sum_i (a_i . w_i) for a fixed w on the dense float64 formula gives
+    the gradients with respect to y and b for the upstream gradient g = w."""
+    import torch
+    rng = _rng(18)
+    for (M, N, D, C, sigma) in ((13, 9, 3, 1, 0.35), (6, 11, 2, 3, 0.9)):
+        x = rng.random((M, D)).astype(np.float32)
+        y = rng.random((N, D)).astype(np.float32)
+        b = rng.standard_normal((N, C)).astype(np.float32)
+        w = rng.standard_normal((M, C))
+        xt = torch.from_numpy(x.astype(np.float64))
+        yt = torch.tensor(y.astype(np.float64), requires_grad=True)
+        bt = torch.tensor(b.astype(np.float64), requires_grad=True)
+        Dij = ((xt[:, None, :] - yt[None, :, :]) ** 2).sum(-1)
+        a = torch.exp(-Dij / (2 * sigma * sigma)) @ bt
+        gy, gb = torch.autograd.grad((a * torch.from_numpy(w)).sum(), [yt, bt])
+        got_y, _ = o.gauss_sum_grad_y(x, y, b, w, sigma)
+        got_b, _ = o.gauss_sum_grad_b(x, y, w, sigma)
+        assert np.allclose(got_y, gy.numpy(), rtol=1e-11, atol=1e-12)
+        assert np.allclose(got_b, gb.numpy(), rtol=1e-11, atol=1e-12)
+
+
+def check_grad_y_finite_differences_and_limits(o):
+    """Central differences in y of the forward; sigma -> infinity makes grad_b_j = sum_i g_i;
+    moving every point by the same vector leaves both gradients unchanged."""
+    rng = _rng(19)
+    x = rng.random((7, 3))
+    y = rng.random((5, 3))
+    b = rng.standard_normal((5, 2))
+    g = rng.standard_normal((7, 2))
+    sigma = 0.45
+    got, _ = o.gauss_sum_grad_y(x, y, b, g, sigma)
+    h = 1e-6
+    for j in range(5):
+        for d in range(3):
+            yp = y.copy(); yp[j, d] += h
+            ym = y.copy(); ym[j, d] -= h
+            sp, _ = o.gauss_sum(x, yp, b, sigma)
+            sm, _ = o.gauss_sum(x, ym, b, sigma)
+            fd = float((g * (sp - sm)).sum() / (2 * h))
+            assert abs(fd - got[j, d]) <= 1e-7 * max(1.0, abs(fd))
+    gb, _ = o.gauss_sum_grad_b(x, y, g, 1e30)
+    assert np.allclose(gb, np.broadcast_to(g.sum(axis=0), gb.shape), rtol=0, atol=1e-12)
+    shift = np.array([-2.0, 7.0, 0.5])
+    a1, _ = o.gauss_sum_grad_y(x, y, b, g, sigma)
+    a2, _ = o.gauss_sum_grad_y(x + shift, y + shift, b, g, sigma)
+    assert np.allclose(a1, a2, rtol=1e-9, atol=1e-12)
+
+
 GAUSS_CHECKS = [check_gauss_sigma_infinity, check_gauss_hand_values, check_gauss_coincident_columns,
                 check_gauss_self_term, check_gauss_lattice_integral, check_gauss_vs_sklearn,
                 check_keops_example_convention, check_gauss_permutations]
@@ -437,4 +486,5 @@ LSE_CHECKS = [check_lse_vs_scipy, check_lse_identical_columns, check_lse_far_clo
 ARGK_CHECKS = [check_argkmin_exact_bruteforce, check_argkmin_k1_is_argmin, check_argkmin_vs_kdtree,
                check_keys_exact_flag]
 GRAD_CHECKS = [check_grad_vs_autograd, check_grad_finite_differences, check_grad_limits]
-ALL_CHECKS = GAUSS_CHECKS + BATCHED_CHECKS + LSE_CHECKS + ARGK_CHECKS + GRAD_CHECKS
+GRADYB_CHECKS = [check_grad_yb_vs_autograd, check_grad_y_finite_differences_and_limits]
+ALL_CHECKS = GAUSS_CHECKS + BATCHED_CHECKS + LSE_CHECKS + ARGK_CHECKS + GRAD_CHECKS + GRADYB_CHECKS

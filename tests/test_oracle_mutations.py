@@ -44,6 +44,14 @@ MUTATIONS = [
      "diff = y[:, d][None, :] - x[sl, d][:, None]", pins.GRAD_CHECKS),
     ("grad: missing 1/sigma^2", "grad[sl, d] = -term.sum(axis=1) / sigma2", "grad[sl, d] = -term.sum(axis=1)",
      pins.GRAD_CHECKS),
+    ("grad_y: wrong sign", "grad[sl, d] = term.sum(axis=1) / sigma2", "grad[sl, d] = -term.sum(axis=1) / sigma2",
+     pins.GRADYB_CHECKS),
+    ("grad_y: transposed weights", "w = k * (b[sl] @ g.T)", "w = k * (b[sl] @ g.T).sum(axis=0)",
+     pins.GRADYB_CHECKS),
+    ("grad_b: |g| instead of g", "grad[sl] = k @ g", "grad[sl] = k @ absg", pins.GRADYB_CHECKS),
+    ("grad_b: sigma^2 instead of 2 sigma^2",
+     "two_sigma2 = 2.0 * float(sigma) * float(sigma)\n    absg",
+     "two_sigma2 = float(sigma) * float(sigma)\n    absg", pins.GRADYB_CHECKS),
 ]
 
 

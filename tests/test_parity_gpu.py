@@ -270,3 +270,76 @@ def test_gauss_sum_fp16_workload_sampled():
     rows = workloads.sample_rows(inp["M"], 256, seed=3)
     want, norm = oracle.gauss_sum_batched(inp["x"][:, rows], inp["y"], inp["b"], 1.0, workers=8)
     assert_normalised(got[:, rows], want, norm, TOL_F16, "fp16 workload")
+
+
+# ------------------------------------------------- full-size workloads, sampled rows
+# The device runs the whole workload in the configuration bench.py times; the oracle
+# computes a seeded sample of rows (plus the first and last 64) against every column.
+
+def test_gauss_sum_workload_1m_sampled():
+    import pairwise_reductions_amd as pr
+    inp = workloads.make_inputs("gauss_sum_1m")
+    _announce("gauss_sum_1m", M=inp["M"], N=inp["N"])
+    sig = float(inp["sigma"])
+    got = _host(pr.gauss_sum(_dev(inp["x"]), _dev(inp["y"]), _dev(inp["b"]), sig))
+    rows = workloads.sample_rows(inp["M"], 256, seed=1)
+    want, norm = oracle.gauss_sum(inp["x"][rows], inp["y"], inp["b"], sig, workers=8)
+    assert_normalised(got[rows], want, norm, TOL_F32, "gauss_sum_1m")
+
+
+def test_grad_x_workload_100k_mixture_sampled():
+    import pairwise_reductions_amd as pr
+    inp = workloads.make_inputs("gauss_sum_grad_x_100k_mixture")
+    M, N, C = inp["M"], inp["N"], inp["C"]
+    _announce("gauss_sum_grad_x_100k", M=M, N=N)
+    sig = float(inp["sigma"])
+    g = workloads.upstream_gradient(M, C)
+    xd, yd, bd = _dev(inp["x"]), _dev(inp["y"]), _dev(inp["b"])
+    s = _host(pr.gauss_sum(xd, yd, bd, sig))
+    grad = _host(pr.gauss_sum_grad_x(xd, yd, bd, _dev(g), sig))
+    rows = workloads.sample_rows(M, 512, seed=1)
+    want_s, norm_s = oracle.gauss_sum(inp["x"][rows], inp["y"], inp["b"], sig, workers=8)
+    assert_normalised(s[rows], want_s, norm_s, TOL_F32, "forward 100k")
+    want_g, norm_g = oracle.gauss_sum_grad_x(inp["x"][rows], inp["y"], inp["b"], g[rows], sig, workers=8)
+    assert_normalised(grad[rows], want_g, norm_g, TOL_F32, "grad_x 100k")
+
+
+def test_argkmin_lse_workload_100k_sampled():
+    import pairwise_reductions_amd as pr
+    inp = workloads.make_inputs("argkmin_lse_100k")
+    M, N, K = inp["M"], inp["N"], inp["K"]
+    _announce("argkmin_lse_100k", M=M, N=N, K=K)
+    sig = float(inp["sigma"])
+    xd, yd = _dev(inp["x"]), _dev(inp["y"])
+    idx, dist = pr.argkmin(xd, yd, K, with_dist=True)
+    lse = _host(pr.lse(xd, yd, sig))
+    idx, dist = _host(idx), _host(dist)
+    rows = workloads.sample_rows(M, 1024, seed=1)
+    assert oracle.keys_are_exact(inp["x"], inp["y"])
+    want_idx, want_d2 = oracle.argkmin(inp["x"][rows], inp["y"], K, workers=8)
+    assert np.array_equal(idx[rows].astype(np.int64), want_idx)
+    assert np.allclose(dist[rows], want_d2, rtol=1e-6, atol=0)
+    want_lse = oracle.logsumexp_reduction(inp["x"][rows], inp["y"], sig, workers=8)
+    assert np.all(np.abs(lse[rows] - want_lse) <= lse_bound(want_lse))
+    # properties that hold for every row: sorted keys, distinct in-range indices
+    assert np.all(np.diff(dist, axis=1) >= 0)
+    assert idx.min() >= 0 and idx.max() < N
+    assert np.all(np.sort(idx, axis=1)[:, 1:] != np.sort(idx, axis=1)[:, :-1])
+
+
+def test_all_ops_deterministic():
+    import pairwise_reductions_amd as pr
+    _announce("determinism")
+    rng = np.random.default_rng(9)
+    x = workloads.grid24(rng, (5000, 3))
+    y = workloads.grid24(rng, (70000, 3))
+    b = rng.standard_normal((70000, 2)).astype(np.float32)
+    g = rng.standard_normal((5000, 2)).astype(np.float32)
+    xd, yd, bd, gd = _dev(x), _dev(y), _dev(b), _dev(g)
+    runs = [(_host(pr.lse(xd, yd, 0.05)), _host(pr.argkmin(xd, yd, 7)),
+             _host(pr.gauss_sum_grad_x(xd, yd, bd, gd, 0.05))) for _ in range(2)]
+    for a, c in zip(runs[0], runs[1]):
+        assert np.array_equal(a, c)
+    q, k, v = _highd_inputs(10, 2, 1000, 3000, 32, 32)
+    qd, kd, vd = _dev(q), _dev(k), _dev(v)
+    assert np.array_equal(_host(pr.gauss_sum(qd, kd, vd, 1.0)), _host(pr.gauss_sum(qd, kd, vd, 1.0)))
