@@ -57,7 +57,9 @@ typedef enum {
   KEOPS_OP_GAUSS_SUM = 0,
   KEOPS_OP_LSE = 1,
   KEOPS_OP_ARGKMIN = 2,
-  KEOPS_OP_GAUSS_SUM_GRAD_X = 3
+  KEOPS_OP_GAUSS_SUM_GRAD_X = 3,
+  KEOPS_OP_GAUSS_SUM_GRAD_Y = 4,
+  KEOPS_OP_GAUSS_SUM_GRAD_B = 5
 } keops_op;
 
 /*
@@ -114,6 +116,28 @@ KEOPS_API int keops_gauss_sum_grad_x(const float* x, const float* y, const float
                            float* grad, int64_t M, int64_t N, int32_t D, int32_t C,
                            float sigma, void* workspace, size_t workspace_bytes,
                            hipStream_t stream);
+
+/*
+ * Gradient of the Gauss sum with respect to the columns y ("Kernel matrix reduction",
+ * Variants: each partial derivative is its own reduction), for the upstream gradient g:
+ *   grad_y[j][:] = (1/sigma^2) sum_i k_ij (g_i . b_j) (x_i - y_j)
+ * Shapes: x (M, D), y (N, D), b (N, C), g (M, C), grad_y (N, D), all float32.
+ * Requires 1 <= D <= 8, 1 <= C <= 8. M = 0 writes zeros; N = 0 is a no-op.
+ */
+KEOPS_API int keops_gauss_sum_grad_y(const float* x, const float* y, const float* b, const float* g,
+                                     float* grad_y, int64_t M, int64_t N, int32_t D, int32_t C,
+                                     float sigma, void* workspace, size_t workspace_bytes,
+                                     hipStream_t stream);
+
+/*
+ * Gradient of the Gauss sum with respect to the weights b (the sum is linear in b):
+ *   grad_b[j][c] = sum_i k_ij g[i][c]
+ * Shapes: x (M, D), y (N, D), g (M, C), grad_b (N, C), all float32.
+ * Requires 1 <= D <= 8, 1 <= C <= 8. M = 0 writes zeros; N = 0 is a no-op.
+ */
+KEOPS_API int keops_gauss_sum_grad_b(const float* x, const float* y, const float* g, float* grad_b,
+                                     int64_t M, int64_t N, int32_t D, int32_t C, float sigma,
+                                     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Workspace bytes `op` (a keops_op) needs for these arguments on the current device
  * (unused arguments are ignored). Returns 0 for unsupported or invalid arguments. */

@@ -12,7 +12,8 @@ from typing import Optional, Tuple
 from . import _lib
 from ._lib import KeopsError  # noqa: F401
 
-__all__ = ["gauss_sum", "lse", "argkmin", "gauss_sum_grad_x", "workspace_bytes", "KeopsError", "version"]
+__all__ = ["gauss_sum", "lse", "argkmin", "gauss_sum_grad_x", "gauss_sum_grad_y", "gauss_sum_grad_b",
+           "gauss_sum_autograd", "workspace_bytes", "KeopsError", "version"]
 
 
 def _torch():
@@ -139,3 +140,45 @@ def gauss_sum_grad_x(x, y, b, g, sigma: float, out=None, workspace=None):
                                     _ptr(ws), have, _stream(x.device))
     _lib.check(st, "keops_gauss_sum_grad_x")
     return out
+
+
+def gauss_sum_grad_y(x, y, b, g, sigma: float, out=None, workspace=None):
+    """grad_y[j] = (1/sigma^2) sum_i k_ij (g_i . b_j)(x_i - y_j); all float32, returns (N, D)."""
+    torch = _torch()
+    lib = _lib.load()
+    M, D = _dims(x, 2)
+    N, _ = _dims(y, 2)
+    _, C = _dims(b, 2)
+    _dims(g, 2)
+    if out is None:
+        out = torch.empty((N, D), dtype=torch.float32, device=y.device)
+    nbytes = lib.keops_workspace_bytes(_lib.OP_GAUSS_SUM_GRAD_Y, 1, M, N, D, C, 0, _lib.KEOPS_F32)
+    ws, have = _workspace(nbytes, y.device, workspace)
+    st = lib.keops_gauss_sum_grad_y(_ptr(x), _ptr(y), _ptr(b), _ptr(g), _ptr(out), M, N, D, C, float(sigma),
+                                    _ptr(ws), have, _stream(y.device))
+    _lib.check(st, "keops_gauss_sum_grad_y")
+    return out
+
+
+def gauss_sum_grad_b(x, y, g, sigma: float, out=None, workspace=None):
+    """grad_b[j] = sum_i k_ij g_i; all float32, returns (N, C)."""
+    torch = _torch()
+    lib = _lib.load()
+    M, D = _dims(x, 2)
+    N, _ = _dims(y, 2)
+    _, C = _dims(g, 2)
+    if out is None:
+        out = torch.empty((N, C), dtype=torch.float32, device=y.device)
+    nbytes = lib.keops_workspace_bytes(_lib.OP_GAUSS_SUM_GRAD_B, 1, M, N, D, C, 0, _lib.KEOPS_F32)
+    ws, have = _workspace(nbytes, y.device, workspace)
+    st = lib.keops_gauss_sum_grad_b(_ptr(x), _ptr(y), _ptr(g), _ptr(out), M, N, D, C, float(sigma),
+                                    _ptr(ws), have, _stream(y.device))
+    _lib.check(st, "keops_gauss_sum_grad_b")
+    return out
+
+
+def gauss_sum_autograd(x, y, b, sigma: float):
+    """The float32 Gauss sum as a differentiable PyTorch op: forward and the gradients with
+    respect to x, y and b all run in this library's kernels."""
+    from .autograd import GaussSum
+    return GaussSum.apply(x, y, b, float(sigma))

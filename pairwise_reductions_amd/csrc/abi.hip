@@ -175,6 +175,12 @@ size_t keops_workspace_bytes(int op, int64_t B, int64_t M, int64_t N, int32_t D,
     case KEOPS_OP_GAUSS_SUM_GRAD_X:
       if (D < 1 || D > keops::kMaxLowD || C < 1 || C > keops::kMaxLowC) return 0;
       return lowd_layout(op, M, N, D, C, 0).total;
+    case KEOPS_OP_GAUSS_SUM_GRAD_Y:  // the x-gradient kernel over the transposed pairs
+      if (D < 1 || D > keops::kMaxLowD || C < 1 || C > keops::kMaxLowC) return 0;
+      return lowd_layout(KEOPS_OP_GAUSS_SUM_GRAD_X, N, M, D, C, 0).total;
+    case KEOPS_OP_GAUSS_SUM_GRAD_B:  // the Gauss sum over the transposed pairs
+      if (D < 1 || D > keops::kMaxLowD || C < 1 || C > keops::kMaxLowC) return 0;
+      return lowd_layout(KEOPS_OP_GAUSS_SUM, N, M, D, C, 0).total;
   }
   return 0;
 }
@@ -337,6 +343,82 @@ int keops_gauss_sum_grad_x(const float* x, const float* y, const float* b, const
   float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.part_off);
   KEOPS_HIP(keops::launch_grad_x_lowd(x, y, b, g, grad, part, M, N, D, C, c2f, inv_sigma2, L.plan, stream),
             "grad_x_lowd");
+  return ok();
+}
+
+// d/dy: the x-gradient reduction with the roles of (x, g) and (y, b) exchanged, since
+// -(1/s^2) sum_i k_ij (b_j . g_i)(y_j - x_i) = (1/s^2) sum_i k_ij (g_i . b_j)(x_i - y_j).
+int keops_gauss_sum_grad_y(const float* x, const float* y, const float* b, const float* g, float* grad_y,
+                           int64_t M, int64_t N, int32_t D, int32_t C, float sigma, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+  KEOPS_TRY(check_extent(M, "M"));
+  KEOPS_TRY(check_extent(N, "N"));
+  KEOPS_TRY(check_sigma(sigma));
+  if (D < 1 || D > keops::kMaxLowD || C < 1 || C > keops::kMaxLowC)
+    return fail(KEOPS_ERR_UNSUPPORTED, "grad_y needs 1 <= D <= %d and 1 <= C <= %d (got D=%d C=%d)",
+                keops::kMaxLowD, keops::kMaxLowC, D, C);
+  const Range rx{x, (size_t)(M * D) * 4}, ry{y, (size_t)(N * D) * 4}, rb{b, (size_t)(N * C) * 4};
+  const Range rg{g, (size_t)(M * C) * 4}, ro{grad_y, (size_t)(N * D) * 4};
+  KEOPS_TRY(check_ptr(x, "x", 4, rx.bytes));
+  KEOPS_TRY(check_ptr(y, "y", 4, ry.bytes));
+  KEOPS_TRY(check_ptr(b, "b", 4, rb.bytes));
+  KEOPS_TRY(check_ptr(g, "g", 4, rg.bytes));
+  KEOPS_TRY(check_ptr(grad_y, "grad_y", 4, ro.bytes));
+  if (overlaps(ro, rx) || overlaps(ro, ry) || overlaps(ro, rb) || overlaps(ro, rg))
+    return fail(KEOPS_ERR_INVALID_ARG, "grad_y overlaps an input");
+  if (N == 0) return ok();
+  if (M == 0) {
+    KEOPS_HIP(keops::launch_fill(grad_y, N * D, 0.0f, stream), "fill");
+    return ok();
+  }
+  const LowdLayout L = lowd_layout(KEOPS_OP_GAUSS_SUM_GRAD_X, N, M, D, C, 0);
+  KEOPS_TRY(check_workspace(workspace, workspace_bytes, L.total));
+  const Range rw{workspace, L.total};
+  if (overlaps(rw, ro) || overlaps(rw, rx) || overlaps(rw, ry) || overlaps(rw, rb) || overlaps(rw, rg))
+    return fail(KEOPS_ERR_INVALID_ARG, "workspace overlaps an input or the output");
+  const double s = (double)sigma;
+  const float c2f = (float)c2_of(sigma);
+  const float inv_sigma2 = (float)(1.0 / (s * s));
+  float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.part_off);
+  KEOPS_HIP(keops::launch_grad_x_lowd(y, x, g, b, grad_y, part, N, M, D, C, c2f, inv_sigma2, L.plan, stream),
+            "grad_y_lowd");
+  return ok();
+}
+
+// d/db: s is linear in b, so grad_b[j] = sum_i k_ij g_i, the Gauss sum over transposed pairs.
+int keops_gauss_sum_grad_b(const float* x, const float* y, const float* g, float* grad_b, int64_t M, int64_t N,
+                           int32_t D, int32_t C, float sigma, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+  KEOPS_TRY(check_extent(M, "M"));
+  KEOPS_TRY(check_extent(N, "N"));
+  KEOPS_TRY(check_sigma(sigma));
+  if (D < 1 || D > keops::kMaxLowD || C < 1 || C > keops::kMaxLowC)
+    return fail(KEOPS_ERR_UNSUPPORTED, "grad_b needs 1 <= D <= %d and 1 <= C <= %d (got D=%d C=%d)",
+                keops::kMaxLowD, keops::kMaxLowC, D, C);
+  const Range rx{x, (size_t)(M * D) * 4}, ry{y, (size_t)(N * D) * 4}, rg{g, (size_t)(M * C) * 4};
+  const Range ro{grad_b, (size_t)(N * C) * 4};
+  KEOPS_TRY(check_ptr(x, "x", 4, rx.bytes));
+  KEOPS_TRY(check_ptr(y, "y", 4, ry.bytes));
+  KEOPS_TRY(check_ptr(g, "g", 4, rg.bytes));
+  KEOPS_TRY(check_ptr(grad_b, "grad_b", 4, ro.bytes));
+  if (overlaps(ro, rx) || overlaps(ro, ry) || overlaps(ro, rg)) return fail(KEOPS_ERR_INVALID_ARG, "grad_b overlaps an input");
+  if (N == 0) return ok();
+  if (M == 0) {
+    KEOPS_HIP(keops::launch_fill(grad_b, N * C, 0.0f, stream), "fill");
+    return ok();
+  }
+  const LowdLayout L = lowd_layout(KEOPS_OP_GAUSS_SUM, N, M, D, C, 0);
+  KEOPS_TRY(check_workspace(workspace, workspace_bytes, L.total));
+  const Range rw{workspace, L.total};
+  if (overlaps(rw, ro) || overlaps(rw, rx) || overlaps(rw, ry) || overlaps(rw, rg))
+    return fail(KEOPS_ERR_INVALID_ARG, "workspace overlaps an input or the output");
+  char* ws = static_cast<char*>(workspace);
+  double* cols = reinterpret_cast<double*>(ws + L.cols_off);
+  float* part = reinterpret_cast<float*>(ws + L.part_off);
+  const double c2 = c2_of(sigma);
+  KEOPS_HIP(keops::launch_prep_cols(x, cols, M, D, c2, true, stream), "prep_cols");
+  KEOPS_HIP(keops::launch_gauss_sum_lowd(y, x, cols, g, grad_b, part, N, M, D, C, c2, L.plan, stream),
+            "grad_b_lowd");
   return ok();
 }
 

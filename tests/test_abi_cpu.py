@@ -30,6 +30,7 @@ def _err(lib):
 def test_exports_every_declared_symbol(lib):
     names = _lib.header_symbols()
     assert set(names) == {"keops_gauss_sum", "keops_lse", "keops_argkmin", "keops_gauss_sum_grad_x",
+                          "keops_gauss_sum_grad_y", "keops_gauss_sum_grad_b",
                           "keops_workspace_bytes", "keops_status_string", "keops_last_error", "keops_version"}
     for name in names:
         assert hasattr(lib, name), name
@@ -141,3 +142,17 @@ def test_error_is_thread_local(lib):
     t.join()
     assert seen == [""]
     assert "D=9" in _err(lib)
+
+
+def test_grad_yb_reject(lib):
+    fy, fb = lib.keops_gauss_sum_grad_y, lib.keops_gauss_sum_grad_b
+    assert fy(X, Y, B, None, OUT, 10, 10, 3, 1, 0.1, WS, 1 << 30, None) == INVALID
+    assert fy(X, Y, B, G, OUT, 10, 10, 9, 1, 0.1, WS, 1 << 30, None) == UNSUPPORTED
+    assert fy(X, Y, B, G, Y, 10, 10, 3, 1, 0.1, WS, 1 << 30, None) == INVALID   # grad_y aliases y
+    assert fy(X, Y, B, G, OUT, 10, 0, 3, 1, 0.1, None, 0, None) == 0             # N = 0: no-op
+    assert fb(X, Y, None, OUT, 10, 10, 3, 1, 0.1, WS, 1 << 30, None) == INVALID
+    assert fb(X, Y, G, OUT, 10, 10, 3, 1, -1.0, WS, 1 << 30, None) == INVALID
+    assert fb(X, Y, G, OUT, 10, 10, 3, 0, 0.1, WS, 1 << 30, None) == UNSUPPORTED
+    assert fb(X, Y, G, OUT, 10, 0, 3, 1, 0.1, None, 0, None) == 0
+    ws = lib.keops_workspace_bytes
+    assert ws(4, 1, 100_000, 100, 3, 1, 0, F32) > 0 and ws(5, 1, 100_000, 100, 3, 2, 0, F32) > 0

@@ -343,3 +343,49 @@ def test_all_ops_deterministic():
     q, k, v = _highd_inputs(10, 2, 1000, 3000, 32, 32)
     qd, kd, vd = _dev(q), _dev(k), _dev(v)
     assert np.array_equal(_host(pr.gauss_sum(qd, kd, vd, 1.0)), _host(pr.gauss_sum(qd, kd, vd, 1.0)))
+
+
+# ------------------------------------------------ gradients with respect to y and b
+GRADYB_SHAPES = [(1, 1, 3, 1, 0.1), (1000, 257, 3, 1, 0.1), (513, 1025, 1, 2, 0.05), (2000, 700, 2, 3, 0.2),
+                 (1500, 513, 8, 8, 0.5), (100_003, 100, 3, 2, 0.05), (777, 20_001, 3, 1, 0.1)]
+
+
+@pytest.mark.parametrize("M,N,D,C,sigma", GRADYB_SHAPES)
+def test_grad_y_and_b_shapes(M, N, D, C, sigma):
+    import pairwise_reductions_amd as pr
+    _announce("grad_y_b", M=M, N=N, D=D, C=C, sigma=sigma)
+    x, y, b = _rand(M * 11 + N, M, N, D, C)
+    g = np.random.default_rng(N).standard_normal((M, C)).astype(np.float32)
+    sig = float(np.float32(sigma))
+    xd, yd, bd, gd = _dev(x), _dev(y), _dev(b), _dev(g)
+    gy = _host(pr.gauss_sum_grad_y(xd, yd, bd, gd, sig))
+    gb = _host(pr.gauss_sum_grad_b(xd, yd, gd, sig))
+    want_y, norm_y = oracle.gauss_sum_grad_y(x, y, b, g, sig, workers=8)
+    want_b, norm_b = oracle.gauss_sum_grad_b(x, y, g, sig, workers=8)
+    assert_normalised(gy, want_y, norm_y, TOL_F32, "grad_y")
+    assert_normalised(gb, want_b, norm_b, TOL_F32, "grad_b")
+
+
+def test_autograd_function_all_gradients():
+    """loss = sum_i s_i . w_i through the autograd wrapper: forward and the three gradients
+    against the oracle with the upstream gradient g = w."""
+    import torch
+    import pairwise_reductions_amd as pr
+    _announce("autograd")
+    inp = workloads.make_inputs("gauss_sum_grad_x_100k_mixture", M=3000, N=5000)
+    sig = float(inp["sigma"])
+    w = workloads.upstream_gradient(3000, 1, seed=5)
+    x = _dev(inp["x"]).requires_grad_(True)
+    y = _dev(inp["y"]).requires_grad_(True)
+    b = _dev(inp["b"]).requires_grad_(True)
+    s = pr.gauss_sum_autograd(x, y, b, sig)
+    (s * _dev(w)).sum().backward()
+    torch.cuda.synchronize()
+    want_s, norm_s = oracle.gauss_sum(inp["x"], inp["y"], inp["b"], sig, workers=8)
+    assert_normalised(s.detach().cpu().numpy(), want_s, norm_s, TOL_F32, "autograd forward")
+    gx, nx = oracle.gauss_sum_grad_x(inp["x"], inp["y"], inp["b"], w, sig, workers=8)
+    gy, ny = oracle.gauss_sum_grad_y(inp["x"], inp["y"], inp["b"], w, sig, workers=8)
+    gb, nb = oracle.gauss_sum_grad_b(inp["x"], inp["y"], w, sig, workers=8)
+    assert_normalised(x.grad.cpu().numpy(), gx, nx, TOL_F32, "autograd x")
+    assert_normalised(y.grad.cpu().numpy(), gy, ny, TOL_F32, "autograd y")
+    assert_normalised(b.grad.cpu().numpy(), gb, nb, TOL_F32, "autograd b")
