@@ -59,7 +59,8 @@ typedef enum {
   KEOPS_OP_ARGKMIN = 2,
   KEOPS_OP_GAUSS_SUM_GRAD_X = 3,
   KEOPS_OP_GAUSS_SUM_GRAD_Y = 4,
-  KEOPS_OP_GAUSS_SUM_GRAD_B = 5
+  KEOPS_OP_GAUSS_SUM_GRAD_B = 5,
+  KEOPS_OP_ARGKMIN_LSE = 6
 } keops_op;
 
 /*
@@ -103,6 +104,19 @@ KEOPS_API int keops_lse(const float* x, const float* y, float* out, int64_t M, i
 KEOPS_API int keops_argkmin(const float* x, const float* y, int32_t* idx, float* dist, int64_t M,
                   int64_t N, int32_t D, int32_t K, void* workspace, size_t workspace_bytes,
                   hipStream_t stream);
+
+/*
+ * argKmin and the log-sum-exp reduction of the same pairs in one sweep ("Kernel matrix
+ * reduction", Overview: minima, indices of the K smallest entries and log-sum-exp are all
+ * reductions of one pairwise formula):
+ *   idx, dist as keops_argkmin;  lse[i] = log sum_j exp(-||x_i - y_j||^2 / (2 sigma^2))
+ * Shapes: x (M, D), y (N, D) float32; idx (M, K) int32; dist (M, K) float32 or NULL;
+ * lse (M,) float32 (must not be NULL). Same limits as keops_argkmin, plus sigma as in
+ * keops_lse. The running row shift of the log-sum-exp is the smallest key found so far.
+ */
+KEOPS_API int keops_argkmin_lse(const float* x, const float* y, int32_t* idx, float* dist, float* lse,
+                                int64_t M, int64_t N, int32_t D, int32_t K, float sigma,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Gradient of the Gauss sum with respect to x ("Kernel matrix reduction", Variants:

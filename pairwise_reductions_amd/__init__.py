@@ -12,7 +12,7 @@ from typing import Optional, Tuple
 from . import _lib
 from ._lib import KeopsError  # noqa: F401
 
-__all__ = ["gauss_sum", "lse", "argkmin", "gauss_sum_grad_x", "gauss_sum_grad_y", "gauss_sum_grad_b",
+__all__ = ["gauss_sum", "lse", "argkmin", "argkmin_lse", "gauss_sum_grad_x", "gauss_sum_grad_y", "gauss_sum_grad_b",
            "gauss_sum_autograd", "workspace_bytes", "KeopsError", "version"]
 
 
@@ -122,6 +122,27 @@ def argkmin(x, y, K: int, with_dist: bool = False, idx=None, dist=None, workspac
                            _stream(x.device))
     _lib.check(st, "keops_argkmin")
     return (idx, dist) if with_dist else idx
+
+
+def argkmin_lse(x, y, K: int, sigma: float, with_dist: bool = False, idx=None, dist=None, lse_out=None,
+                workspace=None):
+    """argKmin and the log-sum-exp reduction in one sweep; returns (idx, lse) or (idx, dist, lse)."""
+    torch = _torch()
+    lib = _lib.load()
+    M, D = _dims(x, 2)
+    N, _ = _dims(y, 2)
+    if idx is None:
+        idx = torch.empty((M, K), dtype=torch.int32, device=x.device)
+    if with_dist and dist is None:
+        dist = torch.empty((M, K), dtype=torch.float32, device=x.device)
+    if lse_out is None:
+        lse_out = torch.empty((M,), dtype=torch.float32, device=x.device)
+    nbytes = lib.keops_workspace_bytes(_lib.OP_ARGKMIN_LSE, 1, M, N, D, 1, K, _lib.KEOPS_F32)
+    ws, have = _workspace(nbytes, x.device, workspace)
+    st = lib.keops_argkmin_lse(_ptr(x), _ptr(y), _ptr(idx), _ptr(dist), _ptr(lse_out), M, N, D, int(K), float(sigma),
+                               _ptr(ws), have, _stream(x.device))
+    _lib.check(st, "keops_argkmin_lse")
+    return (idx, dist, lse_out) if with_dist else (idx, lse_out)
 
 
 def gauss_sum_grad_x(x, y, b, g, sigma: float, out=None, workspace=None):

@@ -78,8 +78,10 @@ double c2_of(float sigma) {
 // ---- workspace layouts ------------------------------------------------------------------
 struct LowdLayout {
   keops::Plan plan;
-  size_t cols_off, cols_bytes;
-  size_t part_off, part_bytes;
+  size_t cols_off, cols_bytes;  // column table
+  size_t aux_off;               // one double: the largest column norm (argKmin screening)
+  size_t part_off, part_bytes;  // per-split partials (argKmin lists for ops 2 and 6)
+  size_t lse_off;               // per-split (m, l) pairs of the fused argKmin + LSE (op 6)
   size_t total;
 };
 
@@ -87,13 +89,26 @@ LowdLayout lowd_layout(int op, int64_t M, int64_t N, int D, int C, int K) {
   LowdLayout L;
   L.plan = keops::plan_lowd(op, M, N, D, C, K, keops::device_cus());
   const bool needs_cols = (op != KEOPS_OP_GAUSS_SUM_GRAD_X);
+  const bool knn = (op == KEOPS_OP_ARGKMIN || op == KEOPS_OP_ARGKMIN_LSE);
+  const size_t S = (size_t)L.plan.splits, Mz = (size_t)M;
   L.cols_off = 0;
   L.cols_bytes = needs_cols ? keops::align_up((size_t)N * keops::col_stride(D) * sizeof(double)) : 0;
-  L.part_off = L.cols_bytes;
-  L.part_bytes = L.plan.splits > 1
-                     ? keops::align_up((size_t)L.plan.splits * (size_t)M * keops::partial_bytes_per_row(op, D, C, K))
-                     : 0;
-  L.total = L.cols_bytes + L.part_bytes;
+  L.aux_off = L.cols_bytes;
+  const size_t aux_bytes = knn ? keops::kAlign : 0;
+  L.part_off = L.aux_off + aux_bytes;
+  size_t lse_bytes = 0;
+  if (S > 1) {
+    if (knn) {
+      L.part_bytes = keops::align_up(S * Mz * keops::partial_bytes_per_row(KEOPS_OP_ARGKMIN, D, C, K));
+      if (op == KEOPS_OP_ARGKMIN_LSE) lse_bytes = keops::align_up(S * Mz * keops::partial_bytes_per_row(KEOPS_OP_LSE, D, C, K));
+    } else {
+      L.part_bytes = keops::align_up(S * Mz * keops::partial_bytes_per_row(op, D, C, K));
+    }
+  } else {
+    L.part_bytes = 0;
+  }
+  L.lse_off = L.part_off + L.part_bytes;
+  L.total = L.lse_off + lse_bytes;
   if (M == 0 || N == 0) L.total = 0;
   return L;
 }
@@ -170,6 +185,7 @@ size_t keops_workspace_bytes(int op, int64_t B, int64_t M, int64_t N, int32_t D,
       if (D < 1 || D > keops::kMaxLowD) return 0;
       return lowd_layout(op, M, N, D, 1, 0).total;
     case KEOPS_OP_ARGKMIN:
+    case KEOPS_OP_ARGKMIN_LSE:
       if (D < 1 || D > keops::kMaxLowD || K < 1 || K > keops::kMaxK || K > N) return 0;
       return lowd_layout(op, M, N, D, 1, K).total;
     case KEOPS_OP_GAUSS_SUM_GRAD_X:
@@ -279,34 +295,60 @@ int keops_lse(const float* x, const float* y, float* out, int64_t M, int64_t N, 
   return ok();
 }
 
-int keops_argkmin(const float* x, const float* y, int32_t* idx, float* dist, int64_t M, int64_t N, int32_t D,
-                  int32_t K, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+namespace {
+
+// Shared by keops_argkmin and keops_argkmin_lse (lse == NULL for the former).
+int argkmin_impl(const float* x, const float* y, int32_t* idx, float* dist, float* lse, int64_t M, int64_t N,
+                 int32_t D, int32_t K, float sigma, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const bool with_lse = (lse != nullptr);
   KEOPS_TRY(check_extent(M, "M"));
   KEOPS_TRY(check_extent(N, "N"));
+  if (with_lse) KEOPS_TRY(check_sigma(sigma));
   if (D < 1 || D > keops::kMaxLowD)
     return fail(KEOPS_ERR_UNSUPPORTED, "argkmin needs 1 <= D <= %d (got %d)", keops::kMaxLowD, D);
   if (K < 1 || K > N) return fail(KEOPS_ERR_INVALID_ARG, "argkmin needs 1 <= K <= N (got K=%d N=%lld)", K, (long long)N);
   if (K > keops::kMaxK) return fail(KEOPS_ERR_UNSUPPORTED, "argkmin supports K <= %d (got %d)", keops::kMaxK, K);
   const Range rx{x, (size_t)(M * D) * 4}, ry{y, (size_t)(N * D) * 4};
   const Range ri{idx, (size_t)(M * K) * 4}, rd{dist, dist ? (size_t)(M * K) * 4 : 0};
+  const Range rl{lse, with_lse ? (size_t)M * 4 : 0};
   KEOPS_TRY(check_ptr(x, "x", 4, rx.bytes));
   KEOPS_TRY(check_ptr(y, "y", 4, ry.bytes));
   KEOPS_TRY(check_ptr(idx, "idx", 4, ri.bytes));
   if (dist && !aligned(dist, 4)) return fail(KEOPS_ERR_INVALID_ARG, "dist must be 4-byte aligned");
-  if (overlaps(ri, rx) || overlaps(ri, ry) || overlaps(rd, rx) || overlaps(rd, ry) || overlaps(ri, rd))
-    return fail(KEOPS_ERR_INVALID_ARG, "idx/dist overlap an input or each other");
+  if (with_lse && !aligned(lse, 4)) return fail(KEOPS_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+  if (overlaps(ri, rx) || overlaps(ri, ry) || overlaps(rd, rx) || overlaps(rd, ry) || overlaps(ri, rd) ||
+      overlaps(rl, rx) || overlaps(rl, ry) || overlaps(rl, ri) || overlaps(rl, rd))
+    return fail(KEOPS_ERR_INVALID_ARG, "idx/dist/lse overlap an input or each other");
   if (M == 0) return ok();
-  const LowdLayout L = lowd_layout(KEOPS_OP_ARGKMIN, M, N, D, 1, K);
+  const int op = with_lse ? KEOPS_OP_ARGKMIN_LSE : KEOPS_OP_ARGKMIN;
+  const LowdLayout L = lowd_layout(op, M, N, D, 1, K);
   KEOPS_TRY(check_workspace(workspace, workspace_bytes, L.total));
   const Range rw{workspace, L.total};
-  if (overlaps(rw, ri) || overlaps(rw, rd) || overlaps(rw, rx) || overlaps(rw, ry))
+  if (overlaps(rw, ri) || overlaps(rw, rd) || overlaps(rw, rl) || overlaps(rw, rx) || overlaps(rw, ry))
     return fail(KEOPS_ERR_INVALID_ARG, "workspace overlaps an input or an output");
   char* ws = static_cast<char*>(workspace);
   double* cols = reinterpret_cast<double*>(ws + L.cols_off);
-  KEOPS_HIP(keops::launch_prep_cols(y, cols, N, D, 0.0, false, stream), "prep_cols");
-  KEOPS_HIP(keops::launch_argkmin_lowd(x, y, cols, idx, dist, ws + L.part_off, M, N, D, K, L.plan, stream),
+  double* ymax = reinterpret_cast<double*>(ws + L.aux_off);
+  double* lse_part = reinterpret_cast<double*>(ws + L.lse_off);
+  const double c2 = with_lse ? c2_of(sigma) : 0.0;
+  KEOPS_HIP(keops::launch_knn_lowd(x, y, cols, ymax, idx, dist, ws + L.part_off, lse, lse_part, M, N, D, K, c2,
+                                   with_lse, L.plan, stream),
             "argkmin_lowd");
   return ok();
+}
+
+}  // namespace
+
+int keops_argkmin(const float* x, const float* y, int32_t* idx, float* dist, int64_t M, int64_t N, int32_t D,
+                  int32_t K, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return argkmin_impl(x, y, idx, dist, nullptr, M, N, D, K, 1.0f, workspace, workspace_bytes, stream);
+}
+
+int keops_argkmin_lse(const float* x, const float* y, int32_t* idx, float* dist, float* lse, int64_t M, int64_t N,
+                      int32_t D, int32_t K, float sigma, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
+  if (!lse && M > 0) return fail(KEOPS_ERR_INVALID_ARG, "lse must not be NULL");
+  return argkmin_impl(x, y, idx, dist, lse, M, N, D, K, sigma, workspace, workspace_bytes, stream);
 }
 
 int keops_gauss_sum_grad_x(const float* x, const float* y, const float* b, const float* g, float* grad,

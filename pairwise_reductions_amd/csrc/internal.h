@@ -31,7 +31,7 @@ struct Plan {
 Plan plan_lowd(int op, int64_t M, int64_t N, int D, int C, int K, int num_cus);
 int device_cus();
 
-// Per-op partial-result bytes per (split, row).
+// Per-op partial-result bytes per (split, row). Ops follow keops_op; 6 is argKmin + LSE.
 size_t partial_bytes_per_row(int op, int D, int C, int K);
 
 // ---- launchers (return hipError_t of the launch) ----------------------------------------
@@ -45,9 +45,12 @@ hipError_t launch_gauss_sum_lowd(const float* x, const float* y, const double* c
 hipError_t launch_lse_lowd(const float* x, const float* y, const double* cols, float* out,
                            double* partial, int64_t M, int64_t N, int D, double c2,
                            const Plan& p, hipStream_t s);
-hipError_t launch_argkmin_lowd(const float* x, const float* y, const double* cols,
-                               int32_t* idx, float* dist, void* partial, int64_t M, int64_t N,
-                               int D, int K, const Plan& p, hipStream_t s);
+// argKmin, optionally fused with the log-sum-exp reduction (with_lse): builds the uncentred
+// column table in `cols` and the largest column norm in *ymax, then screens every pair.
+hipError_t launch_knn_lowd(const float* x, const float* y, double* cols, double* ymax, int32_t* idx,
+                           float* dist, void* partial, float* lse_out, double* lse_partial, int64_t M,
+                           int64_t N, int D, int K, double c2, bool with_lse, const Plan& p,
+                           hipStream_t s);
 hipError_t launch_grad_x_lowd(const float* x, const float* y, const float* b, const float* g,
                               float* grad, float* partial, int64_t M, int64_t N, int D, int C,
                               float c2f, float inv_sigma2, const Plan& p, hipStream_t s);

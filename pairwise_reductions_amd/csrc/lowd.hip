@@ -302,44 +302,141 @@ __device__ __forceinline__ double sq_dist_key(const double (&xu)[D], const doubl
   return key;
 }
 
-template <int D, int K, int R>
+// Largest squared norm in the column table (cols[j][D] holds |y_j|^2), one workgroup, fixed
+// reduction order.
+__global__ void __launch_bounds__(1024)
+max_norm_kernel(const double* __restrict__ cols, int64_t N, int P, int D, double* __restrict__ out) {
+  __shared__ double red[1024];
+  double m = 0.0;
+  for (int64_t j = threadIdx.x; j < N; j += 1024) m = fmax(m, cols[j * P + D]);
+  red[threadIdx.x] = m;
+  __syncthreads();
+  for (int w = 512; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] = fmax(red[threadIdx.x], red[threadIdx.x + w]);
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *out = red[0];
+}
+
+// Screening bound: the float64 expansion a = |x|^2 + |y|^2 - 2 x.y (D+1 FMAs after the two
+// norms, each rounded once) differs from the exact squared distance by at most
+// (4D + 8) 2^-53 (|x|^2 + |y|^2) <= 2^-46 (|x|^2 + max_j |y_j|^2) for D <= 8.
+constexpr double kScreenMargin = 1.4210854715202004e-14;  // 2^-46
+
+// argKmin (and, with LSE, the log-sum-exp of -c2 d^2 in base 2) over the columns of one split.
+// Each pair first gets the cheap expansion a_ij; only when a_ij is below the row's K-th key
+// plus the margin is the exact key computed and the sorted list updated, which after the
+// first columns is rare. For the log-sum-exp the row's running shift is -c2 times its
+// smallest key so far, raised lazily (only when it grows by more than kLseSlack), so every
+// term 2^(-c2 a_ij - m) stays below 2^kLseSlack; it is updated before a tile's terms are added.
+template <int D, int K, int R, bool LSE>
 __global__ void __launch_bounds__(kBlock)
-argkmin_kernel(const float* __restrict__ x, const double* __restrict__ cols,
-               int32_t* __restrict__ idx, float* __restrict__ dist, KeyIdx* __restrict__ partial,
-               int64_t M, int64_t N, int64_t cps, int Kout) {
+knn_kernel(const float* __restrict__ x, const double* __restrict__ cols, const double* __restrict__ ymax,
+           int32_t* __restrict__ idx, float* __restrict__ dist, KeyIdx* __restrict__ partial,
+           float* __restrict__ lse_out, LsePartial* __restrict__ lse_partial, int64_t M, int64_t N,
+           int64_t cps, int Kout, double c2) {
   constexpr int P = (D + 2) & ~1;
+  constexpr int U = D <= 4 ? 4 : 2;  // columns per screened tile
   const int64_t split = blockIdx.y;
   const int64_t j0 = split * cps;
   const int64_t j1 = (j0 + cps < N) ? j0 + cps : N;
   const int64_t row0 = (int64_t)blockIdx.x * (kBlock * R) + threadIdx.x;
+  const double bmax = *ymax;
 
-  double xu[R][D];
+  double xd[R][D], xp[R][D], A[R], marg[R], thr[R];
   double keys[R][K];
   int32_t ids[R][K];
+  double mref[R];
+  float l[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     int64_t i = row0 + (int64_t)r * kBlock;
     i = i < M ? i : M - 1;
+    double s = 0.0;
 #pragma unroll
-    for (int d = 0; d < D; ++d) xu[r][d] = (double)x[i * D + d];
+    for (int d = 0; d < D; ++d) {
+      xd[r][d] = (double)x[i * D + d];
+      xp[r][d] = -2.0 * xd[r][d];
+      s = fma(xd[r][d], xd[r][d], s);
+    }
+    A[r] = s;
+    marg[r] = kScreenMargin * (s + bmax);
+    thr[r] = INFINITY;
 #pragma unroll
     for (int k = 0; k < K; ++k) {
       keys[r][k] = INFINITY;
       ids[r][k] = -1;
     }
+    mref[r] = -INFINITY;
+    l[r] = 0.0f;
   }
 
-#pragma unroll 2
-  for (int64_t j = j0; j < j1; ++j) {
-    const double* cj = cols + j * P;
-    double v[D];
+  // Columns [j, j + n) of a tile, n <= U, for row r: screen, update the list, add LSE terms.
+  auto tile = [&](int r, int64_t j, int n, const double (&yv)[U][D], const double (&bv)[U]) {
+    double a[U];
+    double mn = INFINITY;
 #pragma unroll
-    for (int d = 0; d < D; ++d) v[d] = cj[d];
+    for (int u = 0; u < U; ++u) {
+      if (u < n) {
+        double t = A[r] + bv[u];
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const double key = sq_dist_key<D>(xu[r], v);
-      if (key < keys[r][K - 1]) topk_insert<K>(keys[r], ids[r], key, (int32_t)j);
+        for (int d = 0; d < D; ++d) t = fma(xp[r][d], yv[u][d], t);
+        a[u] = t;
+        mn = fmin(mn, t);
+      }
     }
+    if (mn < thr[r]) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (u < n && a[u] < thr[r]) {
+          const double key = sq_dist_key<D>(xd[r], yv[u]);
+          if (key < keys[r][K - 1]) {
+            topk_insert<K>(keys[r], ids[r], key, (int32_t)(j + u));
+            thr[r] = keys[r][K - 1] + marg[r];
+            if constexpr (LSE) {
+              const double nm = -c2 * keys[r][0];
+              if (nm > mref[r] + (double)kLseSlack) {
+                l[r] *= exp2_hw((float)(mref[r] - nm));
+                mref[r] = nm;
+              }
+            }
+          }
+        }
+      }
+    }
+    if constexpr (LSE) {
+      float t = 0.0f;
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (u < n) t += exp2_hw((float)fma(a[u], -c2, -mref[r]));
+      l[r] += t;
+    }
+  };
+
+  int64_t j = j0;
+  for (; j + U <= j1; j += U) {
+    double yv[U][D], bv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+      for (int d = 0; d < D; ++d) yv[u][d] = cols[(j + u) * P + d];
+      bv[u] = cols[(j + u) * P + D];
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) tile(r, j, U, yv, bv);
+  }
+  if (j < j1) {
+    const int n = (int)(j1 - j);
+    double yv[U][D], bv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t jj = (u < n) ? j + u : j;
+#pragma unroll
+      for (int d = 0; d < D; ++d) yv[u][d] = cols[jj * P + d];
+      bv[u] = cols[jj * P + D];
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) tile(r, j, n, yv, bv);
   }
 
 #pragma unroll
@@ -354,6 +451,7 @@ argkmin_kernel(const float* __restrict__ x, const double* __restrict__ cols,
           if (dist) dist[i * Kout + k] = (float)keys[r][k];
         }
       }
+      if constexpr (LSE) lse_out[i] = (float)((mref[r] + (double)log2f(l[r])) * M_LN2);
     } else {
 #pragma unroll
       for (int k = 0; k < K; ++k) {
@@ -362,6 +460,13 @@ argkmin_kernel(const float* __restrict__ x, const double* __restrict__ cols,
         p.idx = ids[r][k];
         p.pad = 0;
         partial[(split * M + i) * K + k] = p;
+      }
+      if constexpr (LSE) {
+        LsePartial p;
+        p.m = mref[r];
+        p.l = l[r];
+        p.pad = 0.0f;
+        lse_partial[split * M + i] = p;
       }
     }
   }
@@ -559,32 +664,41 @@ hipError_t lse_d(const float* x, const float* y, const double* cols, float* out,
   return hipGetLastError();
 }
 
-template <int D, int K>
-hipError_t argk_dk(const float* x, const double* cols, int32_t* idx, float* dist, void* partial,
-                   int64_t M, int64_t N, int Kout, const Plan& p, hipStream_t s) {
+template <int D, int K, bool LSE>
+hipError_t knn_dk(const float* x, const double* cols, const double* ymax, int32_t* idx, float* dist,
+                  void* partial, float* lse_out, double* lse_partial, int64_t M, int64_t N, int Kout, double c2,
+                  const Plan& p, hipStream_t s) {
   dim3 grid((unsigned)p.row_blocks, (unsigned)p.splits);
-  argkmin_kernel<D, K, (K <= 16 ? 2 : 1)><<<grid, kBlock, 0, s>>>(
-      x, cols, idx, dist, reinterpret_cast<KeyIdx*>(partial), M, N, p.cols_per_split, Kout);
+  knn_kernel<D, K, (K <= 16 ? 2 : 1), LSE><<<grid, kBlock, 0, s>>>(
+      x, cols, ymax, idx, dist, reinterpret_cast<KeyIdx*>(partial), lse_out,
+      reinterpret_cast<LsePartial*>(lse_partial), M, N, p.cols_per_split, Kout, c2);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
   merge_topk_kernel<K><<<(unsigned)ceil_div(M, kBlock), kBlock, 0, s>>>(
       reinterpret_cast<const KeyIdx*>(partial), idx, dist, M, p.splits, Kout);
+  e = hipGetLastError();
+  if (e != hipSuccess || !LSE) return e;
+  combine_lse_kernel<<<(unsigned)ceil_div(M, kBlock), kBlock, 0, s>>>(
+      reinterpret_cast<const LsePartial*>(lse_partial), lse_out, M, p.splits);
   return hipGetLastError();
 }
 
-template <int D>
-hipError_t argk_d(int Kb, const float* x, const double* cols, int32_t* idx, float* dist, void* partial,
-                  int64_t M, int64_t N, int Kout, const Plan& p, hipStream_t s) {
+template <int D, bool LSE>
+hipError_t knn_d(int Kb, const float* x, const double* cols, const double* ymax, int32_t* idx, float* dist,
+                 void* partial, float* lse_out, double* lse_partial, int64_t M, int64_t N, int Kout, double c2,
+                 const Plan& p, hipStream_t s) {
+#define KEOPS_KNN_K(Kv) return knn_dk<D, Kv, LSE>(x, cols, ymax, idx, dist, partial, lse_out, lse_partial, M, N, Kout, c2, p, s)
   switch (Kb) {
-    case 1: return argk_dk<D, 1>(x, cols, idx, dist, partial, M, N, Kout, p, s);
-    case 2: return argk_dk<D, 2>(x, cols, idx, dist, partial, M, N, Kout, p, s);
-    case 4: return argk_dk<D, 4>(x, cols, idx, dist, partial, M, N, Kout, p, s);
-    case 8: return argk_dk<D, 8>(x, cols, idx, dist, partial, M, N, Kout, p, s);
-    case 10: return argk_dk<D, 10>(x, cols, idx, dist, partial, M, N, Kout, p, s);
-    case 16: return argk_dk<D, 16>(x, cols, idx, dist, partial, M, N, Kout, p, s);
-    case 32: return argk_dk<D, 32>(x, cols, idx, dist, partial, M, N, Kout, p, s);
-    case 64: return argk_dk<D, 64>(x, cols, idx, dist, partial, M, N, Kout, p, s);
+    case 1: KEOPS_KNN_K(1);
+    case 2: KEOPS_KNN_K(2);
+    case 4: KEOPS_KNN_K(4);
+    case 8: KEOPS_KNN_K(8);
+    case 10: KEOPS_KNN_K(10);
+    case 16: KEOPS_KNN_K(16);
+    case 32: KEOPS_KNN_K(32);
+    case 64: KEOPS_KNN_K(64);
   }
+#undef KEOPS_KNN_K
   return hipErrorInvalidValue;
 }
 
@@ -609,6 +723,7 @@ size_t partial_bytes_per_row(int op, int D, int C, int K) {
     case 0: return sizeof(float) * (size_t)C;
     case 1: return sizeof(LsePartial);
     case 2: return sizeof(KeyIdx) * (size_t)argk_bucket(K);
+    case 6: return sizeof(KeyIdx) * (size_t)argk_bucket(K) + sizeof(LsePartial);
     case 3: return sizeof(float) * (size_t)D;
   }
   return 0;
@@ -621,7 +736,8 @@ Plan plan_lowd(int op, int64_t M, int64_t N, int D, int C, int K, int num_cus) {
   switch (op) {
     case 0: p.R = kRowsSum; break;
     case 1: p.R = kRowsLse; break;
-    case 2: p.R = argk_rows(argk_bucket(K)); break;
+    case 2:
+    case 6: p.R = argk_rows(argk_bucket(K)); break;
     default: p.R = kRowsGrad; break;
   }
   p.rows_per_block = kBlock * p.R;
@@ -635,7 +751,7 @@ Plan plan_lowd(int op, int64_t M, int64_t N, int D, int C, int K, int num_cus) {
   if (p.row_blocks > 0 && p.row_blocks < target) S = ceil_div(target, p.row_blocks);
   if (S < ceil_div(N, kSplitCols)) S = ceil_div(N, kSplitCols);
   int64_t max_split = N / 256 > 1 ? N / 256 : 1;
-  if (op == 2 && max_split > 16) max_split = 16;  // argKmin partial lists are K entries per row
+  if ((op == 2 || op == 6) && max_split > 16) max_split = 16;  // argKmin partial lists are K entries per row
   if (S > max_split) S = max_split;
   if (S < 1) S = 1;
   int64_t cps = S > 1 ? ceil_div(N, S) : (N > 0 ? N : 1);
@@ -693,15 +809,25 @@ hipError_t launch_lse_lowd(const float* x, const float* y, const double* cols, f
   return hipGetLastError();
 }
 
-hipError_t launch_argkmin_lowd(const float* x, const float* y, const double* cols, int32_t* idx, float* dist,
-                               void* partial, int64_t M, int64_t N, int D, int K, const Plan& p,
-                               hipStream_t s) {
-  (void)y;
-  (void)N;
+hipError_t launch_knn_lowd(const float* x, const float* y, double* cols, double* ymax, int32_t* idx,
+                           float* dist, void* partial, float* lse_out, double* lse_partial, int64_t M, int64_t N,
+                           int D, int K, double c2, bool with_lse, const Plan& p, hipStream_t s) {
+  // column table (y_j, |y_j|^2) uncentred, then its largest norm for the screening margin
+  hipError_t e = launch_prep_cols(y, cols, N, D, -1.0, false, s);
+  if (e != hipSuccess) return e;
+  max_norm_kernel<<<1, 1024, 0, s>>>(cols, N, col_stride(D), D, ymax);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
   const int Kb = argk_bucket(K);
-#define KEOPS_AK(Dv) argk_d<Dv>(Kb, x, cols, idx, dist, partial, M, N, K, p, s)
-  auto run = [&]() -> hipError_t { KEOPS_SWITCH_D(D, KEOPS_AK) };
-#undef KEOPS_AK
+  if (with_lse) {
+#define KEOPS_KNN(Dv) knn_d<Dv, true>(Kb, x, cols, ymax, idx, dist, partial, lse_out, lse_partial, M, N, K, c2, p, s)
+    auto run = [&]() -> hipError_t { KEOPS_SWITCH_D(D, KEOPS_KNN) };
+#undef KEOPS_KNN
+    return run();
+  }
+#define KEOPS_KNN(Dv) knn_d<Dv, false>(Kb, x, cols, ymax, idx, dist, partial, lse_out, lse_partial, M, N, K, c2, p, s)
+  auto run = [&]() -> hipError_t { KEOPS_SWITCH_D(D, KEOPS_KNN) };
+#undef KEOPS_KNN
   return run();
 }
 

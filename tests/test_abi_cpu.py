@@ -30,7 +30,7 @@ def _err(lib):
 def test_exports_every_declared_symbol(lib):
     names = _lib.header_symbols()
     assert set(names) == {"keops_gauss_sum", "keops_lse", "keops_argkmin", "keops_gauss_sum_grad_x",
-                          "keops_gauss_sum_grad_y", "keops_gauss_sum_grad_b",
+                          "keops_gauss_sum_grad_y", "keops_gauss_sum_grad_b", "keops_argkmin_lse",
                           "keops_workspace_bytes", "keops_status_string", "keops_last_error", "keops_version"}
     for name in names:
         assert hasattr(lib, name), name
@@ -156,3 +156,13 @@ def test_grad_yb_reject(lib):
     assert fb(X, Y, G, OUT, 10, 0, 3, 1, 0.1, None, 0, None) == 0
     ws = lib.keops_workspace_bytes
     assert ws(4, 1, 100_000, 100, 3, 1, 0, F32) > 0 and ws(5, 1, 100_000, 100, 3, 2, 0, F32) > 0
+
+
+def test_argkmin_lse_rejects(lib):
+    f = lib.keops_argkmin_lse
+    assert f(X, Y, IDX, None, None, 10, 10, 3, 4, 0.1, WS, 1 << 30, None) == INVALID   # lse NULL
+    assert f(X, Y, IDX, None, OUT, 10, 10, 3, 4, 0.0, WS, 1 << 30, None) == INVALID   # sigma
+    assert f(X, Y, IDX, None, IDX, 10, 10, 3, 4, 0.1, WS, 1 << 30, None) == INVALID   # lse aliases idx
+    assert f(X, Y, IDX, None, OUT, 10, 10, 3, 11, 0.1, WS, 1 << 30, None) == INVALID  # K > N
+    assert f(X, Y, IDX, None, OUT, 0, 10, 3, 4, 0.1, None, 0, None) == 0              # M = 0
+    assert lib.keops_workspace_bytes(6, 1, 100, 100_000, 3, 1, 10, F32) > lib.keops_workspace_bytes(2, 1, 100, 100_000, 3, 1, 10, F32)

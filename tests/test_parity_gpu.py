@@ -389,3 +389,59 @@ def test_autograd_function_all_gradients():
     assert_normalised(x.grad.cpu().numpy(), gx, nx, TOL_F32, "autograd x")
     assert_normalised(y.grad.cpu().numpy(), gy, ny, TOL_F32, "autograd y")
     assert_normalised(b.grad.cpu().numpy(), gb, nb, TOL_F32, "autograd b")
+
+
+# --------------------------------------------------- fused argKmin + log-sum-exp
+@pytest.mark.parametrize("M,N,D,K", ARGK_SHAPES)
+def test_argkmin_lse_shapes(M, N, D, K):
+    import pairwise_reductions_amd as pr
+    _announce("argkmin_lse", M=M, N=N, D=D, K=K)
+    rng = np.random.default_rng(M + 2 * N + K)
+    x = workloads.grid24(rng, (M, D))
+    y = workloads.grid24(rng, (N, D))
+    sig = float(np.float32(0.1))
+    idx, dist, lse = pr.argkmin_lse(_dev(x), _dev(y), K, sig, with_dist=True)
+    idx, dist, lse = _host(idx), _host(dist), _host(lse)
+    want_idx, want_d2 = oracle.argkmin(x, y, K, workers=8)
+    assert np.array_equal(idx.astype(np.int64), want_idx)
+    assert np.allclose(dist, want_d2, rtol=1e-6, atol=0)
+    want_lse = oracle.logsumexp_reduction(x, y, sig, workers=8)
+    assert np.all(np.abs(lse - want_lse) <= lse_bound(want_lse))
+
+
+def test_argkmin_screening_far_from_origin_and_unaligned_values():
+    """The screening bound grows with |x|^2 + max|y|^2: points near 1000 on a coarse grid
+    (many exact ties) and plain float32 values (keys not exact) must still give the oracle's
+    indices bit for bit, ties to the lower index."""
+    import pairwise_reductions_amd as pr
+    _announce("argkmin_screening")
+    rng = np.random.default_rng(31)
+    x = (1000.0 + rng.integers(0, 16, size=(3000, 3)) / 16.0).astype(np.float32)
+    y = (1000.0 + rng.integers(0, 16, size=(9000, 3)) / 16.0).astype(np.float32)
+    for K in (1, 10, 32):
+        idx = _host(pr.argkmin(_dev(x), _dev(y), K)).astype(np.int64)
+        want, _ = oracle.argkmin(x, y, K, workers=8)
+        assert np.array_equal(idx, want), K
+    x2 = (rng.standard_normal((2000, 5)) * 3.0).astype(np.float32)
+    y2 = (rng.standard_normal((7000, 5)) * 3.0).astype(np.float32)
+    y2[500:600] = y2[0]
+    idx, lse = pr.argkmin_lse(_dev(x2), _dev(y2), 12, 0.7)
+    want, _ = oracle.argkmin(x2, y2, 12, workers=8)
+    assert np.array_equal(_host(idx).astype(np.int64), want)
+    want_lse = oracle.logsumexp_reduction(x2, y2, float(np.float32(0.7)), workers=8)
+    assert np.all(np.abs(_host(lse) - want_lse) <= lse_bound(want_lse))
+
+
+def test_argkmin_lse_workload_100k_fused_sampled():
+    import pairwise_reductions_amd as pr
+    inp = workloads.make_inputs("argkmin_lse_100k")
+    M, N, K = inp["M"], inp["N"], inp["K"]
+    _announce("argkmin_lse_100k_fused", M=M, N=N, K=K)
+    sig = float(inp["sigma"])
+    idx, lse = pr.argkmin_lse(_dev(inp["x"]), _dev(inp["y"]), K, sig)
+    idx, lse = _host(idx), _host(lse)
+    rows = workloads.sample_rows(M, 1024, seed=4)
+    want_idx, _ = oracle.argkmin(inp["x"][rows], inp["y"], K, workers=8)
+    assert np.array_equal(idx[rows].astype(np.int64), want_idx)
+    want_lse = oracle.logsumexp_reduction(inp["x"][rows], inp["y"], sig, workers=8)
+    assert np.all(np.abs(lse[rows] - want_lse) <= lse_bound(want_lse))
