@@ -69,9 +69,10 @@ typedef enum {
  *   out[t][i][c] = sum_j exp(-||x[t][i] - y[t][j]||^2 / (2 sigma^2)) * b[t][j][c]
  * Shapes: x (B, M, D), y (B, N, D), b (B, N, C), out (B, M, C) float32.
  * dtype KEOPS_F32: x, y, b are float32; requires B = 1, 1 <= D <= 8, 1 <= C <= 8.
- * dtype KEOPS_F16: x, y, b are fp16; requires D = 32 or 64 and C = 32 or 64 (matrix-core
- * path: fp32 accumulation, the kernel values are rounded to fp16 before they multiply b);
- * any B >= 1. KEOPS_BF16 is reserved and returns KEOPS_ERR_UNSUPPORTED.
+ * dtype KEOPS_F16: x, y, b are fp16; requires D = 32 or 64 and 1 <= C <= 64 (matrix-core
+ * path: fp32 accumulation, the kernel values are rounded to fp16 before they multiply b;
+ * channels are processed in tiles of 16); any B >= 1. KEOPS_BF16 is reserved and returns
+ * KEOPS_ERR_UNSUPPORTED.
  * N = 0 writes zeros.
  */
 KEOPS_API int keops_gauss_sum(const void* x, const void* y, const void* b, float* out,

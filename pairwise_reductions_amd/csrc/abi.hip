@@ -213,7 +213,7 @@ int keops_gauss_sum(const void* x, const void* y, const void* b, float* out, int
   if (dtype == KEOPS_BF16) return fail(KEOPS_ERR_UNSUPPORTED, "the bf16 matrix-core path is not built (use KEOPS_F16)");
   if (half) {
     if (!keops::highd_supported(D, C))
-      return fail(KEOPS_ERR_UNSUPPORTED, "fp16/bf16 path needs D in {32, 64} and C in {32, 64} (got D=%d C=%d)", D, C);
+      return fail(KEOPS_ERR_UNSUPPORTED, "fp16 path needs D in {32, 64} and 1 <= C <= 64 (got D=%d C=%d)", D, C);
   } else {
     if (B != 1) return fail(KEOPS_ERR_UNSUPPORTED, "float32 path needs B = 1 (got %lld)", (long long)B);
     if (D < 1 || D > keops::kMaxLowD || C < 1 || C > keops::kMaxLowC)

@@ -31,7 +31,10 @@ constexpr int kStageKeys = 64;      // keys per LDS stage (32-key subtiles stage
 // Query tiles per wave and register budget. Measured on the B=4, 16384^2, D=C=32 workload,
 // more independent query tiles per wave beat more resident waves: the matrix cores and the
 // exp pipe overlap within a wave. Larger D or C take fewer tiles to stay within registers.
-constexpr int query_tiles(int D, int C) { return (D == 32 && C == 32) ? 8 : 4; }
+constexpr int query_tiles(int D, int C) { return (D == 32 && C <= 32) ? 8 : 4; }
+// Channels are processed in tiles of 16; a call with C channels runs the kernel for
+// padded_channels(C) and stores the first C.
+constexpr int padded_channels(int C) { return C <= 16 ? 16 : (C <= 32 ? 32 : 64); }
 constexpr int kMinBlocks = 1;       // workgroups per CU the register budget is sized for
 constexpr int kSplitTarget = 2;     // column splits aim for this many workgroups per CU
 constexpr int kKeyPad = 256;        // key counts are padded to a multiple of this
@@ -55,10 +58,11 @@ __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + 
 inline int64_t padded_keys(int64_t N) { return ceil_div(N, kKeyPad) * kKeyPad; }
 
 // beta[t][j] = -|k_j|^2 / 2 for j < N and -inf for N <= j < Npad;
-// vp[t][j / 32][c][key_slot(j % 32)] = v[t][j][c] (zero for padded keys).
+// vp[t][j / 32][c][key_slot(j % 32)] = v[t][j][c] for c < C, zero for padded keys and for the
+// padding channels C <= c < Cp.
 __global__ void __launch_bounds__(256)
 highd_prep_kernel(const _Float16* __restrict__ k, const _Float16* __restrict__ v, float* __restrict__ beta,
-                  _Float16* __restrict__ vp, int64_t N, int64_t Npad, int D, int C) {
+                  _Float16* __restrict__ vp, int64_t N, int64_t Npad, int D, int C, int Cp) {
   const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t t = blockIdx.y;
   if (j >= Npad) return;
@@ -72,15 +76,15 @@ highd_prep_kernel(const _Float16* __restrict__ k, const _Float16* __restrict__ v
     }
   }
   beta[t * Npad + j] = (j < N) ? -0.5f * s : -INFINITY;
-  _Float16* dst = vp + (t * Npad + (j / 32) * 32) * C + key_slot((int)(j % 32));
-  for (int c = 0; c < C; ++c) dst[(int64_t)c * 32] = (j < N) ? vr[c] : (_Float16)0.0f;
+  _Float16* dst = vp + (t * Npad + (j / 32) * 32) * Cp + key_slot((int)(j % 32));
+  for (int c = 0; c < Cp; ++c) dst[(int64_t)c * 32] = (j < N && c < C) ? vr[c] : (_Float16)0.0f;
 }
 
 template <int D, int C, int QT, int kMinB, int kStage, bool kPipe>
 __global__ void __launch_bounds__(256, kMinB)
 highd_kernel(const _Float16* __restrict__ q, const _Float16* __restrict__ k, const float* __restrict__ beta,
              const _Float16* __restrict__ vp, float* __restrict__ out, int64_t M, int64_t N, int64_t Npad,
-             int64_t kps, float cs) {
+             int64_t kps, float cs, int Cout) {
   constexpr int DS = D / 32;     // K-steps of S^T
   constexpr int CT = C / 16;     // 16-channel output tiles
   constexpr int KP = D + 8;      // LDS row pitch of K, halves
@@ -134,8 +138,10 @@ highd_kernel(const _Float16* __restrict__ q, const _Float16* __restrict__ k, con
   // Stage loads: global -> registers (issued before the current stage is computed) and
   // registers -> LDS (after it), so global latency hides behind the matrix work.
   constexpr int KCH = kStage * D / 8 / 256;       // 16-byte K chunks per thread
-  constexpr int VCH = NSUB * C * 4 / 256;         // 16-byte V chunks per thread
-  static_assert(KCH >= 1 && VCH >= 1 && kStage / 4 <= 256, "tile shapes");
+  constexpr int kVChunks = NSUB * C * 4;          // 16-byte V chunks per stage
+  constexpr int VCH = (kVChunks + 255) / 256;     // ... per thread (the last round may be partial)
+  static_assert(KCH * 256 * 8 == kStage * D && kStage / 4 <= 256, "tile shapes");
+  static_assert(kVChunks % 256 == 0 || VCH == 1, "tile shapes");
   half8 rk[KCH], rv[VCH];
   f32x4 rb = {};
   auto fetch = [&](int64_t st) {
@@ -152,7 +158,7 @@ highd_kernel(const _Float16* __restrict__ q, const _Float16* __restrict__ k, con
     for (int r = 0; r < VCH; ++r) {
       const int c = tid + 256 * r;
       const int t = c / (C * 4), rem = c % (C * 4), ch = rem / 4, part = (rem % 4) * 8;
-      rv[r] = *reinterpret_cast<const half8*>(vb + ((jb / 32 + t) * C + ch) * 32 + part);
+      if (c < kVChunks) rv[r] = *reinterpret_cast<const half8*>(vb + ((jb / 32 + t) * C + ch) * 32 + part);
     }
     if (tid < kStage / 4) rb = *reinterpret_cast<const f32x4*>(bb + jb + 4 * tid);
   };
@@ -166,7 +172,7 @@ highd_kernel(const _Float16* __restrict__ q, const _Float16* __restrict__ k, con
     for (int r = 0; r < VCH; ++r) {
       const int c = tid + 256 * r;
       const int t = c / (C * 4), rem = c % (C * 4);
-      *reinterpret_cast<half8*>(&sV[buf][t][rem / 4][(rem % 4) * 8]) = rv[r];
+      if (c < kVChunks) *reinterpret_cast<half8*>(&sV[buf][t][rem / 4][(rem % 4) * 8]) = rv[r];
     }
     if (tid < kStage / 4) *reinterpret_cast<f32x4*>(&sB[buf][4 * tid]) = rb;
   };
@@ -270,15 +276,27 @@ highd_kernel(const _Float16* __restrict__ q, const _Float16* __restrict__ k, con
   for (; st < nstages && !settled; ++st) stage(st, std::true_type{});
   for (; st < nstages; ++st) stage(st, std::false_type{});
 
-  const int64_t BMC = (int64_t)gridDim.z * M * C;
-  float* dst = out + split * BMC + bt * M * C;
+  // Store the first Cout channels (C here is Cout rounded up to a multiple of 16).
+  const int64_t BMC = (int64_t)gridDim.z * M * Cout;
+  float* dst = out + split * BMC + bt * M * Cout;
+  const bool vec = (Cout % 4) == 0;
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     const int64_t i = row_base + qt * 16 + l16;
     if (i >= M) continue;
     const float scale = exp2_hw(mrow[qt]);
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct) *reinterpret_cast<f32x4*>(dst + i * C + 16 * ct + 4 * g) = O[qt][ct] * scale;
+    for (int ct = 0; ct < CT; ++ct) {
+      const int c0 = 16 * ct + 4 * g;
+      const f32x4 o = O[qt][ct] * scale;
+      if (vec && c0 + 4 <= Cout) {
+        *reinterpret_cast<f32x4*>(dst + i * Cout + c0) = o;
+      } else {
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          if (c0 + v < Cout) dst[i * Cout + c0 + v] = o[v];
+      }
+    }
   }
 }
 
@@ -298,8 +316,9 @@ struct HighdPlan {
 
 HighdPlan highd_plan(int64_t B, int64_t M, int64_t N, int D, int C, int num_cus) {
   HighdPlan p;
+  const int Cp = padded_channels(C);
   p.Npad = padded_keys(N);
-  p.row_blocks = ceil_div(M, kWaves * query_tiles(D, C) * 16);
+  p.row_blocks = ceil_div(M, kWaves * query_tiles(D, Cp) * 16);
   const int64_t blocks = p.row_blocks * B;
   const int64_t target = (int64_t)num_cus * kSplitTarget;
   int64_t S = blocks < target ? ceil_div(target, blocks) : 1;
@@ -310,7 +329,7 @@ HighdPlan highd_plan(int64_t B, int64_t M, int64_t N, int D, int C, int num_cus)
   p.splits = S;
   p.kps = kps;
   p.beta_bytes = align_up((size_t)B * p.Npad * sizeof(float));
-  p.vp_bytes = align_up((size_t)B * p.Npad * C * sizeof(_Float16));
+  p.vp_bytes = align_up((size_t)B * p.Npad * Cp * sizeof(_Float16));
   p.part_bytes = S > 1 ? align_up((size_t)S * B * M * C * sizeof(float)) : 0;
   p.total = p.beta_bytes + p.vp_bytes + p.part_bytes;
   return p;
@@ -318,7 +337,7 @@ HighdPlan highd_plan(int64_t B, int64_t M, int64_t N, int D, int C, int num_cus)
 
 }  // namespace
 
-bool highd_supported(int D, int C) { return (D == 32 || D == 64) && (C == 32 || C == 64); }
+bool highd_supported(int D, int C) { return (D == 32 || D == 64) && C >= 1 && C <= 64; }
 
 size_t highd_workspace_bytes(int64_t B, int64_t M, int64_t N, int D, int C) {
   if (B == 0 || M == 0 || N == 0) return 0;
@@ -339,18 +358,22 @@ hipError_t launch_gauss_sum_highd(const void* x, const void* y, const void* b, f
   const _Float16* v = static_cast<const _Float16*>(b);
   const double sd = (double)sigma;
   const float cs = (float)(1.4426950408889634 / (sd * sd));  // tau log2(e)
-  highd_prep_kernel<<<dim3((unsigned)ceil_div(p.Npad, 256), (unsigned)B), 256, 0, s>>>(k, v, beta, vpm, N, p.Npad, D, C);
+  const int Cp = padded_channels(C);
+  highd_prep_kernel<<<dim3((unsigned)ceil_div(p.Npad, 256), (unsigned)B), 256, 0, s>>>(k, v, beta, vpm, N, p.Npad, D, C,
+                                                                                       Cp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   float* dst = p.splits > 1 ? part : out;
   const dim3 grid((unsigned)p.row_blocks, (unsigned)p.splits, (unsigned)B);
 #define KEOPS_HD(Dv, Cv)                                                                          \
   highd_kernel<Dv, Cv, query_tiles(Dv, Cv), kMinBlocks, kStageKeys, false><<<grid, 256, 0, s>>>( \
-      q, k, beta, vpm, dst, M, N, p.Npad, p.kps, cs)
-  if (D == 32 && C == 32) KEOPS_HD(32, 32);
-  else if (D == 32 && C == 64) KEOPS_HD(32, 64);
-  else if (D == 64 && C == 32) KEOPS_HD(64, 32);
-  else if (D == 64 && C == 64) KEOPS_HD(64, 64);
+      q, k, beta, vpm, dst, M, N, p.Npad, p.kps, cs, C)
+  if (D == 32 && Cp == 16) KEOPS_HD(32, 16);
+  else if (D == 32 && Cp == 32) KEOPS_HD(32, 32);
+  else if (D == 32 && Cp == 64) KEOPS_HD(32, 64);
+  else if (D == 64 && Cp == 16) KEOPS_HD(64, 16);
+  else if (D == 64 && Cp == 32) KEOPS_HD(64, 32);
+  else if (D == 64 && Cp == 64) KEOPS_HD(64, 64);
   else return hipErrorInvalidValue;
 #undef KEOPS_HD
   e = hipGetLastError();

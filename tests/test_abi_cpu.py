@@ -82,6 +82,7 @@ def _gs(lib, x=X, y=Y, b=B, out=OUT, Bt=1, M=100, N=100, D=3, C=1, sigma=0.1, dt
     (dict(D=9), UNSUPPORTED), (dict(D=0), UNSUPPORTED), (dict(C=0), UNSUPPORTED), (dict(C=9), UNSUPPORTED),
     (dict(Bt=2), UNSUPPORTED), (dict(dtype=F16, D=3), UNSUPPORTED), (dict(dtype=7), INVALID),
     (dict(dtype=2, D=32, C=32), UNSUPPORTED), (dict(dtype=F16, D=48, C=32), UNSUPPORTED),
+    (dict(dtype=F16, D=32, C=65), UNSUPPORTED),
     (dict(dtype=F16, D=32, C=32, x=X + 8), INVALID),
     (dict(x=X + 2), INVALID), (dict(out=X + 4), INVALID), (dict(M=1 << 31), UNSUPPORTED),
     (dict(ws=None, wsb=0), INVALID), (dict(wsb=16), INVALID), (dict(ws=WS + 8), INVALID),

@@ -219,6 +219,9 @@ HIGHD_SHAPES = [
     (1, 1, 1, 32, 32, 1.0), (1, 100, 77, 32, 32, 1.0), (2, 300, 1000, 32, 32, 0.7),
     (4, 513, 2049, 32, 32, 1.0), (1, 1024, 4096, 64, 32, 1.5), (1, 257, 300, 32, 64, 1.0),
     (2, 700, 5000, 64, 64, 2.0), (3, 4097, 8191, 32, 32, 1.0),
+    # channel counts that are not multiples of 16 (padded inside the library), as in the flash
+    # page's C = 1 figures
+    (4, 1000, 3000, 32, 1, 1.0), (2, 513, 2000, 32, 3, 0.8), (1, 300, 1000, 64, 17, 1.0), (2, 200, 700, 32, 48, 1.0),
 ]
 
 
