@@ -23,7 +23,8 @@
  *   - Kernel-execution faults surface at the caller's next synchronisation, as for any HIP
  *     launch. No C++ exception crosses this boundary.
  *   - M = 0 is a no-op. Results are deterministic: the same inputs on the same device give
- *     bit-identical outputs (every reduction runs in a fixed order; no atomics).
+ *     bit-identical outputs (every sum runs in a fixed order; the only atomics take maxima,
+ *     whose result does not depend on the order).
  *   - sigma is the Gaussian bandwidth: k(x, y) = exp(-||x - y||^2 / (2 sigma^2)). The
  *     flash-attention page's Phi_tau = exp(-tau/2 ||q - k||^2) is sigma = 1/sqrt(tau).
  */
@@ -60,7 +61,10 @@ typedef enum {
   KEOPS_OP_GAUSS_SUM_GRAD_X = 3,
   KEOPS_OP_GAUSS_SUM_GRAD_Y = 4,
   KEOPS_OP_GAUSS_SUM_GRAD_B = 5,
-  KEOPS_OP_ARGKMIN_LSE = 6
+  KEOPS_OP_ARGKMIN_LSE = 6,
+  KEOPS_OP_GAUSS_SUM_SCALED = 7,
+  KEOPS_OP_GAUSS_SUM_BACKWARD = 8,
+  KEOPS_OP_DIFFUSION_SCALING = 9
 } keops_op;
 
 /*
@@ -69,10 +73,10 @@ typedef enum {
  *   out[t][i][c] = sum_j exp(-||x[t][i] - y[t][j]||^2 / (2 sigma^2)) * b[t][j][c]
  * Shapes: x (B, M, D), y (B, N, D), b (B, N, C), out (B, M, C) float32.
  * dtype KEOPS_F32: x, y, b are float32; requires B = 1, 1 <= D <= 8, 1 <= C <= 8.
- * dtype KEOPS_F16: x, y, b are fp16; requires D = 32 or 64 and 1 <= C <= 64 (matrix-core
- * path: fp32 accumulation, the kernel values are rounded to fp16 before they multiply b;
- * channels are processed in tiles of 16); any B >= 1. KEOPS_BF16 is reserved and returns
- * KEOPS_ERR_UNSUPPORTED.
+ * dtype KEOPS_F16: x, y, b are fp16; requires D a multiple of 16 in [16, 128] and
+ * 1 <= C <= 64 (matrix-core path: fp32 accumulation, the kernel values are rounded to fp16
+ * before they multiply b; features run in steps of 32 and channels in tiles of 16, padding
+ * read as zero); any B >= 1. KEOPS_BF16 is reserved and returns KEOPS_ERR_UNSUPPORTED.
  * N = 0 writes zeros.
  */
 KEOPS_API int keops_gauss_sum(const void* x, const void* y, const void* b, float* out,
@@ -154,8 +158,58 @@ KEOPS_API int keops_gauss_sum_grad_b(const float* x, const float* y, const float
                                      int64_t M, int64_t N, int32_t D, int32_t C, float sigma,
                                      void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Two-sided scaled Gauss sum ("FlashDiffusion: Fused Tiled Kernel Spectral Decomposition",
+ * section 2.2: the operator diag(s) K diag(s) applied to a block V, with the right scaling
+ * folded into the block and the left scaling into the accumulation):
+ *   out[t][i][c] = row_scale[t][i] * sum_j k_ij col_scale[t][j] b[t][j][c]
+ * Shapes and dtypes as keops_gauss_sum; row_scale (B, M) and col_scale (B, N) are float32 and
+ * either may be NULL (= all ones). The diffusion operator is row_scale = col_scale = s with
+ * x = y (see keops_diffusion_scaling). On the fp16 path a col_scale (of any sign) is applied
+ * in float32 before the weights are normalised and rounded to fp16.
+ */
+KEOPS_API int keops_gauss_sum_scaled(const void* x, const void* y, const void* b, const float* row_scale,
+                                     const float* col_scale, float* out, int64_t B, int64_t M, int64_t N,
+                                     int32_t D, int32_t C, float sigma, keops_dtype dtype, void* workspace,
+                                     size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Backward pass of the Gauss sum out = keops_gauss_sum(x, y, b) for an upstream gradient
+ * g = dL/d out (the reverse-mode rule of "Kernel Operations on the GPU, with Autodiff,
+ * without Memory Overflows": every partial derivative of a reduction is a reduction of the
+ * same pairs; the flash-attention page times this forward + backward in its Figure 2):
+ *   grad_x[t][i] = -(1/sigma^2) sum_j k_ij (g_i . b_j)(x_i - y_j)
+ *   grad_y[t][j] =  (1/sigma^2) sum_i k_ij (g_i . b_j)(x_i - y_j)
+ *   grad_b[t][j] =  sum_i k_ij g_i
+ * Any of grad_x (B, M, D), grad_y (B, N, D), grad_b (B, N, C) may be NULL (not computed).
+ * g (B, M, C) and every gradient are float32. dtype KEOPS_F32: x, y, b float32 with the
+ * limits of keops_gauss_sum_grad_x (B = 1). dtype KEOPS_F16: x, y, b fp16 with the limits of
+ * the fp16 keops_gauss_sum; the pair weights k_ij (g_i . b_j) are rounded to fp16 (after the
+ * weight vectors are normalised, so nothing overflows) and accumulate in fp32.
+ */
+KEOPS_API int keops_gauss_sum_backward(const void* x, const void* y, const void* b, const float* g, float* grad_x,
+                                       float* grad_y, float* grad_b, int64_t B, int64_t M, int64_t N, int32_t D,
+                                       int32_t C, float sigma, keops_dtype dtype, void* workspace,
+                                       size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Normalisation passes of the diffusion operator ("FlashDiffusion: Fused Tiled Kernel
+ * Spectral Decomposition", section 2.2: the q and d passes are kernel applications with the
+ * block replaced by ones and by q^-alpha), for the self-kernel K_ij = k(x_i, x_j):
+ *   q = K 1,   p = q^-alpha,   d = p * (K p),   s = p / sqrt(d)
+ * so that diag(s) K diag(s) = D^-1/2 K_alpha D^-1/2 with K_alpha = diag(p) K diag(p) and
+ * D = diag(K_alpha 1), the symmetric form of the alpha-normalised diffusion matrix.
+ * Shapes: x (B, N, D) (float32 with B = 1 and 1 <= D <= 8, or fp16 with the fp16 limits of
+ * keops_gauss_sum); s (B, N) float32; q and d (B, N) float32 or NULL. alpha must be finite.
+ */
+KEOPS_API int keops_diffusion_scaling(const void* x, float* s, float* q, float* d, int64_t B, int64_t N, int32_t D,
+                                      float sigma, float alpha, keops_dtype dtype, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream);
+
 /* Workspace bytes `op` (a keops_op) needs for these arguments on the current device
- * (unused arguments are ignored). Returns 0 for unsupported or invalid arguments. */
+ * (unused arguments are ignored; KEOPS_OP_DIFFUSION_SCALING reads N, D and B). For
+ * KEOPS_OP_GAUSS_SUM_SCALED and KEOPS_OP_GAUSS_SUM_BACKWARD the size covers every choice of
+ * the optional arguments. Returns 0 for unsupported or invalid arguments. */
 KEOPS_API size_t keops_workspace_bytes(int op, int64_t B, int64_t M, int64_t N, int32_t D, int32_t C,
                              int32_t K, keops_dtype dtype);
 

@@ -16,7 +16,11 @@ Sources (cited by page title and section):
          the LazyTensor example (K_ij = exp(-D_ij), a_i = sum_j K_ij, and the gradient of
          sum_i a_i^2 with respect to x).
   [RUX]  "Fast Gauss Sums via Flash Attention" (Rux & Neumayer): abstract and the Output
-         row of Algorithms 1 and 2, s_m = sum_n Phi_tau(q_m, k_n) v_n with signed weights.
+         row of Algorithms 1 and 2, s_m = sum_n Phi_tau(q_m, k_n) v_n with signed weights;
+         Figure 2 times the same sum's forward and backward.
+  [FD]   "FlashDiffusion: Fused Tiled Kernel Spectral Decomposition", section 2.2: the
+         diffusion operator diag(s) K diag(s) applied to a block V, and its q and d
+         normalisation passes (kernel applications with V replaced by 1 and by q^-alpha).
 
 Inputs are the exact float32 / float16 arrays the device receives, widened exactly to
 float64. sigma is whatever value the caller passes (pass float(np.float32(sigma)) so both
@@ -316,6 +320,64 @@ def gauss_sum_grad_b(x, y, g, sigma: float, workers: Optional[int] = None) -> Tu
     if M > 0:
         _parallel_rows(block, N, M, workers)
     return grad, n
+
+
+def gauss_sum_scaled(x, y, b, sigma: float, row_scale=None, col_scale=None,
+                     workers: Optional[int] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """Two-sided scaled Gauss sum [FD, section 2.2]: out = diag(r) K diag(c) b.
+
+    s[i, c'] = r_i sum_j k_ij c_j b[j, c'], evaluated as the plain Gauss sum of the weights
+    c_j b_j, then scaled row by row. A missing scale is all ones. Returns (s, n) with
+    n[i, c'] = |r_i| sum_j |k_ij c_j b[j, c']|.
+    """
+    b = _f64(b)
+    if b.ndim == 1:
+        b = b[:, None]
+    if col_scale is not None:
+        b = _f64(col_scale)[:, None] * b
+    s, n = gauss_sum(x, y, b, sigma, workers)
+    if row_scale is not None:
+        r = _f64(row_scale)[:, None]
+        s = r * s
+        n = np.abs(r) * n
+    return s, n
+
+
+def diffusion_scaling(x, sigma: float, alpha: float,
+                      workers: Optional[int] = None) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Normalisation of the diffusion operator [FD, section 2.2], for K_ij = k(x_i, x_j).
+
+    The q pass applies K to ones and the d pass applies the alpha-normalised kernel
+    K_alpha = diag(q^-alpha) K diag(q^-alpha) to ones; the symmetric operator is then
+    diag(s) K diag(s) with s = q^-alpha d^-1/2:
+        q = K 1,  p = q^-alpha,  d = p * (K p),  s = p / sqrt(d).
+    Returns (s, q, d).
+    """
+    x = _f64(x)
+    N = x.shape[0]
+    q = gauss_sum(x, x, np.ones(N), sigma, workers)[0][:, 0]
+    p = q ** (-float(alpha))
+    d = p * gauss_sum(x, x, p, sigma, workers)[0][:, 0]
+    return p / np.sqrt(d), q, d
+
+
+def gauss_sum_batched_backward(x, y, b, g, sigma: float, workers: Optional[int] = None) -> dict:
+    """Gradients of the batched Gauss sum [RUX, eq. (1); Figure 2 times forward + backward].
+
+    For every batch index t independently, the gradients of s = sum_j k_ij b_j contracted
+    with the upstream g (B, M, C), as in gauss_sum_grad_x / _grad_y / _grad_b. Returns
+    {"x": (grad, n), "y": (grad, n), "b": (grad, n)}, each stacked over the batch.
+    """
+    x = _f64(x)
+    y = _f64(y)
+    b = _f64(b)
+    g = _f64(g)
+    parts = {"x": [], "y": [], "b": []}
+    for t in range(x.shape[0]):
+        parts["x"].append(gauss_sum_grad_x(x[t], y[t], b[t], g[t], sigma, workers))
+        parts["y"].append(gauss_sum_grad_y(x[t], y[t], b[t], g[t], sigma, workers))
+        parts["b"].append(gauss_sum_grad_b(x[t], y[t], g[t], sigma, workers))
+    return {key: (np.stack([p[0] for p in v]), np.stack([p[1] for p in v])) for key, v in parts.items()}
 
 
 def default_workers() -> int:

@@ -12,8 +12,9 @@ from typing import Optional, Tuple
 from . import _lib
 from ._lib import KeopsError  # noqa: F401
 
-__all__ = ["gauss_sum", "lse", "argkmin", "argkmin_lse", "gauss_sum_grad_x", "gauss_sum_grad_y", "gauss_sum_grad_b",
-           "gauss_sum_autograd", "workspace_bytes", "KeopsError", "version"]
+__all__ = ["gauss_sum", "gauss_sum_scaled", "lse", "argkmin", "argkmin_lse", "gauss_sum_grad_x", "gauss_sum_grad_y",
+           "gauss_sum_grad_b", "gauss_sum_backward", "diffusion_scaling", "gauss_sum_autograd", "workspace_bytes",
+           "KeopsError", "version"]
 
 
 def _torch():
@@ -59,36 +60,107 @@ def workspace_bytes(op: int, B: int, M: int, N: int, D: int, C: int = 1, K: int 
     return int(_lib.load().keops_workspace_bytes(op, B, M, N, D, C, K, dtype))
 
 
-def gauss_sum(x, y, b, sigma: float, out=None, workspace=None):
-    """s[i, c] = sum_j exp(-|x_i - y_j|^2 / (2 sigma^2)) b[j, c].
-
-    float32: x (M, D), y (N, D), b (N, C) -> (M, C).
-    float16 / bfloat16: x (B, M, D), y (B, N, D), b (B, N, C) -> (B, M, C) float32.
-    """
+def _gauss_shapes(x, y, b):
+    """(B, M, N, D, C, dtype code, batched) of a Gauss-sum call: float32 2-D or fp16 3-D."""
     torch = _torch()
-    lib = _lib.load()
     if x.dtype == torch.float32:
         M, D = _dims(x, 2)
         N, _ = _dims(y, 2)
         _, C = _dims(b, 2)
-        B, dt = 1, _lib.KEOPS_F32
-        shape = (M, C)
-    else:
-        dt = {torch.float16: _lib.KEOPS_F16, torch.bfloat16: _lib.KEOPS_BF16}.get(x.dtype)
-        if dt is None:
-            raise ValueError(f"unsupported dtype {x.dtype}")
-        B, M, D = _dims(x, 3)
-        _, N, _ = _dims(y, 3)
-        _, _, C = _dims(b, 3)
-        shape = (B, M, C)
+        return 1, M, N, D, C, _lib.KEOPS_F32, False
+    dt = {torch.float16: _lib.KEOPS_F16, torch.bfloat16: _lib.KEOPS_BF16}.get(x.dtype)
+    if dt is None:
+        raise ValueError(f"unsupported dtype {x.dtype}")
+    B, M, D = _dims(x, 3)
+    _, N, _ = _dims(y, 3)
+    _, _, C = _dims(b, 3)
+    return B, M, N, D, C, dt, True
+
+
+def gauss_sum(x, y, b, sigma: float, out=None, workspace=None):
+    """s[i, c] = sum_j exp(-|x_i - y_j|^2 / (2 sigma^2)) b[j, c].
+
+    float32: x (M, D), y (N, D), b (N, C) -> (M, C).
+    float16: x (B, M, D), y (B, N, D), b (B, N, C) -> (B, M, C) float32.
+    """
+    torch = _torch()
+    lib = _lib.load()
+    B, M, N, D, C, dt, batched = _gauss_shapes(x, y, b)
     if out is None:
-        out = torch.empty(shape, dtype=torch.float32, device=x.device)
+        out = torch.empty((B, M, C) if batched else (M, C), dtype=torch.float32, device=x.device)
     nbytes = lib.keops_workspace_bytes(_lib.OP_GAUSS_SUM, B, M, N, D, C, 0, dt)
     ws, have = _workspace(nbytes, x.device, workspace)
     st = lib.keops_gauss_sum(_ptr(x), _ptr(y), _ptr(b), _ptr(out), B, M, N, D, C, float(sigma), dt,
                              _ptr(ws), have, _stream(x.device))
     _lib.check(st, "keops_gauss_sum")
     return out
+
+
+def gauss_sum_scaled(x, y, b, sigma: float, row_scale=None, col_scale=None, out=None, workspace=None):
+    """out[i, c] = row_scale[i] sum_j k_ij col_scale[j] b[j, c] (either scale may be None).
+
+    Shapes as gauss_sum; row_scale is (M,) or (B, M), col_scale (N,) or (B, N), float32.
+    """
+    torch = _torch()
+    lib = _lib.load()
+    B, M, N, D, C, dt, batched = _gauss_shapes(x, y, b)
+    for t, n in ((row_scale, M), (col_scale, N)):
+        if t is not None and (t.dtype != torch.float32 or t.numel() != B * n or not t.is_contiguous()):
+            raise ValueError("scales must be contiguous float32 with one entry per row / column")
+    if out is None:
+        out = torch.empty((B, M, C) if batched else (M, C), dtype=torch.float32, device=x.device)
+    nbytes = lib.keops_workspace_bytes(_lib.OP_GAUSS_SUM_SCALED, B, M, N, D, C, 0, dt)
+    ws, have = _workspace(nbytes, x.device, workspace)
+    st = lib.keops_gauss_sum_scaled(_ptr(x), _ptr(y), _ptr(b), _ptr(row_scale), _ptr(col_scale), _ptr(out), B, M, N,
+                                    D, C, float(sigma), dt, _ptr(ws), have, _stream(x.device))
+    _lib.check(st, "keops_gauss_sum_scaled")
+    return out
+
+
+def gauss_sum_backward(x, y, b, g, sigma: float, need=("x", "y", "b"), workspace=None):
+    """Gradients of out = gauss_sum(x, y, b) for the upstream gradient g = dL/d out (float32).
+
+    Returns a dict with the requested keys among "x", "y", "b" (float32 tensors shaped like
+    x, y and b). Works for both the float32 and the fp16 (batched) path.
+    """
+    torch = _torch()
+    lib = _lib.load()
+    B, M, N, D, C, dt, batched = _gauss_shapes(x, y, b)
+    if g.dtype != torch.float32 or tuple(g.shape) != ((B, M, C) if batched else (M, C)) or not g.is_contiguous():
+        raise ValueError("g must be contiguous float32 shaped like the forward output")
+    res = {}
+    for key, t in (("x", x), ("y", y), ("b", b)):
+        if key in need:
+            res[key] = torch.empty(t.shape, dtype=torch.float32, device=x.device)
+    nbytes = lib.keops_workspace_bytes(_lib.OP_GAUSS_SUM_BACKWARD, B, M, N, D, C, 0, dt)
+    ws, have = _workspace(nbytes, x.device, workspace)
+    st = lib.keops_gauss_sum_backward(_ptr(x), _ptr(y), _ptr(b), _ptr(g), _ptr(res.get("x")), _ptr(res.get("y")),
+                                      _ptr(res.get("b")), B, M, N, D, C, float(sigma), dt, _ptr(ws), have,
+                                      _stream(x.device))
+    _lib.check(st, "keops_gauss_sum_backward")
+    return res
+
+
+def diffusion_scaling(x, sigma: float, alpha: float, workspace=None):
+    """(s, q, d) of the alpha-normalised diffusion operator diag(s) K diag(s), K_ij = k(x_i, x_j):
+    q = K 1, p = q^-alpha, d = p (K p), s = p / sqrt(d). x is float32 (N, D) or fp16 (B, N, D)."""
+    torch = _torch()
+    lib = _lib.load()
+    if x.dtype == torch.float32:
+        N, D = _dims(x, 2)
+        B, dt, shape = 1, _lib.KEOPS_F32, (N,)
+    elif x.dtype == torch.float16:
+        B, N, D = _dims(x, 3)
+        dt, shape = _lib.KEOPS_F16, (B, N)
+    else:
+        raise ValueError(f"unsupported dtype {x.dtype}")
+    s, q, d = (torch.empty(shape, dtype=torch.float32, device=x.device) for _ in range(3))
+    nbytes = lib.keops_workspace_bytes(_lib.OP_DIFFUSION_SCALING, B, N, N, D, 1, 0, dt)
+    ws, have = _workspace(nbytes, x.device, workspace)
+    st = lib.keops_diffusion_scaling(_ptr(x), _ptr(s), _ptr(q), _ptr(d), B, N, D, float(sigma), float(alpha), dt,
+                                     _ptr(ws), have, _stream(x.device))
+    _lib.check(st, "keops_diffusion_scaling")
+    return s, q, d
 
 
 def lse(x, y, sigma: float, out=None, workspace=None):

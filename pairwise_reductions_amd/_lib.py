@@ -17,7 +17,7 @@ HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "keops_mi355x.h")
 KEOPS_F32, KEOPS_F16, KEOPS_BF16 = 0, 1, 2
 KEOPS_OK, KEOPS_ERR_INVALID_ARG, KEOPS_ERR_UNSUPPORTED, KEOPS_ERR_HIP = 0, 1, 2, 3
 OP_GAUSS_SUM, OP_LSE, OP_ARGKMIN, OP_GAUSS_SUM_GRAD_X, OP_GAUSS_SUM_GRAD_Y, OP_GAUSS_SUM_GRAD_B = 0, 1, 2, 3, 4, 5
-OP_ARGKMIN_LSE = 6
+OP_ARGKMIN_LSE, OP_GAUSS_SUM_SCALED, OP_GAUSS_SUM_BACKWARD, OP_DIFFUSION_SCALING = 6, 7, 8, 9
 
 _vp = ctypes.c_void_p
 _i64 = ctypes.c_int64
@@ -36,6 +36,12 @@ _SIGNATURES = {
     "keops_gauss_sum_grad_y": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i32, _i32, _f32, _vp, _sz,
                                               _vp]),
     "keops_gauss_sum_grad_b": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i32, _i32, _f32, _vp, _sz, _vp]),
+    "keops_gauss_sum_scaled": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _f32,
+                                              ctypes.c_int, _vp, _sz, _vp]),
+    "keops_gauss_sum_backward": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32,
+                                                _f32, ctypes.c_int, _vp, _sz, _vp]),
+    "keops_diffusion_scaling": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i32, _f32, _f32, ctypes.c_int, _vp,
+                                               _sz, _vp]),
     "keops_workspace_bytes": (_sz, [ctypes.c_int, _i64, _i64, _i64, _i32, _i32, _i32, ctypes.c_int]),
     "keops_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "keops_last_error": (ctypes.c_char_p, []),

@@ -1,14 +1,16 @@
-"""torch.autograd glue for the float32 Gauss sum ("Kernel matrix reduction", Variants: each
-partial derivative is its own reduction, plugged into torch.autograd).
+"""torch.autograd glue for the Gauss sum ("Kernel matrix reduction", Variants: each partial
+derivative is its own reduction, plugged into torch.autograd).
 
-Forward: keops_gauss_sum. Backward for the upstream gradient g = dL/ds: keops_gauss_sum_grad_x,
-keops_gauss_sum_grad_y and keops_gauss_sum_grad_b, each only when its input needs a gradient.
+Forward: keops_gauss_sum. Backward for the upstream gradient g = dL/ds: one
+keops_gauss_sum_backward call computing only the gradients whose inputs need one. Works for
+the float32 (M, D) path and the fp16 batched (B, M, D) path; fp16 inputs receive their
+gradients cast back to fp16, as autograd requires.
 """
 from __future__ import annotations
 
 import torch
 
-from . import gauss_sum, gauss_sum_grad_b, gauss_sum_grad_x, gauss_sum_grad_y
+from . import gauss_sum, gauss_sum_backward
 
 
 class GaussSum(torch.autograd.Function):
@@ -22,8 +24,12 @@ class GaussSum(torch.autograd.Function):
     @staticmethod
     def backward(ctx, g):
         x, y, b = ctx.saved_tensors
-        g = g.contiguous()
-        gx = gauss_sum_grad_x(x, y, b, g, ctx.sigma) if ctx.needs_input_grad[0] else None
-        gy = gauss_sum_grad_y(x, y, b, g, ctx.sigma) if ctx.needs_input_grad[1] else None
-        gb = gauss_sum_grad_b(x, y, g, ctx.sigma) if ctx.needs_input_grad[2] else None
-        return gx, gy, gb, None
+        need = tuple(k for k, want in zip(("x", "y", "b"), ctx.needs_input_grad[:3]) if want)
+        if not need:
+            return None, None, None, None
+        grads = gauss_sum_backward(x, y, b, g.to(torch.float32).contiguous(), ctx.sigma, need=need)
+        out = []
+        for key, t in (("x", x), ("y", y), ("b", b)):
+            gk = grads.get(key)
+            out.append(None if gk is None else gk.to(t.dtype))
+        return out[0], out[1], out[2], None

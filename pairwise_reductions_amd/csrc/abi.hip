@@ -170,6 +170,136 @@ const char* keops_status_string(int status) {
 
 const char* keops_last_error(void) { return g_last_error.c_str(); }
 
+}  // extern "C"
+
+namespace {
+
+// Shape checks shared by the Gauss-sum family: the fp16 matrix-core family or the float32
+// low-D family (B = 1).
+int check_gauss_family(keops_dtype dtype, int64_t B, int32_t D, int32_t C, const char* what) {
+  if (dtype == KEOPS_BF16) return fail(KEOPS_ERR_UNSUPPORTED, "%s: the bf16 matrix-core path is not built (use KEOPS_F16)", what);
+  if (dtype == KEOPS_F16) {
+    if (!keops::highd_supported(D, C))
+      return fail(KEOPS_ERR_UNSUPPORTED, "%s: fp16 path needs D a multiple of 16 in [16, 128] and 1 <= C <= 64 "
+                  "(got D=%d C=%d)", what, D, C);
+    return KEOPS_OK;
+  }
+  if (dtype != KEOPS_F32) return fail(KEOPS_ERR_INVALID_ARG, "%s: unknown dtype %d", what, (int)dtype);
+  if (B != 1) return fail(KEOPS_ERR_UNSUPPORTED, "%s: float32 path needs B = 1 (got %lld)", what, (long long)B);
+  if (D < 1 || D > keops::kMaxLowD || C < 1 || C > keops::kMaxLowC)
+    return fail(KEOPS_ERR_UNSUPPORTED, "%s: float32 path needs 1 <= D <= %d and 1 <= C <= %d (got D=%d C=%d)", what,
+                keops::kMaxLowD, keops::kMaxLowC, D, C);
+  return KEOPS_OK;
+}
+
+// Workspace of the float32 scaled Gauss sum: the column-scaled weights, then the low-D layout.
+size_t lowd_scaled_bytes(int64_t M, int64_t N, int D, int C, bool col_scaled) {
+  const size_t tail = lowd_layout(KEOPS_OP_GAUSS_SUM, M, N, D, C, 0).total;
+  if (M == 0 || N == 0) return 0;
+  return (col_scaled ? keops::align_up((size_t)N * C * sizeof(float)) : 0) + tail;
+}
+
+// out = rscale . sum_j k_ij cscale_j b_j on either path; arguments already validated except
+// for the workspace. `ranges` lists the caller's buffers the workspace must not overlap.
+int gauss_sum_run(const void* x, const void* y, const void* b, bool b_f32, const float* rscale, const float* cscale,
+                  float* out, int64_t B, int64_t M, int64_t N, int32_t D, int32_t C, float sigma, bool half,
+                  void* workspace, size_t workspace_bytes, const Range* ranges, int nranges, hipStream_t stream) {
+  if (B == 0 || M == 0) return ok();
+  if (N == 0) {
+    KEOPS_HIP(keops::launch_fill(out, B * M * C, 0.0f, stream), "fill");
+    return ok();
+  }
+  const size_t need = half ? keops::highd_workspace_bytes(B, M, N, D, C, b_f32 || cscale != nullptr)
+                           : lowd_scaled_bytes(M, N, D, C, cscale != nullptr);
+  KEOPS_TRY(check_workspace(workspace, workspace_bytes, need));
+  for (int r = 0; r < nranges; ++r)
+    if (overlaps(Range{workspace, need}, ranges[r]))
+      return fail(KEOPS_ERR_INVALID_ARG, "workspace overlaps an input or an output");
+  if (half) {
+    KEOPS_HIP(keops::launch_gauss_sum_highd(x, y, b, b_f32, rscale, cscale, out, workspace, B, M, N, D, C, sigma,
+                                            stream),
+              "gauss_sum_highd");
+    return ok();
+  }
+  char* ws = static_cast<char*>(workspace);
+  const float* bw = static_cast<const float*>(b);
+  if (cscale) {
+    float* bs = reinterpret_cast<float*>(ws);
+    KEOPS_HIP(keops::launch_scale_rows(bw, cscale, bs, N, C, stream), "scale_cols");
+    bw = bs;
+    ws += keops::align_up((size_t)N * C * sizeof(float));
+  }
+  const LowdLayout L = lowd_layout(KEOPS_OP_GAUSS_SUM, M, N, D, C, 0);
+  double* cols = reinterpret_cast<double*>(ws + L.cols_off);
+  float* part = reinterpret_cast<float*>(ws + L.part_off);
+  const double c2 = c2_of(sigma);
+  KEOPS_HIP(keops::launch_prep_cols(static_cast<const float*>(y), cols, N, D, c2, true, stream), "prep_cols");
+  KEOPS_HIP(keops::launch_gauss_sum_lowd(static_cast<const float*>(x), static_cast<const float*>(y), cols, bw, rscale,
+                                         out, part, M, N, D, C, c2, L.plan, stream),
+            "gauss_sum_lowd");
+  return ok();
+}
+
+int gauss_sum_impl(const void* x, const void* y, const void* b, const float* rscale, const float* cscale, float* out,
+                   int64_t B, int64_t M, int64_t N, int32_t D, int32_t C, float sigma, keops_dtype dtype,
+                   void* workspace, size_t workspace_bytes, hipStream_t stream, const char* what) {
+  KEOPS_TRY(check_extent(B, "B"));
+  KEOPS_TRY(check_extent(M, "M"));
+  KEOPS_TRY(check_extent(N, "N"));
+  KEOPS_TRY(check_sigma(sigma));
+  KEOPS_TRY(check_gauss_family(dtype, B, D, C, what));
+  const bool half = (dtype == KEOPS_F16);
+  const size_t es = half ? 2 : 4;
+  const size_t al = half ? 16 : 4;
+  const Range rx{x, (size_t)(B * M * D) * es}, ry{y, (size_t)(B * N * D) * es}, rb{b, (size_t)(B * N * C) * es};
+  const Range ro{out, (size_t)(B * M * C) * sizeof(float)};
+  const Range rr{rscale, rscale ? (size_t)(B * M) * sizeof(float) : 0};
+  const Range rc{cscale, cscale ? (size_t)(B * N) * sizeof(float) : 0};
+  KEOPS_TRY(check_ptr(x, "x", al, rx.bytes));
+  KEOPS_TRY(check_ptr(y, "y", al, ry.bytes));
+  KEOPS_TRY(check_ptr(b, "b", al, rb.bytes));
+  KEOPS_TRY(check_ptr(out, "out", half ? 16 : 4, ro.bytes));
+  if (rscale && !aligned(rscale, 4)) return fail(KEOPS_ERR_INVALID_ARG, "row_scale must be 4-byte aligned");
+  if (cscale && !aligned(cscale, 4)) return fail(KEOPS_ERR_INVALID_ARG, "col_scale must be 4-byte aligned");
+  if (overlaps(ro, rx) || overlaps(ro, ry) || overlaps(ro, rb) || overlaps(ro, rr) || overlaps(ro, rc))
+    return fail(KEOPS_ERR_INVALID_ARG, "out overlaps an input");
+  const Range all[] = {rx, ry, rb, ro, rr, rc};
+  return gauss_sum_run(x, y, b, false, rscale, cscale, out, B, M, N, D, C, sigma, half, workspace, workspace_bytes,
+                       all, 6, stream);
+}
+
+// Workspace of keops_gauss_sum_backward: the passes run one after another on the stream, so
+// they share one region sized for the largest.
+size_t backward_bytes(int64_t B, int64_t M, int64_t N, int D, int C, bool half, bool want_x, bool want_y,
+                      bool want_b) {
+  size_t need = 0;
+  auto take = [&](size_t v) { need = v > need ? v : need; };
+  if (half) {
+    if (want_x) take(keops::highd_grad_workspace_bytes(B, M, N, D, C));
+    if (want_y) take(keops::highd_grad_workspace_bytes(B, N, M, D, C));
+    if (want_b) take(keops::highd_workspace_bytes(B, N, M, D, C, true));
+  } else {
+    if (want_x) take(lowd_layout(KEOPS_OP_GAUSS_SUM_GRAD_X, M, N, D, C, 0).total);
+    if (want_y) take(lowd_layout(KEOPS_OP_GAUSS_SUM_GRAD_X, N, M, D, C, 0).total);
+    if (want_b) take(lowd_layout(KEOPS_OP_GAUSS_SUM, N, M, D, C, 0).total);
+  }
+  return need;
+}
+
+// Workspace of keops_diffusion_scaling: ones, q, p and d (B N floats each), then the region of
+// the two Gauss sums.
+size_t diffusion_bytes(int64_t B, int64_t N, int D, bool half) {
+  if (B == 0 || N == 0) return 0;
+  const size_t vec = keops::align_up((size_t)(B * N) * sizeof(float));
+  const size_t sums = half ? keops::highd_workspace_bytes(B, N, N, D, 1, true)
+                           : lowd_layout(KEOPS_OP_GAUSS_SUM, N, N, D, 1, 0).total;
+  return 4 * vec + sums;
+}
+
+}  // namespace
+
+extern "C" {
+
 size_t keops_workspace_bytes(int op, int64_t B, int64_t M, int64_t N, int32_t D, int32_t C, int32_t K,
                              keops_dtype dtype) {
   if (B < 0 || M < 0 || N < 0 || M > kMaxExtent || N > kMaxExtent) return 0;
@@ -177,7 +307,7 @@ size_t keops_workspace_bytes(int op, int64_t B, int64_t M, int64_t N, int32_t D,
     case KEOPS_OP_GAUSS_SUM:
       if (dtype == KEOPS_F16) {
         if (!keops::highd_supported(D, C)) return 0;
-        return keops::highd_workspace_bytes(B, M, N, D, C);
+        return keops::highd_workspace_bytes(B, M, N, D, C, false);
       }
       if (dtype != KEOPS_F32 || B != 1 || D < 1 || D > keops::kMaxLowD || C < 1 || C > keops::kMaxLowC) return 0;
       return lowd_layout(op, M, N, D, C, 0).total;
@@ -197,6 +327,28 @@ size_t keops_workspace_bytes(int op, int64_t B, int64_t M, int64_t N, int32_t D,
     case KEOPS_OP_GAUSS_SUM_GRAD_B:  // the Gauss sum over the transposed pairs
       if (D < 1 || D > keops::kMaxLowD || C < 1 || C > keops::kMaxLowC) return 0;
       return lowd_layout(KEOPS_OP_GAUSS_SUM, N, M, D, C, 0).total;
+    case KEOPS_OP_GAUSS_SUM_SCALED:
+      if (dtype == KEOPS_F16) {
+        if (!keops::highd_supported(D, C) || B == 0 || M == 0 || N == 0) return 0;
+        return keops::highd_workspace_bytes(B, M, N, D, C, true);
+      }
+      if (dtype != KEOPS_F32 || B != 1 || D < 1 || D > keops::kMaxLowD || C < 1 || C > keops::kMaxLowC) return 0;
+      return lowd_scaled_bytes(M, N, D, C, true);
+    case KEOPS_OP_GAUSS_SUM_BACKWARD:
+      if (dtype == KEOPS_F16) {
+        if (!keops::highd_supported(D, C) || B == 0 || M == 0 || N == 0) return 0;
+        return backward_bytes(B, M, N, D, C, true, true, true, true);
+      }
+      if (dtype != KEOPS_F32 || B != 1 || D < 1 || D > keops::kMaxLowD || C < 1 || C > keops::kMaxLowC) return 0;
+      if (M == 0 || N == 0) return 0;
+      return backward_bytes(B, M, N, D, C, false, true, true, true);
+    case KEOPS_OP_DIFFUSION_SCALING:
+      if (dtype == KEOPS_F16) {
+        if (!keops::highd_supported(D, 1)) return 0;
+        return diffusion_bytes(B, N, D, true);
+      }
+      if (dtype != KEOPS_F32 || B != 1 || D < 1 || D > keops::kMaxLowD) return 0;
+      return diffusion_bytes(B, N, D, false);
   }
   return 0;
 }
@@ -204,63 +356,148 @@ size_t keops_workspace_bytes(int op, int64_t B, int64_t M, int64_t N, int32_t D,
 int keops_gauss_sum(const void* x, const void* y, const void* b, float* out, int64_t B, int64_t M, int64_t N,
                     int32_t D, int32_t C, float sigma, keops_dtype dtype, void* workspace,
                     size_t workspace_bytes, hipStream_t stream) {
+  return gauss_sum_impl(x, y, b, nullptr, nullptr, out, B, M, N, D, C, sigma, dtype, workspace, workspace_bytes,
+                        stream, "gauss_sum");
+}
+
+int keops_gauss_sum_scaled(const void* x, const void* y, const void* b, const float* row_scale,
+                           const float* col_scale, float* out, int64_t B, int64_t M, int64_t N, int32_t D,
+                           int32_t C, float sigma, keops_dtype dtype, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+  return gauss_sum_impl(x, y, b, row_scale, col_scale, out, B, M, N, D, C, sigma, dtype, workspace,
+                        workspace_bytes, stream, "gauss_sum_scaled");
+}
+
+int keops_gauss_sum_backward(const void* x, const void* y, const void* b, const float* g, float* grad_x,
+                             float* grad_y, float* grad_b, int64_t B, int64_t M, int64_t N, int32_t D, int32_t C,
+                             float sigma, keops_dtype dtype, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
   KEOPS_TRY(check_extent(B, "B"));
   KEOPS_TRY(check_extent(M, "M"));
   KEOPS_TRY(check_extent(N, "N"));
   KEOPS_TRY(check_sigma(sigma));
-  const bool half = (dtype == KEOPS_F16 || dtype == KEOPS_BF16);
-  if (!half && dtype != KEOPS_F32) return fail(KEOPS_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
-  if (dtype == KEOPS_BF16) return fail(KEOPS_ERR_UNSUPPORTED, "the bf16 matrix-core path is not built (use KEOPS_F16)");
-  if (half) {
-    if (!keops::highd_supported(D, C))
-      return fail(KEOPS_ERR_UNSUPPORTED, "fp16 path needs D in {32, 64} and 1 <= C <= 64 (got D=%d C=%d)", D, C);
-  } else {
-    if (B != 1) return fail(KEOPS_ERR_UNSUPPORTED, "float32 path needs B = 1 (got %lld)", (long long)B);
-    if (D < 1 || D > keops::kMaxLowD || C < 1 || C > keops::kMaxLowC)
-      return fail(KEOPS_ERR_UNSUPPORTED, "float32 path needs 1 <= D <= %d and 1 <= C <= %d (got D=%d C=%d)",
-                  keops::kMaxLowD, keops::kMaxLowC, D, C);
-  }
+  KEOPS_TRY(check_gauss_family(dtype, B, D, C, "gauss_sum_backward"));
+  const bool half = (dtype == KEOPS_F16);
   const size_t es = half ? 2 : 4;
   const size_t al = half ? 16 : 4;
   const Range rx{x, (size_t)(B * M * D) * es}, ry{y, (size_t)(B * N * D) * es}, rb{b, (size_t)(B * N * C) * es};
-  const Range ro{out, (size_t)(B * M * C) * sizeof(float)};
+  const Range rg{g, (size_t)(B * M * C) * 4};
+  const Range ogx{grad_x, grad_x ? (size_t)(B * M * D) * 4 : 0};
+  const Range ogy{grad_y, grad_y ? (size_t)(B * N * D) * 4 : 0};
+  const Range ogb{grad_b, grad_b ? (size_t)(B * N * C) * 4 : 0};
   KEOPS_TRY(check_ptr(x, "x", al, rx.bytes));
   KEOPS_TRY(check_ptr(y, "y", al, ry.bytes));
   KEOPS_TRY(check_ptr(b, "b", al, rb.bytes));
-  KEOPS_TRY(check_ptr(out, "out", half ? 16 : 4, ro.bytes));
-  if (overlaps(ro, rx) || overlaps(ro, ry) || overlaps(ro, rb))
-    return fail(KEOPS_ERR_INVALID_ARG, "out overlaps an input");
-  if (B == 0 || M == 0) return ok();
-  if (half) {
-    const size_t need = keops::highd_workspace_bytes(B, M, N, D, C);
-    KEOPS_TRY(check_workspace(workspace, workspace_bytes, need));
-    if (overlaps(Range{workspace, need}, ro)) return fail(KEOPS_ERR_INVALID_ARG, "workspace overlaps out");
-    if (N == 0) {
-      KEOPS_HIP(keops::launch_fill(out, B * M * C, 0.0f, stream), "fill");
-      return ok();
-    }
-    KEOPS_HIP(keops::launch_gauss_sum_highd(x, y, b, out, workspace, B, M, N, D, C, sigma, dtype == KEOPS_BF16,
-                                            stream),
-              "gauss_sum_highd");
-    return ok();
+  KEOPS_TRY(check_ptr(g, "g", 4, rg.bytes));
+  const size_t oal = half ? 16 : 4;
+  if ((grad_x && !aligned(grad_x, oal)) || (grad_y && !aligned(grad_y, oal)) || (grad_b && !aligned(grad_b, oal)))
+    return fail(KEOPS_ERR_INVALID_ARG, "gradients must be %zu-byte aligned", oal);
+  const Range ins[] = {rx, ry, rb, rg};
+  const Range outs[] = {ogx, ogy, ogb};
+  for (const Range& o : outs) {
+    for (const Range& in : ins)
+      if (overlaps(o, in)) return fail(KEOPS_ERR_INVALID_ARG, "a gradient overlaps an input");
   }
-  if (N == 0) {
-    KEOPS_HIP(keops::launch_fill(out, M * C, 0.0f, stream), "fill");
-    return ok();
-  }
-  const LowdLayout L = lowd_layout(KEOPS_OP_GAUSS_SUM, M, N, D, C, 0);
-  KEOPS_TRY(check_workspace(workspace, workspace_bytes, L.total));
-  if (overlaps(Range{workspace, L.total}, ro) || overlaps(Range{workspace, L.total}, rx) ||
-      overlaps(Range{workspace, L.total}, ry) || overlaps(Range{workspace, L.total}, rb))
-    return fail(KEOPS_ERR_INVALID_ARG, "workspace overlaps an input or the output");
+  if (overlaps(ogx, ogy) || overlaps(ogx, ogb) || overlaps(ogy, ogb))
+    return fail(KEOPS_ERR_INVALID_ARG, "gradients overlap each other");
+  if (B == 0) return ok();
+  const bool want_x = grad_x && M > 0, want_y = grad_y && N > 0, want_b = grad_b && N > 0;
+  // Empty sums: a gradient over no pairs is zero.
+  if (want_x && N == 0) KEOPS_HIP(keops::launch_fill(grad_x, B * M * D, 0.0f, stream), "fill");
+  if (want_y && M == 0) KEOPS_HIP(keops::launch_fill(grad_y, B * N * D, 0.0f, stream), "fill");
+  if (want_b && M == 0) KEOPS_HIP(keops::launch_fill(grad_b, B * N * C, 0.0f, stream), "fill");
+  if (M == 0 || N == 0) return ok();
+  const size_t need = backward_bytes(B, M, N, D, C, half, want_x, want_y, want_b);
+  KEOPS_TRY(check_workspace(workspace, workspace_bytes, need));
+  const Range rw{workspace, need};
+  for (const Range& r : {rx, ry, rb, rg, ogx, ogy, ogb})
+    if (overlaps(rw, r)) return fail(KEOPS_ERR_INVALID_ARG, "workspace overlaps an input or an output");
   char* ws = static_cast<char*>(workspace);
-  double* cols = reinterpret_cast<double*>(ws + L.cols_off);
-  float* part = reinterpret_cast<float*>(ws + L.part_off);
-  const double c2 = c2_of(sigma);
-  KEOPS_HIP(keops::launch_prep_cols(static_cast<const float*>(y), cols, N, D, c2, true, stream), "prep_cols");
-  KEOPS_HIP(keops::launch_gauss_sum_lowd(static_cast<const float*>(x), static_cast<const float*>(y), cols,
-                                         static_cast<const float*>(b), out, part, M, N, D, C, c2, L.plan, stream),
-            "gauss_sum_lowd");
+  if (half) {
+    // rows x with weights g against columns y with weights b, and the transpose of that.
+    if (want_x)
+      KEOPS_HIP(keops::launch_gauss_sum_grad_highd(x, y, g, true, b, false, grad_x, ws, B, M, N, D, C, sigma, stream),
+                "grad_x_highd");
+    if (want_y)
+      KEOPS_HIP(keops::launch_gauss_sum_grad_highd(y, x, b, false, g, true, grad_y, ws, B, N, M, D, C, sigma, stream),
+                "grad_y_highd");
+    if (want_b)
+      KEOPS_HIP(keops::launch_gauss_sum_highd(y, x, g, true, nullptr, nullptr, grad_b, ws, B, N, M, D, C, sigma,
+                                              stream),
+                "grad_b_highd");
+    return ok();
+  }
+  const float* xf = static_cast<const float*>(x);
+  const float* yf = static_cast<const float*>(y);
+  const float* bf = static_cast<const float*>(b);
+  const double s = (double)sigma;
+  const float c2f = (float)c2_of(sigma);
+  const float inv_sigma2 = (float)(1.0 / (s * s));
+  if (want_x) {
+    const LowdLayout L = lowd_layout(KEOPS_OP_GAUSS_SUM_GRAD_X, M, N, D, C, 0);
+    KEOPS_HIP(keops::launch_grad_x_lowd(xf, yf, bf, g, grad_x, reinterpret_cast<float*>(ws + L.part_off), M, N, D,
+                                        C, c2f, inv_sigma2, L.plan, stream),
+              "grad_x_lowd");
+  }
+  if (want_y) {
+    const LowdLayout L = lowd_layout(KEOPS_OP_GAUSS_SUM_GRAD_X, N, M, D, C, 0);
+    KEOPS_HIP(keops::launch_grad_x_lowd(yf, xf, g, bf, grad_y, reinterpret_cast<float*>(ws + L.part_off), N, M, D,
+                                        C, c2f, inv_sigma2, L.plan, stream),
+              "grad_y_lowd");
+  }
+  if (want_b) {
+    const LowdLayout L = lowd_layout(KEOPS_OP_GAUSS_SUM, N, M, D, C, 0);
+    double* cols = reinterpret_cast<double*>(ws + L.cols_off);
+    const double c2 = c2_of(sigma);
+    KEOPS_HIP(keops::launch_prep_cols(xf, cols, M, D, c2, true, stream), "prep_cols");
+    KEOPS_HIP(keops::launch_gauss_sum_lowd(yf, xf, cols, g, nullptr, grad_b,
+                                           reinterpret_cast<float*>(ws + L.part_off), N, M, D, C, c2, L.plan, stream),
+              "grad_b_lowd");
+  }
+  return ok();
+}
+
+int keops_diffusion_scaling(const void* x, float* s, float* q, float* d, int64_t B, int64_t N, int32_t D,
+                            float sigma, float alpha, keops_dtype dtype, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream) {
+  KEOPS_TRY(check_extent(B, "B"));
+  KEOPS_TRY(check_extent(N, "N"));
+  KEOPS_TRY(check_sigma(sigma));
+  if (!std::isfinite(alpha)) return fail(KEOPS_ERR_INVALID_ARG, "alpha must be finite (got %g)", (double)alpha);
+  KEOPS_TRY(check_gauss_family(dtype, B, D, 1, "diffusion_scaling"));
+  const bool half = (dtype == KEOPS_F16);
+  const size_t es = half ? 2 : 4;
+  const size_t n = (size_t)(B * N);
+  const Range rx{x, n * D * es}, rs{s, n * 4}, rq{q, q ? n * 4 : 0}, rd{d, d ? n * 4 : 0};
+  KEOPS_TRY(check_ptr(x, "x", half ? 16 : 4, rx.bytes));
+  KEOPS_TRY(check_ptr(s, "s", 4, rs.bytes));
+  if ((q && !aligned(q, 4)) || (d && !aligned(d, 4))) return fail(KEOPS_ERR_INVALID_ARG, "q and d must be 4-byte aligned");
+  if (overlaps(rs, rx) || overlaps(rq, rx) || overlaps(rd, rx) || overlaps(rs, rq) || overlaps(rs, rd) ||
+      overlaps(rq, rd))
+    return fail(KEOPS_ERR_INVALID_ARG, "s, q and d must not overlap x or each other");
+  if (n == 0) return ok();
+  const size_t need = diffusion_bytes(B, N, D, half);
+  KEOPS_TRY(check_workspace(workspace, workspace_bytes, need));
+  const Range rw{workspace, need};
+  if (overlaps(rw, rx) || overlaps(rw, rs) || overlaps(rw, rq) || overlaps(rw, rd))
+    return fail(KEOPS_ERR_INVALID_ARG, "workspace overlaps an input or an output");
+  char* ws = static_cast<char*>(workspace);
+  const size_t vec = keops::align_up(n * sizeof(float));
+  float* ones = reinterpret_cast<float*>(ws);
+  float* qb = q ? q : reinterpret_cast<float*>(ws + vec);
+  float* pb = reinterpret_cast<float*>(ws + 2 * vec);
+  float* db = d ? d : reinterpret_cast<float*>(ws + 3 * vec);
+  char* sub = ws + 4 * vec;
+  const size_t sub_bytes = need - 4 * vec;
+  KEOPS_HIP(keops::launch_fill(ones, (int64_t)n, 1.0f, stream), "fill");
+  // q = K 1; p = q^-alpha; d = p (K p); s = p / sqrt(d)
+  const Range none[] = {};
+  KEOPS_TRY(gauss_sum_run(x, x, ones, true, nullptr, nullptr, qb, B, N, N, D, 1, sigma, half, sub, sub_bytes, none, 0,
+                          stream));
+  KEOPS_HIP(keops::launch_pow(qb, pb, (int64_t)n, -alpha, stream), "pow");
+  KEOPS_TRY(gauss_sum_run(x, x, pb, true, pb, nullptr, db, B, N, N, D, 1, sigma, half, sub, sub_bytes, none, 0,
+                          stream));
+  KEOPS_HIP(keops::launch_div_sqrt(pb, db, s, (int64_t)n, stream), "div_sqrt");
   return ok();
 }
 
@@ -459,7 +696,7 @@ int keops_gauss_sum_grad_b(const float* x, const float* y, const float* g, float
   float* part = reinterpret_cast<float*>(ws + L.part_off);
   const double c2 = c2_of(sigma);
   KEOPS_HIP(keops::launch_prep_cols(x, cols, M, D, c2, true, stream), "prep_cols");
-  KEOPS_HIP(keops::launch_gauss_sum_lowd(y, x, cols, g, grad_b, part, N, M, D, C, c2, L.plan, stream),
+  KEOPS_HIP(keops::launch_gauss_sum_lowd(y, x, cols, g, nullptr, grad_b, part, N, M, D, C, c2, L.plan, stream),
             "grad_b_lowd");
   return ok();
 }

@@ -1,68 +1,35 @@
-// Matrix-core (fp16) batched Gauss sum for gfx950:
-//   out[t][i][c] = sum_j exp(-tau/2 ||q_i - k_j||^2) v[j][c],  tau = 1/sigma^2,
-// the Gauss sum with signed weights of "Fast Gauss Sums via Flash Attention" (its eq. (1)),
-// evaluated with the squared-norm expansion ||q - k||^2 = ||q||^2 + ||k||^2 - 2 q.k so that
-// the O(N M D) part is a dense contraction on the matrix cores.
+// Host side of the matrix-core (fp16) batched Gauss sums: column and row preparation
+// kernels, launch plans and the launchers declared in internal.h. The sweeps themselves live
+// in highd_fwd.h and highd_grad.h and are compiled once per padded feature width
+// (highd_d32.hip ... highd_d128.hip).
 //
-// Tiles are 16 queries x 32 keys on v_mfma_f32_16x16x32_f16. Per wave: QT query tiles.
-//   S^T = K Q^T + B   one MFMA per 16 keys at D = 32; the accumulator starts from
-//                     B[j] = -|k_j|^2 / 2, so S'_ij = q_i.k_j - |k_j|^2/2 comes out whole;
-//   a_ij = c S'_ij + alpha_i,  c = tau log2(e),  alpha_i = -c |q_i|^2 / 2 - m_i   (one FMA);
-//   P = 2^a rounded to fp16;  O^T += V^T P^T   one MFMA per 16 channels (K = 32 keys).
-// In the accumulator of S^T a lane holds one query and 4 keys of each 16-key half; those 8
-// values are exactly the lane's fp16 operand of the P^T product when the 32 keys of a
-// subtile are visited in the order slot_key() (V is stored pre-permuted the same way), so P
-// never moves between lanes. m_i is a running base-2 shift: set by the first subtile and
-// raised only when a subtile would produce a term above 2^kSlack (then O is rescaled).
-#include "internal.h"
+// Column preparation, general form. For a column weight vector w_j (the values b_j times an
+// optional per-column scale c_j, read as fp16 or fp32) with norm n_j = |w_j|_2 and the batch
+// maximum n_max, the sweep sees
+//   beta_j = -|k_j|^2/2 + log2(n_j / n_max) / cs      (the log clamped below at kLogFloor),
+//   w'_j   = w_j / n_j   (fp16, unit norm),
+// and the output is multiplied back by n_max. Since n_j / n_max <= 1 the tracked exponent is
+// still never positive, so the sweep's settled-row rule holds, and no fp16 value can
+// overflow whatever the magnitude of the weights. The fast path (fp16 weights, no scales)
+// copies the weights unchanged.
+#include "highd_common.h"
 
 #include <math.h>
-
-#include <type_traits>
 
 namespace keops {
 namespace {
 
-typedef _Float16 half8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
+using hd::hd_ceil_div;
+using hd::key_slot;
 
-constexpr int kWaves = 4;           // waves per workgroup
-constexpr int kStageKeys = 64;      // keys per LDS stage (32-key subtiles staged together)
-// Query tiles per wave and register budget. Measured on the B=4, 16384^2, D=C=32 workload,
-// more independent query tiles per wave beat more resident waves: the matrix cores and the
-// exp pipe overlap within a wave. Larger D or C take fewer tiles to stay within registers.
-constexpr int query_tiles(int D, int C) { return (D == 32 && C <= 32) ? 8 : 4; }
-// Channels are processed in tiles of 16; a call with C channels runs the kernel for
-// padded_channels(C) and stores the first C.
-constexpr int padded_channels(int C) { return C <= 16 ? 16 : (C <= 32 ? 32 : 64); }
-constexpr int kMinBlocks = 1;       // workgroups per CU the register budget is sized for
-constexpr int kSplitTarget = 2;     // column splits aim for this many workgroups per CU
-constexpr int kKeyPad = 256;        // key counts are padded to a multiple of this
-constexpr float kSlack = 8.0f;      // kernel values may reach 2^kSlack before a rescale
+template <typename T>
+__device__ inline float to_f32(T v) { return (float)v; }
 
-__device__ __forceinline__ float exp2_hw(float v) { return __builtin_amdgcn_exp2f(v); }
-
-// Key offset (0..31 within a subtile) held in fp16 operand slot `slot` = 8*g + s, where g is
-// the lane's 16-lane group: slots 0..3 are keys 4g..4g+3 of the first 16-key half, slots
-// 4..7 the same of the second half. key_slot() is the inverse.
-__host__ __device__ inline int slot_key(int slot) {
-  const int g = slot >> 3, s = slot & 7;
-  return 4 * g + (s & 3) + 16 * (s >> 2);
-}
-__host__ __device__ inline int key_slot(int o) {
-  const int half = o >> 4, rem = o & 15;
-  return 8 * (rem >> 2) + 4 * half + (rem & 3);
-}
-
-__host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
-inline int64_t padded_keys(int64_t N) { return ceil_div(N, kKeyPad) * kKeyPad; }
-
-// beta[t][j] = -|k_j|^2 / 2 for j < N and -inf for N <= j < Npad;
-// vp[t][j / 32][c][key_slot(j % 32)] = v[t][j][c] for c < C, zero for padded keys and for the
-// padding channels C <= c < Cp.
+// Fast path: beta_j = -|k_j|^2/2 (-inf past N); vp[t][j/32][c][key_slot(j%32)] = v[t][j][c]
+// for c < C, zero for padded keys and for the padding channels C <= c < Cp.
 __global__ void __launch_bounds__(256)
-highd_prep_kernel(const _Float16* __restrict__ k, const _Float16* __restrict__ v, float* __restrict__ beta,
-                  _Float16* __restrict__ vp, int64_t N, int64_t Npad, int D, int C, int Cp) {
+fwd_prep_kernel(const _Float16* __restrict__ k, const _Float16* __restrict__ v, float* __restrict__ beta,
+                _Float16* __restrict__ vp, int64_t N, int64_t Npad, int D, int C, int Cp) {
   const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t t = blockIdx.y;
   if (j >= Npad) return;
@@ -80,228 +47,112 @@ highd_prep_kernel(const _Float16* __restrict__ k, const _Float16* __restrict__ v
   for (int c = 0; c < Cp; ++c) dst[(int64_t)c * 32] = (j < N && c < C) ? vr[c] : (_Float16)0.0f;
 }
 
-template <int D, int C, int QT, int kMinB, int kStage, bool kPipe>
-__global__ void __launch_bounds__(256, kMinB)
-highd_kernel(const _Float16* __restrict__ q, const _Float16* __restrict__ k, const float* __restrict__ beta,
-             const _Float16* __restrict__ vp, float* __restrict__ out, int64_t M, int64_t N, int64_t Npad,
-             int64_t kps, float cs, int Cout) {
-  constexpr int DS = D / 32;     // K-steps of S^T
-  constexpr int CT = C / 16;     // 16-channel output tiles
-  constexpr int KP = D + 8;      // LDS row pitch of K, halves
-  constexpr int VP = 32 + 8;     // LDS row pitch of V^T, halves
-  constexpr int NSUB = kStage / 32;
-  constexpr int kRowsPerBlock = kWaves * QT * 16;
-  __shared__ __attribute__((aligned(16))) _Float16 sK[2][kStage][KP];
-  __shared__ __attribute__((aligned(16))) _Float16 sV[2][NSUB][C][VP];
-  __shared__ __attribute__((aligned(16))) float sB[2][kStage];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g = lane >> 4, l16 = lane & 15;
-  const int64_t bt = blockIdx.z, split = blockIdx.y;
-  const int64_t j0 = split * kps;
-  const int64_t j1 = (j0 + kps < N) ? j0 + kps : N;
-  const int64_t nstages = ceil_div(j1 - j0, kStage);
-  const int64_t row_base = (int64_t)blockIdx.x * kRowsPerBlock + wave * (QT * 16);
-
-  const _Float16* qb = q + bt * M * D;
-  const _Float16* kb = k + bt * N * D;
-  const float* bb = beta + bt * Npad;
-  const _Float16* vb = vp + bt * Npad * C;
-
-  half8 qop[QT][DS];
-  float alpha[QT], mrow[QT];
-#pragma unroll
-  for (int qt = 0; qt < QT; ++qt) {
-    int64_t i = row_base + qt * 16 + l16;
-    i = i < M ? i : M - 1;
-    float nrm = 0.0f;
-#pragma unroll
-    for (int ds = 0; ds < DS; ++ds) {
-      qop[qt][ds] = *reinterpret_cast<const half8*>(qb + i * D + 32 * ds + 8 * g);
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const float qv = (float)qop[qt][ds][s];
-        nrm = fmaf(qv, qv, nrm);
-      }
-    }
-    nrm += __shfl_xor(nrm, 16);
-    nrm += __shfl_xor(nrm, 32);
-    alpha[qt] = -0.5f * cs * nrm;
-    mrow[qt] = 0.0f;
+// |c_j w_j|_2 of column j of batch t (c = 1 when cscale is null).
+template <typename T>
+__device__ inline float weight_norm(const T* __restrict__ w, const float* __restrict__ cscale, int64_t t, int64_t j,
+                                    int64_t N, int C) {
+  const T* wr = w + (t * N + j) * C;
+  float s = 0.0f;
+  for (int c = 0; c < C; ++c) {
+    const float v = to_f32(wr[c]);
+    s = fmaf(v, v, s);
   }
-  f32x4 O[QT][CT];
-#pragma unroll
-  for (int qt = 0; qt < QT; ++qt)
-#pragma unroll
-    for (int ct = 0; ct < CT; ++ct) O[qt][ct] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  const float sc = cscale ? fabsf(cscale[t * N + j]) : 1.0f;
+  return sc * sqrtf(s);
+}
 
-  // Stage loads: global -> registers (issued before the current stage is computed) and
-  // registers -> LDS (after it), so global latency hides behind the matrix work.
-  constexpr int KCH = kStage * D / 8 / 256;       // 16-byte K chunks per thread
-  constexpr int kVChunks = NSUB * C * 4;          // 16-byte V chunks per stage
-  constexpr int VCH = (kVChunks + 255) / 256;     // ... per thread (the last round may be partial)
-  static_assert(KCH * 256 * 8 == kStage * D && kStage / 4 <= 256, "tile shapes");
-  static_assert(kVChunks % 256 == 0 || VCH == 1, "tile shapes");
-  half8 rk[KCH], rv[VCH];
-  f32x4 rb = {};
-  auto fetch = [&](int64_t st) {
-    const int64_t jb = j0 + st * kStage;
-#pragma unroll
-    for (int r = 0; r < KCH; ++r) {
-      const int c = tid + 256 * r;
-      const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-      const int64_t j = jb + row;
-      rk[r] = half8{};
-      if (j < j1) rk[r] = *reinterpret_cast<const half8*>(kb + j * D + col);
-    }
-#pragma unroll
-    for (int r = 0; r < VCH; ++r) {
-      const int c = tid + 256 * r;
-      const int t = c / (C * 4), rem = c % (C * 4), ch = rem / 4, part = (rem % 4) * 8;
-      if (c < kVChunks) rv[r] = *reinterpret_cast<const half8*>(vb + ((jb / 32 + t) * C + ch) * 32 + part);
-    }
-    if (tid < kStage / 4) rb = *reinterpret_cast<const f32x4*>(bb + jb + 4 * tid);
-  };
-  auto commit = [&](int buf) {
-#pragma unroll
-    for (int r = 0; r < KCH; ++r) {
-      const int c = tid + 256 * r;
-      *reinterpret_cast<half8*>(&sK[buf][c / (D / 8)][(c % (D / 8)) * 8]) = rk[r];
-    }
-#pragma unroll
-    for (int r = 0; r < VCH; ++r) {
-      const int c = tid + 256 * r;
-      const int t = c / (C * 4), rem = c % (C * 4);
-      if (c < kVChunks) *reinterpret_cast<half8*>(&sV[buf][t][rem / 4][(rem % 4) * 8]) = rv[r];
-    }
-    if (tid < kStage / 4) *reinterpret_cast<f32x4*>(&sB[buf][4 * tid]) = rb;
-  };
-
-  // S'^T of one 32-key subtile for every query tile: S[qt][half] holds keys 16*half + 4g + v.
-  auto scores = [&](int buf, int sub, f32x4 (&S)[QT][2]) {
-    half8 kop[2][DS];
-    f32x4 bc[2];
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-#pragma unroll
-      for (int ds = 0; ds < DS; ++ds)
-        kop[hh][ds] = *reinterpret_cast<const half8*>(&sK[buf][sub * 32 + 16 * hh + l16][32 * ds + 8 * g]);
-      bc[hh] = *reinterpret_cast<const f32x4*>(&sB[buf][sub * 32 + 16 * hh + 4 * g]);
-    }
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        S[qt][hh] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[hh][0], qop[qt][0], bc[hh], 0, 0, 0);
-#pragma unroll
-        for (int ds = 1; ds < DS; ++ds)
-          S[qt][hh] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[hh][ds], qop[qt][ds], S[qt][hh], 0, 0, 0);
-      }
-  };
-  // P = 2^(c S' + alpha) in fp16 and O^T += V^T P^T for one subtile.
-  auto accumulate = [&](int buf, int sub, const f32x4 (&S)[QT][2]) {
-    half8 vop[CT];
-#pragma unroll
-    for (int ct = 0; ct < CT; ++ct) vop[ct] = *reinterpret_cast<const half8*>(&sV[buf][sub][16 * ct + l16][8 * g]);
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
-      half8 pb;
-#pragma unroll
-      for (int s = 0; s < 8; ++s) pb[s] = (_Float16)exp2_hw(fmaf(S[qt][s >> 2][s & 3], cs, alpha[qt]));
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct) O[qt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop[ct], pb, O[qt][ct], 0, 0, 0);
-    }
-  };
-  // A row is settled once its shift m >= -kSlack: every later kernel value is then at most
-  // 2^-m <= 2^kSlack (the Gaussian exponent is never positive), so no row maximum is needed.
-  // Until then each subtile raises the shifts where a term would exceed 2^kSlack (or sets
-  // them, on the first subtile) and rescales O to match.
-  bool first = true, settled = false;
-  auto track_rows = [&](const f32x4 (&S)[QT][2]) {
-    bool all_settled = true;
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
-      float mx = fmaxf(fmaxf(fmaxf(S[qt][0][0], S[qt][0][1]), fmaxf(S[qt][0][2], S[qt][0][3])),
-                       fmaxf(fmaxf(S[qt][1][0], S[qt][1][1]), fmaxf(S[qt][1][2], S[qt][1][3])));
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float amax = fmaf(mx, cs, alpha[qt]);
-      const float delta = (first || amax > kSlack) ? amax : 0.0f;
-      alpha[qt] -= delta;
-      mrow[qt] += delta;
-      const float sc = (first || delta == 0.0f) ? 1.0f : exp2_hw(-delta);
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct) O[qt][ct] *= sc;
-      all_settled = all_settled && (mrow[qt] >= -kSlack);
-    }
-    settled = __all(all_settled);
-    first = false;
-  };
-  // One stage; both phases execute one barrier per stage, so the workgroup stays in step.
-  auto stage = [&](int64_t st, auto track) {
-    constexpr bool kTrack = decltype(track)::value;
-    const int buf = (int)(st & 1);
-    if (st + 1 < nstages) fetch(st + 1);
-    if constexpr (kTrack || !kPipe) {
-#pragma unroll
-      for (int sub = 0; sub < NSUB; ++sub) {
-        f32x4 S[QT][2];
-        scores(buf, sub, S);
-        if constexpr (kTrack) track_rows(S);
-        accumulate(buf, sub, S);
-      }
-    } else {
-      // Software-pipelined: the scores of subtile n+1 are issued to the matrix cores before
-      // the exponentials of subtile n.
-      f32x4 Sa[QT][2], Sb[QT][2];
-      scores(buf, 0, Sa);
-#pragma unroll
-      for (int sub = 0; sub < NSUB; sub += 2) {
-        if (sub + 1 < NSUB) scores(buf, sub + 1, Sb);
-        accumulate(buf, sub, Sa);
-        if (sub + 1 < NSUB) {
-          if (sub + 2 < NSUB) scores(buf, sub + 2, Sa);
-          accumulate(buf, sub + 1, Sb);
-        }
-      }
-    }
-    if (st + 1 < nstages) commit(buf ^ 1);
-    __syncthreads();
-  };
-
-  fetch(0);
-  commit(0);
+// nmax[t] = max_j |c_j w_j|_2. nmax must hold +0 before the launch (float bits of
+// non-negative values order like unsigned integers, so an integer max gives the float max).
+template <typename T>
+__global__ void __launch_bounds__(256)
+weight_norm_max_kernel(const T* __restrict__ w, const float* __restrict__ cscale, int64_t N, int C,
+                       float* __restrict__ nmax) {
+  __shared__ float red[256];
+  const int64_t t = blockIdx.y;
+  float m = 0.0f;
+  for (int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x; j < N; j += (int64_t)gridDim.x * 256)
+    m = fmaxf(m, weight_norm(w, cscale, t, j, N, C));
+  red[threadIdx.x] = m;
   __syncthreads();
-  int64_t st = 0;
-  for (; st < nstages && !settled; ++st) stage(st, std::true_type{});
-  for (; st < nstages; ++st) stage(st, std::false_type{});
+  for (int h = 128; h > 0; h >>= 1) {
+    if ((int)threadIdx.x < h) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + h]);
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) atomicMax(reinterpret_cast<unsigned int*>(nmax + t), __float_as_uint(red[0]));
+}
 
-  // Store the first Cout channels (C here is Cout rounded up to a multiple of 16).
-  const int64_t BMC = (int64_t)gridDim.z * M * Cout;
-  float* dst = out + split * BMC + bt * M * Cout;
-  const bool vec = (Cout % 4) == 0;
-#pragma unroll
-  for (int qt = 0; qt < QT; ++qt) {
-    const int64_t i = row_base + qt * 16 + l16;
-    if (i >= M) continue;
-    const float scale = exp2_hw(mrow[qt]);
-#pragma unroll
-    for (int ct = 0; ct < CT; ++ct) {
-      const int c0 = 16 * ct + 4 * g;
-      const f32x4 o = O[qt][ct] * scale;
-      if (vec && c0 + 4 <= Cout) {
-        *reinterpret_cast<f32x4*>(dst + i * Cout + c0) = o;
-      } else {
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-          if (c0 + v < Cout) dst[i * Cout + c0 + v] = o[v];
-      }
+// General column preparation (see the file comment). kGrad selects the table layout:
+//   forward:  wp[t][j/32][c][key_slot(j%32)] for c < Cw (key-permuted, the A operand of O^T)
+//   gradient: wp[t][j][c] for c < Cw (row-major, the A operand of dP^T), plus
+//             yp[t][j/32][ch][key_slot(j%32)] = k[t][j][ch] for ch < D, 1 at ch = Dp, else 0.
+template <typename T, bool kGrad>
+__global__ void __launch_bounds__(256)
+col_prep_kernel(const _Float16* __restrict__ k, const T* __restrict__ w, const float* __restrict__ cscale,
+                const float* __restrict__ nmax, float* __restrict__ beta, _Float16* __restrict__ wp,
+                _Float16* __restrict__ yp, int64_t N, int64_t Npad, int D, int Dp, int C, int Cw, float cs) {
+  const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t t = blockIdx.y;
+  if (j >= Npad) return;
+  const bool live = j < N;
+  const _Float16* kr = k + (t * N + j) * D;
+  const T* wr = w + (t * N + j) * C;
+  float bj = -INFINITY, inv = 0.0f, sc = 1.0f;
+  if (live) {
+    float s = 0.0f;
+    for (int d = 0; d < D; ++d) {
+      const float kv = (float)kr[d];
+      s = fmaf(kv, kv, s);
     }
+    const float n = weight_norm(w, cscale, t, j, N, C);
+    const float nm = nmax[t];
+    const float ratio = nm > 0.0f ? n / nm : 0.0f;
+    const float lw = fmaxf(log2f(ratio), hd::kLogFloor);
+    bj = -0.5f * s + lw / cs;
+    inv = n > 0.0f ? 1.0f / n : 0.0f;
+    sc = cscale ? cscale[t * N + j] : 1.0f;
+  }
+  beta[t * Npad + j] = bj;
+  if constexpr (kGrad) {
+    _Float16* dst = wp + (t * Npad + j) * Cw;
+    for (int c = 0; c < Cw; ++c) dst[c] = (live && c < C) ? (_Float16)(to_f32(wr[c]) * sc * inv) : (_Float16)0.0f;
+    const int YC = Dp + 16;
+    _Float16* yd = yp + (t * Npad + (j / 32) * 32) * YC + key_slot((int)(j % 32));
+    for (int ch = 0; ch < YC; ++ch) {
+      _Float16 v = (_Float16)0.0f;
+      if (live && ch < D) v = kr[ch];
+      if (live && ch == Dp) v = (_Float16)1.0f;
+      yd[(int64_t)ch * 32] = v;
+    }
+  } else {
+    _Float16* dst = wp + (t * Npad + (j / 32) * 32) * Cw + key_slot((int)(j % 32));
+    for (int c = 0; c < Cw; ++c)
+      dst[(int64_t)c * 32] = (live && c < C) ? (_Float16)(to_f32(wr[c]) * sc * inv) : (_Float16)0.0f;
   }
 }
 
+// Row weights of the gradient sweep: ap[t][i][c] = a_i[c] / |a_i| (zero past C), rho = |a_i|.
+template <typename T>
 __global__ void __launch_bounds__(256)
-highd_combine_kernel(const float* __restrict__ partial, float* __restrict__ out, int64_t n, int64_t S) {
+row_prep_kernel(const T* __restrict__ a, _Float16* __restrict__ ap, float* __restrict__ rho, int64_t M, int C,
+                int Ck) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t t = blockIdx.y;
+  if (i >= M) return;
+  const T* ar = a + (t * M + i) * C;
+  float s = 0.0f;
+  for (int c = 0; c < C; ++c) {
+    const float v = to_f32(ar[c]);
+    s = fmaf(v, v, s);
+  }
+  const float n = sqrtf(s);
+  const float inv = n > 0.0f ? 1.0f / n : 0.0f;
+  rho[t * M + i] = n;
+  _Float16* dst = ap + (t * M + i) * Ck;
+  for (int c = 0; c < Ck; ++c) dst[c] = c < C ? (_Float16)(to_f32(ar[c]) * inv) : (_Float16)0.0f;
+}
+
+__global__ void __launch_bounds__(256)
+combine_kernel(const float* __restrict__ partial, float* __restrict__ out, int64_t n, int64_t S) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= n) return;
   float s = 0.0f;
@@ -309,78 +160,250 @@ highd_combine_kernel(const float* __restrict__ partial, float* __restrict__ out,
   out[i] = s;
 }
 
-struct HighdPlan {
+// ---- plans --------------------------------------------------------------------------------
+struct Split {
   int64_t Npad, row_blocks, splits, kps;
-  size_t beta_bytes, vp_bytes, part_bytes, total;
 };
 
-HighdPlan highd_plan(int64_t B, int64_t M, int64_t N, int D, int C, int num_cus) {
-  HighdPlan p;
-  const int Cp = padded_channels(C);
-  p.Npad = padded_keys(N);
-  p.row_blocks = ceil_div(M, kWaves * query_tiles(D, Cp) * 16);
+// Column splits: enough workgroups for kSplitTarget per CU, each split >= 4 * kKeyPad keys and
+// a multiple of kKeyPad (so split boundaries fall on stage boundaries).
+Split plan_split(int64_t B, int64_t M, int64_t N, int rows_per_block, int num_cus) {
+  Split p;
+  p.Npad = hd::padded_keys(N);
+  p.row_blocks = hd_ceil_div(M, rows_per_block);
   const int64_t blocks = p.row_blocks * B;
-  const int64_t target = (int64_t)num_cus * kSplitTarget;
-  int64_t S = blocks < target ? ceil_div(target, blocks) : 1;
-  const int64_t max_split = p.Npad / (4 * kKeyPad) > 1 ? p.Npad / (4 * kKeyPad) : 1;
+  const int64_t target = (int64_t)num_cus * hd::kSplitTarget;
+  int64_t S = blocks < target ? hd_ceil_div(target, blocks) : 1;
+  const int64_t max_split = p.Npad / (4 * hd::kKeyPad) > 1 ? p.Npad / (4 * hd::kKeyPad) : 1;
   if (S > max_split) S = max_split;
-  int64_t kps = ceil_div(ceil_div(N, S), kKeyPad) * kKeyPad;
-  S = ceil_div(N, kps);
-  p.splits = S;
+  const int64_t kps = hd_ceil_div(hd_ceil_div(N, S), hd::kKeyPad) * hd::kKeyPad;
+  p.splits = hd_ceil_div(N, kps);
   p.kps = kps;
-  p.beta_bytes = align_up((size_t)B * p.Npad * sizeof(float));
-  p.vp_bytes = align_up((size_t)B * p.Npad * Cp * sizeof(_Float16));
-  p.part_bytes = S > 1 ? align_up((size_t)S * B * M * C * sizeof(float)) : 0;
-  p.total = p.beta_bytes + p.vp_bytes + p.part_bytes;
   return p;
+}
+
+// Workspace carving: sections in order, each aligned to kAlign.
+struct Carve {
+  size_t off = 0;
+  size_t take(size_t bytes) {
+    const size_t at = off;
+    off += align_up(bytes);
+    return at;
+  }
+};
+
+struct FwdLayout {
+  Split sp;
+  size_t nmax, beta, vp, part, total;
+};
+
+FwdLayout fwd_layout(int64_t B, int64_t M, int64_t N, int D, int C, bool general, int num_cus) {
+  FwdLayout L;
+  const int Cp = hd::padded_channels(C);
+  L.sp = plan_split(B, M, N, hd::kWaves * hd::fwd_query_tiles(hd::padded_features(D), Cp) * 16, num_cus);
+  Carve c;
+  L.nmax = c.take(general ? (size_t)B * sizeof(float) : 0);
+  L.beta = c.take((size_t)B * L.sp.Npad * sizeof(float));
+  L.vp = c.take((size_t)B * L.sp.Npad * Cp * sizeof(_Float16));
+  L.part = c.take(L.sp.splits > 1 ? (size_t)L.sp.splits * B * M * C * sizeof(float) : 0);
+  L.total = c.off;
+  return L;
+}
+
+struct GradLayout {
+  Split sp;
+  size_t nmax, beta, bvp, yp, ap, rho, part, total;
+};
+
+GradLayout grad_layout(int64_t B, int64_t M, int64_t N, int D, int C, int num_cus) {
+  GradLayout L;
+  const int Dp = hd::padded_features(D), Ck = hd::padded_k_channels(C);
+  L.sp = plan_split(B, M, N, hd::kWaves * hd::grad_query_tiles(Dp) * 16, num_cus);
+  Carve c;
+  L.nmax = c.take((size_t)B * sizeof(float));
+  L.beta = c.take((size_t)B * L.sp.Npad * sizeof(float));
+  L.bvp = c.take((size_t)B * L.sp.Npad * Ck * sizeof(_Float16));
+  L.yp = c.take((size_t)B * L.sp.Npad * (Dp + 16) * sizeof(_Float16));
+  L.ap = c.take((size_t)B * M * Ck * sizeof(_Float16));
+  L.rho = c.take((size_t)B * M * sizeof(float));
+  L.part = c.take(L.sp.splits > 1 ? (size_t)L.sp.splits * B * M * D * sizeof(float) : 0);
+  L.total = c.off;
+  return L;
+}
+
+float cs_of(float sigma) {
+  const double s = (double)sigma;
+  return (float)(1.4426950408889634 / (s * s));  // tau log2(e)
+}
+
+hipError_t fwd_dispatch(const hd::FwdArgs& a) {
+  switch (hd::padded_features(a.D)) {
+    case 32: return hd::fwd_launch<32>(a);
+    case 64: return hd::fwd_launch<64>(a);
+    case 96: return hd::fwd_launch<96>(a);
+    case 128: return hd::fwd_launch<128>(a);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t grad_dispatch(const hd::GradArgs& a) {
+  switch (hd::padded_features(a.D)) {
+    case 32: return hd::grad_launch<32>(a);
+    case 64: return hd::grad_launch<64>(a);
+    case 96: return hd::grad_launch<96>(a);
+    case 128: return hd::grad_launch<128>(a);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t combine(const float* part, float* out, int64_t n, int64_t S, hipStream_t s) {
+  combine_kernel<<<(unsigned)hd_ceil_div(n, 256), 256, 0, s>>>(part, out, n, S);
+  return hipGetLastError();
+}
+
+// nmax[t] = max_j |c_j w_j| for every batch t.
+template <typename T>
+hipError_t weight_norm_max(const T* w, const float* cscale, float* nmax, int64_t B, int64_t N, int C, hipStream_t s) {
+  hipError_t e = launch_fill(nmax, B, 0.0f, s);
+  if (e != hipSuccess) return e;
+  int64_t blocks = hd_ceil_div(N, 256);
+  if (blocks > 256) blocks = 256;
+  weight_norm_max_kernel<T><<<dim3((unsigned)blocks, (unsigned)B), 256, 0, s>>>(w, cscale, N, C, nmax);
+  return hipGetLastError();
 }
 
 }  // namespace
 
-bool highd_supported(int D, int C) { return (D == 32 || D == 64) && C >= 1 && C <= 64; }
+bool highd_supported(int D, int C) { return D >= 16 && D <= 128 && D % 16 == 0 && C >= 1 && C <= 64; }
 
-size_t highd_workspace_bytes(int64_t B, int64_t M, int64_t N, int D, int C) {
+size_t highd_workspace_bytes(int64_t B, int64_t M, int64_t N, int D, int C, bool general) {
   if (B == 0 || M == 0 || N == 0) return 0;
-  return highd_plan(B, M, N, D, C, device_cus()).total;
+  return fwd_layout(B, M, N, D, C, general, device_cus()).total;
 }
 
-hipError_t launch_gauss_sum_highd(const void* x, const void* y, const void* b, float* out, void* workspace,
-                                  int64_t B, int64_t M, int64_t N, int D, int C, float sigma, bool bf16,
-                                  hipStream_t s) {
-  if (bf16) return hipErrorNotSupported;
-  const HighdPlan p = highd_plan(B, M, N, D, C, device_cus());
+size_t highd_grad_workspace_bytes(int64_t B, int64_t M, int64_t N, int D, int C) {
+  if (B == 0 || M == 0 || N == 0) return 0;
+  return grad_layout(B, M, N, D, C, device_cus()).total;
+}
+
+hipError_t launch_gauss_sum_highd(const void* x, const void* y, const void* b, bool b_f32, const float* rscale,
+                                  const float* cscale, float* out, void* workspace, int64_t B, int64_t M, int64_t N,
+                                  int D, int C, float sigma, hipStream_t s) {
+  const bool general = b_f32 || cscale != nullptr;
+  const FwdLayout L = fwd_layout(B, M, N, D, C, general, device_cus());
   char* ws = static_cast<char*>(workspace);
-  float* beta = reinterpret_cast<float*>(ws);
-  _Float16* vpm = reinterpret_cast<_Float16*>(ws + p.beta_bytes);
-  float* part = reinterpret_cast<float*>(ws + p.beta_bytes + p.vp_bytes);
-  const _Float16* q = static_cast<const _Float16*>(x);
+  float* nmax = reinterpret_cast<float*>(ws + L.nmax);
+  float* beta = reinterpret_cast<float*>(ws + L.beta);
+  _Float16* vp = reinterpret_cast<_Float16*>(ws + L.vp);
+  float* part = reinterpret_cast<float*>(ws + L.part);
   const _Float16* k = static_cast<const _Float16*>(y);
-  const _Float16* v = static_cast<const _Float16*>(b);
-  const double sd = (double)sigma;
-  const float cs = (float)(1.4426950408889634 / (sd * sd));  // tau log2(e)
-  const int Cp = padded_channels(C);
-  highd_prep_kernel<<<dim3((unsigned)ceil_div(p.Npad, 256), (unsigned)B), 256, 0, s>>>(k, v, beta, vpm, N, p.Npad, D, C,
-                                                                                       Cp);
-  hipError_t e = hipGetLastError();
+  const float cs = cs_of(sigma);
+  const int Cp = hd::padded_channels(C);
+  const dim3 pgrid((unsigned)hd_ceil_div(L.sp.Npad, 256), (unsigned)B);
+  hipError_t e;
+  if (!general) {
+    fwd_prep_kernel<<<pgrid, 256, 0, s>>>(k, static_cast<const _Float16*>(b), beta, vp, N, L.sp.Npad, D, C, Cp);
+    e = hipGetLastError();
+  } else if (b_f32) {
+    const float* w = static_cast<const float*>(b);
+    e = weight_norm_max(w, cscale, nmax, B, N, C, s);
+    if (e != hipSuccess) return e;
+    col_prep_kernel<float, false><<<pgrid, 256, 0, s>>>(k, w, cscale, nmax, beta, vp, nullptr, N, L.sp.Npad, D, 0, C,
+                                                        Cp, cs);
+    e = hipGetLastError();
+  } else {
+    const _Float16* w = static_cast<const _Float16*>(b);
+    e = weight_norm_max(w, cscale, nmax, B, N, C, s);
+    if (e != hipSuccess) return e;
+    col_prep_kernel<_Float16, false><<<pgrid, 256, 0, s>>>(k, w, cscale, nmax, beta, vp, nullptr, N, L.sp.Npad, D, 0,
+                                                           C, Cp, cs);
+    e = hipGetLastError();
+  }
   if (e != hipSuccess) return e;
-  float* dst = p.splits > 1 ? part : out;
-  const dim3 grid((unsigned)p.row_blocks, (unsigned)p.splits, (unsigned)B);
-#define KEOPS_HD(Dv, Cv)                                                                          \
-  highd_kernel<Dv, Cv, query_tiles(Dv, Cv), kMinBlocks, kStageKeys, false><<<grid, 256, 0, s>>>( \
-      q, k, beta, vpm, dst, M, N, p.Npad, p.kps, cs, C)
-  if (D == 32 && Cp == 16) KEOPS_HD(32, 16);
-  else if (D == 32 && Cp == 32) KEOPS_HD(32, 32);
-  else if (D == 32 && Cp == 64) KEOPS_HD(32, 64);
-  else if (D == 64 && Cp == 16) KEOPS_HD(64, 16);
-  else if (D == 64 && Cp == 32) KEOPS_HD(64, 32);
-  else if (D == 64 && Cp == 64) KEOPS_HD(64, 64);
-  else return hipErrorInvalidValue;
-#undef KEOPS_HD
+  hd::FwdArgs a;
+  a.q = static_cast<const _Float16*>(x);
+  a.k = k;
+  a.beta = beta;
+  a.vp = vp;
+  a.out = L.sp.splits > 1 ? part : out;
+  a.rscale = rscale;
+  a.oscale = general ? nmax : nullptr;
+  a.M = M;
+  a.N = N;
+  a.Npad = L.sp.Npad;
+  a.kps = L.sp.kps;
+  a.cs = cs;
+  a.D = D;
+  a.C = C;
+  a.grid = dim3((unsigned)L.sp.row_blocks, (unsigned)L.sp.splits, (unsigned)B);
+  a.stream = s;
+  e = fwd_dispatch(a);
+  if (e != hipSuccess || L.sp.splits == 1) return e;
+  return combine(part, out, B * M * C, L.sp.splits, s);
+}
+
+hipError_t launch_gauss_sum_grad_highd(const void* x, const void* y, const void* a, bool a_f32, const void* bv,
+                                       bool bv_f32, float* out, void* workspace, int64_t B, int64_t M, int64_t N,
+                                       int D, int C, float sigma, hipStream_t s) {
+  const GradLayout L = grad_layout(B, M, N, D, C, device_cus());
+  char* ws = static_cast<char*>(workspace);
+  float* nmax = reinterpret_cast<float*>(ws + L.nmax);
+  float* beta = reinterpret_cast<float*>(ws + L.beta);
+  _Float16* bvp = reinterpret_cast<_Float16*>(ws + L.bvp);
+  _Float16* yp = reinterpret_cast<_Float16*>(ws + L.yp);
+  _Float16* ap = reinterpret_cast<_Float16*>(ws + L.ap);
+  float* rho = reinterpret_cast<float*>(ws + L.rho);
+  float* part = reinterpret_cast<float*>(ws + L.part);
+  const _Float16* k = static_cast<const _Float16*>(y);
+  const float cs = cs_of(sigma);
+  const int Dp = hd::padded_features(D), Ck = hd::padded_k_channels(C);
+  const dim3 pgrid((unsigned)hd_ceil_div(L.sp.Npad, 256), (unsigned)B);
+  hipError_t e;
+  if (bv_f32) {
+    const float* w = static_cast<const float*>(bv);
+    e = weight_norm_max(w, nullptr, nmax, B, N, C, s);
+    if (e != hipSuccess) return e;
+    col_prep_kernel<float, true><<<pgrid, 256, 0, s>>>(k, w, nullptr, nmax, beta, bvp, yp, N, L.sp.Npad, D, Dp, C,
+                                                       Ck, cs);
+  } else {
+    const _Float16* w = static_cast<const _Float16*>(bv);
+    e = weight_norm_max(w, nullptr, nmax, B, N, C, s);
+    if (e != hipSuccess) return e;
+    col_prep_kernel<_Float16, true><<<pgrid, 256, 0, s>>>(k, w, nullptr, nmax, beta, bvp, yp, N, L.sp.Npad, D, Dp, C,
+                                                          Ck, cs);
+  }
   e = hipGetLastError();
-  if (e != hipSuccess || p.splits == 1) return e;
-  const int64_t n = B * M * C;
-  highd_combine_kernel<<<(unsigned)ceil_div(n, 256), 256, 0, s>>>(part, out, n, p.splits);
-  return hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 rgrid((unsigned)hd_ceil_div(M, 256), (unsigned)B);
+  if (a_f32)
+    row_prep_kernel<float><<<rgrid, 256, 0, s>>>(static_cast<const float*>(a), ap, rho, M, C, Ck);
+  else
+    row_prep_kernel<_Float16><<<rgrid, 256, 0, s>>>(static_cast<const _Float16*>(a), ap, rho, M, C, Ck);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hd::GradArgs g;
+  g.x = static_cast<const _Float16*>(x);
+  g.y = k;
+  g.ap = ap;
+  g.rho = rho;
+  g.beta = beta;
+  g.bvp = bvp;
+  g.yp = yp;
+  g.oscale = nmax;
+  g.out = L.sp.splits > 1 ? part : out;
+  g.M = M;
+  g.N = N;
+  g.Npad = L.sp.Npad;
+  g.kps = L.sp.kps;
+  g.cs = cs;
+  g.tau = (float)(1.0 / ((double)sigma * (double)sigma));
+  g.D = D;
+  g.Ck = Ck;
+  g.grid = dim3((unsigned)L.sp.row_blocks, (unsigned)L.sp.splits, (unsigned)B);
+  g.stream = s;
+  e = grad_dispatch(g);
+  if (e != hipSuccess || L.sp.splits == 1) return e;
+  return combine(part, out, B * M * D, L.sp.splits, s);
 }
 
 }  // namespace keops

@@ -1,0 +1,10 @@
+// Matrix-core sweeps for feature widths padded to 96 (see highd_fwd.h and highd_grad.h).
+#include "highd_fwd.h"
+#include "highd_grad.h"
+
+namespace keops {
+namespace hd {
+template hipError_t fwd_launch<96>(const FwdArgs&);
+template hipError_t grad_launch<96>(const GradArgs&);
+}  // namespace hd
+}  // namespace keops

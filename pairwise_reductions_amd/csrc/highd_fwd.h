@@ -1,0 +1,253 @@
+// Forward matrix-core Gauss sum ("Fast Gauss Sums via Flash Attention", eq. (1), computed
+// from the squared-norm expansion ||q - k||^2 = ||q||^2 + ||k||^2 - 2 q.k, so the O(M N D)
+// part is a dense contraction on the matrix cores). Included by the per-feature-width
+// sources, each of which instantiates fwd_launch<Dp> for one padded D.
+//
+// Tiles are 16 queries x 32 keys on v_mfma_f32_16x16x32_f16. Per wave: QT query tiles.
+//   S^T = K Q^T + B   one MFMA per 16 keys and 32 features; the accumulator starts from
+//                     B[j] = beta_j, so S'_ij = q_i.k_j + beta_j comes out whole;
+//   a_ij = cs S'_ij + alpha_i,  alpha_i = -cs |q_i|^2 / 2 - m_i   (one FMA);
+//   P = 2^a rounded to fp16;  O^T += V^T P^T   one MFMA per 16 channels (K = 32 keys).
+// P never moves between lanes (the key order of slot_key()); m_i is a running base-2 shift,
+// set by the first subtile and raised only when a subtile would produce a term above
+// 2^kSlack (then O is rescaled).
+#pragma once
+
+#include "highd_common.h"
+
+#include <math.h>
+
+#include <type_traits>
+
+namespace keops {
+namespace hd {
+namespace {
+
+template <int D, int C, int QT>
+__global__ void __launch_bounds__(256, 1)
+fwd_kernel(const _Float16* __restrict__ q, const _Float16* __restrict__ k, const float* __restrict__ beta,
+           const _Float16* __restrict__ vp, float* __restrict__ out, const float* __restrict__ rscale,
+           const float* __restrict__ oscale, int64_t M, int64_t N, int64_t Npad, int64_t kps, float cs, int Din,
+           int Cout) {
+  constexpr int kStage = kStageKeys;
+  constexpr int DS = D / 32;     // K-steps of S^T
+  constexpr int CT = C / 16;     // 16-channel output tiles
+  constexpr int KP = D + 8;      // LDS row pitch of K, halves
+  constexpr int VP = 32 + 8;     // LDS row pitch of V^T, halves
+  constexpr int NSUB = kStage / 32;
+  constexpr int kRowsPerBlock = kWaves * QT * 16;
+  __shared__ __attribute__((aligned(16))) _Float16 sK[2][kStage][KP];
+  __shared__ __attribute__((aligned(16))) _Float16 sV[2][NSUB][C][VP];
+  __shared__ __attribute__((aligned(16))) float sB[2][kStage];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, l16 = lane & 15;
+  const int64_t bt = blockIdx.z, split = blockIdx.y;
+  const int64_t j0 = split * kps;
+  const int64_t j1 = (j0 + kps < N) ? j0 + kps : N;
+  const int64_t nstages = hd_ceil_div(j1 - j0, kStage);
+  const int64_t row_base = (int64_t)blockIdx.x * kRowsPerBlock + wave * (QT * 16);
+
+  // D is Din rounded up to a multiple of 32; the features Din <= d < D read as zero.
+  const _Float16* qb = q + bt * M * Din;
+  const _Float16* kb = k + bt * N * Din;
+  const float* bb = beta + bt * Npad;
+  const _Float16* vb = vp + bt * Npad * C;
+
+  half8 qop[QT][DS];
+  float alpha[QT], mrow[QT];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    int64_t i = row_base + qt * 16 + l16;
+    i = i < M ? i : M - 1;
+    float nrm = 0.0f;
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) {
+      const int col = 32 * ds + 8 * g;
+      qop[qt][ds] = half8{};
+      if (col < Din) qop[qt][ds] = *reinterpret_cast<const half8*>(qb + i * Din + col);
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const float qv = (float)qop[qt][ds][s];
+        nrm = fmaf(qv, qv, nrm);
+      }
+    }
+    nrm += __shfl_xor(nrm, 16);
+    nrm += __shfl_xor(nrm, 32);
+    alpha[qt] = -0.5f * cs * nrm;
+    mrow[qt] = 0.0f;
+  }
+  f32x4 O[QT][CT];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) O[qt][ct] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  // Stage loads: global -> registers (issued before the current stage is computed) and
+  // registers -> LDS (after it), so global latency hides behind the matrix work.
+  constexpr int KCH = kStage * D / 8 / 256;       // 16-byte K chunks per thread
+  constexpr int kVChunks = NSUB * C * 4;          // 16-byte V chunks per stage
+  constexpr int VCH = (kVChunks + 255) / 256;     // ... per thread (the last round may be partial)
+  static_assert(KCH * 256 * 8 == kStage * D && kStage / 4 <= 256, "tile shapes");
+  static_assert(kVChunks % 256 == 0 || VCH == 1, "tile shapes");
+  half8 rk[KCH], rv[VCH];
+  f32x4 rb = {};
+  auto fetch = [&](int64_t st) {
+    const int64_t jb = j0 + st * kStage;
+#pragma unroll
+    for (int r = 0; r < KCH; ++r) {
+      const int c = tid + 256 * r;
+      const int row = c / (D / 8), col = (c % (D / 8)) * 8;
+      const int64_t j = jb + row;
+      rk[r] = half8{};
+      if (j < j1 && col < Din) rk[r] = *reinterpret_cast<const half8*>(kb + j * Din + col);
+    }
+#pragma unroll
+    for (int r = 0; r < VCH; ++r) {
+      const int c = tid + 256 * r;
+      const int t = c / (C * 4), rem = c % (C * 4), ch = rem / 4, part = (rem % 4) * 8;
+      if (c < kVChunks) rv[r] = *reinterpret_cast<const half8*>(vb + ((jb / 32 + t) * C + ch) * 32 + part);
+    }
+    if (tid < kStage / 4) rb = *reinterpret_cast<const f32x4*>(bb + jb + 4 * tid);
+  };
+  auto commit = [&](int buf) {
+#pragma unroll
+    for (int r = 0; r < KCH; ++r) {
+      const int c = tid + 256 * r;
+      *reinterpret_cast<half8*>(&sK[buf][c / (D / 8)][(c % (D / 8)) * 8]) = rk[r];
+    }
+#pragma unroll
+    for (int r = 0; r < VCH; ++r) {
+      const int c = tid + 256 * r;
+      const int t = c / (C * 4), rem = c % (C * 4);
+      if (c < kVChunks) *reinterpret_cast<half8*>(&sV[buf][t][rem / 4][(rem % 4) * 8]) = rv[r];
+    }
+    if (tid < kStage / 4) *reinterpret_cast<f32x4*>(&sB[buf][4 * tid]) = rb;
+  };
+
+  // S'^T of one 32-key subtile for every query tile: S[qt][half] holds keys 16*half + 4g + v.
+  auto scores = [&](int buf, int sub, f32x4 (&S)[QT][2]) {
+    half8 kop[2][DS];
+    f32x4 bc[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+      for (int ds = 0; ds < DS; ++ds)
+        kop[hh][ds] = *reinterpret_cast<const half8*>(&sK[buf][sub * 32 + 16 * hh + l16][32 * ds + 8 * g]);
+      bc[hh] = *reinterpret_cast<const f32x4*>(&sB[buf][sub * 32 + 16 * hh + 4 * g]);
+    }
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        S[qt][hh] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[hh][0], qop[qt][0], bc[hh], 0, 0, 0);
+#pragma unroll
+        for (int ds = 1; ds < DS; ++ds)
+          S[qt][hh] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[hh][ds], qop[qt][ds], S[qt][hh], 0, 0, 0);
+      }
+  };
+  // P = 2^(c S' + alpha) in fp16 and O^T += V^T P^T for one subtile.
+  auto accumulate = [&](int buf, int sub, const f32x4 (&S)[QT][2]) {
+    half8 vop[CT];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) vop[ct] = *reinterpret_cast<const half8*>(&sV[buf][sub][16 * ct + l16][8 * g]);
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      half8 pb;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) pb[s] = (_Float16)exp2_hw(fmaf(S[qt][s >> 2][s & 3], cs, alpha[qt]));
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) O[qt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop[ct], pb, O[qt][ct], 0, 0, 0);
+    }
+  };
+  // A row is settled once its shift m >= -kSlack: every later kernel value is then at most
+  // 2^-m <= 2^kSlack (the Gaussian exponent is never positive), so no row maximum is needed.
+  // Until then each subtile raises the shifts where a term would exceed 2^kSlack (or sets
+  // them, on the first subtile) and rescales O to match.
+  bool first = true, settled = false;
+  auto track_rows = [&](const f32x4 (&S)[QT][2]) {
+    bool all_settled = true;
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      float mx = fmaxf(fmaxf(fmaxf(S[qt][0][0], S[qt][0][1]), fmaxf(S[qt][0][2], S[qt][0][3])),
+                       fmaxf(fmaxf(S[qt][1][0], S[qt][1][1]), fmaxf(S[qt][1][2], S[qt][1][3])));
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float amax = fmaf(mx, cs, alpha[qt]);
+      const float delta = (first || amax > kSlack) ? amax : 0.0f;
+      alpha[qt] -= delta;
+      mrow[qt] += delta;
+      const float sc = (first || delta == 0.0f) ? 1.0f : exp2_hw(-delta);
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) O[qt][ct] *= sc;
+      all_settled = all_settled && (mrow[qt] >= -kSlack);
+    }
+    settled = __all(all_settled);
+    first = false;
+  };
+  // One stage; both phases execute one barrier per stage, so the workgroup stays in step.
+  auto stage = [&](int64_t st, auto track) {
+    constexpr bool kTrack = decltype(track)::value;
+    const int buf = (int)(st & 1);
+    if (st + 1 < nstages) fetch(st + 1);
+#pragma unroll
+    for (int sub = 0; sub < NSUB; ++sub) {
+      f32x4 S[QT][2];
+      scores(buf, sub, S);
+      if constexpr (kTrack) track_rows(S);
+      accumulate(buf, sub, S);
+    }
+    if (st + 1 < nstages) commit(buf ^ 1);
+    __syncthreads();
+  };
+
+  fetch(0);
+  commit(0);
+  __syncthreads();
+  int64_t st = 0;
+  for (; st < nstages && !settled; ++st) stage(st, std::true_type{});
+  for (; st < nstages; ++st) stage(st, std::false_type{});
+
+  // Store the first Cout channels (C here is Cout rounded up to a multiple of 16).
+  const int64_t BMC = (int64_t)gridDim.z * M * Cout;
+  float* dst = out + split * BMC + bt * M * Cout;
+  const bool vec = (Cout % 4) == 0;
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    const int64_t i = row_base + qt * 16 + l16;
+    if (i >= M) continue;
+    float scale = exp2_hw(mrow[qt]);
+    if (rscale) scale *= rscale[bt * M + i];
+    if (oscale) scale *= oscale[bt];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      const int c0 = 16 * ct + 4 * g;
+      const f32x4 o = O[qt][ct] * scale;
+      if (vec && c0 + 4 <= Cout) {
+        *reinterpret_cast<f32x4*>(dst + i * Cout + c0) = o;
+      } else {
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          if (c0 + v < Cout) dst[i * Cout + c0 + v] = o[v];
+      }
+    }
+  }
+}
+
+}  // namespace
+
+template <int Dp>
+hipError_t fwd_launch(const FwdArgs& a) {
+  const int Cp = padded_channels(a.C);
+#define KEOPS_FWD(Cv)                                                                              \
+  fwd_kernel<Dp, Cv, fwd_query_tiles(Dp, Cv)><<<a.grid, 256, 0, a.stream>>>(                      \
+      a.q, a.k, a.beta, a.vp, a.out, a.rscale, a.oscale, a.M, a.N, a.Npad, a.kps, a.cs, a.D, a.C)
+  if (Cp == 16) KEOPS_FWD(16);
+  else if (Cp == 32) KEOPS_FWD(32);
+  else KEOPS_FWD(64);
+#undef KEOPS_FWD
+  return hipGetLastError();
+}
+
+}  // namespace hd
+}  // namespace keops

@@ -38,9 +38,10 @@ size_t partial_bytes_per_row(int op, int D, int C, int K);
 // cols[j] = (y_j - o, -c2 |y_j - o|^2) in float64, o = y_0 when `centre`, else o = 0.
 hipError_t launch_prep_cols(const float* y, double* cols, int64_t N, int D, double c2,
                             bool centre, hipStream_t s);
+// out[i][c] = rscale[i] * sum_j 2^{-c2 |x_i - y_j|^2} b[j][c] (rscale may be null).
 hipError_t launch_gauss_sum_lowd(const float* x, const float* y, const double* cols,
-                                 const float* b, float* out, float* partial, int64_t M,
-                                 int64_t N, int D, int C, double c2, const Plan& p,
+                                 const float* b, const float* rscale, float* out, float* partial,
+                                 int64_t M, int64_t N, int D, int C, double c2, const Plan& p,
                                  hipStream_t s);
 hipError_t launch_lse_lowd(const float* x, const float* y, const double* cols, float* out,
                            double* partial, int64_t M, int64_t N, int D, double c2,
@@ -55,12 +56,28 @@ hipError_t launch_grad_x_lowd(const float* x, const float* y, const float* b, co
                               float* grad, float* partial, int64_t M, int64_t N, int D, int C,
                               float c2f, float inv_sigma2, const Plan& p, hipStream_t s);
 hipError_t launch_fill(float* out, int64_t n, float value, hipStream_t s);
+// Element-wise steps: out[j][c] = scale[j] b[j][c]; out = in^e; out = p / sqrt(d).
+hipError_t launch_scale_rows(const float* b, const float* scale, float* out, int64_t N, int C,
+                             hipStream_t s);
+hipError_t launch_pow(const float* in, float* out, int64_t n, float e, hipStream_t s);
+hipError_t launch_div_sqrt(const float* p, const float* d, float* out, int64_t n, hipStream_t s);
 
-// Matrix-core (fp16 / bf16) batched Gauss sum.
+// Matrix-core (fp16) batched Gauss sums. x, y: [B][M|N][D] fp16.
 bool highd_supported(int D, int C);
-size_t highd_workspace_bytes(int64_t B, int64_t M, int64_t N, int D, int C);
-hipError_t launch_gauss_sum_highd(const void* x, const void* y, const void* b, float* out,
-                                  void* workspace, int64_t B, int64_t M, int64_t N, int D,
-                                  int C, float sigma, bool bf16, hipStream_t s);
+// out[t][i][c] = rscale[t][i] * sum_j Phi_ij cscale[t][j] b[t][j][c]; b is fp16 or (b_f32)
+// fp32; rscale and cscale may be null. `general` (b_f32 or a cscale) selects the
+// weight-normalising column preparation, which needs a slightly larger workspace.
+size_t highd_workspace_bytes(int64_t B, int64_t M, int64_t N, int D, int C, bool general);
+hipError_t launch_gauss_sum_highd(const void* x, const void* y, const void* b, bool b_f32,
+                                  const float* rscale, const float* cscale, float* out,
+                                  void* workspace, int64_t B, int64_t M, int64_t N, int D, int C,
+                                  float sigma, hipStream_t s);
+// out[t][i] = -tau sum_j Phi_ij (a_i . bv_j)(x_i - y_j): rows x with weights a [B][M][C],
+// columns y with weights bv [B][N][C] (each fp16, or fp32 when flagged); out [B][M][D].
+size_t highd_grad_workspace_bytes(int64_t B, int64_t M, int64_t N, int D, int C);
+hipError_t launch_gauss_sum_grad_highd(const void* x, const void* y, const void* a, bool a_f32,
+                                       const void* bv, bool bv_f32, float* out, void* workspace,
+                                       int64_t B, int64_t M, int64_t N, int D, int C, float sigma,
+                                       hipStream_t s);
 
 }  // namespace keops

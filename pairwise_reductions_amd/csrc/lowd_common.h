@@ -1,0 +1,90 @@
+// Shared pieces of the low-dimensional (D <= 8) float32 reductions. Internal to the library.
+//
+// Every low-D kernel streams the column set j through wave-uniform loads (the column record
+// of j is the same for all 64 lanes, so it lands in scalar registers) while each lane keeps R
+// rows i in vector registers for the whole sweep; the M-by-N table never exists. Columns are
+// split into ranges reduced independently and combined in a fixed order afterwards.
+#pragma once
+
+#include "internal.h"
+
+#include <math.h>
+
+namespace keops {
+namespace lowd {
+
+__device__ __forceinline__ float exp2_hw(float v) { return __builtin_amdgcn_exp2f(v); }
+
+constexpr int kChunk = 512;            // columns per first-level partial sum
+constexpr float kLseSlack = 16.0f;     // lazy rescale: terms may grow to 2^16 before a rescale
+
+// Rows per lane of each family (register budgets measured on gfx950).
+constexpr int kRowsSum = 4;
+constexpr int kRowsLse = 4;
+constexpr int kRowsGrad = 2;
+constexpr int kLseTile = 8;            // columns per log-sum-exp tile
+constexpr int64_t kSplitCols = 65536;  // largest column range of one split (fits one XCD's L2)
+
+inline int argk_bucket(int K) {
+  if (K <= 1) return 1;
+  if (K <= 2) return 2;
+  if (K <= 4) return 4;
+  if (K <= 8) return 8;
+  if (K <= 10) return 10;
+  if (K <= 16) return 16;
+  if (K <= 32) return 32;
+  return 64;
+}
+inline int argk_rows(int Kb) { return Kb <= 16 ? 2 : 1; }
+
+__host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Per-row partial of a log-sum-exp over one split: l = sum_j 2^{e_ij - m} with the float64
+// shift m in log2 units.
+struct LsePartial {
+  double m;
+  float l;
+  float pad;
+};
+
+// A (key, column) entry of an argKmin list.
+struct KeyIdx {
+  double key;
+  int32_t idx;
+  int32_t pad;
+};
+
+// out[i] = rscale[i / C] * sum over s of partial[s][i] (rscale may be null), in increasing s.
+hipError_t launch_combine_sum(const float* partial, float* out, int64_t n, int64_t S, const float* rscale, int C,
+                              hipStream_t s);
+// out[i] = ln(sum over s of l_s 2^{m_s}), merged in float64.
+hipError_t launch_combine_lse(const LsePartial* partial, float* out, int64_t M, int64_t S, hipStream_t s);
+
+#define KEOPS_SWITCH_D(D_, CALL)                   \
+  switch (D_) {                                    \
+    case 1: return CALL(1);                        \
+    case 2: return CALL(2);                        \
+    case 3: return CALL(3);                        \
+    case 4: return CALL(4);                        \
+    case 5: return CALL(5);                        \
+    case 6: return CALL(6);                        \
+    case 7: return CALL(7);                        \
+    case 8: return CALL(8);                        \
+  }                                                \
+  return hipErrorInvalidValue;
+
+#define KEOPS_SWITCH_C(C_, CALL)                   \
+  switch (C_) {                                    \
+    case 1: return CALL(1);                        \
+    case 2: return CALL(2);                        \
+    case 3: return CALL(3);                        \
+    case 4: return CALL(4);                        \
+    case 5: return CALL(5);                        \
+    case 6: return CALL(6);                        \
+    case 7: return CALL(7);                        \
+    case 8: return CALL(8);                        \
+  }                                                \
+  return hipErrorInvalidValue;
+
+}  // namespace lowd
+}  // namespace keops

@@ -1,0 +1,308 @@
+// Low-D argKmin ("Kernel matrix reduction", Overview: the indices of the K smallest values
+// of a row), alone or fused with the log-sum-exp reduction in the same sweep.
+#include "lowd_common.h"
+
+namespace keops {
+namespace lowd {
+namespace {
+
+// Keys are the float64 squared distances ((dx0*dx0 + dx1*dx1) + dx2*dx2) + ... with every
+// operation rounded separately (no contraction), dx = (double)x - (double)y. Each lane keeps
+// its rows' K best (key, j) sorted ascending; columns arrive in increasing j and a new key
+// enters only when strictly smaller, so equal keys keep the lower j first.
+
+template <int K>
+__device__ __forceinline__ void topk_insert(double (&keys)[K], int32_t (&ids)[K], double key, int32_t j) {
+#pragma unroll
+  for (int k = K - 1; k > 0; --k) {
+    const bool before_prev = key < keys[k - 1];
+    const bool before_this = key < keys[k];
+    const double nk = before_prev ? keys[k - 1] : (before_this ? key : keys[k]);
+    const int32_t ni = before_prev ? ids[k - 1] : (before_this ? j : ids[k]);
+    keys[k] = nk;
+    ids[k] = ni;
+  }
+  if (key < keys[0]) {
+    keys[0] = key;
+    ids[0] = j;
+  }
+}
+
+template <int D>
+__device__ __forceinline__ double sq_dist_key(const double (&xu)[D], const double* v) {
+#pragma clang fp contract(off)
+  double key = 0.0;
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    const double dd = xu[d] - v[d];
+    const double sq = dd * dd;
+    key = (d == 0) ? sq : key + sq;
+  }
+  return key;
+}
+
+// Largest squared norm in the column table (cols[j][D] holds |y_j|^2), one workgroup, fixed
+// reduction order.
+__global__ void __launch_bounds__(1024)
+max_norm_kernel(const double* __restrict__ cols, int64_t N, int P, int D, double* __restrict__ out) {
+  __shared__ double red[1024];
+  double m = 0.0;
+  for (int64_t j = threadIdx.x; j < N; j += 1024) m = fmax(m, cols[j * P + D]);
+  red[threadIdx.x] = m;
+  __syncthreads();
+  for (int w = 512; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] = fmax(red[threadIdx.x], red[threadIdx.x + w]);
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *out = red[0];
+}
+
+// Screening bound: the float64 expansion a = |x|^2 + |y|^2 - 2 x.y (D+1 FMAs after the two
+// norms, each rounded once) differs from the exact squared distance by at most
+// (4D + 8) 2^-53 (|x|^2 + |y|^2) <= 2^-46 (|x|^2 + max_j |y_j|^2) for D <= 8.
+constexpr double kScreenMargin = 1.4210854715202004e-14;  // 2^-46
+
+// argKmin (and, with LSE, the log-sum-exp of -c2 d^2 in base 2) over the columns of one split.
+// Each pair first gets the cheap expansion a_ij; only when a_ij is below the row's K-th key
+// plus the margin is the exact key computed and the sorted list updated, which after the
+// first columns is rare. For the log-sum-exp the row's running shift is -c2 times its
+// smallest key so far, raised lazily (only when it grows by more than kLseSlack), so every
+// term 2^(-c2 a_ij - m) stays below 2^kLseSlack; it is updated before a tile's terms are added.
+template <int D, int K, int R, bool LSE>
+__global__ void __launch_bounds__(kBlock)
+knn_kernel(const float* __restrict__ x, const double* __restrict__ cols, const double* __restrict__ ymax,
+           int32_t* __restrict__ idx, float* __restrict__ dist, KeyIdx* __restrict__ partial,
+           float* __restrict__ lse_out, LsePartial* __restrict__ lse_partial, int64_t M, int64_t N,
+           int64_t cps, int Kout, double c2) {
+  constexpr int P = (D + 2) & ~1;
+  constexpr int U = D <= 4 ? 4 : 2;  // columns per screened tile
+  const int64_t split = blockIdx.y;
+  const int64_t j0 = split * cps;
+  const int64_t j1 = (j0 + cps < N) ? j0 + cps : N;
+  const int64_t row0 = (int64_t)blockIdx.x * (kBlock * R) + threadIdx.x;
+  const double bmax = *ymax;
+
+  double xd[R][D], xp[R][D], A[R], marg[R], thr[R];
+  double keys[R][K];
+  int32_t ids[R][K];
+  double mref[R];
+  float l[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    int64_t i = row0 + (int64_t)r * kBlock;
+    i = i < M ? i : M - 1;
+    double s = 0.0;
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      xd[r][d] = (double)x[i * D + d];
+      xp[r][d] = -2.0 * xd[r][d];
+      s = fma(xd[r][d], xd[r][d], s);
+    }
+    A[r] = s;
+    marg[r] = kScreenMargin * (s + bmax);
+    thr[r] = INFINITY;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      keys[r][k] = INFINITY;
+      ids[r][k] = -1;
+    }
+    mref[r] = -INFINITY;
+    l[r] = 0.0f;
+  }
+
+  // Columns [j, j + n) of a tile, n <= U, for row r: screen, update the list, add LSE terms.
+  auto tile = [&](int r, int64_t j, int n, const double (&yv)[U][D], const double (&bv)[U]) {
+    double a[U];
+    double mn = INFINITY;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (u < n) {
+        double t = A[r] + bv[u];
+#pragma unroll
+        for (int d = 0; d < D; ++d) t = fma(xp[r][d], yv[u][d], t);
+        a[u] = t;
+        mn = fmin(mn, t);
+      }
+    }
+    if (mn < thr[r]) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (u < n && a[u] < thr[r]) {
+          const double key = sq_dist_key<D>(xd[r], yv[u]);
+          if (key < keys[r][K - 1]) {
+            topk_insert<K>(keys[r], ids[r], key, (int32_t)(j + u));
+            thr[r] = keys[r][K - 1] + marg[r];
+            if constexpr (LSE) {
+              const double nm = -c2 * keys[r][0];
+              if (nm > mref[r] + (double)kLseSlack) {
+                l[r] *= exp2_hw((float)(mref[r] - nm));
+                mref[r] = nm;
+              }
+            }
+          }
+        }
+      }
+    }
+    if constexpr (LSE) {
+      float t = 0.0f;
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (u < n) t += exp2_hw((float)fma(a[u], -c2, -mref[r]));
+      l[r] += t;
+    }
+  };
+
+  int64_t j = j0;
+  for (; j + U <= j1; j += U) {
+    double yv[U][D], bv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+      for (int d = 0; d < D; ++d) yv[u][d] = cols[(j + u) * P + d];
+      bv[u] = cols[(j + u) * P + D];
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) tile(r, j, U, yv, bv);
+  }
+  if (j < j1) {
+    const int n = (int)(j1 - j);
+    double yv[U][D], bv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t jj = (u < n) ? j + u : j;
+#pragma unroll
+      for (int d = 0; d < D; ++d) yv[u][d] = cols[jj * P + d];
+      bv[u] = cols[jj * P + D];
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) tile(r, j, n, yv, bv);
+  }
+
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int64_t i = row0 + (int64_t)r * kBlock;
+    if (i >= M) continue;
+    if (gridDim.y == 1) {
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        if (k < Kout) {
+          idx[i * Kout + k] = ids[r][k];
+          if (dist) dist[i * Kout + k] = (float)keys[r][k];
+        }
+      }
+      if constexpr (LSE) lse_out[i] = (float)((mref[r] + (double)log2f(l[r])) * M_LN2);
+    } else {
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        KeyIdx p;
+        p.key = keys[r][k];
+        p.idx = ids[r][k];
+        p.pad = 0;
+        partial[(split * M + i) * K + k] = p;
+      }
+      if constexpr (LSE) {
+        LsePartial p;
+        p.m = mref[r];
+        p.l = l[r];
+        p.pad = 0.0f;
+        lse_partial[split * M + i] = p;
+      }
+    }
+  }
+}
+
+// Merge the S per-split lists of row i in increasing split order (lower columns first), so
+// equal keys keep the lower column index first.
+template <int K>
+__global__ void __launch_bounds__(kBlock)
+merge_topk_kernel(const KeyIdx* __restrict__ partial, int32_t* __restrict__ idx,
+                  float* __restrict__ dist, int64_t M, int64_t S, int Kout) {
+  const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+  if (i >= M) return;
+  double keys[K];
+  int32_t ids[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    keys[k] = INFINITY;
+    ids[k] = -1;
+  }
+  for (int64_t s = 0; s < S; ++s) {
+    const KeyIdx* p = partial + (s * M + i) * K;
+    for (int k = 0; k < K; ++k) {
+      const KeyIdx q = p[k];
+      if (q.idx < 0) break;
+      if (q.key < keys[K - 1]) topk_insert<K>(keys, ids, q.key, q.idx);
+      else break;  // the split's list is sorted: nothing later can enter
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    if (k < Kout) {
+      idx[i * Kout + k] = ids[k];
+      if (dist) dist[i * Kout + k] = (float)keys[k];
+    }
+  }
+}
+
+template <int D, int K, bool LSE>
+hipError_t knn_dk(const float* x, const double* cols, const double* ymax, int32_t* idx, float* dist,
+                  void* partial, float* lse_out, double* lse_partial, int64_t M, int64_t N, int Kout, double c2,
+                  const Plan& p, hipStream_t s) {
+  dim3 grid((unsigned)p.row_blocks, (unsigned)p.splits);
+  knn_kernel<D, K, (K <= 16 ? 2 : 1), LSE><<<grid, kBlock, 0, s>>>(
+      x, cols, ymax, idx, dist, reinterpret_cast<KeyIdx*>(partial), lse_out,
+      reinterpret_cast<LsePartial*>(lse_partial), M, N, p.cols_per_split, Kout, c2);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.splits == 1) return e;
+  merge_topk_kernel<K><<<(unsigned)ceil_div(M, kBlock), kBlock, 0, s>>>(
+      reinterpret_cast<const KeyIdx*>(partial), idx, dist, M, p.splits, Kout);
+  e = hipGetLastError();
+  if (e != hipSuccess || !LSE) return e;
+  return launch_combine_lse(reinterpret_cast<const LsePartial*>(lse_partial), lse_out, M, p.splits, s);
+}
+
+template <int D, bool LSE>
+hipError_t knn_d(int Kb, const float* x, const double* cols, const double* ymax, int32_t* idx, float* dist,
+                 void* partial, float* lse_out, double* lse_partial, int64_t M, int64_t N, int Kout, double c2,
+                 const Plan& p, hipStream_t s) {
+#define KEOPS_KNN_K(Kv) return knn_dk<D, Kv, LSE>(x, cols, ymax, idx, dist, partial, lse_out, lse_partial, M, N, Kout, c2, p, s)
+  switch (Kb) {
+    case 1: KEOPS_KNN_K(1);
+    case 2: KEOPS_KNN_K(2);
+    case 4: KEOPS_KNN_K(4);
+    case 8: KEOPS_KNN_K(8);
+    case 10: KEOPS_KNN_K(10);
+    case 16: KEOPS_KNN_K(16);
+    case 32: KEOPS_KNN_K(32);
+    case 64: KEOPS_KNN_K(64);
+  }
+#undef KEOPS_KNN_K
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+}  // namespace lowd
+
+hipError_t launch_knn_lowd(const float* x, const float* y, double* cols, double* ymax, int32_t* idx,
+                           float* dist, void* partial, float* lse_out, double* lse_partial, int64_t M, int64_t N,
+                           int D, int K, double c2, bool with_lse, const Plan& p, hipStream_t s) {
+  // column table (y_j, |y_j|^2) uncentred, then its largest norm for the screening margin
+  hipError_t e = launch_prep_cols(y, cols, N, D, -1.0, false, s);
+  if (e != hipSuccess) return e;
+  lowd::max_norm_kernel<<<1, 1024, 0, s>>>(cols, N, col_stride(D), D, ymax);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int Kb = lowd::argk_bucket(K);
+  if (with_lse) {
+#define KEOPS_KNN(Dv) lowd::knn_d<Dv, true>(Kb, x, cols, ymax, idx, dist, partial, lse_out, lse_partial, M, N, K, c2, p, s)
+    auto run = [&]() -> hipError_t { KEOPS_SWITCH_D(D, KEOPS_KNN) };
+#undef KEOPS_KNN
+    return run();
+  }
+#define KEOPS_KNN(Dv) lowd::knn_d<Dv, false>(Kb, x, cols, ymax, idx, dist, partial, lse_out, lse_partial, M, N, K, c2, p, s)
+  auto run = [&]() -> hipError_t { KEOPS_SWITCH_D(D, KEOPS_KNN) };
+#undef KEOPS_KNN
+  return run();
+}
+
+}  // namespace keops

@@ -3,10 +3,11 @@
 This module only draws random inputs; it holds none of the reductions' arithmetic, so the
 device path, the CPU oracle and the benchmark can all share it.
 
-The five workloads follow the sizes and distributions the pages use:
+The six workloads follow the sizes and distributions the pages use:
   * "Kernel matrix reduction" (concept page), Variants: Gaussian product, D=3, float32,
     10k / 100k / 1M points;
-  * "Fast Gauss Sums via Flash Attention", Figure 1 (lower row): B=4, D=32, C=32, fp16.
+  * "Fast Gauss Sums via Flash Attention", Figure 1 (lower row): B=4, D=32, C=32, fp16, and
+    Figure 2: forward and backward at B=4, D=32, C=1, fp16.
 Points in the unit cube are drawn on the 2^-24 grid so that every coordinate is an exact
 float32 value and no generator internals beyond integer draws are relied on.
 """
@@ -55,6 +56,11 @@ WORKLOADS: Dict[str, Workload] = {
         C=32, sigma=1.0, dist="normal_over_sqrt_d",
         description="Batched Gaussian kernel sum with signed weights, B=4, M=N=16384, D=32, "
                     "C=32, fp16 inputs, tau=1 (sigma=1)"),
+    "batched_gauss_sum_fp16_fwd_bwd": Workload(
+        key="batched_gauss_sum_fp16_fwd_bwd", op="gauss_sum_batched+backward", B=4, M=16_384, N=16_384,
+        D=32, C=1, sigma=1.0, dist="normal_over_sqrt_d",
+        description="Batched Gaussian kernel sum, forward and backward (gradients with respect "
+                    "to x, y and b), B=4, M=N=16384, D=32, C=1, fp16 inputs, tau=1 (sigma=1)"),
     "argkmin_lse_100k": Workload(
         key="argkmin_lse_100k", op="argkmin+lse", M=100_000, N=100_000, D=3, K=10, sigma=0.1,
         description="Row-wise argKmin (K=10) of squared distance plus log-sum-exp of "
@@ -111,9 +117,11 @@ def make_inputs(key: str, M: Optional[int] = None, N: Optional[int] = None,
     return out
 
 
-def upstream_gradient(M: int, C: int, seed: int = 2) -> np.ndarray:
-    """A seeded upstream gradient g = dL/ds of shape (M, C), float32 ~ N(0,1)."""
-    return np.random.default_rng(seed).standard_normal((M, C)).astype(np.float32)
+def upstream_gradient(M: int, C: int, seed: int = 2, B: Optional[int] = None) -> np.ndarray:
+    """A seeded upstream gradient g = dL/ds of shape (M, C), or (B, M, C) when B is given,
+    float32 ~ N(0,1)."""
+    shape = (M, C) if B is None else (B, M, C)
+    return np.random.default_rng(seed).standard_normal(shape).astype(np.float32)
 
 
 def sample_rows(M: int, count: int, seed: int = 1, edge: int = 64) -> np.ndarray:

@@ -14,7 +14,10 @@ What pins what (page citations are by title and section):
     gradient of the loss sum_i a_i^2 from the KeOps LazyTensor example;
   * exact arithmetic: argKmin against a full sort of exact rational squared distances;
   * limits and invariants: sigma -> infinity, coincident columns, translation invariance,
-    central finite differences of the (separately pinned) forward.
+    central finite differences of the (separately pinned) forward;
+  * spectral facts of the diffusion operator ("FlashDiffusion", section 2.2): the
+    normalised operator has eigenvalue 1 with eigenvector sqrt(d) and no larger one, and
+    its Markov form has unit row sums.
 """
 from __future__ import annotations
 
@@ -477,6 +480,124 @@ def check_grad_y_finite_differences_and_limits(o):
     assert np.allclose(a1, a2, rtol=1e-9, atol=1e-12)
 
 
+# ------------------------------------------------------------- batched backward (fp16 path)
+
+def check_batched_backward_vs_attention_autograd(o):
+    """torch.autograd through "Fast Gauss Sums via Flash Attention", Algorithm 1 (prescale:
+    s = att_tau(q, k, v~) e^{lse_tau(q, k~)} e^{-tau/2 |q|^2} with v~ = v e^{-tau/2 |k|^2}),
+    evaluated with scaled_dot_product_attention and logsumexp in float64, gives the
+    gradients of sum_m (s_m . w_m) with respect to q, k and v."""
+    import torch
+    q, k, v = _rux_inputs(seed=21, B=2, M=9, N=11, D=4, C=3)
+    w = _rng(22).standard_normal((2, 9, 3))
+    for sigma in (0.8, 1.7):
+        tau = 1.0 / (sigma * sigma)
+        qt = torch.tensor(q.astype(np.float64), requires_grad=True)
+        kt = torch.tensor(k.astype(np.float64), requires_grad=True)
+        vt = torch.tensor(v.astype(np.float64), requires_grad=True)
+        kk = (kt * kt).sum(-1)
+        vtil = vt * torch.exp(-0.5 * tau * kk)[..., None]
+        att = torch.nn.functional.scaled_dot_product_attention(qt, kt, vtil, scale=tau)
+        # att uses softmax over tau q.k; undo its normalisation with the log-sum-exp
+        lse = torch.logsumexp(tau * qt @ kt.transpose(-1, -2), dim=-1)
+        s = att * torch.exp(lse - 0.5 * tau * (qt * qt).sum(-1))[..., None]
+        gq, gk, gv = torch.autograd.grad((s * torch.from_numpy(w)).sum(), [qt, kt, vt])
+        got = o.gauss_sum_batched_backward(q, k, v, w, sigma)
+        assert np.allclose(got["x"][0], gq.numpy(), rtol=1e-9, atol=1e-12)
+        assert np.allclose(got["y"][0], gk.numpy(), rtol=1e-9, atol=1e-12)
+        assert np.allclose(got["b"][0], gv.numpy(), rtol=1e-9, atol=1e-12)
+
+
+# ------------------------------------------------------------ scaled operator, diffusion
+
+def _rbf(x, y, sigma):
+    from sklearn.metrics.pairwise import rbf_kernel
+    return rbf_kernel(np.asarray(x, np.float64), np.asarray(y, np.float64), gamma=1.0 / (2.0 * sigma * sigma))
+
+
+def check_scaled_vs_dense_diagonals(o):
+    """"FlashDiffusion", section 2.2: diag(r) K diag(c) V with the kernel matrix from
+    scikit-learn's rbf_kernel and explicit diagonal matrices; signed scales."""
+    rng = _rng(23)
+    x = rng.random((10, 3))
+    y = rng.random((14, 3))
+    b = rng.standard_normal((14, 2))
+    r = rng.standard_normal(10)
+    c = rng.standard_normal(14)
+    sigma = 0.4
+    K = _rbf(x, y, sigma)
+    want = np.diag(r) @ K @ np.diag(c) @ b
+    got, n = o.gauss_sum_scaled(x, y, b, sigma, row_scale=r, col_scale=c)
+    assert np.allclose(got, want, rtol=1e-12, atol=1e-14)
+    assert np.allclose(n, np.abs(np.diag(r) @ K) @ np.abs(np.diag(c) @ b), rtol=1e-12, atol=1e-14)
+    only_r, _ = o.gauss_sum_scaled(x, y, b, sigma, row_scale=r)
+    assert np.allclose(only_r, np.diag(r) @ K @ b, rtol=1e-12, atol=1e-14)
+    only_c, _ = o.gauss_sum_scaled(x, y, b, sigma, col_scale=c)
+    assert np.allclose(only_c, K @ np.diag(c) @ b, rtol=1e-12, atol=1e-14)
+
+
+def check_scaled_single_column(o):
+    """A column scale that keeps one column j0 gives r_i k(x_i, y_j0) c_j0 b_j0 (math.exp)."""
+    rng = _rng(24)
+    x = rng.random((5, 2))
+    y = rng.random((6, 2))
+    b = rng.standard_normal((6, 1))
+    r = rng.random(5) + 0.5
+    c = np.zeros(6)
+    c[3] = -1.75
+    sigma = 0.6
+    got, _ = o.gauss_sum_scaled(x, y, b, sigma, row_scale=r, col_scale=c)
+    for i in range(5):
+        d2 = sum((x[i, d] - y[3, d]) ** 2 for d in range(2))
+        want = r[i] * math.exp(-d2 / (2 * sigma * sigma)) * c[3] * b[3, 0]
+        assert abs(got[i, 0] - want) <= 1e-14 * max(1.0, abs(want))
+
+
+def check_diffusion_dense_formula(o):
+    """The alpha-normalised symmetric diffusion matrix built densely: q = K 1,
+    K_a = diag(q^-a) K diag(q^-a), d = K_a 1, s = q^-a d^-1/2 (kernel from scikit-learn)."""
+    rng = _rng(25)
+    x = rng.random((12, 3))
+    sigma = 0.3
+    K = _rbf(x, x, sigma)
+    q = K.sum(axis=1)
+    for alpha in (0.0, 0.5, 1.0):
+        Ka = np.diag(q ** -alpha) @ K @ np.diag(q ** -alpha)
+        d = Ka.sum(axis=1)
+        s, qo, do = o.diffusion_scaling(x, sigma, alpha)
+        assert np.allclose(qo, q, rtol=1e-12)
+        assert np.allclose(do, d, rtol=1e-12)
+        assert np.allclose(s, q ** -alpha / np.sqrt(d), rtol=1e-12)
+
+
+def check_diffusion_spectrum(o):
+    """A = diag(s) K diag(s) has the eigenvector sqrt(d) with eigenvalue 1, its largest
+    (A is similar to the row-stochastic D^-1 K_alpha), and D^-1 K_alpha has unit row sums."""
+    rng = _rng(26)
+    x = rng.random((15, 2))
+    sigma = 0.25
+    K = _rbf(x, x, sigma)
+    for alpha in (0.5, 1.0):
+        s, q, d = o.diffusion_scaling(x, sigma, alpha)
+        A = np.diag(s) @ K @ np.diag(s)
+        assert np.allclose(A @ np.sqrt(d), np.sqrt(d), rtol=1e-11)
+        ev = np.linalg.eigvalsh(A)
+        assert abs(ev[-1] - 1.0) < 1e-11 and ev[0] > -1.0 - 1e-11
+        p = q ** -alpha
+        P = np.diag(1.0 / d) @ np.diag(p) @ K @ np.diag(p)
+        assert np.allclose(P.sum(axis=1), 1.0, rtol=1e-12)
+
+
+def check_diffusion_sigma_infinity(o):
+    """sigma -> infinity: K is all ones, q = N, d = N^(1 - 2 alpha) and s = 1/sqrt(N)."""
+    x = _rng(27).random((9, 3))
+    for alpha in (0.0, 0.5, 1.0, 2.0):
+        s, q, d = o.diffusion_scaling(x, 1e30, alpha)
+        assert np.allclose(q, 9.0, rtol=1e-14)
+        assert np.allclose(d, 9.0 ** (1 - 2 * alpha), rtol=1e-13)
+        assert np.allclose(s, 1.0 / 3.0, rtol=1e-13)
+
+
 GAUSS_CHECKS = [check_gauss_sigma_infinity, check_gauss_hand_values, check_gauss_coincident_columns,
                 check_gauss_self_term, check_gauss_lattice_integral, check_gauss_vs_sklearn,
                 check_keops_example_convention, check_gauss_permutations]
@@ -487,4 +608,8 @@ ARGK_CHECKS = [check_argkmin_exact_bruteforce, check_argkmin_k1_is_argmin, check
                check_keys_exact_flag]
 GRAD_CHECKS = [check_grad_vs_autograd, check_grad_finite_differences, check_grad_limits]
 GRADYB_CHECKS = [check_grad_yb_vs_autograd, check_grad_y_finite_differences_and_limits]
-ALL_CHECKS = GAUSS_CHECKS + BATCHED_CHECKS + LSE_CHECKS + ARGK_CHECKS + GRAD_CHECKS + GRADYB_CHECKS
+BATCHED_GRAD_CHECKS = [check_batched_backward_vs_attention_autograd]
+SCALED_CHECKS = [check_scaled_vs_dense_diagonals, check_scaled_single_column]
+DIFFUSION_CHECKS = [check_diffusion_dense_formula, check_diffusion_spectrum, check_diffusion_sigma_infinity]
+ALL_CHECKS = (GAUSS_CHECKS + BATCHED_CHECKS + LSE_CHECKS + ARGK_CHECKS + GRAD_CHECKS + GRADYB_CHECKS +
+              BATCHED_GRAD_CHECKS + SCALED_CHECKS + DIFFUSION_CHECKS)

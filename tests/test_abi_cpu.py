@@ -31,6 +31,7 @@ def test_exports_every_declared_symbol(lib):
     names = _lib.header_symbols()
     assert set(names) == {"keops_gauss_sum", "keops_lse", "keops_argkmin", "keops_gauss_sum_grad_x",
                           "keops_gauss_sum_grad_y", "keops_gauss_sum_grad_b", "keops_argkmin_lse",
+                          "keops_gauss_sum_scaled", "keops_gauss_sum_backward", "keops_diffusion_scaling",
                           "keops_workspace_bytes", "keops_status_string", "keops_last_error", "keops_version"}
     for name in names:
         assert hasattr(lib, name), name
@@ -66,7 +67,9 @@ def test_workspace_bytes(lib):
     assert ws(3, 1, 100, 100_000, 3, 1, 0, F32) > 0
     # fp16 matrix-core path: key norms (float) and the permuted fp16 copy of v
     assert ws(0, 4, 16384, 16384, 32, 32, 0, F16) >= 4 * 16384 * (4 + 32 * 2)
-    assert ws(0, 4, 16384, 16384, 48, 32, 0, F16) == 0
+    assert ws(0, 4, 16384, 16384, 48, 32, 0, F16) > 0     # D padded to 64 inside
+    assert ws(0, 4, 16384, 16384, 40, 32, 0, F16) == 0    # D not a multiple of 16
+    assert ws(0, 4, 16384, 16384, 144, 32, 0, F16) == 0   # D > 128
     assert ws(0, 4, 16384, 16384, 32, 32, 0, 2) == 0
 
 
@@ -81,7 +84,8 @@ def _gs(lib, x=X, y=Y, b=B, out=OUT, Bt=1, M=100, N=100, D=3, C=1, sigma=0.1, dt
     (dict(sigma=math.inf), INVALID),
     (dict(D=9), UNSUPPORTED), (dict(D=0), UNSUPPORTED), (dict(C=0), UNSUPPORTED), (dict(C=9), UNSUPPORTED),
     (dict(Bt=2), UNSUPPORTED), (dict(dtype=F16, D=3), UNSUPPORTED), (dict(dtype=7), INVALID),
-    (dict(dtype=2, D=32, C=32), UNSUPPORTED), (dict(dtype=F16, D=48, C=32), UNSUPPORTED),
+    (dict(dtype=2, D=32, C=32), UNSUPPORTED), (dict(dtype=F16, D=40, C=32), UNSUPPORTED),
+    (dict(dtype=F16, D=144, C=32), UNSUPPORTED),
     (dict(dtype=F16, D=32, C=65), UNSUPPORTED),
     (dict(dtype=F16, D=32, C=32, x=X + 8), INVALID),
     (dict(x=X + 2), INVALID), (dict(out=X + 4), INVALID), (dict(M=1 << 31), UNSUPPORTED),
@@ -167,3 +171,63 @@ def test_argkmin_lse_rejects(lib):
     assert f(X, Y, IDX, None, OUT, 10, 10, 3, 11, 0.1, WS, 1 << 30, None) == INVALID  # K > N
     assert f(X, Y, IDX, None, OUT, 0, 10, 3, 4, 0.1, None, 0, None) == 0              # M = 0
     assert lib.keops_workspace_bytes(6, 1, 100, 100_000, 3, 1, 10, F32) > lib.keops_workspace_bytes(2, 1, 100, 100_000, 3, 1, 10, F32)
+
+
+R, CS, GX, GY, GB, S, Q, DD = (0x10000000 * k for k in range(9, 17))
+
+
+def test_gauss_sum_scaled_rejects(lib):
+    f = lib.keops_gauss_sum_scaled
+    args = lambda **kw: dict(dict(x=X, y=Y, b=B, r=R, c=CS, out=OUT, Bt=1, M=100, N=100, D=3, C=1, sigma=0.1,
+                                  dtype=F32, ws=WS, wsb=1 << 30), **kw)
+    call = lambda a: f(a["x"], a["y"], a["b"], a["r"], a["c"], a["out"], a["Bt"], a["M"], a["N"], a["D"], a["C"],
+                       a["sigma"], a["dtype"], a["ws"], a["wsb"], None)
+    assert call(args(r=R + 2)) == INVALID            # misaligned row scale
+    assert call(args(c=CS + 1)) == INVALID
+    assert call(args(out=R)) == INVALID              # out aliases the row scale
+    assert call(args(D=9)) == UNSUPPORTED
+    assert call(args(dtype=F16, D=32, C=32, Bt=2, x=X + 8)) == INVALID   # fp16 inputs need 16-byte alignment
+    assert call(args(dtype=F16, D=24, C=32, Bt=2)) == UNSUPPORTED
+    assert call(args(M=0)) == 0                      # no rows: no-op
+    ws = lib.keops_workspace_bytes
+    assert ws(7, 1, 1000, 1000, 3, 2, 0, F32) > ws(0, 1, 1000, 1000, 3, 2, 0, F32)   # scaled weights copy
+    assert ws(7, 2, 1000, 1000, 32, 8, 0, F16) >= ws(0, 2, 1000, 1000, 32, 8, 0, F16)
+
+
+def test_gauss_sum_backward_rejects(lib):
+    f = lib.keops_gauss_sum_backward
+    call = lambda **kw: f(*[dict(dict(x=X, y=Y, b=B, g=G, gx=GX, gy=GY, gb=GB, Bt=1, M=100, N=100, D=3, C=1,
+                                      sigma=0.1, dtype=F32, ws=WS, wsb=1 << 30), **kw)[k]
+                            for k in ("x", "y", "b", "g", "gx", "gy", "gb", "Bt", "M", "N", "D", "C", "sigma",
+                                      "dtype", "ws", "wsb")], None)
+    assert call(g=None) == INVALID
+    assert call(gx=X) == INVALID                       # a gradient aliases an input
+    assert call(gx=GX, gy=GX) == INVALID               # gradients overlap each other
+    assert call(D=9) == UNSUPPORTED and call(Bt=2) == UNSUPPORTED
+    assert call(dtype=F16, D=40, C=4) == UNSUPPORTED
+    assert call(dtype=F16, D=32, C=4, gx=GX + 4) == INVALID   # fp16 path needs 16-byte aligned outputs
+    assert call(sigma=-1.0) == INVALID
+    assert call(gx=None, gy=None, gb=None, ws=None, wsb=0) == 0   # nothing requested
+    assert call(ws=None, wsb=0) == INVALID             # workspace needed
+    ws = lib.keops_workspace_bytes
+    assert ws(8, 1, 1000, 200, 3, 1, 0, F32) > 0
+    assert ws(8, 4, 16384, 16384, 32, 1, 0, F16) > ws(0, 4, 16384, 16384, 32, 1, 0, F16)
+    assert ws(8, 4, 16384, 16384, 40, 1, 0, F16) == 0
+
+
+def test_diffusion_scaling_rejects(lib):
+    f = lib.keops_diffusion_scaling
+    call = lambda **kw: f(*[dict(dict(x=X, s=S, q=Q, d=DD, Bt=1, N=100, D=3, sigma=0.1, alpha=0.5, dtype=F32,
+                                      ws=WS, wsb=1 << 30), **kw)[k]
+                            for k in ("x", "s", "q", "d", "Bt", "N", "D", "sigma", "alpha", "dtype", "ws", "wsb")],
+                          None)
+    assert call(s=None) == INVALID
+    assert call(alpha=math.nan) == INVALID
+    assert call(q=S) == INVALID                         # q aliases s
+    assert call(D=9) == UNSUPPORTED and call(Bt=3) == UNSUPPORTED
+    assert call(dtype=F16, D=24) == UNSUPPORTED
+    assert call(N=0, ws=None, wsb=0) == 0
+    assert call(ws=None, wsb=0) == INVALID
+    ws = lib.keops_workspace_bytes
+    assert ws(9, 1, 0, 5000, 3, 1, 0, F32) >= 4 * 5000 * 4
+    assert ws(9, 2, 0, 5000, 32, 1, 0, F16) > 0 and ws(9, 2, 0, 5000, 3, 1, 0, F16) == 0

@@ -52,6 +52,17 @@ MUTATIONS = [
     ("grad_b: sigma^2 instead of 2 sigma^2",
      "two_sigma2 = 2.0 * float(sigma) * float(sigma)\n    absg",
      "two_sigma2 = float(sigma) * float(sigma)\n    absg", pins.GRADYB_CHECKS),
+    ("scaled: column scale added, not multiplied", "b = _f64(col_scale)[:, None] * b",
+     "b = _f64(col_scale)[:, None] + b", pins.SCALED_CHECKS),
+    ("scaled: row scale divides", "s = r * s", "s = s / r", pins.SCALED_CHECKS),
+    ("diffusion: q^alpha instead of q^-alpha", "p = q ** (-float(alpha))", "p = q ** float(alpha)",
+     pins.DIFFUSION_CHECKS),
+    ("diffusion: left factor of d dropped", "d = p * gauss_sum(x, x, p, sigma, workers)[0][:, 0]",
+     "d = gauss_sum(x, x, p, sigma, workers)[0][:, 0]", pins.DIFFUSION_CHECKS),
+    ("diffusion: d^-1 instead of d^-1/2", "return p / np.sqrt(d), q, d", "return p / d, q, d", pins.DIFFUSION_CHECKS),
+    ("batched backward: first batch's upstream gradient everywhere",
+     'parts["x"].append(gauss_sum_grad_x(x[t], y[t], b[t], g[t], sigma, workers))',
+     'parts["x"].append(gauss_sum_grad_x(x[t], y[t], b[t], g[0], sigma, workers))', pins.BATCHED_GRAD_CHECKS),
 ]
 
 

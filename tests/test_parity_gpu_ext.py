@@ -1,0 +1,239 @@
+"""Parity of the extended entry points (through the C ABI) with the float64 oracle:
+the fp16 matrix-core backward, the fp16 path at every feature width, the two-sided scaled
+Gauss sum and the diffusion normalisation passes.
+
+Tolerances: fp16 path 2e-3 of the oracle relative to the normaliser (sum_j |k_ij b_j| for
+sums, sum_j |k_ij (g_i.b_j)(x_i - y_j)| / sigma^2 for gradients); float32 path 1e-4; the
+diffusion scalings (positive sums and their powers) within 4e-3 (fp16) / 2e-4 (float32)
+relative.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from pairwise_reductions_amd import workloads
+from test_parity_gpu import TOL_F16, TOL_F32, _announce, _dev, _highd_inputs, _host, _rand, assert_normalised
+
+pytestmark = pytest.mark.gpu
+
+
+def _oracle_backward(x, y, b, g, sigma):
+    return oracle.gauss_sum_batched_backward(x, y, b, g, sigma, workers=8)
+
+
+# ------------------------------------------------------------------ fp16 forward widths
+WIDTH_SHAPES = [
+    # (B, M, N, D, C, sigma): D not a multiple of 32 reads padded features as zero
+    (2, 300, 1000, 16, 32, 0.7), (1, 513, 2000, 48, 16, 1.0), (2, 257, 1500, 96, 32, 1.2),
+    (1, 700, 3000, 128, 64, 1.5), (3, 129, 777, 128, 1, 1.0), (1, 1000, 4096, 80, 8, 1.0),
+]
+
+
+@pytest.mark.parametrize("B,M,N,D,C,sigma", WIDTH_SHAPES)
+def test_gauss_sum_fp16_feature_widths(B, M, N, D, C, sigma):
+    import pairwise_reductions_amd as pr
+    _announce("gauss_sum_fp16_width", B=B, M=M, N=N, D=D, C=C, sigma=sigma)
+    q, k, v = _highd_inputs(B * 7 + M + D, B, M, N, D, C)
+    sig = float(np.float32(sigma))
+    got = _host(pr.gauss_sum(_dev(q), _dev(k), _dev(v), sig))
+    want, norm = oracle.gauss_sum_batched(q, k, v, 1.0 / (sig * sig), workers=8)
+    assert_normalised(got, want, norm, TOL_F16, "fp16 width")
+
+
+# ------------------------------------------------------------------ fp16 backward
+BWD_SHAPES = [
+    # (B, M, N, D, C, sigma)
+    (1, 1, 1, 32, 1, 1.0), (1, 100, 77, 32, 1, 1.0), (2, 300, 1000, 32, 32, 0.7),
+    (4, 513, 2049, 32, 1, 1.0), (1, 1024, 3000, 64, 32, 1.5), (2, 257, 300, 32, 64, 1.0),
+    (1, 700, 1500, 16, 3, 0.8), (1, 400, 900, 96, 17, 1.2), (2, 333, 1200, 128, 48, 1.5),
+    (1, 2000, 600, 48, 2, 0.9),
+]
+
+
+@pytest.mark.parametrize("B,M,N,D,C,sigma", BWD_SHAPES)
+def test_gauss_sum_backward_fp16_shapes(B, M, N, D, C, sigma):
+    import pairwise_reductions_amd as pr
+    _announce("backward_fp16", B=B, M=M, N=N, D=D, C=C, sigma=sigma)
+    q, k, v = _highd_inputs(B * 5 + M * 3 + N, B, M, N, D, C)
+    g = workloads.upstream_gradient(M, C, seed=M + N, B=B)
+    sig = float(np.float32(sigma))
+    got = pr.gauss_sum_backward(_dev(q), _dev(k), _dev(v), _dev(g), sig)
+    want = _oracle_backward(q, k, v, g, sig)
+    for key in ("x", "y", "b"):
+        assert_normalised(_host(got[key]), want[key][0], want[key][1], TOL_F16, f"backward fp16 {key}")
+
+
+def test_gauss_sum_backward_fp16_subsets_and_large_weights():
+    """Only some gradients requested; weights far outside the fp16 range of products
+    (|v| ~ 3e3, |g| ~ 1e5) and zero weight rows / columns, which the normalisation handles."""
+    import pairwise_reductions_amd as pr
+    _announce("backward_fp16_large")
+    B, M, N, D, C = 2, 600, 1100, 32, 4
+    q, k, v = _highd_inputs(91, B, M, N, D, C)
+    v = (v.astype(np.float32) * 3000.0).astype(np.float16)
+    v[:, 5:40] = 0
+    g = workloads.upstream_gradient(M, C, seed=92, B=B) * np.float32(1e5)
+    g[:, 7:19] = 0
+    sig = 1.0
+    want = _oracle_backward(q, k, v, g, sig)
+    for need in (("x",), ("y", "b"), ("x", "y", "b")):
+        got = pr.gauss_sum_backward(_dev(q), _dev(k), _dev(v), _dev(g), sig, need=need)
+        assert set(got) == set(need)
+        for key in need:
+            assert_normalised(_host(got[key]), want[key][0], want[key][1], TOL_F16, f"large {key}")
+
+
+def test_gauss_sum_backward_fp16_far_rows():
+    """Rows far from every key: the kernel values underflow fp16 without the running shift."""
+    import pairwise_reductions_amd as pr
+    _announce("backward_fp16_far")
+    q, k, v = _highd_inputs(93, 2, 500, 2000, 32, 1, shift=1.0)
+    g = workloads.upstream_gradient(500, 1, seed=94, B=2)
+    got = pr.gauss_sum_backward(_dev(q), _dev(k), _dev(v), _dev(g), 1.0)
+    want = _oracle_backward(q, k, v, g, 1.0)
+    for key in ("x", "y", "b"):
+        assert_normalised(_host(got[key]), want[key][0], want[key][1], TOL_F16, f"far {key}")
+
+
+def test_gauss_sum_backward_fp16_workload_sampled():
+    """The B=4, M=N=16384, D=32, C=1 forward + backward at full size: gradients with respect
+    to x on sampled rows, with respect to y and b on sampled columns."""
+    import pairwise_reductions_amd as pr
+    inp = workloads.make_inputs("batched_gauss_sum_fp16_fwd_bwd")
+    B, M, N, C = inp["B"], inp["M"], inp["N"], inp["C"]
+    _announce("backward_fp16_workload", B=B, M=M, N=N, C=C)
+    sig = float(inp["sigma"])
+    xd, yd, bd = _dev(inp["x"]), _dev(inp["y"]), _dev(inp["b"])
+    s = pr.gauss_sum(xd, yd, bd, sig)
+    g = workloads.upstream_gradient(M, C, seed=4, B=B)
+    got = pr.gauss_sum_backward(xd, yd, bd, _dev(g), sig)
+    rows = workloads.sample_rows(M, 128, seed=5)
+    cols = workloads.sample_rows(N, 128, seed=6)
+    x, y, b = inp["x"], inp["y"], inp["b"]
+    want_s, norm_s = oracle.gauss_sum_batched(x[:, rows], y, b, 1.0 / (sig * sig), workers=8)
+    assert_normalised(_host(s)[:, rows], want_s, norm_s, TOL_F16, "workload forward")
+    gx, gy, gb = _host(got["x"]), _host(got["y"]), _host(got["b"])
+    for t in range(B):
+        wx, nx = oracle.gauss_sum_grad_x(x[t, rows], y[t], b[t], g[t, rows], sig, workers=8)
+        assert_normalised(gx[t, rows], wx, nx, TOL_F16, "workload grad x")
+        wy, ny = oracle.gauss_sum_grad_y(x[t], y[t, cols], b[t, cols], g[t], sig, workers=8)
+        assert_normalised(gy[t, cols], wy, ny, TOL_F16, "workload grad y")
+        wb, nb = oracle.gauss_sum_grad_b(x[t], y[t, cols], g[t], sig, workers=8)
+        assert_normalised(gb[t, cols], wb, nb, TOL_F16, "workload grad b")
+
+
+def test_autograd_fp16():
+    """The autograd wrapper on fp16 batched inputs: forward and fp16-cast gradients."""
+    import torch
+    import pairwise_reductions_amd as pr
+    _announce("autograd_fp16")
+    q, k, v = _highd_inputs(95, 2, 300, 700, 32, 2)
+    w = workloads.upstream_gradient(300, 2, seed=96, B=2)
+    qd = _dev(q).requires_grad_(True)
+    kd = _dev(k).requires_grad_(True)
+    vd = _dev(v).requires_grad_(True)
+    s = pr.gauss_sum_autograd(qd, kd, vd, 1.0)
+    (s * _dev(w)).sum().backward()
+    torch.cuda.synchronize()
+    want = _oracle_backward(q, k, v, w, 1.0)
+    for key, t in (("x", qd), ("y", kd), ("b", vd)):
+        assert t.grad.dtype == torch.float16
+        # the fp16 cast of the gradient adds one more rounding of 2^-11 relative
+        assert_normalised(t.grad.float().cpu().numpy(), want[key][0], want[key][1], 2 * TOL_F16, f"autograd {key}")
+
+
+# ------------------------------------------------------------------ float32 backward entry
+@pytest.mark.parametrize("M,N,D,C,sigma", [(1, 1, 3, 1, 0.1), (700, 2000, 2, 3, 0.2), (2049, 1537, 3, 1, 0.05),
+                                           (513, 4097, 8, 8, 0.5)])
+def test_gauss_sum_backward_f32(M, N, D, C, sigma):
+    import pairwise_reductions_amd as pr
+    _announce("backward_f32", M=M, N=N, D=D, C=C, sigma=sigma)
+    x, y, b = _rand(M + 3 * N, M, N, D, C)
+    g = workloads.upstream_gradient(M, C, seed=M)
+    sig = float(np.float32(sigma))
+    got = pr.gauss_sum_backward(_dev(x), _dev(y), _dev(b), _dev(g), sig)
+    wx, nx = oracle.gauss_sum_grad_x(x, y, b, g, sig, workers=8)
+    wy, ny = oracle.gauss_sum_grad_y(x, y, b, g, sig, workers=8)
+    wb, nb = oracle.gauss_sum_grad_b(x, y, g, sig, workers=8)
+    assert_normalised(_host(got["x"]), wx, nx, TOL_F32, "backward f32 x")
+    assert_normalised(_host(got["y"]), wy, ny, TOL_F32, "backward f32 y")
+    assert_normalised(_host(got["b"]), wb, nb, TOL_F32, "backward f32 b")
+
+
+# ------------------------------------------------------------------ scaled Gauss sum
+SCALED_SHAPES = [(1, 1, 3, 1, 0.1), (257, 1000, 3, 2, 0.1), (1025, 513, 1, 1, 0.05), (3000, 70_001, 3, 4, 0.02)]
+
+
+@pytest.mark.parametrize("M,N,D,C,sigma", SCALED_SHAPES)
+def test_gauss_sum_scaled_f32(M, N, D, C, sigma):
+    import pairwise_reductions_amd as pr
+    _announce("scaled_f32", M=M, N=N, D=D, C=C, sigma=sigma)
+    x, y, b = _rand(M * 5 + N, M, N, D, C)
+    rng = np.random.default_rng(M + N)
+    r = rng.standard_normal(M).astype(np.float32)
+    c = rng.standard_normal(N).astype(np.float32)
+    sig = float(np.float32(sigma))
+    for rs, cs in ((r, c), (r, None), (None, c), (None, None)):
+        got = _host(pr.gauss_sum_scaled(_dev(x), _dev(y), _dev(b), sig,
+                                        row_scale=None if rs is None else _dev(rs),
+                                        col_scale=None if cs is None else _dev(cs)))
+        want, norm = oracle.gauss_sum_scaled(x, y, b, sig, row_scale=rs, col_scale=cs, workers=8)
+        assert_normalised(got, want, norm, TOL_F32, "scaled f32")
+
+
+@pytest.mark.parametrize("B,M,N,D,C,sigma", [(2, 300, 1000, 32, 32, 0.7), (1, 513, 2049, 64, 3, 1.0),
+                                             (3, 100, 4000, 16, 1, 1.0)])
+def test_gauss_sum_scaled_fp16(B, M, N, D, C, sigma):
+    import pairwise_reductions_amd as pr
+    _announce("scaled_fp16", B=B, M=M, N=N, D=D, C=C, sigma=sigma)
+    q, k, v = _highd_inputs(B + M + N, B, M, N, D, C)
+    rng = np.random.default_rng(M * N)
+    r = rng.standard_normal((B, M)).astype(np.float32)
+    c = (rng.standard_normal((B, N)) * 100.0).astype(np.float32)
+    sig = float(np.float32(sigma))
+    got = _host(pr.gauss_sum_scaled(_dev(q), _dev(k), _dev(v), sig, row_scale=_dev(r), col_scale=_dev(c)))
+    for t in range(B):
+        want, norm = oracle.gauss_sum_scaled(q[t], k[t], v[t], sig, row_scale=r[t], col_scale=c[t], workers=8)
+        assert_normalised(got[t], want, norm, TOL_F16, "scaled fp16")
+
+
+# ------------------------------------------------------------------ diffusion scaling
+@pytest.mark.parametrize("N,D,sigma,alpha", [(1, 3, 0.1, 0.5), (1000, 3, 0.1, 0.5), (4097, 2, 0.05, 1.0),
+                                             (20_000, 3, 0.05, 0.0)])
+def test_diffusion_scaling_f32(N, D, sigma, alpha):
+    import pairwise_reductions_amd as pr
+    _announce("diffusion_f32", N=N, D=D, sigma=sigma, alpha=alpha)
+    x, _, _ = _rand(N + D, N, 1, D, 1)
+    sig = float(np.float32(sigma))
+    s, q, d = (_host(t) for t in pr.diffusion_scaling(_dev(x), sig, alpha))
+    ws, wq, wd = oracle.diffusion_scaling(x, sig, alpha, workers=8)
+    for got, want, name in ((q, wq, "q"), (d, wd, "d"), (s, ws, "s")):
+        rel = np.max(np.abs(got - want) / np.abs(want))
+        assert rel <= 2e-4, f"diffusion f32 {name}: {rel:.3e}"
+
+
+@pytest.mark.parametrize("B,N,D,sigma,alpha", [(2, 1000, 32, 1.0, 0.5), (1, 3000, 64, 1.5, 1.0)])
+def test_diffusion_scaling_fp16(B, N, D, sigma, alpha):
+    import pairwise_reductions_amd as pr
+    _announce("diffusion_fp16", B=B, N=N, D=D, sigma=sigma, alpha=alpha)
+    x, _, _ = _highd_inputs(N + B, B, N, 1, D, 1)
+    sig = float(np.float32(sigma))
+    s, q, d = (_host(t) for t in pr.diffusion_scaling(_dev(x), sig, alpha))
+    for t in range(B):
+        ws, wq, wd = oracle.diffusion_scaling(x[t], sig, alpha, workers=8)
+        for got, want, name in ((q[t], wq, "q"), (d[t], wd, "d"), (s[t], ws, "s")):
+            rel = np.max(np.abs(got - want) / np.abs(want))
+            assert rel <= 4e-3, f"diffusion fp16 {name}: {rel:.3e}"
+
+
+def test_diffusion_operator_eigenvector():
+    """diag(s) K diag(s) applied through the scaled Gauss sum maps sqrt(d) to itself."""
+    import pairwise_reductions_amd as pr
+    _announce("diffusion_eigen")
+    x, _, _ = _rand(7, 5000, 1, 3, 1)
+    sig = 0.05
+    s, q, d = pr.diffusion_scaling(_dev(x), sig, 0.5)
+    v = d.sqrt().reshape(-1, 1).contiguous()
+    out = _host(pr.gauss_sum_scaled(_dev(x), _dev(x), v, sig, row_scale=s, col_scale=s))
+    want = _host(v)
+    assert np.max(np.abs(out - want) / want) <= 3e-4
