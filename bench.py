@@ -38,17 +38,28 @@ def grad_flops_per_pair(D, C):
 
 # HBM bytes per launch of the dominant kernel on the 1M workload, from rocprofv3 --pmc
 # FETCH_SIZE and WRITE_SIZE (each scaled by what it reads for a 256 MiB copy: x2.0 and x1.0).
-# Reported only while the kernel source is byte-identical to the one that was measured.
-MEASURED_TRAFFIC = {"bytes": 851386226, "source": "pairwise_reductions_amd/csrc/lowd.hip",
-                    "sha256_prefix": "d9b71c3ac747c558"}
+# Reported only while the sources the kernel is compiled from are byte-identical to the ones
+# that were measured (sha256 over the listed files, concatenated in order).
+MEASURED_TRAFFIC = {"bytes": None,
+                    "sources": ["pairwise_reductions_amd/csrc/lowd_sum.hip",
+                                "pairwise_reductions_amd/csrc/lowd_common.h"],
+                    "sha256_prefix": ""}
+
+
+def kernel_source_digest(paths):
+    import hashlib
+    h = hashlib.sha256()
+    for rel in paths:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def measured_traffic():
-    import hashlib
-    path = os.path.join(ROOT, MEASURED_TRAFFIC["source"])
+    if not MEASURED_TRAFFIC["bytes"] or not MEASURED_TRAFFIC["sha256_prefix"]:
+        return None
     try:
-        with open(path, "rb") as f:
-            digest = hashlib.sha256(f.read()).hexdigest()
+        digest = kernel_source_digest(MEASURED_TRAFFIC["sources"])
     except OSError:
         return None
     return MEASURED_TRAFFIC["bytes"] if digest.startswith(MEASURED_TRAFFIC["sha256_prefix"]) else None
@@ -213,6 +224,55 @@ def bench_all(steps, warmup):
                                       "mfma_tflops": mflops / t / 1e12,
                                       "frac_fp16_mfma_peak": mflops / t / 1e12 / PEAK_FP16_MFMA_TFLOPS}
 
+    # Batched Gauss sum forward + backward, fp16: B=4, M=N=16384, D=32, C=1 (the flash page's
+    # Figure 2 shape); the backward computes the gradients with respect to x, y and b.
+    inp = workloads.make_inputs("batched_gauss_sum_fp16_fwd_bwd")
+    q, k, v = _resident(inp, ("x", "y", "b"), dev)
+    Bt, M, N, D, C = inp["B"], inp["M"], inp["N"], inp["D"], inp["C"]
+    sig = float(inp["sigma"])
+    out = torch.empty((Bt, M, C), device=dev)
+    gup = torch.from_numpy(workloads.upstream_gradient(M, C, seed=4, B=Bt)).to(dev)
+    ws = torch.empty(max(1, pr.workspace_bytes(_lib.OP_GAUSS_SUM_BACKWARD, Bt, M, N, D, C, 0, _lib.KEOPS_F16),
+                         pr.workspace_bytes(0, Bt, M, N, D, C, 0, _lib.KEOPS_F16)), dtype=torch.uint8, device=dev)
+    tf = _events_time(lambda: pr.gauss_sum(q, k, v, sig, out=out, workspace=ws), max(steps, 50), warmup)
+    tb = _events_time(lambda: pr.gauss_sum_backward(q, k, v, gup, sig, workspace=ws), max(steps, 50), warmup)
+    tbx = _events_time(lambda: pr.gauss_sum_backward(q, k, v, gup, sig, need=("x",), workspace=ws),
+                       max(steps, 50), warmup)
+    pairs = float(Bt) * M * N
+    rows["batched_gauss_sum_fp16_fwd_bwd"] = {"fwd_ms": tf * 1e3, "bwd_ms": tb * 1e3, "bwd_x_only_ms": tbx * 1e3,
+                                              "fwd_bwd_ms": (tf + tb) * 1e3, "fwd_pairs_per_s": pairs / tf}
+
+    # Sweep over D of the fp16 forward at B=64, M=N=16384, C=1 (the flash page's Figure 3 shape)
+    for D in (16, 32, 64, 128):
+        Bt, M, N, C = 64, 16384, 16384, 1
+        rng = torch.Generator(device="cpu").manual_seed(D)
+        q = (torch.randn((Bt, M, D), generator=rng) / D ** 0.5).to(torch.float16).to(dev)
+        k = (torch.randn((Bt, N, D), generator=rng) / D ** 0.5).to(torch.float16).to(dev)
+        v = torch.randn((Bt, N, C), generator=rng).to(torch.float16).to(dev)
+        out = torch.empty((Bt, M, C), device=dev)
+        ws = torch.empty(max(1, pr.workspace_bytes(0, Bt, M, N, D, C, 0, _lib.KEOPS_F16)), dtype=torch.uint8,
+                         device=dev)
+        t = _events_time(lambda: pr.gauss_sum(q, k, v, 1.0, out=out, workspace=ws), max(steps, 20), warmup)
+        pairs = float(Bt) * M * N
+        rows[f"fp16_d_sweep_B64_C1_D{D}"] = {"ms": t * 1e3, "pairs_per_s": pairs / t}
+        del q, k, v, out, ws
+
+    # Diffusion operator (fp32, D=3): the q and d normalisation passes and one application of
+    # diag(s) K diag(s) to a block of 4 vectors, N = 2^17.
+    N, D, Cb = 1 << 17, 3, 4
+    rng = torch.Generator(device="cpu").manual_seed(7)
+    xs = torch.rand((N, D), generator=rng).to(dev)
+    vb = torch.randn((N, Cb), generator=rng).to(dev)
+    sv, qv, dv = pr.diffusion_scaling(xs, 0.05, 0.5)
+    outb = torch.empty((N, Cb), device=dev)
+    ws = torch.empty(max(1, pr.workspace_bytes(_lib.OP_DIFFUSION_SCALING, 1, N, N, D, 1),
+                         pr.workspace_bytes(_lib.OP_GAUSS_SUM_SCALED, 1, N, N, D, Cb)), dtype=torch.uint8, device=dev)
+    ts = _events_time(lambda: pr.diffusion_scaling(xs, 0.05, 0.5, workspace=ws), steps, warmup)
+    ta = _events_time(lambda: pr.gauss_sum_scaled(xs, xs, vb, 0.05, row_scale=sv, col_scale=sv, out=outb,
+                                                  workspace=ws), steps, warmup)
+    rows["diffusion_operator_fp32_n131072_d3"] = {"scaling_ms": ts * 1e3, "apply_block4_ms": ta * 1e3,
+                                                  "apply_pairs_per_s": float(N) * N / ta}
+
     # argKmin (K=10) + log-sum-exp, 100k uniform
     inp = workloads.make_inputs("argkmin_lse_100k")
     x, y = _resident(inp, ("x", "y"), dev)
@@ -249,6 +309,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--all", action="store_true", help="also time the other workloads")
     ap.add_argument("--all-out", default=os.path.join("gpurun_out", "bench_all.json"))
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run one 256 MiB device-to-device copy (the reference kernel that scales the "
+                         "FETCH_SIZE / WRITE_SIZE counters to bytes) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this engine has no multi-GPU path (asked for --gpus {args.gpus})",
@@ -258,6 +321,14 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        a = torch.ones(1 << 26, device="cuda")
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": a.numel() * 4}), flush=True)
+        return
     if args.all:
         rows = bench_all(args.steps, args.warmup)
         os.makedirs(os.path.dirname(os.path.abspath(args.all_out)), exist_ok=True)

@@ -19,33 +19,12 @@
 namespace keops {
 namespace {
 
+using hd::half8;
 using hd::hd_ceil_div;
-using hd::key_slot;
+using hd::slot_key;
 
 template <typename T>
 __device__ inline float to_f32(T v) { return (float)v; }
-
-// Fast path: beta_j = -|k_j|^2/2 (-inf past N); vp[t][j/32][c][key_slot(j%32)] = v[t][j][c]
-// for c < C, zero for padded keys and for the padding channels C <= c < Cp.
-__global__ void __launch_bounds__(256)
-fwd_prep_kernel(const _Float16* __restrict__ k, const _Float16* __restrict__ v, float* __restrict__ beta,
-                _Float16* __restrict__ vp, int64_t N, int64_t Npad, int D, int C, int Cp) {
-  const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t t = blockIdx.y;
-  if (j >= Npad) return;
-  const _Float16* kr = k + (t * N + j) * D;
-  const _Float16* vr = v + (t * N + j) * C;
-  float s = 0.0f;
-  if (j < N) {
-    for (int d = 0; d < D; ++d) {
-      const float kv = (float)kr[d];
-      s = fmaf(kv, kv, s);
-    }
-  }
-  beta[t * Npad + j] = (j < N) ? -0.5f * s : -INFINITY;
-  _Float16* dst = vp + (t * Npad + (j / 32) * 32) * Cp + key_slot((int)(j % 32));
-  for (int c = 0; c < Cp; ++c) dst[(int64_t)c * 32] = (j < N && c < C) ? vr[c] : (_Float16)0.0f;
-}
 
 // |c_j w_j|_2 of column j of batch t (c = 1 when cscale is null).
 template <typename T>
@@ -81,52 +60,105 @@ weight_norm_max_kernel(const T* __restrict__ w, const float* __restrict__ cscale
   if (threadIdx.x == 0) atomicMax(reinterpret_cast<unsigned int*>(nmax + t), __float_as_uint(red[0]));
 }
 
-// General column preparation (see the file comment). kGrad selects the table layout:
-//   forward:  wp[t][j/32][c][key_slot(j%32)] for c < Cw (key-permuted, the A operand of O^T)
-//   gradient: wp[t][j][c] for c < Cw (row-major, the A operand of dP^T), plus
-//             yp[t][j/32][ch][key_slot(j%32)] = k[t][j][ch] for ch < D, 1 at ch = Dp, else 0.
-template <typename T, bool kGrad>
+// Column tables, one workgroup per 32-key block of one batch. The block's keys and weights are
+// staged through LDS so that every global read and write is contiguous.
+//   kMode kCopy:    beta_j = -|k_j|^2/2, wp = the fp16 weights unchanged (fast forward path);
+//   kMode kNormFwd: the general form of the file comment, forward layout;
+//   kMode kNormGrad: the general form, gradient layout, plus the key-permuted columns yp.
+// Layouts: forward wp[t][j/32][c][key_slot(j%32)] for c < Cw (the A operand of O^T);
+// gradient wp[t][j][c] for c < Cw (the A operand of dP^T) and yp[t][j/32][ch][key_slot(j%32)]
+// = k[t][j][ch] for ch < D, 1 at ch = Dp, else 0. Keys past N get beta = -inf and zeros.
+enum { kCopy = 0, kNormFwd = 1, kNormGrad = 2 };
+constexpr int kMaxPrepD = 128;
+constexpr int kMaxPrepC = 64;
+
+template <typename T, int kMode>
 __global__ void __launch_bounds__(256)
 col_prep_kernel(const _Float16* __restrict__ k, const T* __restrict__ w, const float* __restrict__ cscale,
                 const float* __restrict__ nmax, float* __restrict__ beta, _Float16* __restrict__ wp,
                 _Float16* __restrict__ yp, int64_t N, int64_t Npad, int D, int Dp, int C, int Cw, float cs) {
-  const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  __shared__ __attribute__((aligned(16))) _Float16 sk[32][kMaxPrepD];
+  __shared__ float sw[32][kMaxPrepC + 1];
+  __shared__ float sinv[32];
+  const int tid = threadIdx.x;
   const int64_t t = blockIdx.y;
-  if (j >= Npad) return;
-  const bool live = j < N;
-  const _Float16* kr = k + (t * N + j) * D;
-  const T* wr = w + (t * N + j) * C;
-  float bj = -INFINITY, inv = 0.0f, sc = 1.0f;
-  if (live) {
-    float s = 0.0f;
-    for (int d = 0; d < D; ++d) {
-      const float kv = (float)kr[d];
-      s = fmaf(kv, kv, s);
-    }
-    const float n = weight_norm(w, cscale, t, j, N, C);
-    const float nm = nmax[t];
-    const float ratio = nm > 0.0f ? n / nm : 0.0f;
-    const float lw = fmaxf(log2f(ratio), hd::kLogFloor);
-    bj = -0.5f * s + lw / cs;
-    inv = n > 0.0f ? 1.0f / n : 0.0f;
-    sc = cscale ? cscale[t * N + j] : 1.0f;
+  const int64_t j0 = (int64_t)blockIdx.x * 32;
+  const int live = N - j0 >= 32 ? 32 : (N > j0 ? (int)(N - j0) : 0);
+
+  // keys (D is a multiple of 8, so rows move in 16-byte chunks)
+  const int kch = 32 * D / 8;
+  for (int c = tid; c < kch; c += 256) {
+    const int key = c / (D / 8), col = (c % (D / 8)) * 8;
+    half8 v = half8{};
+    if (key < live) v = *reinterpret_cast<const half8*>(k + (t * N + j0 + key) * D + col);
+    *reinterpret_cast<half8*>(&sk[key][col]) = v;
   }
-  beta[t * Npad + j] = bj;
-  if constexpr (kGrad) {
-    _Float16* dst = wp + (t * Npad + j) * Cw;
-    for (int c = 0; c < Cw; ++c) dst[c] = (live && c < C) ? (_Float16)(to_f32(wr[c]) * sc * inv) : (_Float16)0.0f;
+  // weights, times the column scale
+  for (int e = tid; e < 32 * C; e += 256) {
+    const int key = e / C, c = e % C;
+    float v = 0.0f;
+    if (key < live) {
+      v = to_f32(w[(t * N + j0) * C + e]);
+      if (cscale) v *= cscale[t * N + j0 + key];
+    }
+    sw[key][c] = v;
+  }
+  __syncthreads();
+
+  // squared key norms and weight norms: 8 lanes per key
+  {
+    const int key = tid >> 3, part = tid & 7;
+    float kn = 0.0f, wn = 0.0f;
+    for (int d = part; d < D; d += 8) {
+      const float v = (float)sk[key][d];
+      kn = fmaf(v, v, kn);
+    }
+    for (int c = part; c < C; c += 8) wn = fmaf(sw[key][c], sw[key][c], wn);
+#pragma unroll
+    for (int o = 1; o < 8; o <<= 1) {
+      kn += __shfl_xor(kn, o, 8);
+      wn += __shfl_xor(wn, o, 8);
+    }
+    if (part == 0) {
+      float bj = -INFINITY, inv = 0.0f;
+      if (key < live) {
+        bj = -0.5f * kn;
+        inv = 1.0f;
+        if constexpr (kMode != kCopy) {
+          const float n = sqrtf(wn);
+          const float nm = nmax[t];
+          const float ratio = nm > 0.0f ? n / nm : 0.0f;
+          bj += fmaxf(log2f(ratio), hd::kLogFloor) / cs;
+          inv = n > 0.0f ? 1.0f / n : 0.0f;
+        }
+      }
+      beta[t * Npad + j0 + key] = bj;
+      sinv[key] = inv;
+    }
+  }
+  __syncthreads();
+
+  if constexpr (kMode == kNormGrad) {
+    _Float16* dst = wp + (t * Npad + j0) * Cw;
+    for (int e = tid; e < 32 * Cw; e += 256) {
+      const int key = e / Cw, c = e % Cw;
+      dst[e] = (_Float16)(c < C ? sw[key][c] * sinv[key] : 0.0f);
+    }
     const int YC = Dp + 16;
-    _Float16* yd = yp + (t * Npad + (j / 32) * 32) * YC + key_slot((int)(j % 32));
-    for (int ch = 0; ch < YC; ++ch) {
+    _Float16* yd = yp + (t * Npad + j0) * YC;
+    for (int e = tid; e < 32 * YC; e += 256) {
+      const int ch = e / 32, key = slot_key(e % 32);
       _Float16 v = (_Float16)0.0f;
-      if (live && ch < D) v = kr[ch];
-      if (live && ch == Dp) v = (_Float16)1.0f;
-      yd[(int64_t)ch * 32] = v;
+      if (ch < D) v = sk[key][ch];
+      else if (ch == Dp && key < live) v = (_Float16)1.0f;
+      yd[e] = v;
     }
   } else {
-    _Float16* dst = wp + (t * Npad + (j / 32) * 32) * Cw + key_slot((int)(j % 32));
-    for (int c = 0; c < Cw; ++c)
-      dst[(int64_t)c * 32] = (live && c < C) ? (_Float16)(to_f32(wr[c]) * sc * inv) : (_Float16)0.0f;
+    _Float16* dst = wp + (t * Npad + j0) * Cw;
+    for (int e = tid; e < 32 * Cw; e += 256) {
+      const int c = e / 32, key = slot_key(e % 32);
+      dst[e] = (_Float16)(c < C ? sw[key][c] * sinv[key] : 0.0f);
+    }
   }
 }
 
@@ -299,24 +331,25 @@ hipError_t launch_gauss_sum_highd(const void* x, const void* y, const void* b, b
   const _Float16* k = static_cast<const _Float16*>(y);
   const float cs = cs_of(sigma);
   const int Cp = hd::padded_channels(C);
-  const dim3 pgrid((unsigned)hd_ceil_div(L.sp.Npad, 256), (unsigned)B);
+  const dim3 pgrid((unsigned)(L.sp.Npad / 32), (unsigned)B);
   hipError_t e;
   if (!general) {
-    fwd_prep_kernel<<<pgrid, 256, 0, s>>>(k, static_cast<const _Float16*>(b), beta, vp, N, L.sp.Npad, D, C, Cp);
+    col_prep_kernel<_Float16, kCopy><<<pgrid, 256, 0, s>>>(k, static_cast<const _Float16*>(b), nullptr, nullptr, beta,
+                                                           vp, nullptr, N, L.sp.Npad, D, 0, C, Cp, cs);
     e = hipGetLastError();
   } else if (b_f32) {
     const float* w = static_cast<const float*>(b);
     e = weight_norm_max(w, cscale, nmax, B, N, C, s);
     if (e != hipSuccess) return e;
-    col_prep_kernel<float, false><<<pgrid, 256, 0, s>>>(k, w, cscale, nmax, beta, vp, nullptr, N, L.sp.Npad, D, 0, C,
-                                                        Cp, cs);
+    col_prep_kernel<float, kNormFwd><<<pgrid, 256, 0, s>>>(k, w, cscale, nmax, beta, vp, nullptr, N, L.sp.Npad, D, 0,
+                                                           C, Cp, cs);
     e = hipGetLastError();
   } else {
     const _Float16* w = static_cast<const _Float16*>(b);
     e = weight_norm_max(w, cscale, nmax, B, N, C, s);
     if (e != hipSuccess) return e;
-    col_prep_kernel<_Float16, false><<<pgrid, 256, 0, s>>>(k, w, cscale, nmax, beta, vp, nullptr, N, L.sp.Npad, D, 0,
-                                                           C, Cp, cs);
+    col_prep_kernel<_Float16, kNormFwd><<<pgrid, 256, 0, s>>>(k, w, cscale, nmax, beta, vp, nullptr, N, L.sp.Npad, D,
+                                                              0, C, Cp, cs);
     e = hipGetLastError();
   }
   if (e != hipSuccess) return e;
@@ -357,20 +390,20 @@ hipError_t launch_gauss_sum_grad_highd(const void* x, const void* y, const void*
   const _Float16* k = static_cast<const _Float16*>(y);
   const float cs = cs_of(sigma);
   const int Dp = hd::padded_features(D), Ck = hd::padded_k_channels(C);
-  const dim3 pgrid((unsigned)hd_ceil_div(L.sp.Npad, 256), (unsigned)B);
+  const dim3 pgrid((unsigned)(L.sp.Npad / 32), (unsigned)B);
   hipError_t e;
   if (bv_f32) {
     const float* w = static_cast<const float*>(bv);
     e = weight_norm_max(w, nullptr, nmax, B, N, C, s);
     if (e != hipSuccess) return e;
-    col_prep_kernel<float, true><<<pgrid, 256, 0, s>>>(k, w, nullptr, nmax, beta, bvp, yp, N, L.sp.Npad, D, Dp, C,
-                                                       Ck, cs);
+    col_prep_kernel<float, kNormGrad><<<pgrid, 256, 0, s>>>(k, w, nullptr, nmax, beta, bvp, yp, N, L.sp.Npad, D, Dp,
+                                                            C, Ck, cs);
   } else {
     const _Float16* w = static_cast<const _Float16*>(bv);
     e = weight_norm_max(w, nullptr, nmax, B, N, C, s);
     if (e != hipSuccess) return e;
-    col_prep_kernel<_Float16, true><<<pgrid, 256, 0, s>>>(k, w, nullptr, nmax, beta, bvp, yp, N, L.sp.Npad, D, Dp, C,
-                                                          Ck, cs);
+    col_prep_kernel<_Float16, kNormGrad><<<pgrid, 256, 0, s>>>(k, w, nullptr, nmax, beta, bvp, yp, N, L.sp.Npad, D,
+                                                               Dp, C, Ck, cs);
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
