@@ -64,7 +64,8 @@ typedef enum {
   KEOPS_OP_ARGKMIN_LSE = 6,
   KEOPS_OP_GAUSS_SUM_SCALED = 7,
   KEOPS_OP_GAUSS_SUM_BACKWARD = 8,
-  KEOPS_OP_DIFFUSION_SCALING = 9
+  KEOPS_OP_DIFFUSION_SCALING = 9,
+  KEOPS_OP_ARGKMIN_WEIGHTED = 10
 } keops_op;
 
 /*
@@ -109,6 +110,23 @@ KEOPS_API int keops_lse(const float* x, const float* y, float* out, int64_t M, i
 KEOPS_API int keops_argkmin(const float* x, const float* y, int32_t* idx, float* dist, int64_t M,
                   int64_t N, int32_t D, int32_t K, void* workspace, size_t workspace_bytes,
                   hipStream_t stream);
+
+/*
+ * Weighted argKmin, the min / max reduction of an additively weighted squared distance
+ * ("Kernel matrix reduction", Overview: minima and indices of the K smallest entries of a
+ * pairwise formula):
+ *   idx[i][0..K-1] = the columns j with the K smallest keys d2_ij - w_j, ascending; equal
+ *   keys keep the lower j first;  dist[i][k] = that key rounded to float32.
+ * d2_ij is the float64 key of keops_argkmin and w_j is widened exactly to float64; the key
+ * is their float64 difference (one rounding). K = 1 is the weighted min and argmin, i.e. the
+ * max of w_j - d2_ij; with w_j = 2 sigma^2 ln b_j (b_j > 0) it is the max over j of the
+ * weighted kernel b_j exp(-d2_ij / (2 sigma^2)) and its argmax.
+ * Shapes: x (M, D), y (N, D), w (N,) float32; idx (M, K) int32; dist (M, K) float32 or NULL.
+ * Limits as keops_argkmin; the workspace is that of KEOPS_OP_ARGKMIN_WEIGHTED.
+ */
+KEOPS_API int keops_argkmin_weighted(const float* x, const float* y, const float* w, int32_t* idx, float* dist,
+                                     int64_t M, int64_t N, int32_t D, int32_t K, void* workspace,
+                                     size_t workspace_bytes, hipStream_t stream);
 
 /*
  * argKmin and the log-sum-exp reduction of the same pairs in one sweep ("Kernel matrix

@@ -5,6 +5,7 @@ package. The device library never imports, links or calls it.
 """
 from .reductions import (  # noqa: F401
     argkmin,
+    argkmin_weighted,
     default_workers,
     diffusion_scaling,
     gauss_sum,

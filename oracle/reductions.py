@@ -222,6 +222,33 @@ def argkmin(x, y, K: int, workers: Optional[int] = None) -> Tuple[np.ndarray, np
     return idx, dist
 
 
+def argkmin_weighted(x, y, w, K: int, workers: Optional[int] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """Indices of the K smallest additively weighted squared distances per row [KMR, Overview:
+    minima and indices of the K smallest entries of a pairwise formula].
+
+    Row i ranks the columns j by the key (d2_ij - w_j, j) ascending (a stable sort of the row
+    of keys), d2_ij as in ``squared_distances`` and the difference taken in float64. Returns
+    (idx (M, K) int64, keys (M, K) float64). Requires 1 <= K <= N.
+    """
+    x = _f64(x)
+    y = _f64(y)
+    w = _f64(w)
+    M, N = x.shape[0], y.shape[0]
+    if not (1 <= K <= N):
+        raise ValueError("argkmin needs 1 <= K <= N")
+    idx = np.zeros((M, K), dtype=np.int64)
+    keys = np.zeros((M, K))
+
+    def block(sl):
+        kk = squared_distances(x[sl], y) - w[None, :]
+        order = np.argsort(kk, axis=1, kind="stable")[:, :K]
+        idx[sl] = order
+        keys[sl] = np.take_along_axis(kk, order, axis=1)
+
+    _parallel_rows(block, M, N, workers)
+    return idx, keys
+
+
 def gauss_sum_grad_x(x, y, b, g, sigma: float, workers: Optional[int] = None) -> Tuple[np.ndarray, np.ndarray]:
     """Gradient of the Gauss sum with respect to x, contracted with an upstream gradient.
 

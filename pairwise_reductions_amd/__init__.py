@@ -12,7 +12,7 @@ from typing import Optional, Tuple
 from . import _lib
 from ._lib import KeopsError  # noqa: F401
 
-__all__ = ["gauss_sum", "gauss_sum_scaled", "lse", "argkmin", "argkmin_lse", "gauss_sum_grad_x", "gauss_sum_grad_y",
+__all__ = ["gauss_sum", "gauss_sum_scaled", "lse", "argkmin", "argkmin_weighted", "argkmin_lse", "gauss_sum_grad_x", "gauss_sum_grad_y",
            "gauss_sum_grad_b", "gauss_sum_backward", "diffusion_scaling", "gauss_sum_autograd", "workspace_bytes",
            "KeopsError", "version"]
 
@@ -193,6 +193,27 @@ def argkmin(x, y, K: int, with_dist: bool = False, idx=None, dist=None, workspac
     st = lib.keops_argkmin(_ptr(x), _ptr(y), _ptr(idx), _ptr(dist), M, N, D, int(K), _ptr(ws), have,
                            _stream(x.device))
     _lib.check(st, "keops_argkmin")
+    return (idx, dist) if with_dist else idx
+
+
+def argkmin_weighted(x, y, w, K: int, with_dist: bool = False, idx=None, dist=None, workspace=None):
+    """Indices (int32) of the K smallest keys |x_i - y_j|^2 - w_j per row, ascending, ties to
+    the lower index; w is float32 (N,). K = 1 gives the weighted min / argmin."""
+    torch = _torch()
+    lib = _lib.load()
+    M, D = _dims(x, 2)
+    N, _ = _dims(y, 2)
+    if w.dtype != torch.float32 or w.numel() != N or not w.is_contiguous():
+        raise ValueError("w must be contiguous float32 with one entry per column")
+    if idx is None:
+        idx = torch.empty((M, K), dtype=torch.int32, device=x.device)
+    if with_dist and dist is None:
+        dist = torch.empty((M, K), dtype=torch.float32, device=x.device)
+    nbytes = lib.keops_workspace_bytes(_lib.OP_ARGKMIN_WEIGHTED, 1, M, N, D, 1, K, _lib.KEOPS_F32)
+    ws, have = _workspace(nbytes, x.device, workspace)
+    st = lib.keops_argkmin_weighted(_ptr(x), _ptr(y), _ptr(w), _ptr(idx), _ptr(dist), M, N, D, int(K), _ptr(ws),
+                                    have, _stream(x.device))
+    _lib.check(st, "keops_argkmin_weighted")
     return (idx, dist) if with_dist else idx
 
 

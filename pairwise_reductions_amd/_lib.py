@@ -18,6 +18,7 @@ KEOPS_F32, KEOPS_F16, KEOPS_BF16 = 0, 1, 2
 KEOPS_OK, KEOPS_ERR_INVALID_ARG, KEOPS_ERR_UNSUPPORTED, KEOPS_ERR_HIP = 0, 1, 2, 3
 OP_GAUSS_SUM, OP_LSE, OP_ARGKMIN, OP_GAUSS_SUM_GRAD_X, OP_GAUSS_SUM_GRAD_Y, OP_GAUSS_SUM_GRAD_B = 0, 1, 2, 3, 4, 5
 OP_ARGKMIN_LSE, OP_GAUSS_SUM_SCALED, OP_GAUSS_SUM_BACKWARD, OP_DIFFUSION_SCALING = 6, 7, 8, 9
+OP_ARGKMIN_WEIGHTED = 10
 
 _vp = ctypes.c_void_p
 _i64 = ctypes.c_int64
@@ -30,6 +31,7 @@ _SIGNATURES = {
                                        _vp, _sz, _vp]),
     "keops_lse": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i32, _f32, _vp, _sz, _vp]),
     "keops_argkmin": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i32, _i32, _vp, _sz, _vp]),
+    "keops_argkmin_weighted": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i32, _i32, _vp, _sz, _vp]),
     "keops_argkmin_lse": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i32, _i32, _f32, _vp, _sz, _vp]),
     "keops_gauss_sum_grad_x": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i32, _i32, _f32, _vp, _sz,
                                               _vp]),

@@ -314,6 +314,9 @@ size_t keops_workspace_bytes(int op, int64_t B, int64_t M, int64_t N, int32_t D,
     case KEOPS_OP_LSE:
       if (D < 1 || D > keops::kMaxLowD) return 0;
       return lowd_layout(op, M, N, D, 1, 0).total;
+    case KEOPS_OP_ARGKMIN_WEIGHTED:
+      if (D < 1 || D > keops::kMaxLowD || K < 1 || K > keops::kMaxK || K > N) return 0;
+      return lowd_layout(KEOPS_OP_ARGKMIN, M, N, D, 1, K).total;
     case KEOPS_OP_ARGKMIN:
     case KEOPS_OP_ARGKMIN_LSE:
       if (D < 1 || D > keops::kMaxLowD || K < 1 || K > keops::kMaxK || K > N) return 0;
@@ -534,9 +537,11 @@ int keops_lse(const float* x, const float* y, float* out, int64_t M, int64_t N, 
 
 namespace {
 
-// Shared by keops_argkmin and keops_argkmin_lse (lse == NULL for the former).
-int argkmin_impl(const float* x, const float* y, int32_t* idx, float* dist, float* lse, int64_t M, int64_t N,
-                 int32_t D, int32_t K, float sigma, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+// Shared by keops_argkmin, keops_argkmin_weighted (w != NULL) and keops_argkmin_lse
+// (lse != NULL).
+int argkmin_impl(const float* x, const float* y, const float* w, int32_t* idx, float* dist, float* lse, int64_t M,
+                 int64_t N, int32_t D, int32_t K, float sigma, void* workspace, size_t workspace_bytes,
+                 hipStream_t stream) {
   const bool with_lse = (lse != nullptr);
   KEOPS_TRY(check_extent(M, "M"));
   KEOPS_TRY(check_extent(N, "N"));
@@ -548,27 +553,31 @@ int argkmin_impl(const float* x, const float* y, int32_t* idx, float* dist, floa
   const Range rx{x, (size_t)(M * D) * 4}, ry{y, (size_t)(N * D) * 4};
   const Range ri{idx, (size_t)(M * K) * 4}, rd{dist, dist ? (size_t)(M * K) * 4 : 0};
   const Range rl{lse, with_lse ? (size_t)M * 4 : 0};
+  const Range rwt{w, w ? (size_t)N * 4 : 0};
   KEOPS_TRY(check_ptr(x, "x", 4, rx.bytes));
   KEOPS_TRY(check_ptr(y, "y", 4, ry.bytes));
+  if (w && !aligned(w, 4)) return fail(KEOPS_ERR_INVALID_ARG, "w must be 4-byte aligned");
   KEOPS_TRY(check_ptr(idx, "idx", 4, ri.bytes));
   if (dist && !aligned(dist, 4)) return fail(KEOPS_ERR_INVALID_ARG, "dist must be 4-byte aligned");
   if (with_lse && !aligned(lse, 4)) return fail(KEOPS_ERR_INVALID_ARG, "lse must be 4-byte aligned");
   if (overlaps(ri, rx) || overlaps(ri, ry) || overlaps(rd, rx) || overlaps(rd, ry) || overlaps(ri, rd) ||
-      overlaps(rl, rx) || overlaps(rl, ry) || overlaps(rl, ri) || overlaps(rl, rd))
+      overlaps(rl, rx) || overlaps(rl, ry) || overlaps(rl, ri) || overlaps(rl, rd) || overlaps(ri, rwt) ||
+      overlaps(rd, rwt) || overlaps(rl, rwt))
     return fail(KEOPS_ERR_INVALID_ARG, "idx/dist/lse overlap an input or each other");
   if (M == 0) return ok();
   const int op = with_lse ? KEOPS_OP_ARGKMIN_LSE : KEOPS_OP_ARGKMIN;
   const LowdLayout L = lowd_layout(op, M, N, D, 1, K);
   KEOPS_TRY(check_workspace(workspace, workspace_bytes, L.total));
   const Range rw{workspace, L.total};
-  if (overlaps(rw, ri) || overlaps(rw, rd) || overlaps(rw, rl) || overlaps(rw, rx) || overlaps(rw, ry))
+  if (overlaps(rw, ri) || overlaps(rw, rd) || overlaps(rw, rl) || overlaps(rw, rx) || overlaps(rw, ry) ||
+      overlaps(rw, rwt))
     return fail(KEOPS_ERR_INVALID_ARG, "workspace overlaps an input or an output");
   char* ws = static_cast<char*>(workspace);
   double* cols = reinterpret_cast<double*>(ws + L.cols_off);
   double* ymax = reinterpret_cast<double*>(ws + L.aux_off);
   double* lse_part = reinterpret_cast<double*>(ws + L.lse_off);
   const double c2 = with_lse ? c2_of(sigma) : 0.0;
-  KEOPS_HIP(keops::launch_knn_lowd(x, y, cols, ymax, idx, dist, ws + L.part_off, lse, lse_part, M, N, D, K, c2,
+  KEOPS_HIP(keops::launch_knn_lowd(x, y, w, cols, ymax, idx, dist, ws + L.part_off, lse, lse_part, M, N, D, K, c2,
                                    with_lse, L.plan, stream),
             "argkmin_lowd");
   return ok();
@@ -578,14 +587,21 @@ int argkmin_impl(const float* x, const float* y, int32_t* idx, float* dist, floa
 
 int keops_argkmin(const float* x, const float* y, int32_t* idx, float* dist, int64_t M, int64_t N, int32_t D,
                   int32_t K, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  return argkmin_impl(x, y, idx, dist, nullptr, M, N, D, K, 1.0f, workspace, workspace_bytes, stream);
+  return argkmin_impl(x, y, nullptr, idx, dist, nullptr, M, N, D, K, 1.0f, workspace, workspace_bytes, stream);
+}
+
+int keops_argkmin_weighted(const float* x, const float* y, const float* w, int32_t* idx, float* dist, int64_t M,
+                           int64_t N, int32_t D, int32_t K, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+  if (!w && N > 0) return fail(KEOPS_ERR_INVALID_ARG, "w must not be NULL");
+  return argkmin_impl(x, y, w, idx, dist, nullptr, M, N, D, K, 1.0f, workspace, workspace_bytes, stream);
 }
 
 int keops_argkmin_lse(const float* x, const float* y, int32_t* idx, float* dist, float* lse, int64_t M, int64_t N,
                       int32_t D, int32_t K, float sigma, void* workspace, size_t workspace_bytes,
                       hipStream_t stream) {
   if (!lse && M > 0) return fail(KEOPS_ERR_INVALID_ARG, "lse must not be NULL");
-  return argkmin_impl(x, y, idx, dist, lse, M, N, D, K, sigma, workspace, workspace_bytes, stream);
+  return argkmin_impl(x, y, nullptr, idx, dist, lse, M, N, D, K, sigma, workspace, workspace_bytes, stream);
 }
 
 int keops_gauss_sum_grad_x(const float* x, const float* y, const float* b, const float* g, float* grad,

@@ -46,12 +46,13 @@ hipError_t launch_gauss_sum_lowd(const float* x, const float* y, const double* c
 hipError_t launch_lse_lowd(const float* x, const float* y, const double* cols, float* out,
                            double* partial, int64_t M, int64_t N, int D, double c2,
                            const Plan& p, hipStream_t s);
-// argKmin, optionally fused with the log-sum-exp reduction (with_lse): builds the uncentred
-// column table in `cols` and the largest column norm in *ymax, then screens every pair.
-hipError_t launch_knn_lowd(const float* x, const float* y, double* cols, double* ymax, int32_t* idx,
-                           float* dist, void* partial, float* lse_out, double* lse_partial, int64_t M,
-                           int64_t N, int D, int K, double c2, bool with_lse, const Plan& p,
-                           hipStream_t s);
+// argKmin of d^2_ij - w_j (w may be null), optionally fused with the log-sum-exp reduction
+// (with_lse, only without weights): builds the uncentred column table in `cols` and the
+// screening bound in *ymax, then screens every pair.
+hipError_t launch_knn_lowd(const float* x, const float* y, const float* w, double* cols, double* ymax,
+                           int32_t* idx, float* dist, void* partial, float* lse_out,
+                           double* lse_partial, int64_t M, int64_t N, int D, int K, double c2,
+                           bool with_lse, const Plan& p, hipStream_t s);
 hipError_t launch_grad_x_lowd(const float* x, const float* y, const float* b, const float* g,
                               float* grad, float* partial, int64_t M, int64_t N, int D, int C,
                               float c2f, float inv_sigma2, const Plan& p, hipStream_t s);

@@ -41,13 +41,24 @@ __device__ __forceinline__ double sq_dist_key(const double (&xu)[D], const doubl
   return key;
 }
 
-// Largest squared norm in the column table (cols[j][D] holds |y_j|^2), one workgroup, fixed
-// reduction order.
+// Largest |y_j|^2 + |w_j| over the column table (cols[j][D] holds |y_j|^2 on entry; w may be
+// null), one workgroup, fixed reduction order. With weights the table's screening term becomes
+// |y_j|^2 - w_j (each entry is rewritten by the one thread that reads it).
 __global__ void __launch_bounds__(1024)
-max_norm_kernel(const double* __restrict__ cols, int64_t N, int P, int D, double* __restrict__ out) {
+max_norm_kernel(double* __restrict__ cols, const float* __restrict__ w, int64_t N, int P, int D,
+                double* __restrict__ out) {
   __shared__ double red[1024];
   double m = 0.0;
-  for (int64_t j = threadIdx.x; j < N; j += 1024) m = fmax(m, cols[j * P + D]);
+  for (int64_t j = threadIdx.x; j < N; j += 1024) {
+    const double yy = cols[j * P + D];
+    if (w) {
+      const double wj = (double)w[j];
+      m = fmax(m, yy + fabs(wj));
+      cols[j * P + D] = yy - wj;
+    } else {
+      m = fmax(m, yy);
+    }
+  }
   red[threadIdx.x] = m;
   __syncthreads();
   for (int w = 512; w > 0; w >>= 1) {
@@ -57,12 +68,14 @@ max_norm_kernel(const double* __restrict__ cols, int64_t N, int P, int D, double
   if (threadIdx.x == 0) *out = red[0];
 }
 
-// Screening bound: the float64 expansion a = |x|^2 + |y|^2 - 2 x.y (D+1 FMAs after the two
-// norms, each rounded once) differs from the exact squared distance by at most
-// (4D + 8) 2^-53 (|x|^2 + |y|^2) <= 2^-46 (|x|^2 + max_j |y_j|^2) for D <= 8.
+// Screening bound: the float64 expansion a = |x|^2 + (|y|^2 - w) - 2 x.y (D+1 FMAs after the
+// norms, each rounded once) differs from the key d^2 - w by at most
+// (4D + 12) 2^-53 (|x|^2 + |y|^2 + |w|) <= 2^-46 (|x|^2 + max_j (|y_j|^2 + |w_j|)) for D <= 8
+// (w = 0 without weights).
 constexpr double kScreenMargin = 1.4210854715202004e-14;  // 2^-46
 
-// argKmin (and, with LSE, the log-sum-exp of -c2 d^2 in base 2) over the columns of one split.
+// argKmin of d^2_ij - w_j (w_j = 0 when w is null; with LSE, also the log-sum-exp of -c2 d^2 in
+// base 2, never combined with weights) over the columns of one split.
 // Each pair first gets the cheap expansion a_ij; only when a_ij is below the row's K-th key
 // plus the margin is the exact key computed and the sorted list updated, which after the
 // first columns is rare. For the log-sum-exp the row's running shift is -c2 times its
@@ -70,8 +83,8 @@ constexpr double kScreenMargin = 1.4210854715202004e-14;  // 2^-46
 // term 2^(-c2 a_ij - m) stays below 2^kLseSlack; it is updated before a tile's terms are added.
 template <int D, int K, int R, bool LSE>
 __global__ void __launch_bounds__(kBlock)
-knn_kernel(const float* __restrict__ x, const double* __restrict__ cols, const double* __restrict__ ymax,
-           int32_t* __restrict__ idx, float* __restrict__ dist, KeyIdx* __restrict__ partial,
+knn_kernel(const float* __restrict__ x, const double* __restrict__ cols, const float* __restrict__ w,
+           const double* __restrict__ ymax, int32_t* __restrict__ idx, float* __restrict__ dist, KeyIdx* __restrict__ partial,
            float* __restrict__ lse_out, LsePartial* __restrict__ lse_partial, int64_t M, int64_t N,
            int64_t cps, int Kout, double c2) {
   constexpr int P = (D + 2) & ~1;
@@ -128,7 +141,8 @@ knn_kernel(const float* __restrict__ x, const double* __restrict__ cols, const d
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         if (u < n && a[u] < thr[r]) {
-          const double key = sq_dist_key<D>(xd[r], yv[u]);
+          double key = sq_dist_key<D>(xd[r], yv[u]);
+          if (w) key -= (double)w[j + u];
           if (key < keys[r][K - 1]) {
             topk_insert<K>(keys[r], ids[r], key, (int32_t)(j + u));
             thr[r] = keys[r][K - 1] + marg[r];
@@ -245,12 +259,12 @@ merge_topk_kernel(const KeyIdx* __restrict__ partial, int32_t* __restrict__ idx,
 }
 
 template <int D, int K, bool LSE>
-hipError_t knn_dk(const float* x, const double* cols, const double* ymax, int32_t* idx, float* dist,
+hipError_t knn_dk(const float* x, const double* cols, const float* w, const double* ymax, int32_t* idx, float* dist,
                   void* partial, float* lse_out, double* lse_partial, int64_t M, int64_t N, int Kout, double c2,
                   const Plan& p, hipStream_t s) {
   dim3 grid((unsigned)p.row_blocks, (unsigned)p.splits);
   knn_kernel<D, K, (K <= 16 ? 2 : 1), LSE><<<grid, kBlock, 0, s>>>(
-      x, cols, ymax, idx, dist, reinterpret_cast<KeyIdx*>(partial), lse_out,
+      x, cols, w, ymax, idx, dist, reinterpret_cast<KeyIdx*>(partial), lse_out,
       reinterpret_cast<LsePartial*>(lse_partial), M, N, p.cols_per_split, Kout, c2);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
@@ -262,10 +276,10 @@ hipError_t knn_dk(const float* x, const double* cols, const double* ymax, int32_
 }
 
 template <int D, bool LSE>
-hipError_t knn_d(int Kb, const float* x, const double* cols, const double* ymax, int32_t* idx, float* dist,
+hipError_t knn_d(int Kb, const float* x, const double* cols, const float* w, const double* ymax, int32_t* idx, float* dist,
                  void* partial, float* lse_out, double* lse_partial, int64_t M, int64_t N, int Kout, double c2,
                  const Plan& p, hipStream_t s) {
-#define KEOPS_KNN_K(Kv) return knn_dk<D, Kv, LSE>(x, cols, ymax, idx, dist, partial, lse_out, lse_partial, M, N, Kout, c2, p, s)
+#define KEOPS_KNN_K(Kv) return knn_dk<D, Kv, LSE>(x, cols, w, ymax, idx, dist, partial, lse_out, lse_partial, M, N, Kout, c2, p, s)
   switch (Kb) {
     case 1: KEOPS_KNN_K(1);
     case 2: KEOPS_KNN_K(2);
@@ -283,23 +297,24 @@ hipError_t knn_d(int Kb, const float* x, const double* cols, const double* ymax,
 }  // namespace
 }  // namespace lowd
 
-hipError_t launch_knn_lowd(const float* x, const float* y, double* cols, double* ymax, int32_t* idx,
-                           float* dist, void* partial, float* lse_out, double* lse_partial, int64_t M, int64_t N,
-                           int D, int K, double c2, bool with_lse, const Plan& p, hipStream_t s) {
-  // column table (y_j, |y_j|^2) uncentred, then its largest norm for the screening margin
+hipError_t launch_knn_lowd(const float* x, const float* y, const float* w, double* cols, double* ymax,
+                           int32_t* idx, float* dist, void* partial, float* lse_out, double* lse_partial, int64_t M,
+                           int64_t N, int D, int K, double c2, bool with_lse, const Plan& p, hipStream_t s) {
+  // column table (y_j, |y_j|^2 - w_j) uncentred, then the largest |y_j|^2 + |w_j| for the
+  // screening margin
   hipError_t e = launch_prep_cols(y, cols, N, D, -1.0, false, s);
   if (e != hipSuccess) return e;
-  lowd::max_norm_kernel<<<1, 1024, 0, s>>>(cols, N, col_stride(D), D, ymax);
+  lowd::max_norm_kernel<<<1, 1024, 0, s>>>(cols, w, N, col_stride(D), D, ymax);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int Kb = lowd::argk_bucket(K);
   if (with_lse) {
-#define KEOPS_KNN(Dv) lowd::knn_d<Dv, true>(Kb, x, cols, ymax, idx, dist, partial, lse_out, lse_partial, M, N, K, c2, p, s)
+#define KEOPS_KNN(Dv) lowd::knn_d<Dv, true>(Kb, x, cols, w, ymax, idx, dist, partial, lse_out, lse_partial, M, N, K, c2, p, s)
     auto run = [&]() -> hipError_t { KEOPS_SWITCH_D(D, KEOPS_KNN) };
 #undef KEOPS_KNN
     return run();
   }
-#define KEOPS_KNN(Dv) lowd::knn_d<Dv, false>(Kb, x, cols, ymax, idx, dist, partial, lse_out, lse_partial, M, N, K, c2, p, s)
+#define KEOPS_KNN(Dv) lowd::knn_d<Dv, false>(Kb, x, cols, w, ymax, idx, dist, partial, lse_out, lse_partial, M, N, K, c2, p, s)
   auto run = [&]() -> hipError_t { KEOPS_SWITCH_D(D, KEOPS_KNN) };
 #undef KEOPS_KNN
   return run();

@@ -480,6 +480,55 @@ def check_grad_y_finite_differences_and_limits(o):
     assert np.allclose(a1, a2, rtol=1e-9, atol=1e-12)
 
 
+def check_argkmin_weighted_exact(o):
+    """Weighted keys d2 - w as exact rationals (grid points, weights on a dyadic grid, so the
+    float64 difference is exact), sorted by (key, j); planted equal keys (a column twice with
+    the same weight, and two columns whose distance difference the weights cancel) resolve to
+    the lower index."""
+    rng = _rng(28)
+    x = _grid_points(rng, (8, 3))
+    y = _grid_points(rng, (25, 3))
+    w = (rng.integers(-2 ** 10, 2 ** 10, size=25) * 2.0 ** -12).astype(np.float32)
+    y[9] = y[4]
+    w[9] = w[4]
+    # column 15 at distance^2 0.25 from x[2] with weight 0.25 - 0.0625 ties column 16 at 0.0625, weight 0
+    y[15] = x[2] + np.array([0.5, 0, 0], dtype=np.float32)
+    w[15] = np.float32(0.1875)
+    y[16] = x[2] + np.array([0, 0.25, 0], dtype=np.float32)
+    w[16] = np.float32(0.0)
+    for K in (1, 3, 25):
+        idx, keys = o.argkmin_weighted(x, y, w, K)
+        for i in range(x.shape[0]):
+            exact = []
+            for j in range(25):
+                d2 = sum((Fraction(float(x[i, d])) - Fraction(float(y[j, d]))) ** 2 for d in range(3))
+                exact.append((d2 - Fraction(float(w[j])), j))
+            exact.sort()
+            assert list(idx[i]) == [j for _, j in exact[:K]]
+            assert all(Fraction(keys[i, r]) == exact[r][0] for r in range(K))
+
+
+def check_argkmin_weighted_reductions(o):
+    """w = 0 is plain argKmin; a constant weight changes no index and shifts every key; with
+    w_j = 2 sigma^2 ln b_j the K = 1 column is the argmax of b_j exp(-d2/(2 sigma^2))
+    (numpy exp, well-separated maxima)."""
+    rng = _rng(29)
+    x = rng.random((30, 3))
+    y = rng.random((40, 3))
+    i0, k0 = o.argkmin(x, y, 5)
+    i1, k1 = o.argkmin_weighted(x, y, np.zeros(40), 5)
+    assert np.array_equal(i0, i1) and np.array_equal(k0, k1)
+    i2, k2 = o.argkmin_weighted(x, y, np.full(40, 0.375), 5)
+    assert np.array_equal(i0, i2) and np.allclose(k2, k0 - 0.375, rtol=0, atol=1e-15)
+    sigma = 0.2
+    b = rng.random(40) + 0.1
+    idx, _ = o.argkmin_weighted(x, y, 2 * sigma * sigma * np.log(b), 1)
+    vals = b[None, :] * np.exp(-((x[:, None, :] - y[None, :, :]) ** 2).sum(-1) / (2 * sigma * sigma))
+    top2 = np.sort(vals, axis=1)[:, -2:]
+    sep = top2[:, 1] > top2[:, 0] * (1 + 1e-9)
+    assert np.array_equal(idx[sep, 0], np.argmax(vals, axis=1)[sep])
+
+
 # ------------------------------------------------------------- batched backward (fp16 path)
 
 def check_batched_backward_vs_attention_autograd(o):
@@ -606,10 +655,11 @@ LSE_CHECKS = [check_lse_vs_scipy, check_lse_identical_columns, check_lse_far_clo
               check_lse_empty, check_lse_consistent_with_sum]
 ARGK_CHECKS = [check_argkmin_exact_bruteforce, check_argkmin_k1_is_argmin, check_argkmin_vs_kdtree,
                check_keys_exact_flag]
+WARGK_CHECKS = [check_argkmin_weighted_exact, check_argkmin_weighted_reductions]
 GRAD_CHECKS = [check_grad_vs_autograd, check_grad_finite_differences, check_grad_limits]
 GRADYB_CHECKS = [check_grad_yb_vs_autograd, check_grad_y_finite_differences_and_limits]
 BATCHED_GRAD_CHECKS = [check_batched_backward_vs_attention_autograd]
 SCALED_CHECKS = [check_scaled_vs_dense_diagonals, check_scaled_single_column]
 DIFFUSION_CHECKS = [check_diffusion_dense_formula, check_diffusion_spectrum, check_diffusion_sigma_infinity]
 ALL_CHECKS = (GAUSS_CHECKS + BATCHED_CHECKS + LSE_CHECKS + ARGK_CHECKS + GRAD_CHECKS + GRADYB_CHECKS +
-              BATCHED_GRAD_CHECKS + SCALED_CHECKS + DIFFUSION_CHECKS)
+              BATCHED_GRAD_CHECKS + SCALED_CHECKS + DIFFUSION_CHECKS + WARGK_CHECKS)

@@ -32,6 +32,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == {"keops_gauss_sum", "keops_lse", "keops_argkmin", "keops_gauss_sum_grad_x",
                           "keops_gauss_sum_grad_y", "keops_gauss_sum_grad_b", "keops_argkmin_lse",
                           "keops_gauss_sum_scaled", "keops_gauss_sum_backward", "keops_diffusion_scaling",
+                          "keops_argkmin_weighted",
                           "keops_workspace_bytes", "keops_status_string", "keops_last_error", "keops_version"}
     for name in names:
         assert hasattr(lib, name), name
@@ -231,3 +232,16 @@ def test_diffusion_scaling_rejects(lib):
     ws = lib.keops_workspace_bytes
     assert ws(9, 1, 0, 5000, 3, 1, 0, F32) >= 4 * 5000 * 4
     assert ws(9, 2, 0, 5000, 32, 1, 0, F16) > 0 and ws(9, 2, 0, 5000, 3, 1, 0, F16) == 0
+
+
+def test_argkmin_weighted_rejects(lib):
+    f = lib.keops_argkmin_weighted
+    W = 0x10000000 * 17
+    assert f(X, Y, None, IDX, None, 10, 10, 3, 4, WS, 1 << 30, None) == INVALID      # w NULL
+    assert f(X, Y, W + 2, IDX, None, 10, 10, 3, 4, WS, 1 << 30, None) == INVALID     # misaligned w
+    assert f(X, Y, IDX, IDX, None, 10, 10, 3, 4, WS, 1 << 30, None) == INVALID      # idx aliases w
+    assert f(X, Y, W, IDX, None, 10, 10, 3, 11, WS, 1 << 30, None) == INVALID       # K > N
+    assert f(X, Y, W, IDX, None, 10, 10, 9, 4, WS, 1 << 30, None) == UNSUPPORTED
+    assert f(X, Y, W, IDX, None, 0, 10, 3, 4, None, 0, None) == 0                    # M = 0
+    ws = lib.keops_workspace_bytes
+    assert ws(10, 1, 100, 100_000, 3, 1, 10, F32) == ws(2, 1, 100, 100_000, 3, 1, 10, F32) > 0

@@ -63,6 +63,10 @@ MUTATIONS = [
     ("batched backward: first batch's upstream gradient everywhere",
      'parts["x"].append(gauss_sum_grad_x(x[t], y[t], b[t], g[t], sigma, workers))',
      'parts["x"].append(gauss_sum_grad_x(x[t], y[t], b[t], g[0], sigma, workers))', pins.BATCHED_GRAD_CHECKS),
+    ("weighted argkmin: weight added", "kk = squared_distances(x[sl], y) - w[None, :]",
+     "kk = squared_distances(x[sl], y) + w[None, :]", pins.WARGK_CHECKS),
+    ("weighted argkmin: unstable sort", 'order = np.argsort(kk, axis=1, kind="stable")[:, :K]',
+     'order = (kk.shape[1] - 1 - np.argsort(kk[:, ::-1], axis=1, kind="stable"))[:, :K]', pins.WARGK_CHECKS),
 ]
 
 

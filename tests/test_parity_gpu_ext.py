@@ -237,3 +237,49 @@ def test_diffusion_operator_eigenvector():
     out = _host(pr.gauss_sum_scaled(_dev(x), _dev(x), v, sig, row_scale=s, col_scale=s))
     want = _host(v)
     assert np.max(np.abs(out - want) / want) <= 3e-4
+
+
+# ------------------------------------------------------------------ weighted argKmin
+WARGK_SHAPES = [(1, 1, 3, 1), (257, 1000, 3, 10), (1025, 513, 1, 4), (700, 2000, 2, 16), (300, 5000, 8, 64),
+                (2000, 70_001, 3, 1), (4097, 20_000, 3, 32)]
+
+
+def _grid(rng, shape, bits=24):
+    return (rng.integers(0, 2 ** bits, size=shape) * 2.0 ** -bits).astype(np.float32)
+
+
+@pytest.mark.parametrize("M,N,D,K", WARGK_SHAPES)
+def test_argkmin_weighted_shapes(M, N, D, K):
+    """Indices bit-exact, keys within 1e-6 relative (they are float64 keys rounded to float32)."""
+    import pairwise_reductions_amd as pr
+    _announce("argkmin_weighted", M=M, N=N, D=D, K=K)
+    rng = np.random.default_rng(M * 3 + N)
+    x, y = _grid(rng, (M, D)), _grid(rng, (N, D))
+    w = (rng.integers(-2 ** 20, 2 ** 20, size=N) * 2.0 ** -24).astype(np.float32)   # |w| < 1/16
+    idx, dist = pr.argkmin_weighted(_dev(x), _dev(y), _dev(w), K, with_dist=True)
+    want_i, want_k = oracle.argkmin_weighted(x, y, w, K, workers=8)
+    assert np.array_equal(_host(idx), want_i), "weighted argkmin indices"
+    got_k = _host(dist).astype(np.float64)
+    assert np.all(np.abs(got_k - want_k) <= 1e-6 * np.maximum(np.abs(want_k), 1e-30) + 1e-45)
+
+
+def test_argkmin_weighted_ties_and_large_weights():
+    """Planted equal keys (duplicate columns with equal weights, and distance differences the
+    weights cancel) resolve to the lower index; weights far larger than the distances, of both
+    signs, keep the ranking exact (the screening bound covers |w|)."""
+    import pairwise_reductions_amd as pr
+    _announce("argkmin_weighted_ties")
+    rng = np.random.default_rng(55)
+    M, N = 600, 3000
+    x = _grid(rng, (M, 3), bits=8)
+    y = _grid(rng, (N, 3), bits=8)
+    w = (rng.integers(-4, 5, size=N) * 2.0 ** -8).astype(np.float32)
+    y[100:200] = y[0:100]
+    w[100:200] = w[0:100]
+    idx = pr.argkmin_weighted(_dev(x), _dev(y), _dev(w), 8)
+    want, _ = oracle.argkmin_weighted(x, y, w, 8, workers=8)
+    assert np.array_equal(_host(idx), want)
+    w2 = (rng.integers(-2 ** 20, 2 ** 20, size=N) * 2.0 ** -4).astype(np.float32)    # |w| up to 65536
+    idx2 = pr.argkmin_weighted(_dev(x), _dev(y), _dev(w2), 5)
+    want2, _ = oracle.argkmin_weighted(x, y, w2, 5, workers=8)
+    assert np.array_equal(_host(idx2), want2)
