@@ -257,6 +257,34 @@ def bench_all(steps, warmup):
         rows[f"fp16_d_sweep_B64_C1_D{D}"] = {"ms": t * 1e3, "pairs_per_s": pairs / t}
         del q, k, v, out, ws
 
+    # bf16 and float32 inputs on the matrix cores at the flash page's Figure 5 shape (B=4,
+    # M=N=16384, D=C=32; float32 runs as fp16 hi + lo parts, three products each) and the
+    # float32 D sweep of its Figure 4 shape (B=64, M=N=16384, C=1).
+    for dtype, name in ((torch.bfloat16, "bf16"), (torch.float32, "f32")):
+        Bt, M, N, D, C = 4, 16384, 16384, 32, 32
+        rng = torch.Generator(device="cpu").manual_seed(11)
+        q = (torch.randn((Bt, M, D), generator=rng) / D ** 0.5).to(dtype).to(dev)
+        k = (torch.randn((Bt, N, D), generator=rng) / D ** 0.5).to(dtype).to(dev)
+        v = torch.randn((Bt, N, C), generator=rng).to(dtype).to(dev)
+        out = torch.empty((Bt, M, C), device=dev)
+        dt = _lib.KEOPS_BF16 if dtype == torch.bfloat16 else _lib.KEOPS_F32
+        ws = torch.empty(max(1, pr.workspace_bytes(0, Bt, M, N, D, C, 0, dt)), dtype=torch.uint8, device=dev)
+        t = _events_time(lambda: pr.gauss_sum(q, k, v, 1.0, out=out, workspace=ws), max(steps, 20), warmup)
+        pairs = float(Bt) * M * N
+        rows[f"batched_gauss_sum_{name}_B4_D32_C32"] = {"ms": t * 1e3, "pairs_per_s": pairs / t}
+    for D in (16, 32, 64, 128):
+        Bt, M, N, C = 64, 16384, 16384, 1
+        rng = torch.Generator(device="cpu").manual_seed(D + 100)
+        q = (torch.randn((Bt, M, D), generator=rng) / D ** 0.5).to(dev)
+        k = (torch.randn((Bt, N, D), generator=rng) / D ** 0.5).to(dev)
+        v = torch.randn((Bt, N, C), generator=rng).to(dev)
+        out = torch.empty((Bt, M, C), device=dev)
+        ws = torch.empty(max(1, pr.workspace_bytes(0, Bt, M, N, D, C, 0, _lib.KEOPS_F32)), dtype=torch.uint8,
+                         device=dev)
+        t = _events_time(lambda: pr.gauss_sum(q, k, v, 1.0, out=out, workspace=ws), max(steps, 5), warmup)
+        rows[f"f32_d_sweep_B64_C1_D{D}"] = {"ms": t * 1e3, "pairs_per_s": float(Bt) * M * N / t}
+        del q, k, v, out, ws
+
     # Diffusion operator (fp32, D=3): the q and d normalisation passes and one application of
     # diag(s) K diag(s) to a block of 4 vectors, N = 2^17.
     N, D, Cb = 1 << 17, 3, 4

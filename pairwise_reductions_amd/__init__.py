@@ -61,16 +61,19 @@ def workspace_bytes(op: int, B: int, M: int, N: int, D: int, C: int = 1, K: int 
 
 
 def _gauss_shapes(x, y, b):
-    """(B, M, N, D, C, dtype code, batched) of a Gauss-sum call: float32 2-D or fp16 3-D."""
+    """(B, M, N, D, C, dtype code, batched) of a Gauss-sum call: float32 (M, D) points, or
+    batched (B, M, D) points in float16, bfloat16 or float32."""
     torch = _torch()
-    if x.dtype == torch.float32:
+    if x.dtype == torch.float32 and x.dim() == 2:
         M, D = _dims(x, 2)
         N, _ = _dims(y, 2)
         _, C = _dims(b, 2)
         return 1, M, N, D, C, _lib.KEOPS_F32, False
-    dt = {torch.float16: _lib.KEOPS_F16, torch.bfloat16: _lib.KEOPS_BF16}.get(x.dtype)
+    dt = {torch.float16: _lib.KEOPS_F16, torch.bfloat16: _lib.KEOPS_BF16, torch.float32: _lib.KEOPS_F32}.get(x.dtype)
     if dt is None:
         raise ValueError(f"unsupported dtype {x.dtype}")
+    if y.dtype != x.dtype or b.dtype != x.dtype:
+        raise ValueError("x, y and b must share one dtype")
     B, M, D = _dims(x, 3)
     _, N, _ = _dims(y, 3)
     _, _, C = _dims(b, 3)
@@ -80,8 +83,9 @@ def _gauss_shapes(x, y, b):
 def gauss_sum(x, y, b, sigma: float, out=None, workspace=None):
     """s[i, c] = sum_j exp(-|x_i - y_j|^2 / (2 sigma^2)) b[j, c].
 
-    float32: x (M, D), y (N, D), b (N, C) -> (M, C).
-    float16: x (B, M, D), y (B, N, D), b (B, N, C) -> (B, M, C) float32.
+    float32: x (M, D), y (N, D), b (N, C) -> (M, C) (D <= 8 runs the float32 VALU kernels).
+    batched: x (B, M, D), y (B, N, D), b (B, N, C) in float16, bfloat16 or float32 with D a
+    multiple of 16 up to 128 (the matrix-core kernels) -> (B, M, C) float32.
     """
     torch = _torch()
     lib = _lib.load()
@@ -143,15 +147,17 @@ def gauss_sum_backward(x, y, b, g, sigma: float, need=("x", "y", "b"), workspace
 
 def diffusion_scaling(x, sigma: float, alpha: float, workspace=None):
     """(s, q, d) of the alpha-normalised diffusion operator diag(s) K diag(s), K_ij = k(x_i, x_j):
-    q = K 1, p = q^-alpha, d = p (K p), s = p / sqrt(d). x is float32 (N, D) or fp16 (B, N, D)."""
+    q = K 1, p = q^-alpha, d = p (K p), s = p / sqrt(d). x is float32 (N, D) or batched
+    (B, N, D) in float16, bfloat16 or float32 (D a multiple of 16)."""
     torch = _torch()
     lib = _lib.load()
-    if x.dtype == torch.float32:
+    if x.dtype == torch.float32 and x.dim() == 2:
         N, D = _dims(x, 2)
         B, dt, shape = 1, _lib.KEOPS_F32, (N,)
-    elif x.dtype == torch.float16:
+    elif x.dtype in (torch.float16, torch.bfloat16, torch.float32):
         B, N, D = _dims(x, 3)
-        dt, shape = _lib.KEOPS_F16, (B, N)
+        dt = {torch.float16: _lib.KEOPS_F16, torch.bfloat16: _lib.KEOPS_BF16, torch.float32: _lib.KEOPS_F32}[x.dtype]
+        shape = (B, N)
     else:
         raise ValueError(f"unsupported dtype {x.dtype}")
     s, q, d = (torch.empty(shape, dtype=torch.float32, device=x.device) for _ in range(3))

@@ -174,19 +174,29 @@ const char* keops_last_error(void) { return g_last_error.c_str(); }
 
 namespace {
 
-// Shape checks shared by the Gauss-sum family: the fp16 matrix-core family or the float32
-// low-D family (B = 1).
+// The two families of Gauss-sum kernels: float32 with D <= 8 runs the low-D VALU kernels
+// (B = 1); fp16, bf16, and float32 with larger D run the matrix-core kernels (any B).
+bool is_highd(keops_dtype dtype, int32_t D) { return dtype != KEOPS_F32 || D > keops::kMaxLowD; }
+
+keops::ElemType elem_of(keops_dtype dtype) {
+  return dtype == KEOPS_F16 ? keops::kElemF16 : (dtype == KEOPS_BF16 ? keops::kElemBF16 : keops::kElemF32);
+}
+
+size_t elem_size(keops_dtype dtype) { return dtype == KEOPS_F32 ? 4 : 2; }
+
+// Shape checks shared by the Gauss-sum family.
 int check_gauss_family(keops_dtype dtype, int64_t B, int32_t D, int32_t C, const char* what) {
-  if (dtype == KEOPS_BF16) return fail(KEOPS_ERR_UNSUPPORTED, "%s: the bf16 matrix-core path is not built (use KEOPS_F16)", what);
-  if (dtype == KEOPS_F16) {
+  if (dtype != KEOPS_F32 && dtype != KEOPS_F16 && dtype != KEOPS_BF16)
+    return fail(KEOPS_ERR_INVALID_ARG, "%s: unknown dtype %d", what, (int)dtype);
+  if (is_highd(dtype, D)) {
     if (!keops::highd_supported(D, C))
-      return fail(KEOPS_ERR_UNSUPPORTED, "%s: fp16 path needs D a multiple of 16 in [16, 128] and 1 <= C <= 64 "
-                  "(got D=%d C=%d)", what, D, C);
+      return fail(KEOPS_ERR_UNSUPPORTED, "%s: the matrix-core path needs D a multiple of 16 in [16, 128] and "
+                  "1 <= C <= 64 (got D=%d C=%d)", what, D, C);
     return KEOPS_OK;
   }
-  if (dtype != KEOPS_F32) return fail(KEOPS_ERR_INVALID_ARG, "%s: unknown dtype %d", what, (int)dtype);
-  if (B != 1) return fail(KEOPS_ERR_UNSUPPORTED, "%s: float32 path needs B = 1 (got %lld)", what, (long long)B);
-  if (D < 1 || D > keops::kMaxLowD || C < 1 || C > keops::kMaxLowC)
+  if (B != 1) return fail(KEOPS_ERR_UNSUPPORTED, "%s: the float32 path for D <= %d needs B = 1 (got %lld)", what,
+                          keops::kMaxLowD, (long long)B);
+  if (D < 1 || C < 1 || C > keops::kMaxLowC)
     return fail(KEOPS_ERR_UNSUPPORTED, "%s: float32 path needs 1 <= D <= %d and 1 <= C <= %d (got D=%d C=%d)", what,
                 keops::kMaxLowD, keops::kMaxLowC, D, C);
   return KEOPS_OK;
@@ -200,23 +210,28 @@ size_t lowd_scaled_bytes(int64_t M, int64_t N, int D, int C, bool col_scaled) {
 }
 
 // out = rscale . sum_j k_ij cscale_j b_j on either path; arguments already validated except
-// for the workspace. `ranges` lists the caller's buffers the workspace must not overlap.
-int gauss_sum_run(const void* x, const void* y, const void* b, bool b_f32, const float* rscale, const float* cscale,
-                  float* out, int64_t B, int64_t M, int64_t N, int32_t D, int32_t C, float sigma, bool half,
-                  void* workspace, size_t workspace_bytes, const Range* ranges, int nranges, hipStream_t stream) {
+// for the workspace. b is of type bt (the low-D path takes float32 only). `ranges` lists the
+// caller's buffers the workspace must not overlap.
+int gauss_sum_run(const void* x, const void* y, keops_dtype dtype, const void* b, keops::ElemType bt,
+                  const float* rscale, const float* cscale, float* out, int64_t B, int64_t M, int64_t N, int32_t D,
+                  int32_t C, float sigma, void* workspace, size_t workspace_bytes, const Range* ranges, int nranges,
+                  hipStream_t stream) {
   if (B == 0 || M == 0) return ok();
   if (N == 0) {
     KEOPS_HIP(keops::launch_fill(out, B * M * C, 0.0f, stream), "fill");
     return ok();
   }
-  const size_t need = half ? keops::highd_workspace_bytes(B, M, N, D, C, b_f32 || cscale != nullptr)
-                           : lowd_scaled_bytes(M, N, D, C, cscale != nullptr);
+  const bool highd = is_highd(dtype, D);
+  const keops::ElemType xy = elem_of(dtype);
+  const size_t need = highd ? keops::highd_workspace_bytes(B, M, N, D, C, xy,
+                                                           keops::highd_general(xy, bt, cscale != nullptr))
+                            : lowd_scaled_bytes(M, N, D, C, cscale != nullptr);
   KEOPS_TRY(check_workspace(workspace, workspace_bytes, need));
   for (int r = 0; r < nranges; ++r)
     if (overlaps(Range{workspace, need}, ranges[r]))
       return fail(KEOPS_ERR_INVALID_ARG, "workspace overlaps an input or an output");
-  if (half) {
-    KEOPS_HIP(keops::launch_gauss_sum_highd(x, y, b, b_f32, rscale, cscale, out, workspace, B, M, N, D, C, sigma,
+  if (highd) {
+    KEOPS_HIP(keops::launch_gauss_sum_highd(x, y, xy, b, bt, rscale, cscale, out, workspace, B, M, N, D, C, sigma,
                                             stream),
               "gauss_sum_highd");
     return ok();
@@ -248,24 +263,24 @@ int gauss_sum_impl(const void* x, const void* y, const void* b, const float* rsc
   KEOPS_TRY(check_extent(N, "N"));
   KEOPS_TRY(check_sigma(sigma));
   KEOPS_TRY(check_gauss_family(dtype, B, D, C, what));
-  const bool half = (dtype == KEOPS_F16);
-  const size_t es = half ? 2 : 4;
-  const size_t al = half ? 16 : 4;
+  const bool highd = is_highd(dtype, D);
+  const size_t es = elem_size(dtype);
+  const size_t al = highd ? 16 : 4;
   const Range rx{x, (size_t)(B * M * D) * es}, ry{y, (size_t)(B * N * D) * es}, rb{b, (size_t)(B * N * C) * es};
   const Range ro{out, (size_t)(B * M * C) * sizeof(float)};
   const Range rr{rscale, rscale ? (size_t)(B * M) * sizeof(float) : 0};
   const Range rc{cscale, cscale ? (size_t)(B * N) * sizeof(float) : 0};
   KEOPS_TRY(check_ptr(x, "x", al, rx.bytes));
   KEOPS_TRY(check_ptr(y, "y", al, ry.bytes));
-  KEOPS_TRY(check_ptr(b, "b", al, rb.bytes));
-  KEOPS_TRY(check_ptr(out, "out", half ? 16 : 4, ro.bytes));
+  KEOPS_TRY(check_ptr(b, "b", highd ? es : 4, rb.bytes));
+  KEOPS_TRY(check_ptr(out, "out", al, ro.bytes));
   if (rscale && !aligned(rscale, 4)) return fail(KEOPS_ERR_INVALID_ARG, "row_scale must be 4-byte aligned");
   if (cscale && !aligned(cscale, 4)) return fail(KEOPS_ERR_INVALID_ARG, "col_scale must be 4-byte aligned");
   if (overlaps(ro, rx) || overlaps(ro, ry) || overlaps(ro, rb) || overlaps(ro, rr) || overlaps(ro, rc))
     return fail(KEOPS_ERR_INVALID_ARG, "out overlaps an input");
   const Range all[] = {rx, ry, rb, ro, rr, rc};
-  return gauss_sum_run(x, y, b, false, rscale, cscale, out, B, M, N, D, C, sigma, half, workspace, workspace_bytes,
-                       all, 6, stream);
+  return gauss_sum_run(x, y, dtype, b, elem_of(dtype), rscale, cscale, out, B, M, N, D, C, sigma, workspace,
+                       workspace_bytes, all, 6, stream);
 }
 
 // Workspace of keops_gauss_sum_backward: the passes run one after another on the stream, so
@@ -277,7 +292,7 @@ size_t backward_bytes(int64_t B, int64_t M, int64_t N, int D, int C, bool half, 
   if (half) {
     if (want_x) take(keops::highd_grad_workspace_bytes(B, M, N, D, C));
     if (want_y) take(keops::highd_grad_workspace_bytes(B, N, M, D, C));
-    if (want_b) take(keops::highd_workspace_bytes(B, N, M, D, C, true));
+    if (want_b) take(keops::highd_workspace_bytes(B, N, M, D, C, keops::kElemF16, true));
   } else {
     if (want_x) take(lowd_layout(KEOPS_OP_GAUSS_SUM_GRAD_X, M, N, D, C, 0).total);
     if (want_y) take(lowd_layout(KEOPS_OP_GAUSS_SUM_GRAD_X, N, M, D, C, 0).total);
@@ -288,11 +303,11 @@ size_t backward_bytes(int64_t B, int64_t M, int64_t N, int D, int C, bool half, 
 
 // Workspace of keops_diffusion_scaling: ones, q, p and d (B N floats each), then the region of
 // the two Gauss sums.
-size_t diffusion_bytes(int64_t B, int64_t N, int D, bool half) {
+size_t diffusion_bytes(int64_t B, int64_t N, int D, keops_dtype dtype) {
   if (B == 0 || N == 0) return 0;
   const size_t vec = keops::align_up((size_t)(B * N) * sizeof(float));
-  const size_t sums = half ? keops::highd_workspace_bytes(B, N, N, D, 1, true)
-                           : lowd_layout(KEOPS_OP_GAUSS_SUM, N, N, D, 1, 0).total;
+  const size_t sums = is_highd(dtype, D) ? keops::highd_workspace_bytes(B, N, N, D, 1, elem_of(dtype), true)
+                                         : lowd_layout(KEOPS_OP_GAUSS_SUM, N, N, D, 1, 0).total;
   return 4 * vec + sums;
 }
 
@@ -305,12 +320,17 @@ size_t keops_workspace_bytes(int op, int64_t B, int64_t M, int64_t N, int32_t D,
   if (B < 0 || M < 0 || N < 0 || M > kMaxExtent || N > kMaxExtent) return 0;
   switch (op) {
     case KEOPS_OP_GAUSS_SUM:
-      if (dtype == KEOPS_F16) {
-        if (!keops::highd_supported(D, C)) return 0;
-        return keops::highd_workspace_bytes(B, M, N, D, C, false);
+    case KEOPS_OP_GAUSS_SUM_SCALED: {
+      if (dtype != KEOPS_F32 && dtype != KEOPS_F16 && dtype != KEOPS_BF16) return 0;
+      const bool scaled = op == KEOPS_OP_GAUSS_SUM_SCALED;
+      if (is_highd(dtype, D)) {
+        if (!keops::highd_supported(D, C) || B == 0 || M == 0 || N == 0) return 0;
+        const keops::ElemType xy = elem_of(dtype);
+        return keops::highd_workspace_bytes(B, M, N, D, C, xy, keops::highd_general(xy, xy, scaled));
       }
-      if (dtype != KEOPS_F32 || B != 1 || D < 1 || D > keops::kMaxLowD || C < 1 || C > keops::kMaxLowC) return 0;
-      return lowd_layout(op, M, N, D, C, 0).total;
+      if (B != 1 || D < 1 || C < 1 || C > keops::kMaxLowC) return 0;
+      return lowd_scaled_bytes(M, N, D, C, scaled);
+    }
     case KEOPS_OP_LSE:
       if (D < 1 || D > keops::kMaxLowD) return 0;
       return lowd_layout(op, M, N, D, 1, 0).total;
@@ -330,14 +350,8 @@ size_t keops_workspace_bytes(int op, int64_t B, int64_t M, int64_t N, int32_t D,
     case KEOPS_OP_GAUSS_SUM_GRAD_B:  // the Gauss sum over the transposed pairs
       if (D < 1 || D > keops::kMaxLowD || C < 1 || C > keops::kMaxLowC) return 0;
       return lowd_layout(KEOPS_OP_GAUSS_SUM, N, M, D, C, 0).total;
-    case KEOPS_OP_GAUSS_SUM_SCALED:
-      if (dtype == KEOPS_F16) {
-        if (!keops::highd_supported(D, C) || B == 0 || M == 0 || N == 0) return 0;
-        return keops::highd_workspace_bytes(B, M, N, D, C, true);
-      }
-      if (dtype != KEOPS_F32 || B != 1 || D < 1 || D > keops::kMaxLowD || C < 1 || C > keops::kMaxLowC) return 0;
-      return lowd_scaled_bytes(M, N, D, C, true);
     case KEOPS_OP_GAUSS_SUM_BACKWARD:
+      if (dtype == KEOPS_BF16 || (dtype == KEOPS_F32 && is_highd(dtype, D))) return 0;
       if (dtype == KEOPS_F16) {
         if (!keops::highd_supported(D, C) || B == 0 || M == 0 || N == 0) return 0;
         return backward_bytes(B, M, N, D, C, true, true, true, true);
@@ -346,12 +360,13 @@ size_t keops_workspace_bytes(int op, int64_t B, int64_t M, int64_t N, int32_t D,
       if (M == 0 || N == 0) return 0;
       return backward_bytes(B, M, N, D, C, false, true, true, true);
     case KEOPS_OP_DIFFUSION_SCALING:
-      if (dtype == KEOPS_F16) {
+      if (dtype != KEOPS_F32 && dtype != KEOPS_F16 && dtype != KEOPS_BF16) return 0;
+      if (is_highd(dtype, D)) {
         if (!keops::highd_supported(D, 1)) return 0;
-        return diffusion_bytes(B, N, D, true);
+      } else if (B != 1 || D < 1) {
+        return 0;
       }
-      if (dtype != KEOPS_F32 || B != 1 || D < 1 || D > keops::kMaxLowD) return 0;
-      return diffusion_bytes(B, N, D, false);
+      return diffusion_bytes(B, N, D, dtype);
   }
   return 0;
 }
@@ -380,6 +395,9 @@ int keops_gauss_sum_backward(const void* x, const void* y, const void* b, const 
   KEOPS_TRY(check_extent(N, "N"));
   KEOPS_TRY(check_sigma(sigma));
   KEOPS_TRY(check_gauss_family(dtype, B, D, C, "gauss_sum_backward"));
+  if (dtype == KEOPS_BF16 || (dtype == KEOPS_F32 && is_highd(dtype, D)))
+    return fail(KEOPS_ERR_UNSUPPORTED, "gauss_sum_backward: the matrix-core backward takes fp16 inputs "
+                "(float32 gradients are built for D <= %d)", keops::kMaxLowD);
   const bool half = (dtype == KEOPS_F16);
   const size_t es = half ? 2 : 4;
   const size_t al = half ? 16 : 4;
@@ -425,8 +443,8 @@ int keops_gauss_sum_backward(const void* x, const void* y, const void* b, const 
       KEOPS_HIP(keops::launch_gauss_sum_grad_highd(y, x, b, false, g, true, grad_y, ws, B, N, M, D, C, sigma, stream),
                 "grad_y_highd");
     if (want_b)
-      KEOPS_HIP(keops::launch_gauss_sum_highd(y, x, g, true, nullptr, nullptr, grad_b, ws, B, N, M, D, C, sigma,
-                                              stream),
+      KEOPS_HIP(keops::launch_gauss_sum_highd(y, x, keops::kElemF16, g, keops::kElemF32, nullptr, nullptr, grad_b, ws,
+                                              B, N, M, D, C, sigma, stream),
                 "grad_b_highd");
     return ok();
   }
@@ -468,18 +486,18 @@ int keops_diffusion_scaling(const void* x, float* s, float* q, float* d, int64_t
   KEOPS_TRY(check_sigma(sigma));
   if (!std::isfinite(alpha)) return fail(KEOPS_ERR_INVALID_ARG, "alpha must be finite (got %g)", (double)alpha);
   KEOPS_TRY(check_gauss_family(dtype, B, D, 1, "diffusion_scaling"));
-  const bool half = (dtype == KEOPS_F16);
-  const size_t es = half ? 2 : 4;
+  const bool highd = is_highd(dtype, D);
+  const size_t es = elem_size(dtype);
   const size_t n = (size_t)(B * N);
   const Range rx{x, n * D * es}, rs{s, n * 4}, rq{q, q ? n * 4 : 0}, rd{d, d ? n * 4 : 0};
-  KEOPS_TRY(check_ptr(x, "x", half ? 16 : 4, rx.bytes));
+  KEOPS_TRY(check_ptr(x, "x", highd ? 16 : 4, rx.bytes));
   KEOPS_TRY(check_ptr(s, "s", 4, rs.bytes));
   if ((q && !aligned(q, 4)) || (d && !aligned(d, 4))) return fail(KEOPS_ERR_INVALID_ARG, "q and d must be 4-byte aligned");
   if (overlaps(rs, rx) || overlaps(rq, rx) || overlaps(rd, rx) || overlaps(rs, rq) || overlaps(rs, rd) ||
       overlaps(rq, rd))
     return fail(KEOPS_ERR_INVALID_ARG, "s, q and d must not overlap x or each other");
   if (n == 0) return ok();
-  const size_t need = diffusion_bytes(B, N, D, half);
+  const size_t need = diffusion_bytes(B, N, D, dtype);
   KEOPS_TRY(check_workspace(workspace, workspace_bytes, need));
   const Range rw{workspace, need};
   if (overlaps(rw, rx) || overlaps(rw, rs) || overlaps(rw, rq) || overlaps(rw, rd))
@@ -495,11 +513,11 @@ int keops_diffusion_scaling(const void* x, float* s, float* q, float* d, int64_t
   KEOPS_HIP(keops::launch_fill(ones, (int64_t)n, 1.0f, stream), "fill");
   // q = K 1; p = q^-alpha; d = p (K p); s = p / sqrt(d)
   const Range none[] = {};
-  KEOPS_TRY(gauss_sum_run(x, x, ones, true, nullptr, nullptr, qb, B, N, N, D, 1, sigma, half, sub, sub_bytes, none, 0,
-                          stream));
+  KEOPS_TRY(gauss_sum_run(x, x, dtype, ones, keops::kElemF32, nullptr, nullptr, qb, B, N, N, D, 1, sigma, sub,
+                          sub_bytes, none, 0, stream));
   KEOPS_HIP(keops::launch_pow(qb, pb, (int64_t)n, -alpha, stream), "pow");
-  KEOPS_TRY(gauss_sum_run(x, x, pb, true, pb, nullptr, db, B, N, N, D, 1, sigma, half, sub, sub_bytes, none, 0,
-                          stream));
+  KEOPS_TRY(gauss_sum_run(x, x, dtype, pb, keops::kElemF32, pb, nullptr, db, B, N, N, D, 1, sigma, sub, sub_bytes,
+                          none, 0, stream));
   KEOPS_HIP(keops::launch_div_sqrt(pb, db, s, (int64_t)n, stream), "div_sqrt");
   return ok();
 }

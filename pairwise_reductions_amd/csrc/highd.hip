@@ -26,6 +26,8 @@ using hd::slot_key;
 template <typename T>
 __device__ inline float to_f32(T v) { return (float)v; }
 
+typedef __bf16 bf16_t;
+
 // |c_j w_j|_2 of column j of batch t (c = 1 when cscale is null).
 template <typename T>
 __device__ inline float weight_norm(const T* __restrict__ w, const float* __restrict__ cscale, int64_t t, int64_t j,
@@ -72,12 +74,13 @@ enum { kCopy = 0, kNormFwd = 1, kNormGrad = 2 };
 constexpr int kMaxPrepD = 128;
 constexpr int kMaxPrepC = 64;
 
-template <typename T, int kMode>
+template <typename TK, typename T, int kMode>
 __global__ void __launch_bounds__(256)
-col_prep_kernel(const _Float16* __restrict__ k, const T* __restrict__ w, const float* __restrict__ cscale,
+col_prep_kernel(const TK* __restrict__ k, const T* __restrict__ w, const float* __restrict__ cscale,
                 const float* __restrict__ nmax, float* __restrict__ beta, _Float16* __restrict__ wp,
-                _Float16* __restrict__ yp, int64_t N, int64_t Npad, int D, int Dp, int C, int Cw, float cs) {
-  __shared__ __attribute__((aligned(16))) _Float16 sk[32][kMaxPrepD];
+                _Float16* __restrict__ wpl, _Float16* __restrict__ yp, int64_t N, int64_t Npad, int D, int Dp, int C,
+                int Cw, float cs) {
+  __shared__ float sk[32][kMaxPrepD + 1];
   __shared__ float sw[32][kMaxPrepC + 1];
   __shared__ float sinv[32];
   const int tid = threadIdx.x;
@@ -85,13 +88,10 @@ col_prep_kernel(const _Float16* __restrict__ k, const T* __restrict__ w, const f
   const int64_t j0 = (int64_t)blockIdx.x * 32;
   const int live = N - j0 >= 32 ? 32 : (N > j0 ? (int)(N - j0) : 0);
 
-  // keys (D is a multiple of 8, so rows move in 16-byte chunks)
-  const int kch = 32 * D / 8;
-  for (int c = tid; c < kch; c += 256) {
-    const int key = c / (D / 8), col = (c % (D / 8)) * 8;
-    half8 v = half8{};
-    if (key < live) v = *reinterpret_cast<const half8*>(k + (t * N + j0 + key) * D + col);
-    *reinterpret_cast<half8*>(&sk[key][col]) = v;
+  // keys, contiguous in global memory: thread e takes element e of the block's rows
+  for (int e = tid; e < 32 * D; e += 256) {
+    const int key = e / D, d = e % D;
+    sk[key][d] = key < live ? to_f32(k[(t * N + j0) * D + e]) : 0.0f;
   }
   // weights, times the column scale
   for (int e = tid; e < 32 * C; e += 256) {
@@ -109,10 +109,7 @@ col_prep_kernel(const _Float16* __restrict__ k, const T* __restrict__ w, const f
   {
     const int key = tid >> 3, part = tid & 7;
     float kn = 0.0f, wn = 0.0f;
-    for (int d = part; d < D; d += 8) {
-      const float v = (float)sk[key][d];
-      kn = fmaf(v, v, kn);
-    }
+    for (int d = part; d < D; d += 8) kn = fmaf(sk[key][d], sk[key][d], kn);
     for (int c = part; c < C; c += 8) wn = fmaf(sw[key][c], sw[key][c], wn);
 #pragma unroll
     for (int o = 1; o < 8; o <<= 1) {
@@ -149,15 +146,20 @@ col_prep_kernel(const _Float16* __restrict__ k, const T* __restrict__ w, const f
     for (int e = tid; e < 32 * YC; e += 256) {
       const int ch = e / 32, key = slot_key(e % 32);
       _Float16 v = (_Float16)0.0f;
-      if (ch < D) v = sk[key][ch];
+      if (ch < D) v = (_Float16)sk[key][ch];
       else if (ch == Dp && key < live) v = (_Float16)1.0f;
       yd[e] = v;
     }
   } else {
+    // forward layout; with wpl the fp16 lo parts of float32 weights as well
     _Float16* dst = wp + (t * Npad + j0) * Cw;
+    _Float16* dsl = wpl ? wpl + (t * Npad + j0) * Cw : nullptr;
     for (int e = tid; e < 32 * Cw; e += 256) {
       const int c = e / 32, key = slot_key(e % 32);
-      dst[e] = (_Float16)(c < C ? sw[key][c] * sinv[key] : 0.0f);
+      const float v = c < C ? sw[key][c] * sinv[key] : 0.0f;
+      const _Float16 h = (_Float16)v;
+      dst[e] = h;
+      if (dsl) dsl[e] = (_Float16)(v - (float)h);
     }
   }
 }
@@ -226,17 +228,20 @@ struct Carve {
 
 struct FwdLayout {
   Split sp;
-  size_t nmax, beta, vp, part, total;
+  size_t nmax, beta, vp, vpl, part, total;
 };
 
-FwdLayout fwd_layout(int64_t B, int64_t M, int64_t N, int D, int C, bool general, int num_cus) {
+FwdLayout fwd_layout(int64_t B, int64_t M, int64_t N, int D, int C, ElemType xy, bool general, int num_cus) {
   FwdLayout L;
   const int Cp = hd::padded_channels(C);
-  L.sp = plan_split(B, M, N, hd::kWaves * hd::fwd_query_tiles(hd::padded_features(D), Cp) * 16, num_cus);
+  const bool split = xy == kElemF32;
+  L.sp = plan_split(B, M, N, hd::kWaves * hd::fwd_query_tiles(hd::padded_features(D), Cp, split) * 16, num_cus);
   Carve c;
+  const size_t table = (size_t)B * L.sp.Npad * Cp * sizeof(_Float16);
   L.nmax = c.take(general ? (size_t)B * sizeof(float) : 0);
   L.beta = c.take((size_t)B * L.sp.Npad * sizeof(float));
-  L.vp = c.take((size_t)B * L.sp.Npad * Cp * sizeof(_Float16));
+  L.vp = c.take(table);
+  L.vpl = c.take(split ? table : 0);
   L.part = c.take(L.sp.splits > 1 ? (size_t)L.sp.splits * B * M * C * sizeof(float) : 0);
   L.total = c.off;
   return L;
@@ -268,12 +273,22 @@ float cs_of(float sigma) {
   return (float)(1.4426950408889634 / (s * s));  // tau log2(e)
 }
 
-hipError_t fwd_dispatch(const hd::FwdArgs& a) {
+template <typename TIn>
+hipError_t fwd_dispatch_t(const hd::FwdArgs& a) {
   switch (hd::padded_features(a.D)) {
-    case 32: return hd::fwd_launch<32>(a);
-    case 64: return hd::fwd_launch<64>(a);
-    case 96: return hd::fwd_launch<96>(a);
-    case 128: return hd::fwd_launch<128>(a);
+    case 32: return hd::fwd_launch<TIn, 32>(a);
+    case 64: return hd::fwd_launch<TIn, 64>(a);
+    case 96: return hd::fwd_launch<TIn, 96>(a);
+    case 128: return hd::fwd_launch<TIn, 128>(a);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t fwd_dispatch(const hd::FwdArgs& a, ElemType xy) {
+  switch (xy) {
+    case kElemF16: return fwd_dispatch_t<_Float16>(a);
+    case kElemBF16: return fwd_dispatch_t<bf16_t>(a);
+    case kElemF32: return fwd_dispatch_t<float>(a);
   }
   return hipErrorInvalidValue;
 }
@@ -308,9 +323,13 @@ hipError_t weight_norm_max(const T* w, const float* cscale, float* nmax, int64_t
 
 bool highd_supported(int D, int C) { return D >= 16 && D <= 128 && D % 16 == 0 && C >= 1 && C <= 64; }
 
-size_t highd_workspace_bytes(int64_t B, int64_t M, int64_t N, int D, int C, bool general) {
+bool highd_general(ElemType xy, ElemType bt, bool col_scaled) {
+  return xy != kElemF16 || bt != kElemF16 || col_scaled;
+}
+
+size_t highd_workspace_bytes(int64_t B, int64_t M, int64_t N, int D, int C, ElemType xy, bool general) {
   if (B == 0 || M == 0 || N == 0) return 0;
-  return fwd_layout(B, M, N, D, C, general, device_cus()).total;
+  return fwd_layout(B, M, N, D, C, xy, general, device_cus()).total;
 }
 
 size_t highd_grad_workspace_bytes(int64_t B, int64_t M, int64_t N, int D, int C) {
@@ -318,46 +337,76 @@ size_t highd_grad_workspace_bytes(int64_t B, int64_t M, int64_t N, int D, int C)
   return grad_layout(B, M, N, D, C, device_cus()).total;
 }
 
-hipError_t launch_gauss_sum_highd(const void* x, const void* y, const void* b, bool b_f32, const float* rscale,
-                                  const float* cscale, float* out, void* workspace, int64_t B, int64_t M, int64_t N,
-                                  int D, int C, float sigma, hipStream_t s) {
-  const bool general = b_f32 || cscale != nullptr;
-  const FwdLayout L = fwd_layout(B, M, N, D, C, general, device_cus());
+namespace {
+
+// Column tables of the general forward form for keys of type TK and weights of type T.
+template <typename TK, typename T>
+hipError_t fwd_prep_general(const TK* k, const T* w, const float* cscale, float* nmax, float* beta, _Float16* vp,
+                            _Float16* vpl, int64_t B, int64_t N, int64_t Npad, int D, int C, int Cp, float cs,
+                            hipStream_t s) {
+  hipError_t e = weight_norm_max(w, cscale, nmax, B, N, C, s);
+  if (e != hipSuccess) return e;
+  col_prep_kernel<TK, T, kNormFwd><<<dim3((unsigned)(Npad / 32), (unsigned)B), 256, 0, s>>>(
+      k, w, cscale, nmax, beta, vp, vpl, nullptr, N, Npad, D, 0, C, Cp, cs);
+  return hipGetLastError();
+}
+
+template <typename TK>
+hipError_t fwd_prep_general_w(const TK* k, const void* w, ElemType bt, const float* cscale, float* nmax, float* beta,
+                              _Float16* vp, _Float16* vpl, int64_t B, int64_t N, int64_t Npad, int D, int C, int Cp,
+                              float cs, hipStream_t s) {
+  switch (bt) {
+    case kElemF16:
+      return fwd_prep_general(k, static_cast<const _Float16*>(w), cscale, nmax, beta, vp, vpl, B, N, Npad, D, C, Cp,
+                              cs, s);
+    case kElemBF16:
+      return fwd_prep_general(k, static_cast<const bf16_t*>(w), cscale, nmax, beta, vp, vpl, B, N, Npad, D, C, Cp,
+                              cs, s);
+    case kElemF32:
+      return fwd_prep_general(k, static_cast<const float*>(w), cscale, nmax, beta, vp, vpl, B, N, Npad, D, C, Cp, cs,
+                              s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_gauss_sum_highd(const void* x, const void* y, ElemType xy, const void* b, ElemType bt,
+                                  const float* rscale, const float* cscale, float* out, void* workspace, int64_t B,
+                                  int64_t M, int64_t N, int D, int C, float sigma, hipStream_t s) {
+  const bool general = highd_general(xy, bt, cscale != nullptr);
+  const FwdLayout L = fwd_layout(B, M, N, D, C, xy, general, device_cus());
   char* ws = static_cast<char*>(workspace);
   float* nmax = reinterpret_cast<float*>(ws + L.nmax);
   float* beta = reinterpret_cast<float*>(ws + L.beta);
   _Float16* vp = reinterpret_cast<_Float16*>(ws + L.vp);
+  _Float16* vpl = xy == kElemF32 ? reinterpret_cast<_Float16*>(ws + L.vpl) : nullptr;
   float* part = reinterpret_cast<float*>(ws + L.part);
-  const _Float16* k = static_cast<const _Float16*>(y);
   const float cs = cs_of(sigma);
   const int Cp = hd::padded_channels(C);
-  const dim3 pgrid((unsigned)(L.sp.Npad / 32), (unsigned)B);
   hipError_t e;
   if (!general) {
-    col_prep_kernel<_Float16, kCopy><<<pgrid, 256, 0, s>>>(k, static_cast<const _Float16*>(b), nullptr, nullptr, beta,
-                                                           vp, nullptr, N, L.sp.Npad, D, 0, C, Cp, cs);
+    col_prep_kernel<_Float16, _Float16, kCopy><<<dim3((unsigned)(L.sp.Npad / 32), (unsigned)B), 256, 0, s>>>(
+        static_cast<const _Float16*>(y), static_cast<const _Float16*>(b), nullptr, nullptr, beta, vp, nullptr,
+        nullptr, N, L.sp.Npad, D, 0, C, Cp, cs);
     e = hipGetLastError();
-  } else if (b_f32) {
-    const float* w = static_cast<const float*>(b);
-    e = weight_norm_max(w, cscale, nmax, B, N, C, s);
-    if (e != hipSuccess) return e;
-    col_prep_kernel<float, kNormFwd><<<pgrid, 256, 0, s>>>(k, w, cscale, nmax, beta, vp, nullptr, N, L.sp.Npad, D, 0,
-                                                           C, Cp, cs);
-    e = hipGetLastError();
+  } else if (xy == kElemF16) {
+    e = fwd_prep_general_w(static_cast<const _Float16*>(y), b, bt, cscale, nmax, beta, vp, vpl, B, N, L.sp.Npad, D,
+                           C, Cp, cs, s);
+  } else if (xy == kElemBF16) {
+    e = fwd_prep_general_w(static_cast<const bf16_t*>(y), b, bt, cscale, nmax, beta, vp, vpl, B, N, L.sp.Npad, D, C,
+                           Cp, cs, s);
   } else {
-    const _Float16* w = static_cast<const _Float16*>(b);
-    e = weight_norm_max(w, cscale, nmax, B, N, C, s);
-    if (e != hipSuccess) return e;
-    col_prep_kernel<_Float16, kNormFwd><<<pgrid, 256, 0, s>>>(k, w, cscale, nmax, beta, vp, nullptr, N, L.sp.Npad, D,
-                                                              0, C, Cp, cs);
-    e = hipGetLastError();
+    e = fwd_prep_general_w(static_cast<const float*>(y), b, bt, cscale, nmax, beta, vp, vpl, B, N, L.sp.Npad, D, C,
+                           Cp, cs, s);
   }
   if (e != hipSuccess) return e;
   hd::FwdArgs a;
-  a.q = static_cast<const _Float16*>(x);
-  a.k = k;
+  a.q = x;
+  a.k = y;
   a.beta = beta;
   a.vp = vp;
+  a.vpl = vpl;
   a.out = L.sp.splits > 1 ? part : out;
   a.rscale = rscale;
   a.oscale = general ? nmax : nullptr;
@@ -370,7 +419,7 @@ hipError_t launch_gauss_sum_highd(const void* x, const void* y, const void* b, b
   a.C = C;
   a.grid = dim3((unsigned)L.sp.row_blocks, (unsigned)L.sp.splits, (unsigned)B);
   a.stream = s;
-  e = fwd_dispatch(a);
+  e = fwd_dispatch(a, xy);
   if (e != hipSuccess || L.sp.splits == 1) return e;
   return combine(part, out, B * M * C, L.sp.splits, s);
 }
@@ -396,14 +445,14 @@ hipError_t launch_gauss_sum_grad_highd(const void* x, const void* y, const void*
     const float* w = static_cast<const float*>(bv);
     e = weight_norm_max(w, nullptr, nmax, B, N, C, s);
     if (e != hipSuccess) return e;
-    col_prep_kernel<float, kNormGrad><<<pgrid, 256, 0, s>>>(k, w, nullptr, nmax, beta, bvp, yp, N, L.sp.Npad, D, Dp,
-                                                            C, Ck, cs);
+    col_prep_kernel<_Float16, float, kNormGrad><<<pgrid, 256, 0, s>>>(k, w, nullptr, nmax, beta, bvp, nullptr, yp, N,
+                                                                      L.sp.Npad, D, Dp, C, Ck, cs);
   } else {
     const _Float16* w = static_cast<const _Float16*>(bv);
     e = weight_norm_max(w, nullptr, nmax, B, N, C, s);
     if (e != hipSuccess) return e;
-    col_prep_kernel<_Float16, kNormGrad><<<pgrid, 256, 0, s>>>(k, w, nullptr, nmax, beta, bvp, yp, N, L.sp.Npad, D,
-                                                               Dp, C, Ck, cs);
+    col_prep_kernel<_Float16, _Float16, kNormGrad><<<pgrid, 256, 0, s>>>(k, w, nullptr, nmax, beta, bvp, nullptr, yp,
+                                                                         N, L.sp.Npad, D, Dp, C, Ck, cs);
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -25,7 +25,10 @@ constexpr float kLogFloor = -60.0f; // log2 of the smallest column weight kept a
 // Query tiles (16 rows each) per wave, forward kernel. Measured on B=4, 16384^2, D=C=32: more
 // independent tiles per wave beat more resident waves, since the matrix cores and the exp
 // pipe overlap within a wave. Wider tiles take fewer to stay within 256 VGPRs.
-constexpr int fwd_query_tiles(int D, int C) { return (D == 32 && C <= 32) ? 8 : (D <= 64 ? 4 : 2); }
+// Float32 inputs (split into fp16 hi + lo parts) hold twice the operands, so they take fewer.
+constexpr int fwd_query_tiles(int D, int C, bool split) {
+  return split ? (D <= 64 ? 4 : 2) : ((D == 32 && C <= 32) ? 8 : (D <= 64 ? 4 : 2));
+}
 // The gradient kernel holds three products per subtile, so it takes fewer.
 constexpr int grad_query_tiles(int D) { return D <= 32 ? 4 : (D <= 64 ? 2 : 1); }
 // Features run in steps of 32 (the K of one MFMA) and are read as zero past D; output and
@@ -59,10 +62,11 @@ __host__ __device__ inline int key_slot(int o) {
 // split's keys, where the stored column weights vp and the key terms beta may carry a per-key
 // factor (see the column preparation in highd.hip).
 struct FwdArgs {
-  const _Float16* q;
-  const _Float16* k;
+  const void* q;           // [B][M][D] of the input type
+  const void* k;           // [B][N][D] of the input type
   const float* beta;       // [B][Npad]: -|k_j|^2/2 (+ log2 of the key weight / cs), -inf past N
   const _Float16* vp;      // [B][Npad/32][Cp][32] key-permuted column weights
+  const _Float16* vpl;     // the same for the lo parts (float32 inputs), else null
   float* out;              // [S][B][M][C]
   const float* rscale;     // [B][M] or null
   const float* oscale;     // [B] or null
@@ -92,7 +96,7 @@ struct GradArgs {
   hipStream_t stream;
 };
 
-template <int Dp>
+template <typename TIn, int Dp>
 hipError_t fwd_launch(const FwdArgs& a);
 template <int Dp>
 hipError_t grad_launch(const GradArgs& a);

@@ -4,7 +4,9 @@
 
 namespace keops {
 namespace hd {
-template hipError_t fwd_launch<128>(const FwdArgs&);
+template hipError_t fwd_launch<_Float16, 128>(const FwdArgs&);
+template hipError_t fwd_launch<__bf16, 128>(const FwdArgs&);
+template hipError_t fwd_launch<float, 128>(const FwdArgs&);
 template hipError_t grad_launch<128>(const GradArgs&);
 }  // namespace hd
 }  // namespace keops

@@ -4,7 +4,9 @@
 
 namespace keops {
 namespace hd {
-template hipError_t fwd_launch<32>(const FwdArgs&);
+template hipError_t fwd_launch<_Float16, 32>(const FwdArgs&);
+template hipError_t fwd_launch<__bf16, 32>(const FwdArgs&);
+template hipError_t fwd_launch<float, 32>(const FwdArgs&);
 template hipError_t grad_launch<32>(const GradArgs&);
 }  // namespace hd
 }  // namespace keops

@@ -1,9 +1,9 @@
 // Forward matrix-core Gauss sum ("Fast Gauss Sums via Flash Attention", eq. (1), computed
 // from the squared-norm expansion ||q - k||^2 = ||q||^2 + ||k||^2 - 2 q.k, so the O(M N D)
 // part is a dense contraction on the matrix cores). Included by the per-feature-width
-// sources, each of which instantiates fwd_launch<Dp> for one padded D.
+// sources, each of which instantiates fwd_launch<TIn, Dp> for one padded D.
 //
-// Tiles are 16 queries x 32 keys on v_mfma_f32_16x16x32_f16. Per wave: QT query tiles.
+// Tiles are 16 queries x 32 keys on 16x16x32 MFMAs. Per wave: QT query tiles.
 //   S^T = K Q^T + B   one MFMA per 16 keys and 32 features; the accumulator starts from
 //                     B[j] = beta_j, so S'_ij = q_i.k_j + beta_j comes out whole;
 //   a_ij = cs S'_ij + alpha_i,  alpha_i = -cs |q_i|^2 / 2 - m_i   (one FMA);
@@ -11,6 +11,16 @@
 // P never moves between lanes (the key order of slot_key()); m_i is a running base-2 shift,
 // set by the first subtile and raised only when a subtile would produce a term above
 // 2^kSlack (then O is rescaled).
+//
+// Input types (TIn, the type of q and k):
+//   _Float16  fp16 MFMAs throughout;
+//   __bf16    S^T on bf16 MFMAs (exact products of the inputs), the weights arrive as a
+//             normalised fp16 table, P and O as for fp16;
+//   float     every operand is split into fp16 hi + lo parts (v = hi + lo to about 2^-22
+//             relative) and each product takes three MFMAs, hi.hi + lo.hi + hi.lo (the lo.lo
+//             term is below 2^-22); q and k are split as they are read, P in registers and
+//             the weights by the column preparation. This keeps the matrix cores at float32
+//             accuracy for the cost of three times the MFMA work.
 #pragma once
 
 #include "highd_common.h"
@@ -23,21 +33,102 @@ namespace keops {
 namespace hd {
 namespace {
 
-template <int D, int C, int QT>
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// One 8-feature slice of a point, as the S^T product consumes it.
+template <typename TIn>
+struct Op;
+template <>
+struct Op<_Float16> {
+  half8 h;
+};
+template <>
+struct Op<__bf16> {
+  bf16x8 h;
+};
+template <>
+struct Op<float> {
+  half8 h, l;
+};
+
+template <typename TIn>
+constexpr bool kSplit = std::is_same<TIn, float>::value;
+
+// Read 8 consecutive elements at p (16-byte aligned) into an operand; with kNorm, add their
+// squares to nrm in float32.
+template <typename TIn, bool kNorm>
+__device__ __forceinline__ Op<TIn> load_op(const TIn* p, float& nrm) {
+  Op<TIn> o;
+  if constexpr (kSplit<TIn>) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const float v = s < 4 ? a[s] : b[s - 4];
+      if constexpr (kNorm) nrm = fmaf(v, v, nrm);
+      o.h[s] = (_Float16)v;
+      o.l[s] = (_Float16)(v - (float)o.h[s]);
+    }
+  } else {
+    if constexpr (std::is_same<TIn, _Float16>::value)
+      o.h = *reinterpret_cast<const half8*>(p);
+    else
+      o.h = *reinterpret_cast<const bf16x8*>(p);
+    if constexpr (kNorm) {
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const float v = (float)o.h[s];
+        nrm = fmaf(v, v, nrm);
+      }
+    }
+  }
+  return o;
+}
+
+template <typename TIn>
+__device__ __forceinline__ Op<TIn> zero_op() {
+  Op<TIn> o;
+  if constexpr (kSplit<TIn>) {
+    o.h = half8{};
+    o.l = half8{};
+  } else {
+    o.h = decltype(o.h){};
+  }
+  return o;
+}
+
+// acc += k-slice (A operand, rows = keys) x q-slice (B operand, columns = queries)
+template <typename TIn>
+__device__ __forceinline__ f32x4 s_mfma(const Op<TIn>& k, const Op<TIn>& q, f32x4 acc) {
+  if constexpr (kSplit<TIn>) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(k.h, q.h, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(k.l, q.h, acc, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(k.h, q.l, acc, 0, 0, 0);
+  } else if constexpr (std::is_same<TIn, _Float16>::value) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(k.h, q.h, acc, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(k.h, q.h, acc, 0, 0, 0);
+  }
+}
+
+template <typename TIn, int D, int C, int QT, int kStage>
 __global__ void __launch_bounds__(256, 1)
-fwd_kernel(const _Float16* __restrict__ q, const _Float16* __restrict__ k, const float* __restrict__ beta,
-           const _Float16* __restrict__ vp, float* __restrict__ out, const float* __restrict__ rscale,
-           const float* __restrict__ oscale, int64_t M, int64_t N, int64_t Npad, int64_t kps, float cs, int Din,
-           int Cout) {
-  constexpr int kStage = kStageKeys;
-  constexpr int DS = D / 32;     // K-steps of S^T
-  constexpr int CT = C / 16;     // 16-channel output tiles
-  constexpr int KP = D + 8;      // LDS row pitch of K, halves
-  constexpr int VP = 32 + 8;     // LDS row pitch of V^T, halves
+fwd_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const float* __restrict__ beta,
+           const _Float16* __restrict__ vp, const _Float16* __restrict__ vpl, float* __restrict__ out,
+           const float* __restrict__ rscale, const float* __restrict__ oscale, int64_t M, int64_t N, int64_t Npad,
+           int64_t kps, float cs, int Din, int Cout) {
+  constexpr bool SPLIT = kSplit<TIn>;
+  constexpr int NP = SPLIT ? 2 : 1;  // operand parts kept in LDS (hi, lo)
+  constexpr int DS = D / 32;         // K-steps of S^T
+  constexpr int CT = C / 16;         // 16-channel output tiles
+  constexpr int KP = D + 8;          // LDS row pitch of K, 16-bit elements
+  constexpr int VP = 32 + 8;         // LDS row pitch of V^T, halves
   constexpr int NSUB = kStage / 32;
   constexpr int kRowsPerBlock = kWaves * QT * 16;
-  __shared__ __attribute__((aligned(16))) _Float16 sK[2][kStage][KP];
-  __shared__ __attribute__((aligned(16))) _Float16 sV[2][NSUB][C][VP];
+  using Raw = typename std::conditional<std::is_same<TIn, __bf16>::value, __bf16, _Float16>::type;
+  using Raw8 = decltype(Op<TIn>{}.h);
+  __shared__ __attribute__((aligned(16))) Raw sK[NP][2][kStage][KP];
+  __shared__ __attribute__((aligned(16))) _Float16 sV[NP][2][NSUB][C][VP];
   __shared__ __attribute__((aligned(16))) float sB[2][kStage];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -49,12 +140,14 @@ fwd_kernel(const _Float16* __restrict__ q, const _Float16* __restrict__ k, const
   const int64_t row_base = (int64_t)blockIdx.x * kRowsPerBlock + wave * (QT * 16);
 
   // D is Din rounded up to a multiple of 32; the features Din <= d < D read as zero.
-  const _Float16* qb = q + bt * M * Din;
-  const _Float16* kb = k + bt * N * Din;
+  const TIn* qb = q + bt * M * Din;
+  const TIn* kb = k + bt * N * Din;
   const float* bb = beta + bt * Npad;
-  const _Float16* vb = vp + bt * Npad * C;
+  const _Float16* vb[NP];
+  vb[0] = vp + bt * Npad * C;
+  if constexpr (SPLIT) vb[NP - 1] = vpl + bt * Npad * C;
 
-  half8 qop[QT][DS];
+  Op<TIn> qop[QT][DS];
   float alpha[QT], mrow[QT];
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
@@ -64,13 +157,7 @@ fwd_kernel(const _Float16* __restrict__ q, const _Float16* __restrict__ k, const
 #pragma unroll
     for (int ds = 0; ds < DS; ++ds) {
       const int col = 32 * ds + 8 * g;
-      qop[qt][ds] = half8{};
-      if (col < Din) qop[qt][ds] = *reinterpret_cast<const half8*>(qb + i * Din + col);
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const float qv = (float)qop[qt][ds][s];
-        nrm = fmaf(qv, qv, nrm);
-      }
+      qop[qt][ds] = col < Din ? load_op<TIn, true>(qb + i * Din + col, nrm) : zero_op<TIn>();
     }
     nrm += __shfl_xor(nrm, 16);
     nrm += __shfl_xor(nrm, 32);
@@ -84,13 +171,13 @@ fwd_kernel(const _Float16* __restrict__ q, const _Float16* __restrict__ k, const
     for (int ct = 0; ct < CT; ++ct) O[qt][ct] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
   // Stage loads: global -> registers (issued before the current stage is computed) and
-  // registers -> LDS (after it), so global latency hides behind the matrix work.
-  constexpr int KCH = kStage * D / 8 / 256;       // 16-byte K chunks per thread
-  constexpr int kVChunks = NSUB * C * 4;          // 16-byte V chunks per stage
-  constexpr int VCH = (kVChunks + 255) / 256;     // ... per thread (the last round may be partial)
-  static_assert(KCH * 256 * 8 == kStage * D && kStage / 4 <= 256, "tile shapes");
-  static_assert(kVChunks % 256 == 0 || VCH == 1, "tile shapes");
-  half8 rk[KCH], rv[VCH];
+  // registers -> LDS (after it), so global latency hides behind the matrix work. Tables are
+  // cut into 8-element chunks dealt round-robin to the 256 threads.
+  constexpr int kKChunks = kStage * D / 8, KCH = (kKChunks + 255) / 256;
+  constexpr int kVChunks = NSUB * C * 4, VCH = (kVChunks + 255) / 256;
+  static_assert(kStage / 4 <= 256 && kStage % 32 == 0, "tile shapes");
+  Raw8 rk[NP][KCH];
+  half8 rv[NP][VCH];
   f32x4 rb = {};
   auto fetch = [&](int64_t st) {
     const int64_t jb = j0 + st * kStage;
@@ -99,65 +186,88 @@ fwd_kernel(const _Float16* __restrict__ q, const _Float16* __restrict__ k, const
       const int c = tid + 256 * r;
       const int row = c / (D / 8), col = (c % (D / 8)) * 8;
       const int64_t j = jb + row;
-      rk[r] = half8{};
-      if (j < j1 && col < Din) rk[r] = *reinterpret_cast<const half8*>(kb + j * Din + col);
+      float unused = 0.0f;
+      const Op<TIn> o = (c < kKChunks && j < j1 && col < Din) ? load_op<TIn, false>(kb + j * Din + col, unused)
+                                                              : zero_op<TIn>();
+      rk[0][r] = o.h;
+      if constexpr (SPLIT) rk[NP - 1][r] = o.l;
     }
 #pragma unroll
-    for (int r = 0; r < VCH; ++r) {
-      const int c = tid + 256 * r;
-      const int t = c / (C * 4), rem = c % (C * 4), ch = rem / 4, part = (rem % 4) * 8;
-      if (c < kVChunks) rv[r] = *reinterpret_cast<const half8*>(vb + ((jb / 32 + t) * C + ch) * 32 + part);
-    }
+    for (int p = 0; p < NP; ++p)
+#pragma unroll
+      for (int r = 0; r < VCH; ++r) {
+        const int c = tid + 256 * r;
+        const int t = c / (C * 4), rem = c % (C * 4), ch = rem / 4, part = (rem % 4) * 8;
+        if (c < kVChunks) rv[p][r] = *reinterpret_cast<const half8*>(vb[p] + ((jb / 32 + t) * C + ch) * 32 + part);
+      }
     if (tid < kStage / 4) rb = *reinterpret_cast<const f32x4*>(bb + jb + 4 * tid);
   };
   auto commit = [&](int buf) {
 #pragma unroll
-    for (int r = 0; r < KCH; ++r) {
-      const int c = tid + 256 * r;
-      *reinterpret_cast<half8*>(&sK[buf][c / (D / 8)][(c % (D / 8)) * 8]) = rk[r];
-    }
+    for (int p = 0; p < NP; ++p) {
 #pragma unroll
-    for (int r = 0; r < VCH; ++r) {
-      const int c = tid + 256 * r;
-      const int t = c / (C * 4), rem = c % (C * 4);
-      if (c < kVChunks) *reinterpret_cast<half8*>(&sV[buf][t][rem / 4][(rem % 4) * 8]) = rv[r];
+      for (int r = 0; r < KCH; ++r) {
+        const int c = tid + 256 * r;
+        if (c < kKChunks) *reinterpret_cast<Raw8*>(&sK[p][buf][c / (D / 8)][(c % (D / 8)) * 8]) = rk[p][r];
+      }
+#pragma unroll
+      for (int r = 0; r < VCH; ++r) {
+        const int c = tid + 256 * r;
+        const int t = c / (C * 4), rem = c % (C * 4);
+        if (c < kVChunks) *reinterpret_cast<half8*>(&sV[p][buf][t][rem / 4][(rem % 4) * 8]) = rv[p][r];
+      }
     }
     if (tid < kStage / 4) *reinterpret_cast<f32x4*>(&sB[buf][4 * tid]) = rb;
   };
 
   // S'^T of one 32-key subtile for every query tile: S[qt][half] holds keys 16*half + 4g + v.
   auto scores = [&](int buf, int sub, f32x4 (&S)[QT][2]) {
-    half8 kop[2][DS];
+    Op<TIn> kop[2][DS];
     f32x4 bc[2];
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll
-      for (int ds = 0; ds < DS; ++ds)
-        kop[hh][ds] = *reinterpret_cast<const half8*>(&sK[buf][sub * 32 + 16 * hh + l16][32 * ds + 8 * g]);
+      for (int ds = 0; ds < DS; ++ds) {
+        const int key = sub * 32 + 16 * hh + l16, col = 32 * ds + 8 * g;
+        kop[hh][ds].h = *reinterpret_cast<const Raw8*>(&sK[0][buf][key][col]);
+        if constexpr (SPLIT) kop[hh][ds].l = *reinterpret_cast<const half8*>(&sK[NP - 1][buf][key][col]);
+      }
       bc[hh] = *reinterpret_cast<const f32x4*>(&sB[buf][sub * 32 + 16 * hh + 4 * g]);
     }
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
-        S[qt][hh] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[hh][0], qop[qt][0], bc[hh], 0, 0, 0);
+        S[qt][hh] = s_mfma<TIn>(kop[hh][0], qop[qt][0], bc[hh]);
 #pragma unroll
-        for (int ds = 1; ds < DS; ++ds)
-          S[qt][hh] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[hh][ds], qop[qt][ds], S[qt][hh], 0, 0, 0);
+        for (int ds = 1; ds < DS; ++ds) S[qt][hh] = s_mfma<TIn>(kop[hh][ds], qop[qt][ds], S[qt][hh]);
       }
   };
-  // P = 2^(c S' + alpha) in fp16 and O^T += V^T P^T for one subtile.
+  // P = 2^(c S' + alpha) in fp16 (hi and lo parts when split) and O^T += V^T P^T.
   auto accumulate = [&](int buf, int sub, const f32x4 (&S)[QT][2]) {
-    half8 vop[CT];
+    half8 vop[NP][CT];
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct) vop[ct] = *reinterpret_cast<const half8*>(&sV[buf][sub][16 * ct + l16][8 * g]);
+    for (int p = 0; p < NP; ++p)
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+        vop[p][ct] = *reinterpret_cast<const half8*>(&sV[p][buf][sub][16 * ct + l16][8 * g]);
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
-      half8 pb;
+      half8 ph, pl;
 #pragma unroll
-      for (int s = 0; s < 8; ++s) pb[s] = (_Float16)exp2_hw(fmaf(S[qt][s >> 2][s & 3], cs, alpha[qt]));
+      for (int s = 0; s < 8; ++s) {
+        const float pv = exp2_hw(fmaf(S[qt][s >> 2][s & 3], cs, alpha[qt]));
+        ph[s] = (_Float16)pv;
+        if constexpr (SPLIT) pl[s] = (_Float16)(pv - (float)ph[s]);
+      }
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct) O[qt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop[ct], pb, O[qt][ct], 0, 0, 0);
+      for (int ct = 0; ct < CT; ++ct) {
+        O[qt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop[0][ct], ph, O[qt][ct], 0, 0, 0);
+        if constexpr (SPLIT) {
+          O[qt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop[NP - 1][ct], ph, O[qt][ct], 0, 0, 0);
+          O[qt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop[0][ct], pl, O[qt][ct], 0, 0, 0);
+        }
+      }
     }
   };
   // A row is settled once its shift m >= -kSlack: every later kernel value is then at most
@@ -236,12 +346,15 @@ fwd_kernel(const _Float16* __restrict__ q, const _Float16* __restrict__ k, const
 
 }  // namespace
 
-template <int Dp>
+template <typename TIn, int Dp>
 hipError_t fwd_launch(const FwdArgs& a) {
   const int Cp = padded_channels(a.C);
-#define KEOPS_FWD(Cv)                                                                              \
-  fwd_kernel<Dp, Cv, fwd_query_tiles(Dp, Cv)><<<a.grid, 256, 0, a.stream>>>(                      \
-      a.q, a.k, a.beta, a.vp, a.out, a.rscale, a.oscale, a.M, a.N, a.Npad, a.kps, a.cs, a.D, a.C)
+  constexpr int kStage = kSplit<TIn> ? 32 : kStageKeys;
+  const TIn* q = static_cast<const TIn*>(a.q);
+  const TIn* k = static_cast<const TIn*>(a.k);
+#define KEOPS_FWD(Cv)                                                                                       \
+  fwd_kernel<TIn, Dp, Cv, fwd_query_tiles(Dp, Cv, kSplit<TIn>), kStage><<<a.grid, 256, 0, a.stream>>>(       \
+      q, k, a.beta, a.vp, a.vpl, a.out, a.rscale, a.oscale, a.M, a.N, a.Npad, a.kps, a.cs, a.D, a.C)
   if (Cp == 16) KEOPS_FWD(16);
   else if (Cp == 32) KEOPS_FWD(32);
   else KEOPS_FWD(64);

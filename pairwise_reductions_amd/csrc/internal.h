@@ -63,13 +63,17 @@ hipError_t launch_scale_rows(const float* b, const float* scale, float* out, int
 hipError_t launch_pow(const float* in, float* out, int64_t n, float e, hipStream_t s);
 hipError_t launch_div_sqrt(const float* p, const float* d, float* out, int64_t n, hipStream_t s);
 
-// Matrix-core (fp16) batched Gauss sums. x, y: [B][M|N][D] fp16.
+// Matrix-core batched Gauss sums. x, y: [B][M|N][D] of `xy` type (fp16, bf16, or float32
+// split into fp16 hi + lo parts on the matrix cores).
+enum ElemType { kElemF16 = 0, kElemBF16 = 1, kElemF32 = 2 };
 bool highd_supported(int D, int C);
-// out[t][i][c] = rscale[t][i] * sum_j Phi_ij cscale[t][j] b[t][j][c]; b is fp16 or (b_f32)
-// fp32; rscale and cscale may be null. `general` (b_f32 or a cscale) selects the
-// weight-normalising column preparation, which needs a slightly larger workspace.
-size_t highd_workspace_bytes(int64_t B, int64_t M, int64_t N, int D, int C, bool general);
-hipError_t launch_gauss_sum_highd(const void* x, const void* y, const void* b, bool b_f32,
+// out[t][i][c] = rscale[t][i] * sum_j Phi_ij cscale[t][j] b[t][j][c]; b is of type bt;
+// rscale and cscale may be null. Anything but fp16 points with fp16 weights and no column
+// scale takes the weight-normalising column preparation (`general`), which needs a slightly
+// larger workspace.
+bool highd_general(ElemType xy, ElemType bt, bool col_scaled);
+size_t highd_workspace_bytes(int64_t B, int64_t M, int64_t N, int D, int C, ElemType xy, bool general);
+hipError_t launch_gauss_sum_highd(const void* x, const void* y, ElemType xy, const void* b, ElemType bt,
                                   const float* rscale, const float* cscale, float* out,
                                   void* workspace, int64_t B, int64_t M, int64_t N, int D, int C,
                                   float sigma, hipStream_t s);

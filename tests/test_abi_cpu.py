@@ -71,7 +71,8 @@ def test_workspace_bytes(lib):
     assert ws(0, 4, 16384, 16384, 48, 32, 0, F16) > 0     # D padded to 64 inside
     assert ws(0, 4, 16384, 16384, 40, 32, 0, F16) == 0    # D not a multiple of 16
     assert ws(0, 4, 16384, 16384, 144, 32, 0, F16) == 0   # D > 128
-    assert ws(0, 4, 16384, 16384, 32, 32, 0, 2) == 0
+    assert ws(0, 4, 16384, 16384, 32, 32, 0, 2) > 0       # bf16
+    assert ws(0, 4, 16384, 16384, 32, 32, 0, F32) >= 4 * 16384 * (4 + 2 * 32 * 2)   # hi + lo weight tables
 
 
 def _gs(lib, x=X, y=Y, b=B, out=OUT, Bt=1, M=100, N=100, D=3, C=1, sigma=0.1, dtype=F32, ws=WS, wsb=1 << 30):
@@ -85,7 +86,9 @@ def _gs(lib, x=X, y=Y, b=B, out=OUT, Bt=1, M=100, N=100, D=3, C=1, sigma=0.1, dt
     (dict(sigma=math.inf), INVALID),
     (dict(D=9), UNSUPPORTED), (dict(D=0), UNSUPPORTED), (dict(C=0), UNSUPPORTED), (dict(C=9), UNSUPPORTED),
     (dict(Bt=2), UNSUPPORTED), (dict(dtype=F16, D=3), UNSUPPORTED), (dict(dtype=7), INVALID),
-    (dict(dtype=2, D=32, C=32), UNSUPPORTED), (dict(dtype=F16, D=40, C=32), UNSUPPORTED),
+    (dict(dtype=2, D=40, C=32), UNSUPPORTED), (dict(dtype=F16, D=40, C=32), UNSUPPORTED),
+    (dict(dtype=F32, D=24, C=4), UNSUPPORTED), (dict(dtype=2, D=32, C=65), UNSUPPORTED),
+    (dict(dtype=F32, D=32, C=4, Bt=2, x=X + 4), INVALID),     # matrix-core path: 16-byte alignment
     (dict(dtype=F16, D=144, C=32), UNSUPPORTED),
     (dict(dtype=F16, D=32, C=65), UNSUPPORTED),
     (dict(dtype=F16, D=32, C=32, x=X + 8), INVALID),
@@ -206,6 +209,8 @@ def test_gauss_sum_backward_rejects(lib):
     assert call(gx=GX, gy=GX) == INVALID               # gradients overlap each other
     assert call(D=9) == UNSUPPORTED and call(Bt=2) == UNSUPPORTED
     assert call(dtype=F16, D=40, C=4) == UNSUPPORTED
+    assert call(dtype=2, D=32, C=4) == UNSUPPORTED                # bf16 backward is not built
+    assert call(dtype=F32, D=32, C=4) == UNSUPPORTED              # nor the float32 matrix-core one
     assert call(dtype=F16, D=32, C=4, gx=GX + 4) == INVALID   # fp16 path needs 16-byte aligned outputs
     assert call(sigma=-1.0) == INVALID
     assert call(gx=None, gy=None, gb=None, ws=None, wsb=0) == 0   # nothing requested

@@ -283,3 +283,81 @@ def test_argkmin_weighted_ties_and_large_weights():
     idx2 = pr.argkmin_weighted(_dev(x), _dev(y), _dev(w2), 5)
     want2, _ = oracle.argkmin_weighted(x, y, w2, 5, workers=8)
     assert np.array_equal(_host(idx2), want2)
+
+
+# ------------------------------------------------- bf16 and float32 inputs, matrix-core path
+TYPED_SHAPES = [
+    # (B, M, N, D, C, sigma)
+    (1, 1, 1, 32, 1, 1.0), (2, 300, 1000, 32, 32, 0.7), (1, 513, 2049, 64, 3, 1.0), (3, 129, 777, 128, 64, 1.5),
+    (2, 400, 1500, 16, 17, 1.0), (1, 1000, 4096, 96, 8, 1.2),
+]
+
+
+def _typed_inputs(seed, B, M, N, D, C, dtype, shift=0.0):
+    """Points ~ N(0, I/D) (+ shift) and weights ~ N(0, 1), rounded to `dtype`; returns the
+    device tensors and their exact float64 values for the oracle."""
+    import torch
+    g = torch.Generator().manual_seed(seed)
+    q = (torch.randn((B, M, D), generator=g, dtype=torch.float64) / D ** 0.5 + shift).to(dtype)
+    k = (torch.randn((B, N, D), generator=g, dtype=torch.float64) / D ** 0.5).to(dtype)
+    v = torch.randn((B, N, C), generator=g, dtype=torch.float64).to(dtype)
+    host = [t.to(torch.float64).numpy() for t in (q, k, v)]
+    return (q.cuda(), k.cuda(), v.cuda()), host
+
+
+@pytest.mark.parametrize("B,M,N,D,C,sigma", TYPED_SHAPES)
+def test_gauss_sum_bf16_shapes(B, M, N, D, C, sigma):
+    import torch
+    import pairwise_reductions_amd as pr
+    _announce("gauss_sum_bf16", B=B, M=M, N=N, D=D, C=C, sigma=sigma)
+    (q, k, v), (qh, kh, vh) = _typed_inputs(B * 31 + M + D, B, M, N, D, C, torch.bfloat16)
+    sig = float(np.float32(sigma))
+    got = _host(pr.gauss_sum(q, k, v, sig))
+    want, norm = oracle.gauss_sum_batched(qh, kh, vh, 1.0 / (sig * sig), workers=8)
+    assert_normalised(got, want, norm, TOL_F16, "bf16")
+
+
+@pytest.mark.parametrize("B,M,N,D,C,sigma", TYPED_SHAPES)
+def test_gauss_sum_f32_matrix_core_shapes(B, M, N, D, C, sigma):
+    """float32 inputs on the matrix cores (hi + lo fp16 parts, three products each) meet the
+    float32 tolerance."""
+    import torch
+    import pairwise_reductions_amd as pr
+    _announce("gauss_sum_f32_mfma", B=B, M=M, N=N, D=D, C=C, sigma=sigma)
+    (q, k, v), (qh, kh, vh) = _typed_inputs(B * 37 + M + D, B, M, N, D, C, torch.float32)
+    sig = float(np.float32(sigma))
+    got = _host(pr.gauss_sum(q, k, v, sig))
+    want, norm = oracle.gauss_sum_batched(qh, kh, vh, 1.0 / (sig * sig), workers=8)
+    assert_normalised(got, want, norm, TOL_F32, "f32 matrix-core")
+
+
+def test_gauss_sum_f32_bf16_far_rows_and_scaled():
+    """Rows far from every key (the running shift), and the scaled form, for both input types."""
+    import torch
+    import pairwise_reductions_amd as pr
+    _announce("typed_far_scaled")
+    for dtype, tol in ((torch.float32, TOL_F32), (torch.bfloat16, TOL_F16)):
+        (q, k, v), (qh, kh, vh) = _typed_inputs(61, 2, 500, 2000, 32, 4, dtype, shift=1.0)
+        got = _host(pr.gauss_sum(q, k, v, 1.0))
+        want, norm = oracle.gauss_sum_batched(qh, kh, vh, 1.0, workers=8)
+        assert_normalised(got, want, norm, tol, f"far {dtype}")
+        rng = np.random.default_rng(62)
+        r = rng.standard_normal((2, 500)).astype(np.float32)
+        c = rng.standard_normal((2, 2000)).astype(np.float32)
+        got = _host(pr.gauss_sum_scaled(q, k, v, 1.0, row_scale=_dev(r), col_scale=_dev(c)))
+        for t in range(2):
+            want, norm = oracle.gauss_sum_scaled(qh[t], kh[t], vh[t], 1.0, row_scale=r[t], col_scale=c[t], workers=8)
+            assert_normalised(got[t], want, norm, tol, f"scaled {dtype}")
+
+
+def test_diffusion_scaling_f32_matrix_core():
+    import torch
+    import pairwise_reductions_amd as pr
+    _announce("diffusion_f32_mfma")
+    (x, _, _), (xh, _, _) = _typed_inputs(63, 2, 1500, 1, 32, 1, torch.float32)
+    s, q, d = (_host(t) for t in pr.diffusion_scaling(x, 1.0, 0.5))
+    for t in range(2):
+        ws, wq, wd = oracle.diffusion_scaling(xh[t], 1.0, 0.5, workers=8)
+        for got, want, name in ((q[t], wq, "q"), (d[t], wd, "d"), (s[t], ws, "s")):
+            rel = np.max(np.abs(got - want) / np.abs(want))
+            assert rel <= 2e-4, f"diffusion f32 matrix-core {name}: {rel:.3e}"
