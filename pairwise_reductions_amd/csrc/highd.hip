@@ -255,7 +255,7 @@ struct GradLayout {
 GradLayout grad_layout(int64_t B, int64_t M, int64_t N, int D, int C, int num_cus) {
   GradLayout L;
   const int Dp = hd::padded_features(D), Ck = hd::padded_k_channels(C);
-  L.sp = plan_split(B, M, N, hd::kWaves * hd::grad_query_tiles(Dp) * 16, num_cus);
+  L.sp = plan_split(B, M, N, hd::kWaves * hd::grad_query_tiles(Dp, Ck) * 16, num_cus);
   Carve c;
   L.nmax = c.take((size_t)B * sizeof(float));
   L.beta = c.take((size_t)B * L.sp.Npad * sizeof(float));

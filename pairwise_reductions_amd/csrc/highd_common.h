@@ -27,10 +27,19 @@ constexpr float kLogFloor = -60.0f; // log2 of the smallest column weight kept a
 // pipe overlap within a wave. Wider tiles take fewer to stay within 256 VGPRs.
 // Float32 inputs (split into fp16 hi + lo parts) hold twice the operands, so they take fewer.
 constexpr int fwd_query_tiles(int D, int C, bool split) {
-  return split ? (D <= 64 ? 4 : 2) : ((D == 32 && C <= 32) ? 8 : (D <= 64 ? 4 : 2));
+  return split ? ((D <= 64 && C <= 32) || D == 32 ? 4 : (D > 64 && C == 64 ? 1 : 2))
+               : ((D == 32 && C <= 32) ? 8 : (D <= 64 ? 4 : 2));
+}
+// Where scoring every query tile of a subtile before using them needs more than 256 VGPRs
+// (one wave per SIMD), the forward kernel scores and uses one tile at a time instead, which
+// keeps two waves per SIMD; elsewhere the tile-batched order runs faster (more independent
+// products in flight). Measured on the register counts of the compiled kernels.
+constexpr bool fwd_fused(int D, int C, bool split) {
+  return split ? (C == 64 && D >= 64) : ((D == 32 && C == 32) || (D == 64 && C == 64));
 }
 // The gradient kernel holds three products per subtile, so it takes fewer.
-constexpr int grad_query_tiles(int D) { return D <= 32 ? 4 : (D <= 64 ? 2 : 1); }
+// (Sizes chosen so every instantiation fits 256 VGPRs, i.e. two waves per SIMD.)
+constexpr int grad_query_tiles(int D, int CK) { return D <= 32 ? (CK <= 32 ? 4 : 2) : 1; }
 // Features run in steps of 32 (the K of one MFMA) and are read as zero past D; output and
 // weight channels run in tiles of 16.
 constexpr int padded_features(int D) { return (D + 31) / 32 * 32; }

@@ -111,7 +111,7 @@ __device__ __forceinline__ f32x4 s_mfma(const Op<TIn>& k, const Op<TIn>& q, f32x
   }
 }
 
-template <typename TIn, int D, int C, int QT, int kStage>
+template <typename TIn, int D, int C, int QT, int kStage, bool kFused>
 __global__ void __launch_bounds__(256, 1)
 fwd_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const float* __restrict__ beta,
            const _Float16* __restrict__ vp, const _Float16* __restrict__ vpl, float* __restrict__ out,
@@ -295,8 +295,9 @@ fwd_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const float* __
     settled = __all(all_settled);
     first = false;
   };
-  // One stage; both phases execute one barrier per stage, so the workgroup stays in step.
-  auto stage = [&](int64_t st, auto track) {
+  // One stage, scores of every query tile first; both phases execute one barrier per stage,
+  // so the workgroup stays in step.
+  auto stage_batched = [&](int64_t st, auto track) {
     constexpr bool kTrack = decltype(track)::value;
     const int buf = (int)(st & 1);
     if (st + 1 < nstages) fetch(st + 1);
@@ -311,12 +312,95 @@ fwd_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const float* __
     __syncthreads();
   };
 
+  // One stage. Per 32-key subtile the key and weight operands are read from LDS once, then
+  // each query tile runs S'^T (two MFMAs per 32 features), the row-shift update while
+  // tracking, P = 2^(cs S' + alpha) in fp16 and O^T += V^T P^T. Taking the tiles one at a
+  // time keeps a single tile's scores live, which leaves room for two waves per SIMD at eight
+  // tiles; both phases execute one barrier per stage, so the workgroup stays in step.
+  auto stage_fused = [&](int64_t st, auto track) {
+    constexpr bool kTrack = decltype(track)::value;
+    const int buf = (int)(st & 1);
+    if (st + 1 < nstages) fetch(st + 1);
+#pragma unroll
+    for (int sub = 0; sub < NSUB; ++sub) {
+      Op<TIn> kop[2][DS];
+      f32x4 bc[2];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+        for (int ds = 0; ds < DS; ++ds) {
+          const int key = sub * 32 + 16 * hh + l16, col = 32 * ds + 8 * g;
+          kop[hh][ds].h = *reinterpret_cast<const Raw8*>(&sK[0][buf][key][col]);
+          if constexpr (SPLIT) kop[hh][ds].l = *reinterpret_cast<const half8*>(&sK[NP - 1][buf][key][col]);
+        }
+        bc[hh] = *reinterpret_cast<const f32x4*>(&sB[buf][sub * 32 + 16 * hh + 4 * g]);
+      }
+      half8 vop[NP][CT];
+#pragma unroll
+      for (int p = 0; p < NP; ++p)
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+          vop[p][ct] = *reinterpret_cast<const half8*>(&sV[p][buf][sub][16 * ct + l16][8 * g]);
+      bool all_settled = true;
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        f32x4 S[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          S[hh] = s_mfma<TIn>(kop[hh][0], qop[qt][0], bc[hh]);
+#pragma unroll
+          for (int ds = 1; ds < DS; ++ds) S[hh] = s_mfma<TIn>(kop[hh][ds], qop[qt][ds], S[hh]);
+        }
+        if constexpr (kTrack) {
+          float mx = fmaxf(fmaxf(fmaxf(S[0][0], S[0][1]), fmaxf(S[0][2], S[0][3])),
+                           fmaxf(fmaxf(S[1][0], S[1][1]), fmaxf(S[1][2], S[1][3])));
+          mx = fmaxf(mx, __shfl_xor(mx, 16));
+          mx = fmaxf(mx, __shfl_xor(mx, 32));
+          const float amax = fmaf(mx, cs, alpha[qt]);
+          const float delta = (first || amax > kSlack) ? amax : 0.0f;
+          alpha[qt] -= delta;
+          mrow[qt] += delta;
+          const float sc = (first || delta == 0.0f) ? 1.0f : exp2_hw(-delta);
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) O[qt][ct] *= sc;
+          all_settled = all_settled && (mrow[qt] >= -kSlack);
+        }
+        half8 ph, pl;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          const float pv = exp2_hw(fmaf(S[s >> 2][s & 3], cs, alpha[qt]));
+          ph[s] = (_Float16)pv;
+          if constexpr (SPLIT) pl[s] = (_Float16)(pv - (float)ph[s]);
+        }
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          O[qt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop[0][ct], ph, O[qt][ct], 0, 0, 0);
+          if constexpr (SPLIT) {
+            O[qt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop[NP - 1][ct], ph, O[qt][ct], 0, 0, 0);
+            O[qt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop[0][ct], pl, O[qt][ct], 0, 0, 0);
+          }
+        }
+      }
+      if constexpr (kTrack) {
+        settled = __all(all_settled);
+        first = false;
+      }
+    }
+    if (st + 1 < nstages) commit(buf ^ 1);
+    __syncthreads();
+  };
+
   fetch(0);
   commit(0);
   __syncthreads();
   int64_t st = 0;
-  for (; st < nstages && !settled; ++st) stage(st, std::true_type{});
-  for (; st < nstages; ++st) stage(st, std::false_type{});
+  if constexpr (kFused) {
+    for (; st < nstages && !settled; ++st) stage_fused(st, std::true_type{});
+    for (; st < nstages; ++st) stage_fused(st, std::false_type{});
+  } else {
+    for (; st < nstages && !settled; ++st) stage_batched(st, std::true_type{});
+    for (; st < nstages; ++st) stage_batched(st, std::false_type{});
+  }
 
   // Store the first Cout channels (C here is Cout rounded up to a multiple of 16).
   const int64_t BMC = (int64_t)gridDim.z * M * Cout;
@@ -353,7 +437,8 @@ hipError_t fwd_launch(const FwdArgs& a) {
   const TIn* q = static_cast<const TIn*>(a.q);
   const TIn* k = static_cast<const TIn*>(a.k);
 #define KEOPS_FWD(Cv)                                                                                       \
-  fwd_kernel<TIn, Dp, Cv, fwd_query_tiles(Dp, Cv, kSplit<TIn>), kStage><<<a.grid, 256, 0, a.stream>>>(       \
+  fwd_kernel<TIn, Dp, Cv, fwd_query_tiles(Dp, Cv, kSplit<TIn>), kStage, fwd_fused(Dp, Cv, kSplit<TIn>)>          \
+      <<<a.grid, 256, 0, a.stream>>>(                                                                              \
       q, k, a.beta, a.vp, a.vpl, a.out, a.rscale, a.oscale, a.M, a.N, a.Npad, a.kps, a.cs, a.D, a.C)
   if (Cp == 16) KEOPS_FWD(16);
   else if (Cp == 32) KEOPS_FWD(32);

@@ -148,82 +148,75 @@ grad_kernel(const _Float16* __restrict__ x, const _Float16* __restrict__ y, cons
     if (tid < kStage / 4) *reinterpret_cast<f32x4*>(&sB[buf][4 * tid]) = rb;
   };
 
-  // S'^T and dP^T of one 32-key subtile for every row tile (keys 16*half + 4g + v).
-  auto scores = [&](int buf, int sub, f32x4 (&S)[QT][2], f32x4 (&P)[QT][2]) {
-    half8 kop[2][DS], bop[2][KS];
-    f32x4 bc[2];
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const int key = sub * 32 + 16 * hh + l16;
-#pragma unroll
-      for (int ds = 0; ds < DS; ++ds) kop[hh][ds] = *reinterpret_cast<const half8*>(&sK[buf][key][32 * ds + 8 * g]);
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) bop[hh][ks] = *reinterpret_cast<const half8*>(&sA[buf][key][32 * ks + 8 * g]);
-      bc[hh] = *reinterpret_cast<const f32x4*>(&sB[buf][sub * 32 + 16 * hh + 4 * g]);
-    }
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        S[qt][hh] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[hh][0], qop[qt][0], bc[hh], 0, 0, 0);
-#pragma unroll
-        for (int ds = 1; ds < DS; ++ds)
-          S[qt][hh] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[hh][ds], qop[qt][ds], S[qt][hh], 0, 0, 0);
-        P[qt][hh] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bop[hh][0], aop[qt][0], f32x4{0.0f, 0.0f, 0.0f, 0.0f},
-                                                           0, 0, 0);
-#pragma unroll
-        for (int ks = 1; ks < KS; ++ks)
-          P[qt][hh] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bop[hh][ks], aop[qt][ks], P[qt][hh], 0, 0, 0);
-      }
-  };
-  // W = 2^(cs S' + alpha) dP in fp16 and O^T += Y'^T W^T for one subtile.
-  auto accumulate = [&](int buf, int sub, const f32x4 (&S)[QT][2], const f32x4 (&P)[QT][2]) {
-    half8 yop[OT];
-#pragma unroll
-    for (int ot = 0; ot < OT; ++ot) yop[ot] = *reinterpret_cast<const half8*>(&sY[buf][sub][16 * ot + l16][8 * g]);
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
-      half8 wb;
-#pragma unroll
-      for (int s = 0; s < 8; ++s)
-        wb[s] = (_Float16)(exp2_hw(fmaf(S[qt][s >> 2][s & 3], cs, alpha[qt])) * P[qt][s >> 2][s & 3]);
-#pragma unroll
-      for (int ot = 0; ot < OT; ++ot) O[qt][ot] = __builtin_amdgcn_mfma_f32_16x16x32_f16(yop[ot], wb, O[qt][ot], 0, 0, 0);
-    }
-  };
   // Row shifts, as in the forward kernel: once m_i >= -kSlack every later scaled kernel value
   // is at most 2^kSlack, so the tracking stops for the whole wave.
   bool first = true, settled = false;
-  auto track_rows = [&](const f32x4 (&S)[QT][2]) {
-    bool all_settled = true;
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
-      float mx = fmaxf(fmaxf(fmaxf(S[qt][0][0], S[qt][0][1]), fmaxf(S[qt][0][2], S[qt][0][3])),
-                       fmaxf(fmaxf(S[qt][1][0], S[qt][1][1]), fmaxf(S[qt][1][2], S[qt][1][3])));
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float amax = fmaf(mx, cs, alpha[qt]);
-      const float delta = (first || amax > kSlack) ? amax : 0.0f;
-      alpha[qt] -= delta;
-      mrow[qt] += delta;
-      const float sc = (first || delta == 0.0f) ? 1.0f : exp2_hw(-delta);
-#pragma unroll
-      for (int ot = 0; ot < OT; ++ot) O[qt][ot] *= sc;
-      all_settled = all_settled && (mrow[qt] >= -kSlack);
-    }
-    settled = __all(all_settled);
-    first = false;
-  };
+  // One stage. Per 32-key subtile the key, weight and column operands are read from LDS once;
+  // then each row tile runs S'^T and dP^T, the row-shift update while tracking,
+  // W = 2^(cs S' + alpha) dP in fp16 and O^T += Y'^T W^T, one tile at a time so that only one
+  // tile's products are live.
   auto stage = [&](int64_t st, auto track) {
     constexpr bool kTrack = decltype(track)::value;
     const int buf = (int)(st & 1);
     if (st + 1 < nstages) fetch(st + 1);
 #pragma unroll
     for (int sub = 0; sub < NSUB; ++sub) {
-      f32x4 S[QT][2], P[QT][2];
-      scores(buf, sub, S, P);
-      if constexpr (kTrack) track_rows(S);
-      accumulate(buf, sub, S, P);
+      half8 kop[2][DS], bop[2][KS];
+      f32x4 bc[2];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int key = sub * 32 + 16 * hh + l16;
+#pragma unroll
+        for (int ds = 0; ds < DS; ++ds) kop[hh][ds] = *reinterpret_cast<const half8*>(&sK[buf][key][32 * ds + 8 * g]);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) bop[hh][ks] = *reinterpret_cast<const half8*>(&sA[buf][key][32 * ks + 8 * g]);
+        bc[hh] = *reinterpret_cast<const f32x4*>(&sB[buf][sub * 32 + 16 * hh + 4 * g]);
+      }
+      half8 yop[OT];
+#pragma unroll
+      for (int ot = 0; ot < OT; ++ot) yop[ot] = *reinterpret_cast<const half8*>(&sY[buf][sub][16 * ot + l16][8 * g]);
+      bool all_settled = true;
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        f32x4 S[2], P[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          S[hh] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[hh][0], qop[qt][0], bc[hh], 0, 0, 0);
+#pragma unroll
+          for (int ds = 1; ds < DS; ++ds)
+            S[hh] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[hh][ds], qop[qt][ds], S[hh], 0, 0, 0);
+          P[hh] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bop[hh][0], aop[qt][0], f32x4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0,
+                                                         0);
+#pragma unroll
+          for (int ks = 1; ks < KS; ++ks)
+            P[hh] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bop[hh][ks], aop[qt][ks], P[hh], 0, 0, 0);
+        }
+        if constexpr (kTrack) {
+          float mx = fmaxf(fmaxf(fmaxf(S[0][0], S[0][1]), fmaxf(S[0][2], S[0][3])),
+                           fmaxf(fmaxf(S[1][0], S[1][1]), fmaxf(S[1][2], S[1][3])));
+          mx = fmaxf(mx, __shfl_xor(mx, 16));
+          mx = fmaxf(mx, __shfl_xor(mx, 32));
+          const float amax = fmaf(mx, cs, alpha[qt]);
+          const float delta = (first || amax > kSlack) ? amax : 0.0f;
+          alpha[qt] -= delta;
+          mrow[qt] += delta;
+          const float sc = (first || delta == 0.0f) ? 1.0f : exp2_hw(-delta);
+#pragma unroll
+          for (int ot = 0; ot < OT; ++ot) O[qt][ot] *= sc;
+          all_settled = all_settled && (mrow[qt] >= -kSlack);
+        }
+        half8 wb;
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+          wb[s] = (_Float16)(exp2_hw(fmaf(S[s >> 2][s & 3], cs, alpha[qt])) * P[s >> 2][s & 3]);
+#pragma unroll
+        for (int ot = 0; ot < OT; ++ot)
+          O[qt][ot] = __builtin_amdgcn_mfma_f32_16x16x32_f16(yop[ot], wb, O[qt][ot], 0, 0, 0);
+      }
+      if constexpr (kTrack) {
+        settled = __all(all_settled);
+        first = false;
+      }
     }
     if (st + 1 < nstages) commit(buf ^ 1);
     __syncthreads();
@@ -266,10 +259,9 @@ grad_kernel(const _Float16* __restrict__ x, const _Float16* __restrict__ y, cons
 
 template <int Dp>
 hipError_t grad_launch(const GradArgs& a) {
-  constexpr int QT = grad_query_tiles(Dp);
   constexpr int kStage = Dp <= 64 ? kStageKeys : 32;
 #define KEOPS_GRAD(CKv)                                                                               \
-  grad_kernel<Dp, CKv, QT, kStage><<<a.grid, 256, 0, a.stream>>>(a.x, a.y, a.ap, a.rho, a.beta, a.bvp, a.yp, \
+  grad_kernel<Dp, CKv, grad_query_tiles(Dp, CKv), kStage><<<a.grid, 256, 0, a.stream>>>(a.x, a.y, a.ap, a.rho, a.beta, a.bvp, a.yp, \
                                                                  a.oscale, a.out, a.M, a.N, a.Npad, a.kps,   \
                                                                  a.cs, a.tau, a.D)
   if (a.Ck == 32) KEOPS_GRAD(32);
