@@ -40,10 +40,10 @@ def grad_flops_per_pair(D, C):
 # FETCH_SIZE and WRITE_SIZE (each scaled by what it reads for a 256 MiB copy: x2.0 and x1.0).
 # Reported only while the sources the kernel is compiled from are byte-identical to the ones
 # that were measured (sha256 over the listed files, concatenated in order).
-MEASURED_TRAFFIC = {"bytes": 851506173,
+MEASURED_TRAFFIC = {"bytes": 851385782,
                     "sources": ["pairwise_reductions_amd/csrc/lowd_sum.hip",
                                 "pairwise_reductions_amd/csrc/lowd_common.h"],
-                    "sha256_prefix": "9ef51312caff0233"}
+                    "sha256_prefix": "ed0a377aad6cdb7b"}
 
 
 def kernel_source_digest(paths):

@@ -121,6 +121,12 @@ Plan plan_lowd(int op, int64_t M, int64_t N, int D, int C, int K, int num_cus) {
     case 6: p.R = lowd::argk_rows(lowd::argk_bucket(K)); break;
     default: p.R = lowd::kRowsGrad; break;
   }
+  if (op == 0) {
+    // Few rows: four rows per lane would leave most CUs idle even with every column split,
+    // so take one row per lane.
+    const int64_t max_cols_splits = N / 256 > 1 ? N / 256 : 1;
+    if (ceil_div(M, (int64_t)kBlock * p.R) * max_cols_splits < (int64_t)num_cus * 4) p.R = lowd::kRowsSumSmall;
+  }
   p.rows_per_block = kBlock * p.R;
   p.row_blocks = M > 0 ? ceil_div(M, p.rows_per_block) : 0;
   // Split the columns so that (a) there are at least eight workgroups (32 wave64s) per compute

@@ -20,6 +20,7 @@ constexpr float kLseSlack = 16.0f;     // lazy rescale: terms may grow to 2^16 b
 
 // Rows per lane of each family (register budgets measured on gfx950).
 constexpr int kRowsSum = 4;
+constexpr int kRowsSumSmall = 1;       // small M: more, smaller row blocks to fill the chip
 constexpr int kRowsLse = 4;
 constexpr int kRowsGrad = 2;
 constexpr int kLseTile = 8;            // columns per log-sum-exp tile

@@ -96,7 +96,11 @@ template <int D, int C>
 hipError_t gauss_sum_dc(const float* x, const float* y, const double* cols, const float* b, float* dst,
                         const float* rscale, int64_t M, int64_t N, double c2, const Plan& p, hipStream_t s) {
   dim3 grid((unsigned)p.row_blocks, (unsigned)p.splits);
-  gauss_sum_kernel<D, C, kRowsSum><<<grid, kBlock, 0, s>>>(x, y, cols, b, dst, rscale, M, N, p.cols_per_split, c2);
+  if (p.R == kRowsSumSmall)
+    gauss_sum_kernel<D, C, kRowsSumSmall><<<grid, kBlock, 0, s>>>(x, y, cols, b, dst, rscale, M, N, p.cols_per_split,
+                                                                   c2);
+  else
+    gauss_sum_kernel<D, C, kRowsSum><<<grid, kBlock, 0, s>>>(x, y, cols, b, dst, rscale, M, N, p.cols_per_split, c2);
   return hipGetLastError();
 }
 
