@@ -361,3 +361,69 @@ def test_diffusion_scaling_f32_matrix_core():
         for got, want, name in ((q[t], wq, "q"), (d[t], wd, "d"), (s[t], ws, "s")):
             rel = np.max(np.abs(got - want) / np.abs(want))
             assert rel <= 2e-4, f"diffusion f32 matrix-core {name}: {rel:.3e}"
+
+
+# ------------------------------------------------------------------ edge cases of the extensions
+def test_extension_edge_cases():
+    """Empty sides, all-zero weights and scales, and sigma -> infinity for the backward, the
+    scaled sum, the diffusion passes and the weighted argKmin."""
+    import torch
+    import pairwise_reductions_amd as pr
+    _announce("extension_edges")
+    # fp16 backward: N = 0 gives zero x-gradients; M = 0 gives zero y- and b-gradients
+    q, k, v = _highd_inputs(71, 2, 100, 300, 32, 3)
+    g = workloads.upstream_gradient(100, 3, seed=72, B=2)
+    got = pr.gauss_sum_backward(_dev(q), _dev(k[:, :0].copy()), _dev(v[:, :0].copy()), _dev(g), 1.0, need=("x",))
+    assert np.all(_host(got["x"]) == 0.0)
+    got = pr.gauss_sum_backward(_dev(q[:, :0].copy()), _dev(k), _dev(v), _dev(g[:, :0].copy()), 1.0, need=("y", "b"))
+    assert np.all(_host(got["y"]) == 0.0) and np.all(_host(got["b"]) == 0.0)
+    # all-zero upstream gradient and all-zero weights: every gradient is exactly zero
+    zg = np.zeros_like(g)
+    got = pr.gauss_sum_backward(_dev(q), _dev(k), _dev(v), _dev(zg), 1.0)
+    for key in ("x", "y", "b"):
+        assert np.all(_host(got[key]) == 0.0), key
+    got = pr.gauss_sum_backward(_dev(q), _dev(k), _dev(np.zeros_like(v)), _dev(g), 1.0, need=("x", "y"))
+    assert np.all(_host(got["x"]) == 0.0) and np.all(_host(got["y"]) == 0.0)
+    # float32 backward with M = 1 = N and x = y: the x-gradient is exactly zero
+    x1 = np.array([[0.25, 0.5, 0.75]], np.float32)
+    got = pr.gauss_sum_backward(_dev(x1), _dev(x1), _dev(np.ones((1, 1), np.float32)), _dev(np.ones((1, 1), np.float32)),
+                                0.1, need=("x",))
+    assert np.all(_host(got["x"]) == 0.0)
+    # scaled sum: a zero column scale zeroes the output, a zero row scale too, on both paths
+    x, y, b = _rand(73, 300, 900, 3, 2)
+    out = _host(pr.gauss_sum_scaled(_dev(x), _dev(y), _dev(b), 0.1, col_scale=_dev(np.zeros(900, np.float32))))
+    assert np.all(out == 0.0)
+    out = _host(pr.gauss_sum_scaled(_dev(q), _dev(k), _dev(v), 1.0, row_scale=_dev(np.zeros((2, 100), np.float32))))
+    assert np.all(out == 0.0)
+    out = _host(pr.gauss_sum_scaled(_dev(q), _dev(k), _dev(v), 1.0, col_scale=_dev(np.zeros((2, 300), np.float32))))
+    assert np.all(out == 0.0)
+    # diffusion: sigma -> infinity gives s = 1/sqrt(N) for any alpha; one point gives s = 1
+    xs, _, _ = _rand(74, 1000, 1, 3, 1)
+    s, qd, dd = (_host(t) for t in pr.diffusion_scaling(_dev(xs), 1e30, 0.5))
+    assert np.allclose(qd, 1000.0, rtol=1e-5) and np.allclose(s, 1.0 / np.sqrt(1000.0), rtol=1e-5)
+    s1, _, _ = (_host(t) for t in pr.diffusion_scaling(_dev(xs[:1]), 0.1, 1.0))
+    assert np.allclose(s1, 1.0, rtol=1e-6)
+    # weighted argKmin with K = N returns a full ordering; M = 0 is a no-op
+    xw, yw, _ = _rand(75, 50, 20, 2, 1)
+    w = np.random.default_rng(76).standard_normal(20).astype(np.float32)
+    idx = _host(pr.argkmin_weighted(_dev(xw), _dev(yw), _dev(w), 20))
+    want, _ = oracle.argkmin_weighted(xw, yw, w, 20)
+    assert np.array_equal(idx, want)
+    pr.argkmin_weighted(_dev(xw[:0]), _dev(yw), _dev(w), 3)
+    torch.cuda.synchronize()
+
+
+def test_extension_determinism():
+    """Two runs of each extension give bit-identical outputs."""
+    import pairwise_reductions_amd as pr
+    _announce("extension_determinism")
+    q, k, v = _highd_inputs(81, 2, 700, 3000, 32, 2)
+    g = workloads.upstream_gradient(700, 2, seed=82, B=2)
+    a = pr.gauss_sum_backward(_dev(q), _dev(k), _dev(v), _dev(g), 1.0)
+    b = pr.gauss_sum_backward(_dev(q), _dev(k), _dev(v), _dev(g), 1.0)
+    for key in a:
+        assert np.array_equal(_host(a[key]), _host(b[key])), key
+    x, _, _ = _rand(83, 5000, 1, 3, 1)
+    s1 = _host(pr.diffusion_scaling(_dev(x), 0.05, 0.5)[0])
+    s2 = _host(pr.diffusion_scaling(_dev(x), 0.05, 0.5)[0])
+    assert np.array_equal(s1, s2)
