@@ -76,11 +76,18 @@ constexpr double kScreenMargin = 1.4210854715202004e-14;  // 2^-46
 
 // argKmin of d^2_ij - w_j (w_j = 0 when w is null; with LSE, also the log-sum-exp of -c2 d^2 in
 // base 2, never combined with weights) over the columns of one split.
-// Each pair first gets the cheap expansion a_ij; only when a_ij is below the row's K-th key
-// plus the margin is the exact key computed and the sorted list updated, which after the
-// first columns is rare. For the log-sum-exp the row's running shift is -c2 times its
-// smallest key so far, raised lazily (only when it grows by more than kLseSlack), so every
-// term 2^(-c2 a_ij - m) stays below 2^kLseSlack; it is updated before a tile's terms are added.
+// Each pair first gets the cheap expansion a_ij. A column whose a_ij is below the row's K-th
+// key plus the margin is only queued (its index goes into the lane's queue in LDS); when some
+// lane's queue could overflow on the next tile, every lane of the wave computes the exact keys
+// of its queued columns, in column order, and updates its sorted list and threshold. The
+// wave thus runs the list updates once per kQueue candidates of its busiest lane instead of
+// once per tile in which any of its 64 lanes has a candidate. The threshold a column is
+// screened against may lag behind the list (it is refreshed at each flush), which only
+// queues extra columns. For the log-sum-exp the row's running shift m (log2 units) is raised
+// lazily, whenever a tile holds a term above 2^kLseSlack, so every term 2^(-c2 a_ij - m) stays
+// below 2^kLseSlack.
+constexpr int kQueue = 16;  // queued candidate columns per lane and row
+
 template <int D, int K, int R, bool LSE>
 __global__ void __launch_bounds__(kBlock)
 knn_kernel(const float* __restrict__ x, const double* __restrict__ cols, const float* __restrict__ w,
@@ -89,6 +96,8 @@ knn_kernel(const float* __restrict__ x, const double* __restrict__ cols, const f
            int64_t cps, int Kout, double c2) {
   constexpr int P = (D + 2) & ~1;
   constexpr int U = D <= 4 ? 4 : 2;  // columns per screened tile
+  static_assert(kQueue >= 2 * U, "queue holds at least two tiles");
+  __shared__ int32_t queue[R][kQueue][kBlock];
   const int64_t split = blockIdx.y;
   const int64_t j0 = split * cps;
   const int64_t j1 = (j0 + cps < N) ? j0 + cps : N;
@@ -98,6 +107,7 @@ knn_kernel(const float* __restrict__ x, const double* __restrict__ cols, const f
   double xd[R][D], xp[R][D], A[R], marg[R], thr[R];
   double keys[R][K];
   int32_t ids[R][K];
+  int cnt[R];
   double mref[R];
   float l[R];
 #pragma unroll
@@ -119,12 +129,26 @@ knn_kernel(const float* __restrict__ x, const double* __restrict__ cols, const f
       keys[r][k] = INFINITY;
       ids[r][k] = -1;
     }
+    cnt[r] = 0;
     mref[r] = -INFINITY;
     l[r] = 0.0f;
   }
 
-  // Columns [j, j + n) of a tile, n <= U, for row r: screen, update the list, add LSE terms.
+  // Exact keys of this lane's queued columns for row r, in queue (= column) order.
+  auto flush = [&](int r) {
+    for (int e = 0; e < cnt[r]; ++e) {
+      const int32_t jj = queue[r][e][threadIdx.x];
+      double key = sq_dist_key<D>(xd[r], cols + (int64_t)jj * P);
+      if (w) key -= (double)w[jj];
+      if (key < keys[r][K - 1]) topk_insert<K>(keys[r], ids[r], key, jj);
+    }
+    thr[r] = keys[r][K - 1] + marg[r];
+    cnt[r] = 0;
+  };
+
+  // Columns [j, j + n) of a tile, n <= U, for row r: screen, queue, add LSE terms.
   auto tile = [&](int r, int64_t j, int n, const double (&yv)[U][D], const double (&bv)[U]) {
+    if (__any(cnt[r] > kQueue - U)) flush(r);
     double a[U];
     double mn = INFINITY;
 #pragma unroll
@@ -135,29 +159,17 @@ knn_kernel(const float* __restrict__ x, const double* __restrict__ cols, const f
         for (int d = 0; d < D; ++d) t = fma(xp[r][d], yv[u][d], t);
         a[u] = t;
         mn = fmin(mn, t);
-      }
-    }
-    if (mn < thr[r]) {
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if (u < n && a[u] < thr[r]) {
-          double key = sq_dist_key<D>(xd[r], yv[u]);
-          if (w) key -= (double)w[j + u];
-          if (key < keys[r][K - 1]) {
-            topk_insert<K>(keys[r], ids[r], key, (int32_t)(j + u));
-            thr[r] = keys[r][K - 1] + marg[r];
-            if constexpr (LSE) {
-              const double nm = -c2 * keys[r][0];
-              if (nm > mref[r] + (double)kLseSlack) {
-                l[r] *= exp2_hw((float)(mref[r] - nm));
-                mref[r] = nm;
-              }
-            }
-          }
-        }
+        // written every time, kept only when the count advances
+        queue[r][cnt[r]][threadIdx.x] = (int32_t)(j + u);
+        cnt[r] += (t < thr[r]) ? 1 : 0;
       }
     }
     if constexpr (LSE) {
+      const double nm = -c2 * mn;
+      if (nm > mref[r] + (double)kLseSlack) {
+        l[r] *= exp2_hw((float)(mref[r] - nm));
+        mref[r] = nm;
+      }
       float t = 0.0f;
 #pragma unroll
       for (int u = 0; u < U; ++u)
@@ -191,6 +203,8 @@ knn_kernel(const float* __restrict__ x, const double* __restrict__ cols, const f
 #pragma unroll
     for (int r = 0; r < R; ++r) tile(r, j, n, yv, bv);
   }
+#pragma unroll
+  for (int r = 0; r < R; ++r) flush(r);
 
 #pragma unroll
   for (int r = 0; r < R; ++r) {
