@@ -88,10 +88,15 @@ col_prep_kernel(const TK* __restrict__ k, const T* __restrict__ w, const float* 
   const int64_t j0 = (int64_t)blockIdx.x * 32;
   const int live = N - j0 >= 32 ? 32 : (N > j0 ? (int)(N - j0) : 0);
 
-  // keys, contiguous in global memory: thread e takes element e of the block's rows
-  for (int e = tid; e < 32 * D; e += 256) {
-    const int key = e / D, d = e % D;
-    sk[key][d] = key < live ? to_f32(k[(t * N + j0) * D + e]) : 0.0f;
+  // keys, contiguous in global memory, in 16-byte vectors (D is a multiple of 16)
+  constexpr int EV = 16 / (int)sizeof(TK);
+  typedef TK vec_t __attribute__((ext_vector_type(EV)));
+  for (int c = tid; c < 32 * D / EV; c += 256) {
+    const int key = (c * EV) / D, d = (c * EV) % D;
+    vec_t v = vec_t{};
+    if (key < live) v = *reinterpret_cast<const vec_t*>(k + (t * N + j0) * D + c * EV);
+#pragma unroll
+    for (int u = 0; u < EV; ++u) sk[key][d + u] = to_f32(v[u]);
   }
   // weights, times the column scale
   for (int e = tid; e < 32 * C; e += 256) {

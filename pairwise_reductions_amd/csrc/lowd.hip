@@ -141,9 +141,41 @@ Plan plan_lowd(int op, int64_t M, int64_t N, int D, int C, int K, int num_cus) {
   if ((op == 2 || op == 6) && max_split > 16) max_split = 16;  // argKmin partial lists are K entries per row
   if (S > max_split) S = max_split;
   if (S < 1) S = 1;
-  int64_t cps = S > 1 ? ceil_div(N, S) : (N > 0 ? N : 1);
-  cps = ceil_div(cps, 8) * 8;
-  if (S > 1) S = ceil_div(N, cps);
+  // Columns per split: a multiple of 8; the split count is what that leaves.
+  auto split_of = [&](int64_t s, int64_t& cps_out) {
+    int64_t c = s > 1 ? ceil_div(N, s) : (N > 0 ? N : 1);
+    c = ceil_div(c, 8) * 8;
+    cps_out = c;
+    return s > 1 ? ceil_div(N, c) : (int64_t)1;
+  };
+  int64_t cps = 0;
+  S = split_of(S, cps);
+  // The sweeps are long and uniform, so the launch runs in rounds of one workgroup per
+  // resident slot; a last round that is only partly filled idles the rest of the chip for a
+  // whole workgroup's duration. Among split counts between half and twice the one above
+  // (keeping the L2 bound), take the one whose workgroups fill their rounds best.
+  const int occupancy = op == 1 ? 7 : 8;  // resident workgroups per CU (register budgets)
+  if ((op == 0 || op == 1 || op == 3) && p.row_blocks > 0) {
+    const int64_t slots = (int64_t)num_cus * occupancy;
+    const int64_t s_min = ceil_div(N, lowd::kSplitCols);
+    const int64_t lo = S / 2 > s_min ? S / 2 : s_min;
+    const int64_t hi = 2 * S < max_split ? 2 * S : max_split;
+    double best = -1.0;
+    int64_t best_s = S, best_cps = cps;
+    for (int64_t s = lo > 1 ? lo : 1; s <= hi; ++s) {
+      int64_t c = 0;
+      const int64_t real = split_of(s, c);
+      const int64_t total = p.row_blocks * real;
+      const double fill = (double)total / (double)(ceil_div(total, slots) * slots);
+      if (fill > best + 1e-9) {
+        best = fill;
+        best_s = real;
+        best_cps = c;
+      }
+    }
+    S = best_s;
+    cps = best_cps;
+  }
   p.splits = S;
   p.cols_per_split = cps;
   return p;
