@@ -290,9 +290,11 @@ size_t backward_bytes(int64_t B, int64_t M, int64_t N, int D, int C, bool half, 
   size_t need = 0;
   auto take = [&](size_t v) { need = v > need ? v : need; };
   if (half) {
-    if (want_x) take(keops::highd_grad_workspace_bytes(B, M, N, D, C));
-    if (want_y) take(keops::highd_grad_workspace_bytes(B, N, M, D, C));
-    if (want_b) take(keops::highd_workspace_bytes(B, N, M, D, C, keops::kElemF16, true));
+    // the y-gradient sweep also yields the b-gradient when C is small enough
+    const bool fuse_b = want_y && want_b && C <= keops::hd_fused_weight_channels();
+    if (want_x) take(keops::highd_grad_workspace_bytes(B, M, N, D, C, false));
+    if (want_y) take(keops::highd_grad_workspace_bytes(B, N, M, D, C, fuse_b));
+    if (want_b && !fuse_b) take(keops::highd_workspace_bytes(B, N, M, D, C, keops::kElemF16, true));
   } else {
     if (want_x) take(lowd_layout(KEOPS_OP_GAUSS_SUM_GRAD_X, M, N, D, C, 0).total);
     if (want_y) take(lowd_layout(KEOPS_OP_GAUSS_SUM_GRAD_X, N, M, D, C, 0).total);
@@ -437,12 +439,15 @@ int keops_gauss_sum_backward(const void* x, const void* y, const void* b, const 
   if (half) {
     // rows x with weights g against columns y with weights b, and the transpose of that.
     if (want_x)
-      KEOPS_HIP(keops::launch_gauss_sum_grad_highd(x, y, g, true, b, false, grad_x, ws, B, M, N, D, C, sigma, stream),
+      KEOPS_HIP(keops::launch_gauss_sum_grad_highd(x, y, g, true, b, false, grad_x, nullptr, ws, B, M, N, D, C, sigma,
+                                                   stream),
                 "grad_x_highd");
+    const bool fuse_b = want_y && want_b && C <= keops::hd_fused_weight_channels();
     if (want_y)
-      KEOPS_HIP(keops::launch_gauss_sum_grad_highd(y, x, b, false, g, true, grad_y, ws, B, N, M, D, C, sigma, stream),
+      KEOPS_HIP(keops::launch_gauss_sum_grad_highd(y, x, b, false, g, true, grad_y, fuse_b ? grad_b : nullptr, ws, B, N,
+                                                   M, D, C, sigma, stream),
                 "grad_y_highd");
-    if (want_b)
+    if (want_b && !fuse_b)
       KEOPS_HIP(keops::launch_gauss_sum_highd(y, x, keops::kElemF16, g, keops::kElemF32, nullptr, nullptr, grad_b, ws,
                                               B, N, M, D, C, sigma, stream),
                 "grad_b_highd");

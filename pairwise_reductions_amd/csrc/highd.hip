@@ -66,7 +66,9 @@ weight_norm_max_kernel(const T* __restrict__ w, const float* __restrict__ cscale
 // staged through LDS so that every global read and write is contiguous.
 //   kMode kCopy:    beta_j = -|k_j|^2/2, wp = the fp16 weights unchanged (fast forward path);
 //   kMode kNormFwd: the general form of the file comment, forward layout;
-//   kMode kNormGrad: the general form, gradient layout, plus the key-permuted columns yp.
+//   kMode kNormGrad: the general form, gradient layout, plus the key-permuted columns yp and,
+//                    when wpl is given, the weights key-permuted again for the fused second
+//                    output of the gradient sweep.
 // Layouts: forward wp[t][j/32][c][key_slot(j%32)] for c < Cw (the A operand of O^T);
 // gradient wp[t][j][c] for c < Cw (the A operand of dP^T) and yp[t][j/32][ch][key_slot(j%32)]
 // = k[t][j][ch] for ch < D, 1 at ch = Dp, else 0. Keys past N get beta = -inf and zeros.
@@ -145,6 +147,14 @@ col_prep_kernel(const TK* __restrict__ k, const T* __restrict__ w, const float* 
     for (int e = tid; e < 32 * Cw; e += 256) {
       const int key = e / Cw, c = e % Cw;
       dst[e] = (_Float16)(c < C ? sw[key][c] * sinv[key] : 0.0f);
+    }
+    if (wpl) {  // the same unit weights key-permuted over hd::kFusedWeightChannels channels
+      constexpr int CF = hd::kFusedWeightChannels;
+      _Float16* d2 = wpl + (t * Npad + j0) * CF;
+      for (int e = tid; e < 32 * CF; e += 256) {
+        const int c = e / 32, key = slot_key(e % 32);
+        d2[e] = (_Float16)(c < C ? sw[key][c] * sinv[key] : 0.0f);
+      }
     }
     const int YC = Dp + 16;
     _Float16* yd = yp + (t * Npad + j0) * YC;
@@ -254,13 +264,14 @@ FwdLayout fwd_layout(int64_t B, int64_t M, int64_t N, int D, int C, ElemType xy,
 
 struct GradLayout {
   Split sp;
-  size_t nmax, beta, bvp, yp, ap, rho, part, total;
+  size_t nmax, beta, bvp, yp, ap, rho, part, gp, part2, total;
 };
 
-GradLayout grad_layout(int64_t B, int64_t M, int64_t N, int D, int C, int num_cus) {
+GradLayout grad_layout(int64_t B, int64_t M, int64_t N, int D, int C, bool fused, int num_cus) {
   GradLayout L;
   const int Dp = hd::padded_features(D), Ck = hd::padded_k_channels(C);
-  L.sp = plan_split(B, M, N, hd::kWaves * hd::grad_query_tiles(Dp, Ck) * 16, num_cus);
+  L.sp = plan_split(B, M, N, hd::kWaves * hd::grad_query_tiles(Dp, Ck, fused ? hd::kFusedWeightChannels : 0) * 16,
+                    num_cus);
   Carve c;
   L.nmax = c.take((size_t)B * sizeof(float));
   L.beta = c.take((size_t)B * L.sp.Npad * sizeof(float));
@@ -269,6 +280,8 @@ GradLayout grad_layout(int64_t B, int64_t M, int64_t N, int D, int C, int num_cu
   L.ap = c.take((size_t)B * M * Ck * sizeof(_Float16));
   L.rho = c.take((size_t)B * M * sizeof(float));
   L.part = c.take(L.sp.splits > 1 ? (size_t)L.sp.splits * B * M * D * sizeof(float) : 0);
+  L.gp = c.take(fused ? (size_t)B * L.sp.Npad * hd::kFusedWeightChannels * sizeof(_Float16) : 0);
+  L.part2 = c.take(fused && L.sp.splits > 1 ? (size_t)L.sp.splits * B * M * C * sizeof(float) : 0);
   L.total = c.off;
   return L;
 }
@@ -326,6 +339,8 @@ hipError_t weight_norm_max(const T* w, const float* cscale, float* nmax, int64_t
 
 }  // namespace
 
+int hd_fused_weight_channels() { return hd::kFusedWeightChannels; }
+
 bool highd_supported(int D, int C) { return D >= 16 && D <= 128 && D % 16 == 0 && C >= 1 && C <= 64; }
 
 bool highd_general(ElemType xy, ElemType bt, bool col_scaled) {
@@ -337,9 +352,9 @@ size_t highd_workspace_bytes(int64_t B, int64_t M, int64_t N, int D, int C, Elem
   return fwd_layout(B, M, N, D, C, xy, general, device_cus()).total;
 }
 
-size_t highd_grad_workspace_bytes(int64_t B, int64_t M, int64_t N, int D, int C) {
+size_t highd_grad_workspace_bytes(int64_t B, int64_t M, int64_t N, int D, int C, bool fused) {
   if (B == 0 || M == 0 || N == 0) return 0;
-  return grad_layout(B, M, N, D, C, device_cus()).total;
+  return grad_layout(B, M, N, D, C, fused, device_cus()).total;
 }
 
 namespace {
@@ -430,9 +445,11 @@ hipError_t launch_gauss_sum_highd(const void* x, const void* y, ElemType xy, con
 }
 
 hipError_t launch_gauss_sum_grad_highd(const void* x, const void* y, const void* a, bool a_f32, const void* bv,
-                                       bool bv_f32, float* out, void* workspace, int64_t B, int64_t M, int64_t N,
-                                       int D, int C, float sigma, hipStream_t s) {
-  const GradLayout L = grad_layout(B, M, N, D, C, device_cus());
+                                       bool bv_f32, float* out, float* out2, void* workspace, int64_t B, int64_t M,
+                                       int64_t N, int D, int C, float sigma, hipStream_t s) {
+  const bool fused = out2 != nullptr;
+  if (fused && C > hd::kFusedWeightChannels) return hipErrorInvalidValue;
+  const GradLayout L = grad_layout(B, M, N, D, C, fused, device_cus());
   char* ws = static_cast<char*>(workspace);
   float* nmax = reinterpret_cast<float*>(ws + L.nmax);
   float* beta = reinterpret_cast<float*>(ws + L.beta);
@@ -441,6 +458,8 @@ hipError_t launch_gauss_sum_grad_highd(const void* x, const void* y, const void*
   _Float16* ap = reinterpret_cast<_Float16*>(ws + L.ap);
   float* rho = reinterpret_cast<float*>(ws + L.rho);
   float* part = reinterpret_cast<float*>(ws + L.part);
+  _Float16* gp = fused ? reinterpret_cast<_Float16*>(ws + L.gp) : nullptr;
+  float* part2 = reinterpret_cast<float*>(ws + L.part2);
   const _Float16* k = static_cast<const _Float16*>(y);
   const float cs = cs_of(sigma);
   const int Dp = hd::padded_features(D), Ck = hd::padded_k_channels(C);
@@ -450,13 +469,13 @@ hipError_t launch_gauss_sum_grad_highd(const void* x, const void* y, const void*
     const float* w = static_cast<const float*>(bv);
     e = weight_norm_max(w, nullptr, nmax, B, N, C, s);
     if (e != hipSuccess) return e;
-    col_prep_kernel<_Float16, float, kNormGrad><<<pgrid, 256, 0, s>>>(k, w, nullptr, nmax, beta, bvp, nullptr, yp, N,
+    col_prep_kernel<_Float16, float, kNormGrad><<<pgrid, 256, 0, s>>>(k, w, nullptr, nmax, beta, bvp, gp, yp, N,
                                                                       L.sp.Npad, D, Dp, C, Ck, cs);
   } else {
     const _Float16* w = static_cast<const _Float16*>(bv);
     e = weight_norm_max(w, nullptr, nmax, B, N, C, s);
     if (e != hipSuccess) return e;
-    col_prep_kernel<_Float16, _Float16, kNormGrad><<<pgrid, 256, 0, s>>>(k, w, nullptr, nmax, beta, bvp, nullptr, yp,
+    col_prep_kernel<_Float16, _Float16, kNormGrad><<<pgrid, 256, 0, s>>>(k, w, nullptr, nmax, beta, bvp, gp, yp,
                                                                          N, L.sp.Npad, D, Dp, C, Ck, cs);
   }
   e = hipGetLastError();
@@ -478,6 +497,9 @@ hipError_t launch_gauss_sum_grad_highd(const void* x, const void* y, const void*
   g.yp = yp;
   g.oscale = nmax;
   g.out = L.sp.splits > 1 ? part : out;
+  g.gp = gp;
+  g.out2 = fused ? (L.sp.splits > 1 ? part2 : out2) : nullptr;
+  g.C2 = C;
   g.M = M;
   g.N = N;
   g.Npad = L.sp.Npad;
@@ -490,7 +512,9 @@ hipError_t launch_gauss_sum_grad_highd(const void* x, const void* y, const void*
   g.stream = s;
   e = grad_dispatch(g);
   if (e != hipSuccess || L.sp.splits == 1) return e;
-  return combine(part, out, B * M * D, L.sp.splits, s);
+  e = combine(part, out, B * M * D, L.sp.splits, s);
+  if (e != hipSuccess || !fused) return e;
+  return combine(part2, out2, B * M * C, L.sp.splits, s);
 }
 
 }  // namespace keops

@@ -39,7 +39,10 @@ constexpr bool fwd_fused(int D, int C, bool split) {
 }
 // The gradient kernel holds three products per subtile, so it takes fewer.
 // (Sizes chosen so every instantiation fits 256 VGPRs, i.e. two waves per SIMD.)
-constexpr int grad_query_tiles(int D, int CK) { return D <= 32 ? (CK <= 32 ? 4 : 2) : 1; }
+constexpr int grad_query_tiles(int D, int CK, int CB) { return D <= 32 ? (CK <= 32 && CB == 0 ? 4 : 2) : 1; }
+// The gradient sweep can also produce the weights' gradient (a second output of at most
+// kFusedWeightChannels channels) from the same kernel values.
+constexpr int kFusedWeightChannels = 16;
 // Features run in steps of 32 (the K of one MFMA) and are read as zero past D; output and
 // weight channels run in tiles of 16.
 constexpr int padded_features(int D) { return (D + 31) / 32 * 32; }
@@ -98,9 +101,11 @@ struct GradArgs {
   const _Float16* yp;      // [B][Npad/32][Dp + 16][32] key-permuted columns plus a ones channel
   const float* oscale;     // [B] largest column weight norm
   float* out;              // [S][B][M][D]
+  const _Float16* gp;      // [B][Npad/32][16][32] key-permuted unit column weights (second output), or null
+  float* out2;             // [S][B][M][C2] second output sum_j Phi_ij bv_j, or null
   int64_t M, N, Npad, kps;
   float cs, tau;
-  int D, Ck;
+  int D, Ck, C2;
   dim3 grid;
   hipStream_t stream;
 };

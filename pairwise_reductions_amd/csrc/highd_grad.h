@@ -14,6 +14,10 @@
 //   W    = 2^(cs S' + alpha) * dP, rounded to fp16 in the lanes that computed it
 //   O^T += Y'^T W^T              (Y' = the columns plus a channel of ones, so the row sums
 //                                 sum_j W_ij come out of the same product)
+// With CB > 0 the same sweep also accumulates the plain weighted sum O2^T += Bv'^T P^T over the
+// kernel values P (before the dP factor), which in the y-gradient role (rows y, columns x,
+// column weights g) is the gradient with respect to b, sum_i Phi_ij g_i, at the cost of one
+// conversion per kernel value and CB/16 more MFMAs, with no further exponential.
 // Overflow of W in fp16 is ruled out by scaling: a'_i = a_i/|a_i| and bv'_j = bv_j/|bv_j| have
 // unit norm, so |a'.bv'| <= 1, and log2(|bv_j| / max_j |bv_j|) is folded into beta_j, so the
 // tracked exponent still never exceeds zero before the shift. The epilogue restores
@@ -30,12 +34,13 @@ namespace keops {
 namespace hd {
 namespace {
 
-template <int D, int CK, int QT, int kStage>
+template <int D, int CK, int QT, int kStage, int CB>
 __global__ void __launch_bounds__(256, 1)
 grad_kernel(const _Float16* __restrict__ x, const _Float16* __restrict__ y, const _Float16* __restrict__ ap,
             const float* __restrict__ rho, const float* __restrict__ beta, const _Float16* __restrict__ bvp,
-            const _Float16* __restrict__ yp, const float* __restrict__ oscale, float* __restrict__ out, int64_t M,
-            int64_t N, int64_t Npad, int64_t kps, float cs, float tau, int Din) {
+            const _Float16* __restrict__ yp, const _Float16* __restrict__ gp, const float* __restrict__ oscale,
+            float* __restrict__ out, float* __restrict__ out2, int64_t M, int64_t N, int64_t Npad, int64_t kps,
+            float cs, float tau, int Din, int Cout2) {
   constexpr int DS = D / 32;           // K-steps of S^T
   constexpr int KS = CK / 32;          // K-steps of dP^T
   constexpr int YC = D + 16;           // channels of Y': D features, then the ones tile
@@ -49,6 +54,8 @@ grad_kernel(const _Float16* __restrict__ x, const _Float16* __restrict__ y, cons
   __shared__ __attribute__((aligned(16))) _Float16 sA[2][kStage][AP];
   __shared__ __attribute__((aligned(16))) _Float16 sY[2][NSUB][YC][VP];
   __shared__ __attribute__((aligned(16))) float sB[2][kStage];
+  constexpr int CBT = CB > 0 ? CB / 16 : 1;  // 16-channel tiles of the second output
+  __shared__ __attribute__((aligned(16))) _Float16 sG[2][NSUB][CB > 0 ? CB : 1][VP];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, l16 = lane & 15;
@@ -64,6 +71,7 @@ grad_kernel(const _Float16* __restrict__ x, const _Float16* __restrict__ y, cons
   const float* bb = beta + bt * Npad;
   const _Float16* vb = bvp + bt * Npad * CK;
   const _Float16* pb = yp + bt * Npad * YC;
+  const _Float16* gb = CB > 0 ? gp + bt * Npad * CB : nullptr;
 
   half8 qop[QT][DS], aop[QT][KS];
   float alpha[QT], mrow[QT];
@@ -90,19 +98,23 @@ grad_kernel(const _Float16* __restrict__ x, const _Float16* __restrict__ y, cons
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) aop[qt][ks] = *reinterpret_cast<const half8*>(ab + i * CK + 32 * ks + 8 * g);
   }
-  f32x4 O[QT][OT];
+  f32x4 O[QT][OT], O2[QT][CBT];
 #pragma unroll
-  for (int qt = 0; qt < QT; ++qt)
+  for (int qt = 0; qt < QT; ++qt) {
 #pragma unroll
     for (int ot = 0; ot < OT; ++ot) O[qt][ot] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int cb = 0; cb < CBT; ++cb) O2[qt][cb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  }
 
   // Stage loads, global -> registers before the current stage is computed, registers -> LDS
   // after it. Each table is cut into 16-byte chunks dealt round-robin to the 256 threads.
   constexpr int kKChunks = kStage * D / 8, KCH = (kKChunks + 255) / 256;
   constexpr int kAChunks = kStage * CK / 8, ACH = (kAChunks + 255) / 256;
   constexpr int kYChunks = NSUB * YC * 4, YCH = (kYChunks + 255) / 256;
+  constexpr int kGChunks = CB > 0 ? NSUB * CB * 4 : 0, GCH = kGChunks > 0 ? (kGChunks + 255) / 256 : 1;
   static_assert(kStage / 4 <= 256 && kStage % 32 == 0, "tile shapes");
-  half8 rk[KCH], ra[ACH], ry[YCH];
+  half8 rk[KCH], ra[ACH], ry[YCH], rg[GCH];
   f32x4 rb = {};
   auto fetch = [&](int64_t st) {
     const int64_t jb = j0 + st * kStage;
@@ -126,6 +138,14 @@ grad_kernel(const _Float16* __restrict__ x, const _Float16* __restrict__ y, cons
       const int t = c / (YC * 4), rem = c % (YC * 4), ch = rem / 4, part = (rem % 4) * 8;
       if (c < kYChunks) ry[r] = *reinterpret_cast<const half8*>(pb + ((jb / 32 + t) * YC + ch) * 32 + part);
     }
+    if constexpr (CB > 0) {
+#pragma unroll
+      for (int r = 0; r < GCH; ++r) {
+        const int c = tid + 256 * r;
+        const int t = c / (CB * 4), rem = c % (CB * 4), ch = rem / 4, part = (rem % 4) * 8;
+        if (c < kGChunks) rg[r] = *reinterpret_cast<const half8*>(gb + ((jb / 32 + t) * CB + ch) * 32 + part);
+      }
+    }
     if (tid < kStage / 4) rb = *reinterpret_cast<const f32x4*>(bb + jb + 4 * tid);
   };
   auto commit = [&](int buf) {
@@ -144,6 +164,14 @@ grad_kernel(const _Float16* __restrict__ x, const _Float16* __restrict__ y, cons
       const int c = tid + 256 * r;
       const int t = c / (YC * 4), rem = c % (YC * 4);
       if (c < kYChunks) *reinterpret_cast<half8*>(&sY[buf][t][rem / 4][(rem % 4) * 8]) = ry[r];
+    }
+    if constexpr (CB > 0) {
+#pragma unroll
+      for (int r = 0; r < GCH; ++r) {
+        const int c = tid + 256 * r;
+        const int t = c / (CB * 4), rem = c % (CB * 4);
+        if (c < kGChunks) *reinterpret_cast<half8*>(&sG[buf][t][rem / 4][(rem % 4) * 8]) = rg[r];
+      }
     }
     if (tid < kStage / 4) *reinterpret_cast<f32x4*>(&sB[buf][4 * tid]) = rb;
   };
@@ -172,9 +200,14 @@ grad_kernel(const _Float16* __restrict__ x, const _Float16* __restrict__ y, cons
         for (int ks = 0; ks < KS; ++ks) bop[hh][ks] = *reinterpret_cast<const half8*>(&sA[buf][key][32 * ks + 8 * g]);
         bc[hh] = *reinterpret_cast<const f32x4*>(&sB[buf][sub * 32 + 16 * hh + 4 * g]);
       }
-      half8 yop[OT];
+      half8 yop[OT], gop[CBT];
 #pragma unroll
       for (int ot = 0; ot < OT; ++ot) yop[ot] = *reinterpret_cast<const half8*>(&sY[buf][sub][16 * ot + l16][8 * g]);
+      if constexpr (CB > 0) {
+#pragma unroll
+        for (int cb = 0; cb < CBT; ++cb)
+          gop[cb] = *reinterpret_cast<const half8*>(&sG[buf][sub][16 * cb + l16][8 * g]);
+      }
       bool all_settled = true;
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) {
@@ -203,15 +236,27 @@ grad_kernel(const _Float16* __restrict__ x, const _Float16* __restrict__ y, cons
           const float sc = (first || delta == 0.0f) ? 1.0f : exp2_hw(-delta);
 #pragma unroll
           for (int ot = 0; ot < OT; ++ot) O[qt][ot] *= sc;
+          if constexpr (CB > 0) {
+#pragma unroll
+            for (int cb = 0; cb < CBT; ++cb) O2[qt][cb] *= sc;
+          }
           all_settled = all_settled && (mrow[qt] >= -kSlack);
         }
-        half8 wb;
+        half8 wb, pb8;
 #pragma unroll
-        for (int s = 0; s < 8; ++s)
-          wb[s] = (_Float16)(exp2_hw(fmaf(S[s >> 2][s & 3], cs, alpha[qt])) * P[s >> 2][s & 3]);
+        for (int s = 0; s < 8; ++s) {
+          const float pv = exp2_hw(fmaf(S[s >> 2][s & 3], cs, alpha[qt]));
+          wb[s] = (_Float16)(pv * P[s >> 2][s & 3]);
+          if constexpr (CB > 0) pb8[s] = (_Float16)pv;
+        }
 #pragma unroll
         for (int ot = 0; ot < OT; ++ot)
           O[qt][ot] = __builtin_amdgcn_mfma_f32_16x16x32_f16(yop[ot], wb, O[qt][ot], 0, 0, 0);
+        if constexpr (CB > 0) {
+#pragma unroll
+          for (int cb = 0; cb < CBT; ++cb)
+            O2[qt][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(gop[cb], pb8, O2[qt][cb], 0, 0, 0);
+        }
       }
       if constexpr (kTrack) {
         settled = __all(all_settled);
@@ -253,6 +298,23 @@ grad_kernel(const _Float16* __restrict__ x, const _Float16* __restrict__ y, cons
       *reinterpret_cast<f32x4*>(dst + i * Din + d0) = o;
     }
   }
+  // Second output: sum_j Phi_ij bv_j = 2^m_i max|bv| sum_j P'_ij bv'_j, first Cout2 channels.
+  if constexpr (CB > 0) {
+    float* dst2 = out2 + (split * gridDim.z + bt) * M * Cout2;
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      const int64_t i = row_base + qt * 16 + l16;
+      if (i >= M) continue;
+      const float scale = exp2_hw(mrow[qt]) * osc;
+#pragma unroll
+      for (int cb = 0; cb < CBT; ++cb)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int c = 16 * cb + 4 * g + v;
+          if (c < Cout2) dst2[i * Cout2 + c] = scale * O2[qt][cb][v];
+        }
+    }
+  }
 }
 
 }  // namespace
@@ -260,12 +322,18 @@ grad_kernel(const _Float16* __restrict__ x, const _Float16* __restrict__ y, cons
 template <int Dp>
 hipError_t grad_launch(const GradArgs& a) {
   constexpr int kStage = Dp <= 64 ? kStageKeys : 32;
-#define KEOPS_GRAD(CKv)                                                                               \
-  grad_kernel<Dp, CKv, grad_query_tiles(Dp, CKv), kStage><<<a.grid, 256, 0, a.stream>>>(a.x, a.y, a.ap, a.rho, a.beta, a.bvp, a.yp, \
-                                                                 a.oscale, a.out, a.M, a.N, a.Npad, a.kps,   \
-                                                                 a.cs, a.tau, a.D)
-  if (a.Ck == 32) KEOPS_GRAD(32);
-  else KEOPS_GRAD(64);
+#define KEOPS_GRAD(CKv, CBv)                                                                                     \
+  grad_kernel<Dp, CKv, grad_query_tiles(Dp, CKv, CBv), kStage, CBv><<<a.grid, 256, 0, a.stream>>>(               \
+      a.x, a.y, a.ap, a.rho, a.beta, a.bvp, a.yp, a.gp, a.oscale, a.out, a.out2, a.M, a.N, a.Npad, a.kps, a.cs, \
+      a.tau, a.D, a.C2)
+  if (a.out2) {
+    if (a.Ck == 32) KEOPS_GRAD(32, 16);
+    else return hipErrorInvalidValue;
+  } else if (a.Ck == 32) {
+    KEOPS_GRAD(32, 0);
+  } else {
+    KEOPS_GRAD(64, 0);
+  }
 #undef KEOPS_GRAD
   return hipGetLastError();
 }

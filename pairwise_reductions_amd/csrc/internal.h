@@ -79,10 +79,13 @@ hipError_t launch_gauss_sum_highd(const void* x, const void* y, ElemType xy, con
                                   float sigma, hipStream_t s);
 // out[t][i] = -tau sum_j Phi_ij (a_i . bv_j)(x_i - y_j): rows x with weights a [B][M][C],
 // columns y with weights bv [B][N][C] (each fp16, or fp32 when flagged); out [B][M][D].
-size_t highd_grad_workspace_bytes(int64_t B, int64_t M, int64_t N, int D, int C);
+// Channels of b up to which the y-gradient sweep also produces the b-gradient.
+int hd_fused_weight_channels();
+// With out2 (C <= hd_fused_weight_channels() only), the same sweep also writes out2[t][i] = sum_j Phi_ij bv_j, [B][M][C].
+size_t highd_grad_workspace_bytes(int64_t B, int64_t M, int64_t N, int D, int C, bool fused);
 hipError_t launch_gauss_sum_grad_highd(const void* x, const void* y, const void* a, bool a_f32,
-                                       const void* bv, bool bv_f32, float* out, void* workspace,
-                                       int64_t B, int64_t M, int64_t N, int D, int C, float sigma,
-                                       hipStream_t s);
+                                       const void* bv, bool bv_f32, float* out, float* out2,
+                                       void* workspace, int64_t B, int64_t M, int64_t N, int D,
+                                       int C, float sigma, hipStream_t s);
 
 }  // namespace keops
