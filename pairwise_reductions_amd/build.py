@@ -17,12 +17,13 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libkeops_mi355x.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 HIGHD_SOURCES = ["highd.hip", "highd_d32.hip", "highd_d64.hip", "highd_d96.hip", "highd_d128.hip"]
-SOURCES = ["abi.hip", "lowd.hip", "lowd_sum.hip", "lowd_lse.hip", "lowd_knn.hip", "lowd_grad.hip"] + HIGHD_SOURCES
+SOURCES = ["abi.hip", "lowd.hip", "lowd_sum.hip", "lowd_mfma.hip", "lowd_lse.hip", "lowd_knn.hip", "lowd_grad.hip"] + HIGHD_SOURCES
 # Per-source extras. The matrix-core sources keep matrix-core accumulators in ordinary VGPRs (the
 # exponent and max steps read every accumulator value, so AGPR copies would cost a VALU op
 # each) and runs with IEEE mode off, so max needs no NaN quieting.
 EXTRA_FLAGS = {src: ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mno-amdgpu-ieee", "-fno-honor-nans"]
                for src in HIGHD_SOURCES}
+EXTRA_FLAGS["lowd_mfma.hip"] = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
 ARCH = os.environ.get("KEOPS_OFFLOAD_ARCH", "gfx950")
 
 # Packed-FP32 instruction selection is switched off: every float32 op is a plain VALU op.

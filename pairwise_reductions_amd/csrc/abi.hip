@@ -82,6 +82,7 @@ struct LowdLayout {
   size_t aux_off;               // one double: the largest column norm (argKmin screening)
   size_t part_off, part_bytes;  // per-split partials (argKmin lists for ops 2 and 6)
   size_t lse_off;               // per-split (m, l) pairs of the fused argKmin + LSE (op 6)
+  size_t mf_off;                // Gauss sum: the matrix-core operand region
   size_t total;
 };
 
@@ -108,7 +109,8 @@ LowdLayout lowd_layout(int op, int64_t M, int64_t N, int D, int C, int K) {
     L.part_bytes = 0;
   }
   L.lse_off = L.part_off + L.part_bytes;
-  L.total = L.lse_off + lse_bytes;
+  L.mf_off = L.lse_off + lse_bytes;
+  L.total = L.mf_off + (op == KEOPS_OP_GAUSS_SUM ? keops::mf_region_bytes(M, N, D) : 0);
   if (M == 0 || N == 0) L.total = 0;
   return L;
 }
@@ -248,9 +250,8 @@ int gauss_sum_run(const void* x, const void* y, keops_dtype dtype, const void* b
   double* cols = reinterpret_cast<double*>(ws + L.cols_off);
   float* part = reinterpret_cast<float*>(ws + L.part_off);
   const double c2 = c2_of(sigma);
-  KEOPS_HIP(keops::launch_prep_cols(static_cast<const float*>(y), cols, N, D, c2, true, stream), "prep_cols");
   KEOPS_HIP(keops::launch_gauss_sum_lowd(static_cast<const float*>(x), static_cast<const float*>(y), cols, bw, rscale,
-                                         out, part, M, N, D, C, c2, L.plan, stream),
+                                         out, part, ws + L.mf_off, M, N, D, C, c2, L.plan, stream),
             "gauss_sum_lowd");
   return ok();
 }
@@ -475,9 +476,8 @@ int keops_gauss_sum_backward(const void* x, const void* y, const void* b, const 
     const LowdLayout L = lowd_layout(KEOPS_OP_GAUSS_SUM, N, M, D, C, 0);
     double* cols = reinterpret_cast<double*>(ws + L.cols_off);
     const double c2 = c2_of(sigma);
-    KEOPS_HIP(keops::launch_prep_cols(xf, cols, M, D, c2, true, stream), "prep_cols");
-    KEOPS_HIP(keops::launch_gauss_sum_lowd(yf, xf, cols, g, nullptr, grad_b,
-                                           reinterpret_cast<float*>(ws + L.part_off), N, M, D, C, c2, L.plan, stream),
+    KEOPS_HIP(keops::launch_gauss_sum_lowd(yf, xf, cols, g, nullptr, grad_b, reinterpret_cast<float*>(ws + L.part_off),
+                                           ws + L.mf_off, N, M, D, C, c2, L.plan, stream),
               "grad_b_lowd");
   }
   return ok();
@@ -734,8 +734,8 @@ int keops_gauss_sum_grad_b(const float* x, const float* y, const float* g, float
   double* cols = reinterpret_cast<double*>(ws + L.cols_off);
   float* part = reinterpret_cast<float*>(ws + L.part_off);
   const double c2 = c2_of(sigma);
-  KEOPS_HIP(keops::launch_prep_cols(x, cols, M, D, c2, true, stream), "prep_cols");
-  KEOPS_HIP(keops::launch_gauss_sum_lowd(y, x, cols, g, nullptr, grad_b, part, N, M, D, C, c2, L.plan, stream),
+  KEOPS_HIP(keops::launch_gauss_sum_lowd(y, x, cols, g, nullptr, grad_b, part, ws + L.mf_off, N, M, D, C, c2, L.plan,
+                                         stream),
             "grad_b_lowd");
   return ok();
 }

@@ -26,6 +26,10 @@ struct Plan {
   int64_t row_blocks;   // ceil(M / rows_per_block)
   int64_t splits;       // S: column ranges reduced independently, then combined in order
   int64_t cols_per_split;
+  // Gauss sum only: the matrix-core sweep's row tiles of 16 per wave and its workgroup count
+  // along the rows (it shares the column splits with the float64 sweep).
+  int mf_rt = 0;
+  int64_t mf_row_blocks = 0;
 };
 
 Plan plan_lowd(int op, int64_t M, int64_t N, int D, int C, int K, int num_cus);
@@ -36,13 +40,27 @@ size_t partial_bytes_per_row(int op, int D, int C, int K);
 
 // ---- launchers (return hipError_t of the launch) ----------------------------------------
 // cols[j] = (y_j - o, -c2 |y_j - o|^2) in float64, o = y_0 when `centre`, else o = 0.
+// Skipped on the device when `skip` is given and *skip is nonzero.
 hipError_t launch_prep_cols(const float* y, double* cols, int64_t N, int D, double c2,
-                            bool centre, hipStream_t s);
-// out[i][c] = rscale[i] * sum_j 2^{-c2 |x_i - y_j|^2} b[j][c] (rscale may be null).
-hipError_t launch_gauss_sum_lowd(const float* x, const float* y, const double* cols,
-                                 const float* b, const float* rscale, float* out, float* partial,
+                            bool centre, hipStream_t s, const int* skip = nullptr);
+// out[i][c] = rscale[i] * sum_j 2^{-c2 |x_i - y_j|^2} b[j][c] (rscale may be null). Runs the
+// matrix-core sweep when the operand preparation in `mf` (mf_region_bytes) admits the inputs,
+// else builds the float64 column table in `cols` and runs the float64 sweep; the choice is made
+// on the device.
+hipError_t launch_gauss_sum_lowd(const float* x, const float* y, double* cols, const float* b,
+                                 const float* rscale, float* out, float* partial, void* mf,
                                  int64_t M, int64_t N, int D, int C, double c2, const Plan& p,
                                  hipStream_t s);
+// Matrix-core Gauss sum pieces (lowd_mfma.hip): operand region size, the device-side decision
+// (nonzero: matrix-core sweep), row tiles per wave for C channels, preparation and sweep.
+size_t mf_region_bytes(int64_t M, int64_t N, int D);
+const int* mf_gate(const void* region);
+int mf_rows_per_lane(int C);
+int mf_occupancy(int D, int C, int rt);  // resident workgroups per CU of the matrix-core sweep
+hipError_t launch_mf_prepare(const float* x, const float* y, void* region, int64_t M, int64_t N, int D,
+                             double c2, hipStream_t s);
+hipError_t launch_mf_sum(const float* b, const float* rscale, float* dst, void* region, int64_t M,
+                         int64_t N, int D, int C, const Plan& p, hipStream_t s);
 hipError_t launch_lse_lowd(const float* x, const float* y, const double* cols, float* out,
                            double* partial, int64_t M, int64_t N, int D, double c2,
                            const Plan& p, hipStream_t s);

@@ -11,9 +11,9 @@ namespace {
 // cols[j] = (y_j - o, B_j) in float64, o = y_0 when `centre`, else o = 0 (then B_j unused).
 __global__ void __launch_bounds__(kBlock)
 prep_cols_kernel(const float* __restrict__ y, double* __restrict__ cols, int64_t N, int D, int P,
-                 double c2, int centre) {
+                 double c2, int centre, const int* __restrict__ skip) {
   const int64_t j = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-  if (j >= N) return;
+  if (j >= N || (skip && *skip)) return;
   double s = 0.0;
   for (int d = 0; d < D; ++d) {
     const double o = centre ? (double)y[d] : 0.0;
@@ -111,8 +111,6 @@ size_t partial_bytes_per_row(int op, int D, int C, int K) {
 }
 
 Plan plan_lowd(int op, int64_t M, int64_t N, int D, int C, int K, int num_cus) {
-  (void)D;
-  (void)C;
   Plan p;
   switch (op) {
     case 0: p.R = lowd::kRowsSum; break;
@@ -129,22 +127,36 @@ Plan plan_lowd(int op, int64_t M, int64_t N, int D, int C, int K, int num_cus) {
   }
   p.rows_per_block = kBlock * p.R;
   p.row_blocks = M > 0 ? ceil_div(M, p.rows_per_block) : 0;
+  // The Gauss sum's matrix-core sweep takes 16 RT rows per wave; the column splits are planned
+  // for it (the float64 sweep, which runs only when the matrix-core one declines, shares them).
+  int64_t lead_blocks = p.row_blocks;
+  int64_t granule = 8;
+  if (op == 0) {
+    const int64_t max_cols_splits = N / 256 > 1 ? N / 256 : 1;
+    int rt = mf_rows_per_lane(C);
+    while (rt > 1 && ceil_div(M, (int64_t)64 * rt) * max_cols_splits < (int64_t)num_cus * 4) rt /= 2;
+    p.mf_rt = rt;
+    p.mf_row_blocks = M > 0 ? ceil_div(M, (int64_t)64 * rt) : 0;
+    lead_blocks = p.mf_row_blocks;
+    granule = 16;
+  }
   // Split the columns so that (a) there are at least eight workgroups (32 wave64s) per compute
   // unit over the launch, and (b) one split's column table stays within lowd::kSplitCols columns,
   // a working set that fits one XCD's L2 while the resident workgroups (consecutive row
   // blocks of the same split) stream it together. Every split keeps >= 256 columns.
   const int64_t target = (int64_t)num_cus * 8;
   int64_t S = 1;
-  if (p.row_blocks > 0 && p.row_blocks < target) S = ceil_div(target, p.row_blocks);
+  if (lead_blocks > 0 && lead_blocks < target) S = ceil_div(target, lead_blocks);
   if (S < ceil_div(N, lowd::kSplitCols)) S = ceil_div(N, lowd::kSplitCols);
   int64_t max_split = N / 256 > 1 ? N / 256 : 1;
   if ((op == 2 || op == 6) && max_split > 16) max_split = 16;  // argKmin partial lists are K entries per row
   if (S > max_split) S = max_split;
   if (S < 1) S = 1;
-  // Columns per split: a multiple of 8; the split count is what that leaves.
+  // Columns per split: a multiple of 8 (16 for the matrix-core tiles); the split count is what
+  // that leaves.
   auto split_of = [&](int64_t s, int64_t& cps_out) {
     int64_t c = s > 1 ? ceil_div(N, s) : (N > 0 ? N : 1);
-    c = ceil_div(c, 8) * 8;
+    c = ceil_div(c, granule) * granule;
     cps_out = c;
     return s > 1 ? ceil_div(N, c) : (int64_t)1;
   };
@@ -154,8 +166,9 @@ Plan plan_lowd(int op, int64_t M, int64_t N, int D, int C, int K, int num_cus) {
   // resident slot; a last round that is only partly filled idles the rest of the chip for a
   // whole workgroup's duration. Among split counts between half and twice the one above
   // (keeping the L2 bound), take the one whose workgroups fill their rounds best.
-  const int occupancy = op == 1 ? 7 : 8;  // resident workgroups per CU (register budgets)
-  if ((op == 0 || op == 1 || op == 3) && p.row_blocks > 0) {
+  // resident workgroups per CU (register budgets)
+  const int occupancy = op == 0 ? mf_occupancy(D, C, p.mf_rt) : (op == 1 ? 7 : 8);
+  if ((op == 0 || op == 1 || op == 3) && lead_blocks > 0) {
     const int64_t slots = (int64_t)num_cus * occupancy;
     const int64_t s_min = ceil_div(N, lowd::kSplitCols);
     const int64_t lo = S / 2 > s_min ? S / 2 : s_min;
@@ -165,7 +178,7 @@ Plan plan_lowd(int op, int64_t M, int64_t N, int D, int C, int K, int num_cus) {
     for (int64_t s = lo > 1 ? lo : 1; s <= hi; ++s) {
       int64_t c = 0;
       const int64_t real = split_of(s, c);
-      const int64_t total = p.row_blocks * real;
+      const int64_t total = lead_blocks * real;
       const double fill = (double)total / (double)(ceil_div(total, slots) * slots);
       if (fill > best + 1e-9) {
         best = fill;
@@ -183,10 +196,10 @@ Plan plan_lowd(int op, int64_t M, int64_t N, int D, int C, int K, int num_cus) {
 
 // ------------------------------------------------------------------------- launchers
 hipError_t launch_prep_cols(const float* y, double* cols, int64_t N, int D, double c2, bool centre,
-                            hipStream_t s) {
+                            hipStream_t s, const int* skip) {
   if (N <= 0) return hipSuccess;
   lowd::prep_cols_kernel<<<(unsigned)ceil_div(N, kBlock), kBlock, 0, s>>>(y, cols, N, D, col_stride(D), c2,
-                                                                           centre ? 1 : 0);
+                                                                           centre ? 1 : 0, skip);
   return hipGetLastError();
 }
 

@@ -1,0 +1,572 @@
+// Low-D float32 Gauss sum with the exponent on the fp16 matrix cores ("Kernel matrix
+// reduction", Implementation sketch: a_i = sum_j exp(-|x_i - y_j|^2 / (2 sigma^2)) b_j; the same
+// reduction as lowd_sum.hip, which remains the float64 path for inputs this one declines).
+//
+// Exponent, base 2: e_ij = -c |u_i - v_j|^2 with u = (x - o)/h and v = (y - o)/h, o the centre
+// and h the half-width of the bounding box of all points (so |u_d|, |v_d| <= 1), c = c2 h^2.
+// Expanded, e_ij = A_i + B_j + sum_d a_id v_jd with a = 2c u, A = -c|u|^2, B = -c|v|^2, and the
+// three terms cancel to a small e for the pairs that matter. A float32 accumulator adds
+// multiples of 2^g without error while every partial sum stays below 2^(g+24), in any order.
+// So each operand is cut, in fixed point, into fp16 pieces:
+//   high part   Ah_i + Bh1_j + Bh2_j + sum_d ah_id vh_jd
+//               ah, vh: a and v rounded to grids whose product grid is 2^g (11 significant bits
+//               each at most); Ah, Bh = Bh1 + Bh2: A and B rounded to 2^g. Every term is a
+//               multiple of 2^g and the partial sums are below 2^(g+23): the sum is exact.
+//   low part    sum_d (ah vl1 + ah vl2 + al1 vh + al2 vh + al1 vl1) + Al1 + Bl1
+//               vl1, vl2 and al1, al2: the next two 11-bit pieces of v - vh and a - ah;
+//               Al1, Bl1: the remainders of A and B. Terms dropped are below 2^-20 of e.
+// One 16x16x32 MFMA starts from Ah in the accumulator and adds the high part exactly; a second
+// adds the low part onto it. Its float32 rounding is relative to |e| plus the size of the low
+// part (a few units here), not to the cancelling terms (up to 2^(g+23)), which is what makes
+// float32 accumulation exact enough. Each fp16 piece is scaled by a power of two (row side
+// 2^-s, column side 2^s, one s per product kind) to sit inside fp16's range. The preparations
+// check that every piece converts exactly; when one does not, or when the low part could grow
+// past 32 (a narrow kernel on widely spread data), the float64 path runs instead: both sweeps
+// are launched and each reads the decision from device memory, so nothing waits on the host.
+//
+// Per pair the VALU then does one v_exp_f32 and C FMAs; the two MFMAs of a 16 x 16 tile run on
+// the matrix core beside them.
+#include "lowd_common.h"
+
+#include <math.h>
+
+#include <atomic>
+
+namespace keops {
+namespace lowd {
+namespace {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kMinK = 4;           // exponent scales below 2^4 are treated as 2^4
+constexpr double kMaxLow = 32.0;   // largest admissible bound on the low part
+
+// Product kinds (row piece x column piece); the shift table is indexed by these.
+enum Slot { kAhVh = 0, kOneBh1, kOneBh2, kAhVl1, kAhVl2, kAl1Vh, kAl2Vh, kAl1Vl1, kAl1One, kOneBl1, kSlots };
+
+// Decisions and constants shared by the preparation and the sweeps, written on the device.
+struct MfParams {
+  int gate;           // nonzero: the matrix-core sweep runs; zero: the float64 sweep runs
+  int alpha, beta, gamma;
+  int sh[kSlots];
+  unsigned int mm[2 * kMaxLowD];  // order-preserving encodings of the per-dimension min, max
+  double o[kMaxLowD];
+  double inv_h;
+  double cp;          // c2 h^2
+};
+
+__device__ __forceinline__ unsigned int ord_of(float f) {
+  const unsigned int u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float float_of(unsigned int u) {
+  return __uint_as_float((u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
+}
+// v rounded to the nearest multiple of 2^g
+__device__ __forceinline__ double rnd(double v, int g) { return ldexp(rint(ldexp(v, -g)), g); }
+
+__global__ void mf_init_kernel(MfParams* P) {
+  const int t = threadIdx.x;
+  if (t < kMaxLowD) {
+    P->mm[t] = 0xffffffffu;
+    P->mm[kMaxLowD + t] = 0u;
+  }
+}
+
+// Per-dimension min and max over the rows of x and of y.
+__global__ void __launch_bounds__(kBlock)
+mf_bounds_kernel(const float* __restrict__ x, const float* __restrict__ y, int64_t M, int64_t N, int D,
+                 MfParams* P) {
+  unsigned int lo[kMaxLowD], hi[kMaxLowD];
+#pragma unroll
+  for (int d = 0; d < kMaxLowD; ++d) {
+    lo[d] = 0xffffffffu;
+    hi[d] = 0u;
+  }
+  const int64_t n = M > N ? M : N;
+  for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n; i += (int64_t)gridDim.x * kBlock) {
+#pragma unroll
+    for (int d = 0; d < kMaxLowD; ++d) {
+      if (d >= D) break;
+      if (i < M) {
+        const unsigned int v = ord_of(x[i * D + d]);
+        lo[d] = v < lo[d] ? v : lo[d];
+        hi[d] = v > hi[d] ? v : hi[d];
+      }
+      if (i < N) {
+        const unsigned int v = ord_of(y[i * D + d]);
+        lo[d] = v < lo[d] ? v : lo[d];
+        hi[d] = v > hi[d] ? v : hi[d];
+      }
+    }
+  }
+#pragma unroll
+  for (int d = 0; d < kMaxLowD; ++d) {
+    if (d >= D) break;
+    unsigned int a = lo[d], b = hi[d];
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+      const unsigned int a2 = __shfl_xor(a, m), b2 = __shfl_xor(b, m);
+      a = a2 < a ? a2 : a;
+      b = b2 > b ? b2 : b;
+    }
+    if ((threadIdx.x & 63) == 0) {
+      atomicMin(&P->mm[d], a);
+      atomicMax(&P->mm[kMaxLowD + d], b);
+    }
+  }
+}
+
+// Centre, scale, grids and shifts; clears the gate when the low part could exceed kMaxLow or a
+// shift has no admissible value. One thread.
+__global__ void mf_params_kernel(MfParams* P, int D, double c2) {
+  if (threadIdx.x != 0) return;
+  double h = 0.0;
+  bool finite = true;
+  for (int d = 0; d < D; ++d) {
+    const double lo = (double)float_of(P->mm[d]), hi = (double)float_of(P->mm[kMaxLowD + d]);
+    finite = finite && isfinite(lo) && isfinite(hi);
+    const double o = (double)(float)(0.5 * (lo + hi));
+    P->o[d] = o;
+    h = fmax(h, fmax(hi - o, o - lo));
+  }
+  if (!(h > 0.0)) h = 1.0;  // all points equal: any scale will do
+  h *= 1.0 + 0x1p-40;       // keeps |u|, |v| <= 1 after rounding
+  const double cp = c2 * h * h;
+  P->inv_h = 1.0 / h;
+  P->cp = cp;
+  int gate = finite && isfinite(cp) && cp > 0.0;
+  int k = kMinK;
+  if (gate) {
+    int ex = 0;
+    const double m = frexp(2.0 * cp, &ex);  // 2cp = m 2^ex, m in [0.5, 1)
+    const int kc = (m == 0.5) ? ex - 1 : ex;  // ceil(log2(2cp))
+    k = kc > kMinK ? kc : kMinK;
+  }
+  int lg = 0;
+  while ((1 << lg) < D) ++lg;
+  const int gamma = k + 1 + lg - 23;  // partial sums of the high part stay below 2^(gamma + 23)
+  const int alpha = k - 11;           // ah: 11 bits below |a| <= 2^k
+  const int beta = gamma - alpha;     // vh: the grid that puts ah vh on 2^gamma
+  const double low = D * (ldexp(1.0, k + beta - 1) + ldexp(1.0, k - 12));
+  if (!(low <= kMaxLow)) gate = 0;
+  // (largest power of two, grid) of each piece, as exponents
+  const int ahM = k, ahQ = alpha, vhM = 0, vhQ = beta, vl1M = beta - 1, vl1Q = beta - 12, vl2M = beta - 13,
+            vl2Q = beta - 24, al1M = alpha - 1, al1Q = alpha - 12, al2M = alpha - 13, al2Q = alpha - 24,
+            smM = gamma - 1, smQ = gamma - 12, bh1M = gamma + 21, bh1Q = gamma + 11, bh2M = gamma + 10,
+            bh2Q = gamma;
+  const int rowM[kSlots] = {ahM, 0, 0, ahM, ahM, al1M, al2M, al1M, smM, 0};
+  const int rowQ[kSlots] = {ahQ, 0, 0, ahQ, ahQ, al1Q, al2Q, al1Q, smQ, 0};
+  const int colM[kSlots] = {vhM, bh1M, bh2M, vl1M, vl2M, vhM, vhM, vl1M, 0, smM};
+  const int colQ[kSlots] = {vhQ, bh1Q, bh2Q, vl1Q, vl2Q, vhQ, vhQ, vl1Q, 0, smQ};
+  for (int s = 0; s < kSlots; ++s) {
+    // fp16 holds magnitudes up to 2^15 and grids down to 2^-24
+    const int lo = max(rowM[s] - 15, -24 - colQ[s]);
+    const int hi = min(rowQ[s] + 24, 15 - colM[s]);
+    const int want = (int)floor(0.25 * (double)(rowM[s] + rowQ[s] - colM[s] - colQ[s]) + 0.5);
+    if (lo > hi) gate = 0;
+    P->sh[s] = want < lo ? lo : (want > hi ? hi : want);
+  }
+  P->alpha = alpha;
+  P->beta = beta;
+  P->gamma = gamma;
+  P->gate = gate;
+}
+
+// v 2^s as fp16; clears ok when that is not exact.
+__device__ __forceinline__ _Float16 piece(double v, int s, bool& ok) {
+  const double w = ldexp(v, s);
+  const _Float16 r = (_Float16)w;
+  ok = ok && ((double)r == w);
+  return r;
+}
+
+// Row operands: rhi[i] (8 NH fp16), rlo[i] (32 NL fp16), rA[i] = Ah_i.
+template <int NH, int NL>
+__global__ void __launch_bounds__(kBlock)
+mf_rows_kernel(const float* __restrict__ x, half8* __restrict__ rhi, half8* __restrict__ rlo, float* __restrict__ rA,
+               int64_t M, int D, MfParams* P) {
+  const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+  if (i >= M || !P->gate) return;
+  const double cp = P->cp, inv_h = P->inv_h;
+  const int alpha = P->alpha, gamma = P->gamma;
+  int sh[kSlots];
+#pragma unroll
+  for (int s = 0; s < kSlots; ++s) sh[s] = P->sh[s];
+  _Float16 hi[8 * NH], lo[32 * NL];
+#pragma unroll
+  for (int k = 0; k < 8 * NH; ++k) hi[k] = (_Float16)0.0f;
+#pragma unroll
+  for (int k = 0; k < 32 * NL; ++k) lo[k] = (_Float16)0.0f;
+  bool ok = true;
+  double nrm = 0.0;
+#pragma unroll
+  for (int d = 0; d < kMaxLowD; ++d) {
+    if (d >= D) break;
+    const double u = ((double)x[i * D + d] - P->o[d]) * inv_h;
+    nrm = fma(u, u, nrm);
+    const double a = 2.0 * cp * u;
+    const double ah = rnd(a, alpha);
+    const double al1 = rnd(a - ah, alpha - 12);
+    const double al2 = rnd(a - ah - al1, alpha - 24);
+    hi[d] = piece(ah, -sh[kAhVh], ok);
+    lo[5 * d + 0] = piece(ah, -sh[kAhVl1], ok);
+    lo[5 * d + 1] = piece(ah, -sh[kAhVl2], ok);
+    lo[5 * d + 2] = piece(al1, -sh[kAl1Vh], ok);
+    lo[5 * d + 3] = piece(al2, -sh[kAl2Vh], ok);
+    lo[5 * d + 4] = piece(al1, -sh[kAl1Vl1], ok);
+  }
+  hi[D] = piece(1.0, -sh[kOneBh1], ok);
+  hi[D + 1] = piece(1.0, -sh[kOneBh2], ok);
+  const double A = -cp * nrm;
+  const double Ah = rnd(A, gamma);
+  lo[5 * D] = piece(rnd(A - Ah, gamma - 12), -sh[kAl1One], ok);
+  lo[5 * D + 1] = piece(1.0, -sh[kOneBl1], ok);
+  const float Ahf = (float)Ah;
+  ok = ok && ((double)Ahf == Ah);
+  rA[i] = Ahf;
+#pragma unroll
+  for (int m = 0; m < NH; ++m) {
+    half8 v;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = hi[8 * m + k];
+    rhi[i * NH + m] = v;
+  }
+#pragma unroll
+  for (int m = 0; m < 4 * NL; ++m) {
+    half8 v;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = lo[8 * m + k];
+    rlo[i * 4 * NL + m] = v;
+  }
+  if (!ok) P->gate = 0;
+}
+
+// Column operands chi[j], clo[j] for j < Npad (padding columns are all zero).
+template <int NH, int NL>
+__global__ void __launch_bounds__(kBlock)
+mf_cols_kernel(const float* __restrict__ y, half8* __restrict__ chi, half8* __restrict__ clo, int64_t N,
+               int64_t Npad, int D, MfParams* P) {
+  const int64_t j = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+  if (j >= Npad || !P->gate) return;
+  const double cp = P->cp, inv_h = P->inv_h;
+  const int beta = P->beta, gamma = P->gamma;
+  int sh[kSlots];
+#pragma unroll
+  for (int s = 0; s < kSlots; ++s) sh[s] = P->sh[s];
+  _Float16 hi[8 * NH], lo[32 * NL];
+#pragma unroll
+  for (int k = 0; k < 8 * NH; ++k) hi[k] = (_Float16)0.0f;
+#pragma unroll
+  for (int k = 0; k < 32 * NL; ++k) lo[k] = (_Float16)0.0f;
+  bool ok = true;
+  if (j < N) {
+    double nrm = 0.0;
+#pragma unroll
+    for (int d = 0; d < kMaxLowD; ++d) {
+      if (d >= D) break;
+      const double v = ((double)y[j * D + d] - P->o[d]) * inv_h;
+      nrm = fma(v, v, nrm);
+      const double vh = rnd(v, beta);
+      const double vl1 = rnd(v - vh, beta - 12);
+      const double vl2 = rnd(v - vh - vl1, beta - 24);
+      hi[d] = piece(vh, sh[kAhVh], ok);
+      lo[5 * d + 0] = piece(vl1, sh[kAhVl1], ok);
+      lo[5 * d + 1] = piece(vl2, sh[kAhVl2], ok);
+      lo[5 * d + 2] = piece(vh, sh[kAl1Vh], ok);
+      lo[5 * d + 3] = piece(vh, sh[kAl2Vh], ok);
+      lo[5 * d + 4] = piece(vl1, sh[kAl1Vl1], ok);
+    }
+    const double Bv = -cp * nrm;
+    const double Bh = rnd(Bv, gamma);
+    const double Bh1 = rnd(Bh, gamma + 11);
+    hi[D] = piece(Bh1, sh[kOneBh1], ok);
+    hi[D + 1] = piece(Bh - Bh1, sh[kOneBh2], ok);
+    lo[5 * D] = piece(1.0, sh[kAl1One], ok);
+    lo[5 * D + 1] = piece(rnd(Bv - Bh, gamma - 12), sh[kOneBl1], ok);
+  }
+#pragma unroll
+  for (int m = 0; m < NH; ++m) {
+    half8 v;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = hi[8 * m + k];
+    chi[j * NH + m] = v;
+  }
+#pragma unroll
+  for (int m = 0; m < 4 * NL; ++m) {
+    half8 v;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = lo[8 * m + k];
+    clo[j * 4 * NL + m] = v;
+  }
+  if (!ok) P->gate = 0;
+}
+
+// out[i][c] = sum_j 2^{e_ij} b[j][c] over the columns [j0, j1) of this split (times rscale[i]
+// with one split), else partial[split][i][c]. A wave holds RT tiles of 16 rows; lane (g, l)
+// (g = lane / 16, l = lane % 16) feeds row l and features 8g..8g+7 of each tile to the MFMA and
+// gets back e for rows 4g..4g+3 against column l of the current 16-column tile. Lanes keep
+// per-column partial sums; the 16 lanes of a row group add theirs at the end.
+template <int C, int RT, int NH, int NL>
+__global__ void __launch_bounds__(kBlock)
+gauss_sum_mf_kernel(const half8* __restrict__ rhi, const half8* __restrict__ rlo, const float* __restrict__ rA,
+                    const half8* __restrict__ chi, const half8* __restrict__ clo, const float* __restrict__ b,
+                    float* __restrict__ out, const float* __restrict__ rscale, const MfParams* __restrict__ P,
+                    int64_t M, int64_t N, int64_t cps) {
+  if (!P->gate) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
+  const int64_t split = blockIdx.y;
+  const int64_t j0 = split * cps;
+  const int64_t j1 = (j0 + cps < N) ? j0 + cps : N;
+  const int64_t base = ((int64_t)blockIdx.x * (kBlock / 64) + wave) * 16 * RT;
+  const half8 zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
+
+  half8 ahi[RT], alo[RT][NL];
+  f32x4 cinit[RT];
+  float acc[RT][4][C], part[RT][4][C];
+#pragma unroll
+  for (int r = 0; r < RT; ++r) {
+    int64_t i = base + r * 16 + l16;
+    i = i < M ? i : M - 1;
+    ahi[r] = g < NH ? rhi[i * NH + g] : zero8;
+#pragma unroll
+    for (int m = 0; m < NL; ++m) alo[r][m] = rlo[i * 4 * NL + m * 4 + g];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      int64_t ii = base + r * 16 + 4 * g + q;
+      ii = ii < M ? ii : M - 1;
+      cinit[r][q] = rA[ii];
+#pragma unroll
+      for (int c = 0; c < C; ++c) acc[r][q][c] = 0.0f;
+    }
+  }
+  const int gh = g < NH ? g : 0;
+  for (int64_t jc = j0; jc < j1; jc += kChunk) {
+    const int64_t je = (jc + kChunk < j1) ? jc + kChunk : j1;
+#pragma unroll
+    for (int r = 0; r < RT; ++r)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int c = 0; c < C; ++c) part[r][q][c] = 0.0f;
+    for (int64_t jt = jc; jt < je; jt += 16) {
+      const int64_t j = jt + l16;
+      const half8 bhi = chi[j * NH + gh];
+      half8 blo[NL];
+#pragma unroll
+      for (int m = 0; m < NL; ++m) blo[m] = clo[j * 4 * NL + m * 4 + g];
+      float bj[C];
+#pragma unroll
+      for (int c = 0; c < C; ++c) bj[c] = j < N ? b[j * C + c] : 0.0f;
+#pragma unroll
+      for (int r = 0; r < RT; ++r) {
+        f32x4 e = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[r], bhi, cinit[r], 0, 0, 0);
+#pragma unroll
+        for (int m = 0; m < NL; ++m) e = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[r][m], blo[m], e, 0, 0, 0);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float k = exp2_hw(e[q]);
+#pragma unroll
+          for (int c = 0; c < C; ++c) part[r][q][c] = fmaf(k, bj[c], part[r][q][c]);
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < RT; ++r)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int c = 0; c < C; ++c) acc[r][q][c] += part[r][q][c];
+  }
+  // add the 16 per-column partials of each row (lanes 16g .. 16g + 15)
+#pragma unroll
+  for (int r = 0; r < RT; ++r)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        float v = acc[r][q][c];
+        v += __shfl_xor(v, 1);
+        v += __shfl_xor(v, 2);
+        v += __shfl_xor(v, 4);
+        v += __shfl_xor(v, 8);
+        acc[r][q][c] = v;
+      }
+  float* dst = out + split * M * C;
+  const bool scaled = rscale && gridDim.y == 1;
+#pragma unroll
+  for (int r = 0; r < RT; ++r)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t i = base + r * 16 + 4 * g + q;
+      if (l16 == q && i < M) {
+        const float sc = scaled ? rscale[i] : 1.0f;
+#pragma unroll
+        for (int c = 0; c < C; ++c) dst[i * C + c] = sc * acc[r][q][c];
+      }
+    }
+}
+
+// Byte offsets of the operand region: parameters, row operands, column operands.
+struct MfLayout {
+  int NH, NL;
+  int64_t Npad;
+  size_t rhi, rlo, rA, chi, clo, total;
+};
+
+MfLayout mf_layout(int64_t M, int64_t N, int D) {
+  MfLayout L;
+  L.NH = (D + 2 <= 8) ? 1 : 2;
+  L.NL = (5 * D + 2 <= 32) ? 1 : 2;
+  L.Npad = ceil_div(N, 16) * 16;
+  size_t off = align_up(sizeof(MfParams));
+  L.rhi = off;
+  off += align_up((size_t)M * 16 * L.NH);
+  L.rlo = off;
+  off += align_up((size_t)M * 64 * L.NL);
+  L.rA = off;
+  off += align_up((size_t)M * sizeof(float));
+  L.chi = off;
+  off += align_up((size_t)L.Npad * 16 * L.NH);
+  L.clo = off;
+  off += align_up((size_t)L.Npad * 64 * L.NL);
+  L.total = off;
+  return L;
+}
+
+template <int C, int RT, int NH, int NL>
+hipError_t sweep(char* r, const MfLayout& L, const float* b, float* dst, const float* rscale, int64_t M, int64_t N,
+                 const Plan& p, hipStream_t s) {
+  dim3 grid((unsigned)p.mf_row_blocks, (unsigned)p.splits);
+  gauss_sum_mf_kernel<C, RT, NH, NL><<<grid, kBlock, 0, s>>>(
+      reinterpret_cast<const half8*>(r + L.rhi), reinterpret_cast<const half8*>(r + L.rlo),
+      reinterpret_cast<const float*>(r + L.rA), reinterpret_cast<const half8*>(r + L.chi),
+      reinterpret_cast<const half8*>(r + L.clo), b, dst, rscale, reinterpret_cast<const MfParams*>(r), M, N,
+      p.cols_per_split);
+  return hipGetLastError();
+}
+
+// Row tiles per wave: 4 for C <= 2, 2 for C <= 4, else 1 (register budgets); fewer for few rows.
+constexpr int max_rt(int C) { return C <= 2 ? 4 : (C <= 4 ? 2 : 1); }
+
+template <int C, int NH, int NL>
+hipError_t sweep_rt(char* r, const MfLayout& L, const float* b, float* dst, const float* rscale, int64_t M,
+                    int64_t N, const Plan& p, hipStream_t s) {
+  if constexpr (max_rt(C) >= 4)
+    if (p.mf_rt == 4) return sweep<C, 4, NH, NL>(r, L, b, dst, rscale, M, N, p, s);
+  if constexpr (max_rt(C) >= 2)
+    if (p.mf_rt == 2) return sweep<C, 2, NH, NL>(r, L, b, dst, rscale, M, N, p, s);
+  if (p.mf_rt == 1) return sweep<C, 1, NH, NL>(r, L, b, dst, rscale, M, N, p, s);
+  return hipErrorInvalidValue;
+}
+
+template <int C, int RT, int NH, int NL>
+int occupancy_of() {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gauss_sum_mf_kernel<C, RT, NH, NL>, kBlock, 0) != hipSuccess ||
+      n < 1)
+    n = 4;
+  return n;
+}
+
+template <int C, int NH, int NL>
+int occupancy_rt(int rt) {
+  if constexpr (max_rt(C) >= 4)
+    if (rt == 4) return occupancy_of<C, 4, NH, NL>();
+  if constexpr (max_rt(C) >= 2)
+    if (rt == 2) return occupancy_of<C, 2, NH, NL>();
+  return occupancy_of<C, 1, NH, NL>();
+}
+
+template <int C>
+int occupancy_c(bool wide, int rt) {
+  return wide ? occupancy_rt<C, 2, 2>(rt) : occupancy_rt<C, 1, 1>(rt);
+}
+
+template <int C>
+hipError_t sweep_c(char* r, const MfLayout& L, const float* b, float* dst, const float* rscale, int64_t M, int64_t N,
+                   const Plan& p, hipStream_t s) {
+  if (L.NH == 1 && L.NL == 1) return sweep_rt<C, 1, 1>(r, L, b, dst, rscale, M, N, p, s);
+  return sweep_rt<C, 2, 2>(r, L, b, dst, rscale, M, N, p, s);
+}
+
+}  // namespace
+}  // namespace lowd
+
+size_t mf_region_bytes(int64_t M, int64_t N, int D) { return lowd::mf_layout(M, N, D).total; }
+
+const int* mf_gate(const void* region) { return &static_cast<const lowd::MfParams*>(region)->gate; }
+
+int mf_rows_per_lane(int C) { return lowd::max_rt(C); }
+
+int mf_occupancy(int D, int C, int rt) {
+  // resident workgroups per CU of the sweep instance, from its register use (cached per
+  // instance; 4 when the runtime cannot say)
+  static std::atomic<int> cache[2][kMaxLowC + 1][5];
+  const int wide = lowd::mf_layout(1, 1, D).NH == 2 ? 1 : 0;
+  int dev = 0;
+  if (C < 1 || C > kMaxLowC || (rt != 1 && rt != 2 && rt != 4) || hipGetDevice(&dev) != hipSuccess) return 4;
+  std::atomic<int>& slot = cache[wide][C][rt];
+  int n = slot.load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  auto query = [&]() -> int {
+#define KEOPS_MF_OCC(Cv) lowd::occupancy_c<Cv>(wide != 0, rt)
+    switch (C) {
+      case 1: return KEOPS_MF_OCC(1);
+      case 2: return KEOPS_MF_OCC(2);
+      case 3: return KEOPS_MF_OCC(3);
+      case 4: return KEOPS_MF_OCC(4);
+      case 5: return KEOPS_MF_OCC(5);
+      case 6: return KEOPS_MF_OCC(6);
+      case 7: return KEOPS_MF_OCC(7);
+      case 8: return KEOPS_MF_OCC(8);
+    }
+#undef KEOPS_MF_OCC
+    return 4;
+  };
+  n = query();
+  slot.store(n, std::memory_order_relaxed);
+  return n;
+}
+
+hipError_t launch_mf_prepare(const float* x, const float* y, void* region, int64_t M, int64_t N, int D, double c2,
+                             hipStream_t s) {
+  using namespace lowd;
+  char* r = static_cast<char*>(region);
+  const MfLayout L = mf_layout(M, N, D);
+  MfParams* P = reinterpret_cast<MfParams*>(r);
+  mf_init_kernel<<<1, 64, 0, s>>>(P);
+  const int64_t n = M > N ? M : N;
+  int64_t blocks = ceil_div(n, kBlock);
+  if (blocks > 1024) blocks = 1024;
+  mf_bounds_kernel<<<(unsigned)blocks, kBlock, 0, s>>>(x, y, M, N, D, P);
+  mf_params_kernel<<<1, 64, 0, s>>>(P, D, c2);
+  half8* rhi = reinterpret_cast<half8*>(r + L.rhi);
+  half8* rlo = reinterpret_cast<half8*>(r + L.rlo);
+  float* rA = reinterpret_cast<float*>(r + L.rA);
+  half8* chi = reinterpret_cast<half8*>(r + L.chi);
+  half8* clo = reinterpret_cast<half8*>(r + L.clo);
+  const unsigned rb = (unsigned)ceil_div(M, kBlock), cb = (unsigned)ceil_div(L.Npad, kBlock);
+  if (L.NH == 1 && L.NL == 1) {
+    mf_rows_kernel<1, 1><<<rb, kBlock, 0, s>>>(x, rhi, rlo, rA, M, D, P);
+    mf_cols_kernel<1, 1><<<cb, kBlock, 0, s>>>(y, chi, clo, N, L.Npad, D, P);
+  } else {
+    mf_rows_kernel<2, 2><<<rb, kBlock, 0, s>>>(x, rhi, rlo, rA, M, D, P);
+    mf_cols_kernel<2, 2><<<cb, kBlock, 0, s>>>(y, chi, clo, N, L.Npad, D, P);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_mf_sum(const float* b, const float* rscale, float* dst, void* region, int64_t M, int64_t N, int D,
+                         int C, const Plan& p, hipStream_t s) {
+  using namespace lowd;
+  char* r = static_cast<char*>(region);
+  const MfLayout L = mf_layout(M, N, D);
+#define KEOPS_MF_C(Cv) sweep_c<Cv>(r, L, b, dst, rscale, M, N, p, s)
+  KEOPS_SWITCH_C(C, KEOPS_MF_C)
+#undef KEOPS_MF_C
+}
+
+}  // namespace keops

@@ -22,7 +22,8 @@ __global__ void __launch_bounds__(kBlock)
 gauss_sum_kernel(const float* __restrict__ x, const float* __restrict__ y,
                  const double* __restrict__ cols, const float* __restrict__ b,
                  float* __restrict__ out, const float* __restrict__ rscale, int64_t M, int64_t N, int64_t cps,
-                 double c2) {
+                 double c2, const int* __restrict__ skip) {
+  if (skip && *skip) return;  // the matrix-core sweep took these inputs
   constexpr int P = (D + 2) & ~1;
   const int64_t split = blockIdx.y;
   const int64_t j0 = split * cps;
@@ -94,20 +95,23 @@ gauss_sum_kernel(const float* __restrict__ x, const float* __restrict__ y,
 
 template <int D, int C>
 hipError_t gauss_sum_dc(const float* x, const float* y, const double* cols, const float* b, float* dst,
-                        const float* rscale, int64_t M, int64_t N, double c2, const Plan& p, hipStream_t s) {
+                        const float* rscale, int64_t M, int64_t N, double c2, const int* skip, const Plan& p,
+                        hipStream_t s) {
   dim3 grid((unsigned)p.row_blocks, (unsigned)p.splits);
   if (p.R == kRowsSumSmall)
     gauss_sum_kernel<D, C, kRowsSumSmall><<<grid, kBlock, 0, s>>>(x, y, cols, b, dst, rscale, M, N, p.cols_per_split,
-                                                                   c2);
+                                                                   c2, skip);
   else
-    gauss_sum_kernel<D, C, kRowsSum><<<grid, kBlock, 0, s>>>(x, y, cols, b, dst, rscale, M, N, p.cols_per_split, c2);
+    gauss_sum_kernel<D, C, kRowsSum><<<grid, kBlock, 0, s>>>(x, y, cols, b, dst, rscale, M, N, p.cols_per_split, c2,
+                                                             skip);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t gauss_sum_d(int C, const float* x, const float* y, const double* cols, const float* b, float* dst,
-                       const float* rscale, int64_t M, int64_t N, double c2, const Plan& p, hipStream_t s) {
-#define KEOPS_GS_C(Cv) gauss_sum_dc<D, Cv>(x, y, cols, b, dst, rscale, M, N, c2, p, s)
+                       const float* rscale, int64_t M, int64_t N, double c2, const int* skip, const Plan& p,
+                       hipStream_t s) {
+#define KEOPS_GS_C(Cv) gauss_sum_dc<D, Cv>(x, y, cols, b, dst, rscale, M, N, c2, skip, p, s)
   KEOPS_SWITCH_C(C, KEOPS_GS_C)
 #undef KEOPS_GS_C
 }
@@ -115,16 +119,25 @@ hipError_t gauss_sum_d(int C, const float* x, const float* y, const double* cols
 }  // namespace
 }  // namespace lowd
 
-hipError_t launch_gauss_sum_lowd(const float* x, const float* y, const double* cols, const float* b,
-                                 const float* rscale, float* out, float* partial, int64_t M, int64_t N, int D, int C,
-                                 double c2, const Plan& p, hipStream_t s) {
+hipError_t launch_gauss_sum_lowd(const float* x, const float* y, double* cols, const float* b, const float* rscale,
+                                 float* out, float* partial, void* mf, int64_t M, int64_t N, int D, int C, double c2,
+                                 const Plan& p, hipStream_t s) {
   float* dst = p.splits > 1 ? partial : out;
+  // Operands for the matrix-core sweep and the device-side choice of sweep; the float64 column
+  // table and sweep return at once when the matrix-core sweep runs.
+  hipError_t e = launch_mf_prepare(x, y, mf, M, N, D, c2, s);
+  if (e != hipSuccess) return e;
+  const int* gate = mf_gate(mf);
+  e = launch_prep_cols(y, cols, N, D, c2, true, s, gate);
+  if (e != hipSuccess) return e;
   auto run = [&]() -> hipError_t {
-#define KEOPS_GS(Dv) lowd::gauss_sum_d<Dv>(C, x, y, cols, b, dst, rscale, M, N, c2, p, s)
+#define KEOPS_GS(Dv) lowd::gauss_sum_d<Dv>(C, x, y, cols, b, dst, rscale, M, N, c2, gate, p, s)
     KEOPS_SWITCH_D(D, KEOPS_GS)
 #undef KEOPS_GS
   };
-  const hipError_t e = run();
+  e = run();
+  if (e != hipSuccess) return e;
+  e = launch_mf_sum(b, rscale, dst, mf, M, N, D, C, p, s);
   if (e != hipSuccess || p.splits == 1) return e;
   return lowd::launch_combine_sum(partial, out, M * C, p.splits, rscale, C, s);
 }
