@@ -110,7 +110,7 @@ LowdLayout lowd_layout(int op, int64_t M, int64_t N, int D, int C, int K) {
   }
   L.lse_off = L.part_off + L.part_bytes;
   L.mf_off = L.lse_off + lse_bytes;
-  L.total = L.mf_off + (op == KEOPS_OP_GAUSS_SUM ? keops::mf_region_bytes(M, N, D) : 0);
+  L.total = L.mf_off + (op == KEOPS_OP_GAUSS_SUM ? keops::mf_region_bytes(M, N, D, C) : 0);
   if (M == 0 || N == 0) L.total = 0;
   return L;
 }

@@ -15,7 +15,7 @@ constexpr size_t kAlign = 256;       // alignment of workspace sections
 
 // Column record stride (doubles) of the prepared low-D column table: D centred coordinates
 // followed by one per-column exponent term, padded to an even count (16-byte records).
-inline int col_stride(int D) { return (D + 2) & ~1; }
+__host__ __device__ inline int col_stride(int D) { return (D + 2) & ~1; }
 
 inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
@@ -40,27 +40,26 @@ size_t partial_bytes_per_row(int op, int D, int C, int K);
 
 // ---- launchers (return hipError_t of the launch) ----------------------------------------
 // cols[j] = (y_j - o, -c2 |y_j - o|^2) in float64, o = y_0 when `centre`, else o = 0.
-// Skipped on the device when `skip` is given and *skip is nonzero.
 hipError_t launch_prep_cols(const float* y, double* cols, int64_t N, int D, double c2,
-                            bool centre, hipStream_t s, const int* skip = nullptr);
-// out[i][c] = rscale[i] * sum_j 2^{-c2 |x_i - y_j|^2} b[j][c] (rscale may be null). Runs the
-// matrix-core sweep when the operand preparation in `mf` (mf_region_bytes) admits the inputs,
-// else builds the float64 column table in `cols` and runs the float64 sweep; the choice is made
-// on the device.
+                            bool centre, hipStream_t s);
+// out[i][c] = rscale[i] * sum_j 2^{-c2 |x_i - y_j|^2} b[j][c] (rscale may be null). Prepares the
+// matrix-core operands in `mf` (mf_region_bytes) and the float64 column table in `cols`, then
+// launches both sweeps; the device-side decision lets exactly one of them do the work.
 hipError_t launch_gauss_sum_lowd(const float* x, const float* y, double* cols, const float* b,
                                  const float* rscale, float* out, float* partial, void* mf,
                                  int64_t M, int64_t N, int D, int C, double c2, const Plan& p,
                                  hipStream_t s);
-// Matrix-core Gauss sum pieces (lowd_mfma.hip): operand region size, the device-side decision
-// (nonzero: matrix-core sweep), row tiles per wave for C channels, preparation and sweep.
-size_t mf_region_bytes(int64_t M, int64_t N, int D);
-const int* mf_gate(const void* region);
+// Matrix-core Gauss sum pieces (lowd_mfma.hip): operand region size; the decision, two ints
+// (gate, bad): the matrix-core sweep runs when gate != 0 and bad == 0; row tiles per wave for C
+// channels; preparation (also writes the float64 column table) and sweep.
+size_t mf_region_bytes(int64_t M, int64_t N, int D, int C);
+const int* mf_decision(const void* region);
 int mf_rows_per_lane(int C);
 int mf_occupancy(int D, int C, int rt);  // resident workgroups per CU of the matrix-core sweep
-hipError_t launch_mf_prepare(const float* x, const float* y, void* region, int64_t M, int64_t N, int D,
-                             double c2, hipStream_t s);
-hipError_t launch_mf_sum(const float* b, const float* rscale, float* dst, void* region, int64_t M,
-                         int64_t N, int D, int C, const Plan& p, hipStream_t s);
+hipError_t launch_mf_prepare(const float* x, const float* y, const float* b, double* cols, void* region,
+                             int64_t M, int64_t N, int D, int C, double c2, hipStream_t s);
+hipError_t launch_mf_sum(const float* rscale, float* dst, void* region, int64_t M, int64_t N, int D,
+                         int C, const Plan& p, hipStream_t s);
 hipError_t launch_lse_lowd(const float* x, const float* y, const double* cols, float* out,
                            double* partial, int64_t M, int64_t N, int D, double c2,
                            const Plan& p, hipStream_t s);

@@ -11,9 +11,9 @@ namespace {
 // cols[j] = (y_j - o, B_j) in float64, o = y_0 when `centre`, else o = 0 (then B_j unused).
 __global__ void __launch_bounds__(kBlock)
 prep_cols_kernel(const float* __restrict__ y, double* __restrict__ cols, int64_t N, int D, int P,
-                 double c2, int centre, const int* __restrict__ skip) {
+                 double c2, int centre) {
   const int64_t j = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-  if (j >= N || (skip && *skip)) return;
+  if (j >= N) return;
   double s = 0.0;
   for (int d = 0; d < D; ++d) {
     const double o = centre ? (double)y[d] : 0.0;
@@ -196,10 +196,10 @@ Plan plan_lowd(int op, int64_t M, int64_t N, int D, int C, int K, int num_cus) {
 
 // ------------------------------------------------------------------------- launchers
 hipError_t launch_prep_cols(const float* y, double* cols, int64_t N, int D, double c2, bool centre,
-                            hipStream_t s, const int* skip) {
+                            hipStream_t s) {
   if (N <= 0) return hipSuccess;
   lowd::prep_cols_kernel<<<(unsigned)ceil_div(N, kBlock), kBlock, 0, s>>>(y, cols, N, D, col_stride(D), c2,
-                                                                           centre ? 1 : 0, skip);
+                                                                           centre ? 1 : 0);
   return hipGetLastError();
 }
 

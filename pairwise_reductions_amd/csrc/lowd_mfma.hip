@@ -41,16 +41,19 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kMinK = 4;           // exponent scales below 2^4 are treated as 2^4
 constexpr double kMaxLow = 32.0;   // largest admissible bound on the low part
+constexpr int kBoundBlocks = 256;  // most workgroups of the bounds pass
+constexpr int kChunkTiles = kChunk / 16;
 
 // Product kinds (row piece x column piece); the shift table is indexed by these.
 enum Slot { kAhVh = 0, kOneBh1, kOneBh2, kAhVl1, kAhVl2, kAl1Vh, kAl2Vh, kAl1Vl1, kAl1One, kOneBl1, kSlots };
 
 // Decisions and constants shared by the preparation and the sweeps, written on the device.
+// The matrix-core sweep runs when gate != 0 and bad == 0, the float64 sweep otherwise.
 struct MfParams {
-  int gate;           // nonzero: the matrix-core sweep runs; zero: the float64 sweep runs
+  int gate;           // the scales admit the matrix-core path
+  int bad;            // some piece did not convert exactly
   int alpha, beta, gamma;
   int sh[kSlots];
-  unsigned int mm[2 * kMaxLowD];  // order-preserving encodings of the per-dimension min, max
   double o[kMaxLowD];
   double inv_h;
   double cp;          // c2 h^2
@@ -66,18 +69,13 @@ __device__ __forceinline__ float float_of(unsigned int u) {
 // v rounded to the nearest multiple of 2^g
 __device__ __forceinline__ double rnd(double v, int g) { return ldexp(rint(ldexp(v, -g)), g); }
 
-__global__ void mf_init_kernel(MfParams* P) {
-  const int t = threadIdx.x;
-  if (t < kMaxLowD) {
-    P->mm[t] = 0xffffffffu;
-    P->mm[kMaxLowD + t] = 0u;
-  }
-}
-
-// Per-dimension min and max over the rows of x and of y.
+// Per-dimension min and max over the rows of x and of y: one (min, max) record per workgroup in
+// parts[blockIdx] (order-preserving unsigned encodings, dimension d at d and kMaxLowD + d).
+// Workgroup 0 also clears the bad flag.
 __global__ void __launch_bounds__(kBlock)
 mf_bounds_kernel(const float* __restrict__ x, const float* __restrict__ y, int64_t M, int64_t N, int D,
-                 MfParams* P) {
+                 unsigned int* __restrict__ parts, MfParams* __restrict__ P) {
+  __shared__ unsigned int red[kBlock / 64][2 * kMaxLowD];
   unsigned int lo[kMaxLowD], hi[kMaxLowD];
 #pragma unroll
   for (int d = 0; d < kMaxLowD; ++d) {
@@ -101,9 +99,9 @@ mf_bounds_kernel(const float* __restrict__ x, const float* __restrict__ y, int64
       }
     }
   }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int d = 0; d < kMaxLowD; ++d) {
-    if (d >= D) break;
     unsigned int a = lo[d], b = hi[d];
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) {
@@ -111,36 +109,46 @@ mf_bounds_kernel(const float* __restrict__ x, const float* __restrict__ y, int64
       a = a2 < a ? a2 : a;
       b = b2 > b ? b2 : b;
     }
-    if ((threadIdx.x & 63) == 0) {
-      atomicMin(&P->mm[d], a);
-      atomicMax(&P->mm[kMaxLowD + d], b);
+    if (lane == 0) {
+      red[wave][d] = a;
+      red[wave][kMaxLowD + d] = b;
     }
   }
+  __syncthreads();
+  if (threadIdx.x < 2 * kMaxLowD) {
+    const int t = threadIdx.x;
+    unsigned int v = red[0][t];
+    for (int w = 1; w < kBlock / 64; ++w) {
+      const unsigned int u = red[w][t];
+      v = (t < kMaxLowD) ? (u < v ? u : v) : (u > v ? u : v);
+    }
+    parts[blockIdx.x * 2 * kMaxLowD + t] = v;
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) P->bad = 0;
 }
 
-// Centre, scale, grids and shifts; clears the gate when the low part could exceed kMaxLow or a
-// shift has no admissible value. One thread.
-__global__ void mf_params_kernel(MfParams* P, int D, double c2) {
-  if (threadIdx.x != 0) return;
+// Centre, scale, grids and shifts from the bounds; gate = 0 when the low part could exceed
+// kMaxLow or a shift has no admissible value. One thread.
+__device__ void mf_params(const unsigned int* mm, int D, double c2, MfParams& P) {
   double h = 0.0;
   bool finite = true;
   for (int d = 0; d < D; ++d) {
-    const double lo = (double)float_of(P->mm[d]), hi = (double)float_of(P->mm[kMaxLowD + d]);
+    const double lo = (double)float_of(mm[d]), hi = (double)float_of(mm[kMaxLowD + d]);
     finite = finite && isfinite(lo) && isfinite(hi);
     const double o = (double)(float)(0.5 * (lo + hi));
-    P->o[d] = o;
+    P.o[d] = o;
     h = fmax(h, fmax(hi - o, o - lo));
   }
   if (!(h > 0.0)) h = 1.0;  // all points equal: any scale will do
   h *= 1.0 + 0x1p-40;       // keeps |u|, |v| <= 1 after rounding
   const double cp = c2 * h * h;
-  P->inv_h = 1.0 / h;
-  P->cp = cp;
+  P.inv_h = 1.0 / h;
+  P.cp = cp;
   int gate = finite && isfinite(cp) && cp > 0.0;
   int k = kMinK;
   if (gate) {
     int ex = 0;
-    const double m = frexp(2.0 * cp, &ex);  // 2cp = m 2^ex, m in [0.5, 1)
+    const double m = frexp(2.0 * cp, &ex);    // 2cp = m 2^ex, m in [0.5, 1)
     const int kc = (m == 0.5) ? ex - 1 : ex;  // ceil(log2(2cp))
     k = kc > kMinK ? kc : kMinK;
   }
@@ -166,12 +174,12 @@ __global__ void mf_params_kernel(MfParams* P, int D, double c2) {
     const int hi = min(rowQ[s] + 24, 15 - colM[s]);
     const int want = (int)floor(0.25 * (double)(rowM[s] + rowQ[s] - colM[s] - colQ[s]) + 0.5);
     if (lo > hi) gate = 0;
-    P->sh[s] = want < lo ? lo : (want > hi ? hi : want);
+    P.sh[s] = want < lo ? lo : (want > hi ? hi : want);
   }
-  P->alpha = alpha;
-  P->beta = beta;
-  P->gamma = gamma;
-  P->gate = gate;
+  P.alpha = alpha;
+  P.beta = beta;
+  P.gamma = gamma;
+  P.gate = gate;
 }
 
 // v 2^s as fp16; clears ok when that is not exact.
@@ -182,139 +190,170 @@ __device__ __forceinline__ _Float16 piece(double v, int s, bool& ok) {
   return r;
 }
 
-// Row operands: rhi[i] (8 NH fp16), rlo[i] (32 NL fp16), rA[i] = Ah_i.
-template <int NH, int NL>
-__global__ void __launch_bounds__(kBlock)
-mf_rows_kernel(const float* __restrict__ x, half8* __restrict__ rhi, half8* __restrict__ rlo, float* __restrict__ rA,
-               int64_t M, int D, MfParams* P) {
-  const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-  if (i >= M || !P->gate) return;
-  const double cp = P->cp, inv_h = P->inv_h;
-  const int alpha = P->alpha, gamma = P->gamma;
-  int sh[kSlots];
+template <int W>
+__device__ __forceinline__ void store_pieces(half8* __restrict__ dst, const _Float16 (&v)[8 * W]) {
 #pragma unroll
-  for (int s = 0; s < kSlots; ++s) sh[s] = P->sh[s];
-  _Float16 hi[8 * NH], lo[32 * NL];
+  for (int m = 0; m < W; ++m) {
+    half8 h;
 #pragma unroll
-  for (int k = 0; k < 8 * NH; ++k) hi[k] = (_Float16)0.0f;
-#pragma unroll
-  for (int k = 0; k < 32 * NL; ++k) lo[k] = (_Float16)0.0f;
-  bool ok = true;
-  double nrm = 0.0;
-#pragma unroll
-  for (int d = 0; d < kMaxLowD; ++d) {
-    if (d >= D) break;
-    const double u = ((double)x[i * D + d] - P->o[d]) * inv_h;
-    nrm = fma(u, u, nrm);
-    const double a = 2.0 * cp * u;
-    const double ah = rnd(a, alpha);
-    const double al1 = rnd(a - ah, alpha - 12);
-    const double al2 = rnd(a - ah - al1, alpha - 24);
-    hi[d] = piece(ah, -sh[kAhVh], ok);
-    lo[5 * d + 0] = piece(ah, -sh[kAhVl1], ok);
-    lo[5 * d + 1] = piece(ah, -sh[kAhVl2], ok);
-    lo[5 * d + 2] = piece(al1, -sh[kAl1Vh], ok);
-    lo[5 * d + 3] = piece(al2, -sh[kAl2Vh], ok);
-    lo[5 * d + 4] = piece(al1, -sh[kAl1Vl1], ok);
+    for (int k = 0; k < 8; ++k) h[k] = v[8 * m + k];
+    dst[m] = h;
   }
-  hi[D] = piece(1.0, -sh[kOneBh1], ok);
-  hi[D + 1] = piece(1.0, -sh[kOneBh2], ok);
-  const double A = -cp * nrm;
-  const double Ah = rnd(A, gamma);
-  lo[5 * D] = piece(rnd(A - Ah, gamma - 12), -sh[kAl1One], ok);
-  lo[5 * D + 1] = piece(1.0, -sh[kOneBl1], ok);
-  const float Ahf = (float)Ah;
-  ok = ok && ((double)Ahf == Ah);
-  rA[i] = Ahf;
-#pragma unroll
-  for (int m = 0; m < NH; ++m) {
-    half8 v;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) v[k] = hi[8 * m + k];
-    rhi[i * NH + m] = v;
-  }
-#pragma unroll
-  for (int m = 0; m < 4 * NL; ++m) {
-    half8 v;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) v[k] = lo[8 * m + k];
-    rlo[i * 4 * NL + m] = v;
-  }
-  if (!ok) P->gate = 0;
 }
 
-// Column operands chi[j], clo[j] for j < Npad (padding columns are all zero).
+// Operand preparation, one thread per row (workgroups [0, rb)) or per column (the rest):
+//   rows     rhi[i] (8 NH fp16), rlo[i] (32 NL fp16), rA[i] = Ah_i
+//   columns  chi[j], clo[j] and bpad[j][c] = b[j][c] for j < Npad (zero past N), and the float64
+//            column table cols[j] = (y_j - y_0, -c2 |y_j - y_0|^2) of the float64 sweep
+// Each workgroup reduces the bounds records and derives the parameters itself (identically);
+// workgroup 0 publishes them. A piece that does not convert exactly sets P->bad.
 template <int NH, int NL>
 __global__ void __launch_bounds__(kBlock)
-mf_cols_kernel(const float* __restrict__ y, half8* __restrict__ chi, half8* __restrict__ clo, int64_t N,
-               int64_t Npad, int D, MfParams* P) {
-  const int64_t j = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-  if (j >= Npad || !P->gate) return;
-  const double cp = P->cp, inv_h = P->inv_h;
-  const int beta = P->beta, gamma = P->gamma;
-  int sh[kSlots];
+mf_prep_kernel(const float* __restrict__ x, const float* __restrict__ y, const float* __restrict__ b, int C,
+               double* __restrict__ cols, half8* __restrict__ rhi, half8* __restrict__ rlo, float* __restrict__ rA,
+               half8* __restrict__ chi, half8* __restrict__ clo, float* __restrict__ bpad,
+               const unsigned int* __restrict__ parts, int nparts, int64_t M, int64_t N, int64_t Npad, int D,
+               double c2, int64_t rb, MfParams* __restrict__ P) {
+  __shared__ unsigned int red[kBlock / 64][2 * kMaxLowD];
+  __shared__ MfParams sp;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
-  for (int s = 0; s < kSlots; ++s) sh[s] = P->sh[s];
-  _Float16 hi[8 * NH], lo[32 * NL];
+  for (int t = 0; t < 2 * kMaxLowD; ++t) {
+    unsigned int v = t < kMaxLowD ? 0xffffffffu : 0u;
+    if ((int)threadIdx.x < nparts) v = parts[threadIdx.x * 2 * kMaxLowD + t];
 #pragma unroll
-  for (int k = 0; k < 8 * NH; ++k) hi[k] = (_Float16)0.0f;
-#pragma unroll
-  for (int k = 0; k < 32 * NL; ++k) lo[k] = (_Float16)0.0f;
+    for (int m = 32; m >= 1; m >>= 1) {
+      const unsigned int u = __shfl_xor(v, m);
+      v = t < kMaxLowD ? (u < v ? u : v) : (u > v ? u : v);
+    }
+    if (lane == 0) red[wave][t] = v;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned int mm[2 * kMaxLowD];
+    for (int t = 0; t < 2 * kMaxLowD; ++t) {
+      unsigned int v = red[0][t];
+      for (int w = 1; w < kBlock / 64; ++w) {
+        const unsigned int u = red[w][t];
+        v = t < kMaxLowD ? (u < v ? u : v) : (u > v ? u : v);
+      }
+      mm[t] = v;
+    }
+    mf_params(mm, D, c2, sp);
+    if (blockIdx.x == 0) {
+      P->gate = sp.gate;
+      P->alpha = sp.alpha;
+      P->beta = sp.beta;
+      P->gamma = sp.gamma;
+      for (int s = 0; s < kSlots; ++s) P->sh[s] = sp.sh[s];
+    }
+  }
+  __syncthreads();
+  const bool gate = sp.gate != 0;
+  const double cp = sp.cp, inv_h = sp.inv_h;
   bool ok = true;
-  if (j < N) {
+  if ((int64_t)blockIdx.x < rb) {
+    const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (i >= M || !gate) return;
+    _Float16 hi[8 * NH], lo[32 * NL];
+#pragma unroll
+    for (int k = 0; k < 8 * NH; ++k) hi[k] = (_Float16)0.0f;
+#pragma unroll
+    for (int k = 0; k < 32 * NL; ++k) lo[k] = (_Float16)0.0f;
     double nrm = 0.0;
 #pragma unroll
     for (int d = 0; d < kMaxLowD; ++d) {
       if (d >= D) break;
-      const double v = ((double)y[j * D + d] - P->o[d]) * inv_h;
-      nrm = fma(v, v, nrm);
-      const double vh = rnd(v, beta);
-      const double vl1 = rnd(v - vh, beta - 12);
-      const double vl2 = rnd(v - vh - vl1, beta - 24);
-      hi[d] = piece(vh, sh[kAhVh], ok);
-      lo[5 * d + 0] = piece(vl1, sh[kAhVl1], ok);
-      lo[5 * d + 1] = piece(vl2, sh[kAhVl2], ok);
-      lo[5 * d + 2] = piece(vh, sh[kAl1Vh], ok);
-      lo[5 * d + 3] = piece(vh, sh[kAl2Vh], ok);
-      lo[5 * d + 4] = piece(vl1, sh[kAl1Vl1], ok);
+      const double u = ((double)x[i * D + d] - sp.o[d]) * inv_h;
+      nrm = fma(u, u, nrm);
+      const double a = 2.0 * cp * u;
+      const double ah = rnd(a, sp.alpha);
+      const double al1 = rnd(a - ah, sp.alpha - 12);
+      const double al2 = rnd(a - ah - al1, sp.alpha - 24);
+      hi[d] = piece(ah, -sp.sh[kAhVh], ok);
+      lo[5 * d + 0] = piece(ah, -sp.sh[kAhVl1], ok);
+      lo[5 * d + 1] = piece(ah, -sp.sh[kAhVl2], ok);
+      lo[5 * d + 2] = piece(al1, -sp.sh[kAl1Vh], ok);
+      lo[5 * d + 3] = piece(al2, -sp.sh[kAl2Vh], ok);
+      lo[5 * d + 4] = piece(al1, -sp.sh[kAl1Vl1], ok);
     }
-    const double Bv = -cp * nrm;
-    const double Bh = rnd(Bv, gamma);
-    const double Bh1 = rnd(Bh, gamma + 11);
-    hi[D] = piece(Bh1, sh[kOneBh1], ok);
-    hi[D + 1] = piece(Bh - Bh1, sh[kOneBh2], ok);
-    lo[5 * D] = piece(1.0, sh[kAl1One], ok);
-    lo[5 * D + 1] = piece(rnd(Bv - Bh, gamma - 12), sh[kOneBl1], ok);
+    hi[D] = piece(1.0, -sp.sh[kOneBh1], ok);
+    hi[D + 1] = piece(1.0, -sp.sh[kOneBh2], ok);
+    const double A = -cp * nrm;
+    const double Ah = rnd(A, sp.gamma);
+    lo[5 * D] = piece(rnd(A - Ah, sp.gamma - 12), -sp.sh[kAl1One], ok);
+    lo[5 * D + 1] = piece(1.0, -sp.sh[kOneBl1], ok);
+    const float Ahf = (float)Ah;
+    ok = ok && ((double)Ahf == Ah);
+    rA[i] = Ahf;
+    store_pieces<NH>(rhi + i * NH, hi);
+    store_pieces<4 * NL>(rlo + i * 4 * NL, lo);
+  } else {
+    const int64_t j = ((int64_t)blockIdx.x - rb) * kBlock + threadIdx.x;
+    if (j >= Npad) return;
+    for (int c = 0; c < C; ++c) bpad[j * C + c] = j < N ? b[j * C + c] : 0.0f;
+    if (j < N) {  // float64 column table
+      const int P64 = col_stride(D);
+      double s = 0.0;
+      for (int d = 0; d < D; ++d) {
+        const double v = (double)y[j * D + d] - (double)y[d];
+        cols[j * P64 + d] = v;
+        s = fma(v, v, s);
+      }
+      cols[j * P64 + D] = -c2 * s;
+      for (int d = D + 1; d < P64; ++d) cols[j * P64 + d] = 0.0;
+    }
+    if (!gate) return;
+    _Float16 hi[8 * NH], lo[32 * NL];
+#pragma unroll
+    for (int k = 0; k < 8 * NH; ++k) hi[k] = (_Float16)0.0f;
+#pragma unroll
+    for (int k = 0; k < 32 * NL; ++k) lo[k] = (_Float16)0.0f;
+    if (j < N) {
+      double nrm = 0.0;
+#pragma unroll
+      for (int d = 0; d < kMaxLowD; ++d) {
+        if (d >= D) break;
+        const double v = ((double)y[j * D + d] - sp.o[d]) * inv_h;
+        nrm = fma(v, v, nrm);
+        const double vh = rnd(v, sp.beta);
+        const double vl1 = rnd(v - vh, sp.beta - 12);
+        const double vl2 = rnd(v - vh - vl1, sp.beta - 24);
+        hi[d] = piece(vh, sp.sh[kAhVh], ok);
+        lo[5 * d + 0] = piece(vl1, sp.sh[kAhVl1], ok);
+        lo[5 * d + 1] = piece(vl2, sp.sh[kAhVl2], ok);
+        lo[5 * d + 2] = piece(vh, sp.sh[kAl1Vh], ok);
+        lo[5 * d + 3] = piece(vh, sp.sh[kAl2Vh], ok);
+        lo[5 * d + 4] = piece(vl1, sp.sh[kAl1Vl1], ok);
+      }
+      const double Bv = -cp * nrm;
+      const double Bh = rnd(Bv, sp.gamma);
+      const double Bh1 = rnd(Bh, sp.gamma + 11);
+      hi[D] = piece(Bh1, sp.sh[kOneBh1], ok);
+      hi[D + 1] = piece(Bh - Bh1, sp.sh[kOneBh2], ok);
+      lo[5 * D] = piece(1.0, sp.sh[kAl1One], ok);
+      lo[5 * D + 1] = piece(rnd(Bv - Bh, sp.gamma - 12), sp.sh[kOneBl1], ok);
+    }
+    store_pieces<NH>(chi + j * NH, hi);
+    store_pieces<4 * NL>(clo + j * 4 * NL, lo);
   }
-#pragma unroll
-  for (int m = 0; m < NH; ++m) {
-    half8 v;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) v[k] = hi[8 * m + k];
-    chi[j * NH + m] = v;
-  }
-#pragma unroll
-  for (int m = 0; m < 4 * NL; ++m) {
-    half8 v;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) v[k] = lo[8 * m + k];
-    clo[j * 4 * NL + m] = v;
-  }
-  if (!ok) P->gate = 0;
+  if (!ok) P->bad = 1;
 }
 
 // out[i][c] = sum_j 2^{e_ij} b[j][c] over the columns [j0, j1) of this split (times rscale[i]
 // with one split), else partial[split][i][c]. A wave holds RT tiles of 16 rows; lane (g, l)
 // (g = lane / 16, l = lane % 16) feeds row l and features 8g..8g+7 of each tile to the MFMA and
 // gets back e for rows 4g..4g+3 against column l of the current 16-column tile. Lanes keep
-// per-column partial sums; the 16 lanes of a row group add theirs at the end.
+// per-column partial sums (folded into the totals every kChunk columns); the 16 lanes of a
+// row group add theirs at the end. The next tile's operands are loaded while the current one
+// is reduced.
 template <int C, int RT, int NH, int NL>
 __global__ void __launch_bounds__(kBlock)
 gauss_sum_mf_kernel(const half8* __restrict__ rhi, const half8* __restrict__ rlo, const float* __restrict__ rA,
-                    const half8* __restrict__ chi, const half8* __restrict__ clo, const float* __restrict__ b,
+                    const half8* __restrict__ chi, const half8* __restrict__ clo, const float* __restrict__ bpad,
                     float* __restrict__ out, const float* __restrict__ rscale, const MfParams* __restrict__ P,
                     int64_t M, int64_t N, int64_t cps) {
-  if (!P->gate) return;
+  if (!P->gate || P->bad) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, g = lane >> 4;
   const int64_t split = blockIdx.y;
@@ -339,55 +378,64 @@ gauss_sum_mf_kernel(const half8* __restrict__ rhi, const half8* __restrict__ rlo
       ii = ii < M ? ii : M - 1;
       cinit[r][q] = rA[ii];
 #pragma unroll
-      for (int c = 0; c < C; ++c) acc[r][q][c] = 0.0f;
+      for (int c = 0; c < C; ++c) acc[r][q][c] = part[r][q][c] = 0.0f;
     }
   }
   const int gh = g < NH ? g : 0;
-  for (int64_t jc = j0; jc < j1; jc += kChunk) {
-    const int64_t je = (jc + kChunk < j1) ? jc + kChunk : j1;
+  half8 bhi = zero8, blo[NL];
+  float bj[C];
+  auto load = [&](int64_t jt, half8& h, half8 (&l)[NL], float (&w)[C]) {
+    const int64_t j = jt + l16;
+    h = chi[j * NH + gh];
 #pragma unroll
-    for (int r = 0; r < RT; ++r)
+    for (int m = 0; m < NL; ++m) l[m] = clo[j * 4 * NL + m * 4 + g];
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
+    for (int c = 0; c < C; ++c) w[c] = bpad[j * C + c];
+  };
+  if (j0 < j1) load(j0, bhi, blo, bj);
+  int tiles = 0;
+  for (int64_t jt = j0; jt < j1; jt += 16) {
+    half8 nhi, nlo[NL];
+    float nb[C];
+    load(jt + 16 < j1 ? jt + 16 : jt, nhi, nlo, nb);
 #pragma unroll
-        for (int c = 0; c < C; ++c) part[r][q][c] = 0.0f;
-    for (int64_t jt = jc; jt < je; jt += 16) {
-      const int64_t j = jt + l16;
-      const half8 bhi = chi[j * NH + gh];
-      half8 blo[NL];
+    for (int r = 0; r < RT; ++r) {
+      f32x4 e = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[r], bhi, cinit[r], 0, 0, 0);
 #pragma unroll
-      for (int m = 0; m < NL; ++m) blo[m] = clo[j * 4 * NL + m * 4 + g];
-      float bj[C];
+      for (int m = 0; m < NL; ++m) e = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[r][m], blo[m], e, 0, 0, 0);
 #pragma unroll
-      for (int c = 0; c < C; ++c) bj[c] = j < N ? b[j * C + c] : 0.0f;
+      for (int q = 0; q < 4; ++q) {
+        const float k = exp2_hw(e[q]);
 #pragma unroll
-      for (int r = 0; r < RT; ++r) {
-        f32x4 e = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[r], bhi, cinit[r], 0, 0, 0);
-#pragma unroll
-        for (int m = 0; m < NL; ++m) e = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[r][m], blo[m], e, 0, 0, 0);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float k = exp2_hw(e[q]);
-#pragma unroll
-          for (int c = 0; c < C; ++c) part[r][q][c] = fmaf(k, bj[c], part[r][q][c]);
-        }
+        for (int c = 0; c < C; ++c) part[r][q][c] = fmaf(k, bj[c], part[r][q][c]);
       }
     }
+    if (++tiles == kChunkTiles) {
+      tiles = 0;
 #pragma unroll
-    for (int r = 0; r < RT; ++r)
+      for (int r = 0; r < RT; ++r)
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
+        for (int q = 0; q < 4; ++q)
 #pragma unroll
-        for (int c = 0; c < C; ++c) acc[r][q][c] += part[r][q][c];
+          for (int c = 0; c < C; ++c) {
+            acc[r][q][c] += part[r][q][c];
+            part[r][q][c] = 0.0f;
+          }
+    }
+    bhi = nhi;
+#pragma unroll
+    for (int m = 0; m < NL; ++m) blo[m] = nlo[m];
+#pragma unroll
+    for (int c = 0; c < C; ++c) bj[c] = nb[c];
   }
-  // add the 16 per-column partials of each row (lanes 16g .. 16g + 15)
+  // fold the last chunk, then add the 16 per-column partials of each row (lanes 16g .. 16g+15)
 #pragma unroll
   for (int r = 0; r < RT; ++r)
 #pragma unroll
     for (int q = 0; q < 4; ++q)
 #pragma unroll
       for (int c = 0; c < C; ++c) {
-        float v = acc[r][q][c];
+        float v = acc[r][q][c] + part[r][q][c];
         v += __shfl_xor(v, 1);
         v += __shfl_xor(v, 2);
         v += __shfl_xor(v, 4);
@@ -409,19 +457,22 @@ gauss_sum_mf_kernel(const half8* __restrict__ rhi, const half8* __restrict__ rlo
     }
 }
 
-// Byte offsets of the operand region: parameters, row operands, column operands.
+// Byte offsets of the operand region: parameters, bounds records, row operands, column
+// operands, padded weights.
 struct MfLayout {
   int NH, NL;
   int64_t Npad;
-  size_t rhi, rlo, rA, chi, clo, total;
+  size_t parts, rhi, rlo, rA, chi, clo, bpad, total;
 };
 
-MfLayout mf_layout(int64_t M, int64_t N, int D) {
+MfLayout mf_layout(int64_t M, int64_t N, int D, int C) {
   MfLayout L;
   L.NH = (D + 2 <= 8) ? 1 : 2;
   L.NL = (5 * D + 2 <= 32) ? 1 : 2;
   L.Npad = ceil_div(N, 16) * 16;
   size_t off = align_up(sizeof(MfParams));
+  L.parts = off;
+  off += align_up((size_t)kBoundBlocks * 2 * kMaxLowD * sizeof(unsigned int));
   L.rhi = off;
   off += align_up((size_t)M * 16 * L.NH);
   L.rlo = off;
@@ -432,19 +483,21 @@ MfLayout mf_layout(int64_t M, int64_t N, int D) {
   off += align_up((size_t)L.Npad * 16 * L.NH);
   L.clo = off;
   off += align_up((size_t)L.Npad * 64 * L.NL);
+  L.bpad = off;
+  off += align_up((size_t)L.Npad * C * sizeof(float));
   L.total = off;
   return L;
 }
 
 template <int C, int RT, int NH, int NL>
-hipError_t sweep(char* r, const MfLayout& L, const float* b, float* dst, const float* rscale, int64_t M, int64_t N,
-                 const Plan& p, hipStream_t s) {
+hipError_t sweep(char* r, const MfLayout& L, float* dst, const float* rscale, int64_t M, int64_t N, const Plan& p,
+                 hipStream_t s) {
   dim3 grid((unsigned)p.mf_row_blocks, (unsigned)p.splits);
   gauss_sum_mf_kernel<C, RT, NH, NL><<<grid, kBlock, 0, s>>>(
       reinterpret_cast<const half8*>(r + L.rhi), reinterpret_cast<const half8*>(r + L.rlo),
       reinterpret_cast<const float*>(r + L.rA), reinterpret_cast<const half8*>(r + L.chi),
-      reinterpret_cast<const half8*>(r + L.clo), b, dst, rscale, reinterpret_cast<const MfParams*>(r), M, N,
-      p.cols_per_split);
+      reinterpret_cast<const half8*>(r + L.clo), reinterpret_cast<const float*>(r + L.bpad), dst, rscale,
+      reinterpret_cast<const MfParams*>(r), M, N, p.cols_per_split);
   return hipGetLastError();
 }
 
@@ -452,13 +505,13 @@ hipError_t sweep(char* r, const MfLayout& L, const float* b, float* dst, const f
 constexpr int max_rt(int C) { return C <= 2 ? 4 : (C <= 4 ? 2 : 1); }
 
 template <int C, int NH, int NL>
-hipError_t sweep_rt(char* r, const MfLayout& L, const float* b, float* dst, const float* rscale, int64_t M,
-                    int64_t N, const Plan& p, hipStream_t s) {
+hipError_t sweep_rt(char* r, const MfLayout& L, float* dst, const float* rscale, int64_t M, int64_t N, const Plan& p,
+                    hipStream_t s) {
   if constexpr (max_rt(C) >= 4)
-    if (p.mf_rt == 4) return sweep<C, 4, NH, NL>(r, L, b, dst, rscale, M, N, p, s);
+    if (p.mf_rt == 4) return sweep<C, 4, NH, NL>(r, L, dst, rscale, M, N, p, s);
   if constexpr (max_rt(C) >= 2)
-    if (p.mf_rt == 2) return sweep<C, 2, NH, NL>(r, L, b, dst, rscale, M, N, p, s);
-  if (p.mf_rt == 1) return sweep<C, 1, NH, NL>(r, L, b, dst, rscale, M, N, p, s);
+    if (p.mf_rt == 2) return sweep<C, 2, NH, NL>(r, L, dst, rscale, M, N, p, s);
+  if (p.mf_rt == 1) return sweep<C, 1, NH, NL>(r, L, dst, rscale, M, N, p, s);
   return hipErrorInvalidValue;
 }
 
@@ -486,18 +539,18 @@ int occupancy_c(bool wide, int rt) {
 }
 
 template <int C>
-hipError_t sweep_c(char* r, const MfLayout& L, const float* b, float* dst, const float* rscale, int64_t M, int64_t N,
-                   const Plan& p, hipStream_t s) {
-  if (L.NH == 1 && L.NL == 1) return sweep_rt<C, 1, 1>(r, L, b, dst, rscale, M, N, p, s);
-  return sweep_rt<C, 2, 2>(r, L, b, dst, rscale, M, N, p, s);
+hipError_t sweep_c(char* r, const MfLayout& L, float* dst, const float* rscale, int64_t M, int64_t N, const Plan& p,
+                   hipStream_t s) {
+  if (L.NH == 1 && L.NL == 1) return sweep_rt<C, 1, 1>(r, L, dst, rscale, M, N, p, s);
+  return sweep_rt<C, 2, 2>(r, L, dst, rscale, M, N, p, s);
 }
 
 }  // namespace
 }  // namespace lowd
 
-size_t mf_region_bytes(int64_t M, int64_t N, int D) { return lowd::mf_layout(M, N, D).total; }
+size_t mf_region_bytes(int64_t M, int64_t N, int D, int C) { return lowd::mf_layout(M, N, D, C).total; }
 
-const int* mf_gate(const void* region) { return &static_cast<const lowd::MfParams*>(region)->gate; }
+const int* mf_decision(const void* region) { return &static_cast<const lowd::MfParams*>(region)->gate; }
 
 int mf_rows_per_lane(int C) { return lowd::max_rt(C); }
 
@@ -505,7 +558,7 @@ int mf_occupancy(int D, int C, int rt) {
   // resident workgroups per CU of the sweep instance, from its register use (cached per
   // instance; 4 when the runtime cannot say)
   static std::atomic<int> cache[2][kMaxLowC + 1][5];
-  const int wide = lowd::mf_layout(1, 1, D).NH == 2 ? 1 : 0;
+  const int wide = lowd::mf_layout(1, 1, D, 1).NH == 2 ? 1 : 0;
   int dev = 0;
   if (C < 1 || C > kMaxLowC || (rt != 1 && rt != 2 && rt != 4) || hipGetDevice(&dev) != hipSuccess) return 4;
   std::atomic<int>& slot = cache[wide][C][rt];
@@ -531,40 +584,39 @@ int mf_occupancy(int D, int C, int rt) {
   return n;
 }
 
-hipError_t launch_mf_prepare(const float* x, const float* y, void* region, int64_t M, int64_t N, int D, double c2,
-                             hipStream_t s) {
+hipError_t launch_mf_prepare(const float* x, const float* y, const float* b, double* cols, void* region, int64_t M,
+                             int64_t N, int D, int C, double c2, hipStream_t s) {
   using namespace lowd;
   char* r = static_cast<char*>(region);
-  const MfLayout L = mf_layout(M, N, D);
+  const MfLayout L = mf_layout(M, N, D, C);
   MfParams* P = reinterpret_cast<MfParams*>(r);
-  mf_init_kernel<<<1, 64, 0, s>>>(P);
+  unsigned int* parts = reinterpret_cast<unsigned int*>(r + L.parts);
   const int64_t n = M > N ? M : N;
-  int64_t blocks = ceil_div(n, kBlock);
-  if (blocks > 1024) blocks = 1024;
-  mf_bounds_kernel<<<(unsigned)blocks, kBlock, 0, s>>>(x, y, M, N, D, P);
-  mf_params_kernel<<<1, 64, 0, s>>>(P, D, c2);
+  int64_t nb = ceil_div(n, kBlock);
+  if (nb > kBoundBlocks) nb = kBoundBlocks;
+  mf_bounds_kernel<<<(unsigned)nb, kBlock, 0, s>>>(x, y, M, N, D, parts, P);
+  const int64_t rb = ceil_div(M, kBlock), cb = ceil_div(L.Npad, kBlock);
   half8* rhi = reinterpret_cast<half8*>(r + L.rhi);
   half8* rlo = reinterpret_cast<half8*>(r + L.rlo);
   float* rA = reinterpret_cast<float*>(r + L.rA);
   half8* chi = reinterpret_cast<half8*>(r + L.chi);
   half8* clo = reinterpret_cast<half8*>(r + L.clo);
-  const unsigned rb = (unsigned)ceil_div(M, kBlock), cb = (unsigned)ceil_div(L.Npad, kBlock);
-  if (L.NH == 1 && L.NL == 1) {
-    mf_rows_kernel<1, 1><<<rb, kBlock, 0, s>>>(x, rhi, rlo, rA, M, D, P);
-    mf_cols_kernel<1, 1><<<cb, kBlock, 0, s>>>(y, chi, clo, N, L.Npad, D, P);
-  } else {
-    mf_rows_kernel<2, 2><<<rb, kBlock, 0, s>>>(x, rhi, rlo, rA, M, D, P);
-    mf_cols_kernel<2, 2><<<cb, kBlock, 0, s>>>(y, chi, clo, N, L.Npad, D, P);
-  }
+  float* bpad = reinterpret_cast<float*>(r + L.bpad);
+  if (L.NH == 1 && L.NL == 1)
+    mf_prep_kernel<1, 1><<<(unsigned)(rb + cb), kBlock, 0, s>>>(x, y, b, C, cols, rhi, rlo, rA, chi, clo, bpad, parts,
+                                                               (int)nb, M, N, L.Npad, D, c2, rb, P);
+  else
+    mf_prep_kernel<2, 2><<<(unsigned)(rb + cb), kBlock, 0, s>>>(x, y, b, C, cols, rhi, rlo, rA, chi, clo, bpad, parts,
+                                                               (int)nb, M, N, L.Npad, D, c2, rb, P);
   return hipGetLastError();
 }
 
-hipError_t launch_mf_sum(const float* b, const float* rscale, float* dst, void* region, int64_t M, int64_t N, int D,
-                         int C, const Plan& p, hipStream_t s) {
+hipError_t launch_mf_sum(const float* rscale, float* dst, void* region, int64_t M, int64_t N, int D, int C,
+                         const Plan& p, hipStream_t s) {
   using namespace lowd;
   char* r = static_cast<char*>(region);
-  const MfLayout L = mf_layout(M, N, D);
-#define KEOPS_MF_C(Cv) sweep_c<Cv>(r, L, b, dst, rscale, M, N, p, s)
+  const MfLayout L = mf_layout(M, N, D, C);
+#define KEOPS_MF_C(Cv) sweep_c<Cv>(r, L, dst, rscale, M, N, p, s)
   KEOPS_SWITCH_C(C, KEOPS_MF_C)
 #undef KEOPS_MF_C
 }

@@ -23,7 +23,7 @@ gauss_sum_kernel(const float* __restrict__ x, const float* __restrict__ y,
                  const double* __restrict__ cols, const float* __restrict__ b,
                  float* __restrict__ out, const float* __restrict__ rscale, int64_t M, int64_t N, int64_t cps,
                  double c2, const int* __restrict__ skip) {
-  if (skip && *skip) return;  // the matrix-core sweep took these inputs
+  if (skip && skip[0] && !skip[1]) return;  // the matrix-core sweep takes these inputs
   constexpr int P = (D + 2) & ~1;
   const int64_t split = blockIdx.y;
   const int64_t j0 = split * cps;
@@ -123,13 +123,10 @@ hipError_t launch_gauss_sum_lowd(const float* x, const float* y, double* cols, c
                                  float* out, float* partial, void* mf, int64_t M, int64_t N, int D, int C, double c2,
                                  const Plan& p, hipStream_t s) {
   float* dst = p.splits > 1 ? partial : out;
-  // Operands for the matrix-core sweep and the device-side choice of sweep; the float64 column
-  // table and sweep return at once when the matrix-core sweep runs.
-  hipError_t e = launch_mf_prepare(x, y, mf, M, N, D, c2, s);
+  // Operands of both sweeps and the device-side choice between them.
+  hipError_t e = launch_mf_prepare(x, y, b, cols, mf, M, N, D, C, c2, s);
   if (e != hipSuccess) return e;
-  const int* gate = mf_gate(mf);
-  e = launch_prep_cols(y, cols, N, D, c2, true, s, gate);
-  if (e != hipSuccess) return e;
+  const int* gate = mf_decision(mf);
   auto run = [&]() -> hipError_t {
 #define KEOPS_GS(Dv) lowd::gauss_sum_d<Dv>(C, x, y, cols, b, dst, rscale, M, N, c2, gate, p, s)
     KEOPS_SWITCH_D(D, KEOPS_GS)
@@ -137,7 +134,7 @@ hipError_t launch_gauss_sum_lowd(const float* x, const float* y, double* cols, c
   };
   e = run();
   if (e != hipSuccess) return e;
-  e = launch_mf_sum(b, rscale, dst, mf, M, N, D, C, p, s);
+  e = launch_mf_sum(rscale, dst, mf, M, N, D, C, p, s);
   if (e != hipSuccess || p.splits == 1) return e;
   return lowd::launch_combine_sum(partial, out, M * C, p.splits, rscale, C, s);
 }

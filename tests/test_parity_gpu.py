@@ -76,6 +76,38 @@ def test_gauss_sum_shapes(M, N, D, C, sigma):
     assert_normalised(got, want, norm, TOL_F32, "gauss_sum")
 
 
+# The float32 low-D sum computes its exponent on the matrix cores when the exponent scale
+# 2 c2 h^2 (h: half-width of the points' bounding box, c2 = log2(e) / (2 sigma^2)) is small
+# enough for the low part of the split exponent to stay below 32 (2 c2 h^2 <= 2^13 at D = 3,
+# <= 2^10 at D = 8), and falls back to the float64 sweep otherwise. These cases sit on both
+# sides of that line, plus spreads that move h: an offset cube, a symmetric box, an outlier.
+EXPONENT_REGIMES = [
+    # (D, sigma, lo, hi, outlier)
+    (3, 0.3, 0.0, 1.0, False), (3, 0.01, 0.0, 1.0, False), (3, 0.0067, 0.0, 1.0, False),
+    (3, 0.006, 0.0, 1.0, False), (3, 0.001, 0.0, 1.0, False), (3, 0.05, 1000.0, 1001.0, False),
+    (3, 0.5, -5.0, 5.0, False), (3, 0.05, 0.0, 1.0, True), (1, 0.004, 0.0, 1.0, False),
+    (8, 0.5, 0.0, 1.0, False), (8, 0.03, 0.0, 1.0, False), (8, 0.015, 0.0, 1.0, False),
+    (6, 0.2, -1.0, 1.0, False), (7, 0.3, 0.0, 1.0, False),
+]
+
+
+@pytest.mark.parametrize("D,sigma,lo,hi,outlier", EXPONENT_REGIMES)
+def test_gauss_sum_exponent_regimes(D, sigma, lo, hi, outlier):
+    import pairwise_reductions_amd as pr
+    _announce("gauss_sum_regime", D=D, sigma=sigma, lo=lo, hi=hi, outlier=outlier)
+    M, N, C = 700, 3001, 2
+    x, y, b = _rand(int(sigma * 1e4) + 31 * D, M, N, D, C, lo, hi)
+    # every row gets a column within about sigma, so no row's sum underflows float32
+    rng = np.random.default_rng(D)
+    y[:M] = x + (0.5 * sigma * rng.standard_normal((M, D))).astype(np.float32)
+    if outlier:
+        y[M + 17] = 1000.0
+    sig = float(np.float32(sigma))
+    got = _host(pr.gauss_sum(_dev(x), _dev(y), _dev(b), sig))
+    want, norm = oracle.gauss_sum(x, y, b, sig, workers=8)
+    assert_normalised(got, want, norm, TOL_F32, "gauss_sum regime")
+
+
 def test_gauss_sum_workload_10k_all_rows():
     import pairwise_reductions_amd as pr
     inp = workloads.make_inputs("gauss_sum_10k")
