@@ -138,7 +138,7 @@ Plan plan_lowd(int op, int64_t M, int64_t N, int D, int C, int K, int num_cus) {
     p.mf_rt = rt;
     p.mf_row_blocks = M > 0 ? ceil_div(M, (int64_t)64 * rt) : 0;
     lead_blocks = p.mf_row_blocks;
-    granule = 16;
+    granule = 32;
   }
   // Split the columns so that (a) there are at least eight workgroups (32 wave64s) per compute
   // unit over the launch, and (b) one split's column table stays within lowd::kSplitCols columns,
@@ -152,8 +152,8 @@ Plan plan_lowd(int op, int64_t M, int64_t N, int D, int C, int K, int num_cus) {
   if ((op == 2 || op == 6) && max_split > 16) max_split = 16;  // argKmin partial lists are K entries per row
   if (S > max_split) S = max_split;
   if (S < 1) S = 1;
-  // Columns per split: a multiple of 8 (16 for the matrix-core tiles); the split count is what
-  // that leaves.
+  // Columns per split: a multiple of 8 (32, two tiles, for the matrix-core sweep); the split
+  // count is what that leaves.
   auto split_of = [&](int64_t s, int64_t& cps_out) {
     int64_t c = s > 1 ? ceil_div(N, s) : (N > 0 ? N : 1);
     c = ceil_div(c, granule) * granule;

@@ -381,36 +381,51 @@ gauss_sum_mf_kernel(const half8* __restrict__ rhi, const half8* __restrict__ rlo
       for (int c = 0; c < C; ++c) acc[r][q][c] = part[r][q][c] = 0.0f;
     }
   }
-  const int gh = g < NH ? g : 0;
-  half8 bhi = zero8, blo[NL];
-  float bj[C];
-  auto load = [&](int64_t jt, half8& h, half8 (&l)[NL], float (&w)[C]) {
-    const int64_t j = jt + l16;
-    h = chi[j * NH + gh];
-#pragma unroll
-    for (int m = 0; m < NL; ++m) l[m] = clo[j * 4 * NL + m * 4 + g];
-#pragma unroll
-    for (int c = 0; c < C; ++c) w[c] = bpad[j * C + c];
+  // Per-lane element offsets into a 16-column tile; the tile bases are wave-uniform.
+  const int ochi = l16 * NH + (g < NH ? g : 0), oclo = l16 * 4 * NL + g, ob = l16 * C;
+  struct Ops {
+    half8 h, l[NL];
+    float w[C];
   };
-  if (j0 < j1) load(j0, bhi, blo, bj);
-  int tiles = 0;
-  for (int64_t jt = j0; jt < j1; jt += 16) {
-    half8 nhi, nlo[NL];
-    float nb[C];
-    load(jt + 16 < j1 ? jt + 16 : jt, nhi, nlo, nb);
+  auto load = [&](int64_t jt, Ops& o) {
+    const half8* ph = chi + jt * NH;
+    const half8* pl = clo + jt * 4 * NL;
+    const float* pw = bpad + jt * C;
+    o.h = ph[ochi];
+#pragma unroll
+    for (int m = 0; m < NL; ++m) o.l[m] = pl[oclo + 4 * m];
+#pragma unroll
+    for (int c = 0; c < C; ++c) o.w[c] = pw[ob + c];
+  };
+  auto tile = [&](const Ops& o) {
 #pragma unroll
     for (int r = 0; r < RT; ++r) {
-      f32x4 e = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[r], bhi, cinit[r], 0, 0, 0);
+      f32x4 e = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[r], o.h, cinit[r], 0, 0, 0);
 #pragma unroll
-      for (int m = 0; m < NL; ++m) e = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[r][m], blo[m], e, 0, 0, 0);
+      for (int m = 0; m < NL; ++m) e = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[r][m], o.l[m], e, 0, 0, 0);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const float k = exp2_hw(e[q]);
 #pragma unroll
-        for (int c = 0; c < C; ++c) part[r][q][c] = fmaf(k, bj[c], part[r][q][c]);
+        for (int c = 0; c < C; ++c) part[r][q][c] = fmaf(k, o.w[c], part[r][q][c]);
       }
     }
-    if (++tiles == kChunkTiles) {
+  };
+  // Two tiles per trip with alternating operand sets: each load is issued one tile ahead of its
+  // use, and the sets never need copying. Column ranges are whole pairs of tiles (splits are
+  // multiples of 32 columns and the tables are zero-padded to a multiple of 32).
+  const int64_t ntiles = j1 > j0 ? 2 * ((j1 - j0 + 31) / 32) : 0;
+  Ops A, B;
+  if (ntiles > 0) load(j0, A);
+  int tiles = 0;
+  for (int64_t t = 0; t < ntiles; t += 2) {
+    const int64_t ja = j0 + t * 16;
+    load(ja + 16, B);
+    tile(A);
+    load(t + 2 < ntiles ? ja + 32 : ja, A);
+    tile(B);
+    tiles += 2;
+    if (tiles == kChunkTiles) {
       tiles = 0;
 #pragma unroll
       for (int r = 0; r < RT; ++r)
@@ -422,11 +437,6 @@ gauss_sum_mf_kernel(const half8* __restrict__ rhi, const half8* __restrict__ rlo
             part[r][q][c] = 0.0f;
           }
     }
-    bhi = nhi;
-#pragma unroll
-    for (int m = 0; m < NL; ++m) blo[m] = nlo[m];
-#pragma unroll
-    for (int c = 0; c < C; ++c) bj[c] = nb[c];
   }
   // fold the last chunk, then add the 16 per-column partials of each row (lanes 16g .. 16g+15)
 #pragma unroll
@@ -469,7 +479,7 @@ MfLayout mf_layout(int64_t M, int64_t N, int D, int C) {
   MfLayout L;
   L.NH = (D + 2 <= 8) ? 1 : 2;
   L.NL = (5 * D + 2 <= 32) ? 1 : 2;
-  L.Npad = ceil_div(N, 16) * 16;
+  L.Npad = ceil_div(N, 32) * 32;
   size_t off = align_up(sizeof(MfParams));
   L.parts = off;
   off += align_up((size_t)kBoundBlocks * 2 * kMaxLowD * sizeof(unsigned int));
