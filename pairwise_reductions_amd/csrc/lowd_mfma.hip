@@ -42,6 +42,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kMinK = 4;           // exponent scales below 2^4 are treated as 2^4
 constexpr double kMaxLow = 32.0;   // largest admissible bound on the low part
 constexpr int kBoundBlocks = 256;  // most workgroups of the bounds pass
+constexpr uint32_t kXcds = 8;      // accelerator complexes (each with its own L2) on the chip
+constexpr int64_t kMaxLaunch = int64_t(1) << 30;  // most workgroups per sweep launch
 constexpr int kChunkTiles = kChunk / 16;
 
 // Product kinds (row piece x column piece); the shift table is indexed by these.
@@ -352,14 +354,21 @@ __global__ void __launch_bounds__(kBlock)
 gauss_sum_mf_kernel(const half8* __restrict__ rhi, const half8* __restrict__ rlo, const float* __restrict__ rA,
                     const half8* __restrict__ chi, const half8* __restrict__ clo, const float* __restrict__ bpad,
                     float* __restrict__ out, const float* __restrict__ rscale, const MfParams* __restrict__ P,
-                    int64_t M, int64_t N, int64_t cps) {
+                    int64_t M, int64_t N, int64_t cps, int64_t row_blocks, int64_t splits, int64_t pair0) {
   if (!P->gate || P->bad) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, g = lane >> 4;
-  const int64_t split = blockIdx.y;
+  // Workgroups go to the chip's 8 XCDs round-robin by id. Renumber them so that each XCD takes a
+  // contiguous run of (split, row block) pairs, split-major: the workgroups resident on one XCD
+  // then sweep the same split's column table, which stays in that XCD's L2. (This launch covers
+  // pairs [pair0, pair0 + gridDim.x).)
+  const uint32_t wg = blockIdx.x, total = gridDim.x;
+  const uint32_t per = total / kXcds, extra = total % kXcds, xcd = wg % kXcds;
+  const int64_t pair = pair0 + xcd * per + (xcd < extra ? xcd : extra) + wg / kXcds;
+  const int64_t split = pair / row_blocks;
   const int64_t j0 = split * cps;
   const int64_t j1 = (j0 + cps < N) ? j0 + cps : N;
-  const int64_t base = ((int64_t)blockIdx.x * (kBlock / 64) + wave) * 16 * RT;
+  const int64_t base = ((int64_t)(pair % row_blocks) * (kBlock / 64) + wave) * 16 * RT;
   const half8 zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
 
   half8 ahi[RT], alo[RT][NL];
@@ -453,7 +462,7 @@ gauss_sum_mf_kernel(const half8* __restrict__ rhi, const half8* __restrict__ rlo
         acc[r][q][c] = v;
       }
   float* dst = out + split * M * C;
-  const bool scaled = rscale && gridDim.y == 1;
+  const bool scaled = rscale && splits == 1;
 #pragma unroll
   for (int r = 0; r < RT; ++r)
 #pragma unroll
@@ -502,13 +511,19 @@ MfLayout mf_layout(int64_t M, int64_t N, int D, int C) {
 template <int C, int RT, int NH, int NL>
 hipError_t sweep(char* r, const MfLayout& L, float* dst, const float* rscale, int64_t M, int64_t N, const Plan& p,
                  hipStream_t s) {
-  dim3 grid((unsigned)p.mf_row_blocks, (unsigned)p.splits);
-  gauss_sum_mf_kernel<C, RT, NH, NL><<<grid, kBlock, 0, s>>>(
-      reinterpret_cast<const half8*>(r + L.rhi), reinterpret_cast<const half8*>(r + L.rlo),
-      reinterpret_cast<const float*>(r + L.rA), reinterpret_cast<const half8*>(r + L.chi),
-      reinterpret_cast<const half8*>(r + L.clo), reinterpret_cast<const float*>(r + L.bpad), dst, rscale,
-      reinterpret_cast<const MfParams*>(r), M, N, p.cols_per_split);
-  return hipGetLastError();
+  // one launch per 2^30 workgroups (a launch's grid is limited to 2^31 - 1)
+  const int64_t pairs = p.mf_row_blocks * p.splits;
+  for (int64_t pair0 = 0; pair0 < pairs; pair0 += kMaxLaunch) {
+    const int64_t n = pairs - pair0 < kMaxLaunch ? pairs - pair0 : kMaxLaunch;
+    gauss_sum_mf_kernel<C, RT, NH, NL><<<(unsigned)n, kBlock, 0, s>>>(
+        reinterpret_cast<const half8*>(r + L.rhi), reinterpret_cast<const half8*>(r + L.rlo),
+        reinterpret_cast<const float*>(r + L.rA), reinterpret_cast<const half8*>(r + L.chi),
+        reinterpret_cast<const half8*>(r + L.clo), reinterpret_cast<const float*>(r + L.bpad), dst, rscale,
+        reinterpret_cast<const MfParams*>(r), M, N, p.cols_per_split, p.mf_row_blocks, p.splits, pair0);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 // Row tiles per wave: 4 for C <= 2, 2 for C <= 4, else 1 (register budgets); fewer for few rows.
