@@ -349,8 +349,13 @@ mf_prep_kernel(const float* __restrict__ x, const float* __restrict__ y, const f
 // per-column partial sums (folded into the totals every kChunk columns); the 16 lanes of a
 // row group add theirs at the end. The next tile's operands are loaded while the current one
 // is reduced.
+// Waves per SIMD the register allocation must leave room for: 4 for the narrow single-channel
+// form with 4 row tiles (it then fits 128 VGPRs without spilling), else no constraint.
+template <int C, int RT, int NH>
+constexpr int sweep_waves() { return (NH == 1 && C == 1 && RT == 4) ? 4 : 1; }
+
 template <int C, int RT, int NH, int NL>
-__global__ void __launch_bounds__(kBlock)
+__global__ void __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(sweep_waves<C, RT, NH>())))
 gauss_sum_mf_kernel(const half8* __restrict__ rhi, const half8* __restrict__ rlo, const float* __restrict__ rA,
                     const half8* __restrict__ chi, const half8* __restrict__ clo, const float* __restrict__ bpad,
                     float* __restrict__ out, const float* __restrict__ rscale, const MfParams* __restrict__ P,
