@@ -82,7 +82,7 @@ struct LowdLayout {
   size_t aux_off;               // one double: the largest column norm (argKmin screening)
   size_t part_off, part_bytes;  // per-split partials (argKmin lists for ops 2 and 6)
   size_t lse_off;               // per-split (m, l) pairs of the fused argKmin + LSE (op 6)
-  size_t mf_off;                // Gauss sum: the matrix-core operand region
+  size_t mf_off;                // Gauss sum and LSE: the matrix-core operand region
   size_t total;
 };
 
@@ -110,7 +110,8 @@ LowdLayout lowd_layout(int op, int64_t M, int64_t N, int D, int C, int K) {
   }
   L.lse_off = L.part_off + L.part_bytes;
   L.mf_off = L.lse_off + lse_bytes;
-  L.total = L.mf_off + (op == KEOPS_OP_GAUSS_SUM ? keops::mf_region_bytes(M, N, D, C) : 0);
+  L.total = L.mf_off + (op == KEOPS_OP_GAUSS_SUM ? keops::mf_region_bytes(M, N, D, C)
+                                               : op == KEOPS_OP_LSE ? keops::mf_region_bytes(M, N, D, 0) : 0);
   if (M == 0 || N == 0) L.total = 0;
   return L;
 }
@@ -553,8 +554,7 @@ int keops_lse(const float* x, const float* y, float* out, int64_t M, int64_t N, 
   double* cols = reinterpret_cast<double*>(ws + L.cols_off);
   double* part = reinterpret_cast<double*>(ws + L.part_off);
   const double c2 = c2_of(sigma);
-  KEOPS_HIP(keops::launch_prep_cols(y, cols, N, D, c2, true, stream), "prep_cols");
-  KEOPS_HIP(keops::launch_lse_lowd(x, y, cols, out, part, M, N, D, c2, L.plan, stream), "lse_lowd");
+  KEOPS_HIP(keops::launch_lse_lowd(x, y, cols, out, part, ws + L.mf_off, M, N, D, c2, L.plan, stream), "lse_lowd");
   return ok();
 }
 

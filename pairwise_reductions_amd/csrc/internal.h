@@ -49,9 +49,10 @@ hipError_t launch_gauss_sum_lowd(const float* x, const float* y, double* cols, c
                                  const float* rscale, float* out, float* partial, void* mf,
                                  int64_t M, int64_t N, int D, int C, double c2, const Plan& p,
                                  hipStream_t s);
-// Matrix-core Gauss sum pieces (lowd_mfma.hip): operand region size; the decision, two ints
-// (gate, bad): the matrix-core sweep runs when gate != 0 and bad == 0; row tiles per wave for C
-// channels; preparation (also writes the float64 column table) and sweep.
+// Matrix-core Gauss sum pieces (lowd_mfma.hip): operand region size (C = 0: no weights); the
+// decision, two ints (gate, bad): the matrix-core sweep runs when gate != 0 and bad == 0; row
+// tiles per wave for C channels; preparation (also writes the float64 column table; b may be
+// null) and sweeps.
 size_t mf_region_bytes(int64_t M, int64_t N, int D, int C);
 const int* mf_decision(const void* region);
 int mf_rows_per_lane(int C);
@@ -60,8 +61,13 @@ hipError_t launch_mf_prepare(const float* x, const float* y, const float* b, dou
                              int64_t M, int64_t N, int D, int C, double c2, hipStream_t s);
 hipError_t launch_mf_sum(const float* rscale, float* dst, void* region, int64_t M, int64_t N, int D,
                          int C, const Plan& p, hipStream_t s);
-hipError_t launch_lse_lowd(const float* x, const float* y, const double* cols, float* out,
-                           double* partial, int64_t M, int64_t N, int D, double c2,
+// log-sum-exp on the matrix cores: out (one split) or per-split (m, l) pairs in `partial`
+hipError_t launch_mf_lse(float* out, void* partial, void* region, int64_t M, int64_t N, int D,
+                         const Plan& p, hipStream_t s);
+// log-sum-exp: prepares as launch_gauss_sum_lowd (no weights) and runs the matrix-core or the
+// float64 sweep, chosen on the device.
+hipError_t launch_lse_lowd(const float* x, const float* y, double* cols, float* out,
+                           double* partial, void* mf, int64_t M, int64_t N, int D, double c2,
                            const Plan& p, hipStream_t s);
 // argKmin of d^2_ij - w_j (w may be null), optionally fused with the log-sum-exp reduction
 // (with_lse, only without weights): builds the uncentred column table in `cols` and the

@@ -127,13 +127,14 @@ Plan plan_lowd(int op, int64_t M, int64_t N, int D, int C, int K, int num_cus) {
   }
   p.rows_per_block = kBlock * p.R;
   p.row_blocks = M > 0 ? ceil_div(M, p.rows_per_block) : 0;
-  // The Gauss sum's matrix-core sweep takes 16 RT rows per wave; the column splits are planned
-  // for it (the float64 sweep, which runs only when the matrix-core one declines, shares them).
+  // The Gauss sum's and the log-sum-exp's matrix-core sweeps take 16 RT rows per wave; the
+  // column splits are planned for them (the float64 sweeps, which run only when the matrix-core
+  // ones decline, share them).
   int64_t lead_blocks = p.row_blocks;
   int64_t granule = 8;
-  if (op == 0) {
+  if (op == 0 || op == 1) {
     const int64_t max_cols_splits = N / 256 > 1 ? N / 256 : 1;
-    int rt = mf_rows_per_lane(C);
+    int rt = mf_rows_per_lane(op == 1 ? 0 : C);
     while (rt > 1 && ceil_div(M, (int64_t)64 * rt) * max_cols_splits < (int64_t)num_cus * 4) rt /= 2;
     p.mf_rt = rt;
     p.mf_row_blocks = M > 0 ? ceil_div(M, (int64_t)64 * rt) : 0;
@@ -167,7 +168,7 @@ Plan plan_lowd(int op, int64_t M, int64_t N, int D, int C, int K, int num_cus) {
   // whole workgroup's duration. Among split counts between half and twice the one above
   // (keeping the L2 bound), take the one whose workgroups fill their rounds best.
   // resident workgroups per CU (register budgets)
-  const int occupancy = op == 0 ? mf_occupancy(D, C, p.mf_rt) : (op == 1 ? 7 : 8);
+  const int occupancy = (op == 0 || op == 1) ? mf_occupancy(D, op == 1 ? 0 : C, p.mf_rt) : 8;
   if ((op == 0 || op == 1 || op == 3) && lead_blocks > 0) {
     const int64_t slots = (int64_t)num_cus * occupancy;
     const int64_t s_min = ceil_div(N, lowd::kSplitCols);

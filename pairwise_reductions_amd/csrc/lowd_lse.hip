@@ -1,6 +1,7 @@
 // Low-D log-sum-exp reduction ("Kernel matrix reduction", Overview: the reductions include
 // a log-sum-exp over j): out_i = log sum_j exp(-|x_i - y_j|^2 / (2 sigma^2)), with the
-// exponent evaluated as in lowd_sum.hip.
+// exponent evaluated as in lowd_sum.hip. The float64 form of lowd_mfma.hip's matrix-core sweep:
+// it runs when the device-side decision declines the matrix cores.
 #include "lowd_common.h"
 
 namespace keops {
@@ -13,7 +14,9 @@ template <int D, int R, int U>
 __global__ void __launch_bounds__(kBlock)
 lse_kernel(const float* __restrict__ x, const float* __restrict__ y,
            const double* __restrict__ cols, float* __restrict__ out,
-           LsePartial* __restrict__ partial, int64_t M, int64_t N, int64_t cps, double c2) {
+           LsePartial* __restrict__ partial, int64_t M, int64_t N, int64_t cps, double c2,
+           const int* __restrict__ skip) {
+  if (skip[0] && !skip[1]) return;  // the matrix-core sweep takes these inputs
   constexpr int P = (D + 2) & ~1;
   const int64_t split = blockIdx.y;
   const int64_t j0 = split * cps;
@@ -70,8 +73,16 @@ lse_kernel(const float* __restrict__ x, const float* __restrict__ y,
         l[r] *= exp2_hw(-tmax);
         mref[r] += (double)tmax;
         Ap[r] -= (double)tmax;
+        // The float values were rounded relative to the old shift (up to 2^-9 at |e| ~ 2^14):
+        // evaluate the tile again, in float64, relative to the new one.
 #pragma unroll
-        for (int u = 0; u < U; ++u) e32[r][u] -= tmax;
+        for (int u = 0; u < U; ++u) {
+          const double* cj = cols + (j + u) * P;
+          double e = Ap[r] + cj[D];
+#pragma unroll
+          for (int d = 0; d < D; ++d) e = fma(xp[r][d], cj[d], e);
+          e32[r][u] = (float)e;
+        }
       }
       float t = 0.0f;
 #pragma unroll
@@ -91,7 +102,7 @@ lse_kernel(const float* __restrict__ x, const float* __restrict__ y,
         l[r] *= exp2_hw(-e32);
         mref[r] += (double)e32;
         Ap[r] -= (double)e32;
-        e32 = 0.0f;
+        e32 = (float)(e - (double)e32);  // the remainder the float rounding dropped
       }
       l[r] += exp2_hw(e32);
     }
@@ -115,25 +126,29 @@ lse_kernel(const float* __restrict__ x, const float* __restrict__ y,
 
 template <int D>
 hipError_t lse_d(const float* x, const float* y, const double* cols, float* out, double* partial,
-                 int64_t M, int64_t N, double c2, const Plan& p, hipStream_t s) {
+                 int64_t M, int64_t N, double c2, const int* skip, const Plan& p, hipStream_t s) {
   dim3 grid((unsigned)p.row_blocks, (unsigned)p.splits);
   lse_kernel<D, kRowsLse, kLseTile><<<grid, kBlock, 0, s>>>(
-      x, y, cols, out, reinterpret_cast<LsePartial*>(partial), M, N, p.cols_per_split, c2);
+      x, y, cols, out, reinterpret_cast<LsePartial*>(partial), M, N, p.cols_per_split, c2, skip);
   return hipGetLastError();
 }
 
 }  // namespace
 }  // namespace lowd
 
-hipError_t launch_lse_lowd(const float* x, const float* y, const double* cols, float* out, double* partial,
+hipError_t launch_lse_lowd(const float* x, const float* y, double* cols, float* out, double* partial, void* mf,
                            int64_t M, int64_t N, int D, double c2, const Plan& p, hipStream_t s) {
-  hipError_t e;
+  hipError_t e = launch_mf_prepare(x, y, nullptr, cols, mf, M, N, D, 0, c2, s);
+  if (e != hipSuccess) return e;
+  const int* skip = mf_decision(mf);
   {
-#define KEOPS_LSE(Dv) lowd::lse_d<Dv>(x, y, cols, out, partial, M, N, c2, p, s)
+#define KEOPS_LSE(Dv) lowd::lse_d<Dv>(x, y, cols, out, partial, M, N, c2, skip, p, s)
     auto run = [&]() -> hipError_t { KEOPS_SWITCH_D(D, KEOPS_LSE) };
 #undef KEOPS_LSE
     e = run();
   }
+  if (e != hipSuccess) return e;
+  e = launch_mf_lse(out, partial, mf, M, N, D, p, s);
   if (e != hipSuccess || p.splits == 1) return e;
   return lowd::launch_combine_lse(reinterpret_cast<const lowd::LsePartial*>(partial), out, M, p.splits, s);
 }

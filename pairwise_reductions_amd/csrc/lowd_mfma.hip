@@ -205,7 +205,8 @@ __device__ __forceinline__ void store_pieces(half8* __restrict__ dst, const _Flo
 
 // Operand preparation, one thread per row (workgroups [0, rb)) or per column (the rest):
 //   rows     rhi[i] (8 NH fp16), rlo[i] (32 NL fp16), rA[i] = Ah_i
-//   columns  chi[j], clo[j] and bpad[j][c] = b[j][c] for j < Npad (zero past N), and the float64
+//   columns  chi[j], clo[j] and bpad[j][c] = b[j][c] for j < Npad (b = null: no weights; zero past
+//            N; padding columns get an exponent that underflows), and the float64
 //            column table cols[j] = (y_j - y_0, -c2 |y_j - y_0|^2) of the float64 sweep
 // Each workgroup reduces the bounds records and derives the parameters itself (identically);
 // workgroup 0 publishes them. A piece that does not convert exactly sets P->bad.
@@ -293,7 +294,8 @@ mf_prep_kernel(const float* __restrict__ x, const float* __restrict__ y, const f
   } else {
     const int64_t j = ((int64_t)blockIdx.x - rb) * kBlock + threadIdx.x;
     if (j >= Npad) return;
-    for (int c = 0; c < C; ++c) bpad[j * C + c] = j < N ? b[j * C + c] : 0.0f;
+    if (b)
+      for (int c = 0; c < C; ++c) bpad[j * C + c] = j < N ? b[j * C + c] : 0.0f;
     if (j < N) {  // float64 column table
       const int P64 = col_stride(D);
       double s = 0.0;
@@ -335,6 +337,10 @@ mf_prep_kernel(const float* __restrict__ x, const float* __restrict__ y, const f
       hi[D + 1] = piece(Bh - Bh1, sp.sh[kOneBh2], ok);
       lo[5 * D] = piece(1.0, sp.sh[kAl1One], ok);
       lo[5 * D + 1] = piece(rnd(Bv - Bh, sp.gamma - 12), sp.sh[kOneBl1], ok);
+    } else {
+      // padding column: e = A_i - 65504 2^-s, far below every real exponent (those are at least
+      // -2^(gamma+23)), so 2^e is exactly 0 and no reduction sees it
+      hi[D] = (_Float16)-65504.0f;
     }
     store_pieces<NH>(chi + j * NH, hi);
     store_pieces<4 * NL>(clo + j * 4 * NL, lo);
@@ -481,6 +487,127 @@ gauss_sum_mf_kernel(const half8* __restrict__ rhi, const half8* __restrict__ rlo
     }
 }
 
+// out_i = ln sum_j 2^{e_ij} over the columns [j0, j1) of this split with one split, else the
+// split's (m, l) pair. Same tiles and lanes as the sum; per lane and row slot a running shift
+// m (an integer, base 2) and l = sum 2^{e - m} over the lane's columns. m is raised, for every
+// slot of the wave at once, only in a tile where some lane's term would exceed 2^kLseSlack
+// (from -inf in the first tile); the 16 lanes of a row merge their (m, l) at the end.
+template <int RT, int NH, int NL>
+__global__ void __launch_bounds__(kBlock)
+lse_mf_kernel(const half8* __restrict__ rhi, const half8* __restrict__ rlo, const float* __restrict__ rA,
+              const half8* __restrict__ chi, const half8* __restrict__ clo, float* __restrict__ out,
+              LsePartial* __restrict__ partial, const MfParams* __restrict__ P, int64_t M, int64_t N, int64_t cps,
+              int64_t row_blocks, int64_t splits, int64_t pair0) {
+  if (!P->gate || P->bad) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
+  const uint32_t wg = blockIdx.x, total = gridDim.x;
+  const uint32_t per = total / kXcds, extra = total % kXcds, xcd = wg % kXcds;
+  const int64_t pair = pair0 + xcd * per + (xcd < extra ? xcd : extra) + wg / kXcds;
+  const int64_t split = pair / row_blocks;
+  const int64_t j0 = split * cps;
+  const int64_t j1 = (j0 + cps < N) ? j0 + cps : N;
+  const int64_t base = ((int64_t)(pair % row_blocks) * (kBlock / 64) + wave) * 16 * RT;
+  const half8 zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
+
+  half8 ahi[RT], alo[RT][NL];
+  f32x4 cinit[RT];
+  float m[RT][4], l[RT][4];
+#pragma unroll
+  for (int r = 0; r < RT; ++r) {
+    int64_t i = base + r * 16 + l16;
+    i = i < M ? i : M - 1;
+    ahi[r] = g < NH ? rhi[i * NH + g] : zero8;
+#pragma unroll
+    for (int n = 0; n < NL; ++n) alo[r][n] = rlo[i * 4 * NL + n * 4 + g];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      int64_t ii = base + r * 16 + 4 * g + q;
+      ii = ii < M ? ii : M - 1;
+      cinit[r][q] = rA[ii];
+      m[r][q] = -INFINITY;
+      l[r][q] = 0.0f;
+    }
+  }
+  const int ochi = l16 * NH + (g < NH ? g : 0), oclo = l16 * 4 * NL + g;
+  struct Ops {
+    half8 h, l[NL];
+  };
+  auto load = [&](int64_t jt, Ops& o) {
+    const half8* ph = chi + jt * NH;
+    const half8* pl = clo + jt * 4 * NL;
+    o.h = ph[ochi];
+#pragma unroll
+    for (int n = 0; n < NL; ++n) o.l[n] = pl[oclo + 4 * n];
+  };
+  auto tile = [&](const Ops& o) {
+    float e[RT][4], d[RT][4];
+    float dmax = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+      f32x4 t = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[r], o.h, cinit[r], 0, 0, 0);
+#pragma unroll
+      for (int n = 0; n < NL; ++n) t = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[r][n], o.l[n], t, 0, 0, 0);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        e[r][q] = t[q];
+        d[r][q] = t[q] - m[r][q];
+        dmax = fmaxf(dmax, d[r][q]);
+      }
+    }
+    if (__any(dmax > kLseSlack)) {
+#pragma unroll
+      for (int r = 0; r < RT; ++r)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float mn = fmaxf(m[r][q], ceilf(e[r][q]));
+          l[r][q] *= exp2_hw(m[r][q] - mn);
+          m[r][q] = mn;
+          d[r][q] = e[r][q] - mn;
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < RT; ++r)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) l[r][q] += exp2_hw(d[r][q]);
+  };
+  const int64_t ntiles = j1 > j0 ? 2 * ((j1 - j0 + 31) / 32) : 0;
+  Ops A, B;
+  if (ntiles > 0) load(j0, A);
+  for (int64_t t = 0; t < ntiles; t += 2) {
+    const int64_t ja = j0 + t * 16;
+    load(ja + 16, B);
+    tile(A);
+    load(t + 2 < ntiles ? ja + 32 : ja, A);
+    tile(B);
+  }
+  // merge the 16 lanes of each row: m = max, l = sum l 2^(m_lane - m)
+  const bool last = splits == 1;
+#pragma unroll
+  for (int r = 0; r < RT; ++r)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float mm = m[r][q];
+#pragma unroll
+      for (int s = 1; s < 16; s <<= 1) mm = fmaxf(mm, __shfl_xor(mm, s));
+      float ll = m[r][q] == -INFINITY ? 0.0f : l[r][q] * exp2_hw(m[r][q] - mm);
+#pragma unroll
+      for (int s = 1; s < 16; s <<= 1) ll += __shfl_xor(ll, s);
+      const int64_t i = base + r * 16 + 4 * g + q;
+      if (l16 == q && i < M) {
+        if (last) {
+          out[i] = (float)(((double)mm + (double)log2f(ll)) * M_LN2);
+        } else {
+          LsePartial pp;
+          pp.m = (double)mm;
+          pp.l = ll;
+          pp.pad = 0.0f;
+          partial[split * M + i] = pp;
+        }
+      }
+    }
+}
+
 // Byte offsets of the operand region: parameters, bounds records, row operands, column
 // operands, padded weights.
 struct MfLayout {
@@ -575,6 +702,42 @@ hipError_t sweep_c(char* r, const MfLayout& L, float* dst, const float* rscale, 
   return sweep_rt<C, 2, 2>(r, L, dst, rscale, M, N, p, s);
 }
 
+template <int RT, int NH, int NL>
+hipError_t sweep_lse(char* r, const MfLayout& L, float* out, LsePartial* part, int64_t M, int64_t N, const Plan& p,
+                     hipStream_t s) {
+  const int64_t pairs = p.mf_row_blocks * p.splits;
+  for (int64_t pair0 = 0; pair0 < pairs; pair0 += kMaxLaunch) {
+    const int64_t n = pairs - pair0 < kMaxLaunch ? pairs - pair0 : kMaxLaunch;
+    lse_mf_kernel<RT, NH, NL><<<(unsigned)n, kBlock, 0, s>>>(
+        reinterpret_cast<const half8*>(r + L.rhi), reinterpret_cast<const half8*>(r + L.rlo),
+        reinterpret_cast<const float*>(r + L.rA), reinterpret_cast<const half8*>(r + L.chi),
+        reinterpret_cast<const half8*>(r + L.clo), out, part, reinterpret_cast<const MfParams*>(r), M, N,
+        p.cols_per_split, p.mf_row_blocks, p.splits, pair0);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+template <int NH, int NL>
+hipError_t sweep_lse_rt(char* r, const MfLayout& L, float* out, LsePartial* part, int64_t M, int64_t N,
+                        const Plan& p, hipStream_t s) {
+  switch (p.mf_rt) {
+    case 4: return sweep_lse<4, NH, NL>(r, L, out, part, M, N, p, s);
+    case 2: return sweep_lse<2, NH, NL>(r, L, out, part, M, N, p, s);
+    case 1: return sweep_lse<1, NH, NL>(r, L, out, part, M, N, p, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int RT, int NH, int NL>
+int occupancy_lse() {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, lse_mf_kernel<RT, NH, NL>, kBlock, 0) != hipSuccess || n < 1)
+    n = 4;
+  return n;
+}
+
 }  // namespace
 }  // namespace lowd
 
@@ -586,15 +749,20 @@ int mf_rows_per_lane(int C) { return lowd::max_rt(C); }
 
 int mf_occupancy(int D, int C, int rt) {
   // resident workgroups per CU of the sweep instance, from its register use (cached per
-  // instance; 4 when the runtime cannot say)
+  // instance; 4 when the runtime cannot say). C = 0 is the log-sum-exp sweep.
   static std::atomic<int> cache[2][kMaxLowC + 1][5];
   const int wide = lowd::mf_layout(1, 1, D, 1).NH == 2 ? 1 : 0;
   int dev = 0;
-  if (C < 1 || C > kMaxLowC || (rt != 1 && rt != 2 && rt != 4) || hipGetDevice(&dev) != hipSuccess) return 4;
+  if (C < 0 || C > kMaxLowC || (rt != 1 && rt != 2 && rt != 4) || hipGetDevice(&dev) != hipSuccess) return 4;
   std::atomic<int>& slot = cache[wide][C][rt];
   int n = slot.load(std::memory_order_relaxed);
   if (n > 0) return n;
   auto query = [&]() -> int {
+    if (C == 0) {
+      if (rt == 4) return wide ? lowd::occupancy_lse<4, 2, 2>() : lowd::occupancy_lse<4, 1, 1>();
+      if (rt == 2) return wide ? lowd::occupancy_lse<2, 2, 2>() : lowd::occupancy_lse<2, 1, 1>();
+      return wide ? lowd::occupancy_lse<1, 2, 2>() : lowd::occupancy_lse<1, 1, 1>();
+    }
 #define KEOPS_MF_OCC(Cv) lowd::occupancy_c<Cv>(wide != 0, rt)
     switch (C) {
       case 1: return KEOPS_MF_OCC(1);
@@ -639,6 +807,16 @@ hipError_t launch_mf_prepare(const float* x, const float* y, const float* b, dou
     mf_prep_kernel<2, 2><<<(unsigned)(rb + cb), kBlock, 0, s>>>(x, y, b, C, cols, rhi, rlo, rA, chi, clo, bpad, parts,
                                                                (int)nb, M, N, L.Npad, D, c2, rb, P);
   return hipGetLastError();
+}
+
+hipError_t launch_mf_lse(float* out, void* partial, void* region, int64_t M, int64_t N, int D, const Plan& p,
+                         hipStream_t s) {
+  using namespace lowd;
+  char* r = static_cast<char*>(region);
+  const MfLayout L = mf_layout(M, N, D, 0);
+  LsePartial* part = static_cast<LsePartial*>(partial);
+  if (L.NH == 1 && L.NL == 1) return sweep_lse_rt<1, 1>(r, L, out, part, M, N, p, s);
+  return sweep_lse_rt<2, 2>(r, L, out, part, M, N, p, s);
 }
 
 hipError_t launch_mf_sum(const float* rscale, float* dst, void* region, int64_t M, int64_t N, int D, int C,

@@ -108,6 +108,23 @@ def test_gauss_sum_exponent_regimes(D, sigma, lo, hi, outlier):
     assert_normalised(got, want, norm, TOL_F32, "gauss_sum regime")
 
 
+@pytest.mark.parametrize("D,sigma,lo,hi,outlier", EXPONENT_REGIMES)
+def test_lse_exponent_regimes(D, sigma, lo, hi, outlier):
+    import pairwise_reductions_amd as pr
+    _announce("lse_regime", D=D, sigma=sigma, lo=lo, hi=hi, outlier=outlier)
+    M, N = 700, 3001
+    x, y, _ = _rand(int(sigma * 1e4) + 37 * D, M, N, D, 1, lo, hi)
+    rng = np.random.default_rng(D + 1)
+    y[:M] = x + (0.5 * sigma * rng.standard_normal((M, D))).astype(np.float32)
+    if outlier:
+        y[M + 17] = 1000.0
+    sig = float(np.float32(sigma))
+    got = _host(pr.lse(_dev(x), _dev(y), sig)).astype(np.float64)
+    want = oracle.logsumexp_reduction(x, y, sig, workers=8)
+    err = np.abs(got - want)
+    assert np.all(err <= lse_bound(want)), f"lse regime: max error {err.max():.3e}"
+
+
 def test_gauss_sum_workload_10k_all_rows():
     import pairwise_reductions_amd as pr
     inp = workloads.make_inputs("gauss_sum_10k")
