@@ -82,7 +82,7 @@ struct LowdLayout {
   size_t aux_off;               // one double: the largest column norm (argKmin screening)
   size_t part_off, part_bytes;  // per-split partials (argKmin lists for ops 2 and 6)
   size_t lse_off;               // per-split (m, l) pairs of the fused argKmin + LSE (op 6)
-  size_t mf_off;                // Gauss sum and LSE: the matrix-core operand region
+  size_t mf_off;                // Gauss sum, LSE, one-channel gradient: the matrix-core operands
   size_t total;
 };
 
@@ -110,8 +110,11 @@ LowdLayout lowd_layout(int op, int64_t M, int64_t N, int D, int C, int K) {
   }
   L.lse_off = L.part_off + L.part_bytes;
   L.mf_off = L.lse_off + lse_bytes;
-  L.total = L.mf_off + (op == KEOPS_OP_GAUSS_SUM ? keops::mf_region_bytes(M, N, D, C)
-                                               : op == KEOPS_OP_LSE ? keops::mf_region_bytes(M, N, D, 0) : 0);
+  size_t mf = 0;
+  if (op == KEOPS_OP_GAUSS_SUM) mf = keops::mf_region_bytes(M, N, D, C);
+  if (op == KEOPS_OP_LSE) mf = keops::mf_region_bytes(M, N, D, 0);
+  if (op == KEOPS_OP_GAUSS_SUM_GRAD_X && C == 1) mf = keops::mf_region_bytes(M, N, D, 1 + D);
+  L.total = L.mf_off + mf;
   if (M == 0 || N == 0) L.total = 0;
   return L;
 }
@@ -463,14 +466,14 @@ int keops_gauss_sum_backward(const void* x, const void* y, const void* b, const 
   const float inv_sigma2 = (float)(1.0 / (s * s));
   if (want_x) {
     const LowdLayout L = lowd_layout(KEOPS_OP_GAUSS_SUM_GRAD_X, M, N, D, C, 0);
-    KEOPS_HIP(keops::launch_grad_x_lowd(xf, yf, bf, g, grad_x, reinterpret_cast<float*>(ws + L.part_off), M, N, D,
-                                        C, c2f, inv_sigma2, L.plan, stream),
+    KEOPS_HIP(keops::launch_grad_x_lowd(xf, yf, bf, g, grad_x, reinterpret_cast<float*>(ws + L.part_off), ws + L.mf_off,
+                                        M, N, D, C, c2f, inv_sigma2, L.plan, stream),
               "grad_x_lowd");
   }
   if (want_y) {
     const LowdLayout L = lowd_layout(KEOPS_OP_GAUSS_SUM_GRAD_X, N, M, D, C, 0);
-    KEOPS_HIP(keops::launch_grad_x_lowd(yf, xf, g, bf, grad_y, reinterpret_cast<float*>(ws + L.part_off), N, M, D,
-                                        C, c2f, inv_sigma2, L.plan, stream),
+    KEOPS_HIP(keops::launch_grad_x_lowd(yf, xf, g, bf, grad_y, reinterpret_cast<float*>(ws + L.part_off), ws + L.mf_off,
+                                        N, M, D, C, c2f, inv_sigma2, L.plan, stream),
               "grad_y_lowd");
   }
   if (want_b) {
@@ -658,8 +661,10 @@ int keops_gauss_sum_grad_x(const float* x, const float* y, const float* b, const
   const double s = (double)sigma;
   const float c2f = (float)c2_of(sigma);
   const float inv_sigma2 = (float)(1.0 / (s * s));
-  float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.part_off);
-  KEOPS_HIP(keops::launch_grad_x_lowd(x, y, b, g, grad, part, M, N, D, C, c2f, inv_sigma2, L.plan, stream),
+  char* ws = static_cast<char*>(workspace);
+  float* part = reinterpret_cast<float*>(ws + L.part_off);
+  KEOPS_HIP(keops::launch_grad_x_lowd(x, y, b, g, grad, part, ws + L.mf_off, M, N, D, C, c2f, inv_sigma2, L.plan,
+                                      stream),
             "grad_x_lowd");
   return ok();
 }
@@ -697,8 +702,10 @@ int keops_gauss_sum_grad_y(const float* x, const float* y, const float* b, const
   const double s = (double)sigma;
   const float c2f = (float)c2_of(sigma);
   const float inv_sigma2 = (float)(1.0 / (s * s));
-  float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.part_off);
-  KEOPS_HIP(keops::launch_grad_x_lowd(y, x, g, b, grad_y, part, N, M, D, C, c2f, inv_sigma2, L.plan, stream),
+  char* ws = static_cast<char*>(workspace);
+  float* part = reinterpret_cast<float*>(ws + L.part_off);
+  KEOPS_HIP(keops::launch_grad_x_lowd(y, x, g, b, grad_y, part, ws + L.mf_off, N, M, D, C, c2f, inv_sigma2, L.plan,
+                                      stream),
             "grad_y_lowd");
   return ok();
 }

@@ -53,12 +53,15 @@ hipError_t launch_gauss_sum_lowd(const float* x, const float* y, double* cols, c
 // decision, two ints (gate, bad): the matrix-core sweep runs when gate != 0 and bad == 0; row
 // tiles per wave for C channels; preparation (also writes the float64 column table; b may be
 // null) and sweeps.
-size_t mf_region_bytes(int64_t M, int64_t N, int D, int C);
+size_t mf_region_bytes(int64_t M, int64_t N, int D, int W);  // W: floats per column record
 const int* mf_decision(const void* region);
-int mf_rows_per_lane(int C);
-int mf_occupancy(int D, int C, int rt);  // resident workgroups per CU of the matrix-core sweep
-hipError_t launch_mf_prepare(const float* x, const float* y, const float* b, double* cols, void* region,
-                             int64_t M, int64_t N, int D, int C, double c2, hipStream_t s);
+int mf_rows_per_lane(int op, int D, int C);   // op: 0 sum, 1 log-sum-exp, 3 gradient
+int mf_occupancy(int op, int D, int C, int rt);  // resident workgroups per CU of that sweep
+hipError_t launch_mf_prepare(const float* x, const float* y, const float* b, bool with_y, double* cols,
+                             void* region, int64_t M, int64_t N, int D, int C, double c2, hipStream_t s);
+// gradient with respect to x, one channel: dst[i][d] = -(g_i / sigma^2) sum_j k_ij b_j (x_i - y_j)
+hipError_t launch_mf_grad(const float* x, const float* g, float* dst, float inv_sigma2, void* region,
+                          int64_t M, int64_t N, int D, const Plan& p, hipStream_t s);
 hipError_t launch_mf_sum(const float* rscale, float* dst, void* region, int64_t M, int64_t N, int D,
                          int C, const Plan& p, hipStream_t s);
 // log-sum-exp on the matrix cores: out (one split) or per-split (m, l) pairs in `partial`
@@ -76,8 +79,10 @@ hipError_t launch_knn_lowd(const float* x, const float* y, const float* w, doubl
                            int32_t* idx, float* dist, void* partial, float* lse_out,
                            double* lse_partial, int64_t M, int64_t N, int D, int K, double c2,
                            bool with_lse, const Plan& p, hipStream_t s);
+// Gradient with respect to x (float32 sweep; with C = 1 the matrix-core sweep, prepared in `mf`,
+// takes it when the device-side decision admits the inputs).
 hipError_t launch_grad_x_lowd(const float* x, const float* y, const float* b, const float* g,
-                              float* grad, float* partial, int64_t M, int64_t N, int D, int C,
+                              float* grad, float* partial, void* mf, int64_t M, int64_t N, int D, int C,
                               float c2f, float inv_sigma2, const Plan& p, hipStream_t s);
 hipError_t launch_fill(float* out, int64_t n, float value, hipStream_t s);
 // Element-wise steps: out[j][c] = scale[j] b[j][c]; out = in^e; out = p / sqrt(d).

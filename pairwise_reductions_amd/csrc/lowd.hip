@@ -127,14 +127,15 @@ Plan plan_lowd(int op, int64_t M, int64_t N, int D, int C, int K, int num_cus) {
   }
   p.rows_per_block = kBlock * p.R;
   p.row_blocks = M > 0 ? ceil_div(M, p.rows_per_block) : 0;
-  // The Gauss sum's and the log-sum-exp's matrix-core sweeps take 16 RT rows per wave; the
-  // column splits are planned for them (the float64 sweeps, which run only when the matrix-core
-  // ones decline, share them).
+  // The matrix-core sweeps (Gauss sum, log-sum-exp, one-channel gradient) take 16 RT rows per
+  // wave; the column splits are planned for them (the float64 / float32 sweeps, which run only
+  // when the matrix-core ones decline, share them).
   int64_t lead_blocks = p.row_blocks;
   int64_t granule = 8;
-  if (op == 0 || op == 1) {
+  const bool mf = op == 0 || op == 1 || (op == 3 && C == 1);
+  if (mf) {
     const int64_t max_cols_splits = N / 256 > 1 ? N / 256 : 1;
-    int rt = mf_rows_per_lane(op == 1 ? 0 : C);
+    int rt = mf_rows_per_lane(op, D, C);
     while (rt > 1 && ceil_div(M, (int64_t)64 * rt) * max_cols_splits < (int64_t)num_cus * 4) rt /= 2;
     p.mf_rt = rt;
     p.mf_row_blocks = M > 0 ? ceil_div(M, (int64_t)64 * rt) : 0;
@@ -168,7 +169,7 @@ Plan plan_lowd(int op, int64_t M, int64_t N, int D, int C, int K, int num_cus) {
   // whole workgroup's duration. Among split counts between half and twice the one above
   // (keeping the L2 bound), take the one whose workgroups fill their rounds best.
   // resident workgroups per CU (register budgets)
-  const int occupancy = (op == 0 || op == 1) ? mf_occupancy(D, op == 1 ? 0 : C, p.mf_rt) : 8;
+  const int occupancy = mf ? mf_occupancy(op, D, C, p.mf_rt) : 8;
   if ((op == 0 || op == 1 || op == 3) && lead_blocks > 0) {
     const int64_t slots = (int64_t)num_cus * occupancy;
     const int64_t s_min = ceil_div(N, lowd::kSplitCols);

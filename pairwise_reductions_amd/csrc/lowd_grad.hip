@@ -14,7 +14,8 @@ template <int D, int C, int R>
 __global__ void __launch_bounds__(kBlock)
 grad_x_kernel(const float* __restrict__ x, const float* __restrict__ y, const float* __restrict__ b,
               const float* __restrict__ g, float* __restrict__ out, int64_t M, int64_t N,
-              int64_t cps, float c2f, float inv_sigma2) {
+              int64_t cps, float c2f, float inv_sigma2, const int* __restrict__ skip) {
+  if (skip && skip[0] && !skip[1]) return;  // the matrix-core sweep takes these inputs
   const int64_t split = blockIdx.y;
   const int64_t j0 = split * cps;
   const int64_t j1 = (j0 + cps < N) ? j0 + cps : N;
@@ -90,43 +91,50 @@ grad_x_kernel(const float* __restrict__ x, const float* __restrict__ y, const fl
 
 template <int D, int C>
 hipError_t grad_dc(const float* x, const float* y, const float* b, const float* g, float* dst,
-                   int64_t M, int64_t N, float c2f, float inv_sigma2, const Plan& p, hipStream_t s) {
+                   int64_t M, int64_t N, float c2f, float inv_sigma2, const int* skip, const Plan& p,
+                   hipStream_t s) {
   dim3 grid((unsigned)p.row_blocks, (unsigned)p.splits);
-  grad_x_kernel<D, C, kRowsGrad><<<grid, kBlock, 0, s>>>(x, y, b, g, dst, M, N, p.cols_per_split, c2f, inv_sigma2);
+  grad_x_kernel<D, C, kRowsGrad><<<grid, kBlock, 0, s>>>(x, y, b, g, dst, M, N, p.cols_per_split, c2f, inv_sigma2,
+                                                         skip);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t grad_d(int C, const float* x, const float* y, const float* b, const float* g, float* dst,
-                  int64_t M, int64_t N, float c2f, float inv_sigma2, const Plan& p, hipStream_t s) {
-  switch (C) {
-    case 1: return grad_dc<D, 1>(x, y, b, g, dst, M, N, c2f, inv_sigma2, p, s);
-    case 2: return grad_dc<D, 2>(x, y, b, g, dst, M, N, c2f, inv_sigma2, p, s);
-    case 3: return grad_dc<D, 3>(x, y, b, g, dst, M, N, c2f, inv_sigma2, p, s);
-    case 4: return grad_dc<D, 4>(x, y, b, g, dst, M, N, c2f, inv_sigma2, p, s);
-    case 5: return grad_dc<D, 5>(x, y, b, g, dst, M, N, c2f, inv_sigma2, p, s);
-    case 6: return grad_dc<D, 6>(x, y, b, g, dst, M, N, c2f, inv_sigma2, p, s);
-    case 7: return grad_dc<D, 7>(x, y, b, g, dst, M, N, c2f, inv_sigma2, p, s);
-    case 8: return grad_dc<D, 8>(x, y, b, g, dst, M, N, c2f, inv_sigma2, p, s);
-  }
-  return hipErrorInvalidValue;
+                  int64_t M, int64_t N, float c2f, float inv_sigma2, const int* skip, const Plan& p,
+                  hipStream_t s) {
+#define KEOPS_GR_C(Cv) grad_dc<D, Cv>(x, y, b, g, dst, M, N, c2f, inv_sigma2, skip, p, s)
+  KEOPS_SWITCH_C(C, KEOPS_GR_C)
+#undef KEOPS_GR_C
 }
 
 }  // namespace
 }  // namespace lowd
 
 hipError_t launch_grad_x_lowd(const float* x, const float* y, const float* b, const float* g, float* grad,
-                              float* partial, int64_t M, int64_t N, int D, int C, float c2f,
+                              float* partial, void* mf, int64_t M, int64_t N, int D, int C, float c2f,
                               float inv_sigma2, const Plan& p, hipStream_t s) {
   float* dst = p.splits > 1 ? partial : grad;
-  hipError_t e;
+  hipError_t e = hipSuccess;
+  const int* skip = nullptr;
+  if (C == 1) {
+    // the matrix-core sweep's operands: row and column pieces, (b_j, y_j) per column
+    e = launch_mf_prepare(x, y, b, true, nullptr, mf, M, N, D, 1, (double)c2f, s);
+    if (e != hipSuccess) return e;
+    skip = mf_decision(mf);
+  }
   {
-#define KEOPS_GR(Dv) lowd::grad_d<Dv>(C, x, y, b, g, dst, M, N, c2f, inv_sigma2, p, s)
+#define KEOPS_GR(Dv) lowd::grad_d<Dv>(C, x, y, b, g, dst, M, N, c2f, inv_sigma2, skip, p, s)
     auto run = [&]() -> hipError_t { KEOPS_SWITCH_D(D, KEOPS_GR) };
 #undef KEOPS_GR
     e = run();
   }
-  if (e != hipSuccess || p.splits == 1) return e;
+  if (e != hipSuccess) return e;
+  if (C == 1) {
+    e = launch_mf_grad(x, g, dst, inv_sigma2, mf, M, N, D, p, s);
+    if (e != hipSuccess) return e;
+  }
+  if (p.splits == 1) return e;
   const int64_t n = M * D;
   return lowd::launch_combine_sum(partial, grad, n, p.splits, nullptr, 1, s);
 }

@@ -138,7 +138,7 @@ hipError_t lse_d(const float* x, const float* y, const double* cols, float* out,
 
 hipError_t launch_lse_lowd(const float* x, const float* y, double* cols, float* out, double* partial, void* mf,
                            int64_t M, int64_t N, int D, double c2, const Plan& p, hipStream_t s) {
-  hipError_t e = launch_mf_prepare(x, y, nullptr, cols, mf, M, N, D, 0, c2, s);
+  hipError_t e = launch_mf_prepare(x, y, nullptr, false, cols, mf, M, N, D, 0, c2, s);
   if (e != hipSuccess) return e;
   const int* skip = mf_decision(mf);
   {

@@ -205,15 +205,16 @@ __device__ __forceinline__ void store_pieces(half8* __restrict__ dst, const _Flo
 
 // Operand preparation, one thread per row (workgroups [0, rb)) or per column (the rest):
 //   rows     rhi[i] (8 NH fp16), rlo[i] (32 NL fp16), rA[i] = Ah_i
-//   columns  chi[j], clo[j] and bpad[j][c] = b[j][c] for j < Npad (b = null: no weights; zero past
-//            N; padding columns get an exponent that underflows), and the float64
+//   columns  chi[j], clo[j] and bpad[j] = (b[j][0..C), with_y: y[j][0..D)) for j < Npad (b = null:
+//            no weights; zero past N; padding columns get an exponent that underflows), and
+//            (cols not null) the float64
 //            column table cols[j] = (y_j - y_0, -c2 |y_j - y_0|^2) of the float64 sweep
 // Each workgroup reduces the bounds records and derives the parameters itself (identically);
 // workgroup 0 publishes them. A piece that does not convert exactly sets P->bad.
 template <int NH, int NL>
 __global__ void __launch_bounds__(kBlock)
 mf_prep_kernel(const float* __restrict__ x, const float* __restrict__ y, const float* __restrict__ b, int C,
-               double* __restrict__ cols, half8* __restrict__ rhi, half8* __restrict__ rlo, float* __restrict__ rA,
+               int with_y, double* __restrict__ cols, half8* __restrict__ rhi, half8* __restrict__ rlo, float* __restrict__ rA,
                half8* __restrict__ chi, half8* __restrict__ clo, float* __restrict__ bpad,
                const unsigned int* __restrict__ parts, int nparts, int64_t M, int64_t N, int64_t Npad, int D,
                double c2, int64_t rb, MfParams* __restrict__ P) {
@@ -294,9 +295,12 @@ mf_prep_kernel(const float* __restrict__ x, const float* __restrict__ y, const f
   } else {
     const int64_t j = ((int64_t)blockIdx.x - rb) * kBlock + threadIdx.x;
     if (j >= Npad) return;
+    const int W = C + (with_y ? D : 0);
     if (b)
-      for (int c = 0; c < C; ++c) bpad[j * C + c] = j < N ? b[j * C + c] : 0.0f;
-    if (j < N) {  // float64 column table
+      for (int c = 0; c < C; ++c) bpad[j * W + c] = j < N ? b[j * C + c] : 0.0f;
+    if (with_y)
+      for (int d = 0; d < D; ++d) bpad[j * W + C + d] = j < N ? y[j * D + d] : 0.0f;
+    if (cols && j < N) {  // float64 column table
       const int P64 = col_stride(D);
       double s = 0.0;
       for (int d = 0; d < D; ++d) {
@@ -608,6 +612,132 @@ lse_mf_kernel(const half8* __restrict__ rhi, const half8* __restrict__ rlo, cons
     }
 }
 
+// Gradient with respect to x, one channel ("Kernel Operations on the GPU, with Autodiff, without
+// Memory Overflows": the derivative of a reduction is a reduction over the same pairs):
+//   out_i = -(g_i / sigma^2) sum_j k_ij b_j (x_i - y_j)
+// k_ij from the matrix-core exponent as in the sum; the differences are taken per pair in
+// float32 from the original coordinates (no x_i sum - sum y cancellation). bw[j] = (b_j, y_j).
+// Lanes keep per-column partials for their 4 rows per tile, folded every kChunk columns and
+// across the 16 lanes of a row at the end.
+template <int D, int RT, int NH, int NL>
+__global__ void __launch_bounds__(kBlock)
+grad_mf_kernel(const half8* __restrict__ rhi, const half8* __restrict__ rlo, const float* __restrict__ rA,
+               const half8* __restrict__ chi, const half8* __restrict__ clo, const float* __restrict__ bw,
+               const float* __restrict__ x, const float* __restrict__ g, float* __restrict__ out, float inv_sigma2,
+               const MfParams* __restrict__ P, int64_t M, int64_t N, int64_t cps, int64_t row_blocks,
+               int64_t splits, int64_t pair0) {
+  if (!P->gate || P->bad) return;
+  constexpr int W = 1 + D;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l16 = lane & 15, g4 = lane >> 4;
+  const uint32_t wg = blockIdx.x, total = gridDim.x;
+  const uint32_t per = total / kXcds, extra = total % kXcds, xcd = wg % kXcds;
+  const int64_t pair = pair0 + xcd * per + (xcd < extra ? xcd : extra) + wg / kXcds;
+  const int64_t split = pair / row_blocks;
+  const int64_t j0 = split * cps;
+  const int64_t j1 = (j0 + cps < N) ? j0 + cps : N;
+  const int64_t base = ((int64_t)(pair % row_blocks) * (kBlock / 64) + wave) * 16 * RT;
+  const half8 zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
+
+  half8 ahi[RT], alo[RT][NL];
+  f32x4 cinit[RT];
+  float xr[RT][4][D], acc[RT][4][D], part[RT][4][D];
+#pragma unroll
+  for (int r = 0; r < RT; ++r) {
+    int64_t i = base + r * 16 + l16;
+    i = i < M ? i : M - 1;
+    ahi[r] = g4 < NH ? rhi[i * NH + g4] : zero8;
+#pragma unroll
+    for (int n = 0; n < NL; ++n) alo[r][n] = rlo[i * 4 * NL + n * 4 + g4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      int64_t ii = base + r * 16 + 4 * g4 + q;
+      ii = ii < M ? ii : M - 1;
+      cinit[r][q] = rA[ii];
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        xr[r][q][d] = x[ii * D + d];
+        acc[r][q][d] = part[r][q][d] = 0.0f;
+      }
+    }
+  }
+  const int ochi = l16 * NH + (g4 < NH ? g4 : 0), oclo = l16 * 4 * NL + g4, ow = l16 * W;
+  struct Ops {
+    half8 h, l[NL];
+    float w[W];
+  };
+  auto load = [&](int64_t jt, Ops& o) {
+    const half8* ph = chi + jt * NH;
+    const half8* pl = clo + jt * 4 * NL;
+    const float* pw = bw + jt * W;
+    o.h = ph[ochi];
+#pragma unroll
+    for (int n = 0; n < NL; ++n) o.l[n] = pl[oclo + 4 * n];
+#pragma unroll
+    for (int c = 0; c < W; ++c) o.w[c] = pw[ow + c];
+  };
+  auto tile = [&](const Ops& o) {
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+      f32x4 e = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[r], o.h, cinit[r], 0, 0, 0);
+#pragma unroll
+      for (int n = 0; n < NL; ++n) e = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[r][n], o.l[n], e, 0, 0, 0);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float kw = exp2_hw(e[q]) * o.w[0];
+#pragma unroll
+        for (int d = 0; d < D; ++d) part[r][q][d] = fmaf(kw, xr[r][q][d] - o.w[1 + d], part[r][q][d]);
+      }
+    }
+  };
+  const int64_t ntiles = j1 > j0 ? 2 * ((j1 - j0 + 31) / 32) : 0;
+  Ops A, B;
+  if (ntiles > 0) load(j0, A);
+  int tiles = 0;
+  for (int64_t t = 0; t < ntiles; t += 2) {
+    const int64_t ja = j0 + t * 16;
+    load(ja + 16, B);
+    tile(A);
+    load(t + 2 < ntiles ? ja + 32 : ja, A);
+    tile(B);
+    tiles += 2;
+    if (tiles == kChunkTiles) {
+      tiles = 0;
+#pragma unroll
+      for (int r = 0; r < RT; ++r)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int d = 0; d < D; ++d) {
+            acc[r][q][d] += part[r][q][d];
+            part[r][q][d] = 0.0f;
+          }
+    }
+  }
+  float* dst = out + split * M * D;
+#pragma unroll
+  for (int r = 0; r < RT; ++r)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float v[D];
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        float t = acc[r][q][d] + part[r][q][d];
+        t += __shfl_xor(t, 1);
+        t += __shfl_xor(t, 2);
+        t += __shfl_xor(t, 4);
+        t += __shfl_xor(t, 8);
+        v[d] = t;
+      }
+      const int64_t i = base + r * 16 + 4 * g4 + q;
+      if (l16 == q && i < M) {
+        const float sc = -inv_sigma2 * g[i];
+#pragma unroll
+        for (int d = 0; d < D; ++d) dst[i * D + d] = sc * v[d];
+      }
+    }
+}
+
 // Byte offsets of the operand region: parameters, bounds records, row operands, column
 // operands, padded weights.
 struct MfLayout {
@@ -616,7 +746,8 @@ struct MfLayout {
   size_t parts, rhi, rlo, rA, chi, clo, bpad, total;
 };
 
-MfLayout mf_layout(int64_t M, int64_t N, int D, int C) {
+// W: floats per padded column record (the weights, and for the gradient also y_j)
+MfLayout mf_layout(int64_t M, int64_t N, int D, int W) {
   MfLayout L;
   L.NH = (D + 2 <= 8) ? 1 : 2;
   L.NL = (5 * D + 2 <= 32) ? 1 : 2;
@@ -635,7 +766,7 @@ MfLayout mf_layout(int64_t M, int64_t N, int D, int C) {
   L.clo = off;
   off += align_up((size_t)L.Npad * 64 * L.NL);
   L.bpad = off;
-  off += align_up((size_t)L.Npad * C * sizeof(float));
+  off += align_up((size_t)L.Npad * W * sizeof(float));
   L.total = off;
   return L;
 }
@@ -738,22 +869,84 @@ int occupancy_lse() {
   return n;
 }
 
+// Row tiles per wave of the gradient sweep: the per-row coordinates and accumulators take
+// 12 D registers per tile.
+constexpr int grad_rt(int D) { return D <= 4 ? 2 : 1; }
+
+template <int D>
+hipError_t sweep_grad(char* r, const MfLayout& L, const float* x, const float* g, float* dst, float inv_sigma2,
+                      int64_t M, int64_t N, const Plan& p, hipStream_t s) {
+  const int64_t pairs = p.mf_row_blocks * p.splits;
+  for (int64_t pair0 = 0; pair0 < pairs; pair0 += kMaxLaunch) {
+    const int64_t n = pairs - pair0 < kMaxLaunch ? pairs - pair0 : kMaxLaunch;
+#define KEOPS_MF_GRAD_LAUNCH(NHv)                                                                            \
+  grad_mf_kernel<D, grad_rt(D), NHv, NHv><<<(unsigned)n, kBlock, 0, s>>>(                                    \
+      reinterpret_cast<const half8*>(r + L.rhi), reinterpret_cast<const half8*>(r + L.rlo),                   \
+      reinterpret_cast<const float*>(r + L.rA), reinterpret_cast<const half8*>(r + L.chi),                    \
+      reinterpret_cast<const half8*>(r + L.clo), reinterpret_cast<const float*>(r + L.bpad), x, g, dst,       \
+      inv_sigma2, reinterpret_cast<const MfParams*>(r), M, N, p.cols_per_split, p.mf_row_blocks, p.splits, pair0)
+    if (L.NH == 1 && L.NL == 1)
+      KEOPS_MF_GRAD_LAUNCH(1);
+    else
+      KEOPS_MF_GRAD_LAUNCH(2);
+#undef KEOPS_MF_GRAD_LAUNCH
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+template <int D>
+int occupancy_grad(bool wide) {
+  int n = 0;
+  const hipError_t e = wide ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, grad_mf_kernel<D, grad_rt(D), 2, 2>,
+                                                                            kBlock, 0)
+                            : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, grad_mf_kernel<D, grad_rt(D), 1, 1>,
+                                                                            kBlock, 0);
+  return (e != hipSuccess || n < 1) ? 4 : n;
+}
+
 }  // namespace
 }  // namespace lowd
 
-size_t mf_region_bytes(int64_t M, int64_t N, int D, int C) { return lowd::mf_layout(M, N, D, C).total; }
+size_t mf_region_bytes(int64_t M, int64_t N, int D, int W) { return lowd::mf_layout(M, N, D, W).total; }
 
 const int* mf_decision(const void* region) { return &static_cast<const lowd::MfParams*>(region)->gate; }
 
-int mf_rows_per_lane(int C) { return lowd::max_rt(C); }
+int mf_rows_per_lane(int op, int D, int C) {
+  if (op == 3) return lowd::grad_rt(D);
+  return lowd::max_rt(op == 1 ? 0 : C);
+}
 
-int mf_occupancy(int D, int C, int rt) {
+int mf_occupancy(int op, int D, int C, int rt) {
   // resident workgroups per CU of the sweep instance, from its register use (cached per
-  // instance; 4 when the runtime cannot say). C = 0 is the log-sum-exp sweep.
+  // instance; 4 when the runtime cannot say)
   static std::atomic<int> cache[2][kMaxLowC + 1][5];
+  static std::atomic<int> cache_grad[kMaxLowD + 1];
   const int wide = lowd::mf_layout(1, 1, D, 1).NH == 2 ? 1 : 0;
   int dev = 0;
-  if (C < 0 || C > kMaxLowC || (rt != 1 && rt != 2 && rt != 4) || hipGetDevice(&dev) != hipSuccess) return 4;
+  if (op == 1) C = 0;  // the log-sum-exp sweep
+  if (D < 1 || D > kMaxLowD || C < 0 || C > kMaxLowC || (rt != 1 && rt != 2 && rt != 4) ||
+      hipGetDevice(&dev) != hipSuccess)
+    return 4;
+  if (op == 3) {
+    int n = cache_grad[D].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+#define KEOPS_MF_OG(Dv) n = lowd::occupancy_grad<Dv>(wide != 0)
+    switch (D) {
+      case 1: KEOPS_MF_OG(1); break;
+      case 2: KEOPS_MF_OG(2); break;
+      case 3: KEOPS_MF_OG(3); break;
+      case 4: KEOPS_MF_OG(4); break;
+      case 5: KEOPS_MF_OG(5); break;
+      case 6: KEOPS_MF_OG(6); break;
+      case 7: KEOPS_MF_OG(7); break;
+      case 8: KEOPS_MF_OG(8); break;
+    }
+#undef KEOPS_MF_OG
+    cache_grad[D].store(n, std::memory_order_relaxed);
+    return n;
+  }
   std::atomic<int>& slot = cache[wide][C][rt];
   int n = slot.load(std::memory_order_relaxed);
   if (n > 0) return n;
@@ -782,11 +975,11 @@ int mf_occupancy(int D, int C, int rt) {
   return n;
 }
 
-hipError_t launch_mf_prepare(const float* x, const float* y, const float* b, double* cols, void* region, int64_t M,
-                             int64_t N, int D, int C, double c2, hipStream_t s) {
+hipError_t launch_mf_prepare(const float* x, const float* y, const float* b, bool with_y, double* cols, void* region,
+                             int64_t M, int64_t N, int D, int C, double c2, hipStream_t s) {
   using namespace lowd;
   char* r = static_cast<char*>(region);
-  const MfLayout L = mf_layout(M, N, D, C);
+  const MfLayout L = mf_layout(M, N, D, C + (with_y ? D : 0));
   MfParams* P = reinterpret_cast<MfParams*>(r);
   unsigned int* parts = reinterpret_cast<unsigned int*>(r + L.parts);
   const int64_t n = M > N ? M : N;
@@ -801,11 +994,11 @@ hipError_t launch_mf_prepare(const float* x, const float* y, const float* b, dou
   half8* clo = reinterpret_cast<half8*>(r + L.clo);
   float* bpad = reinterpret_cast<float*>(r + L.bpad);
   if (L.NH == 1 && L.NL == 1)
-    mf_prep_kernel<1, 1><<<(unsigned)(rb + cb), kBlock, 0, s>>>(x, y, b, C, cols, rhi, rlo, rA, chi, clo, bpad, parts,
-                                                               (int)nb, M, N, L.Npad, D, c2, rb, P);
+    mf_prep_kernel<1, 1><<<(unsigned)(rb + cb), kBlock, 0, s>>>(x, y, b, C, with_y ? 1 : 0, cols, rhi, rlo, rA, chi,
+                                                               clo, bpad, parts, (int)nb, M, N, L.Npad, D, c2, rb, P);
   else
-    mf_prep_kernel<2, 2><<<(unsigned)(rb + cb), kBlock, 0, s>>>(x, y, b, C, cols, rhi, rlo, rA, chi, clo, bpad, parts,
-                                                               (int)nb, M, N, L.Npad, D, c2, rb, P);
+    mf_prep_kernel<2, 2><<<(unsigned)(rb + cb), kBlock, 0, s>>>(x, y, b, C, with_y ? 1 : 0, cols, rhi, rlo, rA, chi,
+                                                               clo, bpad, parts, (int)nb, M, N, L.Npad, D, c2, rb, P);
   return hipGetLastError();
 }
 
@@ -817,6 +1010,16 @@ hipError_t launch_mf_lse(float* out, void* partial, void* region, int64_t M, int
   LsePartial* part = static_cast<LsePartial*>(partial);
   if (L.NH == 1 && L.NL == 1) return sweep_lse_rt<1, 1>(r, L, out, part, M, N, p, s);
   return sweep_lse_rt<2, 2>(r, L, out, part, M, N, p, s);
+}
+
+hipError_t launch_mf_grad(const float* x, const float* g, float* dst, float inv_sigma2, void* region, int64_t M,
+                          int64_t N, int D, const Plan& p, hipStream_t s) {
+  using namespace lowd;
+  char* r = static_cast<char*>(region);
+  const MfLayout L = mf_layout(M, N, D, 1 + D);
+#define KEOPS_MF_G(Dv) sweep_grad<Dv>(r, L, x, g, dst, inv_sigma2, M, N, p, s)
+  KEOPS_SWITCH_D(D, KEOPS_MF_G)
+#undef KEOPS_MF_G
 }
 
 hipError_t launch_mf_sum(const float* rscale, float* dst, void* region, int64_t M, int64_t N, int D, int C,

@@ -124,7 +124,7 @@ hipError_t launch_gauss_sum_lowd(const float* x, const float* y, double* cols, c
                                  const Plan& p, hipStream_t s) {
   float* dst = p.splits > 1 ? partial : out;
   // Operands of both sweeps and the device-side choice between them.
-  hipError_t e = launch_mf_prepare(x, y, b, cols, mf, M, N, D, C, c2, s);
+  hipError_t e = launch_mf_prepare(x, y, b, false, cols, mf, M, N, D, C, c2, s);
   if (e != hipSuccess) return e;
   const int* gate = mf_decision(mf);
   auto run = [&]() -> hipError_t {

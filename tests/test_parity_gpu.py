@@ -248,6 +248,30 @@ def test_grad_x_shapes(M, N, D, C, sigma):
     assert_normalised(got, want, norm, TOL_F32, "grad_x")
 
 
+@pytest.mark.parametrize("D,sigma,lo,hi,outlier", EXPONENT_REGIMES)
+def test_grad_xy_exponent_regimes(D, sigma, lo, hi, outlier):
+    """One-channel gradients on both sides of the matrix-core / float32 decision. Every x has a
+    y within about sigma and every y an x (both gradients then have rows whose kernel values
+    stay in float32 range; a row with none underflows to 0 by reading 10)."""
+    import pairwise_reductions_amd as pr
+    _announce("grad_regime", D=D, sigma=sigma, lo=lo, hi=hi, outlier=outlier)
+    M = N = 1501
+    x, y, b = _rand(int(sigma * 1e4) + 41 * D, M, N, D, 1, lo, hi)
+    rng = np.random.default_rng(D + 2)
+    y[:] = x[rng.permutation(M)] + (0.5 * sigma * rng.standard_normal((N, D))).astype(np.float32)
+    if outlier:
+        y[17] = 1000.0
+        x[17] = 1000.02
+    g = rng.standard_normal((M, 1)).astype(np.float32)
+    sig = float(np.float32(sigma))
+    got = _host(pr.gauss_sum_grad_x(_dev(x), _dev(y), _dev(b), _dev(g), sig))
+    want, norm = oracle.gauss_sum_grad_x(x, y, b, g, sig, workers=8)
+    assert_normalised(got, want, norm, TOL_F32, "grad_x regime")
+    got = _host(pr.gauss_sum_grad_y(_dev(x), _dev(y), _dev(b), _dev(g), sig))
+    want, norm = oracle.gauss_sum_grad_y(x, y, b, g, sig, workers=8)
+    assert_normalised(got, want, norm, TOL_F32, "grad_y regime")
+
+
 def test_grad_x_of_squared_loss_mixture():
     """The KeOps example's loss sum_i a_i^2 on the 8-cluster mixture: the upstream gradient
     is g = 2 s with s the oracle's forward, rounded to float32 for both sides."""
