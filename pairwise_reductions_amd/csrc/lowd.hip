@@ -142,11 +142,12 @@ Plan plan_lowd(int op, int64_t M, int64_t N, int D, int C, int K, int num_cus) {
     lead_blocks = p.mf_row_blocks;
     granule = 32;
   }
-  // Split the columns so that (a) there are at least eight workgroups (32 wave64s) per compute
-  // unit over the launch, and (b) one split's column table stays within lowd::kSplitCols columns,
-  // a working set that fits one XCD's L2 while the resident workgroups (consecutive row
-  // blocks of the same split) stream it together. Every split keeps >= 256 columns.
-  const int64_t target = (int64_t)num_cus * 8;
+  // Split the columns so that (a) there are at least lowd::wg_per_cu(op, C) workgroups per
+  // compute unit over the launch, and (b) one split's column table stays within
+  // lowd::kSplitCols columns, a working set that fits one XCD's L2 while the resident
+  // workgroups (consecutive row blocks of the same split) stream it together. Every split
+  // keeps >= 256 columns.
+  const int64_t target = (int64_t)num_cus * lowd::wg_per_cu(op, C);
   int64_t S = 1;
   if (lead_blocks > 0 && lead_blocks < target) S = ceil_div(target, lead_blocks);
   if (S < ceil_div(N, lowd::kSplitCols)) S = ceil_div(N, lowd::kSplitCols);
