@@ -496,6 +496,12 @@ gauss_sum_mf_kernel(const half8* __restrict__ rhi, const half8* __restrict__ rlo
 // m (an integer, base 2) and l = sum 2^{e - m} over the lane's columns. m is raised, for every
 // slot of the wave at once, only in a tile where some lane's term would exceed 2^kLseSlack
 // (from -inf in the first tile); the 16 lanes of a row merge their (m, l) at the end.
+// A slot is settled once m >= kLseSettled (-64): the exponent is never positive (its computed
+// value exceeds 0 by a rounding far below 1), so the plain terms 2^e cannot overflow, and the
+// ones that underflow float32 (below 2^-126) are negligible against the row's largest term
+// (at least 2^(m - 1) >= 2^-65). Once every slot of the wave is settled, the loop adds the
+// plain terms into a second sum (no shift, no test) and folds it in at the end as
+// l + lraw 2^-m (m an integer: exact scaling; at most 2^31 terms times 2^64 stays finite).
 template <int RT, int NH, int NL>
 __global__ void __launch_bounds__(kBlock)
 lse_mf_kernel(const half8* __restrict__ rhi, const half8* __restrict__ rlo, const float* __restrict__ rA,
@@ -516,7 +522,7 @@ lse_mf_kernel(const half8* __restrict__ rhi, const half8* __restrict__ rlo, cons
 
   half8 ahi[RT], alo[RT][NL];
   f32x4 cinit[RT];
-  float m[RT][4], l[RT][4];
+  float m[RT][4], l[RT][4], lraw[RT][4];
 #pragma unroll
   for (int r = 0; r < RT; ++r) {
     int64_t i = base + r * 16 + l16;
@@ -530,7 +536,7 @@ lse_mf_kernel(const half8* __restrict__ rhi, const half8* __restrict__ rlo, cons
       ii = ii < M ? ii : M - 1;
       cinit[r][q] = rA[ii];
       m[r][q] = -INFINITY;
-      l[r][q] = 0.0f;
+      l[r][q] = lraw[r][q] = 0.0f;
     }
   }
   const int ochi = l16 * NH + (g < NH ? g : 0), oclo = l16 * 4 * NL + g;
@@ -575,15 +581,50 @@ lse_mf_kernel(const half8* __restrict__ rhi, const half8* __restrict__ rlo, cons
 #pragma unroll
       for (int q = 0; q < 4; ++q) l[r][q] += exp2_hw(d[r][q]);
   };
+  auto tile_settled = [&](const Ops& o) {
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+      f32x4 t = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[r], o.h, cinit[r], 0, 0, 0);
+#pragma unroll
+      for (int n = 0; n < NL; ++n) t = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[r][n], o.l[n], t, 0, 0, 0);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) lraw[r][q] += exp2_hw(t[q]);
+    }
+  };
+  constexpr float kLseSettled = -64.0f;
+  auto all_settled = [&]() {
+    bool ok = true;
+#pragma unroll
+    for (int r = 0; r < RT; ++r)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) ok = ok && m[r][q] >= kLseSettled;
+    return __all(ok);
+  };
   const int64_t ntiles = j1 > j0 ? 2 * ((j1 - j0 + 31) / 32) : 0;
   Ops A, B;
   if (ntiles > 0) load(j0, A);
-  for (int64_t t = 0; t < ntiles; t += 2) {
+  bool settled = false;
+  int64_t t = 0;
+  for (; t < ntiles && !settled; t += 2) {
     const int64_t ja = j0 + t * 16;
     load(ja + 16, B);
     tile(A);
     load(t + 2 < ntiles ? ja + 32 : ja, A);
     tile(B);
+    settled = all_settled();
+  }
+  for (; t < ntiles; t += 2) {
+    const int64_t ja = j0 + t * 16;
+    load(ja + 16, B);
+    tile_settled(A);
+    load(t + 2 < ntiles ? ja + 32 : ja, A);
+    tile_settled(B);
+  }
+  if (settled) {
+#pragma unroll
+    for (int r = 0; r < RT; ++r)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) l[r][q] += lraw[r][q] * exp2_hw(-m[r][q]);
   }
   // merge the 16 lanes of each row: m = max, l = sum l 2^(m_lane - m)
   const bool last = splits == 1;
