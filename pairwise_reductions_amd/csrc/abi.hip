@@ -113,7 +113,7 @@ LowdLayout lowd_layout(int op, int64_t M, int64_t N, int D, int C, int K) {
   size_t mf = 0;
   if (op == KEOPS_OP_GAUSS_SUM) mf = keops::mf_region_bytes(M, N, D, C);
   if (op == KEOPS_OP_LSE) mf = keops::mf_region_bytes(M, N, D, 0);
-  if (op == KEOPS_OP_GAUSS_SUM_GRAD_X && C == 1) mf = keops::mf_region_bytes(M, N, D, 1 + D);
+  if (op == KEOPS_OP_GAUSS_SUM_GRAD_X && C == 1) mf = keops::mf_region_bytes(M, N, D, 1 + D, true);
   L.total = L.mf_off + mf;
   if (M == 0 || N == 0) L.total = 0;
   return L;

@@ -53,7 +53,7 @@ hipError_t launch_gauss_sum_lowd(const float* x, const float* y, double* cols, c
 // decision, two ints (gate, bad): the matrix-core sweep runs when gate != 0 and bad == 0; row
 // tiles per wave for C channels; preparation (also writes the float64 column table; b may be
 // null) and sweeps.
-size_t mf_region_bytes(int64_t M, int64_t N, int D, int W);  // W: floats per column record
+size_t mf_region_bytes(int64_t M, int64_t N, int D, int W, bool grad = false);  // W: floats per column record
 const int* mf_decision(const void* region);
 int mf_rows_per_lane(int op, int D, int C);   // op: 0 sum, 1 log-sum-exp, 3 gradient
 int mf_occupancy(int op, int D, int C, int rt);  // resident workgroups per CU of that sweep

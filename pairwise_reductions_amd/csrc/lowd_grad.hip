@@ -118,7 +118,8 @@ hipError_t launch_grad_x_lowd(const float* x, const float* y, const float* b, co
   hipError_t e = hipSuccess;
   const int* skip = nullptr;
   if (C == 1) {
-    // the matrix-core sweep's operands: row and column pieces, (b_j, y_j) per column
+    // the matrix-core sweep's operands: row and column pieces (log2 |b_j| in the exponent),
+    // (sign b_j, -sign b_j y_j) per column
     e = launch_mf_prepare(x, y, b, true, nullptr, mf, M, N, D, 1, (double)c2f, s);
     if (e != hipSuccess) return e;
     skip = mf_decision(mf);

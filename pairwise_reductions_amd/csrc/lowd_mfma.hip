@@ -205,10 +205,15 @@ __device__ __forceinline__ void store_pieces(half8* __restrict__ dst, const _Flo
 
 // Operand preparation, one thread per row (workgroups [0, rb)) or per column (the rest):
 //   rows     rhi[i] (8 NH fp16), rlo[i] (32 NL fp16), rA[i] = Ah_i
-//   columns  chi[j], clo[j] and bpad[j] = (b[j][0..C), with_y: y[j][0..D)) for j < Npad (b = null:
-//            no weights; zero past N; padding columns get an exponent that underflows), and
-//            (cols not null) the float64
-//            column table cols[j] = (y_j - y_0, -c2 |y_j - y_0|^2) of the float64 sweep
+//   columns  chi[j], clo[j] and bpad[j] = b[j][0..C) for j < Npad (b = null: no weights; zero
+//            past N; padding columns get an exponent that underflows), and (cols not null) the
+//            float64 column table cols[j] = (y_j - y_0, -c2 |y_j - y_0|^2) of the float64 sweep
+//   with_y   (the one-channel gradient) the weight moves into the exponent: two more low-part
+//            products add L_j = log2 |b_j| (as Lh on a 2^-6 grid plus Ll on a 2^-17 grid, so
+//            to 2^-18; |L_j| >= 32 does not convert exactly and sends the call to the float32
+//            sweep), and the column record is bpad[j] = (s_j, -s_j y_j[0..D)) with s_j the sign
+//            of b_j (0 for b_j = 0), so the sweep forms s_j (x_i - y_j) with one FMA per
+//            coordinate and needs no product with the weight.
 // Each workgroup reduces the bounds records and derives the parameters itself (identically);
 // workgroup 0 publishes them. A piece that does not convert exactly sets P->bad.
 template <int NH, int NL>
@@ -283,6 +288,10 @@ mf_prep_kernel(const float* __restrict__ x, const float* __restrict__ y, const f
     }
     hi[D] = piece(1.0, -sp.sh[kOneBh1], ok);
     hi[D + 1] = piece(1.0, -sp.sh[kOneBh2], ok);
+    if (with_y) {
+      lo[5 * D + 2] = (_Float16)1.0f;
+      lo[5 * D + 3] = (_Float16)0x1p-10f;
+    }
     const double A = -cp * nrm;
     const double Ah = rnd(A, sp.gamma);
     lo[5 * D] = piece(rnd(A - Ah, sp.gamma - 12), -sp.sh[kAl1One], ok);
@@ -296,10 +305,14 @@ mf_prep_kernel(const float* __restrict__ x, const float* __restrict__ y, const f
     const int64_t j = ((int64_t)blockIdx.x - rb) * kBlock + threadIdx.x;
     if (j >= Npad) return;
     const int W = C + (with_y ? D : 0);
-    if (b)
+    if (with_y) {  // (s_j, -s_j y_j), C = 1
+      const float bj = (b && j < N) ? b[j] : 0.0f;
+      const float sj = bj > 0.0f ? 1.0f : (bj < 0.0f ? -1.0f : 0.0f);
+      bpad[j * W] = sj;
+      for (int d = 0; d < D; ++d) bpad[j * W + 1 + d] = j < N ? -(sj * y[j * D + d]) : 0.0f;
+    } else if (b) {
       for (int c = 0; c < C; ++c) bpad[j * W + c] = j < N ? b[j * C + c] : 0.0f;
-    if (with_y)
-      for (int d = 0; d < D; ++d) bpad[j * W + C + d] = j < N ? y[j * D + d] : 0.0f;
+    }
     if (cols && j < N) {  // float64 column table
       const int P64 = col_stride(D);
       double s = 0.0;
@@ -341,6 +354,13 @@ mf_prep_kernel(const float* __restrict__ x, const float* __restrict__ y, const f
       hi[D + 1] = piece(Bh - Bh1, sp.sh[kOneBh2], ok);
       lo[5 * D] = piece(1.0, sp.sh[kAl1One], ok);
       lo[5 * D + 1] = piece(rnd(Bv - Bh, sp.gamma - 12), sp.sh[kOneBl1], ok);
+      if (with_y) {
+        const double bj = b ? (double)b[j] : 0.0;
+        const double L = bj != 0.0 ? log2(fabs(bj)) : 0.0;
+        const double Lh = rnd(L, -6);
+        lo[5 * D + 2] = piece(Lh, 0, ok);
+        lo[5 * D + 3] = piece(rnd(L - Lh, -17), 10, ok);
+      }
     } else {
       // padding column: e = A_i - 65504 2^-s, far below every real exponent (those are at least
       // -2^(gamma+23)), so 2^e is exactly 0 and no reduction sees it
@@ -656,8 +676,10 @@ lse_mf_kernel(const half8* __restrict__ rhi, const half8* __restrict__ rlo, cons
 // Gradient with respect to x, one channel ("Kernel Operations on the GPU, with Autodiff, without
 // Memory Overflows": the derivative of a reduction is a reduction over the same pairs):
 //   out_i = -(g_i / sigma^2) sum_j k_ij b_j (x_i - y_j)
-// k_ij from the matrix-core exponent as in the sum; the differences are taken per pair in
-// float32 from the original coordinates (no x_i sum - sum y cancellation). bw[j] = (b_j, y_j).
+// The exponent carries log2 |b_j| (see the preparation), so 2^e = k_ij |b_j|; the record
+// bw[j] = (s_j, -s_j y_j) gives s_j (x_i - y_j) = fma(s_j, x_i, -s_j y_j), which rounds exactly
+// as x_i - y_j does (s_j = +-1 or 0): per pair one exp and 2 D FMAs, the differences taken in
+// float32 from the original coordinates (no x_i sum - sum y cancellation).
 // Lanes keep per-column partials for their 4 rows per tile, folded every kChunk columns and
 // across the 16 lanes of a row at the end.
 template <int D, int RT, int NH, int NL>
@@ -725,9 +747,9 @@ grad_mf_kernel(const half8* __restrict__ rhi, const half8* __restrict__ rlo, con
       for (int n = 0; n < NL; ++n) e = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[r][n], o.l[n], e, 0, 0, 0);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const float kw = exp2_hw(e[q]) * o.w[0];
+        const float kw = exp2_hw(e[q]);
 #pragma unroll
-        for (int d = 0; d < D; ++d) part[r][q][d] = fmaf(kw, xr[r][q][d] - o.w[1 + d], part[r][q][d]);
+        for (int d = 0; d < D; ++d) part[r][q][d] = fmaf(kw, fmaf(o.w[0], xr[r][q][d], o.w[1 + d]), part[r][q][d]);
       }
     }
   };
@@ -787,11 +809,13 @@ struct MfLayout {
   size_t parts, rhi, rlo, rA, chi, clo, bpad, total;
 };
 
-// W: floats per padded column record (the weights, and for the gradient also y_j)
-MfLayout mf_layout(int64_t M, int64_t N, int D, int W) {
+// W: floats per padded column record (the weights, and for the gradient also y_j); grad: the
+// gradient's two extra low-part products. The sweeps take (NH, NL) = (1, 1) or (2, 2).
+MfLayout mf_layout(int64_t M, int64_t N, int D, int W, bool grad = false) {
   MfLayout L;
-  L.NH = (D + 2 <= 8) ? 1 : 2;
-  L.NL = (5 * D + 2 <= 32) ? 1 : 2;
+  const bool narrow = D + 2 <= 8 && 5 * D + 2 + (grad ? 2 : 0) <= 32;
+  L.NH = narrow ? 1 : 2;
+  L.NL = narrow ? 1 : 2;
   L.Npad = ceil_div(N, 32) * 32;
   size_t off = align_up(sizeof(MfParams));
   L.parts = off;
@@ -950,7 +974,9 @@ int occupancy_grad(bool wide) {
 }  // namespace
 }  // namespace lowd
 
-size_t mf_region_bytes(int64_t M, int64_t N, int D, int W) { return lowd::mf_layout(M, N, D, W).total; }
+size_t mf_region_bytes(int64_t M, int64_t N, int D, int W, bool grad) {
+  return lowd::mf_layout(M, N, D, W, grad).total;
+}
 
 const int* mf_decision(const void* region) { return &static_cast<const lowd::MfParams*>(region)->gate; }
 
@@ -964,7 +990,7 @@ int mf_occupancy(int op, int D, int C, int rt) {
   // instance; 4 when the runtime cannot say)
   static std::atomic<int> cache[2][kMaxLowC + 1][5];
   static std::atomic<int> cache_grad[kMaxLowD + 1];
-  const int wide = lowd::mf_layout(1, 1, D, 1).NH == 2 ? 1 : 0;
+  const int wide = lowd::mf_layout(1, 1, D, 1, op == 3).NH == 2 ? 1 : 0;
   int dev = 0;
   if (op == 1) C = 0;  // the log-sum-exp sweep
   if (D < 1 || D > kMaxLowD || C < 0 || C > kMaxLowC || (rt != 1 && rt != 2 && rt != 4) ||
@@ -1020,7 +1046,7 @@ hipError_t launch_mf_prepare(const float* x, const float* y, const float* b, boo
                              int64_t M, int64_t N, int D, int C, double c2, hipStream_t s) {
   using namespace lowd;
   char* r = static_cast<char*>(region);
-  const MfLayout L = mf_layout(M, N, D, C + (with_y ? D : 0));
+  const MfLayout L = mf_layout(M, N, D, C + (with_y ? D : 0), with_y);
   MfParams* P = reinterpret_cast<MfParams*>(r);
   unsigned int* parts = reinterpret_cast<unsigned int*>(r + L.parts);
   const int64_t n = M > N ? M : N;
@@ -1057,7 +1083,7 @@ hipError_t launch_mf_grad(const float* x, const float* g, float* dst, float inv_
                           int64_t N, int D, const Plan& p, hipStream_t s) {
   using namespace lowd;
   char* r = static_cast<char*>(region);
-  const MfLayout L = mf_layout(M, N, D, 1 + D);
+  const MfLayout L = mf_layout(M, N, D, 1 + D, true);
 #define KEOPS_MF_G(Dv) sweep_grad<Dv>(r, L, x, g, dst, inv_sigma2, M, N, p, s)
   KEOPS_SWITCH_D(D, KEOPS_MF_G)
 #undef KEOPS_MF_G

@@ -272,6 +272,33 @@ def test_grad_xy_exponent_regimes(D, sigma, lo, hi, outlier):
     assert_normalised(got, want, norm, TOL_F32, "grad_y regime")
 
 
+@pytest.mark.parametrize("extreme", [False, True])
+def test_grad_xy_weight_signs_zeros_and_range(extreme):
+    """One-channel gradients with weights of both signs, exact zeros and magnitudes over 2^+-20.
+    The matrix-core sweep carries log2 |b_j| in the exponent and the sign of b_j in the column
+    record; with one weight of 1e-12 (|log2| near 40, beyond what the exponent pieces carry)
+    the call takes the float32 sweep instead. Both must match the oracle, for the x-gradient
+    (weights b) and the y-gradient (the roles exchanged: the upstream g weighs the columns)."""
+    import pairwise_reductions_amd as pr
+    _announce("grad_weight_range", extreme=extreme)
+    M, N, D, sig = 1200, 1700, 3, float(np.float32(0.1))
+    x, y, _ = _rand(9101, M, N, D, 1)
+    rng = np.random.default_rng(9102)
+    b = (rng.standard_normal((N, 1)) * np.exp2(rng.integers(-20, 21, (N, 1)))).astype(np.float32)
+    b[::7] = 0.0
+    g = (rng.standard_normal((M, 1)) * np.exp2(rng.integers(-20, 21, (M, 1)))).astype(np.float32)
+    g[::5] = 0.0
+    if extreme:
+        b[5] = 1e-12
+        g[3] = -1e-12
+    got = _host(pr.gauss_sum_grad_x(_dev(x), _dev(y), _dev(b), _dev(g), sig))
+    want, norm = oracle.gauss_sum_grad_x(x, y, b, g, sig, workers=8)
+    assert_normalised(got, want, norm, TOL_F32, "grad_x weights")
+    got = _host(pr.gauss_sum_grad_y(_dev(x), _dev(y), _dev(b), _dev(g), sig))
+    want, norm = oracle.gauss_sum_grad_y(x, y, b, g, sig, workers=8)
+    assert_normalised(got, want, norm, TOL_F32, "grad_y weights")
+
+
 def test_grad_x_of_squared_loss_mixture():
     """The KeOps example's loss sum_i a_i^2 on the 8-cluster mixture: the upstream gradient
     is g = 2 s with s the oracle's forward, rounded to float32 for both sides."""
