@@ -338,7 +338,7 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=8192, help="rows of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--all", action="store_true", help="also time the other workloads")
-    ap.add_argument("--all-out", default=os.path.join("gpurun_out", "bench_all.json"))
+    ap.add_argument("--all-out", default="bench_all.json")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run one 256 MiB device-to-device copy (the reference kernel that scales the "
                          "FETCH_SIZE / WRITE_SIZE counters to bytes) and exit")

@@ -1,6 +1,7 @@
 // Shared low-D pieces: the column table, fills, the fixed-order combines of per-split
 // partials, a few element-wise steps and the launch planner. The sweeps live in
-// lowd_sum.hip, lowd_lse.hip, lowd_knn.hip and lowd_grad.hip.
+// lowd_mfma.hip (matrix-core exponent), lowd_sum.hip, lowd_lse.hip, lowd_knn.hip and
+// lowd_grad.hip.
 #include "lowd_common.h"
 
 namespace keops {

@@ -2,6 +2,8 @@
 // Autodiff, without Memory Overflows": each partial derivative of a reduction is itself a
 // reduction over the same pairs):
 //   grad_i = -(1/sigma^2) sum_j k_ij (g_i . b_j) (x_i - y_j).
+// With one channel the matrix-core sweep of lowd_mfma.hip runs instead whenever the
+// device-side decision admits the inputs; this float32 sweep covers the rest.
 #include "lowd_common.h"
 
 namespace keops {

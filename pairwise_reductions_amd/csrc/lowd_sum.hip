@@ -1,5 +1,7 @@
 // Low-D float32 Gauss sum ("Kernel matrix reduction", Implementation sketch: the Gaussian
-// kernel matrix-vector product a_i = sum_j exp(-|x_i - y_j|^2 / (2 sigma^2)) b_j).
+// kernel matrix-vector product a_i = sum_j exp(-|x_i - y_j|^2 / (2 sigma^2)) b_j). The sweep
+// here evaluates the exponent in float64; it runs when the device-side decision declines the
+// matrix-core sweep of lowd_mfma.hip (both are launched, one returns at once).
 //
 // Gaussian exponent. For the sum and log-sum-exp reductions the exponent in base 2,
 //   e_ij = -c2 ||x_i - y_j||^2,  c2 = log2(e) / (2 sigma^2),
