@@ -119,6 +119,15 @@ LowdLayout lowd_layout(int op, int64_t M, int64_t N, int D, int C, int K) {
   return L;
 }
 
+// argKmin + LSE: the argKmin layout followed by a log-sum-exp layout whose matrix-core region
+// and partials the matrix-core log-sum-exp sweep uses (the float64 column table of that layout
+// stays unused: the fused sweep, which runs when the matrix cores decline, reads the
+// argKmin one).
+size_t argk_lse_bytes(int64_t M, int64_t N, int D, int K) {
+  if (M == 0 || N == 0) return 0;
+  return lowd_layout(KEOPS_OP_ARGKMIN_LSE, M, N, D, 1, K).total + lowd_layout(KEOPS_OP_LSE, M, N, D, 1, 0).total;
+}
+
 int check_workspace(void* ws, size_t have, size_t need) {
   if (need == 0) return KEOPS_OK;
   if (!ws) return fail(KEOPS_ERR_INVALID_ARG, "workspace is NULL but %zu bytes are needed", need);
@@ -345,9 +354,11 @@ size_t keops_workspace_bytes(int op, int64_t B, int64_t M, int64_t N, int32_t D,
       if (D < 1 || D > keops::kMaxLowD || K < 1 || K > keops::kMaxK || K > N) return 0;
       return lowd_layout(KEOPS_OP_ARGKMIN, M, N, D, 1, K).total;
     case KEOPS_OP_ARGKMIN:
-    case KEOPS_OP_ARGKMIN_LSE:
       if (D < 1 || D > keops::kMaxLowD || K < 1 || K > keops::kMaxK || K > N) return 0;
       return lowd_layout(op, M, N, D, 1, K).total;
+    case KEOPS_OP_ARGKMIN_LSE:  // the argKmin layout, then a log-sum-exp one for the matrix-core sweep
+      if (D < 1 || D > keops::kMaxLowD || K < 1 || K > keops::kMaxK || K > N) return 0;
+      return argk_lse_bytes(M, N, D, K);
     case KEOPS_OP_GAUSS_SUM_GRAD_X:
       if (D < 1 || D > keops::kMaxLowD || C < 1 || C > keops::kMaxLowC) return 0;
       return lowd_layout(op, M, N, D, C, 0).total;
@@ -593,8 +604,9 @@ int argkmin_impl(const float* x, const float* y, const float* w, int32_t* idx, f
   if (M == 0) return ok();
   const int op = with_lse ? KEOPS_OP_ARGKMIN_LSE : KEOPS_OP_ARGKMIN;
   const LowdLayout L = lowd_layout(op, M, N, D, 1, K);
-  KEOPS_TRY(check_workspace(workspace, workspace_bytes, L.total));
-  const Range rw{workspace, L.total};
+  const size_t need = with_lse ? argk_lse_bytes(M, N, D, K) : L.total;
+  KEOPS_TRY(check_workspace(workspace, workspace_bytes, need));
+  const Range rw{workspace, need};
   if (overlaps(rw, ri) || overlaps(rw, rd) || overlaps(rw, rl) || overlaps(rw, rx) || overlaps(rw, ry) ||
       overlaps(rw, rwt))
     return fail(KEOPS_ERR_INVALID_ARG, "workspace overlaps an input or an output");
@@ -603,8 +615,17 @@ int argkmin_impl(const float* x, const float* y, const float* w, int32_t* idx, f
   double* ymax = reinterpret_cast<double*>(ws + L.aux_off);
   double* lse_part = reinterpret_cast<double*>(ws + L.lse_off);
   const double c2 = with_lse ? c2_of(sigma) : 0.0;
+  keops::KnnLse mf_lse{};
+  LowdLayout LL;
+  if (with_lse && N > 0 && !w) {
+    LL = lowd_layout(KEOPS_OP_LSE, M, N, D, 1, 0);
+    char* lws = ws + L.total;
+    mf_lse.region = lws + LL.mf_off;
+    mf_lse.partial = lws + LL.part_off;
+    mf_lse.plan = &LL.plan;
+  }
   KEOPS_HIP(keops::launch_knn_lowd(x, y, w, cols, ymax, idx, dist, ws + L.part_off, lse, lse_part, M, N, D, K, c2,
-                                   with_lse, L.plan, stream),
+                                   with_lse, L.plan, stream, mf_lse.region ? &mf_lse : nullptr),
             "argkmin_lowd");
   return ok();
 }

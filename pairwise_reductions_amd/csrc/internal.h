@@ -72,13 +72,22 @@ hipError_t launch_mf_lse(float* out, void* partial, void* region, int64_t M, int
 hipError_t launch_lse_lowd(const float* x, const float* y, double* cols, float* out,
                            double* partial, void* mf, int64_t M, int64_t N, int D, double c2,
                            const Plan& p, hipStream_t s);
-// argKmin of d^2_ij - w_j (w may be null), optionally fused with the log-sum-exp reduction
+// The matrix-core log-sum-exp that the argKmin + LSE call may run beside a plain argKmin
+// sweep: its operand region, its per-split partials and its plan (a log-sum-exp plan).
+struct KnnLse {
+  void* region;
+  void* partial;
+  const Plan* plan;
+};
+// argKmin of d^2_ij - w_j (w may be null), optionally with the log-sum-exp reduction
 // (with_lse, only without weights): builds the uncentred column table in `cols` and the
-// screening bound in *ymax, then screens every pair.
+// screening bound in *ymax, then screens every pair. With mf_lse the log-sum-exp runs on the
+// matrix cores beside the plain argKmin sweep whenever the device-side decision admits the
+// inputs, and in the fused float64 sweep otherwise.
 hipError_t launch_knn_lowd(const float* x, const float* y, const float* w, double* cols, double* ymax,
                            int32_t* idx, float* dist, void* partial, float* lse_out,
                            double* lse_partial, int64_t M, int64_t N, int D, int K, double c2,
-                           bool with_lse, const Plan& p, hipStream_t s);
+                           bool with_lse, const Plan& p, hipStream_t s, const KnnLse* mf_lse = nullptr);
 // Gradient with respect to x (float32 sweep; with C = 1 the matrix-core sweep, prepared in `mf`,
 // takes it when the device-side decision admits the inputs).
 hipError_t launch_grad_x_lowd(const float* x, const float* y, const float* b, const float* g,

@@ -45,7 +45,8 @@ combine_sum_kernel(const float* __restrict__ partial, float* __restrict__ out, i
 
 __global__ void __launch_bounds__(kBlock)
 combine_lse_kernel(const LsePartial* __restrict__ partial, float* __restrict__ out, int64_t M,
-                   int64_t S) {
+                   int64_t S, const int* __restrict__ mf, int run_if_mf) {
+  if (mf && ((mf[0] && !mf[1]) ? 1 : 0) != run_if_mf) return;  // the other form's partials
   const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
   if (i >= M) return;
   double m = partial[i].m;
@@ -89,9 +90,10 @@ hipError_t launch_combine_sum(const float* partial, float* out, int64_t n, int64
   return hipGetLastError();
 }
 
-hipError_t launch_combine_lse(const LsePartial* partial, float* out, int64_t M, int64_t S, hipStream_t s) {
+hipError_t launch_combine_lse(const LsePartial* partial, float* out, int64_t M, int64_t S, hipStream_t s,
+                              const int* mf, int run_if_mf) {
   if (M <= 0) return hipSuccess;
-  combine_lse_kernel<<<(unsigned)ceil_div(M, kBlock), kBlock, 0, s>>>(partial, out, M, S);
+  combine_lse_kernel<<<(unsigned)ceil_div(M, kBlock), kBlock, 0, s>>>(partial, out, M, S, mf, run_if_mf);
   return hipGetLastError();
 }
 

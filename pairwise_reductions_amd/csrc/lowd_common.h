@@ -70,7 +70,9 @@ struct KeyIdx {
 hipError_t launch_combine_sum(const float* partial, float* out, int64_t n, int64_t S, const float* rscale, int C,
                               hipStream_t s);
 // out[i] = ln(sum over s of l_s 2^{m_s}), merged in float64.
-hipError_t launch_combine_lse(const LsePartial* partial, float* out, int64_t M, int64_t S, hipStream_t s);
+// (mf: a device-side matrix-core decision; the combine then runs only when admitted == run_if_mf)
+hipError_t launch_combine_lse(const LsePartial* partial, float* out, int64_t M, int64_t S, hipStream_t s,
+                              const int* mf = nullptr, int run_if_mf = 0);
 
 #define KEOPS_SWITCH_D(D_, CALL)                   \
   switch (D_) {                                    \

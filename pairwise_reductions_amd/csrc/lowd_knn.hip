@@ -93,7 +93,8 @@ __global__ void __launch_bounds__(kBlock)
 knn_kernel(const float* __restrict__ x, const double* __restrict__ cols, const float* __restrict__ w,
            const double* __restrict__ ymax, int32_t* __restrict__ idx, float* __restrict__ dist, KeyIdx* __restrict__ partial,
            float* __restrict__ lse_out, LsePartial* __restrict__ lse_partial, int64_t M, int64_t N,
-           int64_t cps, int Kout, double c2) {
+           int64_t cps, int Kout, double c2, const int* __restrict__ mf, int run_if_mf) {
+  if (mf && ((mf[0] && !mf[1]) ? 1 : 0) != run_if_mf) return;  // the other form takes these inputs
   constexpr int P = (D + 2) & ~1;
   constexpr int U = D <= 4 ? 4 : 2;  // columns per screened tile
   static_assert(kQueue >= 2 * U, "queue holds at least two tiles");
@@ -272,28 +273,36 @@ merge_topk_kernel(const KeyIdx* __restrict__ partial, int32_t* __restrict__ idx,
   }
 }
 
-template <int D, int K, bool LSE>
+// The sweep(s) and the merges. With mf (the device-side decision of a prepared matrix-core
+// log-sum-exp) the fused sweep runs only when that decision declines and the plain one only
+// when it admits; the caller runs the matrix-core log-sum-exp itself.
+template <int D, int K>
 hipError_t knn_dk(const float* x, const double* cols, const float* w, const double* ymax, int32_t* idx, float* dist,
                   void* partial, float* lse_out, double* lse_partial, int64_t M, int64_t N, int Kout, double c2,
-                  const Plan& p, hipStream_t s) {
+                  bool with_lse, const int* mf, const Plan& p, hipStream_t s) {
+  constexpr int R = K <= 16 ? 2 : 1;
   dim3 grid((unsigned)p.row_blocks, (unsigned)p.splits);
-  knn_kernel<D, K, (K <= 16 ? 2 : 1), LSE><<<grid, kBlock, 0, s>>>(
-      x, cols, w, ymax, idx, dist, reinterpret_cast<KeyIdx*>(partial), lse_out,
-      reinterpret_cast<LsePartial*>(lse_partial), M, N, p.cols_per_split, Kout, c2);
+  KeyIdx* part = reinterpret_cast<KeyIdx*>(partial);
+  LsePartial* lpart = reinterpret_cast<LsePartial*>(lse_partial);
+  if (with_lse)
+    knn_kernel<D, K, R, true><<<grid, kBlock, 0, s>>>(x, cols, w, ymax, idx, dist, part, lse_out, lpart, M, N,
+                                                       p.cols_per_split, Kout, c2, mf, 0);
+  if (!with_lse || mf)
+    knn_kernel<D, K, R, false><<<grid, kBlock, 0, s>>>(x, cols, w, ymax, idx, dist, part, lse_out, lpart, M, N,
+                                                        p.cols_per_split, Kout, c2, mf, 1);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
-  merge_topk_kernel<K><<<(unsigned)ceil_div(M, kBlock), kBlock, 0, s>>>(
-      reinterpret_cast<const KeyIdx*>(partial), idx, dist, M, p.splits, Kout);
+  merge_topk_kernel<K><<<(unsigned)ceil_div(M, kBlock), kBlock, 0, s>>>(part, idx, dist, M, p.splits, Kout);
   e = hipGetLastError();
-  if (e != hipSuccess || !LSE) return e;
-  return launch_combine_lse(reinterpret_cast<const LsePartial*>(lse_partial), lse_out, M, p.splits, s);
+  if (e != hipSuccess || !with_lse) return e;
+  return launch_combine_lse(lpart, lse_out, M, p.splits, s, mf, 0);
 }
 
-template <int D, bool LSE>
+template <int D>
 hipError_t knn_d(int Kb, const float* x, const double* cols, const float* w, const double* ymax, int32_t* idx, float* dist,
                  void* partial, float* lse_out, double* lse_partial, int64_t M, int64_t N, int Kout, double c2,
-                 const Plan& p, hipStream_t s) {
-#define KEOPS_KNN_K(Kv) return knn_dk<D, Kv, LSE>(x, cols, w, ymax, idx, dist, partial, lse_out, lse_partial, M, N, Kout, c2, p, s)
+                 bool with_lse, const int* mf, const Plan& p, hipStream_t s) {
+#define KEOPS_KNN_K(Kv) return knn_dk<D, Kv>(x, cols, w, ymax, idx, dist, partial, lse_out, lse_partial, M, N, Kout, c2, with_lse, mf, p, s)
   switch (Kb) {
     case 1: KEOPS_KNN_K(1);
     case 2: KEOPS_KNN_K(2);
@@ -313,7 +322,8 @@ hipError_t knn_d(int Kb, const float* x, const double* cols, const float* w, con
 
 hipError_t launch_knn_lowd(const float* x, const float* y, const float* w, double* cols, double* ymax,
                            int32_t* idx, float* dist, void* partial, float* lse_out, double* lse_partial, int64_t M,
-                           int64_t N, int D, int K, double c2, bool with_lse, const Plan& p, hipStream_t s) {
+                           int64_t N, int D, int K, double c2, bool with_lse, const Plan& p, hipStream_t s,
+                           const KnnLse* mf_lse) {
   // column table (y_j, |y_j|^2 - w_j) uncentred, then the largest |y_j|^2 + |w_j| for the
   // screening margin
   hipError_t e = launch_prep_cols(y, cols, N, D, -1.0, false, s);
@@ -322,16 +332,25 @@ hipError_t launch_knn_lowd(const float* x, const float* y, const float* w, doubl
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int Kb = lowd::argk_bucket(K);
-  if (with_lse) {
-#define KEOPS_KNN(Dv) lowd::knn_d<Dv, true>(Kb, x, cols, w, ymax, idx, dist, partial, lse_out, lse_partial, M, N, K, c2, p, s)
-    auto run = [&]() -> hipError_t { KEOPS_SWITCH_D(D, KEOPS_KNN) };
-#undef KEOPS_KNN
-    return run();
+  // With the log-sum-exp and a matrix-core region: the matrix-core log-sum-exp sweep and the
+  // plain argKmin sweep when the device-side decision admits the inputs (the two sweeps cost
+  // less than the fused one on this chip), the fused float64 sweep otherwise.
+  const int* mf = nullptr;
+  if (with_lse && mf_lse && !w) {
+    e = launch_mf_prepare(x, y, nullptr, false, nullptr, mf_lse->region, M, N, D, 0, c2, s);
+    if (e != hipSuccess) return e;
+    mf = mf_decision(mf_lse->region);
   }
-#define KEOPS_KNN(Dv) lowd::knn_d<Dv, false>(Kb, x, cols, w, ymax, idx, dist, partial, lse_out, lse_partial, M, N, K, c2, p, s)
+#define KEOPS_KNN(Dv) lowd::knn_d<Dv>(Kb, x, cols, w, ymax, idx, dist, partial, lse_out, lse_partial, M, N, K, c2, with_lse, mf, p, s)
   auto run = [&]() -> hipError_t { KEOPS_SWITCH_D(D, KEOPS_KNN) };
 #undef KEOPS_KNN
-  return run();
+  e = run();
+  if (e != hipSuccess || !mf) return e;
+  const Plan& lp = *mf_lse->plan;
+  e = launch_mf_lse(lse_out, lp.splits > 1 ? mf_lse->partial : nullptr, mf_lse->region, M, N, D, lp, s);
+  if (e != hipSuccess || lp.splits == 1) return e;
+  return lowd::launch_combine_lse(static_cast<const lowd::LsePartial*>(mf_lse->partial), lse_out, M, lp.splits, s,
+                                  mf, 1);
 }
 
 }  // namespace keops

@@ -514,6 +514,30 @@ def test_argkmin_lse_shapes(M, N, D, K):
     assert np.all(np.abs(lse - want_lse) <= lse_bound(want_lse))
 
 
+@pytest.mark.parametrize("D,sigma,lo,hi,outlier", EXPONENT_REGIMES)
+def test_argkmin_lse_exponent_regimes(D, sigma, lo, hi, outlier):
+    """argKmin + LSE on both sides of the matrix-core decision: the matrix-core log-sum-exp
+    beside the plain argKmin sweep where the decision admits the inputs, the fused float64
+    sweep where it declines."""
+    import pairwise_reductions_amd as pr
+    _announce("argkmin_lse_regime", D=D, sigma=sigma, lo=lo, hi=hi, outlier=outlier)
+    M, N, K = 700, 3001, 10
+    x, y, _ = _rand(int(sigma * 1e4) + 43 * D, M, N, D, 1, lo, hi)
+    rng = np.random.default_rng(D + 3)
+    y[:M] = x + (0.5 * sigma * rng.standard_normal((M, D))).astype(np.float32)
+    if outlier:
+        y[M + 17] = 1000.0
+    sig = float(np.float32(sigma))
+    idx, dist, lse = pr.argkmin_lse(_dev(x), _dev(y), K, sig, with_dist=True)
+    idx, dist, lse = _host(idx), _host(dist), _host(lse).astype(np.float64)
+    want_idx, want_d2 = oracle.argkmin(x, y, K, workers=8)
+    assert np.array_equal(idx.astype(np.int64), want_idx)
+    assert np.allclose(dist, want_d2, rtol=1e-6, atol=0)
+    want_lse = oracle.logsumexp_reduction(x, y, sig, workers=8)
+    err = np.abs(lse - want_lse)
+    assert np.all(err <= lse_bound(want_lse)), f"argkmin_lse regime: max LSE error {err.max():.3e}"
+
+
 def test_argkmin_screening_far_from_origin_and_unaligned_values():
     """The screening bound grows with |x|^2 + max|y|^2: points near 1000 on a coarse grid
     (many exact ties) and plain float32 values (keys not exact) must still give the oracle's
