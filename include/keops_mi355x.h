@@ -129,13 +129,15 @@ KEOPS_API int keops_argkmin_weighted(const float* x, const float* y, const float
                                      size_t workspace_bytes, hipStream_t stream);
 
 /*
- * argKmin and the log-sum-exp reduction of the same pairs in one sweep ("Kernel matrix
- * reduction", Overview: minima, indices of the K smallest entries and log-sum-exp are all
- * reductions of one pairwise formula):
+ * argKmin and the log-sum-exp reduction of the same pairs ("Kernel matrix reduction",
+ * Overview: minima, indices of the K smallest entries and log-sum-exp are all reductions of
+ * one pairwise formula):
  *   idx, dist as keops_argkmin;  lse[i] = log sum_j exp(-||x_i - y_j||^2 / (2 sigma^2))
  * Shapes: x (M, D), y (N, D) float32; idx (M, K) int32; dist (M, K) float32 or NULL;
  * lse (M,) float32 (must not be NULL). Same limits as keops_argkmin, plus sigma as in
- * keops_lse. The running row shift of the log-sum-exp is the smallest key found so far.
+ * keops_lse; the workspace is that of KEOPS_OP_ARGKMIN_LSE. Where the matrix-core
+ * log-sum-exp admits the inputs (decided on the device) it runs beside a plain argKmin sweep;
+ * otherwise one fused float64 sweep computes both. idx and dist are the same either way.
  */
 KEOPS_API int keops_argkmin_lse(const float* x, const float* y, int32_t* idx, float* dist, float* lse,
                                 int64_t M, int64_t N, int32_t D, int32_t K, float sigma,
