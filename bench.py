@@ -166,8 +166,13 @@ def _resident(inp, keys, dev):
     return [torch.from_numpy(inp[k]).to(dev) for k in keys]
 
 
-def bench_all(steps, warmup):
-    """Time every workload through the library (inputs resident on the GPU)."""
+ALL_GROUPS = ("gauss_sum_10k", "grad_100k", "fp16", "fp16_fwd_bwd", "fp16_d_sweep", "bf16_f32", "diffusion",
+              "argkmin_lse")
+
+
+def bench_all(steps, warmup, only=None):
+    """Time every workload through the library (inputs resident on the GPU); `only` names one
+    group of ALL_GROUPS."""
     import torch
 
     import pairwise_reductions_amd as pr
@@ -176,157 +181,169 @@ def bench_all(steps, warmup):
     dev = torch.device("cuda:0")
     rows = {}
 
+    def want(group):
+        return only is None or only == group
+
     # Gauss sum 10k (small case: launch-dominated)
-    inp = workloads.make_inputs("gauss_sum_10k")
-    x, y, b = _resident(inp, ("x", "y", "b"), dev)
-    sig = float(inp["sigma"])
-    out = torch.empty((inp["M"], inp["C"]), device=dev)
-    ws = torch.empty(max(1, pr.workspace_bytes(0, 1, inp["M"], inp["N"], 3, 1)), dtype=torch.uint8, device=dev)
-    t = _events_time(lambda: pr.gauss_sum(x, y, b, sig, out=out, workspace=ws), max(steps, 100), warmup)
-    pairs = float(inp["M"]) * inp["N"]
-    rows["gauss_sum_10k"] = {"ms": t * 1e3, "pairs_per_s": pairs / t,
-                             "frac_fp32_peak": pairs * 12 / t / 1e12 / PEAK_FP32_VECTOR_TFLOPS}
+    if want("gauss_sum_10k"):
+        inp = workloads.make_inputs("gauss_sum_10k")
+        x, y, b = _resident(inp, ("x", "y", "b"), dev)
+        sig = float(inp["sigma"])
+        out = torch.empty((inp["M"], inp["C"]), device=dev)
+        ws = torch.empty(max(1, pr.workspace_bytes(0, 1, inp["M"], inp["N"], 3, 1)), dtype=torch.uint8, device=dev)
+        t = _events_time(lambda: pr.gauss_sum(x, y, b, sig, out=out, workspace=ws), max(steps, 100), warmup)
+        pairs = float(inp["M"]) * inp["N"]
+        rows["gauss_sum_10k"] = {"ms": t * 1e3, "pairs_per_s": pairs / t,
+                                 "frac_fp32_peak": pairs * 12 / t / 1e12 / PEAK_FP32_VECTOR_TFLOPS}
 
     # Gauss sum forward + gradient of sum_i s_i^2 (g = 2 s), 100k mixture
-    inp = workloads.make_inputs("gauss_sum_grad_x_100k_mixture")
-    x, y, b = _resident(inp, ("x", "y", "b"), dev)
-    sig = float(inp["sigma"])
-    M, N = inp["M"], inp["N"]
-    out = torch.empty((M, 1), device=dev)
-    g = torch.empty((M, 1), device=dev)
-    grad = torch.empty((M, 3), device=dev)
-    ws = torch.empty(max(pr.workspace_bytes(0, 1, M, N, 3, 1), pr.workspace_bytes(3, 1, M, N, 3, 1), 1),
-                     dtype=torch.uint8, device=dev)
+    if want("grad_100k"):
+        inp = workloads.make_inputs("gauss_sum_grad_x_100k_mixture")
+        x, y, b = _resident(inp, ("x", "y", "b"), dev)
+        sig = float(inp["sigma"])
+        M, N = inp["M"], inp["N"]
+        out = torch.empty((M, 1), device=dev)
+        g = torch.empty((M, 1), device=dev)
+        grad = torch.empty((M, 3), device=dev)
+        ws = torch.empty(max(pr.workspace_bytes(0, 1, M, N, 3, 1), pr.workspace_bytes(3, 1, M, N, 3, 1), 1),
+                         dtype=torch.uint8, device=dev)
 
-    def fwd_bwd():
-        pr.gauss_sum(x, y, b, sig, out=out, workspace=ws)
-        torch.mul(out, 2.0, out=g)
-        pr.gauss_sum_grad_x(x, y, b, g, sig, out=grad, workspace=ws)
+        def fwd_bwd():
+            pr.gauss_sum(x, y, b, sig, out=out, workspace=ws)
+            torch.mul(out, 2.0, out=g)
+            pr.gauss_sum_grad_x(x, y, b, g, sig, out=grad, workspace=ws)
 
-    t = _events_time(fwd_bwd, steps, warmup)
-    tf = _events_time(lambda: pr.gauss_sum(x, y, b, sig, out=out, workspace=ws), steps, warmup)
-    tb = _events_time(lambda: pr.gauss_sum_grad_x(x, y, b, g, sig, out=grad, workspace=ws), steps, warmup)
-    pairs = float(M) * N
-    rows["gauss_sum_grad_x_100k_mixture"] = {
-        "ms": t * 1e3, "fwd_ms": tf * 1e3, "grad_ms": tb * 1e3, "pairs_per_s": 2 * pairs / t,
-        "frac_fp32_peak": pairs * (12 + grad_flops_per_pair(3, 1)) / t / 1e12 / PEAK_FP32_VECTOR_TFLOPS}
+        t = _events_time(fwd_bwd, steps, warmup)
+        tf = _events_time(lambda: pr.gauss_sum(x, y, b, sig, out=out, workspace=ws), steps, warmup)
+        tb = _events_time(lambda: pr.gauss_sum_grad_x(x, y, b, g, sig, out=grad, workspace=ws), steps, warmup)
+        pairs = float(M) * N
+        rows["gauss_sum_grad_x_100k_mixture"] = {
+            "ms": t * 1e3, "fwd_ms": tf * 1e3, "grad_ms": tb * 1e3, "pairs_per_s": 2 * pairs / t,
+            "frac_fp32_peak": pairs * (12 + grad_flops_per_pair(3, 1)) / t / 1e12 / PEAK_FP32_VECTOR_TFLOPS}
 
     # Batched Gauss sum, fp16 matrix-core path: B=4, M=N=16384, D=C=32, tau=1
-    inp = workloads.make_inputs("batched_gauss_sum_fp16")
-    q, k, v = _resident(inp, ("x", "y", "b"), dev)
-    Bt, M, N, D, C = inp["B"], inp["M"], inp["N"], inp["D"], inp["C"]
-    out = torch.empty((Bt, M, C), device=dev)
-    ws = torch.empty(max(1, pr.workspace_bytes(0, Bt, M, N, D, C, 0, _lib.KEOPS_F16)), dtype=torch.uint8,
-                     device=dev)
-    t = _events_time(lambda: pr.gauss_sum(q, k, v, float(inp["sigma"]), out=out, workspace=ws),
-                     max(steps, 100), warmup)
-    pairs = float(Bt) * M * N
-    mflops = pairs * 2 * (D + C)
-    rows["batched_gauss_sum_fp16"] = {"ms": t * 1e3, "pairs_per_s": pairs / t,
-                                      "mfma_tflops": mflops / t / 1e12,
-                                      "frac_fp16_mfma_peak": mflops / t / 1e12 / PEAK_FP16_MFMA_TFLOPS}
-
-    # Batched Gauss sum forward + backward, fp16: B=4, M=N=16384, D=32, C=1 (the flash page's
-    # Figure 2 shape); the backward computes the gradients with respect to x, y and b.
-    inp = workloads.make_inputs("batched_gauss_sum_fp16_fwd_bwd")
-    q, k, v = _resident(inp, ("x", "y", "b"), dev)
-    Bt, M, N, D, C = inp["B"], inp["M"], inp["N"], inp["D"], inp["C"]
-    sig = float(inp["sigma"])
-    out = torch.empty((Bt, M, C), device=dev)
-    gup = torch.from_numpy(workloads.upstream_gradient(M, C, seed=4, B=Bt)).to(dev)
-    ws = torch.empty(max(1, pr.workspace_bytes(_lib.OP_GAUSS_SUM_BACKWARD, Bt, M, N, D, C, 0, _lib.KEOPS_F16),
-                         pr.workspace_bytes(0, Bt, M, N, D, C, 0, _lib.KEOPS_F16)), dtype=torch.uint8, device=dev)
-    tf = _events_time(lambda: pr.gauss_sum(q, k, v, sig, out=out, workspace=ws), max(steps, 50), warmup)
-    tb = _events_time(lambda: pr.gauss_sum_backward(q, k, v, gup, sig, workspace=ws), max(steps, 50), warmup)
-    tbx = _events_time(lambda: pr.gauss_sum_backward(q, k, v, gup, sig, need=("x",), workspace=ws),
-                       max(steps, 50), warmup)
-    pairs = float(Bt) * M * N
-    rows["batched_gauss_sum_fp16_fwd_bwd"] = {"fwd_ms": tf * 1e3, "bwd_ms": tb * 1e3, "bwd_x_only_ms": tbx * 1e3,
-                                              "fwd_bwd_ms": (tf + tb) * 1e3, "fwd_pairs_per_s": pairs / tf}
-
-    # Sweep over D of the fp16 forward at B=64, M=N=16384, C=1 (the flash page's Figure 3 shape)
-    for D in (16, 32, 64, 128):
-        Bt, M, N, C = 64, 16384, 16384, 1
-        rng = torch.Generator(device="cpu").manual_seed(D)
-        q = (torch.randn((Bt, M, D), generator=rng) / D ** 0.5).to(torch.float16).to(dev)
-        k = (torch.randn((Bt, N, D), generator=rng) / D ** 0.5).to(torch.float16).to(dev)
-        v = torch.randn((Bt, N, C), generator=rng).to(torch.float16).to(dev)
+    if want("fp16"):
+        inp = workloads.make_inputs("batched_gauss_sum_fp16")
+        q, k, v = _resident(inp, ("x", "y", "b"), dev)
+        Bt, M, N, D, C = inp["B"], inp["M"], inp["N"], inp["D"], inp["C"]
         out = torch.empty((Bt, M, C), device=dev)
         ws = torch.empty(max(1, pr.workspace_bytes(0, Bt, M, N, D, C, 0, _lib.KEOPS_F16)), dtype=torch.uint8,
                          device=dev)
-        t = _events_time(lambda: pr.gauss_sum(q, k, v, 1.0, out=out, workspace=ws), max(steps, 20), warmup)
+        t = _events_time(lambda: pr.gauss_sum(q, k, v, float(inp["sigma"]), out=out, workspace=ws),
+                         max(steps, 100), warmup)
         pairs = float(Bt) * M * N
-        rows[f"fp16_d_sweep_B64_C1_D{D}"] = {"ms": t * 1e3, "pairs_per_s": pairs / t}
-        del q, k, v, out, ws
+        mflops = pairs * 2 * (D + C)
+        rows["batched_gauss_sum_fp16"] = {"ms": t * 1e3, "pairs_per_s": pairs / t,
+                                          "mfma_tflops": mflops / t / 1e12,
+                                          "frac_fp16_mfma_peak": mflops / t / 1e12 / PEAK_FP16_MFMA_TFLOPS}
+
+    # Batched Gauss sum forward + backward, fp16: B=4, M=N=16384, D=32, C=1 (the flash page's
+    # Figure 2 shape); the backward computes the gradients with respect to x, y and b.
+    if want("fp16_fwd_bwd"):
+        inp = workloads.make_inputs("batched_gauss_sum_fp16_fwd_bwd")
+        q, k, v = _resident(inp, ("x", "y", "b"), dev)
+        Bt, M, N, D, C = inp["B"], inp["M"], inp["N"], inp["D"], inp["C"]
+        sig = float(inp["sigma"])
+        out = torch.empty((Bt, M, C), device=dev)
+        gup = torch.from_numpy(workloads.upstream_gradient(M, C, seed=4, B=Bt)).to(dev)
+        ws = torch.empty(max(1, pr.workspace_bytes(_lib.OP_GAUSS_SUM_BACKWARD, Bt, M, N, D, C, 0, _lib.KEOPS_F16),
+                             pr.workspace_bytes(0, Bt, M, N, D, C, 0, _lib.KEOPS_F16)), dtype=torch.uint8, device=dev)
+        tf = _events_time(lambda: pr.gauss_sum(q, k, v, sig, out=out, workspace=ws), max(steps, 50), warmup)
+        tb = _events_time(lambda: pr.gauss_sum_backward(q, k, v, gup, sig, workspace=ws), max(steps, 50), warmup)
+        tbx = _events_time(lambda: pr.gauss_sum_backward(q, k, v, gup, sig, need=("x",), workspace=ws),
+                           max(steps, 50), warmup)
+        pairs = float(Bt) * M * N
+        rows["batched_gauss_sum_fp16_fwd_bwd"] = {"fwd_ms": tf * 1e3, "bwd_ms": tb * 1e3, "bwd_x_only_ms": tbx * 1e3,
+                                                  "fwd_bwd_ms": (tf + tb) * 1e3, "fwd_pairs_per_s": pairs / tf}
+
+    # Sweep over D of the fp16 forward at B=64, M=N=16384, C=1 (the flash page's Figure 3 shape)
+    if want("fp16_d_sweep"):
+        for D in (16, 32, 64, 128):
+            Bt, M, N, C = 64, 16384, 16384, 1
+            rng = torch.Generator(device="cpu").manual_seed(D)
+            q = (torch.randn((Bt, M, D), generator=rng) / D ** 0.5).to(torch.float16).to(dev)
+            k = (torch.randn((Bt, N, D), generator=rng) / D ** 0.5).to(torch.float16).to(dev)
+            v = torch.randn((Bt, N, C), generator=rng).to(torch.float16).to(dev)
+            out = torch.empty((Bt, M, C), device=dev)
+            ws = torch.empty(max(1, pr.workspace_bytes(0, Bt, M, N, D, C, 0, _lib.KEOPS_F16)), dtype=torch.uint8,
+                             device=dev)
+            t = _events_time(lambda: pr.gauss_sum(q, k, v, 1.0, out=out, workspace=ws), max(steps, 20), warmup)
+            pairs = float(Bt) * M * N
+            rows[f"fp16_d_sweep_B64_C1_D{D}"] = {"ms": t * 1e3, "pairs_per_s": pairs / t}
+            del q, k, v, out, ws
 
     # bf16 and float32 inputs on the matrix cores at the flash page's Figure 5 shape (B=4,
     # M=N=16384, D=C=32; float32 runs as fp16 hi + lo parts, three products each) and the
     # float32 D sweep of its Figure 4 shape (B=64, M=N=16384, C=1).
-    for dtype, name in ((torch.bfloat16, "bf16"), (torch.float32, "f32")):
-        Bt, M, N, D, C = 4, 16384, 16384, 32, 32
-        rng = torch.Generator(device="cpu").manual_seed(11)
-        q = (torch.randn((Bt, M, D), generator=rng) / D ** 0.5).to(dtype).to(dev)
-        k = (torch.randn((Bt, N, D), generator=rng) / D ** 0.5).to(dtype).to(dev)
-        v = torch.randn((Bt, N, C), generator=rng).to(dtype).to(dev)
-        out = torch.empty((Bt, M, C), device=dev)
-        dt = _lib.KEOPS_BF16 if dtype == torch.bfloat16 else _lib.KEOPS_F32
-        ws = torch.empty(max(1, pr.workspace_bytes(0, Bt, M, N, D, C, 0, dt)), dtype=torch.uint8, device=dev)
-        t = _events_time(lambda: pr.gauss_sum(q, k, v, 1.0, out=out, workspace=ws), max(steps, 20), warmup)
-        pairs = float(Bt) * M * N
-        rows[f"batched_gauss_sum_{name}_B4_D32_C32"] = {"ms": t * 1e3, "pairs_per_s": pairs / t}
-    for D in (16, 32, 64, 128):
-        Bt, M, N, C = 64, 16384, 16384, 1
-        rng = torch.Generator(device="cpu").manual_seed(D + 100)
-        q = (torch.randn((Bt, M, D), generator=rng) / D ** 0.5).to(dev)
-        k = (torch.randn((Bt, N, D), generator=rng) / D ** 0.5).to(dev)
-        v = torch.randn((Bt, N, C), generator=rng).to(dev)
-        out = torch.empty((Bt, M, C), device=dev)
-        ws = torch.empty(max(1, pr.workspace_bytes(0, Bt, M, N, D, C, 0, _lib.KEOPS_F32)), dtype=torch.uint8,
-                         device=dev)
-        t = _events_time(lambda: pr.gauss_sum(q, k, v, 1.0, out=out, workspace=ws), max(steps, 5), warmup)
-        rows[f"f32_d_sweep_B64_C1_D{D}"] = {"ms": t * 1e3, "pairs_per_s": float(Bt) * M * N / t}
-        del q, k, v, out, ws
+    if want("bf16_f32"):
+        for dtype, name in ((torch.bfloat16, "bf16"), (torch.float32, "f32")):
+            Bt, M, N, D, C = 4, 16384, 16384, 32, 32
+            rng = torch.Generator(device="cpu").manual_seed(11)
+            q = (torch.randn((Bt, M, D), generator=rng) / D ** 0.5).to(dtype).to(dev)
+            k = (torch.randn((Bt, N, D), generator=rng) / D ** 0.5).to(dtype).to(dev)
+            v = torch.randn((Bt, N, C), generator=rng).to(dtype).to(dev)
+            out = torch.empty((Bt, M, C), device=dev)
+            dt = _lib.KEOPS_BF16 if dtype == torch.bfloat16 else _lib.KEOPS_F32
+            ws = torch.empty(max(1, pr.workspace_bytes(0, Bt, M, N, D, C, 0, dt)), dtype=torch.uint8, device=dev)
+            t = _events_time(lambda: pr.gauss_sum(q, k, v, 1.0, out=out, workspace=ws), max(steps, 20), warmup)
+            pairs = float(Bt) * M * N
+            rows[f"batched_gauss_sum_{name}_B4_D32_C32"] = {"ms": t * 1e3, "pairs_per_s": pairs / t}
+        for D in (16, 32, 64, 128):
+            Bt, M, N, C = 64, 16384, 16384, 1
+            rng = torch.Generator(device="cpu").manual_seed(D + 100)
+            q = (torch.randn((Bt, M, D), generator=rng) / D ** 0.5).to(dev)
+            k = (torch.randn((Bt, N, D), generator=rng) / D ** 0.5).to(dev)
+            v = torch.randn((Bt, N, C), generator=rng).to(dev)
+            out = torch.empty((Bt, M, C), device=dev)
+            ws = torch.empty(max(1, pr.workspace_bytes(0, Bt, M, N, D, C, 0, _lib.KEOPS_F32)), dtype=torch.uint8,
+                             device=dev)
+            t = _events_time(lambda: pr.gauss_sum(q, k, v, 1.0, out=out, workspace=ws), max(steps, 5), warmup)
+            rows[f"f32_d_sweep_B64_C1_D{D}"] = {"ms": t * 1e3, "pairs_per_s": float(Bt) * M * N / t}
+            del q, k, v, out, ws
 
     # Diffusion operator (fp32, D=3): the q and d normalisation passes and one application of
     # diag(s) K diag(s) to a block of 4 vectors, N = 2^17.
-    N, D, Cb = 1 << 17, 3, 4
-    rng = torch.Generator(device="cpu").manual_seed(7)
-    xs = torch.rand((N, D), generator=rng).to(dev)
-    vb = torch.randn((N, Cb), generator=rng).to(dev)
-    sv, qv, dv = pr.diffusion_scaling(xs, 0.05, 0.5)
-    outb = torch.empty((N, Cb), device=dev)
-    ws = torch.empty(max(1, pr.workspace_bytes(_lib.OP_DIFFUSION_SCALING, 1, N, N, D, 1),
-                         pr.workspace_bytes(_lib.OP_GAUSS_SUM_SCALED, 1, N, N, D, Cb)), dtype=torch.uint8, device=dev)
-    ts = _events_time(lambda: pr.diffusion_scaling(xs, 0.05, 0.5, workspace=ws), steps, warmup)
-    ta = _events_time(lambda: pr.gauss_sum_scaled(xs, xs, vb, 0.05, row_scale=sv, col_scale=sv, out=outb,
-                                                  workspace=ws), steps, warmup)
-    rows["diffusion_operator_fp32_n131072_d3"] = {"scaling_ms": ts * 1e3, "apply_block4_ms": ta * 1e3,
-                                                  "apply_pairs_per_s": float(N) * N / ta}
+    if want("diffusion"):
+        N, D, Cb = 1 << 17, 3, 4
+        rng = torch.Generator(device="cpu").manual_seed(7)
+        xs = torch.rand((N, D), generator=rng).to(dev)
+        vb = torch.randn((N, Cb), generator=rng).to(dev)
+        sv, qv, dv = pr.diffusion_scaling(xs, 0.05, 0.5)
+        outb = torch.empty((N, Cb), device=dev)
+        ws = torch.empty(max(1, pr.workspace_bytes(_lib.OP_DIFFUSION_SCALING, 1, N, N, D, 1),
+                             pr.workspace_bytes(_lib.OP_GAUSS_SUM_SCALED, 1, N, N, D, Cb)), dtype=torch.uint8, device=dev)
+        ts = _events_time(lambda: pr.diffusion_scaling(xs, 0.05, 0.5, workspace=ws), steps, warmup)
+        ta = _events_time(lambda: pr.gauss_sum_scaled(xs, xs, vb, 0.05, row_scale=sv, col_scale=sv, out=outb,
+                                                      workspace=ws), steps, warmup)
+        rows["diffusion_operator_fp32_n131072_d3"] = {"scaling_ms": ts * 1e3, "apply_block4_ms": ta * 1e3,
+                                                      "apply_pairs_per_s": float(N) * N / ta}
 
     # argKmin (K=10) + log-sum-exp, 100k uniform
-    inp = workloads.make_inputs("argkmin_lse_100k")
-    x, y = _resident(inp, ("x", "y"), dev)
-    M, N, K = inp["M"], inp["N"], inp["K"]
-    sig = float(inp["sigma"])
-    idx = torch.empty((M, K), dtype=torch.int32, device=dev)
-    lse_out = torch.empty((M,), device=dev)
-    ws = torch.empty(max(pr.workspace_bytes(2, 1, M, N, 3, 1, K), pr.workspace_bytes(1, 1, M, N, 3, 1), 1),
-                     dtype=torch.uint8, device=dev)
+    if want("argkmin_lse"):
+        inp = workloads.make_inputs("argkmin_lse_100k")
+        x, y = _resident(inp, ("x", "y"), dev)
+        M, N, K = inp["M"], inp["N"], inp["K"]
+        sig = float(inp["sigma"])
+        idx = torch.empty((M, K), dtype=torch.int32, device=dev)
+        lse_out = torch.empty((M,), device=dev)
+        ws = torch.empty(max(pr.workspace_bytes(2, 1, M, N, 3, 1, K), pr.workspace_bytes(1, 1, M, N, 3, 1), 1),
+                         dtype=torch.uint8, device=dev)
 
-    def argk_lse():
-        pr.argkmin(x, y, K, idx=idx, workspace=ws)
-        pr.lse(x, y, sig, out=lse_out, workspace=ws)
+        def argk_lse():
+            pr.argkmin(x, y, K, idx=idx, workspace=ws)
+            pr.lse(x, y, sig, out=lse_out, workspace=ws)
 
-    t = _events_time(argk_lse, steps, warmup)
-    ta = _events_time(lambda: pr.argkmin(x, y, K, idx=idx, workspace=ws), steps, warmup)
-    tl = _events_time(lambda: pr.lse(x, y, sig, out=lse_out, workspace=ws), steps, warmup)
-    ws2 = torch.empty(max(pr.workspace_bytes(_lib.OP_ARGKMIN_LSE, 1, M, N, 3, 1, K), 1), dtype=torch.uint8,
-                      device=dev)
-    tf = _events_time(lambda: pr.argkmin_lse(x, y, K, sig, idx=idx, lse_out=lse_out, workspace=ws2), steps, warmup)
-    pairs = float(M) * N
-    rows["argkmin_lse_100k"] = {"ms": t * 1e3, "argkmin_ms": ta * 1e3, "lse_ms": tl * 1e3,
-                                "fused_ms": tf * 1e3, "pairs_per_s": 2 * pairs / t,
-                                "fused_pairs_per_s": pairs / tf}
+        t = _events_time(argk_lse, steps, warmup)
+        ta = _events_time(lambda: pr.argkmin(x, y, K, idx=idx, workspace=ws), steps, warmup)
+        tl = _events_time(lambda: pr.lse(x, y, sig, out=lse_out, workspace=ws), steps, warmup)
+        ws2 = torch.empty(max(pr.workspace_bytes(_lib.OP_ARGKMIN_LSE, 1, M, N, 3, 1, K), 1), dtype=torch.uint8,
+                          device=dev)
+        tf = _events_time(lambda: pr.argkmin_lse(x, y, K, sig, idx=idx, lse_out=lse_out, workspace=ws2), steps, warmup)
+        pairs = float(M) * N
+        rows["argkmin_lse_100k"] = {"ms": t * 1e3, "argkmin_ms": ta * 1e3, "lse_ms": tl * 1e3,
+                                    "fused_ms": tf * 1e3, "pairs_per_s": 2 * pairs / t,
+                                    "fused_pairs_per_s": pairs / tf}
+
     return rows
 
 
@@ -338,6 +355,8 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=8192, help="rows of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--all", action="store_true", help="also time the other workloads")
+    ap.add_argument("--only", choices=ALL_GROUPS, default=None,
+                    help="with --all: time one group of workloads and skip the headline line")
     ap.add_argument("--all-out", default="bench_all.json")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run one 256 MiB device-to-device copy (the reference kernel that scales the "
@@ -360,12 +379,14 @@ def main():
         print(json.dumps({"copy_bytes": a.numel() * 4}), flush=True)
         return
     if args.all:
-        rows = bench_all(args.steps, args.warmup)
+        rows = bench_all(args.steps, args.warmup, args.only)
         os.makedirs(os.path.dirname(os.path.abspath(args.all_out)), exist_ok=True)
         with open(args.all_out, "w") as f:
             json.dump(rows, f, indent=1)
         for k, v in rows.items():
             print(f"[all] {k}: " + ", ".join(f"{a}={b:.4g}" for a, b in v.items()), file=sys.stderr, flush=True)
+        if args.only:
+            return
     res = bench_gauss_1m(args.steps, args.warmup, args.cpu_rows, cpu_baseline=not args.no_cpu_baseline)
     print(json.dumps(res), flush=True)
 
