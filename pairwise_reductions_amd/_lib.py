@@ -48,6 +48,8 @@ _SIGNATURES = {
     "keops_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "keops_last_error": (ctypes.c_char_p, []),
     "keops_version": (ctypes.c_char_p, []),
+    "keops_sweep_timing": (ctypes.c_int, [ctypes.c_int]),
+    "keops_sweep_timing_read": (ctypes.c_int, [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_int)]),
 }
 
 _lib = None

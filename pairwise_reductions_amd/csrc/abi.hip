@@ -9,10 +9,29 @@
 #include <cstdio>
 #include <cstring>
 #include <string>
+#include <utility>
+#include <vector>
 
 namespace {
 
 thread_local std::string g_last_error;
+
+// Event pairs recorded around main-sweep launches while timing is enabled on this thread.
+struct SweepTiming {
+  bool on = false;
+  hipEvent_t open = nullptr;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> pairs;
+  void clear() {
+    if (open) (void)hipEventDestroy(open);
+    open = nullptr;
+    for (auto& pr : pairs) {
+      (void)hipEventDestroy(pr.first);
+      (void)hipEventDestroy(pr.second);
+    }
+    pairs.clear();
+  }
+};
+thread_local SweepTiming g_timing;
 
 int fail(int status, const char* fmt, ...) {
   char buf[512];
@@ -128,6 +147,34 @@ size_t argk_lse_bytes(int64_t M, int64_t N, int D, int K) {
   return lowd_layout(KEOPS_OP_ARGKMIN_LSE, M, N, D, 1, K).total + lowd_layout(KEOPS_OP_LSE, M, N, D, 1, 0).total;
 }
 
+}  // namespace
+
+namespace keops {
+// Called around the main sweep's launch (begin, then end) on its stream; records an event
+// pair while timing is enabled on this thread. Best effort: an event that cannot be created
+// or recorded is skipped, and keops_sweep_timing_read then counts fewer pairs.
+void sweep_event(hipStream_t s, bool begin) {
+  if (!g_timing.on) return;
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return;
+  if (hipEventRecord(e, s) != hipSuccess) {
+    (void)hipEventDestroy(e);
+    return;
+  }
+  if (begin) {
+    if (g_timing.open) (void)hipEventDestroy(g_timing.open);
+    g_timing.open = e;
+  } else if (g_timing.open) {
+    g_timing.pairs.emplace_back(g_timing.open, e);
+    g_timing.open = nullptr;
+  } else {
+    (void)hipEventDestroy(e);
+  }
+}
+}  // namespace keops
+
+namespace {
+
 int check_workspace(void* ws, size_t have, size_t need) {
   if (need == 0) return KEOPS_OK;
   if (!ws) return fail(KEOPS_ERR_INVALID_ARG, "workspace is NULL but %zu bytes are needed", need);
@@ -172,6 +219,32 @@ int device_cus() {
 extern "C" {
 
 const char* keops_version(void) { return "keops_mi355x 0.1.0 (gfx950)"; }
+
+int keops_sweep_timing(int enable) {
+  g_timing.clear();
+  g_timing.on = enable != 0;
+  return ok();
+}
+
+int keops_sweep_timing_read(float* ms, int* count) {
+  if (!ms || !count) return fail(KEOPS_ERR_INVALID_ARG, "ms and count must not be NULL");
+  double total = 0.0;
+  int n = 0;
+  hipError_t err = hipSuccess;
+  for (auto& pr : g_timing.pairs) {
+    float t = 0.0f;
+    err = hipEventSynchronize(pr.second);
+    if (err == hipSuccess) err = hipEventElapsedTime(&t, pr.first, pr.second);
+    if (err != hipSuccess) break;
+    total += t;
+    ++n;
+  }
+  g_timing.clear();
+  if (err != hipSuccess) return hip_fail(err, "sweep timing");
+  *ms = (float)total;
+  *count = n;
+  return ok();
+}
 
 const char* keops_status_string(int status) {
   switch (status) {

@@ -53,6 +53,9 @@ hipError_t launch_gauss_sum_lowd(const float* x, const float* y, double* cols, c
 // decision, two ints (gate, bad): the matrix-core sweep runs when gate != 0 and bad == 0; row
 // tiles per wave for C channels; preparation (also writes the float64 column table; b may be
 // null) and sweeps.
+// Measurement aid: records a HIP event pair on the stream around the main sweep's launch while
+// keops_sweep_timing is enabled on the calling thread (begin before the launch, end after).
+void sweep_event(hipStream_t s, bool begin);
 size_t mf_region_bytes(int64_t M, int64_t N, int D, int W, bool grad = false);  // W: floats per column record
 const int* mf_decision(const void* region);
 int mf_rows_per_lane(int op, int D, int C);   // op: 0 sum, 1 log-sum-exp, 3 gradient

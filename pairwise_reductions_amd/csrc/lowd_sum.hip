@@ -136,7 +136,9 @@ hipError_t launch_gauss_sum_lowd(const float* x, const float* y, double* cols, c
   };
   e = run();
   if (e != hipSuccess) return e;
+  sweep_event(s, true);
   e = launch_mf_sum(rscale, dst, mf, M, N, D, C, p, s);
+  sweep_event(s, false);
   if (e != hipSuccess || p.splits == 1) return e;
   return lowd::launch_combine_sum(partial, out, M * C, p.splits, rscale, C, s);
 }

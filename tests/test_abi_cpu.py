@@ -33,7 +33,8 @@ def test_exports_every_declared_symbol(lib):
                           "keops_gauss_sum_grad_y", "keops_gauss_sum_grad_b", "keops_argkmin_lse",
                           "keops_gauss_sum_scaled", "keops_gauss_sum_backward", "keops_diffusion_scaling",
                           "keops_argkmin_weighted",
-                          "keops_workspace_bytes", "keops_status_string", "keops_last_error", "keops_version"}
+                          "keops_workspace_bytes", "keops_status_string", "keops_last_error", "keops_version",
+                          "keops_sweep_timing", "keops_sweep_timing_read"}
     for name in names:
         assert hasattr(lib, name), name
     # the same names, resolved by the dynamic loader straight from the file
@@ -49,6 +50,17 @@ def test_status_strings_and_version(lib):
     assert lib.keops_status_string(3) == b"HIP runtime error"
     assert lib.keops_status_string(99) == b"unknown status"
     assert b"gfx950" in lib.keops_version()
+
+
+def test_sweep_timing_host_logic(lib):
+    """The measurement aid's bookkeeping (no event is created without a sweep launch)."""
+    ms, n = ctypes.c_float(-1.0), ctypes.c_int(-1)
+    assert lib.keops_sweep_timing(1) == 0
+    assert lib.keops_sweep_timing_read(ctypes.byref(ms), ctypes.byref(n)) == 0
+    assert ms.value == 0.0 and n.value == 0
+    assert lib.keops_sweep_timing_read(None, ctypes.byref(n)) == 1
+    assert "must not be NULL" in _err(lib)
+    assert lib.keops_sweep_timing(0) == 0
 
 
 def test_workspace_bytes(lib):
