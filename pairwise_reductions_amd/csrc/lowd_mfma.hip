@@ -519,9 +519,10 @@ gauss_sum_mf_kernel(const half8* __restrict__ rhi, const half8* __restrict__ rlo
 // A slot is settled once m >= kLseSettled (-64): the exponent is never positive (its computed
 // value exceeds 0 by a rounding far below 1), so the plain terms 2^e cannot overflow, and the
 // ones that underflow float32 (below 2^-126) are negligible against the row's largest term
-// (at least 2^(m - 1) >= 2^-65). Once every slot of the wave is settled, the loop adds the
-// plain terms into a second sum (no shift, no test) and folds it in at the end as
-// l + lraw 2^-m (m an integer: exact scaling; at most 2^31 terms times 2^64 stays finite).
+// (at least 2^(m - 1) >= 2^-65). Once every slot of the wave is settled, each slot's sum is
+// rescaled to the plain scale, l 2^m with m = 0 from then on (m an integer: exact, and
+// l 2^m >= 2^-81 stays normal), and the loop adds the plain terms 2^e with no shift and no
+// test.
 template <int RT, int NH, int NL>
 __global__ void __launch_bounds__(kBlock)
 lse_mf_kernel(const half8* __restrict__ rhi, const half8* __restrict__ rlo, const float* __restrict__ rA,
@@ -542,7 +543,7 @@ lse_mf_kernel(const half8* __restrict__ rhi, const half8* __restrict__ rlo, cons
 
   half8 ahi[RT], alo[RT][NL];
   f32x4 cinit[RT];
-  float m[RT][4], l[RT][4], lraw[RT][4];
+  float m[RT][4], l[RT][4];
 #pragma unroll
   for (int r = 0; r < RT; ++r) {
     int64_t i = base + r * 16 + l16;
@@ -556,7 +557,7 @@ lse_mf_kernel(const half8* __restrict__ rhi, const half8* __restrict__ rlo, cons
       ii = ii < M ? ii : M - 1;
       cinit[r][q] = rA[ii];
       m[r][q] = -INFINITY;
-      l[r][q] = lraw[r][q] = 0.0f;
+      l[r][q] = 0.0f;
     }
   }
   const int ochi = l16 * NH + (g < NH ? g : 0), oclo = l16 * 4 * NL + g;
@@ -608,7 +609,7 @@ lse_mf_kernel(const half8* __restrict__ rhi, const half8* __restrict__ rlo, cons
 #pragma unroll
       for (int n = 0; n < NL; ++n) t = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[r][n], o.l[n], t, 0, 0, 0);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) lraw[r][q] += exp2_hw(t[q]);
+      for (int q = 0; q < 4; ++q) l[r][q] += exp2_hw(t[q]);
     }
   };
   constexpr float kLseSettled = -64.0f;
@@ -633,6 +634,15 @@ lse_mf_kernel(const half8* __restrict__ rhi, const half8* __restrict__ rlo, cons
     tile(B);
     settled = all_settled();
   }
+  if (settled) {
+#pragma unroll
+    for (int r = 0; r < RT; ++r)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        l[r][q] *= exp2_hw(m[r][q]);
+        m[r][q] = 0.0f;
+      }
+  }
   for (; t < ntiles; t += 2) {
     const int64_t ja = j0 + t * 16;
     load(ja + 16, B);
@@ -640,12 +650,7 @@ lse_mf_kernel(const half8* __restrict__ rhi, const half8* __restrict__ rlo, cons
     load(t + 2 < ntiles ? ja + 32 : ja, A);
     tile_settled(B);
   }
-  if (settled) {
-#pragma unroll
-    for (int r = 0; r < RT; ++r)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) l[r][q] += lraw[r][q] * exp2_hw(-m[r][q]);
-  }
+
   // merge the 16 lanes of each row: m = max, l = sum l 2^(m_lane - m)
   const bool last = splits == 1;
 #pragma unroll
