@@ -46,7 +46,7 @@ combine_sum_kernel(const float* __restrict__ partial, float* __restrict__ out, i
 __global__ void __launch_bounds__(kBlock)
 combine_lse_kernel(const LsePartial* __restrict__ partial, float* __restrict__ out, int64_t M,
                    int64_t S, const int* __restrict__ mf, int run_if_mf) {
-  if (mf && ((mf[0] && !mf[1]) ? 1 : 0) != run_if_mf) return;  // the other form's partials
+  if (mf && mf_admits(mf) != run_if_mf) return;  // the other form's partials
   const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
   if (i >= M) return;
   double m = partial[i].m;

@@ -51,6 +51,15 @@ inline int argk_rows(int Kb) { return Kb <= 16 ? 2 : 1; }
 
 __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// The device-side decision of a prepared matrix-core sweep, mf = {gate, bad}: 1 when it admits
+// the matrix-core form (gate set, every piece exact), else 0. Both words are read and combined
+// as integers (a short-circuit form of this test, used to select a value rather than to
+// branch, was compiled into code that ignored its outcome).
+__device__ __forceinline__ int mf_admits(const int* mf) {
+  const int gate = mf[0], bad = mf[1];
+  return (gate != 0 ? 1 : 0) & (bad == 0 ? 1 : 0);
+}
+
 // Per-row partial of a log-sum-exp over one split: l = sum_j 2^{e_ij - m} with the float64
 // shift m in log2 units.
 struct LsePartial {

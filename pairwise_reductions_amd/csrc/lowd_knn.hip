@@ -68,25 +68,41 @@ max_norm_kernel(double* __restrict__ cols, const float* __restrict__ w, int64_t 
   if (threadIdx.x == 0) *out = red[0];
 }
 
-// Screening bound: the float64 expansion a = |x|^2 + (|y|^2 - w) - 2 x.y (D+1 FMAs after the
-// norms, each rounded once) differs from the key d^2 - w by at most
-// (4D + 12) 2^-53 (|x|^2 + |y|^2 + |w|) <= 2^-46 (|x|^2 + max_j (|y_j|^2 + |w_j|)) for D <= 8
-// (w = 0 without weights).
+// Screening bound: the float64 expansion a' = (|y|^2 - w) - 2 x.y (D FMAs from the column's
+// table entry, each rounded once) is compared with the row's threshold (key_K - |x|^2) + margin,
+// key_K the row's current K-th key. With u = 2^-53 and B = |x|^2 + max_j (|y_j|^2 + |w_j|):
+// a' differs from d^2 - w - |x|^2 by at most 2D u B (2|x_d y_d| <= x_d^2 + y_d^2), the row
+// norm |x|^2 (D FMAs) by D u B, the subtraction key_K - |x|^2 (key_K <= 2B) by 3 u B and the
+// added margin by 3 u B: (3D + 6) u B in all, below 2^-46 B for D <= 8 (w = 0 without
+// weights).
 constexpr double kScreenMargin = 1.4210854715202004e-14;  // 2^-46
 
 // argKmin of d^2_ij - w_j (w_j = 0 when w is null; with LSE, also the log-sum-exp of -c2 d^2 in
 // base 2, never combined with weights) over the columns of one split.
-// Each pair first gets the cheap expansion a_ij. A column whose a_ij is below the row's K-th
-// key plus the margin is only queued (its index goes into the lane's queue in LDS); when some
-// lane's queue could overflow on the next tile, every lane of the wave computes the exact keys
-// of its queued columns, in column order, and updates its sorted list and threshold. The
-// wave thus runs the list updates once per kQueue candidates of its busiest lane instead of
-// once per tile in which any of its 64 lanes has a candidate. The threshold a column is
-// screened against may lag behind the list (it is refreshed at each flush), which only
-// queues extra columns. For the log-sum-exp the row's running shift m (log2 units) is raised
-// lazily, whenever a tile holds a term above 2^kLseSlack, so every term 2^(-c2 a_ij - m) stays
-// below 2^kLseSlack.
+// Each pair first gets the cheap expansion a'_ij. A column whose a'_ij is below the row's
+// threshold is only queued (its index goes into the lane's queue in LDS); for K <= 16 the
+// queueing runs only in tiles where some lane of the wave has such a column (a wave-uniform
+// branch), so the common tile costs the D FMAs and one compare per pair. When some lane's queue could overflow,
+// every lane of the wave computes the exact keys of its queued columns, in column order, and
+// updates its sorted list and threshold. The wave thus runs the list updates once per kQueue
+// candidates of its busiest lane instead of once per tile in which any of its 64 lanes has a
+// candidate. The threshold a column is screened against may lag behind the list (it is
+// refreshed at each flush), which only queues extra columns. For the log-sum-exp the row's
+// running shift m (log2 units) is raised lazily, whenever a tile holds a term above
+// 2^kLseSlack, so every term 2^(-c2 (|x|^2 + a'_ij) - m) stays below 2^kLseSlack.
 constexpr int kQueue = 16;  // queued candidate columns per lane and row
+
+// A pointer into the constant address space: loads through it at a wave-uniform address are
+// scalar loads (the data is read-only for the whole launch).
+template <typename T>
+using ConstPtr = const __attribute__((address_space(4))) T*;
+
+// The value of a wave-uniform 64-bit integer, held in scalar registers.
+__device__ __forceinline__ int64_t uniform(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
 
 template <int D, int K, int R, bool LSE>
 __global__ void __launch_bounds__(kBlock)
@@ -94,7 +110,7 @@ knn_kernel(const float* __restrict__ x, const double* __restrict__ cols, const f
            const double* __restrict__ ymax, int32_t* __restrict__ idx, float* __restrict__ dist, KeyIdx* __restrict__ partial,
            float* __restrict__ lse_out, LsePartial* __restrict__ lse_partial, int64_t M, int64_t N,
            int64_t cps, int Kout, double c2, const int* __restrict__ mf, int run_if_mf) {
-  if (mf && ((mf[0] && !mf[1]) ? 1 : 0) != run_if_mf) return;  // the other form takes these inputs
+  if (mf && mf_admits(mf) != run_if_mf) return;  // the other form takes these inputs
   constexpr int P = (D + 2) & ~1;
   constexpr int U = D <= 4 ? 4 : 2;  // columns per screened tile
   static_assert(kQueue >= 2 * U, "queue holds at least two tiles");
@@ -105,10 +121,11 @@ knn_kernel(const float* __restrict__ x, const double* __restrict__ cols, const f
   const int64_t row0 = (int64_t)blockIdx.x * (kBlock * R) + threadIdx.x;
   const double bmax = *ymax;
 
-  double xd[R][D], xp[R][D], A[R], marg[R], thr[R];
+  double xd[R][D], xp[R][D], A[R], marg[R], thr[R], off[R];
   double keys[R][K];
   int32_t ids[R][K];
   int cnt[R];
+  bool full[R];  // wave-uniform: some lane's queue could overflow on the next tile
   double mref[R];
   float l[R];
 #pragma unroll
@@ -131,7 +148,9 @@ knn_kernel(const float* __restrict__ x, const double* __restrict__ cols, const f
       ids[r][k] = -1;
     }
     cnt[r] = 0;
+    full[r] = false;
     mref[r] = -INFINITY;
+    off[r] = 0.0;
     l[r] = 0.0f;
   }
 
@@ -143,54 +162,76 @@ knn_kernel(const float* __restrict__ x, const double* __restrict__ cols, const f
       if (w) key -= (double)w[jj];
       if (key < keys[r][K - 1]) topk_insert<K>(keys[r], ids[r], key, jj);
     }
-    thr[r] = keys[r][K - 1] + marg[r];
+    thr[r] = (keys[r][K - 1] - A[r]) + marg[r];
     cnt[r] = 0;
   };
 
   // Columns [j, j + n) of a tile, n <= U, for row r: screen, queue, add LSE terms.
   auto tile = [&](int r, int64_t j, int n, const double (&yv)[U][D], const double (&bv)[U]) {
-    if (__any(cnt[r] > kQueue - U)) flush(r);
+    if (full[r]) {
+      flush(r);
+      full[r] = false;
+    }
     double a[U];
-    double mn = INFINITY;
+    bool hit[U];
+    uint64_t hits = 0;  // lanes with a candidate in this tile
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      if (u < n) {
-        double t = A[r] + bv[u];
+      double t = bv[u];
 #pragma unroll
-        for (int d = 0; d < D; ++d) t = fma(xp[r][d], yv[u][d], t);
-        a[u] = t;
-        mn = fmin(mn, t);
+      for (int d = 0; d < D; ++d) t = fma(xp[r][d], yv[u][d], t);
+      a[u] = t;
+      hit[u] = u < n && t < thr[r];
+      hits |= __ballot(hit[u]);
+    }
+    // At K > 16 most tiles hold candidates somewhere in the wave: queue without the test.
+    if (K > 16 || __builtin_expect(hits != 0, 0)) {
+      // at most kQueue - U entries on entry, so the U writes stay inside the queue
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
         // written every time, kept only when the count advances
         queue[r][cnt[r]][threadIdx.x] = (int32_t)(j + u);
-        cnt[r] += (t < thr[r]) ? 1 : 0;
+        cnt[r] += hit[u] ? 1 : 0;
       }
+      full[r] = __any(cnt[r] > kQueue - U);
     }
     if constexpr (LSE) {
-      const double nm = -c2 * mn;
+      double mn = INFINITY;
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (u < n) mn = fmin(mn, a[u]);
+      const double nm = fma(mn, -c2, -c2 * A[r]);
       if (nm > mref[r] + (double)kLseSlack) {
         l[r] *= exp2_hw((float)(mref[r] - nm));
         mref[r] = nm;
+        off[r] = -c2 * A[r] - nm;
       }
       float t = 0.0f;
 #pragma unroll
       for (int u = 0; u < U; ++u)
-        if (u < n) t += exp2_hw((float)fma(a[u], -c2, -mref[r]));
+        if (u < n) t += exp2_hw((float)fma(a[u], -c2, off[r]));
       l[r] += t;
     }
   };
 
-  int64_t j = j0;
-  for (; j + U <= j1; j += U) {
+  // The column records are the same for every lane: with two rows per lane they are read
+  // through the scalar unit (at K > 16 the scalar registers they would take are short).
+  ConstPtr<double> ccols = (ConstPtr<double>)cols;
+  auto col = [&](int64_t e) { return R == 2 ? ccols[e] : cols[e]; };
+  const int64_t nfull = (j1 - j0) / U;  // whole tiles of the split
+  for (int64_t t = 0; t < nfull; ++t) {
+    const int64_t ja = uniform(j0 + t * U);
     double yv[U][D], bv[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
 #pragma unroll
-      for (int d = 0; d < D; ++d) yv[u][d] = cols[(j + u) * P + d];
-      bv[u] = cols[(j + u) * P + D];
+      for (int d = 0; d < D; ++d) yv[u][d] = col((ja + u) * P + d);
+      bv[u] = col((ja + u) * P + D);
     }
 #pragma unroll
-    for (int r = 0; r < R; ++r) tile(r, j, U, yv, bv);
+    for (int r = 0; r < R; ++r) tile(r, ja, U, yv, bv);
   }
+  const int64_t j = j0 + nfull * U;
   if (j < j1) {
     const int n = (int)(j1 - j);
     double yv[U][D], bv[U];
