@@ -174,6 +174,15 @@ def cpu_baseline_gauss(inp, rows):
             "seconds": dt}
 
 
+def _oracle_rate(fn, pairs, sample):
+    """The CPU oracle's rate on a bounded sample of a workload (timed beside the device figure)."""
+    t0 = time.perf_counter()
+    fn()
+    dt = time.perf_counter() - t0
+    return {"oracle_pairs_per_s": pairs / dt, "oracle_sample": f"{sample} ({pairs:.3g} pairs, {dt:.2f} s)",
+            "oracle_cores": os.cpu_count() or 1}
+
+
 def _resident(inp, keys, dev):
     import torch
     return [torch.from_numpy(inp[k]).to(dev) for k in keys]
@@ -183,9 +192,11 @@ ALL_GROUPS = ("gauss_sum_10k", "grad_100k", "fp16", "fp16_fwd_bwd", "fp16_d_swee
               "argkmin_lse")
 
 
-def bench_all(steps, warmup, only=None):
+def bench_all(steps, warmup, only=None, cpu=True):
     """Time every workload through the library (inputs resident on the GPU); `only` names one
-    group of ALL_GROUPS."""
+    group of ALL_GROUPS. With `cpu`, each group also reports the CPU oracle's rate on a bounded
+    row sample of the same inputs (a few seconds each)."""
+    import numpy as np
     import torch
 
     import pairwise_reductions_amd as pr
@@ -208,6 +219,11 @@ def bench_all(steps, warmup, only=None):
         pairs = float(inp["M"]) * inp["N"]
         rows["gauss_sum_10k"] = {"ms": t * 1e3, "pairs_per_s": pairs / t,
                                  "frac_fp32_peak": pairs * 12 / t / 1e12 / PEAK_FP32_VECTOR_TFLOPS}
+        if cpu:
+            import oracle
+            rows["gauss_sum_10k"].update(_oracle_rate(
+                lambda: oracle.gauss_sum(inp["x"], inp["y"], inp["b"], sig, workers=os.cpu_count()),
+                pairs, "all rows x all columns"))
 
     # Gauss sum forward + gradient of sum_i s_i^2 (g = 2 s), 100k mixture
     if want("grad_100k"):
@@ -233,6 +249,17 @@ def bench_all(steps, warmup, only=None):
         rows["gauss_sum_grad_x_100k_mixture"] = {
             "ms": t * 1e3, "fwd_ms": tf * 1e3, "grad_ms": tb * 1e3, "pairs_per_s": 2 * pairs / t,
             "frac_fp32_peak": pairs * (12 + grad_flops_per_pair(3, 1)) / t / 1e12 / PEAK_FP32_VECTOR_TFLOPS}
+        if cpu:
+            import oracle
+            n = 1024
+            gs = workloads.upstream_gradient(n, 1, seed=2)
+
+            def oracle_fwd_bwd():
+                oracle.gauss_sum(inp["x"][:n], inp["y"], inp["b"], sig, workers=os.cpu_count())
+                oracle.gauss_sum_grad_x(inp["x"][:n], inp["y"], inp["b"], gs, sig, workers=os.cpu_count())
+
+            rows["gauss_sum_grad_x_100k_mixture"].update(_oracle_rate(
+                oracle_fwd_bwd, 2.0 * n * N, f"forward + gradient, first {n} rows x all {N} columns"))
 
     # Batched Gauss sum, fp16 matrix-core path: B=4, M=N=16384, D=C=32, tau=1
     if want("fp16"):
@@ -249,6 +276,13 @@ def bench_all(steps, warmup, only=None):
         rows["batched_gauss_sum_fp16"] = {"ms": t * 1e3, "pairs_per_s": pairs / t,
                                           "mfma_tflops": mflops / t / 1e12,
                                           "frac_fp16_mfma_peak": mflops / t / 1e12 / PEAK_FP16_MFMA_TFLOPS}
+        if cpu:
+            import oracle
+            n = 256
+            rows["batched_gauss_sum_fp16"].update(_oracle_rate(
+                lambda: oracle.gauss_sum_batched(inp["x"][:, :n], inp["y"], inp["b"], 1.0 / float(inp["sigma"]) ** 2,
+                                                 workers=os.cpu_count()),
+                float(Bt) * n * N, f"first {n} rows of each of the {Bt} problems x all {N} columns"))
 
     # Batched Gauss sum forward + backward, fp16: B=4, M=N=16384, D=32, C=1 (the flash page's
     # Figure 2 shape); the backward computes the gradients with respect to x, y and b.
@@ -330,6 +364,14 @@ def bench_all(steps, warmup, only=None):
                                                       workspace=ws), steps, warmup)
         rows["diffusion_operator_fp32_n131072_d3"] = {"scaling_ms": ts * 1e3, "apply_block4_ms": ta * 1e3,
                                                       "apply_pairs_per_s": float(N) * N / ta}
+        if cpu:
+            import oracle
+            n = 1024
+            xh, vh, sh = xs.cpu().numpy(), vb.cpu().numpy(), sv.cpu().numpy()
+            rows["diffusion_operator_fp32_n131072_d3"].update(_oracle_rate(
+                lambda: oracle.gauss_sum_scaled(xh[:n], xh, vh, 0.05, row_scale=sh[:n], col_scale=sh,
+                                                workers=os.cpu_count()),
+                float(n) * N, f"one block-4 application, first {n} rows x all {N} columns"))
 
     # argKmin (K=10) + log-sum-exp, 100k uniform
     if want("argkmin_lse"):
@@ -356,6 +398,16 @@ def bench_all(steps, warmup, only=None):
         rows["argkmin_lse_100k"] = {"ms": t * 1e3, "argkmin_ms": ta * 1e3, "lse_ms": tl * 1e3,
                                     "fused_ms": tf * 1e3, "pairs_per_s": 2 * pairs / t,
                                     "fused_pairs_per_s": pairs / tf}
+        if cpu:
+            import oracle
+            n = 512
+
+            def oracle_argk_lse():
+                oracle.argkmin(inp["x"][:n], inp["y"], K, workers=os.cpu_count())
+                oracle.logsumexp_reduction(inp["x"][:n], inp["y"], sig, workers=os.cpu_count())
+
+            rows["argkmin_lse_100k"].update(_oracle_rate(
+                oracle_argk_lse, 2.0 * n * N, f"argKmin and LSE, first {n} rows x all {N} columns"))
 
     return rows
 
@@ -392,12 +444,13 @@ def main():
         print(json.dumps({"copy_bytes": a.numel() * 4}), flush=True)
         return
     if args.all:
-        rows = bench_all(args.steps, args.warmup, args.only)
+        rows = bench_all(args.steps, args.warmup, args.only, cpu=not args.no_cpu_baseline)
         os.makedirs(os.path.dirname(os.path.abspath(args.all_out)), exist_ok=True)
         with open(args.all_out, "w") as f:
             json.dump(rows, f, indent=1)
         for k, v in rows.items():
-            print(f"[all] {k}: " + ", ".join(f"{a}={b:.4g}" for a, b in v.items()), file=sys.stderr, flush=True)
+            print(f"[all] {k}: " + ", ".join(f"{a}={b:.4g}" if isinstance(b, float) else f"{a}={b}"
+                                             for a, b in v.items()), file=sys.stderr, flush=True)
         if args.only:
             return
     res = bench_gauss_1m(args.steps, args.warmup, args.cpu_rows, cpu_baseline=not args.no_cpu_baseline)
