@@ -201,7 +201,9 @@ def test_lse_far_rows_and_empty():
 
 ARGK_SHAPES = [(1, 1, 3, 1), (257, 1000, 3, 10), (1025, 513, 1, 4), (700, 2000, 2, 16),
                (513, 1500, 8, 32), (100, 100_003, 3, 10), (50_001, 777, 3, 10), (300, 64, 3, 64),
-               (200, 5000, 3, 64), (333, 20, 5, 20), (1000, 3000, 3, 3)]
+               (200, 5000, 3, 64), (333, 20, 5, 20), (1000, 3000, 3, 3),
+               # two rows per lane with two-column tiles (D > 4), odd column counts
+               (513, 1501, 8, 10), (401, 2999, 5, 8), (129, 4097, 6, 2)]
 
 
 @pytest.mark.parametrize("M,N,D,K", ARGK_SHAPES)

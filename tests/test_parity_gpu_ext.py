@@ -241,7 +241,7 @@ def test_diffusion_operator_eigenvector():
 
 # ------------------------------------------------------------------ weighted argKmin
 WARGK_SHAPES = [(1, 1, 3, 1), (257, 1000, 3, 10), (1025, 513, 1, 4), (700, 2000, 2, 16), (300, 5000, 8, 64),
-                (2000, 70_001, 3, 1), (4097, 20_000, 3, 32)]
+                (2000, 70_001, 3, 1), (4097, 20_000, 3, 32), (350, 1999, 7, 4)]
 
 
 def _grid(rng, shape, bits=24):
