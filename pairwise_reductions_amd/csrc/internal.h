@@ -60,6 +60,7 @@ size_t mf_region_bytes(int64_t M, int64_t N, int D, int W, bool grad = false);  
 const int* mf_decision(const void* region);
 int mf_rows_per_lane(int op, int D, int C);   // op: 0 sum, 1 log-sum-exp, 3 gradient
 int mf_occupancy(int op, int D, int C, int rt);  // resident workgroups per CU of that sweep
+int knn_occupancy(int D, int K);                 // resident workgroups per CU of the argKmin sweep
 hipError_t launch_mf_prepare(const float* x, const float* y, const float* b, bool with_y, double* cols,
                              void* region, int64_t M, int64_t N, int D, int C, double c2, hipStream_t s);
 // gradient with respect to x, one channel: dst[i][d] = -(g_i / sigma^2) sum_j k_ij b_j (x_i - y_j)

@@ -195,6 +195,31 @@ Plan plan_lowd(int op, int64_t M, int64_t N, int D, int C, int K, int num_cus) {
     S = best_s;
     cps = best_cps;
   }
+  // argKmin: every split finds its rows' K smallest keys afresh, so fewer splits queue fewer
+  // candidates. Among 1..8 splits (keeping the L2 bound), take the fewest whose workgroups fill
+  // their rounds of resident slots within 2 % of the best fill (100k x 100k, K = 10: 5 splits
+  // in one round instead of 11 in three, 3.21 -> 3.01 ms).
+  if ((op == 2 || op == 6) && p.row_blocks > 0) {
+    const int64_t slots = (int64_t)num_cus * knn_occupancy(D, K);
+    const int64_t s_min = ceil_div(N, lowd::kSplitCols);
+    const int64_t s_max = max_split < 8 ? max_split : 8;
+    double fill[9] = {};
+    int64_t real[9] = {}, cpss[9] = {};
+    double best = -1.0;
+    for (int64_t s = 1; s <= s_max; ++s) {
+      if (s < s_min) continue;
+      real[s] = split_of(s, cpss[s]);
+      const int64_t total = p.row_blocks * real[s];
+      fill[s] = (double)total / (double)(ceil_div(total, slots) * slots);
+      if (fill[s] > best) best = fill[s];
+    }
+    for (int64_t s = 1; s <= s_max; ++s) {
+      if (s < s_min || fill[s] < best - 0.02) continue;
+      S = real[s];
+      cps = cpss[s];
+      break;
+    }
+  }
   p.splits = S;
   p.cols_per_split = cps;
   return p;

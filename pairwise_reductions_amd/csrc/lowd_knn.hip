@@ -2,6 +2,8 @@
 // of a row), alone or fused with the log-sum-exp reduction in the same sweep.
 #include "lowd_common.h"
 
+#include <atomic>
+
 namespace keops {
 namespace lowd {
 namespace {
@@ -358,8 +360,70 @@ hipError_t knn_d(int Kb, const float* x, const double* cols, const float* w, con
   return hipErrorInvalidValue;
 }
 
+// Resident workgroups per CU of the plain sweep: the runtime's figure, but with the LDS queues
+// strictly inside the CU's LDS (workgroups whose queues would fill it exactly, 5 x 32 KB of
+// 160 KB, measured as 4 resident).
+template <int D, int K>
+int occupancy_dk(int dev) {
+  constexpr int R = K <= 16 ? 2 : 1;
+  auto kernel = knn_kernel<D, K, R, false>;
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, kBlock, 0) != hipSuccess || n < 1) return 1;
+  hipFuncAttributes attr;
+  int lds_cu = 0;
+  if (hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(kernel)) == hipSuccess && attr.sharedSizeBytes > 0 &&
+      hipDeviceGetAttribute(&lds_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) == hipSuccess &&
+      lds_cu > 0) {
+    const int fit = (int)((lds_cu - 1) / (int)attr.sharedSizeBytes);
+    if (fit < n) n = fit > 0 ? fit : 1;
+  }
+  return n;
+}
+
+template <int D>
+int occupancy_d(int Kb, int dev) {
+  switch (Kb) {
+    case 1: return occupancy_dk<D, 1>(dev);
+    case 2: return occupancy_dk<D, 2>(dev);
+    case 4: return occupancy_dk<D, 4>(dev);
+    case 8: return occupancy_dk<D, 8>(dev);
+    case 10: return occupancy_dk<D, 10>(dev);
+    case 16: return occupancy_dk<D, 16>(dev);
+    case 32: return occupancy_dk<D, 32>(dev);
+    case 64: return occupancy_dk<D, 64>(dev);
+  }
+  return 1;
+}
+
 }  // namespace
 }  // namespace lowd
+
+int knn_occupancy(int D, int K) {
+  // resident workgroups per CU of the plain argKmin sweep (cached per instance; 1 when the
+  // runtime cannot say)
+  static std::atomic<int> cache[kMaxLowD + 1][8];
+  int dev = 0;
+  if (D < 1 || D > kMaxLowD || K < 1 || hipGetDevice(&dev) != hipSuccess) return 1;
+  static const int kBuckets[8] = {1, 2, 4, 8, 10, 16, 32, 64};
+  const int Kb = lowd::argk_bucket(K);
+  int kslot = 0;
+  while (kBuckets[kslot] != Kb) ++kslot;
+  std::atomic<int>& slot = cache[D][kslot];
+  int n = slot.load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  switch (D) {
+    case 1: n = lowd::occupancy_d<1>(Kb, dev); break;
+    case 2: n = lowd::occupancy_d<2>(Kb, dev); break;
+    case 3: n = lowd::occupancy_d<3>(Kb, dev); break;
+    case 4: n = lowd::occupancy_d<4>(Kb, dev); break;
+    case 5: n = lowd::occupancy_d<5>(Kb, dev); break;
+    case 6: n = lowd::occupancy_d<6>(Kb, dev); break;
+    case 7: n = lowd::occupancy_d<7>(Kb, dev); break;
+    case 8: n = lowd::occupancy_d<8>(Kb, dev); break;
+  }
+  slot.store(n, std::memory_order_relaxed);
+  return n;
+}
 
 hipError_t launch_knn_lowd(const float* x, const float* y, const float* w, double* cols, double* ymax,
                            int32_t* idx, float* dist, void* partial, float* lse_out, double* lse_partial, int64_t M,
