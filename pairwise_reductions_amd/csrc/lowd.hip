@@ -197,8 +197,9 @@ Plan plan_lowd(int op, int64_t M, int64_t N, int D, int C, int K, int num_cus) {
   }
   // argKmin: every split finds its rows' K smallest keys afresh, so fewer splits queue fewer
   // candidates. Among 1..8 splits (keeping the L2 bound), take the fewest whose workgroups fill
-  // their rounds of resident slots within 2 % of the best fill (100k x 100k, K = 10: 5 splits
-  // in one round instead of 11 in three, 3.21 -> 3.01 ms).
+  // their rounds of resident slots to at least 98 % of the best fill (100k x 100k, K = 10: 5
+  // splits in one round instead of 11 in three, 3.21 -> 3.01 ms; with few row blocks the fill
+  // grows with the split count, so the most splits win).
   if ((op == 2 || op == 6) && p.row_blocks > 0) {
     const int64_t slots = (int64_t)num_cus * knn_occupancy(D, K);
     const int64_t s_min = ceil_div(N, lowd::kSplitCols);
@@ -214,7 +215,7 @@ Plan plan_lowd(int op, int64_t M, int64_t N, int D, int C, int K, int num_cus) {
       if (fill[s] > best) best = fill[s];
     }
     for (int64_t s = 1; s <= s_max; ++s) {
-      if (s < s_min || fill[s] < best - 0.02) continue;
+      if (s < s_min || fill[s] < 0.98 * best) continue;
       S = real[s];
       cps = cpss[s];
       break;
