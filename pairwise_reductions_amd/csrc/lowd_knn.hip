@@ -44,14 +44,20 @@ __device__ __forceinline__ double sq_dist_key(const double (&xu)[D], const doubl
 }
 
 // Largest |y_j|^2 + |w_j| over the column table (cols[j][D] holds |y_j|^2 on entry; w may be
-// null), one workgroup, fixed reduction order. With weights the table's screening term becomes
-// |y_j|^2 - w_j (each entry is rewritten by the one thread that reads it).
-__global__ void __launch_bounds__(1024)
+// null). Each workgroup reduces a grid-strided share and folds it into *out with an atomic
+// maximum on the bit patterns (non-negative doubles order like their bits), so the result is
+// the exact maximum in any order; *out is cleared by zero_kernel first. With weights the
+// table's screening term becomes |y_j|^2 - w_j (each entry is rewritten by the one thread that
+// reads it).
+__global__ void zero_kernel(double* __restrict__ out) { *out = 0.0; }
+
+__global__ void __launch_bounds__(256)
 max_norm_kernel(double* __restrict__ cols, const float* __restrict__ w, int64_t N, int P, int D,
                 double* __restrict__ out) {
-  __shared__ double red[1024];
+  __shared__ double red[256];
   double m = 0.0;
-  for (int64_t j = threadIdx.x; j < N; j += 1024) {
+  const int64_t step = (int64_t)gridDim.x * 256;
+  for (int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x; j < N; j += step) {
     const double yy = cols[j * P + D];
     if (w) {
       const double wj = (double)w[j];
@@ -63,11 +69,12 @@ max_norm_kernel(double* __restrict__ cols, const float* __restrict__ w, int64_t 
   }
   red[threadIdx.x] = m;
   __syncthreads();
-  for (int w = 512; w > 0; w >>= 1) {
-    if ((int)threadIdx.x < w) red[threadIdx.x] = fmax(red[threadIdx.x], red[threadIdx.x + w]);
+  for (int h = 128; h > 0; h >>= 1) {
+    if ((int)threadIdx.x < h) red[threadIdx.x] = fmax(red[threadIdx.x], red[threadIdx.x + h]);
     __syncthreads();
   }
-  if (threadIdx.x == 0) *out = red[0];
+  if (threadIdx.x == 0)
+    atomicMax(reinterpret_cast<unsigned long long*>(out), (unsigned long long)__double_as_longlong(red[0]));
 }
 
 // Screening bound: the float64 expansion a' = (|y|^2 - w) - 2 x.y (D FMAs from the column's
@@ -433,7 +440,9 @@ hipError_t launch_knn_lowd(const float* x, const float* y, const float* w, doubl
   // screening margin
   hipError_t e = launch_prep_cols(y, cols, N, D, -1.0, false, s);
   if (e != hipSuccess) return e;
-  lowd::max_norm_kernel<<<1, 1024, 0, s>>>(cols, w, N, col_stride(D), D, ymax);
+  lowd::zero_kernel<<<1, 1, 0, s>>>(ymax);
+  const int64_t nb = lowd::ceil_div(N, 256);
+  lowd::max_norm_kernel<<<(unsigned)(nb < 512 ? nb : 512), 256, 0, s>>>(cols, w, N, col_stride(D), D, ymax);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int Kb = lowd::argk_bucket(K);
