@@ -571,18 +571,25 @@ lse_mf_kernel(const half8* __restrict__ rhi, const half8* __restrict__ rlo, cons
 #pragma unroll
     for (int n = 0; n < NL; ++n) o.l[n] = pl[oclo + 4 * n];
   };
+  // While the shift is tracked, the high and low parts of the exponent stay in separate
+  // accumulators: eh is exact (a multiple of 2^gamma), so eh - m is exact for every term within
+  // 2^(gamma+24) >= 64 of the shift, and d = (eh - m) + el rounds relative to the small shifted
+  // exponent instead of to |e|. Rows far from every column (|e| in the thousands, where one
+  // float32 rounding of e alone is 2^-11 or more) then keep their log-sum-exp to a few 1e-7.
   auto tile = [&](const Ops& o) {
-    float e[RT][4], d[RT][4];
+    float eh[RT][4], el[RT][4], d[RT][4];
     float dmax = -INFINITY;
 #pragma unroll
     for (int r = 0; r < RT; ++r) {
-      f32x4 t = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[r], o.h, cinit[r], 0, 0, 0);
+      const f32x4 th = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[r], o.h, cinit[r], 0, 0, 0);
+      f32x4 tl = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int n = 0; n < NL; ++n) t = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[r][n], o.l[n], t, 0, 0, 0);
+      for (int n = 0; n < NL; ++n) tl = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[r][n], o.l[n], tl, 0, 0, 0);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        e[r][q] = t[q];
-        d[r][q] = t[q] - m[r][q];
+        eh[r][q] = th[q];
+        el[r][q] = tl[q];
+        d[r][q] = (th[q] - m[r][q]) + tl[q];
         dmax = fmaxf(dmax, d[r][q]);
       }
     }
@@ -591,10 +598,10 @@ lse_mf_kernel(const half8* __restrict__ rhi, const half8* __restrict__ rlo, cons
       for (int r = 0; r < RT; ++r)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const float mn = fmaxf(m[r][q], ceilf(e[r][q]));
+          const float mn = fmaxf(m[r][q], ceilf(eh[r][q] + el[r][q]));
           l[r][q] *= exp2_hw(m[r][q] - mn);
           m[r][q] = mn;
-          d[r][q] = e[r][q] - mn;
+          d[r][q] = (eh[r][q] - mn) + el[r][q];
         }
     }
 #pragma unroll

@@ -14,6 +14,7 @@ if TESTS not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
     config.addinivalue_line("markers", "slow: CPU test that takes more than a few seconds")
+    config.addinivalue_line("markers", "full: GPU test of a whole full-size workload (minutes of oracle time)")
 
 
 def pytest_collection_modifyitems(config, items):

@@ -32,9 +32,10 @@ def _announce(name, **kw):
 
 
 def lse_bound(want):
-    """1e-4 absolute, widened to 4 float32 ulps where |lse| is so large that the float32
-    output itself cannot carry 1e-4 (|lse| above about 200)."""
-    return np.maximum(TOL_LSE, 4.0 * np.finfo(np.float32).eps * np.abs(want))
+    """1e-4 absolute, or one float32 ulp of |lse| where that is larger (|lse| >= 2048: there
+    the correctly rounded float32 output alone may be 1.2e-4 or more away from the exact
+    value)."""
+    return np.maximum(TOL_LSE, np.spacing(np.abs(want).astype(np.float32)).astype(np.float64))
 
 
 def assert_normalised(got, want, norm, tol, what=""):
@@ -368,72 +369,6 @@ def test_gauss_sum_fp16_far_rows_and_rescale():
     _check_highd(qn, kn, vn, 0.25)
 
 
-def test_gauss_sum_fp16_workload_sampled():
-    """The B=4, M=N=16384, D=C=32 workload at full size, checked on sampled rows."""
-    import pairwise_reductions_amd as pr
-    inp = workloads.make_inputs("batched_gauss_sum_fp16")
-    _announce("gauss_sum_fp16_workload", B=inp["B"], M=inp["M"], N=inp["N"])
-    got = _host(pr.gauss_sum(_dev(inp["x"]), _dev(inp["y"]), _dev(inp["b"]), float(inp["sigma"])))
-    rows = workloads.sample_rows(inp["M"], 256, seed=3)
-    want, norm = oracle.gauss_sum_batched(inp["x"][:, rows], inp["y"], inp["b"], 1.0, workers=8)
-    assert_normalised(got[:, rows], want, norm, TOL_F16, "fp16 workload")
-
-
-# ------------------------------------------------- full-size workloads, sampled rows
-# The device runs the whole workload in the configuration bench.py times; the oracle
-# computes a seeded sample of rows (plus the first and last 64) against every column.
-
-def test_gauss_sum_workload_1m_sampled():
-    import pairwise_reductions_amd as pr
-    inp = workloads.make_inputs("gauss_sum_1m")
-    _announce("gauss_sum_1m", M=inp["M"], N=inp["N"])
-    sig = float(inp["sigma"])
-    got = _host(pr.gauss_sum(_dev(inp["x"]), _dev(inp["y"]), _dev(inp["b"]), sig))
-    rows = workloads.sample_rows(inp["M"], 256, seed=1)
-    want, norm = oracle.gauss_sum(inp["x"][rows], inp["y"], inp["b"], sig, workers=8)
-    assert_normalised(got[rows], want, norm, TOL_F32, "gauss_sum_1m")
-
-
-def test_grad_x_workload_100k_mixture_sampled():
-    import pairwise_reductions_amd as pr
-    inp = workloads.make_inputs("gauss_sum_grad_x_100k_mixture")
-    M, N, C = inp["M"], inp["N"], inp["C"]
-    _announce("gauss_sum_grad_x_100k", M=M, N=N)
-    sig = float(inp["sigma"])
-    g = workloads.upstream_gradient(M, C)
-    xd, yd, bd = _dev(inp["x"]), _dev(inp["y"]), _dev(inp["b"])
-    s = _host(pr.gauss_sum(xd, yd, bd, sig))
-    grad = _host(pr.gauss_sum_grad_x(xd, yd, bd, _dev(g), sig))
-    rows = workloads.sample_rows(M, 512, seed=1)
-    want_s, norm_s = oracle.gauss_sum(inp["x"][rows], inp["y"], inp["b"], sig, workers=8)
-    assert_normalised(s[rows], want_s, norm_s, TOL_F32, "forward 100k")
-    want_g, norm_g = oracle.gauss_sum_grad_x(inp["x"][rows], inp["y"], inp["b"], g[rows], sig, workers=8)
-    assert_normalised(grad[rows], want_g, norm_g, TOL_F32, "grad_x 100k")
-
-
-def test_argkmin_lse_workload_100k_sampled():
-    import pairwise_reductions_amd as pr
-    inp = workloads.make_inputs("argkmin_lse_100k")
-    M, N, K = inp["M"], inp["N"], inp["K"]
-    _announce("argkmin_lse_100k", M=M, N=N, K=K)
-    sig = float(inp["sigma"])
-    xd, yd = _dev(inp["x"]), _dev(inp["y"])
-    idx, dist = pr.argkmin(xd, yd, K, with_dist=True)
-    lse = _host(pr.lse(xd, yd, sig))
-    idx, dist = _host(idx), _host(dist)
-    rows = workloads.sample_rows(M, 1024, seed=1)
-    assert oracle.keys_are_exact(inp["x"], inp["y"])
-    want_idx, want_d2 = oracle.argkmin(inp["x"][rows], inp["y"], K, workers=8)
-    assert np.array_equal(idx[rows].astype(np.int64), want_idx)
-    assert np.allclose(dist[rows], want_d2, rtol=1e-6, atol=0)
-    want_lse = oracle.logsumexp_reduction(inp["x"][rows], inp["y"], sig, workers=8)
-    assert np.all(np.abs(lse[rows] - want_lse) <= lse_bound(want_lse))
-    # properties that hold for every row: sorted keys, distinct in-range indices
-    assert np.all(np.diff(dist, axis=1) >= 0)
-    assert idx.min() >= 0 and idx.max() < N
-    assert np.all(np.sort(idx, axis=1)[:, 1:] != np.sort(idx, axis=1)[:, :-1])
-
-
 def test_all_ops_deterministic():
     import pairwise_reductions_amd as pr
     _announce("determinism")
@@ -563,16 +498,3 @@ def test_argkmin_screening_far_from_origin_and_unaligned_values():
     assert np.all(np.abs(_host(lse) - want_lse) <= lse_bound(want_lse))
 
 
-def test_argkmin_lse_workload_100k_fused_sampled():
-    import pairwise_reductions_amd as pr
-    inp = workloads.make_inputs("argkmin_lse_100k")
-    M, N, K = inp["M"], inp["N"], inp["K"]
-    _announce("argkmin_lse_100k_fused", M=M, N=N, K=K)
-    sig = float(inp["sigma"])
-    idx, lse = pr.argkmin_lse(_dev(inp["x"]), _dev(inp["y"]), K, sig)
-    idx, lse = _host(idx), _host(lse)
-    rows = workloads.sample_rows(M, 1024, seed=4)
-    want_idx, _ = oracle.argkmin(inp["x"][rows], inp["y"], K, workers=8)
-    assert np.array_equal(idx[rows].astype(np.int64), want_idx)
-    want_lse = oracle.logsumexp_reduction(inp["x"][rows], inp["y"], sig, workers=8)
-    assert np.all(np.abs(lse[rows] - want_lse) <= lse_bound(want_lse))
