@@ -8,9 +8,12 @@
  *
  * Conventions shared by all entry points
  *   - Data pointers are DEVICE pointers to dense, row-major, contiguous arrays, aligned to
- *     their element size (4 bytes for float32 / int32), to 16 bytes on the fp16 / bf16 path
- *     and for the workspace. The caller owns every buffer (inputs, outputs, workspace). The
- *     library never allocates or frees device memory and keeps no state between calls.
+ *     their element size (4 bytes for float32 / int32), and to 16 bytes where a call says so
+ *     (the matrix-core path's points when D is a multiple of 16, its outputs, and the
+ *     workspace). The caller owns every buffer (inputs, outputs, workspace). The library
+ *     never allocates or frees device memory. It keeps no state between calls that affects
+ *     a result; the only state it holds is a per-device cache of the compute-unit count (used
+ *     to plan launches) and, while keops_sweep_timing is enabled, per-thread HIP events.
  *   - `workspace` must hold keops_workspace_bytes(...) bytes for the same arguments, queried
  *     with the same device current; it may be NULL only when that size is 0. Its contents
  *     on entry are ignored. Two calls in flight at once need two workspaces.
@@ -73,11 +76,18 @@ typedef enum {
  * with signed weights as in "Fast Gauss Sums via Flash Attention", Algorithm 1 Output row):
  *   out[t][i][c] = sum_j exp(-||x[t][i] - y[t][j]||^2 / (2 sigma^2)) * b[t][j][c]
  * Shapes: x (B, M, D), y (B, N, D), b (B, N, C), out (B, M, C) float32.
- * dtype KEOPS_F32: x, y, b are float32; requires B = 1, 1 <= D <= 8, 1 <= C <= 8.
- * dtype KEOPS_F16: x, y, b are fp16; requires D a multiple of 16 in [16, 128] and
- * 1 <= C <= 64 (matrix-core path: fp32 accumulation, the kernel values are rounded to fp16
- * before they multiply b; features run in steps of 32 and channels in tiles of 16, padding
- * read as zero); any B >= 1. KEOPS_BF16 is reserved and returns KEOPS_ERR_UNSUPPORTED.
+ * Two kernel families, chosen by dtype and D:
+ *   - KEOPS_F32 with 1 <= D <= 8: the low-D float32 path. x, y, b float32; requires B = 1 and
+ *     1 <= C <= 8. 4-byte alignment.
+ *   - KEOPS_F16, KEOPS_BF16 (any 1 <= D <= 128), and KEOPS_F32 with 9 <= D <= 128: the
+ *     matrix-core path, any B >= 1, 1 <= C <= 64. x, y, b are of the dtype; fp32
+ *     accumulation. fp16 and bf16 inputs: the kernel values are rounded to fp16 before they
+ *     multiply b. float32 inputs are split into fp16 high and low parts (three products per
+ *     step, float32 accuracy). Features run in steps of 32 and channels in tiles of 16 (both
+ *     read as zero past D and C). When D is a multiple of 16, x and y must be 16-byte aligned
+ *     and are read in place; any other D is first copied, zero-padded to the next multiple of
+ *     16, into the workspace (x and y then need only their element alignment). out must be
+ *     16-byte aligned on this path.
  * N = 0 writes zeros.
  */
 KEOPS_API int keops_gauss_sum(const void* x, const void* y, const void* b, float* out,
@@ -203,9 +213,11 @@ KEOPS_API int keops_gauss_sum_scaled(const void* x, const void* y, const void* b
  *   grad_b[t][j] =  sum_i k_ij g_i
  * Any of grad_x (B, M, D), grad_y (B, N, D), grad_b (B, N, C) may be NULL (not computed).
  * g (B, M, C) and every gradient are float32. dtype KEOPS_F32: x, y, b float32 with the
- * limits of keops_gauss_sum_grad_x (B = 1). dtype KEOPS_F16: x, y, b fp16 with the limits of
- * the fp16 keops_gauss_sum; the pair weights k_ij (g_i . b_j) are rounded to fp16 (after the
- * weight vectors are normalised, so nothing overflows) and accumulate in fp32.
+ * limits of keops_gauss_sum_grad_x (B = 1, 1 <= D <= 8, 1 <= C <= 8). dtype KEOPS_F16: x, y, b
+ * fp16 with the limits and alignment of the fp16 keops_gauss_sum (any B, 1 <= D <= 128,
+ * 1 <= C <= 64), b and every gradient 16-byte aligned; the pair weights k_ij (g_i . b_j) are
+ * rounded to fp16 (after the weight vectors are normalised, so nothing overflows) and
+ * accumulate in fp32. KEOPS_BF16, and KEOPS_F32 with D > 8, return KEOPS_ERR_UNSUPPORTED.
  */
 KEOPS_API int keops_gauss_sum_backward(const void* x, const void* y, const void* b, const float* g, float* grad_x,
                                        float* grad_y, float* grad_b, int64_t B, int64_t M, int64_t N, int32_t D,
@@ -219,8 +231,9 @@ KEOPS_API int keops_gauss_sum_backward(const void* x, const void* y, const void*
  *   q = K 1,   p = q^-alpha,   d = p * (K p),   s = p / sqrt(d)
  * so that diag(s) K diag(s) = D^-1/2 K_alpha D^-1/2 with K_alpha = diag(p) K diag(p) and
  * D = diag(K_alpha 1), the symmetric form of the alpha-normalised diffusion matrix.
- * Shapes: x (B, N, D) (float32 with B = 1 and 1 <= D <= 8, or fp16 with the fp16 limits of
- * keops_gauss_sum); s (B, N) float32; q and d (B, N) float32 or NULL. alpha must be finite.
+ * Shapes: x (B, N, D) of the dtype, with the limits of keops_gauss_sum for C = 1 (float32
+ * with D <= 8 needs B = 1; fp16, bf16, and float32 with 9 <= D <= 128 take any B);
+ * s (B, N) float32; q and d (B, N) float32 or NULL. alpha must be finite.
  */
 KEOPS_API int keops_diffusion_scaling(const void* x, float* s, float* q, float* d, int64_t B, int64_t N, int32_t D,
                                       float sigma, float alpha, keops_dtype dtype, void* workspace,

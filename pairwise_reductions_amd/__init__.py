@@ -83,9 +83,10 @@ def _gauss_shapes(x, y, b):
 def gauss_sum(x, y, b, sigma: float, out=None, workspace=None):
     """s[i, c] = sum_j exp(-|x_i - y_j|^2 / (2 sigma^2)) b[j, c].
 
-    float32: x (M, D), y (N, D), b (N, C) -> (M, C) (D <= 8 runs the float32 VALU kernels).
-    batched: x (B, M, D), y (B, N, D), b (B, N, C) in float16, bfloat16 or float32 with D a
-    multiple of 16 up to 128 (the matrix-core kernels) -> (B, M, C) float32.
+    float32: x (M, D), y (N, D), b (N, C) -> (M, C) (D <= 8 runs the float32 VALU kernels,
+    9 <= D <= 128 the matrix-core kernels).
+    batched: x (B, M, D), y (B, N, D), b (B, N, C) in float16, bfloat16 or float32 with
+    1 <= D <= 128 and 1 <= C <= 64 (the matrix-core kernels) -> (B, M, C) float32.
     """
     torch = _torch()
     lib = _lib.load()

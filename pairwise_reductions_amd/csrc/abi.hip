@@ -278,8 +278,8 @@ int check_gauss_family(keops_dtype dtype, int64_t B, int32_t D, int32_t C, const
     return fail(KEOPS_ERR_INVALID_ARG, "%s: unknown dtype %d", what, (int)dtype);
   if (is_highd(dtype, D)) {
     if (!keops::highd_supported(D, C))
-      return fail(KEOPS_ERR_UNSUPPORTED, "%s: the matrix-core path needs D a multiple of 16 in [16, 128] and "
-                  "1 <= C <= 64 (got D=%d C=%d)", what, D, C);
+      return fail(KEOPS_ERR_UNSUPPORTED, "%s: the matrix-core path needs 1 <= D <= 128 and 1 <= C <= 64 "
+                  "(got D=%d C=%d)", what, D, C);
     return KEOPS_OK;
   }
   if (B != 1) return fail(KEOPS_ERR_UNSUPPORTED, "%s: the float32 path for D <= %d needs B = 1 (got %lld)", what,
@@ -288,6 +288,39 @@ int check_gauss_family(keops_dtype dtype, int64_t B, int32_t D, int32_t C, const
     return fail(KEOPS_ERR_UNSUPPORTED, "%s: float32 path needs 1 <= D <= %d and 1 <= C <= %d (got D=%d C=%d)", what,
                 keops::kMaxLowD, keops::kMaxLowC, D, C);
   return KEOPS_OK;
+}
+
+// Points of a width the matrix-core kernels do not read directly (D not a multiple of 16) are
+// first copied, zero-padded to highd_stored_features(D), to the front of the workspace.
+size_t highd_pad_bytes(int64_t B, int64_t M, int64_t N, int D, size_t es) {
+  const int Ds = keops::highd_stored_features(D);
+  if (Ds == D) return 0;
+  return keops::align_up((size_t)(B * M) * Ds * es) + keops::align_up((size_t)(B * N) * Ds * es);
+}
+
+// Workspace of a matrix-core Gauss sum: the padded points (if any), then the sweep's layout.
+size_t highd_sum_bytes(int64_t B, int64_t M, int64_t N, int D, int C, keops_dtype dtype, bool general) {
+  if (B == 0 || M == 0 || N == 0) return 0;
+  return highd_pad_bytes(B, M, N, D, elem_size(dtype)) +
+         keops::highd_workspace_bytes(B, M, N, keops::highd_stored_features(D), C, elem_of(dtype), general);
+}
+
+// Copies x and y into the workspace with zero features up to Ds = highd_stored_features(D) when
+// D is not already a multiple of 16; on return x, y, D and ws describe what the kernels read.
+hipError_t highd_pad_points(const void*& x, const void*& y, int64_t B, int64_t M, int64_t N, int& D, size_t es,
+                            char*& ws, hipStream_t stream) {
+  const int Ds = keops::highd_stored_features(D);
+  if (Ds == D) return hipSuccess;
+  void* xp = ws;
+  ws += keops::align_up((size_t)(B * M) * Ds * es);
+  void* yp = ws;
+  ws += keops::align_up((size_t)(B * N) * Ds * es);
+  hipError_t e = keops::launch_pad_rows(x, xp, B * M, D, Ds, (int)es, stream);
+  if (e == hipSuccess) e = keops::launch_pad_rows(y, yp, B * N, D, Ds, (int)es, stream);
+  x = xp;
+  y = yp;
+  D = Ds;
+  return e;
 }
 
 // Workspace of the float32 scaled Gauss sum: the column-scaled weights, then the low-D layout.
@@ -311,16 +344,16 @@ int gauss_sum_run(const void* x, const void* y, keops_dtype dtype, const void* b
   }
   const bool highd = is_highd(dtype, D);
   const keops::ElemType xy = elem_of(dtype);
-  const size_t need = highd ? keops::highd_workspace_bytes(B, M, N, D, C, xy,
-                                                           keops::highd_general(xy, bt, cscale != nullptr))
+  const size_t need = highd ? highd_sum_bytes(B, M, N, D, C, dtype, keops::highd_general(xy, bt, cscale != nullptr))
                             : lowd_scaled_bytes(M, N, D, C, cscale != nullptr);
   KEOPS_TRY(check_workspace(workspace, workspace_bytes, need));
   for (int r = 0; r < nranges; ++r)
     if (overlaps(Range{workspace, need}, ranges[r]))
       return fail(KEOPS_ERR_INVALID_ARG, "workspace overlaps an input or an output");
   if (highd) {
-    KEOPS_HIP(keops::launch_gauss_sum_highd(x, y, xy, b, bt, rscale, cscale, out, workspace, B, M, N, D, C, sigma,
-                                            stream),
+    char* hws = static_cast<char*>(workspace);
+    KEOPS_HIP(highd_pad_points(x, y, B, M, N, D, elem_size(dtype), hws, stream), "pad_features");
+    KEOPS_HIP(keops::launch_gauss_sum_highd(x, y, xy, b, bt, rscale, cscale, out, hws, B, M, N, D, C, sigma, stream),
               "gauss_sum_highd");
     return ok();
   }
@@ -352,7 +385,9 @@ int gauss_sum_impl(const void* x, const void* y, const void* b, const float* rsc
   KEOPS_TRY(check_gauss_family(dtype, B, D, C, what));
   const bool highd = is_highd(dtype, D);
   const size_t es = elem_size(dtype);
-  const size_t al = highd ? 16 : 4;
+  // the matrix-core kernels read rows of a multiple of 16 features as 16-byte vectors; other
+  // widths are read element by element into a padded copy
+  const size_t al = highd ? (D % 16 == 0 ? 16 : es) : 4;
   const Range rx{x, (size_t)(B * M * D) * es}, ry{y, (size_t)(B * N * D) * es}, rb{b, (size_t)(B * N * C) * es};
   const Range ro{out, (size_t)(B * M * C) * sizeof(float)};
   const Range rr{rscale, rscale ? (size_t)(B * M) * sizeof(float) : 0};
@@ -360,7 +395,7 @@ int gauss_sum_impl(const void* x, const void* y, const void* b, const float* rsc
   KEOPS_TRY(check_ptr(x, "x", al, rx.bytes));
   KEOPS_TRY(check_ptr(y, "y", al, ry.bytes));
   KEOPS_TRY(check_ptr(b, "b", highd ? es : 4, rb.bytes));
-  KEOPS_TRY(check_ptr(out, "out", al, ro.bytes));
+  KEOPS_TRY(check_ptr(out, "out", highd ? 16 : 4, ro.bytes));
   if (rscale && !aligned(rscale, 4)) return fail(KEOPS_ERR_INVALID_ARG, "row_scale must be 4-byte aligned");
   if (cscale && !aligned(cscale, 4)) return fail(KEOPS_ERR_INVALID_ARG, "col_scale must be 4-byte aligned");
   if (overlaps(ro, rx) || overlaps(ro, ry) || overlaps(ro, rb) || overlaps(ro, rr) || overlaps(ro, rc))
@@ -379,9 +414,14 @@ size_t backward_bytes(int64_t B, int64_t M, int64_t N, int D, int C, bool half, 
   if (half) {
     // the y-gradient sweep also yields the b-gradient when C is small enough
     const bool fuse_b = want_y && want_b && C <= keops::hd_fused_weight_channels();
-    if (want_x) take(keops::highd_grad_workspace_bytes(B, M, N, D, C, false));
-    if (want_y) take(keops::highd_grad_workspace_bytes(B, N, M, D, C, fuse_b));
-    if (want_b && !fuse_b) take(keops::highd_workspace_bytes(B, N, M, D, C, keops::kElemF16, true));
+    const int Ds = keops::highd_stored_features(D);
+    if (want_x) take(keops::highd_grad_workspace_bytes(B, M, N, Ds, C, false));
+    if (want_y) take(keops::highd_grad_workspace_bytes(B, N, M, Ds, C, fuse_b));
+    if (want_b && !fuse_b) take(keops::highd_workspace_bytes(B, N, M, Ds, C, keops::kElemF16, true));
+    // other widths: the padded points and Ds-wide gradients first, narrowed to D at the end
+    if (Ds != D)
+      need += highd_pad_bytes(B, M, N, D, 2) + (want_x ? keops::align_up((size_t)(B * M) * Ds * sizeof(float)) : 0) +
+              (want_y ? keops::align_up((size_t)(B * N) * Ds * sizeof(float)) : 0);
   } else {
     if (want_x) take(lowd_layout(KEOPS_OP_GAUSS_SUM_GRAD_X, M, N, D, C, 0).total);
     if (want_y) take(lowd_layout(KEOPS_OP_GAUSS_SUM_GRAD_X, N, M, D, C, 0).total);
@@ -395,7 +435,7 @@ size_t backward_bytes(int64_t B, int64_t M, int64_t N, int D, int C, bool half, 
 size_t diffusion_bytes(int64_t B, int64_t N, int D, keops_dtype dtype) {
   if (B == 0 || N == 0) return 0;
   const size_t vec = keops::align_up((size_t)(B * N) * sizeof(float));
-  const size_t sums = is_highd(dtype, D) ? keops::highd_workspace_bytes(B, N, N, D, 1, elem_of(dtype), true)
+  const size_t sums = is_highd(dtype, D) ? highd_sum_bytes(B, N, N, D, 1, dtype, true)
                                          : lowd_layout(KEOPS_OP_GAUSS_SUM, N, N, D, 1, 0).total;
   return 4 * vec + sums;
 }
@@ -415,7 +455,7 @@ size_t keops_workspace_bytes(int op, int64_t B, int64_t M, int64_t N, int32_t D,
       if (is_highd(dtype, D)) {
         if (!keops::highd_supported(D, C) || B == 0 || M == 0 || N == 0) return 0;
         const keops::ElemType xy = elem_of(dtype);
-        return keops::highd_workspace_bytes(B, M, N, D, C, xy, keops::highd_general(xy, xy, scaled));
+        return highd_sum_bytes(B, M, N, D, C, dtype, keops::highd_general(xy, xy, scaled));
       }
       if (B != 1 || D < 1 || C < 1 || C > keops::kMaxLowC) return 0;
       return lowd_scaled_bytes(M, N, D, C, scaled);
@@ -491,7 +531,7 @@ int keops_gauss_sum_backward(const void* x, const void* y, const void* b, const 
                 "(float32 gradients are built for D <= %d)", keops::kMaxLowD);
   const bool half = (dtype == KEOPS_F16);
   const size_t es = half ? 2 : 4;
-  const size_t al = half ? 16 : 4;
+  const size_t al = half ? (D % 16 == 0 ? 16 : es) : 4;
   const Range rx{x, (size_t)(B * M * D) * es}, ry{y, (size_t)(B * N * D) * es}, rb{b, (size_t)(B * N * C) * es};
   const Range rg{g, (size_t)(B * M * C) * 4};
   const Range ogx{grad_x, grad_x ? (size_t)(B * M * D) * 4 : 0};
@@ -499,7 +539,7 @@ int keops_gauss_sum_backward(const void* x, const void* y, const void* b, const 
   const Range ogb{grad_b, grad_b ? (size_t)(B * N * C) * 4 : 0};
   KEOPS_TRY(check_ptr(x, "x", al, rx.bytes));
   KEOPS_TRY(check_ptr(y, "y", al, ry.bytes));
-  KEOPS_TRY(check_ptr(b, "b", al, rb.bytes));
+  KEOPS_TRY(check_ptr(b, "b", half ? 16 : 4, rb.bytes));
   KEOPS_TRY(check_ptr(g, "g", 4, rg.bytes));
   const size_t oal = half ? 16 : 4;
   if ((grad_x && !aligned(grad_x, oal)) || (grad_y && !aligned(grad_y, oal)) || (grad_b && !aligned(grad_b, oal)))
@@ -526,20 +566,38 @@ int keops_gauss_sum_backward(const void* x, const void* y, const void* b, const 
     if (overlaps(rw, r)) return fail(KEOPS_ERR_INVALID_ARG, "workspace overlaps an input or an output");
   char* ws = static_cast<char*>(workspace);
   if (half) {
+    // Widths that are not a multiple of 16 run on zero-padded copies of the points; the x and y
+    // gradients then come out Ds wide and are narrowed to D.
+    const int D0 = D;
+    float* gx = grad_x;
+    float* gy = grad_y;
+    KEOPS_HIP(highd_pad_points(x, y, B, M, N, D, es, ws, stream), "pad_features");
+    if (D != D0) {
+      if (want_x) {
+        gx = reinterpret_cast<float*>(ws);
+        ws += keops::align_up((size_t)(B * M) * D * sizeof(float));
+      }
+      if (want_y) {
+        gy = reinterpret_cast<float*>(ws);
+        ws += keops::align_up((size_t)(B * N) * D * sizeof(float));
+      }
+    }
     // rows x with weights g against columns y with weights b, and the transpose of that.
     if (want_x)
-      KEOPS_HIP(keops::launch_gauss_sum_grad_highd(x, y, g, true, b, false, grad_x, nullptr, ws, B, M, N, D, C, sigma,
+      KEOPS_HIP(keops::launch_gauss_sum_grad_highd(x, y, g, true, b, false, gx, nullptr, ws, B, M, N, D, C, sigma,
                                                    stream),
                 "grad_x_highd");
     const bool fuse_b = want_y && want_b && C <= keops::hd_fused_weight_channels();
     if (want_y)
-      KEOPS_HIP(keops::launch_gauss_sum_grad_highd(y, x, b, false, g, true, grad_y, fuse_b ? grad_b : nullptr, ws, B, N,
+      KEOPS_HIP(keops::launch_gauss_sum_grad_highd(y, x, b, false, g, true, gy, fuse_b ? grad_b : nullptr, ws, B, N,
                                                    M, D, C, sigma, stream),
                 "grad_y_highd");
     if (want_b && !fuse_b)
       KEOPS_HIP(keops::launch_gauss_sum_highd(y, x, keops::kElemF16, g, keops::kElemF32, nullptr, nullptr, grad_b, ws,
                                               B, N, M, D, C, sigma, stream),
                 "grad_b_highd");
+    if (want_x && gx != grad_x) KEOPS_HIP(keops::launch_narrow_rows(gx, grad_x, B * M, D, D0, stream), "narrow");
+    if (want_y && gy != grad_y) KEOPS_HIP(keops::launch_narrow_rows(gy, grad_y, B * N, D, D0, stream), "narrow");
     return ok();
   }
   const float* xf = static_cast<const float*>(x);
@@ -583,7 +641,7 @@ int keops_diffusion_scaling(const void* x, float* s, float* q, float* d, int64_t
   const size_t es = elem_size(dtype);
   const size_t n = (size_t)(B * N);
   const Range rx{x, n * D * es}, rs{s, n * 4}, rq{q, q ? n * 4 : 0}, rd{d, d ? n * 4 : 0};
-  KEOPS_TRY(check_ptr(x, "x", highd ? 16 : 4, rx.bytes));
+  KEOPS_TRY(check_ptr(x, "x", highd ? (D % 16 == 0 ? 16 : es) : 4, rx.bytes));
   KEOPS_TRY(check_ptr(s, "s", 4, rs.bytes));
   if ((q && !aligned(q, 4)) || (d && !aligned(d, 4))) return fail(KEOPS_ERR_INVALID_ARG, "q and d must be 4-byte aligned");
   if (overlaps(rs, rx) || overlaps(rq, rx) || overlaps(rd, rx) || overlaps(rs, rq) || overlaps(rs, rd) ||

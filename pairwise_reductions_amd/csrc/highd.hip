@@ -200,6 +200,29 @@ row_prep_kernel(const T* __restrict__ a, _Float16* __restrict__ ap, float* __res
   for (int c = 0; c < Ck; ++c) dst[c] = c < C ? (_Float16)(to_f32(ar[c]) * inv) : (_Float16)0.0f;
 }
 
+// out[r][d] = in[r][d] for d < D and 0 for D <= d < Dp (element bits copied unchanged; the
+// all-zero pattern is +0 in every input format).
+template <typename T>
+__global__ void __launch_bounds__(256)
+pad_rows_kernel(const T* __restrict__ in, T* __restrict__ out, int64_t rows, int D, int Dp) {
+  const int64_t n = rows * Dp;
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < n; e += (int64_t)gridDim.x * 256) {
+    const int64_t r = e / Dp;
+    const int d = (int)(e - r * Dp);
+    out[e] = d < D ? in[r * D + d] : T(0);
+  }
+}
+
+// out[r][d] = in[r][d] for d < D, from rows of Dp values.
+__global__ void __launch_bounds__(256)
+narrow_rows_kernel(const float* __restrict__ in, float* __restrict__ out, int64_t rows, int Dp, int D) {
+  const int64_t n = rows * D;
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < n; e += (int64_t)gridDim.x * 256) {
+    const int64_t r = e / D;
+    out[e] = in[r * Dp + (e - r * D)];
+  }
+}
+
 __global__ void __launch_bounds__(256)
 combine_kernel(const float* __restrict__ partial, float* __restrict__ out, int64_t n, int64_t S) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -341,7 +364,36 @@ hipError_t weight_norm_max(const T* w, const float* cscale, float* nmax, int64_t
 
 int hd_fused_weight_channels() { return hd::kFusedWeightChannels; }
 
-bool highd_supported(int D, int C) { return D >= 16 && D <= 128 && D % 16 == 0 && C >= 1 && C <= 64; }
+bool highd_supported(int D, int C) { return D >= 1 && D <= 128 && C >= 1 && C <= 64; }
+
+int highd_stored_features(int D) { return (D + 15) / 16 * 16; }
+
+namespace {
+int64_t grid_stride_blocks(int64_t n) {
+  const int64_t b = hd_ceil_div(n, 256);
+  return b < 1 ? 1 : (b > 65536 ? 65536 : b);
+}
+}  // namespace
+
+hipError_t launch_pad_rows(const void* in, void* out, int64_t rows, int D, int Dp, int elem_bytes, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  const unsigned blocks = (unsigned)grid_stride_blocks(rows * Dp);
+  if (elem_bytes == 2)
+    pad_rows_kernel<uint16_t><<<blocks, 256, 0, s>>>(static_cast<const uint16_t*>(in), static_cast<uint16_t*>(out),
+                                                     rows, D, Dp);
+  else if (elem_bytes == 4)
+    pad_rows_kernel<uint32_t><<<blocks, 256, 0, s>>>(static_cast<const uint32_t*>(in), static_cast<uint32_t*>(out),
+                                                     rows, D, Dp);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_narrow_rows(const float* in, float* out, int64_t rows, int Dp, int D, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  narrow_rows_kernel<<<(unsigned)grid_stride_blocks(rows * D), 256, 0, s>>>(in, out, rows, Dp, D);
+  return hipGetLastError();
+}
 
 bool highd_general(ElemType xy, ElemType bt, bool col_scaled) {
   return xy != kElemF16 || bt != kElemF16 || col_scaled;

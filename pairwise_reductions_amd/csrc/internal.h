@@ -107,7 +107,16 @@ hipError_t launch_div_sqrt(const float* p, const float* d, float* out, int64_t n
 // Matrix-core batched Gauss sums. x, y: [B][M|N][D] of `xy` type (fp16, bf16, or float32
 // split into fp16 hi + lo parts on the matrix cores).
 enum ElemType { kElemF16 = 0, kElemBF16 = 1, kElemF32 = 2 };
+// Any 1 <= D <= 128 and 1 <= C <= 64. The kernels read rows of a multiple of 16 features
+// (16-byte vectors); other widths are first copied into the workspace with zero features
+// appended (zeros change no squared distance), see highd_stored_features.
 bool highd_supported(int D, int C);
+// Feature count the matrix-core kernels are launched with: D rounded up to a multiple of 16.
+int highd_stored_features(int D);
+// rows x Dp copies of rows x D arrays (elements of elem_bytes = 2 or 4), zero past D; and the
+// float32 narrowing back from Dp to D columns.
+hipError_t launch_pad_rows(const void* in, void* out, int64_t rows, int D, int Dp, int elem_bytes, hipStream_t s);
+hipError_t launch_narrow_rows(const float* in, float* out, int64_t rows, int Dp, int D, hipStream_t s);
 // out[t][i][c] = rscale[t][i] * sum_j Phi_ij cscale[t][j] b[t][j][c]; b is of type bt;
 // rscale and cscale may be null. Anything but fp16 points with fp16 weights and no column
 // scale takes the weight-normalising column preparation (`general`), which needs a slightly

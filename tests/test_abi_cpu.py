@@ -69,7 +69,7 @@ def test_workspace_bytes(lib):
     assert n_cols >= 1_000_000 * 4 * 8           # float64 column table (4 doubles a column)
     assert ws(0, 1, 0, 1000, 3, 1, 0, F32) == 0   # M = 0 needs nothing
     assert ws(0, 1, 10, 0, 3, 1, 0, F32) == 0     # N = 0 needs nothing
-    assert ws(0, 1, 10, 10, 9, 1, 0, F32) == 0    # D out of range
+    assert ws(0, 1, 10, 10, 129, 1, 0, F32) == 0  # D out of range
     assert ws(0, 1, 10, 10, 3, 0, 0, F32) == 0    # C out of range
     assert ws(0, 2, 10, 10, 3, 1, 0, F32) == 0    # batched float32 unsupported
     assert ws(2, 1, 10, 10, 3, 1, 11, F32) == 0   # K > N
@@ -81,7 +81,8 @@ def test_workspace_bytes(lib):
     # fp16 matrix-core path: key norms (float) and the permuted fp16 copy of v
     assert ws(0, 4, 16384, 16384, 32, 32, 0, F16) >= 4 * 16384 * (4 + 32 * 2)
     assert ws(0, 4, 16384, 16384, 48, 32, 0, F16) > 0     # D padded to 64 inside
-    assert ws(0, 4, 16384, 16384, 40, 32, 0, F16) == 0    # D not a multiple of 16
+    # D not a multiple of 16: the padded copies of the points come first
+    assert ws(0, 4, 16384, 16384, 40, 32, 0, F16) >= ws(0, 4, 16384, 16384, 48, 32, 0, F16) + 4 * 2 * 16384 * 48 * 2
     assert ws(0, 4, 16384, 16384, 144, 32, 0, F16) == 0   # D > 128
     assert ws(0, 4, 16384, 16384, 32, 32, 0, 2) > 0       # bf16
     assert ws(0, 4, 16384, 16384, 32, 32, 0, F32) >= 4 * 16384 * (4 + 2 * 32 * 2)   # hi + lo weight tables
@@ -96,10 +97,10 @@ def _gs(lib, x=X, y=Y, b=B, out=OUT, Bt=1, M=100, N=100, D=3, C=1, sigma=0.1, dt
     (dict(M=-1), INVALID), (dict(N=-5), INVALID), (dict(Bt=-1), INVALID),
     (dict(sigma=0.0), INVALID), (dict(sigma=-1.0), INVALID), (dict(sigma=math.nan), INVALID),
     (dict(sigma=math.inf), INVALID),
-    (dict(D=9), UNSUPPORTED), (dict(D=0), UNSUPPORTED), (dict(C=0), UNSUPPORTED), (dict(C=9), UNSUPPORTED),
-    (dict(Bt=2), UNSUPPORTED), (dict(dtype=F16, D=3), UNSUPPORTED), (dict(dtype=7), INVALID),
-    (dict(dtype=2, D=40, C=32), UNSUPPORTED), (dict(dtype=F16, D=40, C=32), UNSUPPORTED),
-    (dict(dtype=F32, D=24, C=4), UNSUPPORTED), (dict(dtype=2, D=32, C=65), UNSUPPORTED),
+    (dict(D=129), UNSUPPORTED), (dict(D=0), UNSUPPORTED), (dict(C=0), UNSUPPORTED), (dict(C=9), UNSUPPORTED),
+    (dict(Bt=2), UNSUPPORTED), (dict(dtype=F16, D=0), UNSUPPORTED), (dict(dtype=7), INVALID),
+    (dict(dtype=2, D=130, C=32), UNSUPPORTED), (dict(dtype=F16, D=40, C=0), UNSUPPORTED),
+    (dict(dtype=F32, D=24, C=65), UNSUPPORTED), (dict(dtype=2, D=32, C=65), UNSUPPORTED),
     (dict(dtype=F32, D=32, C=4, Bt=2, x=X + 4), INVALID),     # matrix-core path: 16-byte alignment
     (dict(dtype=F16, D=144, C=32), UNSUPPORTED),
     (dict(dtype=F16, D=32, C=65), UNSUPPORTED),
@@ -152,7 +153,7 @@ def test_grad_rejects(lib):
 
 def test_error_is_thread_local(lib):
     import threading
-    assert _gs(lib, D=9) == UNSUPPORTED
+    assert _gs(lib, D=129) == UNSUPPORTED
     seen = []
 
     def worker():
@@ -162,7 +163,7 @@ def test_error_is_thread_local(lib):
     t.start()
     t.join()
     assert seen == [""]
-    assert "D=9" in _err(lib)
+    assert "D=129" in _err(lib)
 
 
 def test_grad_yb_reject(lib):
@@ -201,9 +202,9 @@ def test_gauss_sum_scaled_rejects(lib):
     assert call(args(r=R + 2)) == INVALID            # misaligned row scale
     assert call(args(c=CS + 1)) == INVALID
     assert call(args(out=R)) == INVALID              # out aliases the row scale
-    assert call(args(D=9)) == UNSUPPORTED
+    assert call(args(D=129)) == UNSUPPORTED
     assert call(args(dtype=F16, D=32, C=32, Bt=2, x=X + 8)) == INVALID   # fp16 inputs need 16-byte alignment
-    assert call(args(dtype=F16, D=24, C=32, Bt=2)) == UNSUPPORTED
+    assert call(args(dtype=F16, D=136, C=32, Bt=2)) == UNSUPPORTED
     assert call(args(M=0)) == 0                      # no rows: no-op
     ws = lib.keops_workspace_bytes
     assert ws(7, 1, 1000, 1000, 3, 2, 0, F32) > ws(0, 1, 1000, 1000, 3, 2, 0, F32)   # scaled weights copy
@@ -220,7 +221,7 @@ def test_gauss_sum_backward_rejects(lib):
     assert call(gx=X) == INVALID                       # a gradient aliases an input
     assert call(gx=GX, gy=GX) == INVALID               # gradients overlap each other
     assert call(D=9) == UNSUPPORTED and call(Bt=2) == UNSUPPORTED
-    assert call(dtype=F16, D=40, C=4) == UNSUPPORTED
+    assert call(dtype=F16, D=136, C=4) == UNSUPPORTED
     assert call(dtype=2, D=32, C=4) == UNSUPPORTED                # bf16 backward is not built
     assert call(dtype=F32, D=32, C=4) == UNSUPPORTED              # nor the float32 matrix-core one
     assert call(dtype=F16, D=32, C=4, gx=GX + 4) == INVALID   # fp16 path needs 16-byte aligned outputs
@@ -230,7 +231,8 @@ def test_gauss_sum_backward_rejects(lib):
     ws = lib.keops_workspace_bytes
     assert ws(8, 1, 1000, 200, 3, 1, 0, F32) > 0
     assert ws(8, 4, 16384, 16384, 32, 1, 0, F16) > ws(0, 4, 16384, 16384, 32, 1, 0, F16)
-    assert ws(8, 4, 16384, 16384, 40, 1, 0, F16) == 0
+    assert ws(8, 4, 16384, 16384, 40, 1, 0, F16) > ws(8, 4, 16384, 16384, 48, 1, 0, F16)   # padded copies
+    assert ws(8, 4, 16384, 16384, 129, 1, 0, F16) == 0
 
 
 def test_diffusion_scaling_rejects(lib):
@@ -242,13 +244,14 @@ def test_diffusion_scaling_rejects(lib):
     assert call(s=None) == INVALID
     assert call(alpha=math.nan) == INVALID
     assert call(q=S) == INVALID                         # q aliases s
-    assert call(D=9) == UNSUPPORTED and call(Bt=3) == UNSUPPORTED
-    assert call(dtype=F16, D=24) == UNSUPPORTED
+    assert call(D=129) == UNSUPPORTED and call(Bt=3) == UNSUPPORTED
+    assert call(dtype=F16, D=0) == UNSUPPORTED
     assert call(N=0, ws=None, wsb=0) == 0
     assert call(ws=None, wsb=0) == INVALID
     ws = lib.keops_workspace_bytes
     assert ws(9, 1, 0, 5000, 3, 1, 0, F32) >= 4 * 5000 * 4
-    assert ws(9, 2, 0, 5000, 32, 1, 0, F16) > 0 and ws(9, 2, 0, 5000, 3, 1, 0, F16) == 0
+    assert ws(9, 2, 0, 5000, 32, 1, 0, F16) > 0 and ws(9, 2, 0, 5000, 3, 1, 0, F16) > 0
+    assert ws(9, 2, 0, 5000, 129, 1, 0, F16) == 0
 
 
 def test_argkmin_weighted_rejects(lib):
@@ -262,3 +265,59 @@ def test_argkmin_weighted_rejects(lib):
     assert f(X, Y, W, IDX, None, 0, 10, 3, 4, None, 0, None) == 0                    # M = 0
     ws = lib.keops_workspace_bytes
     assert ws(10, 1, 100, 100_000, 3, 1, 10, F32) == ws(2, 1, 100, 100_000, 3, 1, 10, F32) > 0
+
+
+# --------------------------------------------------------------- the header's support rules
+# Each row restates one rule of include/keops_mi355x.h for keops_gauss_sum (and the calls that
+# share its families). An accepted configuration passes every shape check and then stops at the
+# workspace check (a 16-byte workspace is too small for any non-empty call), so nothing is
+# launched; a refused one returns KEOPS_ERR_UNSUPPORTED first.
+BF16 = 2
+SUPPORT_RULES = [
+    # (dtype, B, D, C, accepted)
+    (F32, 1, 1, 1, True), (F32, 1, 3, 1, True), (F32, 1, 8, 8, True),       # low-D float32
+    (F32, 2, 3, 1, False),                                                   # low-D needs B = 1
+    (F32, 1, 3, 9, False),                                                   # low-D needs C <= 8
+    (F32, 1, 9, 1, True), (F32, 4, 12, 3, True), (F32, 4, 32, 32, True),     # float32 matrix cores
+    (F32, 2, 100, 64, True), (F32, 1, 128, 1, True),
+    (F32, 1, 129, 1, False), (F32, 4, 32, 65, False),
+    (F16, 4, 32, 32, True), (F16, 1, 1, 1, True), (F16, 2, 20, 5, True),    # any D <= 128
+    (F16, 3, 50, 64, True), (F16, 1, 100, 17, True), (F16, 1, 128, 64, True),
+    (F16, 1, 129, 1, False), (F16, 1, 32, 65, False), (F16, 1, 32, 0, False), (F16, 1, 0, 1, False),
+    (BF16, 4, 32, 32, True), (BF16, 1, 9, 2, True), (BF16, 1, 136, 2, False),
+]
+
+
+@pytest.mark.parametrize("dtype,Bt,D,C,accepted", SUPPORT_RULES)
+def test_header_support_rules(lib, dtype, Bt, D, C, accepted):
+    code = _gs(lib, dtype=dtype, Bt=Bt, D=D, C=C, wsb=16)
+    if accepted:
+        assert code == INVALID and "workspace too small" in _err(lib), (code, _err(lib))
+        assert lib.keops_workspace_bytes(0, Bt, 100, 100, D, C, 0, dtype) > 16
+        # the scaled form shares the families
+        sc = lib.keops_gauss_sum_scaled(X, Y, B, None, None, OUT, Bt, 100, 100, D, C, 0.1, dtype, WS, 16, None)
+        assert sc == INVALID and "workspace too small" in _err(lib)
+    else:
+        assert code == UNSUPPORTED, (code, _err(lib))
+        assert lib.keops_workspace_bytes(0, Bt, 100, 100, D, C, 0, dtype) == 0
+
+
+@pytest.mark.parametrize("dtype,D,accepted", [(F32, 3, True), (F32, 9, False), (F16, 20, True), (F16, 32, True),
+                                              (F16, 128, True), (F16, 129, False), (BF16, 32, False)])
+def test_header_support_rules_backward(lib, dtype, D, accepted):
+    Bt = 1 if dtype == F32 else 2
+    code = lib.keops_gauss_sum_backward(X, Y, B, G, GX, GY, GB, Bt, 100, 100, D, 1, 0.1, dtype, WS, 16, None)
+    if accepted:
+        assert code == INVALID and "workspace too small" in _err(lib), (code, _err(lib))
+    else:
+        assert code == UNSUPPORTED, (code, _err(lib))
+
+
+@pytest.mark.parametrize("D,accepted", [(1, True), (8, True), (9, False)])
+def test_header_support_rules_lowd_calls(lib, D, accepted):
+    """keops_lse, keops_argkmin and keops_gauss_sum_grad_x take float32 with 1 <= D <= 8."""
+    codes = [lib.keops_lse(X, Y, OUT, 100, 100, D, 0.1, WS, 16, None),
+             lib.keops_argkmin(X, Y, IDX, None, 100, 100, D, 4, WS, 16, None),
+             lib.keops_gauss_sum_grad_x(X, Y, B, G, OUT, 100, 100, D, 1, 0.1, WS, 16, None)]
+    for code in codes:
+        assert code == (INVALID if accepted else UNSUPPORTED)

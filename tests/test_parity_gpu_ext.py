@@ -331,6 +331,45 @@ def test_gauss_sum_f32_matrix_core_shapes(B, M, N, D, C, sigma):
     assert_normalised(got, want, norm, TOL_F32, "f32 matrix-core")
 
 
+# Feature widths that are not a multiple of 16: the points are copied, zero-padded, into the
+# workspace first; float32 with 9 <= D <= 15 takes the matrix-core path this way too.
+ODD_WIDTHS = [
+    # (dtype name, B, M, N, D, C, sigma)
+    ("float32", 1, 700, 2000, 9, 1, 0.6), ("float32", 2, 513, 1500, 12, 3, 0.8), ("float32", 1, 300, 1000, 15, 2, 0.7),
+    ("float32", 2, 400, 1200, 20, 4, 1.0), ("float32", 1, 257, 999, 50, 8, 1.2), ("float32", 1, 200, 777, 100, 1, 1.5),
+    ("float16", 2, 700, 2000, 9, 1, 0.6), ("float16", 1, 513, 1500, 12, 32, 0.8), ("float16", 3, 400, 1200, 20, 4, 1.0),
+    ("float16", 1, 257, 999, 50, 17, 1.2), ("float16", 2, 200, 777, 100, 64, 1.5), ("float16", 1, 300, 900, 3, 2, 0.3),
+    ("bfloat16", 1, 700, 2000, 9, 1, 0.6), ("bfloat16", 2, 400, 1200, 20, 4, 1.0), ("bfloat16", 1, 257, 999, 100, 8, 1.5),
+]
+
+
+@pytest.mark.parametrize("dname,B,M,N,D,C,sigma", ODD_WIDTHS)
+def test_gauss_sum_any_feature_width(dname, B, M, N, D, C, sigma):
+    import torch
+    import pairwise_reductions_amd as pr
+    _announce("gauss_sum_width", dtype=dname, B=B, M=M, N=N, D=D, C=C, sigma=sigma)
+    dtype = getattr(torch, dname)
+    (q, k, v), (qh, kh, vh) = _typed_inputs(B * 53 + M + D, B, M, N, D, C, dtype)
+    sig = float(np.float32(sigma))
+    got = _host(pr.gauss_sum(q, k, v, sig))
+    want, norm = oracle.gauss_sum_batched(qh, kh, vh, 1.0 / (sig * sig), workers=8)
+    assert_normalised(got, want, norm, TOL_F32 if dname == "float32" else TOL_F16, f"width {D} {dname}")
+
+
+@pytest.mark.parametrize("B,M,N,D,C,sigma", [(1, 700, 2000, 20, 1, 1.0), (2, 300, 1000, 50, 3, 1.2),
+                                             (1, 400, 900, 9, 17, 0.8), (2, 257, 600, 100, 2, 1.5)])
+def test_gauss_sum_backward_fp16_any_feature_width(B, M, N, D, C, sigma):
+    import pairwise_reductions_amd as pr
+    _announce("backward_fp16_width", B=B, M=M, N=N, D=D, C=C, sigma=sigma)
+    q, k, v = _highd_inputs(B * 9 + M * 5 + N + D, B, M, N, D, C)
+    g = workloads.upstream_gradient(M, C, seed=M + D, B=B)
+    sig = float(np.float32(sigma))
+    got = pr.gauss_sum_backward(_dev(q), _dev(k), _dev(v), _dev(g), sig)
+    want = _oracle_backward(q, k, v, g, sig)
+    for key in ("x", "y", "b"):
+        assert_normalised(_host(got[key]), want[key][0], want[key][1], TOL_F16, f"backward width {D} {key}")
+
+
 def test_gauss_sum_f32_bf16_far_rows_and_scaled():
     """Rows far from every key (the running shift), and the scaled form, for both input types."""
     import torch
