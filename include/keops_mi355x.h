@@ -96,6 +96,25 @@ KEOPS_API int keops_gauss_sum(const void* x, const void* y, const void* b, float
                     hipStream_t stream);
 
 /*
+ * Allocation-free Gauss sum, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the same reduction,
+ * arguments, limits and results as keops_gauss_sum (bit-identical outputs: the same kernels
+ * and launch plan), without the workspace arguments. A scratch array inside the library,
+ * KEOPS_NOALLOC_SCRATCH_BYTES (64 MiB) of static device memory that every device the library
+ * is loaded on holds until the process ends, takes the workspace's place. Sizes whose
+ * workspace (keops_workspace_bytes for KEOPS_OP_GAUSS_SUM) exceeds it return
+ * KEOPS_ERR_UNSUPPORTED; at D = 3, C = 1 that is above about M = N = 250,000. Nothing is
+ * allocated or freed (no hipMalloc, hipFree or allocating library call); the first call on a
+ * device looks the array's address up once. All calls on one device share that device's
+ * array, and its contents from the last call are never read: calls that overlap in time on
+ * one device (two streams or two threads) race and must be serialised by the caller.
+ */
+#define KEOPS_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+KEOPS_API int keops_gauss_sum_noalloc(const void* x, const void* y, const void* b, float* out, int64_t B, int64_t M,
+                                      int64_t N, int32_t D, int32_t C, float sigma, keops_dtype dtype,
+                                      hipStream_t stream);
+
+/*
  * Log-sum-exp reduction ("Kernel matrix reduction", Overview, list of reductions):
  *   out[i] = log sum_j exp(-||x_i - y_j||^2 / (2 sigma^2))
  * Shapes: x (M, D), y (N, D) float32, out (M,) float32. Requires 1 <= D <= 8.

@@ -12,7 +12,7 @@ from typing import Optional, Tuple
 from . import _lib
 from ._lib import KeopsError  # noqa: F401
 
-__all__ = ["gauss_sum", "gauss_sum_scaled", "lse", "argkmin", "argkmin_weighted", "argkmin_lse", "gauss_sum_grad_x", "gauss_sum_grad_y",
+__all__ = ["gauss_sum", "gauss_sum_noalloc", "gauss_sum_scaled", "lse", "argkmin", "argkmin_weighted", "argkmin_lse", "gauss_sum_grad_x", "gauss_sum_grad_y",
            "gauss_sum_grad_b", "gauss_sum_backward", "diffusion_scaling", "gauss_sum_autograd", "workspace_bytes",
            "KeopsError", "version"]
 
@@ -98,6 +98,19 @@ def gauss_sum(x, y, b, sigma: float, out=None, workspace=None):
     st = lib.keops_gauss_sum(_ptr(x), _ptr(y), _ptr(b), _ptr(out), B, M, N, D, C, float(sigma), dt,
                              _ptr(ws), have, _stream(x.device))
     _lib.check(st, "keops_gauss_sum")
+    return out
+
+
+def gauss_sum_noalloc(x, y, b, sigma: float, out):
+    """gauss_sum through the allocation-free entry point: the library's fixed scratch array
+    replaces the workspace, so nothing is allocated (the caller passes the output). Same
+    shapes, limits and results as gauss_sum; sizes whose workspace exceeds the scratch raise
+    KeopsError (unsupported)."""
+    lib = _lib.load()
+    B, M, N, D, C, dt, _ = _gauss_shapes(x, y, b)
+    st = lib.keops_gauss_sum_noalloc(_ptr(x), _ptr(y), _ptr(b), _ptr(out), B, M, N, D, C, float(sigma), dt,
+                                     _stream(x.device))
+    _lib.check(st, "keops_gauss_sum_noalloc")
     return out
 
 

@@ -29,6 +29,8 @@ _sz = ctypes.c_size_t
 _SIGNATURES = {
     "keops_gauss_sum": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _f32, ctypes.c_int,
                                        _vp, _sz, _vp]),
+    "keops_gauss_sum_noalloc": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _f32, ctypes.c_int,
+                                               _vp]),
     "keops_lse": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i32, _f32, _vp, _sz, _vp]),
     "keops_argkmin": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i32, _i32, _vp, _sz, _vp]),
     "keops_argkmin_weighted": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i32, _i32, _vp, _sz, _vp]),

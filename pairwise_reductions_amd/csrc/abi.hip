@@ -260,6 +260,41 @@ const char* keops_last_error(void) { return g_last_error.c_str(); }
 
 }  // extern "C"
 
+// ---- scratch of the allocation-free entry point -------------------------------------------
+// A fixed device array that stands in for the caller's workspace in keops_gauss_sum_noalloc.
+// Every device the library is loaded on holds its own copy until the process ends. Host code
+// never uses this name as an address: the per-device address comes from hipGetSymbolAddress.
+static __device__ __align__(256) unsigned char scratch[KEOPS_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kScratchDevices = 64;
+std::atomic<uintptr_t> g_scratch_addr[kScratchDevices];
+
+// Device address of the current device's scratch array, looked up once per device (with that
+// device current) and kept.
+int scratch_address(void** addr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kScratchDevices)
+    return fail(KEOPS_ERR_UNSUPPORTED, "gauss_sum_noalloc: device %d is beyond the %d it keeps scratch for", dev,
+                kScratchDevices);
+  uintptr_t a = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (a == 0) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (p == nullptr) return fail(KEOPS_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    a = reinterpret_cast<uintptr_t>(p);
+    g_scratch_addr[dev].store(a, std::memory_order_release);
+  }
+  *addr = reinterpret_cast<void*>(a);
+  return KEOPS_OK;
+}
+
+}  // namespace
+
 namespace {
 
 // The two families of Gauss-sum kernels: float32 with D <= 8 runs the low-D VALU kernels
@@ -333,10 +368,11 @@ size_t lowd_scaled_bytes(int64_t M, int64_t N, int D, int C, bool col_scaled) {
 // out = rscale . sum_j k_ij cscale_j b_j on either path; arguments already validated except
 // for the workspace. b is of type bt (the low-D path takes float32 only). `ranges` lists the
 // caller's buffers the workspace must not overlap.
+// With use_scratch the device's scratch array replaces workspace (which is then ignored).
 int gauss_sum_run(const void* x, const void* y, keops_dtype dtype, const void* b, keops::ElemType bt,
                   const float* rscale, const float* cscale, float* out, int64_t B, int64_t M, int64_t N, int32_t D,
                   int32_t C, float sigma, void* workspace, size_t workspace_bytes, const Range* ranges, int nranges,
-                  hipStream_t stream) {
+                  hipStream_t stream, bool use_scratch = false) {
   if (B == 0 || M == 0) return ok();
   if (N == 0) {
     KEOPS_HIP(keops::launch_fill(out, B * M * C, 0.0f, stream), "fill");
@@ -346,6 +382,17 @@ int gauss_sum_run(const void* x, const void* y, keops_dtype dtype, const void* b
   const keops::ElemType xy = elem_of(dtype);
   const size_t need = highd ? highd_sum_bytes(B, M, N, D, C, dtype, keops::highd_general(xy, bt, cscale != nullptr))
                             : lowd_scaled_bytes(M, N, D, C, cscale != nullptr);
+  if (use_scratch) {
+    if (need > KEOPS_NOALLOC_SCRATCH_BYTES)
+      return fail(KEOPS_ERR_UNSUPPORTED, "gauss_sum_noalloc: these sizes need %zu bytes of scratch, more than the %zu "
+                  "it holds (use keops_gauss_sum with a workspace)", need, (size_t)KEOPS_NOALLOC_SCRATCH_BYTES);
+    workspace = nullptr;
+    workspace_bytes = 0;
+    if (need > 0) {
+      KEOPS_TRY(scratch_address(&workspace));
+      workspace_bytes = KEOPS_NOALLOC_SCRATCH_BYTES;
+    }
+  }
   KEOPS_TRY(check_workspace(workspace, workspace_bytes, need));
   for (int r = 0; r < nranges; ++r)
     if (overlaps(Range{workspace, need}, ranges[r]))
@@ -377,7 +424,8 @@ int gauss_sum_run(const void* x, const void* y, keops_dtype dtype, const void* b
 
 int gauss_sum_impl(const void* x, const void* y, const void* b, const float* rscale, const float* cscale, float* out,
                    int64_t B, int64_t M, int64_t N, int32_t D, int32_t C, float sigma, keops_dtype dtype,
-                   void* workspace, size_t workspace_bytes, hipStream_t stream, const char* what) {
+                   void* workspace, size_t workspace_bytes, hipStream_t stream, const char* what,
+                   bool use_scratch = false) {
   KEOPS_TRY(check_extent(B, "B"));
   KEOPS_TRY(check_extent(M, "M"));
   KEOPS_TRY(check_extent(N, "N"));
@@ -402,7 +450,7 @@ int gauss_sum_impl(const void* x, const void* y, const void* b, const float* rsc
     return fail(KEOPS_ERR_INVALID_ARG, "out overlaps an input");
   const Range all[] = {rx, ry, rb, ro, rr, rc};
   return gauss_sum_run(x, y, dtype, b, elem_of(dtype), rscale, cscale, out, B, M, N, D, C, sigma, workspace,
-                       workspace_bytes, all, 6, stream);
+                       workspace_bytes, all, 6, stream, use_scratch);
 }
 
 // Workspace of keops_gauss_sum_backward: the passes run one after another on the stream, so
@@ -507,6 +555,12 @@ int keops_gauss_sum(const void* x, const void* y, const void* b, float* out, int
                     size_t workspace_bytes, hipStream_t stream) {
   return gauss_sum_impl(x, y, b, nullptr, nullptr, out, B, M, N, D, C, sigma, dtype, workspace, workspace_bytes,
                         stream, "gauss_sum");
+}
+
+int keops_gauss_sum_noalloc(const void* x, const void* y, const void* b, float* out, int64_t B, int64_t M, int64_t N,
+                            int32_t D, int32_t C, float sigma, keops_dtype dtype, hipStream_t stream) {
+  return gauss_sum_impl(x, y, b, nullptr, nullptr, out, B, M, N, D, C, sigma, dtype, nullptr, 0, stream,
+                        "gauss_sum_noalloc", true);
 }
 
 int keops_gauss_sum_scaled(const void* x, const void* y, const void* b, const float* row_scale,

@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == {"keops_gauss_sum", "keops_lse", "keops_argkmin", "keops_gauss_sum_grad_x",
                           "keops_gauss_sum_grad_y", "keops_gauss_sum_grad_b", "keops_argkmin_lse",
                           "keops_gauss_sum_scaled", "keops_gauss_sum_backward", "keops_diffusion_scaling",
-                          "keops_argkmin_weighted",
+                          "keops_argkmin_weighted", "keops_gauss_sum_noalloc",
                           "keops_workspace_bytes", "keops_status_string", "keops_last_error", "keops_version",
                           "keops_sweep_timing", "keops_sweep_timing_read"}
     for name in names:
@@ -321,3 +321,17 @@ def test_header_support_rules_lowd_calls(lib, D, accepted):
              lib.keops_gauss_sum_grad_x(X, Y, B, G, OUT, 100, 100, D, 1, 0.1, WS, 16, None)]
     for code in codes:
         assert code == (INVALID if accepted else UNSUPPORTED)
+
+
+def test_noalloc_rejects_before_any_hip_call(lib):
+    """The allocation-free entry point validates like keops_gauss_sum and refuses sizes whose
+    workspace exceeds its scratch, all before touching the device."""
+    f = lib.keops_gauss_sum_noalloc
+    assert f(None, Y, B, OUT, 1, 100, 100, 3, 1, 0.1, F32, None) == INVALID
+    assert f(X, Y, B, OUT, 1, 100, 100, 129, 1, 0.1, F32, None) == UNSUPPORTED
+    assert f(X, Y, B, OUT, 1, 100, 100, 3, 1, -1.0, F32, None) == INVALID
+    assert f(X, Y, B, X, 1, 100, 100, 3, 1, 0.1, F32, None) == INVALID          # out aliases x
+    assert f(X, Y, B, OUT, 1, 0, 100, 3, 1, 0.1, F32, None) == 0                 # M = 0: no-op
+    assert f(X, Y, B, OUT, 1, 1_000_000, 1_000_000, 3, 1, 0.01, F32, None) == UNSUPPORTED
+    assert "scratch" in _err(lib)
+    assert lib.keops_workspace_bytes(0, 1, 1_000_000, 1_000_000, 3, 1, 0, F32) > 64 << 20
