@@ -6,9 +6,12 @@ and the combine of the column splits. The default workload is the
 1M x 1M, D=3, C=1, float32, sigma=0.01 Gauss sum. Timing uses HIP events recorded on the
 stream the kernels run on, after W warm-up steps, bracketed by device synchronisations.
 
-Prints ONE JSON line (the contract), with two extra objects:
+Prints ONE JSON line (the contract), with extra objects:
+  step_stats    per-step times: mean +- 1 std (sample), median, min, max
   roofline      the dominant kernel against the float32 vector peak (ALU-bound)
   cpu_baseline  the float64 CPU oracle on a bounded row sample of the same workload
+  secondary     the batched fp16 Gauss sum (B=4, M=N=16384, D=C=32) on the matrix cores, timed
+                over at least 100 calls, with its forward sweep against the fp16 matrix-core peak
 --all additionally times the other workloads and writes them to --all-out (not the line).
 """
 from __future__ import annotations
@@ -68,7 +71,10 @@ def measured_traffic():
     return MEASURED_TRAFFIC["bytes"] if digest.startswith(MEASURED_TRAFFIC["sha256_prefix"]) else None
 
 
-def _events_time(fn, steps, warmup, before_timed=None):
+def _events_time(fn, steps, warmup, before_timed=None, per_step=None):
+    """Seconds per step over `steps` timed steps after `warmup` untimed ones, from HIP events on
+    the current stream. With a list `per_step`, an event is recorded between consecutive steps
+    as well and the list receives every step's own duration in milliseconds."""
     import torch
     for _ in range(warmup):
         fn()
@@ -76,14 +82,25 @@ def _events_time(fn, steps, warmup, before_timed=None):
     if before_timed is not None:
         before_timed()
     stream = torch.cuda.current_stream()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for _ in range(steps):
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1 if per_step is not None else 2)]
+    marks[0].record(stream)
+    for k in range(steps):
         fn()
-    end.record(stream)
+        if per_step is not None:
+            marks[k + 1].record(stream)
+    marks[-1].record(stream)
     torch.cuda.synchronize()
-    return start.elapsed_time(end) / 1e3 / steps  # seconds per step
+    if per_step is not None:
+        per_step.extend(marks[k].elapsed_time(marks[k + 1]) for k in range(steps))
+    return marks[0].elapsed_time(marks[-1]) / 1e3 / steps  # seconds per step
+
+
+def _stats(ms):
+    """mean +- 1 std (sample), median, min and max of per-step milliseconds."""
+    import numpy as np
+    a = np.asarray(ms, dtype=np.float64)
+    return {"reps": int(a.size), "mean_ms": float(a.mean()), "std_ms": float(a.std(ddof=1)) if a.size > 1 else 0.0,
+            "median_ms": float(np.median(a)), "min_ms": float(a.min()), "max_ms": float(a.max())}
 
 
 def bench_gauss_1m(steps, warmup, cpu_rows, cpu_baseline=True):
@@ -111,8 +128,10 @@ def bench_gauss_1m(steps, warmup, cpu_rows, cpu_baseline=True):
     # library also records an event pair on that stream around each launch of the dominant
     # kernel, the matrix-core sweep, which gives that kernel's own average duration.
     lib = _lib.load()
+    per_step = []
     t = _events_time(step, steps, warmup, before_timed=lambda: _lib.check(lib.keops_sweep_timing(1),
-                                                                           "keops_sweep_timing"))
+                                                                           "keops_sweep_timing"),
+                     per_step=per_step)
     sweep_ms, sweeps = ctypes.c_float(0.0), ctypes.c_int(0)
     _lib.check(lib.keops_sweep_timing_read(ctypes.byref(sweep_ms), ctypes.byref(sweeps)), "keops_sweep_timing_read")
     _lib.check(lib.keops_sweep_timing(0), "keops_sweep_timing")
@@ -135,6 +154,7 @@ def bench_gauss_1m(steps, warmup, cpu_rows, cpu_baseline=True):
         "data": "synthetic: x, y uniform on the 2^-24 grid in [0,1)^3, b ~ N(0,1), seed 0",
         "config": {"workload": key, "M": M, "N": N, "D": D, "C": C, "sigma": sigma,
                    "pairs_per_step": pairs},
+        "step_stats": _stats(per_step),
         "roofline": {
             "bound": "alu",
             "achieved": achieved,
@@ -154,6 +174,48 @@ def bench_gauss_1m(steps, warmup, cpu_rows, cpu_baseline=True):
     out_host = out.cpu().numpy()
     result["config"]["checksum"] = float(np.sum(out_host, dtype=np.float64))
     return result
+
+
+def bench_fp16_secondary(reps, warmup):
+    """The batched fp16 Gauss sum (B=4, M=N=16384, D=C=32, tau=1) on the matrix cores, as one
+    extra object of the JSON line: whole-call time per rep (mean +- std, median) and the
+    forward sweep's own average duration from events around each of its launches, against the
+    dense fp16 matrix-core peak (2(D + C) flop per pair)."""
+    import torch
+
+    import pairwise_reductions_amd as pr
+    from pairwise_reductions_amd import _lib, workloads
+
+    key = "batched_gauss_sum_fp16"
+    inp = workloads.make_inputs(key)
+    Bt, M, N, D, C = inp["B"], inp["M"], inp["N"], inp["D"], inp["C"]
+    dev = torch.device("cuda:0")
+    q, k, v = _resident(inp, ("x", "y", "b"), dev)
+    sig = float(inp["sigma"])
+    out = torch.empty((Bt, M, C), device=dev)
+    ws = torch.empty(max(1, pr.workspace_bytes(_lib.OP_GAUSS_SUM, Bt, M, N, D, C, 0, _lib.KEOPS_F16)),
+                     dtype=torch.uint8, device=dev)
+    lib = _lib.load()
+    per_step = []
+    t = _events_time(lambda: pr.gauss_sum(q, k, v, sig, out=out, workspace=ws), reps, warmup,
+                     before_timed=lambda: _lib.check(lib.keops_sweep_timing(1), "keops_sweep_timing"),
+                     per_step=per_step)
+    sweep_ms, sweeps = ctypes.c_float(0.0), ctypes.c_int(0)
+    _lib.check(lib.keops_sweep_timing_read(ctypes.byref(sweep_ms), ctypes.byref(sweeps)), "keops_sweep_timing_read")
+    _lib.check(lib.keops_sweep_timing(0), "keops_sweep_timing")
+    kernel_s = sweep_ms.value / 1e3 / sweeps.value if sweeps.value == reps else t
+    pairs = float(Bt) * M * N
+    mflops = pairs * 2 * (D + C)
+    return {
+        "workload": key, "B": Bt, "M": M, "N": N, "D": D, "C": C, "dtype": "f16", "tau": 1.0 / sig ** 2,
+        "pairs_per_s": pairs / t, "ms_per_call": t * 1e3, "step_stats": _stats(per_step),
+        "roofline": {"bound": "mfma", "achieved": mflops / kernel_s / 1e12, "peak": PEAK_FP16_MFMA_TFLOPS,
+                     "unit": "TFLOP/s", "frac": mflops / kernel_s / 1e12 / PEAK_FP16_MFMA_TFLOPS,
+                     "kernel": "fwd_kernel<_Float16,32,32,...>", "flop_per_pair": 2 * (D + C),
+                     "kernel_ms": kernel_s * 1e3,
+                     "kernel_timing": "events around each launch" if sweeps.value == reps else "whole call",
+                     "call_frac": mflops / t / 1e12 / PEAK_FP16_MFMA_TFLOPS},
+    }
 
 
 def cpu_baseline_gauss(inp, rows):
@@ -419,6 +481,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--cpu-rows", type=int, default=8192, help="rows of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the batched fp16 matrix-core workload reported beside the headline")
     ap.add_argument("--all", action="store_true", help="also time the other workloads")
     ap.add_argument("--only", choices=ALL_GROUPS, default=None,
                     help="with --all: time one group of workloads and skip the headline line")
@@ -454,6 +518,8 @@ def main():
         if args.only:
             return
     res = bench_gauss_1m(args.steps, args.warmup, args.cpu_rows, cpu_baseline=not args.no_cpu_baseline)
+    if not args.no_secondary:
+        res["secondary"] = [bench_fp16_secondary(max(100, args.steps), max(3, args.warmup))]
     print(json.dumps(res), flush=True)
 
 

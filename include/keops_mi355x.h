@@ -274,11 +274,13 @@ KEOPS_API const char* keops_last_error(void);
 /* Library version string. */
 KEOPS_API const char* keops_version(void);
 
-/* Measurement aid (not needed to compute anything): timing of the main sweep of the low-D
- * float32 Gauss sum, i.e. the launch of its matrix-core sweep (the kernel that carries the
- * pair work; the preparation and split-combine kernels around it are excluded).
- *   keops_sweep_timing(1) makes every following keops_gauss_sum call on the calling thread
- *   record a pair of HIP events on its stream around that launch; keops_sweep_timing(0)
+/* Measurement aid (not needed to compute anything): timing of the main sweep of a Gauss sum,
+ * i.e. the launch of the kernel that carries the pair work (the low-D float32 family's
+ * matrix-core sweep, or the matrix-core family's forward sweep); the preparation and
+ * split-combine kernels around it are excluded. keops_gauss_sum, keops_gauss_sum_noalloc and
+ * keops_gauss_sum_scaled record it.
+ *   keops_sweep_timing(1) makes every following such call on the calling thread record a
+ *   pair of HIP events on its stream around that launch; keops_sweep_timing(0)
  *   stops and discards what was recorded.
  *   keops_sweep_timing_read(&ms, &count) waits for the recorded pairs, returns their summed
  *   elapsed milliseconds and their number, and clears them (timing stays enabled).

@@ -237,14 +237,15 @@ struct Split {
   int64_t Npad, row_blocks, splits, kps;
 };
 
-// Column splits: enough workgroups for kSplitTarget per CU, each split >= 4 * kKeyPad keys and
-// a multiple of kKeyPad (so split boundaries fall on stage boundaries).
-Split plan_split(int64_t B, int64_t M, int64_t N, int rows_per_block, int num_cus) {
+// Column splits: enough workgroups for kSplitTarget workgroups of kWaves waves per CU (fewer
+// when a workgroup has more waves), each split >= 4 * kKeyPad keys and a multiple of kKeyPad (so
+// split boundaries fall on stage boundaries).
+Split plan_split(int64_t B, int64_t M, int64_t N, int rows_per_block, int num_cus, int waves = hd::kWaves) {
   Split p;
   p.Npad = hd::padded_keys(N);
   p.row_blocks = hd_ceil_div(M, rows_per_block);
   const int64_t blocks = p.row_blocks * B;
-  const int64_t target = (int64_t)num_cus * hd::kSplitTarget;
+  const int64_t target = (int64_t)num_cus * hd::kSplitTarget * hd::kWaves / waves;
   int64_t S = blocks < target ? hd_ceil_div(target, blocks) : 1;
   const int64_t max_split = p.Npad / (4 * hd::kKeyPad) > 1 ? p.Npad / (4 * hd::kKeyPad) : 1;
   if (S > max_split) S = max_split;
@@ -273,7 +274,9 @@ FwdLayout fwd_layout(int64_t B, int64_t M, int64_t N, int D, int C, ElemType xy,
   FwdLayout L;
   const int Cp = hd::padded_channels(C);
   const bool split = xy == kElemF32;
-  L.sp = plan_split(B, M, N, hd::kWaves * hd::fwd_query_tiles(hd::padded_features(D), Cp, split) * 16, num_cus);
+  const int Dp = hd::padded_features(D);
+  const int W = hd::fwd_waves(Dp, Cp, split);
+  L.sp = plan_split(B, M, N, W * hd::fwd_query_tiles(Dp, Cp, split) * 16, num_cus, W);
   Carve c;
   const size_t table = (size_t)B * L.sp.Npad * Cp * sizeof(_Float16);
   L.nmax = c.take(general ? (size_t)B * sizeof(float) : 0);
@@ -491,7 +494,9 @@ hipError_t launch_gauss_sum_highd(const void* x, const void* y, ElemType xy, con
   a.C = C;
   a.grid = dim3((unsigned)L.sp.row_blocks, (unsigned)L.sp.splits, (unsigned)B);
   a.stream = s;
+  sweep_event(s, true);
   e = fwd_dispatch(a, xy);
+  sweep_event(s, false);
   if (e != hipSuccess || L.sp.splits == 1) return e;
   return combine(part, out, B * M * C, L.sp.splits, s);
 }

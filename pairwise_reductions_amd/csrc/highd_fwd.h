@@ -111,8 +111,8 @@ __device__ __forceinline__ f32x4 s_mfma(const Op<TIn>& k, const Op<TIn>& q, f32x
   }
 }
 
-template <typename TIn, int D, int C, int QT, int kStage, bool kFused>
-__global__ void __launch_bounds__(256, 1)
+template <typename TIn, int D, int C, int QT, int kStage, bool kFused, int kW>
+__global__ void __launch_bounds__(64 * kW, 1)
 fwd_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const float* __restrict__ beta,
            const _Float16* __restrict__ vp, const _Float16* __restrict__ vpl, float* __restrict__ out,
            const float* __restrict__ rscale, const float* __restrict__ oscale, int64_t M, int64_t N, int64_t Npad,
@@ -124,7 +124,8 @@ fwd_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const float* __
   constexpr int KP = D + 8;          // LDS row pitch of K, 16-bit elements
   constexpr int VP = 32 + 8;         // LDS row pitch of V^T, halves
   constexpr int NSUB = kStage / 32;
-  constexpr int kRowsPerBlock = kWaves * QT * 16;
+  constexpr int kRowsPerBlock = kW * QT * 16;
+  constexpr int kThreads = 64 * kW;
   using Raw = typename std::conditional<std::is_same<TIn, __bf16>::value, __bf16, _Float16>::type;
   using Raw8 = decltype(Op<TIn>{}.h);
   __shared__ __attribute__((aligned(16))) Raw sK[NP][2][kStage][KP];
@@ -172,10 +173,10 @@ fwd_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const float* __
 
   // Stage loads: global -> registers (issued before the current stage is computed) and
   // registers -> LDS (after it), so global latency hides behind the matrix work. Tables are
-  // cut into 8-element chunks dealt round-robin to the 256 threads.
-  constexpr int kKChunks = kStage * D / 8, KCH = (kKChunks + 255) / 256;
-  constexpr int kVChunks = NSUB * C * 4, VCH = (kVChunks + 255) / 256;
-  static_assert(kStage / 4 <= 256 && kStage % 32 == 0, "tile shapes");
+  // cut into 8-element chunks dealt round-robin to the workgroup's threads.
+  constexpr int kKChunks = kStage * D / 8, KCH = (kKChunks + kThreads - 1) / kThreads;
+  constexpr int kVChunks = NSUB * C * 4, VCH = (kVChunks + kThreads - 1) / kThreads;
+  static_assert(kStage / 4 <= kThreads && kStage % 32 == 0, "tile shapes");
   Raw8 rk[NP][KCH];
   half8 rv[NP][VCH];
   f32x4 rb = {};
@@ -183,7 +184,7 @@ fwd_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const float* __
     const int64_t jb = j0 + st * kStage;
 #pragma unroll
     for (int r = 0; r < KCH; ++r) {
-      const int c = tid + 256 * r;
+      const int c = tid + kThreads * r;
       const int row = c / (D / 8), col = (c % (D / 8)) * 8;
       const int64_t j = jb + row;
       float unused = 0.0f;
@@ -196,7 +197,7 @@ fwd_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const float* __
     for (int p = 0; p < NP; ++p)
 #pragma unroll
       for (int r = 0; r < VCH; ++r) {
-        const int c = tid + 256 * r;
+        const int c = tid + kThreads * r;
         const int t = c / (C * 4), rem = c % (C * 4), ch = rem / 4, part = (rem % 4) * 8;
         if (c < kVChunks) rv[p][r] = *reinterpret_cast<const half8*>(vb[p] + ((jb / 32 + t) * C + ch) * 32 + part);
       }
@@ -207,12 +208,12 @@ fwd_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const float* __
     for (int p = 0; p < NP; ++p) {
 #pragma unroll
       for (int r = 0; r < KCH; ++r) {
-        const int c = tid + 256 * r;
+        const int c = tid + kThreads * r;
         if (c < kKChunks) *reinterpret_cast<Raw8*>(&sK[p][buf][c / (D / 8)][(c % (D / 8)) * 8]) = rk[p][r];
       }
 #pragma unroll
       for (int r = 0; r < VCH; ++r) {
-        const int c = tid + 256 * r;
+        const int c = tid + kThreads * r;
         const int t = c / (C * 4), rem = c % (C * 4);
         if (c < kVChunks) *reinterpret_cast<half8*>(&sV[p][buf][t][rem / 4][(rem % 4) * 8]) = rv[p][r];
       }
@@ -390,13 +391,87 @@ fwd_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const float* __
     __syncthreads();
   };
 
+  // Settled stages, software-pipelined over the stage's (subtile, query tile) units: the
+  // scores of the next unit are issued on the matrix cores before the exponentials of the
+  // current one (two score buffers alternate), and the next subtile's key, bias and weight
+  // operands are read from LDS one subtile ahead (two operand sets alternate), so neither the
+  // VALU nor the matrix cores wait on a result just requested.
+  struct Operands {
+    Op<TIn> k[2][DS];
+    f32x4 b[2];
+    half8 v[NP][CT];
+  };
+  auto read_operands = [&](int buf, int sub, Operands& o) {
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+      for (int ds = 0; ds < DS; ++ds) {
+        const int key = sub * 32 + 16 * hh + l16, col = 32 * ds + 8 * g;
+        o.k[hh][ds].h = *reinterpret_cast<const Raw8*>(&sK[0][buf][key][col]);
+        if constexpr (SPLIT) o.k[hh][ds].l = *reinterpret_cast<const half8*>(&sK[NP - 1][buf][key][col]);
+      }
+      o.b[hh] = *reinterpret_cast<const f32x4*>(&sB[buf][sub * 32 + 16 * hh + 4 * g]);
+    }
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+        o.v[p][ct] = *reinterpret_cast<const half8*>(&sV[p][buf][sub][16 * ct + l16][8 * g]);
+  };
+  auto score_with = [&](const Operands& o, int qt, f32x4 (&S)[2]) {
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      S[hh] = s_mfma<TIn>(o.k[hh][0], qop[qt][0], o.b[hh]);
+#pragma unroll
+      for (int ds = 1; ds < DS; ++ds) S[hh] = s_mfma<TIn>(o.k[hh][ds], qop[qt][ds], S[hh]);
+    }
+  };
+  auto stage_pipe = [&](int64_t st) {
+    const int buf = (int)(st & 1);
+    if (st + 1 < nstages) fetch(st + 1);
+    Operands ops[2];
+    read_operands(buf, 0, ops[0]);
+    f32x4 Sbuf[2][2];
+    score_with(ops[0], 0, Sbuf[0]);
+#pragma unroll
+    for (int u = 0; u < NSUB * QT; ++u) {
+      const int sub = u / QT, qt = u % QT;
+      const Operands& cur = ops[sub & 1];
+      if (qt == 0 && sub + 1 < NSUB) read_operands(buf, sub + 1, ops[(sub + 1) & 1]);
+      if (u + 1 < NSUB * QT) {
+        if (qt + 1 < QT)
+          score_with(cur, qt + 1, Sbuf[(u + 1) & 1]);
+        else
+          score_with(ops[(sub + 1) & 1], 0, Sbuf[(u + 1) & 1]);
+      }
+      const f32x4(&S)[2] = Sbuf[u & 1];
+      half8 ph, pl;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const float pv = exp2_hw(fmaf(S[s >> 2][s & 3], cs, alpha[qt]));
+        ph[s] = (_Float16)pv;
+        if constexpr (SPLIT) pl[s] = (_Float16)(pv - (float)ph[s]);
+      }
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        O[qt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(cur.v[0][ct], ph, O[qt][ct], 0, 0, 0);
+        if constexpr (SPLIT) {
+          O[qt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(cur.v[NP - 1][ct], ph, O[qt][ct], 0, 0, 0);
+          O[qt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(cur.v[0][ct], pl, O[qt][ct], 0, 0, 0);
+        }
+      }
+    }
+    if (st + 1 < nstages) commit(buf ^ 1);
+    __syncthreads();
+  };
+
   fetch(0);
   commit(0);
   __syncthreads();
   int64_t st = 0;
   if constexpr (kFused) {
     for (; st < nstages && !settled; ++st) stage_fused(st, std::true_type{});
-    for (; st < nstages; ++st) stage_fused(st, std::false_type{});
+    for (; st < nstages; ++st) stage_pipe(st);
   } else {
     for (; st < nstages && !settled; ++st) stage_batched(st, std::true_type{});
     for (; st < nstages; ++st) stage_batched(st, std::false_type{});
@@ -433,12 +508,13 @@ fwd_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const float* __
 template <typename TIn, int Dp>
 hipError_t fwd_launch(const FwdArgs& a) {
   const int Cp = padded_channels(a.C);
-  constexpr int kStage = kSplit<TIn> ? 32 : kStageKeys;
   const TIn* q = static_cast<const TIn*>(a.q);
   const TIn* k = static_cast<const TIn*>(a.k);
 #define KEOPS_FWD(Cv)                                                                                       \
-  fwd_kernel<TIn, Dp, Cv, fwd_query_tiles(Dp, Cv, kSplit<TIn>), kStage, fwd_fused(Dp, Cv, kSplit<TIn>)>          \
-      <<<a.grid, 256, 0, a.stream>>>(                                                                              \
+  fwd_kernel<TIn, Dp, Cv, fwd_query_tiles(Dp, Cv, kSplit<TIn>), fwd_stage(Dp, Cv, kSplit<TIn>),                 \
+             fwd_fused(Dp, Cv, kSplit<TIn>),                                                                       \
+             fwd_waves(Dp, Cv, kSplit<TIn>)>                                                                       \
+      <<<a.grid, 64 * fwd_waves(Dp, Cv, kSplit<TIn>), 0, a.stream>>>(                                             \
       q, k, a.beta, a.vp, a.vpl, a.out, a.rscale, a.oscale, a.M, a.N, a.Npad, a.kps, a.cs, a.D, a.C)
   if (Cp == 16) KEOPS_FWD(16);
   else if (Cp == 32) KEOPS_FWD(32);
