@@ -251,7 +251,7 @@ def _resident(inp, keys, dev):
 
 
 ALL_GROUPS = ("gauss_sum_10k", "grad_100k", "fp16", "fp16_fwd_bwd", "fp16_d_sweep", "bf16_f32", "diffusion",
-              "argkmin_lse")
+              "argkmin_lse", "gauss_sum_1m_outliers")
 
 
 def bench_all(steps, warmup, only=None, cpu=True):
@@ -470,6 +470,22 @@ def bench_all(steps, warmup, only=None, cpu=True):
 
             rows["argkmin_lse_100k"].update(_oracle_rate(
                 oracle_argk_lse, 2.0 * n * N, f"argKmin and LSE, first {n} rows x all {N} columns"))
+
+    # The 1M x 1M Gauss sum with one far row and one far column (near (1000, 1000, 1000)): the
+    # two points are set aside and the rest stays on the matrix cores.
+    if want("gauss_sum_1m_outliers"):
+        inp = workloads.make_inputs("gauss_sum_1m")
+        xo, yo = inp["x"].copy(), inp["y"].copy()
+        xo[123_457] = 1000.0
+        yo[876_543] = np.float32(1000.001)
+        x, y, b = (torch.from_numpy(a).to(dev) for a in (xo, yo, inp["b"]))
+        M, N = inp["M"], inp["N"]
+        out = torch.empty((M, 1), device=dev)
+        ws = torch.empty(pr.workspace_bytes(0, 1, M, N, 3, 1), dtype=torch.uint8, device=dev)
+        sig = float(inp["sigma"])
+        t = _events_time(lambda: pr.gauss_sum(x, y, b, sig, out=out, workspace=ws), max(3, min(steps, 10)), warmup)
+        rows["gauss_sum_1m_one_far_row_and_column"] = {"ms": t * 1e3, "pairs_per_s": float(M) * N / t}
+        del x, y, b, out, ws
 
     return rows
 

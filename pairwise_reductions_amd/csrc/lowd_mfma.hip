@@ -24,6 +24,14 @@
 // past 32 (a narrow kernel on widely spread data), the float64 path runs instead: both sweeps
 // are launched and each reads the decision from device memory, so nothing waits on the host.
 //
+// Set-aside points (Gauss sum only). When the bounding box of all points is too wide for the
+// low part, but a box of the largest admissible half-width centred on the per-dimension median
+// of an evenly spaced sample of the points holds all but a few of them (at most kMaxAside rows
+// and kMaxAside columns), those few are set aside: a set-aside column gets the padding record (its 2^e is exactly 0 in the sweep) and
+// a set-aside row zero pieces; afterwards every row gets the set-aside columns' terms added in
+// a fixed order, and every set-aside row is summed over all columns from a float64 exponent.
+// One far outlier thus no longer sends the whole sum to the float64 sweep.
+//
 // Per pair the VALU then does one v_exp_f32 and C FMAs; the two MFMAs of a 16 x 16 tile run on
 // the matrix core beside them.
 #include "lowd_common.h"
@@ -31,6 +39,7 @@
 #include <math.h>
 
 #include <atomic>
+#include <type_traits>
 
 namespace keops {
 namespace lowd {
@@ -44,6 +53,8 @@ constexpr double kMaxLow = 32.0;   // largest admissible bound on the low part
 constexpr int kBoundBlocks = 256;  // most workgroups of the bounds pass
 constexpr uint32_t kXcds = 8;      // accelerator complexes (each with its own L2) on the chip
 constexpr int64_t kMaxLaunch = int64_t(1) << 30;  // most workgroups per sweep launch
+constexpr int kMaxAside = 256;     // most set-aside rows, and most set-aside columns (and samples)
+static_assert(kBoundBlocks <= kMaxAside, "every bounds workgroup records at least one sample");
 constexpr int kChunkTiles = kChunk / 16;
 
 // Product kinds (row piece x column piece); the shift table is indexed by these.
@@ -53,7 +64,9 @@ enum Slot { kAhVh = 0, kOneBh1, kOneBh2, kAhVl1, kAhVl2, kAl1Vh, kAl2Vh, kAl1Vl1
 // The matrix-core sweep runs when gate != 0 and bad == 0, the float64 sweep otherwise.
 struct MfParams {
   int gate;           // the scales admit the matrix-core path
-  int bad;            // some piece did not convert exactly
+  int bad;            // some piece did not convert exactly, or too many points were set aside
+  int robust;         // the box is centred on the mean and points outside it are set aside
+  int nbr, nbc;       // set-aside rows and columns so far (lists in the operand region)
   int alpha, beta, gamma;
   int sh[kSlots];
   double o[kMaxLowD];
@@ -73,16 +86,23 @@ __device__ __forceinline__ double rnd(double v, int g) { return ldexp(rint(ldexp
 
 // Per-dimension min and max over the rows of x and of y: one (min, max) record per workgroup in
 // parts[blockIdx] (order-preserving unsigned encodings, dimension d at d and kMaxLowD + d).
-// Workgroup 0 also clears the bad flag.
+// Workgroup k also records samples k*spw .. k*spw + spw - 1 of an evenly spaced sample of the
+// points (x then y), dimension d of sample s at samples[d * kMaxAside + s]. Workgroup 0 also
+// clears the bad flag and the set-aside counts.
 __global__ void __launch_bounds__(kBlock)
 mf_bounds_kernel(const float* __restrict__ x, const float* __restrict__ y, int64_t M, int64_t N, int D,
-                 unsigned int* __restrict__ parts, MfParams* __restrict__ P) {
+                 unsigned int* __restrict__ parts, float* __restrict__ samples, int spw, MfParams* __restrict__ P) {
   __shared__ unsigned int red[kBlock / 64][2 * kMaxLowD];
   unsigned int lo[kMaxLowD], hi[kMaxLowD];
 #pragma unroll
   for (int d = 0; d < kMaxLowD; ++d) {
     lo[d] = 0xffffffffu;
     hi[d] = 0u;
+  }
+  if ((int)threadIdx.x < spw) {
+    const int64_t ns = (int64_t)gridDim.x * spw, k = (int64_t)blockIdx.x * spw + threadIdx.x;
+    const int64_t pt = k * (M + N) / ns;
+    for (int d = 0; d < D; ++d) samples[d * kMaxAside + k] = pt < M ? x[pt * D + d] : y[(pt - M) * D + d];
   }
   const int64_t n = M > N ? M : N;
   for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n; i += (int64_t)gridDim.x * kBlock) {
@@ -126,23 +146,60 @@ mf_bounds_kernel(const float* __restrict__ x, const float* __restrict__ y, int64
     }
     parts[blockIdx.x * 2 * kMaxLowD + t] = v;
   }
-  if (blockIdx.x == 0 && threadIdx.x == 0) P->bad = 0;
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    P->bad = 0;
+    P->nbr = 0;
+    P->nbc = 0;
+  }
 }
 
-// Centre, scale, grids and shifts from the bounds; gate = 0 when the low part could exceed
-// kMaxLow or a shift has no admissible value. One thread.
-__device__ void mf_params(const unsigned int* mm, int D, double c2, MfParams& P) {
+// Exponent of the largest scale bound 2^k (2 c2 h^2 <= 2^k) whose low part stays within kMaxLow.
+__device__ int max_scale_exp(int D) {
+  int lg = 0;
+  while ((1 << lg) < D) ++lg;
+  int k = kMinK;
+  while (D * (ldexp(1.0, k + 1 + lg - 12) + ldexp(1.0, k + 1 - 12)) <= kMaxLow) ++k;
+  return k;
+}
+
+// Half-width (times 1 + 2^-40, which keeps |u|, |v| <= 1 after rounding) and centre (o, D
+// values) of the bounding box in mm; clears finite when a bound is not finite.
+__device__ double box_of(const unsigned int* mm, int D, double* o, bool& finite) {
   double h = 0.0;
-  bool finite = true;
+  finite = true;
   for (int d = 0; d < D; ++d) {
     const double lo = (double)float_of(mm[d]), hi = (double)float_of(mm[kMaxLowD + d]);
     finite = finite && isfinite(lo) && isfinite(hi);
-    const double o = (double)(float)(0.5 * (lo + hi));
-    P.o[d] = o;
-    h = fmax(h, fmax(hi - o, o - lo));
+    o[d] = (double)(float)(0.5 * (lo + hi));
+    h = fmax(h, fmax(hi - o[d], o[d] - lo));
   }
   if (!(h > 0.0)) h = 1.0;  // all points equal: any scale will do
-  h *= 1.0 + 0x1p-40;       // keeps |u|, |v| <= 1 after rounding
+  return h * (1.0 + 0x1p-40);
+}
+
+// Whether the box of half-width h is too wide for the low part at this c2.
+__device__ bool too_wide(double h, int D, double c2) { return !(2.0 * c2 * h * h <= ldexp(1.0, max_scale_exp(D))); }
+
+// Centre, scale, grids and shifts from the bounds; gate = 0 when the low part could exceed
+// kMaxLow or a shift has no admissible value. With a centre `med` (set-aside mode, given only
+// when the bounding box is too wide), the box is instead the one of the largest admissible
+// half-width around med, and robust = 1: the points outside it are set aside by the
+// preparation. One thread.
+__device__ void mf_params(const unsigned int* mm, const double* med, int D, double c2, MfParams& P) {
+  bool finite = true;
+  double h = box_of(mm, D, P.o, finite);
+  P.robust = 0;
+  if (med && finite) {
+    bool ok = true;
+    for (int d = 0; d < D; ++d) {
+      ok = ok && isfinite(med[d]);
+      P.o[d] = med[d];
+    }
+    // the largest half-width whose scale stays within the bound (kept a little inside it)
+    h = sqrt(ldexp(1.0, max_scale_exp(D) - 1) / c2) * (1.0 - 0x1p-20);
+    if (ok && h > 0.0 && isfinite(h)) P.robust = 1;
+    else finite = false;
+  }
   const double cp = c2 * h * h;
   P.inv_h = 1.0 / h;
   P.cp = cp;
@@ -221,9 +278,14 @@ __global__ void __launch_bounds__(kBlock)
 mf_prep_kernel(const float* __restrict__ x, const float* __restrict__ y, const float* __restrict__ b, int C,
                int with_y, double* __restrict__ cols, half8* __restrict__ rhi, half8* __restrict__ rlo, float* __restrict__ rA,
                half8* __restrict__ chi, half8* __restrict__ clo, float* __restrict__ bpad,
-               const unsigned int* __restrict__ parts, int nparts, int64_t M, int64_t N, int64_t Npad, int D,
-               double c2, int64_t rb, MfParams* __restrict__ P) {
+               const unsigned int* __restrict__ parts, const float* __restrict__ samples, int nsamples, int nparts,
+               int64_t M, int64_t N, int64_t Npad, int D, double c2, int64_t rb, int set_aside,
+               int32_t* __restrict__ aside_rows, int32_t* __restrict__ aside_cols, MfParams* __restrict__ P) {
   __shared__ unsigned int red[kBlock / 64][2 * kMaxLowD];
+  __shared__ unsigned int smm[2 * kMaxLowD];
+  __shared__ float ssort[kMaxAside];
+  __shared__ double smed[kMaxLowD];
+  __shared__ int swide;
   __shared__ MfParams sp;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
@@ -239,18 +301,50 @@ mf_prep_kernel(const float* __restrict__ x, const float* __restrict__ y, const f
   }
   __syncthreads();
   if (threadIdx.x == 0) {
-    unsigned int mm[2 * kMaxLowD];
     for (int t = 0; t < 2 * kMaxLowD; ++t) {
       unsigned int v = red[0][t];
       for (int w = 1; w < kBlock / 64; ++w) {
         const unsigned int u = red[w][t];
         v = t < kMaxLowD ? (u < v ? u : v) : (u > v ? u : v);
       }
-      mm[t] = v;
+      smm[t] = v;
     }
-    mf_params(mm, D, c2, sp);
+    double o[kMaxLowD];
+    bool finite = true;
+    const double h = box_of(smm, D, o, finite);
+    swide = (set_aside && finite && too_wide(h, D, c2)) ? 1 : 0;
+  }
+  __syncthreads();
+  if (swide) {
+    // set-aside mode: the centre is the per-dimension median of the bounds pass's sample
+    // (every workgroup sorts the same values, so all derive the same centre)
+    for (int d = 0; d < D; ++d) {
+      for (int t = threadIdx.x; t < kMaxAside; t += kBlock) ssort[t] = t < nsamples ? samples[d * kMaxAside + t] : INFINITY;
+      __syncthreads();
+      for (int k = 2; k <= kMaxAside; k <<= 1)
+        for (int jstep = k >> 1; jstep > 0; jstep >>= 1) {
+          for (int t = threadIdx.x; t < kMaxAside; t += kBlock) {
+            const int q = t ^ jstep;
+            if (q > t) {
+              const bool up = (t & k) == 0;
+              const float a = ssort[t], c = ssort[q];
+              if ((a > c) == up) {
+                ssort[t] = c;
+                ssort[q] = a;
+              }
+            }
+          }
+          __syncthreads();
+        }
+      if (threadIdx.x == 0) smed[d] = (double)ssort[(nsamples - 1) / 2];
+      __syncthreads();
+    }
+  }
+  if (threadIdx.x == 0) {
+    mf_params(smm, swide ? smed : nullptr, D, c2, sp);
     if (blockIdx.x == 0) {
       P->gate = sp.gate;
+      P->robust = sp.robust;
       P->alpha = sp.alpha;
       P->beta = sp.beta;
       P->gamma = sp.gamma;
@@ -269,6 +363,19 @@ mf_prep_kernel(const float* __restrict__ x, const float* __restrict__ y, const f
     for (int k = 0; k < 8 * NH; ++k) hi[k] = (_Float16)0.0f;
 #pragma unroll
     for (int k = 0; k < 32 * NL; ++k) lo[k] = (_Float16)0.0f;
+    if (sp.robust) {
+      bool inside = true;
+      for (int d = 0; d < D; ++d) inside = inside && fabs(((double)x[i * D + d] - sp.o[d]) * inv_h) <= 1.0;
+      if (!inside) {  // set aside: zero pieces here, summed over all columns afterwards
+        const int slot = atomicAdd(&P->nbr, 1);
+        if (slot < kMaxAside) aside_rows[slot] = (int32_t)i;
+        else P->bad = 1;
+        store_pieces<NH>(rhi + i * NH, hi);
+        store_pieces<4 * NL>(rlo + i * 4 * NL, lo);
+        rA[i] = 0.0f;
+        return;
+      }
+    }
     double nrm = 0.0;
 #pragma unroll
     for (int d = 0; d < kMaxLowD; ++d) {
@@ -330,7 +437,16 @@ mf_prep_kernel(const float* __restrict__ x, const float* __restrict__ y, const f
     for (int k = 0; k < 8 * NH; ++k) hi[k] = (_Float16)0.0f;
 #pragma unroll
     for (int k = 0; k < 32 * NL; ++k) lo[k] = (_Float16)0.0f;
-    if (j < N) {
+    bool inside = true;
+    if (j < N && sp.robust) {
+      for (int d = 0; d < D; ++d) inside = inside && fabs(((double)y[j * D + d] - sp.o[d]) * inv_h) <= 1.0;
+      if (!inside) {  // set aside: the padding record here, its terms added to every row afterwards
+        const int slot = atomicAdd(&P->nbc, 1);
+        if (slot < kMaxAside) aside_cols[slot] = (int32_t)j;
+        else P->bad = 1;
+      }
+    }
+    if (j < N && inside) {
       double nrm = 0.0;
 #pragma unroll
       for (int d = 0; d < kMaxLowD; ++d) {
@@ -813,12 +929,113 @@ grad_mf_kernel(const half8* __restrict__ rhi, const half8* __restrict__ rlo, con
     }
 }
 
+// Terms of the set-aside columns: out[i][c] += rscale[i] sum_j 2^{-c2 |x_i - y_j|^2} b[j][c] over
+// the set-aside columns j in increasing order, for every row (the set-aside rows' own results
+// are overwritten by aside_rows_kernel afterwards). The exponent is the float64 squared
+// distance of the float32 inputs, times c2, rounded to float32 before the exponential; the
+// terms are added in float64, then to the row's float32 result. Each workgroup sorts the
+// (at most kMaxAside) recorded indices itself, so the order does not depend on the order in
+// which the preparation recorded them.
+template <int D, int C>
+__global__ void __launch_bounds__(kBlock)
+aside_cols_kernel(const float* __restrict__ x, const float* __restrict__ y, const float* __restrict__ b,
+                  const float* __restrict__ rscale, float* __restrict__ out, const int32_t* __restrict__ aside_cols,
+                  const MfParams* __restrict__ P, int64_t M, double c2) {
+  if (!P->gate || P->bad || !P->robust || P->nbc == 0) return;
+  const int n = P->nbc < kMaxAside ? P->nbc : kMaxAside;
+  __shared__ int32_t list[kMaxAside];
+  for (int t = threadIdx.x; t < kMaxAside; t += kBlock) list[t] = t < n ? aside_cols[t] : 0x7fffffff;
+  __syncthreads();
+  // bitonic sort of kMaxAside entries, ascending
+  for (int k = 2; k <= kMaxAside; k <<= 1)
+    for (int jstep = k >> 1; jstep > 0; jstep >>= 1) {
+      for (int t = threadIdx.x; t < kMaxAside; t += kBlock) {
+        const int o = t ^ jstep;
+        if (o > t) {
+          const bool up = (t & k) == 0;
+          const int32_t a = list[t], c = list[o];
+          if ((a > c) == up) {
+            list[t] = c;
+            list[o] = a;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+  if (i >= M) return;
+  double xi[D], acc[C];
+#pragma unroll
+  for (int d = 0; d < D; ++d) xi[d] = (double)x[i * D + d];
+#pragma unroll
+  for (int c = 0; c < C; ++c) acc[c] = 0.0;
+  for (int e = 0; e < n; ++e) {
+    const int64_t j = list[e];
+    double d2 = 0.0;
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const double t = xi[d] - (double)y[j * D + d];
+      d2 = fma(t, t, d2);
+    }
+    const double k = (double)exp2_hw((float)(-c2 * d2));
+#pragma unroll
+    for (int c = 0; c < C; ++c) acc[c] = fma(k, (double)b[j * C + c], acc[c]);
+  }
+  const double sc = rscale ? (double)rscale[i] : 1.0;
+#pragma unroll
+  for (int c = 0; c < C; ++c) out[i * C + c] += (float)(sc * acc[c]);
+}
+
+// The set-aside rows, one workgroup each: out[i][c] = rscale[i] sum_j 2^{-c2 |x_i - y_j|^2} b[j][c]
+// over all columns, exponents as in aside_cols_kernel, each thread summing a fixed stride of
+// columns in float64 and the workgroup adding the threads' sums in a fixed tree order.
+template <int D, int C>
+__global__ void __launch_bounds__(kBlock)
+aside_rows_kernel(const float* __restrict__ x, const float* __restrict__ y, const float* __restrict__ b,
+                  const float* __restrict__ rscale, float* __restrict__ out, const int32_t* __restrict__ aside_rows,
+                  const MfParams* __restrict__ P, int64_t N, double c2) {
+  if (!P->gate || P->bad || !P->robust) return;
+  const int n = P->nbr < kMaxAside ? P->nbr : kMaxAside;
+  if ((int)blockIdx.x >= n) return;
+  const int64_t i = aside_rows[blockIdx.x];
+  __shared__ double red[C][kBlock];
+  double xi[D], acc[C];
+#pragma unroll
+  for (int d = 0; d < D; ++d) xi[d] = (double)x[i * D + d];
+#pragma unroll
+  for (int c = 0; c < C; ++c) acc[c] = 0.0;
+  for (int64_t j = threadIdx.x; j < N; j += kBlock) {
+    double d2 = 0.0;
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const double t = xi[d] - (double)y[j * D + d];
+      d2 = fma(t, t, d2);
+    }
+    const double k = (double)exp2_hw((float)(-c2 * d2));
+#pragma unroll
+    for (int c = 0; c < C; ++c) acc[c] = fma(k, (double)b[j * C + c], acc[c]);
+  }
+#pragma unroll
+  for (int c = 0; c < C; ++c) red[c][threadIdx.x] = acc[c];
+  __syncthreads();
+  for (int h = kBlock / 2; h > 0; h >>= 1) {
+    if ((int)threadIdx.x < h)
+#pragma unroll
+      for (int c = 0; c < C; ++c) red[c][threadIdx.x] += red[c][threadIdx.x + h];
+    __syncthreads();
+  }
+  if (threadIdx.x < C) {
+    const double sc = rscale ? (double)rscale[i] : 1.0;
+    out[i * C + threadIdx.x] = (float)(sc * red[threadIdx.x][0]);
+  }
+}
+
 // Byte offsets of the operand region: parameters, bounds records, row operands, column
 // operands, padded weights.
 struct MfLayout {
   int NH, NL;
   int64_t Npad;
-  size_t parts, rhi, rlo, rA, chi, clo, bpad, total;
+  size_t parts, samples, aside, rhi, rlo, rA, chi, clo, bpad, total;
 };
 
 // W: floats per padded column record (the weights, and for the gradient also y_j); grad: the
@@ -832,6 +1049,10 @@ MfLayout mf_layout(int64_t M, int64_t N, int D, int W, bool grad = false) {
   size_t off = align_up(sizeof(MfParams));
   L.parts = off;
   off += align_up((size_t)kBoundBlocks * 2 * kMaxLowD * sizeof(unsigned int));
+  L.samples = off;
+  off += align_up((size_t)kMaxLowD * kMaxAside * sizeof(float));
+  L.aside = off;  // set-aside rows, then set-aside columns
+  off += align_up((size_t)2 * kMaxAside * sizeof(int32_t));
   L.rhi = off;
   off += align_up((size_t)M * 16 * L.NH);
   L.rlo = off;
@@ -1055,16 +1276,19 @@ int mf_occupancy(int op, int D, int C, int rt) {
 }
 
 hipError_t launch_mf_prepare(const float* x, const float* y, const float* b, bool with_y, double* cols, void* region,
-                             int64_t M, int64_t N, int D, int C, double c2, hipStream_t s) {
+                             int64_t M, int64_t N, int D, int C, double c2, hipStream_t s, bool set_aside) {
   using namespace lowd;
   char* r = static_cast<char*>(region);
   const MfLayout L = mf_layout(M, N, D, C + (with_y ? D : 0), with_y);
   MfParams* P = reinterpret_cast<MfParams*>(r);
   unsigned int* parts = reinterpret_cast<unsigned int*>(r + L.parts);
+  float* samples = reinterpret_cast<float*>(r + L.samples);
+  int32_t* aside = reinterpret_cast<int32_t*>(r + L.aside);
   const int64_t n = M > N ? M : N;
   int64_t nb = ceil_div(n, kBlock);
   if (nb > kBoundBlocks) nb = kBoundBlocks;
-  mf_bounds_kernel<<<(unsigned)nb, kBlock, 0, s>>>(x, y, M, N, D, parts, P);
+  const int spw = kMaxAside / (int)nb;  // samples per bounds workgroup (nb <= kMaxAside)
+  mf_bounds_kernel<<<(unsigned)nb, kBlock, 0, s>>>(x, y, M, N, D, parts, samples, spw, P);
   const int64_t rb = ceil_div(M, kBlock), cb = ceil_div(L.Npad, kBlock);
   half8* rhi = reinterpret_cast<half8*>(r + L.rhi);
   half8* rlo = reinterpret_cast<half8*>(r + L.rlo);
@@ -1073,12 +1297,56 @@ hipError_t launch_mf_prepare(const float* x, const float* y, const float* b, boo
   half8* clo = reinterpret_cast<half8*>(r + L.clo);
   float* bpad = reinterpret_cast<float*>(r + L.bpad);
   if (L.NH == 1 && L.NL == 1)
-    mf_prep_kernel<1, 1><<<(unsigned)(rb + cb), kBlock, 0, s>>>(x, y, b, C, with_y ? 1 : 0, cols, rhi, rlo, rA, chi,
-                                                               clo, bpad, parts, (int)nb, M, N, L.Npad, D, c2, rb, P);
+    mf_prep_kernel<1, 1><<<(unsigned)(rb + cb), kBlock, 0, s>>>(
+        x, y, b, C, with_y ? 1 : 0, cols, rhi, rlo, rA, chi, clo, bpad, parts, samples, (int)nb * spw, (int)nb, M, N, L.Npad, D, c2, rb,
+        set_aside ? 1 : 0, aside, aside + kMaxAside, P);
   else
-    mf_prep_kernel<2, 2><<<(unsigned)(rb + cb), kBlock, 0, s>>>(x, y, b, C, with_y ? 1 : 0, cols, rhi, rlo, rA, chi,
-                                                               clo, bpad, parts, (int)nb, M, N, L.Npad, D, c2, rb, P);
+    mf_prep_kernel<2, 2><<<(unsigned)(rb + cb), kBlock, 0, s>>>(
+        x, y, b, C, with_y ? 1 : 0, cols, rhi, rlo, rA, chi, clo, bpad, parts, samples, (int)nb * spw, (int)nb, M, N, L.Npad, D, c2, rb,
+        set_aside ? 1 : 0, aside, aside + kMaxAside, P);
   return hipGetLastError();
+}
+
+hipError_t launch_mf_aside(const float* x, const float* y, const float* b, const float* rscale, float* out,
+                           void* region, int64_t M, int64_t N, int D, int C, double c2, hipStream_t s) {
+  using namespace lowd;
+  char* r = static_cast<char*>(region);
+  const MfLayout L = mf_layout(M, N, D, C);
+  const MfParams* P = reinterpret_cast<const MfParams*>(r);
+  const int32_t* aside = reinterpret_cast<const int32_t*>(r + L.aside);
+  auto run = [&](auto dt, auto ct) -> hipError_t {
+    constexpr int Dv = decltype(dt)::value, Cv = decltype(ct)::value;
+    aside_cols_kernel<Dv, Cv><<<(unsigned)ceil_div(M, kBlock), kBlock, 0, s>>>(x, y, b, rscale, out,
+                                                                              aside + kMaxAside, P, M, c2);
+    aside_rows_kernel<Dv, Cv><<<(unsigned)kMaxAside, kBlock, 0, s>>>(x, y, b, rscale, out, aside, P, N, c2);
+    return hipGetLastError();
+  };
+#define KEOPS_ASIDE_C(Dv, Cv) return run(std::integral_constant<int, Dv>{}, std::integral_constant<int, Cv>{})
+#define KEOPS_ASIDE_D(Dv)                  \
+  switch (C) {                             \
+    case 1: KEOPS_ASIDE_C(Dv, 1);          \
+    case 2: KEOPS_ASIDE_C(Dv, 2);          \
+    case 3: KEOPS_ASIDE_C(Dv, 3);          \
+    case 4: KEOPS_ASIDE_C(Dv, 4);          \
+    case 5: KEOPS_ASIDE_C(Dv, 5);          \
+    case 6: KEOPS_ASIDE_C(Dv, 6);          \
+    case 7: KEOPS_ASIDE_C(Dv, 7);          \
+    case 8: KEOPS_ASIDE_C(Dv, 8);          \
+  }                                        \
+  return hipErrorInvalidValue;
+  switch (D) {
+    case 1: KEOPS_ASIDE_D(1)
+    case 2: KEOPS_ASIDE_D(2)
+    case 3: KEOPS_ASIDE_D(3)
+    case 4: KEOPS_ASIDE_D(4)
+    case 5: KEOPS_ASIDE_D(5)
+    case 6: KEOPS_ASIDE_D(6)
+    case 7: KEOPS_ASIDE_D(7)
+    case 8: KEOPS_ASIDE_D(8)
+  }
+#undef KEOPS_ASIDE_D
+#undef KEOPS_ASIDE_C
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_mf_lse(float* out, void* partial, void* region, int64_t M, int64_t N, int D, const Plan& p,

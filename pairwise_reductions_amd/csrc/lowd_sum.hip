@@ -126,7 +126,7 @@ hipError_t launch_gauss_sum_lowd(const float* x, const float* y, double* cols, c
                                  const Plan& p, hipStream_t s) {
   float* dst = p.splits > 1 ? partial : out;
   // Operands of both sweeps and the device-side choice between them.
-  hipError_t e = launch_mf_prepare(x, y, b, false, cols, mf, M, N, D, C, c2, s);
+  hipError_t e = launch_mf_prepare(x, y, b, false, cols, mf, M, N, D, C, c2, s, true);
   if (e != hipSuccess) return e;
   const int* gate = mf_decision(mf);
   auto run = [&]() -> hipError_t {
@@ -139,8 +139,12 @@ hipError_t launch_gauss_sum_lowd(const float* x, const float* y, double* cols, c
   sweep_event(s, true);
   e = launch_mf_sum(rscale, dst, mf, M, N, D, C, p, s);
   sweep_event(s, false);
-  if (e != hipSuccess || p.splits == 1) return e;
-  return lowd::launch_combine_sum(partial, out, M * C, p.splits, rscale, C, s);
+  if (e != hipSuccess) return e;
+  if (p.splits > 1) {
+    e = lowd::launch_combine_sum(partial, out, M * C, p.splits, rscale, C, s);
+    if (e != hipSuccess) return e;
+  }
+  return launch_mf_aside(x, y, b, rscale, out, mf, M, N, D, C, c2, s);
 }
 
 }  // namespace keops

@@ -109,6 +109,52 @@ def test_gauss_sum_exponent_regimes(D, sigma, lo, hi, outlier):
     assert_normalised(got, want, norm, TOL_F32, "gauss_sum regime")
 
 
+# Points set aside: when the points' bounding box is too wide for the matrix cores but a box of
+# the largest admissible half-width around their mean holds all but at most 256 rows and 256
+# columns, those are summed separately (set-aside columns added to every row in index order,
+# set-aside rows over all columns) and the rest stays on the matrix cores. More than 256 on
+# either side sends the call to the float64 sweep. Every case must match the oracle.
+SET_ASIDE_CASES = [
+    # (name, D, C, sigma, rows set aside, columns set aside, scaled)
+    ("one far column", 3, 1, 0.05, [], [17], False),
+    ("one far row", 3, 1, 0.05, [5], [], False),
+    ("far row next to far column", 3, 2, 0.05, [17], [17], False),
+    ("scattered rows and columns", 3, 3, 0.02, [0, 3, 99, 698, 699], [1, 2, 700, 3000], False),
+    ("scaled, D = 5", 5, 2, 0.1, [9, 10], [11, 2999], True),
+    ("256 rows and 256 columns", 3, 1, 0.05, list(range(0, 700, 3))[:256], list(range(1, 3001, 11))[:256], False),
+    ("more than 256 columns", 3, 1, 0.05, [], list(range(0, 3001, 9))[:300], False),
+    ("D = 1", 1, 1, 0.004, [1], [2], False),
+]
+
+
+@pytest.mark.parametrize("name,D,C,sigma,rows,cols,scaled", SET_ASIDE_CASES, ids=[c[0] for c in SET_ASIDE_CASES])
+def test_gauss_sum_set_aside_points(name, D, C, sigma, rows, cols, scaled):
+    import pairwise_reductions_amd as pr
+    _announce("gauss_sum_set_aside", case=name, D=D, C=C, sigma=sigma)
+    M, N = 700, 3001
+    x, y, b = _rand(len(rows) * 7 + len(cols) + D, M, N, D, C)
+    rng = np.random.default_rng(D + len(cols))
+    y[:M] = x + (0.5 * sigma * rng.standard_normal((M, D))).astype(np.float32)
+    far = (1000.0 + 3.0 * np.arange(max(len(rows), len(cols)))).astype(np.float32)
+    for k, i in enumerate(rows):
+        x[i] = far[k] + 0.25 * sigma * k / max(len(rows), 1)
+    for k, j in enumerate(cols):
+        y[j] = far[k]
+    sig = float(np.float32(sigma))
+    if scaled:
+        r = rng.uniform(0.5, 2.0, M).astype(np.float32)
+        c = rng.uniform(-1.0, 1.0, N).astype(np.float32)
+        got = _host(pr.gauss_sum_scaled(_dev(x), _dev(y), _dev(b), sig, row_scale=_dev(r), col_scale=_dev(c)))
+        want, norm = oracle.gauss_sum_scaled(x, y, b, sig, row_scale=r, col_scale=c, workers=8)
+    else:
+        got = _host(pr.gauss_sum(_dev(x), _dev(y), _dev(b), sig))
+        want, norm = oracle.gauss_sum(x, y, b, sig, workers=8)
+    assert_normalised(got, want, norm, TOL_F32, f"set aside: {name}")
+    if not scaled:
+        again = _host(pr.gauss_sum(_dev(x), _dev(y), _dev(b), sig))
+        assert np.array_equal(got, again), "set-aside results must be reproducible"
+
+
 @pytest.mark.parametrize("D,sigma,lo,hi,outlier", EXPONENT_REGIMES)
 def test_lse_exponent_regimes(D, sigma, lo, hi, outlier):
     import pairwise_reductions_amd as pr

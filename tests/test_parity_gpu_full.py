@@ -137,3 +137,20 @@ def test_gauss_sum_workload_1m_16k_rows(part):
     _announce("gauss_sum_1m rows", part=part, count=sel.size)
     want, norm = oracle.gauss_sum(inp["x"][sel], inp["y"], inp["b"], float(inp["sigma"]), workers=WORKERS)
     assert_normalised(got[sel], want, norm, TOL_F32, "gauss_sum_1m")
+
+
+def test_gauss_sum_workload_1m_with_outliers():
+    """The 1M x 1M workload with one far row and one far column (a point near (1000, 1000,
+    1000) on each side): they are set aside and the rest stays on the matrix cores. Checked on
+    1,024 seeded rows, the first and last 64 and the far row, against all columns."""
+    import pairwise_reductions_amd as pr
+    inp = workloads.make_inputs("gauss_sum_1m")
+    x, y = inp["x"].copy(), inp["y"].copy()
+    x[123_457] = 1000.0
+    y[876_543] = np.float32(1000.001)
+    _announce("gauss_sum_1m_outliers", M=inp["M"], N=inp["N"])
+    sig = float(inp["sigma"])
+    got = _host(pr.gauss_sum(_dev(x), _dev(y), _dev(inp["b"]), sig))
+    rows = np.union1d(workloads.sample_rows(inp["M"], 1024, seed=7), [123_457])
+    want, norm = oracle.gauss_sum(x[rows], y, inp["b"], sig, workers=WORKERS)
+    assert_normalised(got[rows], want, norm, TOL_F32, "gauss_sum_1m with outliers")
