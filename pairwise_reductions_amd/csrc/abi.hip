@@ -99,6 +99,7 @@ struct LowdLayout {
   keops::Plan plan;
   size_t cols_off, cols_bytes;  // column table
   size_t aux_off;               // one double: the largest column norm (argKmin screening)
+  size_t scr_off;               // argKmin: the float32 screening table
   size_t part_off, part_bytes;  // per-split partials (argKmin lists for ops 2 and 6)
   size_t lse_off;               // per-split (m, l) pairs of the fused argKmin + LSE (op 6)
   size_t mf_off;                // Gauss sum, LSE, one-channel gradient: the matrix-core operands
@@ -115,7 +116,9 @@ LowdLayout lowd_layout(int op, int64_t M, int64_t N, int D, int C, int K) {
   L.cols_bytes = needs_cols ? keops::align_up((size_t)N * keops::col_stride(D) * sizeof(double)) : 0;
   L.aux_off = L.cols_bytes;
   const size_t aux_bytes = knn ? keops::kAlign : 0;
-  L.part_off = L.aux_off + aux_bytes;
+  L.scr_off = L.aux_off + aux_bytes;
+  const size_t scr_bytes = knn ? keops::align_up(keops::knn_screen_bytes(N, D)) : 0;
+  L.part_off = L.scr_off + scr_bytes;
   size_t lse_bytes = 0;
   if (S > 1) {
     if (knn) {
@@ -809,7 +812,8 @@ int argkmin_impl(const float* x, const float* y, const float* w, int32_t* idx, f
     mf_lse.partial = lws + LL.part_off;
     mf_lse.plan = &LL.plan;
   }
-  KEOPS_HIP(keops::launch_knn_lowd(x, y, w, cols, ymax, idx, dist, ws + L.part_off, lse, lse_part, M, N, D, K, c2,
+  float* scr = reinterpret_cast<float*>(ws + L.scr_off);
+  KEOPS_HIP(keops::launch_knn_lowd(x, y, w, cols, scr, ymax, idx, dist, ws + L.part_off, lse, lse_part, M, N, D, K, c2,
                                    with_lse, L.plan, stream, mf_lse.region ? &mf_lse : nullptr),
             "argkmin_lowd");
   return ok();

@@ -96,7 +96,9 @@ struct KnnLse {
 // screening bound in *ymax, then screens every pair. With mf_lse the log-sum-exp runs on the
 // matrix cores beside the plain argKmin sweep whenever the device-side decision admits the
 // inputs, and in the fused float64 sweep otherwise.
-hipError_t launch_knn_lowd(const float* x, const float* y, const float* w, double* cols, double* ymax,
+// Bytes of the float32 screening table of the plain argKmin sweep (N records).
+size_t knn_screen_bytes(int64_t N, int D);
+hipError_t launch_knn_lowd(const float* x, const float* y, const float* w, double* cols, float* scr, double* ymax,
                            int32_t* idx, float* dist, void* partial, float* lse_out,
                            double* lse_partial, int64_t M, int64_t N, int D, int K, double c2,
                            bool with_lse, const Plan& p, hipStream_t s, const KnnLse* mf_lse = nullptr);

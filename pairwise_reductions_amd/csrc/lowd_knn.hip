@@ -48,24 +48,29 @@ __device__ __forceinline__ double sq_dist_key(const double (&xu)[D], const doubl
 // maximum on the bit patterns (non-negative doubles order like their bits), so the result is
 // the exact maximum in any order; *out is cleared by zero_kernel first. With weights the
 // table's screening term becomes |y_j|^2 - w_j (each entry is rewritten by the one thread that
-// reads it).
+// reads it). The same pass writes the float32 screening table scr[j] = (y_j, |y_j|^2 - w_j
+// rounded to float32, zeros) with records of S32 floats.
 __global__ void zero_kernel(double* __restrict__ out) { *out = 0.0; }
 
 __global__ void __launch_bounds__(256)
 max_norm_kernel(double* __restrict__ cols, const float* __restrict__ w, int64_t N, int P, int D,
-                double* __restrict__ out) {
+                float* __restrict__ scr, int S32, double* __restrict__ out) {
   __shared__ double red[256];
   double m = 0.0;
   const int64_t step = (int64_t)gridDim.x * 256;
   for (int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x; j < N; j += step) {
-    const double yy = cols[j * P + D];
+    double yy = cols[j * P + D];
     if (w) {
       const double wj = (double)w[j];
       m = fmax(m, yy + fabs(wj));
-      cols[j * P + D] = yy - wj;
+      yy -= wj;
+      cols[j * P + D] = yy;
     } else {
       m = fmax(m, yy);
     }
+    for (int d = 0; d < D; ++d) scr[j * S32 + d] = (float)cols[j * P + d];
+    scr[j * S32 + D] = (float)yy;
+    for (int d = D + 1; d < S32; ++d) scr[j * S32 + d] = 0.0f;
   }
   red[threadIdx.x] = m;
   __syncthreads();
@@ -85,6 +90,29 @@ max_norm_kernel(double* __restrict__ cols, const float* __restrict__ w, int64_t 
 // added margin by 3 u B: (3D + 6) u B in all, below 2^-46 B for D <= 8 (w = 0 without
 // weights).
 constexpr double kScreenMargin = 1.4210854715202004e-14;  // 2^-46
+
+// The plain sweep (no log-sum-exp) screens in float32 instead: a32 = fl(t_j + sum_d (-2 x_d) y_d)
+// with t_j = |y_j|^2 - w_j rounded to float32 (|t_j| <= max_j(|y_j|^2 + |w_j|)) and one rounding
+// per FMA (-2 x_d and y_d are exact float32 values). Every partial sum is at most
+// |t_j| + 2 sum_d |x_d y_d| <= 2B with B = |x|^2 + max_j(|y_j|^2 + |w_j|), so a32 differs from
+// the exact d^2 - w - |x|^2 by at most (2D + 1) 2^-24 B; the float64 threshold (key_K - |x|^2)
+// is rounded up to float32, and 2^-19 B covers both for D <= 8. The float32 FMA issues about
+// 1.6 times as fast as the float64 one on this chip, and a tile's column records take half the
+// scalar registers, so the next tile's records are loaded while the current one is screened.
+constexpr double kScreenMargin32 = 0x1p-19;
+// Floats per record of the float32 screening table: D coordinates and the column term, rounded
+// up to a multiple of 4 (16-byte records for the scalar loads).
+__host__ __device__ constexpr int screen_stride(int D) { return (D + 1 + 3) & ~3; }
+
+// The smallest float32 value >= v (v finite or +inf): the rounded value, moved one step up
+// (one unit in its bit pattern) when rounding went down.
+__device__ __forceinline__ float round_up_f32(double v) {
+  const float f = (float)v;
+  if (!((double)f < v)) return f;
+  if (f == 0.0f) return __int_as_float(1);
+  const int b = __float_as_int(f);
+  return __int_as_float(f > 0.0f ? b + 1 : b - 1);
+}
 
 // argKmin of d^2_ij - w_j (w_j = 0 when w is null; with LSE, also the log-sum-exp of -c2 d^2 in
 // base 2, never combined with weights) over the columns of one split.
@@ -115,10 +143,11 @@ __device__ __forceinline__ int64_t uniform(int64_t v) {
 
 template <int D, int K, int R, bool LSE>
 __global__ void __launch_bounds__(kBlock)
-knn_kernel(const float* __restrict__ x, const double* __restrict__ cols, const float* __restrict__ w,
-           const double* __restrict__ ymax, int32_t* __restrict__ idx, float* __restrict__ dist, KeyIdx* __restrict__ partial,
-           float* __restrict__ lse_out, LsePartial* __restrict__ lse_partial, int64_t M, int64_t N,
-           int64_t cps, int Kout, double c2, const int* __restrict__ mf, int run_if_mf) {
+knn_kernel(const float* __restrict__ x, const double* __restrict__ cols, const float* __restrict__ scr,
+           const float* __restrict__ w, const double* __restrict__ ymax, int32_t* __restrict__ idx,
+           float* __restrict__ dist, KeyIdx* __restrict__ partial, float* __restrict__ lse_out,
+           LsePartial* __restrict__ lse_partial, int64_t M, int64_t N, int64_t cps, int Kout, double c2,
+           const int* __restrict__ mf, int run_if_mf) {
   if (mf && mf_admits(mf) != run_if_mf) return;  // the other form takes these inputs
   constexpr int P = (D + 2) & ~1;
   constexpr int U = D <= 4 ? 4 : 2;  // columns per screened tile
@@ -130,7 +159,9 @@ knn_kernel(const float* __restrict__ x, const double* __restrict__ cols, const f
   const int64_t row0 = (int64_t)blockIdx.x * (kBlock * R) + threadIdx.x;
   const double bmax = *ymax;
 
+  constexpr int S32 = screen_stride(D);
   double xd[R][D], xp[R][D], A[R], marg[R], thr[R], off[R];
+  float xs[R][D], thr32[R];  // the float32 screen (plain sweep): -2 x and the rounded-up threshold
   double keys[R][K];
   int32_t ids[R][K];
   int cnt[R];
@@ -146,11 +177,13 @@ knn_kernel(const float* __restrict__ x, const double* __restrict__ cols, const f
     for (int d = 0; d < D; ++d) {
       xd[r][d] = (double)x[i * D + d];
       xp[r][d] = -2.0 * xd[r][d];
+      xs[r][d] = -2.0f * x[i * D + d];
       s = fma(xd[r][d], xd[r][d], s);
     }
     A[r] = s;
-    marg[r] = kScreenMargin * (s + bmax);
+    marg[r] = (LSE ? kScreenMargin : kScreenMargin32) * (s + bmax);
     thr[r] = INFINITY;
+    thr32[r] = INFINITY;
 #pragma unroll
     for (int k = 0; k < K; ++k) {
       keys[r][k] = INFINITY;
@@ -172,7 +205,36 @@ knn_kernel(const float* __restrict__ x, const double* __restrict__ cols, const f
       if (key < keys[r][K - 1]) topk_insert<K>(keys[r], ids[r], key, jj);
     }
     thr[r] = (keys[r][K - 1] - A[r]) + marg[r];
+    thr32[r] = round_up_f32(thr[r]);
     cnt[r] = 0;
+  };
+
+  // The float32 screen of columns [j, j + n), n <= U, for row r (plain sweep): D FMAs per pair
+  // and one compare per tile (of the smallest of its U values) decide whether any lane has a
+  // candidate; only then are the columns queued.
+  auto tile32 = [&](int r, int64_t j, int n, const float (&yv)[U][D], const float (&tv)[U]) {
+    if (full[r]) {
+      flush(r);
+      full[r] = false;
+    }
+    float a[U];
+    float mn = INFINITY;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float t = tv[u];
+#pragma unroll
+      for (int d = 0; d < D; ++d) t = fmaf(xs[r][d], yv[u][d], t);
+      a[u] = t;
+      if (u < n) mn = fminf(mn, t);
+    }
+    if (K > 16 || __builtin_expect(__any(mn < thr32[r]), 0)) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        queue[r][cnt[r]][threadIdx.x] = (int32_t)(j + u);
+        cnt[r] += (u < n && a[u] < thr32[r]) ? 1 : 0;
+      }
+      full[r] = __any(cnt[r] > kQueue - U);
+    }
   };
 
   // Columns [j, j + n) of a tile, n <= U, for row r: screen, queue, add LSE terms.
@@ -223,12 +285,59 @@ knn_kernel(const float* __restrict__ x, const double* __restrict__ cols, const f
     }
   };
 
+  const int64_t nfull = (j1 - j0) / U;  // whole tiles of the split
+  if constexpr (!LSE) {
+    // float32 records through the scalar unit, the next tile's loaded while the current one is
+    // screened (two alternating sets)
+    ConstPtr<float> cscr = (ConstPtr<float>)scr;
+    struct Recs {
+      float y[U][D], t[U];
+    };
+    auto load = [&](int64_t jt, Recs& o) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) o.y[u][d] = cscr[(jt + u) * S32 + d];
+        o.t[u] = cscr[(jt + u) * S32 + D];
+      }
+    };
+    Recs ra, rb;
+    if (nfull > 0) load(uniform(j0), ra);
+    int64_t t = 0;
+    for (; t + 2 <= nfull; t += 2) {
+      const int64_t ja = uniform(j0 + t * U);
+      load(ja + U, rb);
+#pragma unroll
+      for (int r = 0; r < R; ++r) tile32(r, ja, U, ra.y, ra.t);
+      if (t + 2 < nfull) load(ja + 2 * U, ra);
+#pragma unroll
+      for (int r = 0; r < R; ++r) tile32(r, ja + U, U, rb.y, rb.t);
+    }
+    if (t < nfull) {  // an odd last whole tile, already in ra
+      const int64_t ja = uniform(j0 + t * U);
+#pragma unroll
+      for (int r = 0; r < R; ++r) tile32(r, ja, U, ra.y, ra.t);
+    }
+    const int64_t jr = j0 + nfull * U;
+    if (jr < j1) {
+      const int n = (int)(j1 - jr);
+      Recs rt;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t jj = (u < n) ? jr + u : jr;
+#pragma unroll
+        for (int d = 0; d < D; ++d) rt.y[u][d] = scr[jj * S32 + d];
+        rt.t[u] = scr[jj * S32 + D];
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r) tile32(r, jr, n, rt.y, rt.t);
+    }
+  }
   // The column records are the same for every lane: with two rows per lane they are read
   // through the scalar unit (at K > 16 the scalar registers they would take are short).
   ConstPtr<double> ccols = (ConstPtr<double>)cols;
   auto col = [&](int64_t e) { return R == 2 ? ccols[e] : cols[e]; };
-  const int64_t nfull = (j1 - j0) / U;  // whole tiles of the split
-  for (int64_t t = 0; t < nfull; ++t) {
+  for (int64_t t = 0; LSE && t < nfull; ++t) {
     const int64_t ja = uniform(j0 + t * U);
     double yv[U][D], bv[U];
 #pragma unroll
@@ -241,7 +350,7 @@ knn_kernel(const float* __restrict__ x, const double* __restrict__ cols, const f
     for (int r = 0; r < R; ++r) tile(r, ja, U, yv, bv);
   }
   const int64_t j = j0 + nfull * U;
-  if (j < j1) {
+  if (LSE && j < j1) {
     const int n = (int)(j1 - j);
     double yv[U][D], bv[U];
 #pragma unroll
@@ -327,7 +436,8 @@ merge_topk_kernel(const KeyIdx* __restrict__ partial, int32_t* __restrict__ idx,
 // log-sum-exp) the fused sweep runs only when that decision declines and the plain one only
 // when it admits; the caller runs the matrix-core log-sum-exp itself.
 template <int D, int K>
-hipError_t knn_dk(const float* x, const double* cols, const float* w, const double* ymax, int32_t* idx, float* dist,
+hipError_t knn_dk(const float* x, const double* cols, const float* scr, const float* w, const double* ymax, int32_t* idx,
+                  float* dist,
                   void* partial, float* lse_out, double* lse_partial, int64_t M, int64_t N, int Kout, double c2,
                   bool with_lse, const int* mf, const Plan& p, hipStream_t s) {
   constexpr int R = K <= 16 ? 2 : 1;
@@ -335,10 +445,10 @@ hipError_t knn_dk(const float* x, const double* cols, const float* w, const doub
   KeyIdx* part = reinterpret_cast<KeyIdx*>(partial);
   LsePartial* lpart = reinterpret_cast<LsePartial*>(lse_partial);
   if (with_lse)
-    knn_kernel<D, K, R, true><<<grid, kBlock, 0, s>>>(x, cols, w, ymax, idx, dist, part, lse_out, lpart, M, N,
+    knn_kernel<D, K, R, true><<<grid, kBlock, 0, s>>>(x, cols, scr, w, ymax, idx, dist, part, lse_out, lpart, M, N,
                                                        p.cols_per_split, Kout, c2, mf, 0);
   if (!with_lse || mf)
-    knn_kernel<D, K, R, false><<<grid, kBlock, 0, s>>>(x, cols, w, ymax, idx, dist, part, lse_out, lpart, M, N,
+    knn_kernel<D, K, R, false><<<grid, kBlock, 0, s>>>(x, cols, scr, w, ymax, idx, dist, part, lse_out, lpart, M, N,
                                                         p.cols_per_split, Kout, c2, mf, 1);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
@@ -349,10 +459,11 @@ hipError_t knn_dk(const float* x, const double* cols, const float* w, const doub
 }
 
 template <int D>
-hipError_t knn_d(int Kb, const float* x, const double* cols, const float* w, const double* ymax, int32_t* idx, float* dist,
+hipError_t knn_d(int Kb, const float* x, const double* cols, const float* scr, const float* w, const double* ymax,
+                 int32_t* idx, float* dist,
                  void* partial, float* lse_out, double* lse_partial, int64_t M, int64_t N, int Kout, double c2,
                  bool with_lse, const int* mf, const Plan& p, hipStream_t s) {
-#define KEOPS_KNN_K(Kv) return knn_dk<D, Kv>(x, cols, w, ymax, idx, dist, partial, lse_out, lse_partial, M, N, Kout, c2, with_lse, mf, p, s)
+#define KEOPS_KNN_K(Kv) return knn_dk<D, Kv>(x, cols, scr, w, ymax, idx, dist, partial, lse_out, lse_partial, M, N, Kout, c2, with_lse, mf, p, s)
   switch (Kb) {
     case 1: KEOPS_KNN_K(1);
     case 2: KEOPS_KNN_K(2);
@@ -432,7 +543,9 @@ int knn_occupancy(int D, int K) {
   return n;
 }
 
-hipError_t launch_knn_lowd(const float* x, const float* y, const float* w, double* cols, double* ymax,
+size_t knn_screen_bytes(int64_t N, int D) { return (size_t)N * lowd::screen_stride(D) * sizeof(float); }
+
+hipError_t launch_knn_lowd(const float* x, const float* y, const float* w, double* cols, float* scr, double* ymax,
                            int32_t* idx, float* dist, void* partial, float* lse_out, double* lse_partial, int64_t M,
                            int64_t N, int D, int K, double c2, bool with_lse, const Plan& p, hipStream_t s,
                            const KnnLse* mf_lse) {
@@ -442,7 +555,8 @@ hipError_t launch_knn_lowd(const float* x, const float* y, const float* w, doubl
   if (e != hipSuccess) return e;
   lowd::zero_kernel<<<1, 1, 0, s>>>(ymax);
   const int64_t nb = lowd::ceil_div(N, 256);
-  lowd::max_norm_kernel<<<(unsigned)(nb < 512 ? nb : 512), 256, 0, s>>>(cols, w, N, col_stride(D), D, ymax);
+  lowd::max_norm_kernel<<<(unsigned)(nb < 512 ? nb : 512), 256, 0, s>>>(cols, w, N, col_stride(D), D, scr,
+                                                                         lowd::screen_stride(D), ymax);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int Kb = lowd::argk_bucket(K);
@@ -455,7 +569,7 @@ hipError_t launch_knn_lowd(const float* x, const float* y, const float* w, doubl
     if (e != hipSuccess) return e;
     mf = mf_decision(mf_lse->region);
   }
-#define KEOPS_KNN(Dv) lowd::knn_d<Dv>(Kb, x, cols, w, ymax, idx, dist, partial, lse_out, lse_partial, M, N, K, c2, with_lse, mf, p, s)
+#define KEOPS_KNN(Dv) lowd::knn_d<Dv>(Kb, x, cols, scr, w, ymax, idx, dist, partial, lse_out, lse_partial, M, N, K, c2, with_lse, mf, p, s)
   auto run = [&]() -> hipError_t { KEOPS_SWITCH_D(D, KEOPS_KNN) };
 #undef KEOPS_KNN
   e = run();
