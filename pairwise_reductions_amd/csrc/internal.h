@@ -62,15 +62,17 @@ int mf_rows_per_lane(int op, int D, int C);   // op: 0 sum, 1 log-sum-exp, 3 gra
 int mf_occupancy(int op, int D, int C, int rt);  // resident workgroups per CU of that sweep
 int knn_occupancy(int D, int K);                 // resident workgroups per CU of the argKmin sweep
 // set_aside (the Gauss sum only): a box too wide for the matrix cores may be replaced by one
-// around the mean that sets a few outlying points aside (launch_mf_aside then sums their terms).
+// around the sample median that sets a few outlying points aside (launch_mf_finish then sums
+// their terms).
 hipError_t launch_mf_prepare(const float* x, const float* y, const float* b, bool with_y, double* cols,
                              void* region, int64_t M, int64_t N, int D, int C, double c2, hipStream_t s,
                              bool set_aside = false);
-// After the matrix-core Gauss sum (and its split combine): adds the set-aside columns' terms to
-// every row and sums every set-aside row over all columns; both return at once unless the
-// preparation set points aside.
-hipError_t launch_mf_aside(const float* x, const float* y, const float* b, const float* rscale, float* out,
-                           void* region, int64_t M, int64_t N, int D, int C, double c2, hipStream_t s);
+// The Gauss sum's last step after either sweep: combines the S column splits of partial into out
+// (S > 1) with rscale, and when the preparation set points aside adds the set-aside columns'
+// terms to every other row and sums every set-aside row over all columns.
+hipError_t launch_mf_finish(const float* partial, float* out, const float* x, const float* y, const float* b,
+                            const float* rscale, void* region, int64_t M, int64_t N, int D, int C, int64_t S,
+                            double c2, hipStream_t s);
 // gradient with respect to x, one channel: dst[i][d] = -(g_i / sigma^2) sum_j k_ij b_j (x_i - y_j)
 hipError_t launch_mf_grad(const float* x, const float* g, float* dst, float inv_sigma2, void* region,
                           int64_t M, int64_t N, int D, const Plan& p, hipStream_t s);

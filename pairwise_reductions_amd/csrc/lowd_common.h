@@ -24,7 +24,11 @@ constexpr int kRowsSumSmall = 1;       // small M: more, smaller row blocks to f
 constexpr int kRowsLse = 4;
 constexpr int kRowsGrad = 2;
 constexpr int kLseTile = 8;            // columns per log-sum-exp tile
-constexpr int64_t kSplitCols = 65536;  // largest column range of one split (fits one XCD's L2)
+// Largest column range of one split. A split's matrix-core column pieces (84 bytes a column)
+// then take at most 2.75 MB of an XCD's 4 MB L2 while that XCD's resident workgroups stream
+// them; at 65536 columns (5.5 MB) they did not fit, and the 1M x 1M sum fetched 9.0 GB from
+// HBM per launch instead of 3.3 GB, in the same time.
+constexpr int64_t kSplitCols = 32768;
 // Fewest workgroups per CU a sweep launch aims for, by operation (0 sum, 1 log-sum-exp,
 // 2 / 6 argKmin, 3 gradient) and channel count. The sweeps run in rounds of one workgroup per
 // resident slot; with only a round or two the launch ends with the slowest CU, so more and

@@ -929,24 +929,9 @@ grad_mf_kernel(const half8* __restrict__ rhi, const half8* __restrict__ rlo, con
     }
 }
 
-// Terms of the set-aside columns: out[i][c] += rscale[i] sum_j 2^{-c2 |x_i - y_j|^2} b[j][c] over
-// the set-aside columns j in increasing order, for every row (the set-aside rows' own results
-// are overwritten by aside_rows_kernel afterwards). The exponent is the float64 squared
-// distance of the float32 inputs, times c2, rounded to float32 before the exponential; the
-// terms are added in float64, then to the row's float32 result. Each workgroup sorts the
-// (at most kMaxAside) recorded indices itself, so the order does not depend on the order in
-// which the preparation recorded them.
-template <int D, int C>
-__global__ void __launch_bounds__(kBlock)
-aside_cols_kernel(const float* __restrict__ x, const float* __restrict__ y, const float* __restrict__ b,
-                  const float* __restrict__ rscale, float* __restrict__ out, const int32_t* __restrict__ aside_cols,
-                  const MfParams* __restrict__ P, int64_t M, double c2) {
-  if (!P->gate || P->bad || !P->robust || P->nbc == 0) return;
-  const int n = P->nbc < kMaxAside ? P->nbc : kMaxAside;
-  __shared__ int32_t list[kMaxAside];
-  for (int t = threadIdx.x; t < kMaxAside; t += kBlock) list[t] = t < n ? aside_cols[t] : 0x7fffffff;
-  __syncthreads();
-  // bitonic sort of kMaxAside entries, ascending
+// Sorts kMaxAside indices in LDS ascending (bitonic network; every thread of the workgroup
+// takes part).
+__device__ void sort_aside(int32_t* list) {
   for (int k = 2; k <= kMaxAside; k <<= 1)
     for (int jstep = k >> 1; jstep > 0; jstep >>= 1) {
       for (int t = threadIdx.x; t < kMaxAside; t += kBlock) {
@@ -962,71 +947,122 @@ aside_cols_kernel(const float* __restrict__ x, const float* __restrict__ y, cons
       }
       __syncthreads();
     }
-  const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-  if (i >= M) return;
-  double xi[D], acc[C];
-#pragma unroll
-  for (int d = 0; d < D; ++d) xi[d] = (double)x[i * D + d];
-#pragma unroll
-  for (int c = 0; c < C; ++c) acc[c] = 0.0;
-  for (int e = 0; e < n; ++e) {
-    const int64_t j = list[e];
-    double d2 = 0.0;
-#pragma unroll
-    for (int d = 0; d < D; ++d) {
-      const double t = xi[d] - (double)y[j * D + d];
-      d2 = fma(t, t, d2);
-    }
-    const double k = (double)exp2_hw((float)(-c2 * d2));
-#pragma unroll
-    for (int c = 0; c < C; ++c) acc[c] = fma(k, (double)b[j * C + c], acc[c]);
-  }
-  const double sc = rscale ? (double)rscale[i] : 1.0;
-#pragma unroll
-  for (int c = 0; c < C; ++c) out[i * C + c] += (float)(sc * acc[c]);
 }
 
-// The set-aside rows, one workgroup each: out[i][c] = rscale[i] sum_j 2^{-c2 |x_i - y_j|^2} b[j][c]
-// over all columns, exponents as in aside_cols_kernel, each thread summing a fixed stride of
-// columns in float64 and the workgroup adding the threads' sums in a fixed tree order.
+// 2^{-c2 |x_i - y_j|^2} from the float64 squared distance of the float32 inputs, rounded to
+// float32 before the exponential.
+template <int D>
+__device__ __forceinline__ double aside_term(const double (&xi)[D], const float* __restrict__ yj, double c2) {
+  double d2 = 0.0;
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    const double t = xi[d] - (double)yj[d];
+    d2 = fma(t, t, d2);
+  }
+  return (double)exp2_hw((float)(-c2 * d2));
+}
+
+// The Gauss sum's last step, after either sweep: the first row_wgs workgroups combine the S
+// column splits of their rows in increasing order (S > 1, from partial [S][M][C]; with S = 1 the
+// sweep has written out itself) and apply rscale; the kMaxAside workgroups after them handle the
+// set-aside rows. When the preparation set points aside (matrix-core path only):
+//   - every row that is not set aside gets rscale[i] sum_j 2^{-c2 |x_i - y_j|^2} b[j][c] over the
+//     set-aside columns j in increasing order added (terms in float64, then to the float32 sum;
+//     each workgroup sorts the recorded indices itself, so the order does not depend on the
+//     order in which they were recorded);
+//   - each set-aside row is summed by one workgroup over all columns (each thread a fixed
+//     stride of columns in float64, then a fixed tree) and written as rscale[i] times that.
 template <int D, int C>
 __global__ void __launch_bounds__(kBlock)
-aside_rows_kernel(const float* __restrict__ x, const float* __restrict__ y, const float* __restrict__ b,
-                  const float* __restrict__ rscale, float* __restrict__ out, const int32_t* __restrict__ aside_rows,
-                  const MfParams* __restrict__ P, int64_t N, double c2) {
-  if (!P->gate || P->bad || !P->robust) return;
-  const int n = P->nbr < kMaxAside ? P->nbr : kMaxAside;
-  if ((int)blockIdx.x >= n) return;
-  const int64_t i = aside_rows[blockIdx.x];
+finish_sum_kernel(const float* __restrict__ partial, float* __restrict__ out, const float* __restrict__ x,
+                  const float* __restrict__ y, const float* __restrict__ b, const float* __restrict__ rscale,
+                  const int32_t* __restrict__ aside, const MfParams* __restrict__ P, int64_t M, int64_t N,
+                  int64_t S, int64_t row_wgs, double c2) {
+  __shared__ int32_t rows_l[kMaxAside];
+  __shared__ int32_t cols_l[kMaxAside];
   __shared__ double red[C][kBlock];
-  double xi[D], acc[C];
+  const bool robust = P->gate && !P->bad && P->robust;
+  const int nr = robust ? (P->nbr < kMaxAside ? P->nbr : kMaxAside) : 0;
+  const int nc = robust ? (P->nbc < kMaxAside ? P->nbc : kMaxAside) : 0;
+  if ((int64_t)blockIdx.x >= row_wgs) {  // a set-aside row
+    const int w = (int)((int64_t)blockIdx.x - row_wgs);
+    if (w >= nr) return;
+    const int64_t i = aside[w];
+    double xi[D], acc[C];
 #pragma unroll
-  for (int d = 0; d < D; ++d) xi[d] = (double)x[i * D + d];
+    for (int d = 0; d < D; ++d) xi[d] = (double)x[i * D + d];
 #pragma unroll
-  for (int c = 0; c < C; ++c) acc[c] = 0.0;
-  for (int64_t j = threadIdx.x; j < N; j += kBlock) {
-    double d2 = 0.0;
+    for (int c = 0; c < C; ++c) acc[c] = 0.0;
+    for (int64_t j = threadIdx.x; j < N; j += kBlock) {
+      const double k = aside_term<D>(xi, y + j * D, c2);
 #pragma unroll
-    for (int d = 0; d < D; ++d) {
-      const double t = xi[d] - (double)y[j * D + d];
-      d2 = fma(t, t, d2);
+      for (int c = 0; c < C; ++c) acc[c] = fma(k, (double)b[j * C + c], acc[c]);
     }
-    const double k = (double)exp2_hw((float)(-c2 * d2));
 #pragma unroll
-    for (int c = 0; c < C; ++c) acc[c] = fma(k, (double)b[j * C + c], acc[c]);
-  }
-#pragma unroll
-  for (int c = 0; c < C; ++c) red[c][threadIdx.x] = acc[c];
-  __syncthreads();
-  for (int h = kBlock / 2; h > 0; h >>= 1) {
-    if ((int)threadIdx.x < h)
-#pragma unroll
-      for (int c = 0; c < C; ++c) red[c][threadIdx.x] += red[c][threadIdx.x + h];
+    for (int c = 0; c < C; ++c) red[c][threadIdx.x] = acc[c];
     __syncthreads();
+    for (int h = kBlock / 2; h > 0; h >>= 1) {
+      if ((int)threadIdx.x < h)
+#pragma unroll
+        for (int c = 0; c < C; ++c) red[c][threadIdx.x] += red[c][threadIdx.x + h];
+      __syncthreads();
+    }
+    if (threadIdx.x < C) {
+      const double sc = rscale ? (double)rscale[i] : 1.0;
+      out[i * C + threadIdx.x] = (float)(sc * red[threadIdx.x][0]);
+    }
+    return;
   }
-  if (threadIdx.x < C) {
-    const double sc = rscale ? (double)rscale[i] : 1.0;
-    out[i * C + threadIdx.x] = (float)(sc * red[threadIdx.x][0]);
+  if (nr > 0 || nc > 0) {
+    for (int t = threadIdx.x; t < kMaxAside; t += kBlock) {
+      rows_l[t] = t < nr ? aside[t] : 0x7fffffff;
+      cols_l[t] = t < nc ? aside[kMaxAside + t] : 0x7fffffff;
+    }
+    __syncthreads();
+    if (nr > 0) sort_aside(rows_l);
+    if (nc > 0) sort_aside(cols_l);
+  }
+  const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+  if (i >= M) return;
+  if (nr > 0) {  // a set-aside row is written by its own workgroup
+    int lo = 0, hi = nr;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (rows_l[mid] < i) lo = mid + 1;
+      else hi = mid;
+    }
+    if (lo < nr && rows_l[lo] == i) return;
+  }
+  float v[C];
+  const float sc = rscale ? rscale[i] : 1.0f;
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    if (S > 1) {
+      float t = 0.0f;
+      for (int64_t k = 0; k < S; ++k) t += partial[(k * M + i) * C + c];
+      v[c] = rscale ? t * sc : t;
+    } else {
+      v[c] = out[i * C + c];
+    }
+  }
+  if (nc > 0) {
+    double xi[D], acc[C];
+#pragma unroll
+    for (int d = 0; d < D; ++d) xi[d] = (double)x[i * D + d];
+#pragma unroll
+    for (int c = 0; c < C; ++c) acc[c] = 0.0;
+    for (int e = 0; e < nc; ++e) {
+      const int64_t j = cols_l[e];
+      const double k = aside_term<D>(xi, y + j * D, c2);
+#pragma unroll
+      for (int c = 0; c < C; ++c) acc[c] = fma(k, (double)b[j * C + c], acc[c]);
+    }
+#pragma unroll
+    for (int c = 0; c < C; ++c) v[c] += (float)((double)sc * acc[c]);
+  }
+  if (S > 1 || nc > 0) {
+#pragma unroll
+    for (int c = 0; c < C; ++c) out[i * C + c] = v[c];
   }
 }
 
@@ -1307,45 +1343,46 @@ hipError_t launch_mf_prepare(const float* x, const float* y, const float* b, boo
   return hipGetLastError();
 }
 
-hipError_t launch_mf_aside(const float* x, const float* y, const float* b, const float* rscale, float* out,
-                           void* region, int64_t M, int64_t N, int D, int C, double c2, hipStream_t s) {
+hipError_t launch_mf_finish(const float* partial, float* out, const float* x, const float* y, const float* b,
+                            const float* rscale, void* region, int64_t M, int64_t N, int D, int C, int64_t S,
+                            double c2, hipStream_t s) {
   using namespace lowd;
   char* r = static_cast<char*>(region);
   const MfLayout L = mf_layout(M, N, D, C);
   const MfParams* P = reinterpret_cast<const MfParams*>(r);
   const int32_t* aside = reinterpret_cast<const int32_t*>(r + L.aside);
+  const int64_t row_wgs = ceil_div(M, kBlock);
   auto run = [&](auto dt, auto ct) -> hipError_t {
     constexpr int Dv = decltype(dt)::value, Cv = decltype(ct)::value;
-    aside_cols_kernel<Dv, Cv><<<(unsigned)ceil_div(M, kBlock), kBlock, 0, s>>>(x, y, b, rscale, out,
-                                                                              aside + kMaxAside, P, M, c2);
-    aside_rows_kernel<Dv, Cv><<<(unsigned)kMaxAside, kBlock, 0, s>>>(x, y, b, rscale, out, aside, P, N, c2);
+    finish_sum_kernel<Dv, Cv><<<(unsigned)(row_wgs + kMaxAside), kBlock, 0, s>>>(partial, out, x, y, b, rscale, aside,
+                                                                               P, M, N, S, row_wgs, c2);
     return hipGetLastError();
   };
-#define KEOPS_ASIDE_C(Dv, Cv) return run(std::integral_constant<int, Dv>{}, std::integral_constant<int, Cv>{})
-#define KEOPS_ASIDE_D(Dv)                  \
-  switch (C) {                             \
-    case 1: KEOPS_ASIDE_C(Dv, 1);          \
-    case 2: KEOPS_ASIDE_C(Dv, 2);          \
-    case 3: KEOPS_ASIDE_C(Dv, 3);          \
-    case 4: KEOPS_ASIDE_C(Dv, 4);          \
-    case 5: KEOPS_ASIDE_C(Dv, 5);          \
-    case 6: KEOPS_ASIDE_C(Dv, 6);          \
-    case 7: KEOPS_ASIDE_C(Dv, 7);          \
-    case 8: KEOPS_ASIDE_C(Dv, 8);          \
-  }                                        \
+#define KEOPS_FIN_C(Dv, Cv) return run(std::integral_constant<int, Dv>{}, std::integral_constant<int, Cv>{})
+#define KEOPS_FIN_D(Dv)                  \
+  switch (C) {                           \
+    case 1: KEOPS_FIN_C(Dv, 1);          \
+    case 2: KEOPS_FIN_C(Dv, 2);          \
+    case 3: KEOPS_FIN_C(Dv, 3);          \
+    case 4: KEOPS_FIN_C(Dv, 4);          \
+    case 5: KEOPS_FIN_C(Dv, 5);          \
+    case 6: KEOPS_FIN_C(Dv, 6);          \
+    case 7: KEOPS_FIN_C(Dv, 7);          \
+    case 8: KEOPS_FIN_C(Dv, 8);          \
+  }                                      \
   return hipErrorInvalidValue;
   switch (D) {
-    case 1: KEOPS_ASIDE_D(1)
-    case 2: KEOPS_ASIDE_D(2)
-    case 3: KEOPS_ASIDE_D(3)
-    case 4: KEOPS_ASIDE_D(4)
-    case 5: KEOPS_ASIDE_D(5)
-    case 6: KEOPS_ASIDE_D(6)
-    case 7: KEOPS_ASIDE_D(7)
-    case 8: KEOPS_ASIDE_D(8)
+    case 1: KEOPS_FIN_D(1)
+    case 2: KEOPS_FIN_D(2)
+    case 3: KEOPS_FIN_D(3)
+    case 4: KEOPS_FIN_D(4)
+    case 5: KEOPS_FIN_D(5)
+    case 6: KEOPS_FIN_D(6)
+    case 7: KEOPS_FIN_D(7)
+    case 8: KEOPS_FIN_D(8)
   }
-#undef KEOPS_ASIDE_D
-#undef KEOPS_ASIDE_C
+#undef KEOPS_FIN_D
+#undef KEOPS_FIN_C
   return hipErrorInvalidValue;
 }
 

@@ -140,11 +140,7 @@ hipError_t launch_gauss_sum_lowd(const float* x, const float* y, double* cols, c
   e = launch_mf_sum(rscale, dst, mf, M, N, D, C, p, s);
   sweep_event(s, false);
   if (e != hipSuccess) return e;
-  if (p.splits > 1) {
-    e = lowd::launch_combine_sum(partial, out, M * C, p.splits, rscale, C, s);
-    if (e != hipSuccess) return e;
-  }
-  return launch_mf_aside(x, y, b, rscale, out, mf, M, N, D, C, c2, s);
+  return launch_mf_finish(partial, out, x, y, b, rscale, mf, M, N, D, C, p.splits, c2, s);
 }
 
 }  // namespace keops
