@@ -100,6 +100,7 @@ struct LowdLayout {
   size_t cols_off, cols_bytes;  // column table
   size_t aux_off;               // one double: the largest column norm (argKmin screening)
   size_t scr_off;               // argKmin: the float32 screening table
+  size_t order_off;             // argKmin: the rows' spatial order
   size_t part_off, part_bytes;  // per-split partials (argKmin lists for ops 2 and 6)
   size_t lse_off;               // per-split (m, l) pairs of the fused argKmin + LSE (op 6)
   size_t mf_off;                // Gauss sum, LSE, one-channel gradient: the matrix-core operands
@@ -118,7 +119,9 @@ LowdLayout lowd_layout(int op, int64_t M, int64_t N, int D, int C, int K) {
   const size_t aux_bytes = knn ? keops::kAlign : 0;
   L.scr_off = L.aux_off + aux_bytes;
   const size_t scr_bytes = knn ? keops::align_up(keops::knn_screen_bytes(N, D)) : 0;
-  L.part_off = L.scr_off + scr_bytes;
+  L.order_off = L.scr_off + scr_bytes;
+  const size_t order_bytes = knn ? keops::align_up(keops::knn_order_bytes(M)) : 0;
+  L.part_off = L.order_off + order_bytes;
   size_t lse_bytes = 0;
   if (S > 1) {
     if (knn) {
@@ -813,7 +816,7 @@ int argkmin_impl(const float* x, const float* y, const float* w, int32_t* idx, f
     mf_lse.plan = &LL.plan;
   }
   float* scr = reinterpret_cast<float*>(ws + L.scr_off);
-  KEOPS_HIP(keops::launch_knn_lowd(x, y, w, cols, scr, ymax, idx, dist, ws + L.part_off, lse, lse_part, M, N, D, K, c2,
+  KEOPS_HIP(keops::launch_knn_lowd(x, y, w, cols, scr, ws + L.order_off, ymax, idx, dist, ws + L.part_off, lse, lse_part, M, N, D, K, c2,
                                    with_lse, L.plan, stream, mf_lse.region ? &mf_lse : nullptr),
             "argkmin_lowd");
   return ok();

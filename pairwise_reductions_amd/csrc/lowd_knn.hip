@@ -141,9 +141,114 @@ __device__ __forceinline__ int64_t uniform(int64_t v) {
   return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
+// Rows in spatial order. A wave takes 128 rows; when they lie close together their candidate
+// columns are mostly the same, so far fewer tiles hold a candidate for some lane of the wave
+// than with rows in input order (each row's result does not depend on which lane computes it).
+// The order is a counting sort of the rows by the Morton code of their cell on a 2^15-cell grid
+// over the rows' bounding box (5 bits per dimension over the first three dimensions; 15 bits
+// for D = 1, 7 per dimension for D = 2); rows within one cell keep an arbitrary order.
+constexpr int kOrderBits = 15;
+constexpr int kOrderCells = 1 << kOrderBits;
+
+__device__ __forceinline__ unsigned int ord_of_f(float f) {
+  const unsigned int u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float f_of_ord(unsigned int u) {
+  return __uint_as_float((u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
+}
+
+// box[0..2] = per-dimension minima, box[3..5] maxima (order-preserving encodings; cleared to
+// 0xffffffff / 0 first), counts[0..kOrderCells) = 0.
+__global__ void __launch_bounds__(256) order_clear_kernel(unsigned int* __restrict__ box, unsigned int* __restrict__ counts) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t < kOrderCells) counts[t] = 0u;
+  if (t < 3) box[t] = 0xffffffffu;
+  else if (t < 6) box[t] = 0u;
+}
+
+__global__ void __launch_bounds__(256)
+order_box_kernel(const float* __restrict__ x, int64_t M, int D, unsigned int* __restrict__ box) {
+  const int nd = D < 3 ? D : 3;
+  unsigned int lo[3] = {0xffffffffu, 0xffffffffu, 0xffffffffu}, hi[3] = {0u, 0u, 0u};
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < M; i += (int64_t)gridDim.x * 256)
+    for (int d = 0; d < nd; ++d) {
+      const unsigned int v = ord_of_f(x[i * D + d]);
+      lo[d] = v < lo[d] ? v : lo[d];
+      hi[d] = v > hi[d] ? v : hi[d];
+    }
+  for (int d = 0; d < nd; ++d) {
+    for (int m = 32; m >= 1; m >>= 1) {
+      const unsigned int a = __shfl_xor(lo[d], m), b = __shfl_xor(hi[d], m);
+      lo[d] = a < lo[d] ? a : lo[d];
+      hi[d] = b > hi[d] ? b : hi[d];
+    }
+    if ((threadIdx.x & 63) == 0) {
+      atomicMin(box + d, lo[d]);
+      atomicMax(box + 3 + d, hi[d]);
+    }
+  }
+}
+
+__device__ __forceinline__ unsigned int order_cell(const float* __restrict__ xi, int D, const unsigned int* __restrict__ box) {
+  const int nd = D < 3 ? D : 3;
+  const int bits = kOrderBits / nd;
+  unsigned int c[3] = {0u, 0u, 0u};
+  for (int d = 0; d < nd; ++d) {
+    const float lo = f_of_ord(box[d]), hi = f_of_ord(box[3 + d]);
+    const float span = hi - lo;
+    float t = span > 0.0f ? (xi[d] - lo) / span : 0.0f;
+    int q = (int)(t * (float)(1 << bits));
+    q = q < 0 ? 0 : (q >= (1 << bits) ? (1 << bits) - 1 : q);
+    c[d] = (unsigned int)q;
+  }
+  unsigned int code = 0u;
+  for (int b = bits - 1; b >= 0; --b)
+    for (int d = 0; d < nd; ++d) code = (code << 1) | ((c[d] >> b) & 1u);
+  return code;
+}
+
+__global__ void __launch_bounds__(256)
+order_count_kernel(const float* __restrict__ x, int64_t M, int D, const unsigned int* __restrict__ box,
+                   unsigned int* __restrict__ counts) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < M) atomicAdd(counts + order_cell(x + i * D, D, box), 1u);
+}
+
+// Exclusive prefix sum of the cell counts in place, one workgroup of 1024 threads.
+__global__ void __launch_bounds__(1024) order_scan_kernel(unsigned int* __restrict__ counts) {
+  constexpr int kPer = kOrderCells / 1024;
+  __shared__ unsigned int part[1024];
+  const int t = threadIdx.x;
+  unsigned int sum = 0u;
+  for (int k = 0; k < kPer; ++k) sum += counts[t * kPer + k];
+  part[t] = sum;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {  // inclusive scan (Hillis-Steele)
+    const unsigned int v = t >= off ? part[t - off] : 0u;
+    __syncthreads();
+    part[t] += v;
+    __syncthreads();
+  }
+  unsigned int run = part[t] - sum;
+  for (int k = 0; k < kPer; ++k) {
+    const unsigned int c = counts[t * kPer + k];
+    counts[t * kPer + k] = run;
+    run += c;
+  }
+}
+
+__global__ void __launch_bounds__(256)
+order_scatter_kernel(const float* __restrict__ x, int64_t M, int D, const unsigned int* __restrict__ box,
+                     unsigned int* __restrict__ offsets, int32_t* __restrict__ order) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < M) order[atomicAdd(offsets + order_cell(x + i * D, D, box), 1u)] = (int32_t)i;
+}
+
 template <int D, int K, int R, bool LSE>
 __global__ void __launch_bounds__(kBlock)
-knn_kernel(const float* __restrict__ x, const double* __restrict__ cols, const float* __restrict__ scr,
+knn_kernel(const float* __restrict__ x, const int32_t* __restrict__ order, const double* __restrict__ cols,
+           const float* __restrict__ scr,
            const float* __restrict__ w, const double* __restrict__ ymax, int32_t* __restrict__ idx,
            float* __restrict__ dist, KeyIdx* __restrict__ partial, float* __restrict__ lse_out,
            LsePartial* __restrict__ lse_partial, int64_t M, int64_t N, int64_t cps, int Kout, double c2,
@@ -172,6 +277,7 @@ knn_kernel(const float* __restrict__ x, const double* __restrict__ cols, const f
   for (int r = 0; r < R; ++r) {
     int64_t i = row0 + (int64_t)r * kBlock;
     i = i < M ? i : M - 1;
+    if (order) i = order[i];
     double s = 0.0;
 #pragma unroll
     for (int d = 0; d < D; ++d) {
@@ -368,8 +474,9 @@ knn_kernel(const float* __restrict__ x, const double* __restrict__ cols, const f
 
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const int64_t i = row0 + (int64_t)r * kBlock;
+    int64_t i = row0 + (int64_t)r * kBlock;
     if (i >= M) continue;
+    if (order) i = order[i];
     if (gridDim.y == 1) {
 #pragma unroll
       for (int k = 0; k < K; ++k) {
@@ -436,7 +543,7 @@ merge_topk_kernel(const KeyIdx* __restrict__ partial, int32_t* __restrict__ idx,
 // log-sum-exp) the fused sweep runs only when that decision declines and the plain one only
 // when it admits; the caller runs the matrix-core log-sum-exp itself.
 template <int D, int K>
-hipError_t knn_dk(const float* x, const double* cols, const float* scr, const float* w, const double* ymax, int32_t* idx,
+hipError_t knn_dk(const float* x, const int32_t* order, const double* cols, const float* scr, const float* w, const double* ymax, int32_t* idx,
                   float* dist,
                   void* partial, float* lse_out, double* lse_partial, int64_t M, int64_t N, int Kout, double c2,
                   bool with_lse, const int* mf, const Plan& p, hipStream_t s) {
@@ -445,10 +552,10 @@ hipError_t knn_dk(const float* x, const double* cols, const float* scr, const fl
   KeyIdx* part = reinterpret_cast<KeyIdx*>(partial);
   LsePartial* lpart = reinterpret_cast<LsePartial*>(lse_partial);
   if (with_lse)
-    knn_kernel<D, K, R, true><<<grid, kBlock, 0, s>>>(x, cols, scr, w, ymax, idx, dist, part, lse_out, lpart, M, N,
+    knn_kernel<D, K, R, true><<<grid, kBlock, 0, s>>>(x, order, cols, scr, w, ymax, idx, dist, part, lse_out, lpart, M, N,
                                                        p.cols_per_split, Kout, c2, mf, 0);
   if (!with_lse || mf)
-    knn_kernel<D, K, R, false><<<grid, kBlock, 0, s>>>(x, cols, scr, w, ymax, idx, dist, part, lse_out, lpart, M, N,
+    knn_kernel<D, K, R, false><<<grid, kBlock, 0, s>>>(x, order, cols, scr, w, ymax, idx, dist, part, lse_out, lpart, M, N,
                                                         p.cols_per_split, Kout, c2, mf, 1);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
@@ -459,11 +566,11 @@ hipError_t knn_dk(const float* x, const double* cols, const float* scr, const fl
 }
 
 template <int D>
-hipError_t knn_d(int Kb, const float* x, const double* cols, const float* scr, const float* w, const double* ymax,
+hipError_t knn_d(int Kb, const float* x, const int32_t* order, const double* cols, const float* scr, const float* w, const double* ymax,
                  int32_t* idx, float* dist,
                  void* partial, float* lse_out, double* lse_partial, int64_t M, int64_t N, int Kout, double c2,
                  bool with_lse, const int* mf, const Plan& p, hipStream_t s) {
-#define KEOPS_KNN_K(Kv) return knn_dk<D, Kv>(x, cols, scr, w, ymax, idx, dist, partial, lse_out, lse_partial, M, N, Kout, c2, with_lse, mf, p, s)
+#define KEOPS_KNN_K(Kv) return knn_dk<D, Kv>(x, order, cols, scr, w, ymax, idx, dist, partial, lse_out, lse_partial, M, N, Kout, c2, with_lse, mf, p, s)
   switch (Kb) {
     case 1: KEOPS_KNN_K(1);
     case 2: KEOPS_KNN_K(2);
@@ -545,7 +652,16 @@ int knn_occupancy(int D, int K) {
 
 size_t knn_screen_bytes(int64_t N, int D) { return (size_t)N * lowd::screen_stride(D) * sizeof(float); }
 
-hipError_t launch_knn_lowd(const float* x, const float* y, const float* w, double* cols, float* scr, double* ymax,
+bool knn_orders_rows(int64_t M) { return M >= kKnnOrderMinRows; }
+
+size_t knn_order_bytes(int64_t M) {
+  if (!knn_orders_rows(M)) return 0;
+  return align_up(8 * sizeof(unsigned int)) + align_up((size_t)lowd::kOrderCells * sizeof(unsigned int)) +
+         align_up((size_t)M * sizeof(int32_t));
+}
+
+hipError_t launch_knn_lowd(const float* x, const float* y, const float* w, double* cols, float* scr, void* order_ws,
+                           double* ymax,
                            int32_t* idx, float* dist, void* partial, float* lse_out, double* lse_partial, int64_t M,
                            int64_t N, int D, int K, double c2, bool with_lse, const Plan& p, hipStream_t s,
                            const KnnLse* mf_lse) {
@@ -559,6 +675,24 @@ hipError_t launch_knn_lowd(const float* x, const float* y, const float* w, doubl
                                                                          lowd::screen_stride(D), ymax);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  // rows in spatial order (large M only)
+  const int32_t* order = nullptr;
+  if (knn_orders_rows(M)) {
+    char* ow = static_cast<char*>(order_ws);
+    unsigned int* box = reinterpret_cast<unsigned int*>(ow);
+    unsigned int* counts = reinterpret_cast<unsigned int*>(ow + align_up(8 * sizeof(unsigned int)));
+    int32_t* ord = reinterpret_cast<int32_t*>(ow + align_up(8 * sizeof(unsigned int)) +
+                                              align_up((size_t)lowd::kOrderCells * sizeof(unsigned int)));
+    const int64_t mb = lowd::ceil_div(M, 256);
+    lowd::order_clear_kernel<<<(unsigned)(lowd::kOrderCells / 256), 256, 0, s>>>(box, counts);
+    lowd::order_box_kernel<<<(unsigned)(mb < 256 ? mb : 256), 256, 0, s>>>(x, M, D, box);
+    lowd::order_count_kernel<<<(unsigned)mb, 256, 0, s>>>(x, M, D, box, counts);
+    lowd::order_scan_kernel<<<1, 1024, 0, s>>>(counts);
+    lowd::order_scatter_kernel<<<(unsigned)mb, 256, 0, s>>>(x, M, D, box, counts, ord);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    order = ord;
+  }
   const int Kb = lowd::argk_bucket(K);
   // With the log-sum-exp and a matrix-core region: the matrix-core log-sum-exp sweep and the
   // plain argKmin sweep when the device-side decision admits the inputs (the two sweeps cost
@@ -569,7 +703,7 @@ hipError_t launch_knn_lowd(const float* x, const float* y, const float* w, doubl
     if (e != hipSuccess) return e;
     mf = mf_decision(mf_lse->region);
   }
-#define KEOPS_KNN(Dv) lowd::knn_d<Dv>(Kb, x, cols, scr, w, ymax, idx, dist, partial, lse_out, lse_partial, M, N, K, c2, with_lse, mf, p, s)
+#define KEOPS_KNN(Dv) lowd::knn_d<Dv>(Kb, x, order, cols, scr, w, ymax, idx, dist, partial, lse_out, lse_partial, M, N, K, c2, with_lse, mf, p, s)
   auto run = [&]() -> hipError_t { KEOPS_SWITCH_D(D, KEOPS_KNN) };
 #undef KEOPS_KNN
   e = run();

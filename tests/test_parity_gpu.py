@@ -267,6 +267,36 @@ def test_argkmin_shapes(M, N, D, K):
     assert np.allclose(dist, want_d2, rtol=1e-6, atol=0)
 
 
+# From 16384 rows on, the argKmin sweeps take their rows in spatial order (a counting sort by
+# grid cell); every row's result must still be the oracle's, bit for bit.
+ORDERED_ARGK_SHAPES = [(16384, 2000, 3, 10), (20000, 3001, 1, 4), (20001, 2500, 2, 1), (17000, 4000, 5, 16),
+                       (30000, 1500, 8, 32), (16500, 999, 3, 64)]
+
+
+@pytest.mark.parametrize("M,N,D,K", ORDERED_ARGK_SHAPES)
+def test_argkmin_spatially_ordered_rows(M, N, D, K):
+    import pairwise_reductions_amd as pr
+    _announce("argkmin_ordered", M=M, N=N, D=D, K=K)
+    rng = np.random.default_rng(M + 3 * N + K)
+    x = workloads.grid24(rng, (M, D))
+    y = workloads.grid24(rng, (N, D))
+    x[::7] = (x[::7] * 0.01).astype(np.float32)   # a dense corner: many rows in few cells
+    idx, dist = pr.argkmin(_dev(x), _dev(y), K, with_dist=True)
+    want_idx, want_d2 = oracle.argkmin(x, y, K, workers=8)
+    assert np.array_equal(_host(idx).astype(np.int64), want_idx)
+    assert np.allclose(_host(dist), want_d2, rtol=1e-6, atol=0)
+    w = rng.uniform(-0.01, 0.01, N).astype(np.float32)
+    widx, wkeys = pr.argkmin_weighted(_dev(x), _dev(y), _dev(w), K, with_dist=True)
+    want_widx, _ = oracle.argkmin_weighted(x, y, w, K, workers=8)
+    assert np.array_equal(_host(widx).astype(np.int64), want_widx)
+    if D <= 3:
+        sig = float(np.float32(0.1))
+        fidx, flse = pr.argkmin_lse(_dev(x), _dev(y), K, sig)
+        assert np.array_equal(_host(fidx).astype(np.int64), want_idx)
+        want_lse = oracle.logsumexp_reduction(x, y, sig, workers=8)
+        assert np.all(np.abs(_host(flse) - want_lse) <= lse_bound(want_lse))
+
+
 def test_argkmin_ties_lowest_index():
     import pairwise_reductions_amd as pr
     _announce("argkmin_ties")
