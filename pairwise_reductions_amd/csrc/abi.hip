@@ -100,7 +100,7 @@ struct LowdLayout {
   size_t cols_off, cols_bytes;  // column table
   size_t aux_off;               // one double: the largest column norm (argKmin screening)
   size_t scr_off;               // argKmin: the float32 screening table
-  size_t order_off;             // argKmin: the rows' spatial order
+  size_t order_off;             // argKmin: spatial orders and starting thresholds
   size_t part_off, part_bytes;  // per-split partials (argKmin lists for ops 2 and 6)
   size_t lse_off;               // per-split (m, l) pairs of the fused argKmin + LSE (op 6)
   size_t mf_off;                // Gauss sum, LSE, one-channel gradient: the matrix-core operands
@@ -120,7 +120,7 @@ LowdLayout lowd_layout(int op, int64_t M, int64_t N, int D, int C, int K) {
   L.scr_off = L.aux_off + aux_bytes;
   const size_t scr_bytes = knn ? keops::align_up(keops::knn_screen_bytes(N, D)) : 0;
   L.order_off = L.scr_off + scr_bytes;
-  const size_t order_bytes = knn ? keops::align_up(keops::knn_order_bytes(M)) : 0;
+  const size_t order_bytes = knn ? keops::align_up(keops::knn_order_bytes(M, N)) : 0;
   L.part_off = L.order_off + order_bytes;
   size_t lse_bytes = 0;
   if (S > 1) {

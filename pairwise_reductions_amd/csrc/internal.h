@@ -100,11 +100,13 @@ struct KnnLse {
 // inputs, and in the fused float64 sweep otherwise.
 // Bytes of the float32 screening table of the plain argKmin sweep (N records).
 size_t knn_screen_bytes(int64_t N, int D);
-// argKmin sweeps take their rows in spatial order from this many rows on; the order's
-// workspace (a bounding box, cell counts and the M-entry order) is knn_order_bytes(M).
+// argKmin sweeps take their rows in spatial order, and start each row's screen from the K-th
+// smallest key over a few nearby columns, from this many rows on; the workspace (a bounding
+// box, cell counts, the row and column orders and the M starting thresholds) is
+// knn_order_bytes(M, N).
 constexpr int64_t kKnnOrderMinRows = 16384;
 bool knn_orders_rows(int64_t M);
-size_t knn_order_bytes(int64_t M);
+size_t knn_order_bytes(int64_t M, int64_t N);
 hipError_t launch_knn_lowd(const float* x, const float* y, const float* w, double* cols, float* scr, void* order_ws,
                            double* ymax,
                            int32_t* idx, float* dist, void* partial, float* lse_out,

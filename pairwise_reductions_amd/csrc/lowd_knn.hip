@@ -49,8 +49,11 @@ __device__ __forceinline__ double sq_dist_key(const double (&xu)[D], const doubl
 // the exact maximum in any order; *out is cleared by zero_kernel first. With weights the
 // table's screening term becomes |y_j|^2 - w_j (each entry is rewritten by the one thread that
 // reads it). The same pass writes the float32 screening table scr[j] = (y_j, |y_j|^2 - w_j
-// rounded to float32, zeros) with records of S32 floats.
+// rounded to float32, zeros) with records of S32 floats, followed by kScreenPad records (0, +inf)
+// that no row can take (tiles running past the last column read them).
 __global__ void zero_kernel(double* __restrict__ out) { *out = 0.0; }
+
+constexpr int kScreenPad = 16;  // records after the last column (a sweep reads up to 3 tiles past it)
 
 __global__ void __launch_bounds__(256)
 max_norm_kernel(double* __restrict__ cols, const float* __restrict__ w, int64_t N, int P, int D,
@@ -71,6 +74,10 @@ max_norm_kernel(double* __restrict__ cols, const float* __restrict__ w, int64_t 
     for (int d = 0; d < D; ++d) scr[j * S32 + d] = (float)cols[j * P + d];
     scr[j * S32 + D] = (float)yy;
     for (int d = D + 1; d < S32; ++d) scr[j * S32 + d] = 0.0f;
+  }
+  if (blockIdx.x == 0 && (int)threadIdx.x < kScreenPad * S32) {
+    const int d = (int)threadIdx.x % S32;
+    scr[N * S32 + threadIdx.x] = (d == D) ? INFINITY : 0.0f;
   }
   red[threadIdx.x] = m;
   __syncthreads();
@@ -145,8 +152,9 @@ __device__ __forceinline__ int64_t uniform(int64_t v) {
 // columns are mostly the same, so far fewer tiles hold a candidate for some lane of the wave
 // than with rows in input order (each row's result does not depend on which lane computes it).
 // The order is a counting sort of the rows by the Morton code of their cell on a 2^15-cell grid
-// over the rows' bounding box (5 bits per dimension over the first three dimensions; 15 bits
-// for D = 1, 7 per dimension for D = 2); rows within one cell keep an arbitrary order.
+// over the bounding box of rows and columns together (5 bits per dimension over the first
+// three dimensions; 15 bits for D = 1, 7 per dimension for D = 2); rows within one cell keep an
+// arbitrary order. The columns are sorted the same way, for the starting thresholds below.
 constexpr int kOrderBits = 15;
 constexpr int kOrderCells = 1 << kOrderBits;
 
@@ -159,24 +167,36 @@ __device__ __forceinline__ float f_of_ord(unsigned int u) {
 }
 
 // box[0..2] = per-dimension minima, box[3..5] maxima (order-preserving encodings; cleared to
-// 0xffffffff / 0 first), counts[0..kOrderCells) = 0.
-__global__ void __launch_bounds__(256) order_clear_kernel(unsigned int* __restrict__ box, unsigned int* __restrict__ counts) {
+// 0xffffffff / 0 first), both cell-count tables (rows, columns) = 0.
+__global__ void __launch_bounds__(256)
+order_clear_kernel(unsigned int* __restrict__ box, unsigned int* __restrict__ counts, unsigned int* __restrict__ ccounts) {
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (t < kOrderCells) counts[t] = 0u;
+  if (t < kOrderCells) {
+    counts[t] = 0u;
+    ccounts[t] = 0u;
+  }
   if (t < 3) box[t] = 0xffffffffu;
   else if (t < 6) box[t] = 0u;
 }
 
+// One pass over the rows and the columns; each workgroup reduces its share in LDS and folds it
+// in with one atomic minimum / maximum per dimension.
 __global__ void __launch_bounds__(256)
-order_box_kernel(const float* __restrict__ x, int64_t M, int D, unsigned int* __restrict__ box) {
+order_box_kernel(const float* __restrict__ x, int64_t M, const float* __restrict__ y, int64_t N, int D,
+                 unsigned int* __restrict__ box) {
+  __shared__ unsigned int red[2][3][4];
   const int nd = D < 3 ? D : 3;
   unsigned int lo[3] = {0xffffffffu, 0xffffffffu, 0xffffffffu}, hi[3] = {0u, 0u, 0u};
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < M; i += (int64_t)gridDim.x * 256)
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < M + N; i += stride) {
+    const float* p = i < M ? x + i * D : y + (i - M) * D;
     for (int d = 0; d < nd; ++d) {
-      const unsigned int v = ord_of_f(x[i * D + d]);
+      const unsigned int v = ord_of_f(p[d]);
       lo[d] = v < lo[d] ? v : lo[d];
       hi[d] = v > hi[d] ? v : hi[d];
     }
+  }
+  const int wave = threadIdx.x >> 6;
   for (int d = 0; d < nd; ++d) {
     for (int m = 32; m >= 1; m >>= 1) {
       const unsigned int a = __shfl_xor(lo[d], m), b = __shfl_xor(hi[d], m);
@@ -184,9 +204,20 @@ order_box_kernel(const float* __restrict__ x, int64_t M, int D, unsigned int* __
       hi[d] = b > hi[d] ? b : hi[d];
     }
     if ((threadIdx.x & 63) == 0) {
-      atomicMin(box + d, lo[d]);
-      atomicMax(box + 3 + d, hi[d]);
+      red[0][d][wave] = lo[d];
+      red[1][d][wave] = hi[d];
     }
+  }
+  __syncthreads();
+  if ((int)threadIdx.x < nd) {
+    const int d = threadIdx.x;
+    unsigned int l = red[0][d][0], h = red[1][d][0];
+    for (int w = 1; w < 4; ++w) {
+      l = red[0][d][w] < l ? red[0][d][w] : l;
+      h = red[1][d][w] > h ? red[1][d][w] : h;
+    }
+    atomicMin(box + d, l);
+    atomicMax(box + 3 + d, h);
   }
 }
 
@@ -208,46 +239,115 @@ __device__ __forceinline__ unsigned int order_cell(const float* __restrict__ xi,
   return code;
 }
 
+// Cell counts of the rows (threads [0, M)) and of the columns (threads [M, M + N)).
 __global__ void __launch_bounds__(256)
-order_count_kernel(const float* __restrict__ x, int64_t M, int D, const unsigned int* __restrict__ box,
-                   unsigned int* __restrict__ counts) {
+order_count_kernel(const float* __restrict__ x, int64_t M, const float* __restrict__ y, int64_t N, int D,
+                   const unsigned int* __restrict__ box, unsigned int* __restrict__ counts,
+                   unsigned int* __restrict__ ccounts) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i < M) atomicAdd(counts + order_cell(x + i * D, D, box), 1u);
+  else if (i < M + N) atomicAdd(ccounts + order_cell(y + (i - M) * D, D, box), 1u);
 }
 
-// Exclusive prefix sum of the cell counts in place, one workgroup of 1024 threads.
-__global__ void __launch_bounds__(1024) order_scan_kernel(unsigned int* __restrict__ counts) {
+// Exclusive prefix sums of the two count tables in place, one workgroup of 1024 threads each
+// (workgroup 0: rows, 1: columns).
+__global__ void __launch_bounds__(1024) order_scan_kernel(unsigned int* __restrict__ counts, unsigned int* __restrict__ ccounts) {
   constexpr int kPer = kOrderCells / 1024;
   __shared__ unsigned int part[1024];
+  unsigned int* c = blockIdx.x == 0 ? counts : ccounts;
   const int t = threadIdx.x;
+  unsigned int v[kPer];
   unsigned int sum = 0u;
-  for (int k = 0; k < kPer; ++k) sum += counts[t * kPer + k];
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    v[k] = c[t * kPer + k];
+    sum += v[k];
+  }
   part[t] = sum;
   __syncthreads();
   for (int off = 1; off < 1024; off <<= 1) {  // inclusive scan (Hillis-Steele)
-    const unsigned int v = t >= off ? part[t - off] : 0u;
+    const unsigned int a = t >= off ? part[t - off] : 0u;
     __syncthreads();
-    part[t] += v;
+    part[t] += a;
     __syncthreads();
   }
   unsigned int run = part[t] - sum;
+#pragma unroll
   for (int k = 0; k < kPer; ++k) {
-    const unsigned int c = counts[t * kPer + k];
-    counts[t * kPer + k] = run;
-    run += c;
+    c[t * kPer + k] = run;
+    run += v[k];
   }
 }
 
+// Rows to their places in the row order (threads [0, M)), columns in the column order.
 __global__ void __launch_bounds__(256)
-order_scatter_kernel(const float* __restrict__ x, int64_t M, int D, const unsigned int* __restrict__ box,
-                     unsigned int* __restrict__ offsets, int32_t* __restrict__ order) {
+order_scatter_kernel(const float* __restrict__ x, int64_t M, const float* __restrict__ y, int64_t N, int D,
+                     const unsigned int* __restrict__ box, unsigned int* __restrict__ offsets,
+                     unsigned int* __restrict__ coffsets, int32_t* __restrict__ order, int32_t* __restrict__ corder) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i < M) order[atomicAdd(offsets + order_cell(x + i * D, D, box), 1u)] = (int32_t)i;
+  else if (i < M + N) corder[atomicAdd(coffsets + order_cell(y + (i - M) * D, D, box), 1u)] = (int32_t)(i - M);
+}
+
+// Starting thresholds. Any K columns bound a row's K-th smallest key from above, so the row's
+// screen may start from the K-th smallest exact key over a few columns instead of from
+// infinity: it then drops only columns that cannot enter the result (and every column split
+// starts with a threshold near the final one). The columns taken are the nseed ones around the
+// end of the row's cell in the columns' spatial order (cend[c] = end of cell c there), mostly
+// close to the row; which ones are taken does not change the result. Keys are computed as in
+// the sweep (sq_dist_key, then minus w_j). One thread per row, rows in spatial order.
+template <int D, int K>
+__global__ void __launch_bounds__(256)
+seed_kernel(const float* __restrict__ x, const int32_t* __restrict__ order, const double* __restrict__ cols,
+            const float* __restrict__ w, const int32_t* __restrict__ corder, const unsigned int* __restrict__ cend,
+            const unsigned int* __restrict__ box, int64_t M, int64_t N, int nseed, double* __restrict__ seed) {
+  constexpr int P = (D + 2) & ~1;
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= M) return;
+  const int64_t i = order[t];
+  double xd[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) xd[d] = (double)x[i * D + d];
+  int64_t lo = (int64_t)cend[order_cell(x + i * D, D, box)] - nseed / 2;
+  lo = lo > N - nseed ? N - nseed : lo;
+  lo = lo < 0 ? 0 : lo;
+  const int64_t hi = lo + nseed < N ? lo + nseed : N;
+  double keys[K];
+  int32_t ids[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    keys[k] = INFINITY;
+    ids[k] = -1;
+  }
+  // eight columns at a time: their indices, then their coordinates, are loaded together
+  constexpr int kB = 8;
+  for (int64_t e0 = lo; e0 < hi; e0 += kB) {
+    int32_t jj[kB];
+#pragma unroll
+    for (int u = 0; u < kB; ++u) jj[u] = corder[e0 + u < hi ? e0 + u : e0];
+    double yv[kB][P];
+    float wv[kB];
+#pragma unroll
+    for (int u = 0; u < kB; ++u) {
+#pragma unroll
+      for (int d = 0; d < D; ++d) yv[u][d] = cols[(int64_t)jj[u] * P + d];
+      wv[u] = w ? w[jj[u]] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < kB; ++u) {
+      if (e0 + u >= hi) break;
+      double key = sq_dist_key<D>(xd, yv[u]);
+      if (w) key -= (double)wv[u];
+      if (key < keys[K - 1]) topk_insert<K>(keys, ids, key, jj[u]);
+    }
+  }
+  seed[i] = keys[K - 1];
 }
 
 template <int D, int K, int R, bool LSE>
 __global__ void __launch_bounds__(kBlock)
-knn_kernel(const float* __restrict__ x, const int32_t* __restrict__ order, const double* __restrict__ cols,
+knn_kernel(const float* __restrict__ x, const int32_t* __restrict__ order, const double* __restrict__ seed,
+           const double* __restrict__ cols,
            const float* __restrict__ scr,
            const float* __restrict__ w, const double* __restrict__ ymax, int32_t* __restrict__ idx,
            float* __restrict__ dist, KeyIdx* __restrict__ partial, float* __restrict__ lse_out,
@@ -288,8 +388,10 @@ knn_kernel(const float* __restrict__ x, const int32_t* __restrict__ order, const
     }
     A[r] = s;
     marg[r] = (LSE ? kScreenMargin : kScreenMargin32) * (s + bmax);
-    thr[r] = INFINITY;
-    thr32[r] = INFINITY;
+    // (a starting key of -inf, from infinite weights, would screen out the -inf keys themselves)
+    const double sk = seed ? seed[i] : INFINITY;
+    thr[r] = sk > -INFINITY ? (sk - s) + marg[r] : INFINITY;
+    thr32[r] = round_up_f32(thr[r]);
 #pragma unroll
     for (int k = 0; k < K; ++k) {
       keys[r][k] = INFINITY;
@@ -310,36 +412,49 @@ knn_kernel(const float* __restrict__ x, const int32_t* __restrict__ order, const
       if (w) key -= (double)w[jj];
       if (key < keys[r][K - 1]) topk_insert<K>(keys[r], ids[r], key, jj);
     }
-    thr[r] = (keys[r][K - 1] - A[r]) + marg[r];
-    thr32[r] = round_up_f32(thr[r]);
+    // until the list holds K keys the starting threshold stands
+    if (keys[r][K - 1] < INFINITY) {
+      thr[r] = (keys[r][K - 1] - A[r]) + marg[r];
+      thr32[r] = round_up_f32(thr[r]);
+    }
     cnt[r] = 0;
   };
 
-  // The float32 screen of columns [j, j + n), n <= U, for row r (plain sweep): D FMAs per pair
-  // and one compare per tile (of the smallest of its U values) decide whether any lane has a
-  // candidate; only then are the columns queued.
-  auto tile32 = [&](int r, int64_t j, int n, const float (&yv)[U][D], const float (&tv)[U]) {
-    if (full[r]) {
-      flush(r);
-      full[r] = false;
-    }
-    float a[U];
-    float mn = INFINITY;
+  // The float32 screen (plain sweep). screen32 computes a32 for the U columns of a tile and every
+  // row (D FMAs per pair) and tells whether any lane has a candidate in any row, from the
+  // smallest value of each row (one compare per row and tile, one wave-uniform branch per tile).
+  // Only then does queue32 queue the candidates; the rows are flushed once per two tiles, when
+  // some lane's queue could not take two more, so the common tile runs no other branch. Columns
+  // past the split's end are never candidates: the last split ends in the table's (0, +inf)
+  // records and the others hold whole tiles.
+  auto screen32 = [&](const float (&yv)[U][D], const float (&tv)[U], float (&a)[R][U]) -> bool {
+    bool hit = false;  // this lane, any row
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      float t = tv[u];
-#pragma unroll
-      for (int d = 0; d < D; ++d) t = fmaf(xs[r][d], yv[u][d], t);
-      a[u] = t;
-      if (u < n) mn = fminf(mn, t);
-    }
-    if (K > 16 || __builtin_expect(__any(mn < thr32[r]), 0)) {
+    for (int r = 0; r < R; ++r) {
+      float mn = INFINITY;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        queue[r][cnt[r]][threadIdx.x] = (int32_t)(j + u);
-        cnt[r] += (u < n && a[u] < thr32[r]) ? 1 : 0;
+        float t = tv[u];
+#pragma unroll
+        for (int d = 0; d < D; ++d) t = fmaf(xs[r][d], yv[u][d], t);
+        a[r][u] = t;
+        mn = fminf(mn, t);
       }
-      full[r] = __any(cnt[r] > kQueue - U);
+      hit |= mn < thr32[r];
+    }
+    return hit;
+  };
+  bool need = false;  // wave-uniform: some row's queue could not take two more tiles
+  auto queue32 = [&](int64_t j, const float (&a)[R][U]) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      // at most kQueue - 2 U entries at the last flush check, so the U writes stay inside
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        queue[r][cnt[r]][threadIdx.x] = (int32_t)(j + u);  // kept only when the count advances
+        cnt[r] += a[r][u] < thr32[r] ? 1 : 0;
+      }
+      need = need || __any(cnt[r] > kQueue - 2 * U);
     }
   };
 
@@ -393,50 +508,57 @@ knn_kernel(const float* __restrict__ x, const int32_t* __restrict__ order, const
 
   const int64_t nfull = (j1 - j0) / U;  // whole tiles of the split
   if constexpr (!LSE) {
-    // float32 records through the scalar unit, the next tile's loaded while the current one is
-    // screened (two alternating sets)
-    ConstPtr<float> cscr = (ConstPtr<float>)scr;
+    // float32 records through the scalar unit, two tiles per trip in two alternating register
+    // sets; p walks the split's records. Every split but the last holds an even number of whole
+    // tiles (its column count is a multiple of 8); the last one's tiles past its end (the second
+    // tile of its last trip and the loads two tiles ahead) fall in the table's padding, whose
+    // records no row takes.
+    ConstPtr<float> p = (ConstPtr<float>)scr + j0 * S32;
     struct Recs {
       float y[U][D], t[U];
     };
-    auto load = [&](int64_t jt, Recs& o) {
+    auto load = [&](ConstPtr<float> q, Recs& o) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
 #pragma unroll
-        for (int d = 0; d < D; ++d) o.y[u][d] = cscr[(jt + u) * S32 + d];
-        o.t[u] = cscr[(jt + u) * S32 + D];
+        for (int d = 0; d < D; ++d) o.y[u][d] = q[u * S32 + d];
+        o.t[u] = q[u * S32 + D];
       }
     };
+    // Scalar loads complete out of order, so a wait for one set waits for every load in flight.
+    // ready() makes the wait for a set happen before the next set's load is issued: its result
+    // (always 0) depends on the set and the next load's address depends on it, so that load gets
+    // a whole tile's screening as cover.
+    auto ready = [&](const Recs& o) -> int {
+      int z;
+      asm("s_mov_b32 %0, 0" : "=s"(z) : "s"(__float_as_int(o.t[0])));
+      return z;
+    };
+    const int ntiles = j1 > j0 ? (int)((j1 - j0 + U - 1) / U) : 0;  // fewer than 2^31 columns
     Recs ra, rb;
-    if (nfull > 0) load(uniform(j0), ra);
-    int64_t t = 0;
-    for (; t + 2 <= nfull; t += 2) {
-      const int64_t ja = uniform(j0 + t * U);
-      load(ja + U, rb);
+    if (ntiles > 0) load(p, ra);
+    int64_t j = j0;
+    for (int t = 0; t < ntiles; t += 2) {
+      load(p + ready(ra) + U * S32, rb);
+      __builtin_amdgcn_sched_barrier(0);
+      float aa[R][U], ab[R][U];
+      const bool ha = screen32(ra.y, ra.t, aa);
+      __builtin_amdgcn_sched_barrier(0);
+      load(p + ready(rb) + 2 * U * S32, ra);
+      __builtin_amdgcn_sched_barrier(0);
+      const bool hb = screen32(rb.y, rb.t, ab);
+      if (__builtin_expect(__any(ha || hb), 0)) {
+        queue32(j, aa);
+        queue32(j + U, ab);
+        if (need) {
 #pragma unroll
-      for (int r = 0; r < R; ++r) tile32(r, ja, U, ra.y, ra.t);
-      if (t + 2 < nfull) load(ja + 2 * U, ra);
-#pragma unroll
-      for (int r = 0; r < R; ++r) tile32(r, ja + U, U, rb.y, rb.t);
-    }
-    if (t < nfull) {  // an odd last whole tile, already in ra
-      const int64_t ja = uniform(j0 + t * U);
-#pragma unroll
-      for (int r = 0; r < R; ++r) tile32(r, ja, U, ra.y, ra.t);
-    }
-    const int64_t jr = j0 + nfull * U;
-    if (jr < j1) {
-      const int n = (int)(j1 - jr);
-      Recs rt;
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int64_t jj = (u < n) ? jr + u : jr;
-#pragma unroll
-        for (int d = 0; d < D; ++d) rt.y[u][d] = scr[jj * S32 + d];
-        rt.t[u] = scr[jj * S32 + D];
+          for (int r = 0; r < R; ++r)
+            if (__any(cnt[r] > kQueue - 2 * U)) flush(r);
+          need = false;
+        }
       }
-#pragma unroll
-      for (int r = 0; r < R; ++r) tile32(r, jr, n, rt.y, rt.t);
+      p += 2 * U * S32;
+      j += 2 * U;
     }
   }
   // The column records are the same for every lane: with two rows per lane they are read
@@ -542,21 +664,35 @@ merge_topk_kernel(const KeyIdx* __restrict__ partial, int32_t* __restrict__ idx,
 // The sweep(s) and the merges. With mf (the device-side decision of a prepared matrix-core
 // log-sum-exp) the fused sweep runs only when that decision declines and the plain one only
 // when it admits; the caller runs the matrix-core log-sum-exp itself.
+// The spatial orders and the starting thresholds (all null for few rows).
+struct Order {
+  const int32_t* rows = nullptr;
+  const int32_t* cols = nullptr;
+  const unsigned int* cend = nullptr;
+  const unsigned int* box = nullptr;
+  double* seed = nullptr;
+};
+
 template <int D, int K>
-hipError_t knn_dk(const float* x, const int32_t* order, const double* cols, const float* scr, const float* w, const double* ymax, int32_t* idx,
+hipError_t knn_dk(const float* x, const Order& o, const double* cols, const float* scr, const float* w, const double* ymax, int32_t* idx,
                   float* dist,
                   void* partial, float* lse_out, double* lse_partial, int64_t M, int64_t N, int Kout, double c2,
                   bool with_lse, const int* mf, const Plan& p, hipStream_t s) {
   constexpr int R = K <= 16 ? 2 : 1;
+  if (o.seed) {
+    const int nseed = 4 * K > 64 ? 4 * K : 64;
+    seed_kernel<D, K><<<(unsigned)ceil_div(M, 256), 256, 0, s>>>(x, o.rows, cols, w, o.cols, o.cend, o.box, M, N, nseed,
+                                                                  o.seed);
+  }
   dim3 grid((unsigned)p.row_blocks, (unsigned)p.splits);
   KeyIdx* part = reinterpret_cast<KeyIdx*>(partial);
   LsePartial* lpart = reinterpret_cast<LsePartial*>(lse_partial);
   if (with_lse)
-    knn_kernel<D, K, R, true><<<grid, kBlock, 0, s>>>(x, order, cols, scr, w, ymax, idx, dist, part, lse_out, lpart, M, N,
-                                                       p.cols_per_split, Kout, c2, mf, 0);
+    knn_kernel<D, K, R, true><<<grid, kBlock, 0, s>>>(x, o.rows, o.seed, cols, scr, w, ymax, idx, dist, part, lse_out, lpart,
+                                                       M, N, p.cols_per_split, Kout, c2, mf, 0);
   if (!with_lse || mf)
-    knn_kernel<D, K, R, false><<<grid, kBlock, 0, s>>>(x, order, cols, scr, w, ymax, idx, dist, part, lse_out, lpart, M, N,
-                                                        p.cols_per_split, Kout, c2, mf, 1);
+    knn_kernel<D, K, R, false><<<grid, kBlock, 0, s>>>(x, o.rows, o.seed, cols, scr, w, ymax, idx, dist, part, lse_out, lpart,
+                                                        M, N, p.cols_per_split, Kout, c2, mf, 1);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
   merge_topk_kernel<K><<<(unsigned)ceil_div(M, kBlock), kBlock, 0, s>>>(part, idx, dist, M, p.splits, Kout);
@@ -566,7 +702,7 @@ hipError_t knn_dk(const float* x, const int32_t* order, const double* cols, cons
 }
 
 template <int D>
-hipError_t knn_d(int Kb, const float* x, const int32_t* order, const double* cols, const float* scr, const float* w, const double* ymax,
+hipError_t knn_d(int Kb, const float* x, const Order& order, const double* cols, const float* scr, const float* w, const double* ymax,
                  int32_t* idx, float* dist,
                  void* partial, float* lse_out, double* lse_partial, int64_t M, int64_t N, int Kout, double c2,
                  bool with_lse, const int* mf, const Plan& p, hipStream_t s) {
@@ -650,14 +786,35 @@ int knn_occupancy(int D, int K) {
   return n;
 }
 
-size_t knn_screen_bytes(int64_t N, int D) { return (size_t)N * lowd::screen_stride(D) * sizeof(float); }
+size_t knn_screen_bytes(int64_t N, int D) {
+  return (size_t)(N + lowd::kScreenPad) * lowd::screen_stride(D) * sizeof(float);
+}
 
 bool knn_orders_rows(int64_t M) { return M >= kKnnOrderMinRows; }
 
-size_t knn_order_bytes(int64_t M) {
+namespace {
+// The order workspace: box | row cell counts | column cell counts | row order (M) | column
+// order (N) | starting thresholds (M doubles).
+struct OrderLayout {
+  size_t box, counts, ccounts, rows, cols, seed, total;
+};
+OrderLayout order_layout(int64_t M, int64_t N) {
+  OrderLayout L;
+  const size_t cells = align_up((size_t)lowd::kOrderCells * sizeof(unsigned int));
+  L.box = 0;
+  L.counts = align_up(8 * sizeof(unsigned int));
+  L.ccounts = L.counts + cells;
+  L.rows = L.ccounts + cells;
+  L.cols = L.rows + align_up((size_t)M * sizeof(int32_t));
+  L.seed = L.cols + align_up((size_t)N * sizeof(int32_t));
+  L.total = L.seed + align_up((size_t)M * sizeof(double));
+  return L;
+}
+}  // namespace
+
+size_t knn_order_bytes(int64_t M, int64_t N) {
   if (!knn_orders_rows(M)) return 0;
-  return align_up(8 * sizeof(unsigned int)) + align_up((size_t)lowd::kOrderCells * sizeof(unsigned int)) +
-         align_up((size_t)M * sizeof(int32_t));
+  return order_layout(M, N).total;
 }
 
 hipError_t launch_knn_lowd(const float* x, const float* y, const float* w, double* cols, float* scr, void* order_ws,
@@ -675,23 +832,29 @@ hipError_t launch_knn_lowd(const float* x, const float* y, const float* w, doubl
                                                                          lowd::screen_stride(D), ymax);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // rows in spatial order (large M only)
-  const int32_t* order = nullptr;
+  // rows and columns in spatial order and the rows' starting thresholds (large M only)
+  lowd::Order order;
   if (knn_orders_rows(M)) {
     char* ow = static_cast<char*>(order_ws);
-    unsigned int* box = reinterpret_cast<unsigned int*>(ow);
-    unsigned int* counts = reinterpret_cast<unsigned int*>(ow + align_up(8 * sizeof(unsigned int)));
-    int32_t* ord = reinterpret_cast<int32_t*>(ow + align_up(8 * sizeof(unsigned int)) +
-                                              align_up((size_t)lowd::kOrderCells * sizeof(unsigned int)));
-    const int64_t mb = lowd::ceil_div(M, 256);
-    lowd::order_clear_kernel<<<(unsigned)(lowd::kOrderCells / 256), 256, 0, s>>>(box, counts);
-    lowd::order_box_kernel<<<(unsigned)(mb < 256 ? mb : 256), 256, 0, s>>>(x, M, D, box);
-    lowd::order_count_kernel<<<(unsigned)mb, 256, 0, s>>>(x, M, D, box, counts);
-    lowd::order_scan_kernel<<<1, 1024, 0, s>>>(counts);
-    lowd::order_scatter_kernel<<<(unsigned)mb, 256, 0, s>>>(x, M, D, box, counts, ord);
+    const OrderLayout L = order_layout(M, N);
+    unsigned int* box = reinterpret_cast<unsigned int*>(ow + L.box);
+    unsigned int* counts = reinterpret_cast<unsigned int*>(ow + L.counts);
+    unsigned int* ccounts = reinterpret_cast<unsigned int*>(ow + L.ccounts);
+    int32_t* rord = reinterpret_cast<int32_t*>(ow + L.rows);
+    int32_t* cord = reinterpret_cast<int32_t*>(ow + L.cols);
+    const int64_t tb = lowd::ceil_div(M + N, 256);
+    lowd::order_clear_kernel<<<(unsigned)(lowd::kOrderCells / 256), 256, 0, s>>>(box, counts, ccounts);
+    lowd::order_box_kernel<<<(unsigned)(tb < 64 ? tb : 64), 256, 0, s>>>(x, M, y, N, D, box);
+    lowd::order_count_kernel<<<(unsigned)tb, 256, 0, s>>>(x, M, y, N, D, box, counts, ccounts);
+    lowd::order_scan_kernel<<<2, 1024, 0, s>>>(counts, ccounts);
+    lowd::order_scatter_kernel<<<(unsigned)tb, 256, 0, s>>>(x, M, y, N, D, box, counts, ccounts, rord, cord);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    order = ord;
+    order.rows = rord;
+    order.cols = cord;
+    order.cend = ccounts;  // after the scatter: the end of each cell in the column order
+    order.box = box;
+    order.seed = reinterpret_cast<double*>(ow + L.seed);
   }
   const int Kb = lowd::argk_bucket(K);
   // With the log-sum-exp and a matrix-core region: the matrix-core log-sum-exp sweep and the

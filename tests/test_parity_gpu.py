@@ -297,6 +297,27 @@ def test_argkmin_spatially_ordered_rows(M, N, D, K):
         assert np.all(np.abs(_host(flse) - want_lse) <= lse_bound(want_lse))
 
 
+def test_argkmin_spatially_ordered_rows_ties():
+    """Many rows (spatial order and starting thresholds) on a coarse grid with planted duplicate
+    columns: equal keys still resolve to the lower column index, with and without weights."""
+    import pairwise_reductions_amd as pr
+    _announce("argkmin_ordered_ties")
+    rng = np.random.default_rng(17)
+    M, N = 20_000, 3000
+    x = (rng.integers(0, 8, size=(M, 3)) / 8.0).astype(np.float32)
+    y = (rng.integers(0, 8, size=(N, 3)) / 8.0).astype(np.float32)
+    y[100:200] = y[0]
+    w = (rng.integers(-2, 3, size=N) / 64.0).astype(np.float32)
+    w[100:200] = w[0]
+    for K in (1, 10, 33, 64):
+        idx = _host(pr.argkmin(_dev(x), _dev(y), K)).astype(np.int64)
+        want, _ = oracle.argkmin(x, y, K, workers=8)
+        assert np.array_equal(idx, want), K
+        widx = _host(pr.argkmin_weighted(_dev(x), _dev(y), _dev(w), K)).astype(np.int64)
+        wwant, _ = oracle.argkmin_weighted(x, y, w, K, workers=8)
+        assert np.array_equal(widx, wwant), K
+
+
 def test_argkmin_ties_lowest_index():
     import pairwise_reductions_amd as pr
     _announce("argkmin_ties")
