@@ -65,7 +65,7 @@ enum Slot { kAhVh = 0, kOneBh1, kOneBh2, kAhVl1, kAhVl2, kAl1Vh, kAl2Vh, kAl1Vl1
 struct MfParams {
   int gate;           // the scales admit the matrix-core path
   int bad;            // some piece did not convert exactly, or too many points were set aside
-  int robust;         // the box is centred on the mean and points outside it are set aside
+  int robust;         // the box is centred on the sampled median and points outside it are set aside
   int nbr, nbc;       // set-aside rows and columns so far (lists in the operand region)
   int alpha, beta, gamma;
   int sh[kSlots];
