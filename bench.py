@@ -163,7 +163,7 @@ def bench_gauss_1m(steps, warmup, cpu_rows, cpu_baseline=True):
             "frac": achieved / PEAK_FP32_VECTOR_TFLOPS,
             "traffic": measured_traffic(),
             "traffic_unit": "bytes per launch",
-            "kernel": "gauss_sum_mf_kernel<1,4,1,1>",
+            "kernel": "gauss_sum_mf32_kernel<2>",
             "flop_per_pair": gauss_flops_per_pair(D, C),
             "kernel_ms": kernel_s * 1e3,
             "kernel_timing": "events around each launch" if sweeps.value == steps else "whole step",

@@ -176,6 +176,53 @@ __global__ void __launch_bounds__(256) unit_kernel(float* out, float seed) {
   out[blockIdx.x * 256 + threadIdx.x] = s;
 }
 
+// The float32 Gauss sum's tile structure without memory, per 1024 pairs: a high-part MFMA whose
+// result feeds the low-part MFMA as its accumulator, then per output one exp2 and one FMA into
+// a per-row partial sum. kWide = false: 16x16x32 MFMAs, 4 row tiles of 16 (8 MFMAs per 1024
+// pairs); kWide = true: 32x32x16 MFMAs, 2 row tiles of 32 (2 MFMAs per 1024 pairs). One
+// iteration is 1024 pairs (16x16) or 2048 pairs (32x32).
+template <bool kWide>
+__global__ void __launch_bounds__(256) sum_tile_kernel(float* out, float seed) {
+  const _Float16 hs = (_Float16)(seed * 0.001f);
+  half8 hi = {hs, hs, hs, hs, hs, hs, hs, hs}, lo = hi;
+  float w = seed;
+  constexpr int RT = kWide ? 2 : 4, Q = kWide ? 16 : 4;
+  half8 ahi[RT], alo[RT];
+  f32x4 cinit[RT];
+  float part[RT][Q];
+#pragma unroll
+  for (int r = 0; r < RT; ++r) {
+    ahi[r] = hi * (_Float16)(0.5f + 0.1f * r);
+    alo[r] = lo * (_Float16)(0.25f + 0.1f * r);
+    cinit[r] = f32x4{-1.f, -2.f, -3.f, -4.f};
+#pragma unroll
+    for (int q = 0; q < Q; ++q) part[r][q] = 0.0f;
+  }
+  for (int it = 0; it < kIters / 8; ++it) {
+    asm volatile("" : "+v"(hi), "+v"(lo), "+v"(w));
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+      if constexpr (kWide) {
+        f32x16 e = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi[r], hi, f32x16{}, 0, 0, 0);
+        e = __builtin_amdgcn_mfma_f32_32x32x16_f16(alo[r], lo, e, 0, 0, 0);
+#pragma unroll
+        for (int q = 0; q < Q; ++q) part[r][q] = fmaf(__builtin_amdgcn_exp2f(e[q]), w, part[r][q]);
+      } else {
+        f32x4 e = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[r], hi, cinit[r], 0, 0, 0);
+        e = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[r], lo, e, 0, 0, 0);
+#pragma unroll
+        for (int q = 0; q < Q; ++q) part[r][q] = fmaf(__builtin_amdgcn_exp2f(e[q]), w, part[r][q]);
+      }
+    }
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int r = 0; r < RT; ++r)
+#pragma unroll
+    for (int q = 0; q < Q; ++q) s += part[r][q];
+  out[blockIdx.x * 256 + threadIdx.x] = s;
+}
+
 static void check(hipError_t e, const char* what) {
   if (e != hipSuccess) {
     std::fprintf(stderr, "%s: %s\n", what, hipGetErrorString(e));
@@ -215,7 +262,7 @@ int main() {
   int cus = 0;
   check(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, 0), "hipDeviceGetAttribute");
   std::printf("%-40s %12s %12s %12s\n", "ns per iteration per wave", "1 wave/SIMD", "2 waves/SIMD", "4 waves/SIMD");
-  double t[3][kKinds + 2];
+  double t[3][kKinds + 4];
   for (int w = 0; w < 3; ++w) {
     const int wps = 1 << w;
     const int blocks = cus * wps;  // 4 waves per workgroup: wps waves on every SIMD
@@ -224,9 +271,11 @@ int main() {
     run_all(out, blocks, t[w], std::make_integer_sequence<int, kKinds>{});
     t[w][kKinds] = time_ms([&] { unit_kernel<true><<<blocks, 256>>>(out, 1.0f); }, 5);
     t[w][kKinds + 1] = time_ms([&] { unit_kernel<false><<<blocks, 256>>>(out, 1.0f); }, 5);
+    t[w][kKinds + 2] = time_ms([&] { sum_tile_kernel<false><<<blocks, 256>>>(out, 1.0f); }, 5);
+    t[w][kKinds + 3] = time_ms([&] { sum_tile_kernel<true><<<blocks, 256>>>(out, 1.0f); }, 5) / 2.0;
     check(hipGetLastError(), "launch");
     check(hipFree(out), "hipFree");
-    for (int k = 0; k < kKinds + 2; ++k) t[w][k] = t[w][k] * 1e6 / kIters / wps;
+    for (int k = 0; k < kKinds + 4; ++k) t[w][k] = t[w][k] * 1e6 / kIters / wps;
   }
   for (int k = 0; k < kKinds; ++k)
     std::printf("%-40s %12.2f %12.2f %12.2f\n", kNames[k], t[0][k], t[1][k], t[2][k]);
@@ -234,5 +283,9 @@ int main() {
               t[1][kKinds], t[2][kKinds]);
   std::printf("%-40s %12.2f %12.2f %12.2f   (per 512-pair unit)\n", "fp16 forward unit, no FMA", t[0][kKinds + 1],
               t[1][kKinds + 1], t[2][kKinds + 1]);
+  std::printf("%-40s %12.2f %12.2f %12.2f   (per 1024 pairs)\n", "Gauss-sum tile, 16x16x32, 4 row tiles",
+              t[0][kKinds + 2] * 8, t[1][kKinds + 2] * 8, t[2][kKinds + 2] * 8);
+  std::printf("%-40s %12.2f %12.2f %12.2f   (per 1024 pairs)\n", "Gauss-sum tile, 32x32x16, 2 row tiles",
+              t[0][kKinds + 3] * 8, t[1][kKinds + 3] * 8, t[2][kKinds + 3] * 8);
   return 0;
 }

@@ -60,13 +60,16 @@ size_t mf_region_bytes(int64_t M, int64_t N, int D, int W, bool grad = false);  
 const int* mf_decision(const void* region);
 int mf_rows_per_lane(int op, int D, int C);   // op: 0 sum, 1 log-sum-exp, 3 gradient
 int mf_occupancy(int op, int D, int C, int rt);  // resident workgroups per CU of that sweep
+// The single-channel sum at D <= 3 runs on 32 x 32 tiles when the plan gives 2 or 4 row tiles
+// of 16 per wave (the preparation must then write that layout: square = true).
+bool mf_sum_square(int D, int C, int rt);
 int knn_occupancy(int D, int K);                 // resident workgroups per CU of the argKmin sweep
 // set_aside (the Gauss sum only): a box too wide for the matrix cores may be replaced by one
 // around the sample median that sets a few outlying points aside (launch_mf_finish then sums
 // their terms).
 hipError_t launch_mf_prepare(const float* x, const float* y, const float* b, bool with_y, double* cols,
                              void* region, int64_t M, int64_t N, int D, int C, double c2, hipStream_t s,
-                             bool set_aside = false);
+                             bool set_aside = false, bool square = false);
 // The Gauss sum's last step after either sweep: combines the S column splits of partial into out
 // (S > 1) with rscale, and when the preparation set points aside adds the set-aside columns'
 // terms to every other row and sums every set-aside row over all columns.

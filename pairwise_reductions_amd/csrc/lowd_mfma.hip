@@ -34,6 +34,16 @@
 //
 // Per pair the VALU then does one v_exp_f32 and C FMAs; the two MFMAs of a 16 x 16 tile run on
 // the matrix core beside them.
+//
+// 32 x 32 tiles (the single-channel sum for D <= 3). A 16x16x32 MFMA leaves most of its K unused
+// here (D + 2 high and 5D + 2 low terms of 32), and on this chip each MFMA also delays the
+// exponentials issued beside it. v_mfma_f32_32x32x16_f16 covers 1024 pairs with K = 16: the
+// high MFMA takes A_i as two more products (Ah1, Ah2 against column-side ones, so the
+// accumulator starts at zero; the high part stays a sum of multiples of 2^g whose partial sums
+// are below 2^(g+23), exact in any order), and the low MFMA takes the low part without A's
+// remainder Al1_i (5D + 1 <= 16 terms), which factors out of the row's sum:
+// sum_j 2^{e_ij} b_j = 2^{Al1_i} sum_j 2^{e_ij - Al1_i} b_j, applied once per row at the end.
+// Per 1024 pairs a wave then issues 2 MFMAs instead of 8.
 #include "lowd_common.h"
 
 #include <math.h>
@@ -249,6 +259,19 @@ __device__ __forceinline__ _Float16 piece(double v, int s, bool& ok) {
   return r;
 }
 
+// the first 8 W pieces of v (which may hold more)
+template <int W, int L>
+__device__ __forceinline__ void store_first(half8* __restrict__ dst, const _Float16 (&v)[L]) {
+  static_assert(8 * W <= L, "enough pieces");
+#pragma unroll
+  for (int m = 0; m < W; ++m) {
+    half8 h;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) h[k] = v[8 * m + k];
+    dst[m] = h;
+  }
+}
+
 template <int W>
 __device__ __forceinline__ void store_pieces(half8* __restrict__ dst, const _Float16 (&v)[8 * W]) {
 #pragma unroll
@@ -262,6 +285,9 @@ __device__ __forceinline__ void store_pieces(half8* __restrict__ dst, const _Flo
 
 // Operand preparation, one thread per row (workgroups [0, rb)) or per column (the rest):
 //   rows     rhi[i] (8 NH fp16), rlo[i] (32 NL fp16), rA[i] = Ah_i
+//   sq       (NH = NL = 1, D <= 3, no gradient) the 32 x 32 tile layout instead: rhi[i] with Ah1, Ah2
+//            after the high products, rlo[i] (16 fp16: the low part without Al1), rA[i] = Al1_i;
+//            chi[j] with two ones after Bh1, Bh2, clo[j] (16 fp16)
 //   columns  chi[j], clo[j] and bpad[j] = b[j][0..C) for j < Npad (b = null: no weights; zero
 //            past N; padding columns get an exponent that underflows), and (cols not null) the
 //            float64 column table cols[j] = (y_j - y_0, -c2 |y_j - y_0|^2) of the float64 sweep
@@ -279,7 +305,7 @@ mf_prep_kernel(const float* __restrict__ x, const float* __restrict__ y, const f
                int with_y, double* __restrict__ cols, half8* __restrict__ rhi, half8* __restrict__ rlo, float* __restrict__ rA,
                half8* __restrict__ chi, half8* __restrict__ clo, float* __restrict__ bpad,
                const unsigned int* __restrict__ parts, const float* __restrict__ samples, int nsamples, int nparts,
-               int64_t M, int64_t N, int64_t Npad, int D, double c2, int64_t rb, int set_aside,
+               int64_t M, int64_t N, int64_t Npad, int D, double c2, int64_t rb, int set_aside, int sq,
                int32_t* __restrict__ aside_rows, int32_t* __restrict__ aside_cols, MfParams* __restrict__ P) {
   __shared__ unsigned int red[kBlock / 64][2 * kMaxLowD];
   __shared__ unsigned int smm[2 * kMaxLowD];
@@ -371,7 +397,8 @@ mf_prep_kernel(const float* __restrict__ x, const float* __restrict__ y, const f
         if (slot < kMaxAside) aside_rows[slot] = (int32_t)i;
         else P->bad = 1;
         store_pieces<NH>(rhi + i * NH, hi);
-        store_pieces<4 * NL>(rlo + i * 4 * NL, lo);
+        if (sq) store_first<2>(rlo + i * 2, lo);
+        else store_pieces<4 * NL>(rlo + i * 4 * NL, lo);
         rA[i] = 0.0f;
         return;
       }
@@ -401,13 +428,28 @@ mf_prep_kernel(const float* __restrict__ x, const float* __restrict__ y, const f
     }
     const double A = -cp * nrm;
     const double Ah = rnd(A, sp.gamma);
-    lo[5 * D] = piece(rnd(A - Ah, sp.gamma - 12), -sp.sh[kAl1One], ok);
-    lo[5 * D + 1] = piece(1.0, -sp.sh[kOneBl1], ok);
-    const float Ahf = (float)Ah;
-    ok = ok && ((double)Ahf == Ah);
-    rA[i] = Ahf;
-    store_pieces<NH>(rhi + i * NH, hi);
-    store_pieces<4 * NL>(rlo + i * 4 * NL, lo);
+    const double Al1 = rnd(A - Ah, sp.gamma - 12);
+    if (sq) {
+      // Ah as two products against column-side ones (shifts mirrored from the Bh pieces, which
+      // have the same magnitudes), the low part without Al1, and Al1 itself for the row factor
+      const double Ah1 = rnd(Ah, sp.gamma + 11);
+      hi[D + 2] = piece(Ah1, sp.sh[kOneBh1], ok);
+      hi[D + 3] = piece(Ah - Ah1, sp.sh[kOneBh2], ok);
+      lo[5 * D] = piece(1.0, -sp.sh[kOneBl1], ok);
+      const float Alf = (float)Al1;
+      ok = ok && ((double)Alf == Al1);
+      rA[i] = Alf;
+      store_pieces<NH>(rhi + i * NH, hi);
+      store_first<2>(rlo + i * 2, lo);
+    } else {
+      lo[5 * D] = piece(Al1, -sp.sh[kAl1One], ok);
+      lo[5 * D + 1] = piece(1.0, -sp.sh[kOneBl1], ok);
+      const float Ahf = (float)Ah;
+      ok = ok && ((double)Ahf == Ah);
+      rA[i] = Ahf;
+      store_pieces<NH>(rhi + i * NH, hi);
+      store_pieces<4 * NL>(rlo + i * 4 * NL, lo);
+    }
   } else {
     const int64_t j = ((int64_t)blockIdx.x - rb) * kBlock + threadIdx.x;
     if (j >= Npad) return;
@@ -468,8 +510,14 @@ mf_prep_kernel(const float* __restrict__ x, const float* __restrict__ y, const f
       const double Bh1 = rnd(Bh, sp.gamma + 11);
       hi[D] = piece(Bh1, sp.sh[kOneBh1], ok);
       hi[D + 1] = piece(Bh - Bh1, sp.sh[kOneBh2], ok);
-      lo[5 * D] = piece(1.0, sp.sh[kAl1One], ok);
-      lo[5 * D + 1] = piece(rnd(Bv - Bh, sp.gamma - 12), sp.sh[kOneBl1], ok);
+      if (sq) {
+        hi[D + 2] = piece(1.0, -sp.sh[kOneBh1], ok);
+        hi[D + 3] = piece(1.0, -sp.sh[kOneBh2], ok);
+        lo[5 * D] = piece(rnd(Bv - Bh, sp.gamma - 12), sp.sh[kOneBl1], ok);
+      } else {
+        lo[5 * D] = piece(1.0, sp.sh[kAl1One], ok);
+        lo[5 * D + 1] = piece(rnd(Bv - Bh, sp.gamma - 12), sp.sh[kOneBl1], ok);
+      }
       if (with_y) {
         const double bj = b ? (double)b[j] : 0.0;
         const double L = bj != 0.0 ? log2(fabs(bj)) : 0.0;
@@ -483,7 +531,8 @@ mf_prep_kernel(const float* __restrict__ x, const float* __restrict__ y, const f
       hi[D] = (_Float16)-65504.0f;
     }
     store_pieces<NH>(chi + j * NH, hi);
-    store_pieces<4 * NL>(clo + j * 4 * NL, lo);
+    if (sq) store_first<2>(clo + j * 2, lo);
+    else store_pieces<4 * NL>(clo + j * 4 * NL, lo);
   }
   if (!ok) P->bad = 1;
 }
@@ -623,6 +672,130 @@ gauss_sum_mf_kernel(const half8* __restrict__ rhi, const half8* __restrict__ rlo
         const float sc = scaled ? rscale[i] : 1.0f;
 #pragma unroll
         for (int c = 0; c < C; ++c) dst[i * C + c] = sc * acc[r][q][c];
+      }
+    }
+}
+
+// The single-channel sum on 32 x 32 tiles (operands in the sq layout of mf_prep_kernel):
+// out[i] = 2^{Al1_i} sum_j 2^{e_ij - Al1_i} b[j] over the columns [j0, j1) of this split (times
+// rscale[i] with one split), else partial[split][i]. A wave holds RT tiles of 32 rows; lane
+// (g, l) (g = lane / 32, l = lane % 32) feeds row l and K slots 8g..8g+7 of each tile to the
+// MFMA and gets back the exponents of rows 8(q / 4) + 4g + q % 4 (q < 16) against column l of
+// the current 32-column tile. Lanes keep per-column partial sums (folded into the totals every
+// kChunk columns); the 32 lanes of a row group add theirs at the end.
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+template <int RT>
+__global__ void __launch_bounds__(kBlock)
+gauss_sum_mf32_kernel(const half8* __restrict__ rhi, const half8* __restrict__ rlo, const float* __restrict__ rrem,
+                      const half8* __restrict__ chi, const half8* __restrict__ clo, const float* __restrict__ bpad,
+                      float* __restrict__ out, const float* __restrict__ rscale, const MfParams* __restrict__ P,
+                      int64_t M, int64_t N, int64_t cps, int64_t row_blocks, int64_t splits, int64_t pair0) {
+  if (!P->gate || P->bad) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l32 = lane & 31, g = lane >> 5;
+  // XCD-aware renumbering, as in gauss_sum_mf_kernel
+  const uint32_t wg = blockIdx.x, total = gridDim.x;
+  const uint32_t per = total / kXcds, extra = total % kXcds, xcd = wg % kXcds;
+  const int64_t pair = pair0 + xcd * per + (xcd < extra ? xcd : extra) + wg / kXcds;
+  const int64_t split = pair / row_blocks;
+  const int64_t j0 = split * cps;
+  const int64_t j1 = (j0 + cps < N) ? j0 + cps : N;
+  const int64_t base = ((int64_t)(pair % row_blocks) * (kBlock / 64) + wave) * 32 * RT;
+  const half8 zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
+
+  // The chunk totals live in LDS, each lane in its own slots (32 KB per workgroup at RT = 2):
+  // with them in registers the sweep needs 149 VGPRs and runs three waves per SIMD, with them
+  // here 112 VGPRs and four (1M sum 93.4 -> 91.9 ms).
+  half8 ahi[RT], alo[RT];
+  float part[RT][16];
+  __shared__ float sacc[kBlock / 64][RT][16][64];
+#pragma unroll
+  for (int r = 0; r < RT; ++r) {
+    int64_t i = base + r * 32 + l32;
+    i = i < M ? i : M - 1;
+    ahi[r] = g == 0 ? rhi[i] : zero8;
+    alo[r] = rlo[i * 2 + g];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      part[r][q] = 0.0f;
+      sacc[wave][r][q][lane] = 0.0f;
+    }
+  }
+  struct Ops {
+    half8 h, l;
+    float w;
+  };
+  auto load = [&](int64_t jt, Ops& o) {
+    o.h = chi[jt + l32];
+    o.l = clo[(jt + l32) * 2 + g];
+    o.w = bpad[jt + l32];
+  };
+  const f32x16 zero16 = {};
+  auto tile = [&](const Ops& o) {
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+      f32x16 e = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi[r], o.h, zero16, 0, 0, 0);
+      e = __builtin_amdgcn_mfma_f32_32x32x16_f16(alo[r], o.l, e, 0, 0, 0);
+#pragma unroll
+      for (int q = 0; q < 16; ++q) part[r][q] = fmaf(exp2_hw(e[q]), o.w, part[r][q]);
+    }
+  };
+  auto fold = [&]() {
+#pragma unroll
+    for (int r = 0; r < RT; ++r)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        sacc[wave][r][q][lane] += part[r][q];
+        part[r][q] = 0.0f;
+      }
+  };
+  // Two tiles per trip with alternating operand sets, each load one tile ahead of its use. The
+  // column range is whole 32-column tiles (splits are multiples of 32 columns and the tables are
+  // padded to a multiple of 32); an odd last tile is reduced after the loop.
+  constexpr int kChunkTiles32 = kChunk / 32;
+  const int64_t ntiles = j1 > j0 ? (j1 - j0 + 31) / 32 : 0;
+  Ops A, B;
+  if (ntiles > 0) load(j0, A);
+  int tiles = 0;
+  int64_t t = 0;
+  for (; t + 2 <= ntiles; t += 2) {
+    const int64_t ja = j0 + t * 32;
+    load(ja + 32, B);
+    tile(A);
+    load(t + 2 < ntiles ? ja + 64 : ja, A);
+    tile(B);
+    tiles += 2;
+    if (tiles == kChunkTiles32) {
+      tiles = 0;
+      fold();
+    }
+  }
+  if (t < ntiles) tile(A);
+  fold();
+  // add the 32 per-column partials of each row (the lanes of one half-wave)
+#pragma unroll
+  for (int r = 0; r < RT; ++r)
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      float v = sacc[wave][r][q][lane];
+      v += __shfl_xor(v, 1);
+      v += __shfl_xor(v, 2);
+      v += __shfl_xor(v, 4);
+      v += __shfl_xor(v, 8);
+      v += __shfl_xor(v, 16);
+      part[r][q] = v;
+    }
+  float* dst = out + split * M;
+  const bool scaled = rscale && splits == 1;
+#pragma unroll
+  for (int r = 0; r < RT; ++r)
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int64_t i = base + r * 32 + 8 * (q / 4) + 4 * g + (q % 4);
+      if (l32 == q && i < M) {
+        const float sc = scaled ? rscale[i] : 1.0f;
+        dst[i] = sc * (exp2f(rrem[i]) * part[r][q]);
       }
     }
 }
@@ -1167,6 +1340,32 @@ hipError_t sweep_c(char* r, const MfLayout& L, float* dst, const float* rscale, 
   return sweep_rt<C, 2, 2>(r, L, dst, rscale, M, N, p, s);
 }
 
+// The 32 x 32 form: RT32 tiles of 32 rows per wave, i.e. rt / 2 in units of 16 rows.
+template <int RT32>
+hipError_t sweep32(char* r, const MfLayout& L, float* dst, const float* rscale, int64_t M, int64_t N, const Plan& p,
+                   hipStream_t s) {
+  const int64_t pairs = p.mf_row_blocks * p.splits;
+  for (int64_t pair0 = 0; pair0 < pairs; pair0 += kMaxLaunch) {
+    const int64_t n = pairs - pair0 < kMaxLaunch ? pairs - pair0 : kMaxLaunch;
+    gauss_sum_mf32_kernel<RT32><<<(unsigned)n, kBlock, 0, s>>>(
+        reinterpret_cast<const half8*>(r + L.rhi), reinterpret_cast<const half8*>(r + L.rlo),
+        reinterpret_cast<const float*>(r + L.rA), reinterpret_cast<const half8*>(r + L.chi),
+        reinterpret_cast<const half8*>(r + L.clo), reinterpret_cast<const float*>(r + L.bpad), dst, rscale,
+        reinterpret_cast<const MfParams*>(r), M, N, p.cols_per_split, p.mf_row_blocks, p.splits, pair0);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+template <int RT32>
+int occupancy32() {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gauss_sum_mf32_kernel<RT32>, kBlock, 0) != hipSuccess || n < 1)
+    n = 4;
+  return n;
+}
+
 template <int RT, int NH, int NL>
 hipError_t sweep_lse(char* r, const MfLayout& L, float* out, LsePartial* part, int64_t M, int64_t N, const Plan& p,
                      hipStream_t s) {
@@ -1249,6 +1448,8 @@ size_t mf_region_bytes(int64_t M, int64_t N, int D, int W, bool grad) {
 
 const int* mf_decision(const void* region) { return &static_cast<const lowd::MfParams*>(region)->gate; }
 
+bool mf_sum_square(int D, int C, int rt) { return D >= 1 && D <= 3 && C == 1 && (rt == 2 || rt == 4); }
+
 int mf_rows_per_lane(int op, int D, int C) {
   if (op == 3) return lowd::grad_rt(D);
   return lowd::max_rt(op == 1 ? 0 : C);
@@ -1283,6 +1484,14 @@ int mf_occupancy(int op, int D, int C, int rt) {
     cache_grad[D].store(n, std::memory_order_relaxed);
     return n;
   }
+  if (op == 0 && mf_sum_square(D, C, rt)) {
+    static std::atomic<int> cache32[5];
+    int n = cache32[rt].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    n = rt == 4 ? lowd::occupancy32<2>() : lowd::occupancy32<1>();
+    cache32[rt].store(n, std::memory_order_relaxed);
+    return n;
+  }
   std::atomic<int>& slot = cache[wide][C][rt];
   int n = slot.load(std::memory_order_relaxed);
   if (n > 0) return n;
@@ -1312,7 +1521,7 @@ int mf_occupancy(int op, int D, int C, int rt) {
 }
 
 hipError_t launch_mf_prepare(const float* x, const float* y, const float* b, bool with_y, double* cols, void* region,
-                             int64_t M, int64_t N, int D, int C, double c2, hipStream_t s, bool set_aside) {
+                             int64_t M, int64_t N, int D, int C, double c2, hipStream_t s, bool set_aside, bool square) {
   using namespace lowd;
   char* r = static_cast<char*>(region);
   const MfLayout L = mf_layout(M, N, D, C + (with_y ? D : 0), with_y);
@@ -1332,14 +1541,15 @@ hipError_t launch_mf_prepare(const float* x, const float* y, const float* b, boo
   half8* chi = reinterpret_cast<half8*>(r + L.chi);
   half8* clo = reinterpret_cast<half8*>(r + L.clo);
   float* bpad = reinterpret_cast<float*>(r + L.bpad);
+  const int sq = (square && L.NH == 1 && L.NL == 1 && !with_y && D <= 3) ? 1 : 0;
   if (L.NH == 1 && L.NL == 1)
     mf_prep_kernel<1, 1><<<(unsigned)(rb + cb), kBlock, 0, s>>>(
         x, y, b, C, with_y ? 1 : 0, cols, rhi, rlo, rA, chi, clo, bpad, parts, samples, (int)nb * spw, (int)nb, M, N, L.Npad, D, c2, rb,
-        set_aside ? 1 : 0, aside, aside + kMaxAside, P);
+        set_aside ? 1 : 0, sq, aside, aside + kMaxAside, P);
   else
     mf_prep_kernel<2, 2><<<(unsigned)(rb + cb), kBlock, 0, s>>>(
         x, y, b, C, with_y ? 1 : 0, cols, rhi, rlo, rA, chi, clo, bpad, parts, samples, (int)nb * spw, (int)nb, M, N, L.Npad, D, c2, rb,
-        set_aside ? 1 : 0, aside, aside + kMaxAside, P);
+        set_aside ? 1 : 0, 0, aside, aside + kMaxAside, P);
   return hipGetLastError();
 }
 
@@ -1411,6 +1621,8 @@ hipError_t launch_mf_sum(const float* rscale, float* dst, void* region, int64_t 
   using namespace lowd;
   char* r = static_cast<char*>(region);
   const MfLayout L = mf_layout(M, N, D, C);
+  if (mf_sum_square(D, C, p.mf_rt))
+    return p.mf_rt == 4 ? sweep32<2>(r, L, dst, rscale, M, N, p, s) : sweep32<1>(r, L, dst, rscale, M, N, p, s);
 #define KEOPS_MF_C(Cv) sweep_c<Cv>(r, L, dst, rscale, M, N, p, s)
   KEOPS_SWITCH_C(C, KEOPS_MF_C)
 #undef KEOPS_MF_C
