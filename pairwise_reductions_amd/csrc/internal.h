@@ -63,6 +63,9 @@ int mf_occupancy(int op, int D, int C, int rt);  // resident workgroups per CU o
 // The single-channel sum at D <= 3 runs on 32 x 32 tiles when the plan gives 2 or 4 row tiles
 // of 16 per wave (the preparation must then write that layout: square = true).
 bool mf_sum_square(int D, int C, int rt);
+// The log-sum-exp likewise (D <= 3); its rows far from every column are then recomputed by
+// launch_mf_lse_fix after the split combine.
+bool mf_lse_square(int D, int rt);
 int knn_occupancy(int D, int K);                 // resident workgroups per CU of the argKmin sweep
 // set_aside (the Gauss sum only): a box too wide for the matrix cores may be replaced by one
 // around the sample median that sets a few outlying points aside (launch_mf_finish then sums
@@ -84,6 +87,10 @@ hipError_t launch_mf_sum(const float* rscale, float* dst, void* region, int64_t 
 // log-sum-exp on the matrix cores: out (one split) or per-split (m, l) pairs in `partial`
 hipError_t launch_mf_lse(float* out, void* partial, void* region, int64_t M, int64_t N, int D,
                          const Plan& p, hipStream_t s);
+// Recomputes, from a float64 exponent, the rows of a finished matrix-core log-sum-exp whose value
+// is below 64 ln 2 or not finite (only after the 32 x 32 form; the decision in region gates it).
+hipError_t launch_mf_lse_fix(const float* x, const float* y, float* out, void* region, int64_t M, int64_t N, int D,
+                             double c2, const Plan& p, hipStream_t s);
 // log-sum-exp: prepares as launch_gauss_sum_lowd (no weights) and runs the matrix-core or the
 // float64 sweep, chosen on the device.
 hipError_t launch_lse_lowd(const float* x, const float* y, double* cols, float* out,

@@ -862,7 +862,8 @@ hipError_t launch_knn_lowd(const float* x, const float* y, const float* w, doubl
   // less than the fused one on this chip), the fused float64 sweep otherwise.
   const int* mf = nullptr;
   if (with_lse && mf_lse && !w) {
-    e = launch_mf_prepare(x, y, nullptr, false, nullptr, mf_lse->region, M, N, D, 0, c2, s);
+    e = launch_mf_prepare(x, y, nullptr, false, nullptr, mf_lse->region, M, N, D, 0, c2, s, false,
+                          mf_lse_square(D, mf_lse->plan->mf_rt));
     if (e != hipSuccess) return e;
     mf = mf_decision(mf_lse->region);
   }
@@ -873,9 +874,13 @@ hipError_t launch_knn_lowd(const float* x, const float* y, const float* w, doubl
   if (e != hipSuccess || !mf) return e;
   const Plan& lp = *mf_lse->plan;
   e = launch_mf_lse(lse_out, lp.splits > 1 ? mf_lse->partial : nullptr, mf_lse->region, M, N, D, lp, s);
-  if (e != hipSuccess || lp.splits == 1) return e;
-  return lowd::launch_combine_lse(static_cast<const lowd::LsePartial*>(mf_lse->partial), lse_out, M, lp.splits, s,
-                                  mf, 1);
+  if (e != hipSuccess) return e;
+  if (lp.splits > 1) {
+    e = lowd::launch_combine_lse(static_cast<const lowd::LsePartial*>(mf_lse->partial), lse_out, M, lp.splits, s,
+                                 mf, 1);
+    if (e != hipSuccess) return e;
+  }
+  return launch_mf_lse_fix(x, y, lse_out, mf_lse->region, M, N, D, c2, lp, s);
 }
 
 }  // namespace keops

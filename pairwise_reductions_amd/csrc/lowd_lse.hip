@@ -138,7 +138,7 @@ hipError_t lse_d(const float* x, const float* y, const double* cols, float* out,
 
 hipError_t launch_lse_lowd(const float* x, const float* y, double* cols, float* out, double* partial, void* mf,
                            int64_t M, int64_t N, int D, double c2, const Plan& p, hipStream_t s) {
-  hipError_t e = launch_mf_prepare(x, y, nullptr, false, cols, mf, M, N, D, 0, c2, s);
+  hipError_t e = launch_mf_prepare(x, y, nullptr, false, cols, mf, M, N, D, 0, c2, s, false, mf_lse_square(D, p.mf_rt));
   if (e != hipSuccess) return e;
   const int* skip = mf_decision(mf);
   {
@@ -149,8 +149,12 @@ hipError_t launch_lse_lowd(const float* x, const float* y, double* cols, float* 
   }
   if (e != hipSuccess) return e;
   e = launch_mf_lse(out, partial, mf, M, N, D, p, s);
-  if (e != hipSuccess || p.splits == 1) return e;
-  return lowd::launch_combine_lse(reinterpret_cast<const lowd::LsePartial*>(partial), out, M, p.splits, s);
+  if (e != hipSuccess) return e;
+  if (p.splits > 1) {
+    e = lowd::launch_combine_lse(reinterpret_cast<const lowd::LsePartial*>(partial), out, M, p.splits, s);
+    if (e != hipSuccess) return e;
+  }
+  return launch_mf_lse_fix(x, y, out, mf, M, N, D, c2, p, s);
 }
 
 }  // namespace keops

@@ -974,6 +974,171 @@ lse_mf_kernel(const half8* __restrict__ rhi, const half8* __restrict__ rlo, cons
     }
 }
 
+// The log-sum-exp on 32 x 32 tiles (operands in the sq layout), with no running shift:
+// l_i = sum_j 2^{e_ij - Al1_i} over the columns [j0, j1) of this split, written as
+// ln(2^{Al1_i} l_i) with one split, else as the split's pair (m, l) = (Al1_i, l_i). The
+// exponent is never positive (its computed value exceeds 0 by a rounding far below 1), so no
+// term overflows; what underflows float32 is negligible for every row whose sum is at least
+// 2^-64 (at most N 2^-126 against it). Rows below that, or with no term at all, are far from
+// every column: lse_fix_kernel recomputes them afterwards. Same tiles and lanes as
+// gauss_sum_mf32_kernel; per 1024 pairs a wave issues 2 MFMAs, 16 exponentials and 16 adds.
+template <int RT>
+__global__ void __launch_bounds__(kBlock)
+lse_mf32_kernel(const half8* __restrict__ rhi, const half8* __restrict__ rlo, const float* __restrict__ rrem,
+                const half8* __restrict__ chi, const half8* __restrict__ clo, float* __restrict__ out,
+                LsePartial* __restrict__ partial, const MfParams* __restrict__ P, int64_t M, int64_t N, int64_t cps,
+                int64_t row_blocks, int64_t splits, int64_t pair0) {
+  if (!P->gate || P->bad) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l32 = lane & 31, g = lane >> 5;
+  const uint32_t wg = blockIdx.x, total = gridDim.x;
+  const uint32_t per = total / kXcds, extra = total % kXcds, xcd = wg % kXcds;
+  const int64_t pair = pair0 + xcd * per + (xcd < extra ? xcd : extra) + wg / kXcds;
+  const int64_t split = pair / row_blocks;
+  const int64_t j0 = split * cps;
+  const int64_t j1 = (j0 + cps < N) ? j0 + cps : N;
+  const int64_t base = ((int64_t)(pair % row_blocks) * (kBlock / 64) + wave) * 32 * RT;
+  const half8 zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
+
+  half8 ahi[RT], alo[RT];
+  float l[RT][16];
+#pragma unroll
+  for (int r = 0; r < RT; ++r) {
+    int64_t i = base + r * 32 + l32;
+    i = i < M ? i : M - 1;
+    ahi[r] = g == 0 ? rhi[i] : zero8;
+    alo[r] = rlo[i * 2 + g];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) l[r][q] = 0.0f;
+  }
+  struct Ops {
+    half8 h, l;
+  };
+  auto load = [&](int64_t jt, Ops& o) {
+    o.h = chi[jt + l32];
+    o.l = clo[(jt + l32) * 2 + g];
+  };
+  const f32x16 zero16 = {};
+  auto tile = [&](const Ops& o) {
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+      f32x16 e = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi[r], o.h, zero16, 0, 0, 0);
+      e = __builtin_amdgcn_mfma_f32_32x32x16_f16(alo[r], o.l, e, 0, 0, 0);
+#pragma unroll
+      for (int q = 0; q < 16; ++q) l[r][q] += exp2_hw(e[q]);
+    }
+  };
+  const int64_t ntiles = j1 > j0 ? (j1 - j0 + 31) / 32 : 0;
+  Ops A, B;
+  if (ntiles > 0) load(j0, A);
+  int64_t t = 0;
+  for (; t + 2 <= ntiles; t += 2) {
+    const int64_t ja = j0 + t * 32;
+    load(ja + 32, B);
+    tile(A);
+    load(t + 2 < ntiles ? ja + 64 : ja, A);
+    tile(B);
+  }
+  if (t < ntiles) tile(A);
+#pragma unroll
+  for (int r = 0; r < RT; ++r)
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      float v = l[r][q];
+      v += __shfl_xor(v, 1);
+      v += __shfl_xor(v, 2);
+      v += __shfl_xor(v, 4);
+      v += __shfl_xor(v, 8);
+      v += __shfl_xor(v, 16);
+      l[r][q] = v;
+    }
+  const bool last = splits == 1;
+#pragma unroll
+  for (int r = 0; r < RT; ++r)
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int64_t i = base + r * 32 + 8 * (q / 4) + 4 * g + (q % 4);
+      if (l32 == q && i < M) {
+        if (last) {
+          out[i] = (float)(((double)rrem[i] + (double)log2f(l[r][q])) * M_LN2);
+        } else {
+          LsePartial pp;
+          pp.m = (double)rrem[i];
+          pp.l = l[r][q];
+          pp.pad = 0.0f;
+          partial[split * M + i] = pp;
+        }
+      }
+    }
+}
+
+// After lse_mf32_kernel (and the split combine): rows whose log-sum-exp came out below
+// 64 ln 2 (sum below 2^-64), or not finite, are recomputed from a float64 exponent. Each
+// workgroup looks at its 256 rows and, for each row flagged, all its threads take a fixed stride
+// of the columns with a running maximum (float64), merged in a fixed tree:
+// out_i = ln sum_j exp(-c2 ln 2 |x_i - y_j|^2) exactly in float64 arithmetic up to the final
+// rounding. With no far row every workgroup returns after reading its rows.
+template <int D>
+__global__ void __launch_bounds__(kBlock)
+lse_fix_kernel(const float* __restrict__ x, const float* __restrict__ y, float* __restrict__ out,
+               const MfParams* __restrict__ P, int64_t M, int64_t N, double c2) {
+  if (!P->gate || P->bad) return;
+  __shared__ int rows[kBlock];
+  __shared__ int nflag;
+  __shared__ double rm[kBlock], rl[kBlock];
+  const float kFloor = (float)(-64.0 * M_LN2);
+  if (threadIdx.x == 0) nflag = 0;
+  __syncthreads();
+  const int64_t i0 = (int64_t)blockIdx.x * kBlock;
+  {
+    const int64_t i = i0 + threadIdx.x;
+    if (i < M && !(out[i] >= kFloor)) rows[atomicAdd(&nflag, 1)] = (int)threadIdx.x;
+  }
+  __syncthreads();
+  const int nf = nflag;
+  if (nf == 0) return;
+  // (the rows are recorded in an arbitrary order; each row's result does not depend on it)
+  for (int k = 0; k < nf; ++k) {
+    const int64_t i = i0 + rows[k];
+    double xi[D];
+#pragma unroll
+    for (int d = 0; d < D; ++d) xi[d] = (double)x[i * D + d];
+    double m = -INFINITY, lv = 0.0;
+    for (int64_t j = threadIdx.x; j < N; j += kBlock) {
+      double d2 = 0.0;
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        const double t = xi[d] - (double)y[j * D + d];
+        d2 = fma(t, t, d2);
+      }
+      const double e = -c2 * d2;  // base 2
+      if (!(e > -INFINITY)) continue;  // no contribution
+      if (e > m) {
+        lv = lv * exp2(m - e) + 1.0;
+        m = e;
+      } else {
+        lv += exp2(e - m);
+      }
+    }
+    rm[threadIdx.x] = m;
+    rl[threadIdx.x] = lv;
+    __syncthreads();
+    for (int h = kBlock / 2; h > 0; h >>= 1) {
+      if ((int)threadIdx.x < h) {
+        const double ma = rm[threadIdx.x], mb = rm[threadIdx.x + h];
+        const double mm = ma > mb ? ma : mb;
+        const double la = ma == -INFINITY ? 0.0 : rl[threadIdx.x] * exp2(ma - mm);
+        const double lb = mb == -INFINITY ? 0.0 : rl[threadIdx.x + h] * exp2(mb - mm);
+        rm[threadIdx.x] = mm;
+        rl[threadIdx.x] = la + lb;
+      }
+      __syncthreads();
+    }
+    if (threadIdx.x == 0) out[i] = (float)((rm[0] + log2(rl[0])) * M_LN2);
+    __syncthreads();
+  }
+}
+
 // Gradient with respect to x, one channel ("Kernel Operations on the GPU, with Autodiff, without
 // Memory Overflows": the derivative of a reduction is a reduction over the same pairs):
 //   out_i = -(g_i / sigma^2) sum_j k_ij b_j (x_i - y_j)
@@ -1359,6 +1524,30 @@ hipError_t sweep32(char* r, const MfLayout& L, float* dst, const float* rscale, 
 }
 
 template <int RT32>
+hipError_t sweep32_lse(char* r, const MfLayout& L, float* out, LsePartial* part, int64_t M, int64_t N, const Plan& p,
+                       hipStream_t s) {
+  const int64_t pairs = p.mf_row_blocks * p.splits;
+  for (int64_t pair0 = 0; pair0 < pairs; pair0 += kMaxLaunch) {
+    const int64_t n = pairs - pair0 < kMaxLaunch ? pairs - pair0 : kMaxLaunch;
+    lse_mf32_kernel<RT32><<<(unsigned)n, kBlock, 0, s>>>(
+        reinterpret_cast<const half8*>(r + L.rhi), reinterpret_cast<const half8*>(r + L.rlo),
+        reinterpret_cast<const float*>(r + L.rA), reinterpret_cast<const half8*>(r + L.chi),
+        reinterpret_cast<const half8*>(r + L.clo), out, part, reinterpret_cast<const MfParams*>(r), M, N,
+        p.cols_per_split, p.mf_row_blocks, p.splits, pair0);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+template <int RT32>
+int occupancy32_lse() {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, lse_mf32_kernel<RT32>, kBlock, 0) != hipSuccess || n < 1) n = 4;
+  return n;
+}
+
+template <int RT32>
 int occupancy32() {
   int n = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gauss_sum_mf32_kernel<RT32>, kBlock, 0) != hipSuccess || n < 1)
@@ -1449,6 +1638,7 @@ size_t mf_region_bytes(int64_t M, int64_t N, int D, int W, bool grad) {
 const int* mf_decision(const void* region) { return &static_cast<const lowd::MfParams*>(region)->gate; }
 
 bool mf_sum_square(int D, int C, int rt) { return D >= 1 && D <= 3 && C == 1 && (rt == 2 || rt == 4); }
+bool mf_lse_square(int D, int rt) { return D >= 1 && D <= 3 && (rt == 2 || rt == 4); }
 
 int mf_rows_per_lane(int op, int D, int C) {
   if (op == 3) return lowd::grad_rt(D);
@@ -1484,12 +1674,13 @@ int mf_occupancy(int op, int D, int C, int rt) {
     cache_grad[D].store(n, std::memory_order_relaxed);
     return n;
   }
-  if (op == 0 && mf_sum_square(D, C, rt)) {
-    static std::atomic<int> cache32[5];
-    int n = cache32[rt].load(std::memory_order_relaxed);
+  if ((op == 0 && mf_sum_square(D, C, rt)) || (op == 1 && mf_lse_square(D, rt))) {
+    static std::atomic<int> cache32[2][5];
+    int n = cache32[op][rt].load(std::memory_order_relaxed);
     if (n > 0) return n;
-    n = rt == 4 ? lowd::occupancy32<2>() : lowd::occupancy32<1>();
-    cache32[rt].store(n, std::memory_order_relaxed);
+    if (op == 0) n = rt == 4 ? lowd::occupancy32<2>() : lowd::occupancy32<1>();
+    else n = rt == 4 ? lowd::occupancy32_lse<2>() : lowd::occupancy32_lse<1>();
+    cache32[op][rt].store(n, std::memory_order_relaxed);
     return n;
   }
   std::atomic<int>& slot = cache[wide][C][rt];
@@ -1602,8 +1793,25 @@ hipError_t launch_mf_lse(float* out, void* partial, void* region, int64_t M, int
   char* r = static_cast<char*>(region);
   const MfLayout L = mf_layout(M, N, D, 0);
   LsePartial* part = static_cast<LsePartial*>(partial);
+  if (mf_lse_square(D, p.mf_rt))
+    return p.mf_rt == 4 ? sweep32_lse<2>(r, L, out, part, M, N, p, s) : sweep32_lse<1>(r, L, out, part, M, N, p, s);
   if (L.NH == 1 && L.NL == 1) return sweep_lse_rt<1, 1>(r, L, out, part, M, N, p, s);
   return sweep_lse_rt<2, 2>(r, L, out, part, M, N, p, s);
+}
+
+hipError_t launch_mf_lse_fix(const float* x, const float* y, float* out, void* region, int64_t M, int64_t N, int D,
+                             double c2, const Plan& p, hipStream_t s) {
+  using namespace lowd;
+  if (!mf_lse_square(D, p.mf_rt) || M <= 0) return hipSuccess;
+  const MfParams* P = static_cast<const MfParams*>(region);
+  const unsigned nb = (unsigned)ceil_div(M, kBlock);
+  switch (D) {
+    case 1: lse_fix_kernel<1><<<nb, kBlock, 0, s>>>(x, y, out, P, M, N, c2); break;
+    case 2: lse_fix_kernel<2><<<nb, kBlock, 0, s>>>(x, y, out, P, M, N, c2); break;
+    case 3: lse_fix_kernel<3><<<nb, kBlock, 0, s>>>(x, y, out, P, M, N, c2); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_mf_grad(const float* x, const float* g, float* dst, float inv_sigma2, void* region, int64_t M,

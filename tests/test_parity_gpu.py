@@ -246,6 +246,28 @@ def test_lse_far_rows_and_empty():
     assert np.all(np.isneginf(got))
 
 
+def test_lse_some_far_rows_among_near_ones():
+    """Rows far from every column scattered among ordinary rows, over several column splits: the
+    far ones (log-sum-exp below 64 ln 2) are recomputed after the matrix-core sweep, the others
+    keep its result."""
+    import pairwise_reductions_amd as pr
+    _announce("lse_mixed_far")
+    rng = np.random.default_rng(23)
+    y = rng.random((40_000, 3)).astype(np.float32)
+    x = rng.random((3000, 3)).astype(np.float32)
+    x[::7] += np.float32(2.5)          # every seventh row far outside the columns' cube
+    x[5::97] = np.float32(1.3)         # a few just outside it (sums near 2^-64)
+    for sigma in (0.05, 0.1):
+        sig = float(np.float32(sigma))
+        got = _host(pr.lse(_dev(x), _dev(y), sig)).astype(np.float64)
+        want = oracle.logsumexp_reduction(x, y, sig, workers=8)
+        err = np.abs(got - want)
+        assert np.all(err <= lse_bound(want)), f"sigma {sigma}: max error {err.max():.3e}"
+        idx, flse = pr.argkmin_lse(_dev(x), _dev(y), 4, sig)
+        err = np.abs(_host(flse).astype(np.float64) - want)
+        assert np.all(err <= lse_bound(want)), f"argkmin_lse sigma {sigma}: max error {err.max():.3e}"
+
+
 ARGK_SHAPES = [(1, 1, 3, 1), (257, 1000, 3, 10), (1025, 513, 1, 4), (700, 2000, 2, 16),
                (513, 1500, 8, 32), (100, 100_003, 3, 10), (50_001, 777, 3, 10), (300, 64, 3, 64),
                (200, 5000, 3, 64), (333, 20, 5, 20), (1000, 3000, 3, 3),
