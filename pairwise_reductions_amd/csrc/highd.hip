@@ -69,7 +69,8 @@ weight_norm_max_kernel(const T* __restrict__ w, const float* __restrict__ cscale
 //   kMode kNormGrad: the general form, gradient layout, plus the key-permuted columns yp and,
 //                    when wpl is given, the weights key-permuted again for the fused second
 //                    output of the gradient sweep.
-// Layouts: forward wp[t][j/32][c][key_slot(j%32)] for c < Cw (the A operand of O^T);
+// Layouts: forward wp[t][j/32][c][key_slot(j%32)] for c < Cw (the A operand of O^T; with
+// perm32 the slot32_key() order of the 32x32 tiles instead);
 // gradient wp[t][j][c] for c < Cw (the A operand of dP^T) and yp[t][j/32][ch][key_slot(j%32)]
 // = k[t][j][ch] for ch < D, 1 at ch = Dp, else 0. Keys past N get beta = -inf and zeros.
 enum { kCopy = 0, kNormFwd = 1, kNormGrad = 2 };
@@ -81,7 +82,7 @@ __global__ void __launch_bounds__(256)
 col_prep_kernel(const TK* __restrict__ k, const T* __restrict__ w, const float* __restrict__ cscale,
                 const float* __restrict__ nmax, float* __restrict__ beta, _Float16* __restrict__ wp,
                 _Float16* __restrict__ wpl, _Float16* __restrict__ yp, int64_t N, int64_t Npad, int D, int Dp, int C,
-                int Cw, float cs) {
+                int Cw, float cs, int perm32) {
   __shared__ float sk[32][kMaxPrepD + 1];
   __shared__ float sw[32][kMaxPrepC + 1];
   __shared__ float sinv[32];
@@ -170,7 +171,7 @@ col_prep_kernel(const TK* __restrict__ k, const T* __restrict__ w, const float* 
     _Float16* dst = wp + (t * Npad + j0) * Cw;
     _Float16* dsl = wpl ? wpl + (t * Npad + j0) * Cw : nullptr;
     for (int e = tid; e < 32 * Cw; e += 256) {
-      const int c = e / 32, key = slot_key(e % 32);
+      const int c = e / 32, key = perm32 ? hd::slot32_key(e % 32) : slot_key(e % 32);
       const float v = c < C ? sw[key][c] * sinv[key] : 0.0f;
       const _Float16 h = (_Float16)v;
       dst[e] = h;
@@ -418,28 +419,28 @@ namespace {
 template <typename TK, typename T>
 hipError_t fwd_prep_general(const TK* k, const T* w, const float* cscale, float* nmax, float* beta, _Float16* vp,
                             _Float16* vpl, int64_t B, int64_t N, int64_t Npad, int D, int C, int Cp, float cs,
-                            hipStream_t s) {
+                            int perm32, hipStream_t s) {
   hipError_t e = weight_norm_max(w, cscale, nmax, B, N, C, s);
   if (e != hipSuccess) return e;
   col_prep_kernel<TK, T, kNormFwd><<<dim3((unsigned)(Npad / 32), (unsigned)B), 256, 0, s>>>(
-      k, w, cscale, nmax, beta, vp, vpl, nullptr, N, Npad, D, 0, C, Cp, cs);
+      k, w, cscale, nmax, beta, vp, vpl, nullptr, N, Npad, D, 0, C, Cp, cs, perm32);
   return hipGetLastError();
 }
 
 template <typename TK>
 hipError_t fwd_prep_general_w(const TK* k, const void* w, ElemType bt, const float* cscale, float* nmax, float* beta,
                               _Float16* vp, _Float16* vpl, int64_t B, int64_t N, int64_t Npad, int D, int C, int Cp,
-                              float cs, hipStream_t s) {
+                              float cs, int perm32, hipStream_t s) {
   switch (bt) {
     case kElemF16:
       return fwd_prep_general(k, static_cast<const _Float16*>(w), cscale, nmax, beta, vp, vpl, B, N, Npad, D, C, Cp,
-                              cs, s);
+                              cs, perm32, s);
     case kElemBF16:
       return fwd_prep_general(k, static_cast<const bf16_t*>(w), cscale, nmax, beta, vp, vpl, B, N, Npad, D, C, Cp,
-                              cs, s);
+                              cs, perm32, s);
     case kElemF32:
       return fwd_prep_general(k, static_cast<const float*>(w), cscale, nmax, beta, vp, vpl, B, N, Npad, D, C, Cp, cs,
-                              s);
+                              perm32, s);
   }
   return hipErrorInvalidValue;
 }
@@ -459,21 +460,22 @@ hipError_t launch_gauss_sum_highd(const void* x, const void* y, ElemType xy, con
   float* part = reinterpret_cast<float*>(ws + L.part);
   const float cs = cs_of(sigma);
   const int Cp = hd::padded_channels(C);
+  const int sq = hd::fwd_square(xy == kElemF32, hd::padded_features(D), Cp) ? 1 : 0;
   hipError_t e;
   if (!general) {
     col_prep_kernel<_Float16, _Float16, kCopy><<<dim3((unsigned)(L.sp.Npad / 32), (unsigned)B), 256, 0, s>>>(
         static_cast<const _Float16*>(y), static_cast<const _Float16*>(b), nullptr, nullptr, beta, vp, nullptr,
-        nullptr, N, L.sp.Npad, D, 0, C, Cp, cs);
+        nullptr, N, L.sp.Npad, D, 0, C, Cp, cs, sq);
     e = hipGetLastError();
   } else if (xy == kElemF16) {
     e = fwd_prep_general_w(static_cast<const _Float16*>(y), b, bt, cscale, nmax, beta, vp, vpl, B, N, L.sp.Npad, D,
-                           C, Cp, cs, s);
+                           C, Cp, cs, sq, s);
   } else if (xy == kElemBF16) {
     e = fwd_prep_general_w(static_cast<const bf16_t*>(y), b, bt, cscale, nmax, beta, vp, vpl, B, N, L.sp.Npad, D, C,
-                           Cp, cs, s);
+                           Cp, cs, sq, s);
   } else {
     e = fwd_prep_general_w(static_cast<const float*>(y), b, bt, cscale, nmax, beta, vp, vpl, B, N, L.sp.Npad, D, C,
-                           Cp, cs, s);
+                           Cp, cs, sq, s);
   }
   if (e != hipSuccess) return e;
   hd::FwdArgs a;
@@ -495,7 +497,8 @@ hipError_t launch_gauss_sum_highd(const void* x, const void* y, ElemType xy, con
   a.grid = dim3((unsigned)L.sp.row_blocks, (unsigned)L.sp.splits, (unsigned)B);
   a.stream = s;
   sweep_event(s, true);
-  e = fwd_dispatch(a, xy);
+  if (sq) e = xy == kElemF16 ? hd::fwd32_launch<_Float16>(a) : hd::fwd32_launch<bf16_t>(a);
+  else e = fwd_dispatch(a, xy);
   sweep_event(s, false);
   if (e != hipSuccess || L.sp.splits == 1) return e;
   return combine(part, out, B * M * C, L.sp.splits, s);
@@ -527,13 +530,13 @@ hipError_t launch_gauss_sum_grad_highd(const void* x, const void* y, const void*
     e = weight_norm_max(w, nullptr, nmax, B, N, C, s);
     if (e != hipSuccess) return e;
     col_prep_kernel<_Float16, float, kNormGrad><<<pgrid, 256, 0, s>>>(k, w, nullptr, nmax, beta, bvp, gp, yp, N,
-                                                                      L.sp.Npad, D, Dp, C, Ck, cs);
+                                                                      L.sp.Npad, D, Dp, C, Ck, cs, 0);
   } else {
     const _Float16* w = static_cast<const _Float16*>(bv);
     e = weight_norm_max(w, nullptr, nmax, B, N, C, s);
     if (e != hipSuccess) return e;
     col_prep_kernel<_Float16, _Float16, kNormGrad><<<pgrid, 256, 0, s>>>(k, w, nullptr, nmax, beta, bvp, gp, yp,
-                                                                         N, L.sp.Npad, D, Dp, C, Ck, cs);
+                                                                         N, L.sp.Npad, D, Dp, C, Ck, cs, 0);
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;

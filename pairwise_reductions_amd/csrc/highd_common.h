@@ -77,6 +77,18 @@ __host__ __device__ inline int key_slot(int o) {
   const int half = o >> 4, rem = o & 15;
   return 8 * (rem >> 2) + 4 * half + (rem & 3);
 }
+// The same for 32x32x16 MFMA tiles: a lane of 32-lane group g holds keys 8w + 4g + (v & 3)
+// (w = v >> 2, v < 16) of its column of S^T, and the two K = 16 products of P^T take values
+// v < 8 and v >= 8. So slot 16h + 8g + s holds key 16h + 8(s >> 2) + 4g + (s & 3).
+__host__ __device__ inline int slot32_key(int slot) {
+  const int h = slot >> 4, g = (slot >> 3) & 1, s = slot & 7;
+  return 16 * h + 8 * (s >> 2) + 4 * g + (s & 3);
+}
+
+// The forward on 32x32x16 tiles (fwd32_kernel): fp16 or bf16 inputs with D <= 32 and
+// 17 <= C <= 32 (padded to 32 features and 32 channels). Its column weights are stored in the
+// slot32_key() order.
+inline bool fwd_square(bool split, int Dp, int Cp) { return !split && Dp == 32 && Cp == 32; }
 
 // Forward: out[split][t][i][c] = oscale[t] * rscale[t][i] * sum_j Phi_ij vp_j[c] over the
 // split's keys, where the stored column weights vp and the key terms beta may carry a per-key
@@ -120,6 +132,8 @@ struct GradArgs {
 
 template <typename TIn, int Dp>
 hipError_t fwd_launch(const FwdArgs& a);
+template <typename TIn>
+hipError_t fwd32_launch(const FwdArgs& a);
 template <int Dp>
 hipError_t grad_launch(const GradArgs& a);
 
