@@ -676,16 +676,16 @@ gauss_sum_mf_kernel(const half8* __restrict__ rhi, const half8* __restrict__ rlo
     }
 }
 
-// The single-channel sum on 32 x 32 tiles (operands in the sq layout of mf_prep_kernel):
-// out[i] = 2^{Al1_i} sum_j 2^{e_ij - Al1_i} b[j] over the columns [j0, j1) of this split (times
-// rscale[i] with one split), else partial[split][i]. A wave holds RT tiles of 32 rows; lane
-// (g, l) (g = lane / 32, l = lane % 32) feeds row l and K slots 8g..8g+7 of each tile to the
+// The sum on 32 x 32 tiles (operands in the sq layout of mf_prep_kernel), C <= 4 channels:
+// out[i][c] = 2^{Al1_i} sum_j 2^{e_ij - Al1_i} b[j][c] over the columns [j0, j1) of this split
+// (times rscale[i] with one split), else partial[split][i][c]. A wave holds RT tiles of 32 rows;
+// lane (g, l) (g = lane / 32, l = lane % 32) feeds row l and K slots 8g..8g+7 of each tile to the
 // MFMA and gets back the exponents of rows 8(q / 4) + 4g + q % 4 (q < 16) against column l of
 // the current 32-column tile. Lanes keep per-column partial sums (folded into the totals every
 // kChunk columns); the 32 lanes of a row group add theirs at the end.
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-template <int RT>
+template <int RT, int C>
 __global__ void __launch_bounds__(kBlock)
 gauss_sum_mf32_kernel(const half8* __restrict__ rhi, const half8* __restrict__ rlo, const float* __restrict__ rrem,
                       const half8* __restrict__ chi, const half8* __restrict__ clo, const float* __restrict__ bpad,
@@ -704,12 +704,15 @@ gauss_sum_mf32_kernel(const half8* __restrict__ rhi, const half8* __restrict__ r
   const int64_t base = ((int64_t)(pair % row_blocks) * (kBlock / 64) + wave) * 32 * RT;
   const half8 zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
 
-  // The chunk totals live in LDS, each lane in its own slots (32 KB per workgroup at RT = 2):
-  // with them in registers the sweep needs 149 VGPRs and runs three waves per SIMD, with them
-  // here 112 VGPRs and four (1M sum 93.4 -> 91.9 ms).
+  // With one channel the chunk totals live in LDS, each lane in its own slots (32 KB per
+  // workgroup at RT = 2): with them in registers the sweep needs 149 VGPRs and runs three waves
+  // per SIMD, with them here 112 VGPRs and four (1M sum 93.4 -> 91.9 ms). With more channels
+  // (one row tile) they stay in registers.
+  constexpr bool kLds = C == 1;
   half8 ahi[RT], alo[RT];
-  float part[RT][16];
-  __shared__ float sacc[kBlock / 64][RT][16][64];
+  float part[RT][16][C];
+  float acc[kLds ? 1 : RT][kLds ? 1 : 16][C];
+  __shared__ float sacc[kBlock / 64][kLds ? RT : 1][kLds ? 16 : 1][64];
 #pragma unroll
   for (int r = 0; r < RT; ++r) {
     int64_t i = base + r * 32 + l32;
@@ -717,19 +720,23 @@ gauss_sum_mf32_kernel(const half8* __restrict__ rhi, const half8* __restrict__ r
     ahi[r] = g == 0 ? rhi[i] : zero8;
     alo[r] = rlo[i * 2 + g];
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      part[r][q] = 0.0f;
-      sacc[wave][r][q][lane] = 0.0f;
-    }
+    for (int q = 0; q < 16; ++q)
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        part[r][q][c] = 0.0f;
+        if constexpr (kLds) sacc[wave][r][q][lane] = 0.0f;
+        else acc[r][q][c] = 0.0f;
+      }
   }
   struct Ops {
     half8 h, l;
-    float w;
+    float w[C];
   };
   auto load = [&](int64_t jt, Ops& o) {
     o.h = chi[jt + l32];
     o.l = clo[(jt + l32) * 2 + g];
-    o.w = bpad[jt + l32];
+#pragma unroll
+    for (int c = 0; c < C; ++c) o.w[c] = bpad[(jt + l32) * C + c];
   };
   const f32x16 zero16 = {};
   auto tile = [&](const Ops& o) {
@@ -738,17 +745,24 @@ gauss_sum_mf32_kernel(const half8* __restrict__ rhi, const half8* __restrict__ r
       f32x16 e = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi[r], o.h, zero16, 0, 0, 0);
       e = __builtin_amdgcn_mfma_f32_32x32x16_f16(alo[r], o.l, e, 0, 0, 0);
 #pragma unroll
-      for (int q = 0; q < 16; ++q) part[r][q] = fmaf(exp2_hw(e[q]), o.w, part[r][q]);
+      for (int q = 0; q < 16; ++q) {
+        const float k = exp2_hw(e[q]);
+#pragma unroll
+        for (int c = 0; c < C; ++c) part[r][q][c] = fmaf(k, o.w[c], part[r][q][c]);
+      }
     }
   };
   auto fold = [&]() {
 #pragma unroll
     for (int r = 0; r < RT; ++r)
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        sacc[wave][r][q][lane] += part[r][q];
-        part[r][q] = 0.0f;
-      }
+      for (int q = 0; q < 16; ++q)
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+          if constexpr (kLds) sacc[wave][r][q][lane] += part[r][q][c];
+          else acc[r][q][c] += part[r][q][c];
+          part[r][q][c] = 0.0f;
+        }
   };
   // Two tiles per trip with alternating operand sets, each load one tile ahead of its use. The
   // column range is whole 32-column tiles (splits are multiples of 32 columns and the tables are
@@ -777,16 +791,20 @@ gauss_sum_mf32_kernel(const half8* __restrict__ rhi, const half8* __restrict__ r
 #pragma unroll
   for (int r = 0; r < RT; ++r)
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      float v = sacc[wave][r][q][lane];
-      v += __shfl_xor(v, 1);
-      v += __shfl_xor(v, 2);
-      v += __shfl_xor(v, 4);
-      v += __shfl_xor(v, 8);
-      v += __shfl_xor(v, 16);
-      part[r][q] = v;
-    }
-  float* dst = out + split * M;
+    for (int q = 0; q < 16; ++q)
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        float v;
+        if constexpr (kLds) v = sacc[wave][r][q][lane];
+        else v = acc[r][q][c];
+        v += __shfl_xor(v, 1);
+        v += __shfl_xor(v, 2);
+        v += __shfl_xor(v, 4);
+        v += __shfl_xor(v, 8);
+        v += __shfl_xor(v, 16);
+        part[r][q][c] = v;
+      }
+  float* dst = out + split * M * C;
   const bool scaled = rscale && splits == 1;
 #pragma unroll
   for (int r = 0; r < RT; ++r)
@@ -794,8 +812,9 @@ gauss_sum_mf32_kernel(const half8* __restrict__ rhi, const half8* __restrict__ r
     for (int q = 0; q < 16; ++q) {
       const int64_t i = base + r * 32 + 8 * (q / 4) + 4 * g + (q % 4);
       if (l32 == q && i < M) {
-        const float sc = scaled ? rscale[i] : 1.0f;
-        dst[i] = sc * (exp2f(rrem[i]) * part[r][q]);
+        const float sc = (scaled ? rscale[i] : 1.0f) * exp2f(rrem[i]);
+#pragma unroll
+        for (int c = 0; c < C; ++c) dst[i * C + c] = sc * part[r][q][c];
       }
     }
 }
@@ -1506,13 +1525,13 @@ hipError_t sweep_c(char* r, const MfLayout& L, float* dst, const float* rscale, 
 }
 
 // The 32 x 32 form: RT32 tiles of 32 rows per wave, i.e. rt / 2 in units of 16 rows.
-template <int RT32>
+template <int RT32, int C>
 hipError_t sweep32(char* r, const MfLayout& L, float* dst, const float* rscale, int64_t M, int64_t N, const Plan& p,
                    hipStream_t s) {
   const int64_t pairs = p.mf_row_blocks * p.splits;
   for (int64_t pair0 = 0; pair0 < pairs; pair0 += kMaxLaunch) {
     const int64_t n = pairs - pair0 < kMaxLaunch ? pairs - pair0 : kMaxLaunch;
-    gauss_sum_mf32_kernel<RT32><<<(unsigned)n, kBlock, 0, s>>>(
+    gauss_sum_mf32_kernel<RT32, C><<<(unsigned)n, kBlock, 0, s>>>(
         reinterpret_cast<const half8*>(r + L.rhi), reinterpret_cast<const half8*>(r + L.rlo),
         reinterpret_cast<const float*>(r + L.rA), reinterpret_cast<const half8*>(r + L.chi),
         reinterpret_cast<const half8*>(r + L.clo), reinterpret_cast<const float*>(r + L.bpad), dst, rscale,
@@ -1547,10 +1566,10 @@ int occupancy32_lse() {
   return n;
 }
 
-template <int RT32>
+template <int RT32, int C>
 int occupancy32() {
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gauss_sum_mf32_kernel<RT32>, kBlock, 0) != hipSuccess || n < 1)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gauss_sum_mf32_kernel<RT32, C>, kBlock, 0) != hipSuccess || n < 1)
     n = 4;
   return n;
 }
@@ -1637,11 +1656,14 @@ size_t mf_region_bytes(int64_t M, int64_t N, int D, int W, bool grad) {
 
 const int* mf_decision(const void* region) { return &static_cast<const lowd::MfParams*>(region)->gate; }
 
-bool mf_sum_square(int D, int C, int rt) { return D >= 1 && D <= 3 && C == 1 && (rt == 2 || rt == 4); }
+bool mf_sum_square(int D, int C, int rt) {
+  return D >= 1 && D <= 3 && ((C == 1 && (rt == 2 || rt == 4)) || (C >= 2 && C <= 4 && rt == 2));
+}
 bool mf_lse_square(int D, int rt) { return D >= 1 && D <= 3 && (rt == 2 || rt == 4); }
 
 int mf_rows_per_lane(int op, int D, int C) {
   if (op == 3) return lowd::grad_rt(D);
+  if (op == 0 && D <= 3 && C >= 2 && C <= 4) return 2;  // one 32-row tile of the 32 x 32 form
   return lowd::max_rt(op == 1 ? 0 : C);
 }
 
@@ -1675,12 +1697,15 @@ int mf_occupancy(int op, int D, int C, int rt) {
     return n;
   }
   if ((op == 0 && mf_sum_square(D, C, rt)) || (op == 1 && mf_lse_square(D, rt))) {
-    static std::atomic<int> cache32[2][5];
-    int n = cache32[op][rt].load(std::memory_order_relaxed);
+    static std::atomic<int> cache32[2][5][5];
+    const int cc = op == 0 ? C : 0;
+    int n = cache32[op][rt][cc].load(std::memory_order_relaxed);
     if (n > 0) return n;
-    if (op == 0) n = rt == 4 ? lowd::occupancy32<2>() : lowd::occupancy32<1>();
+    if (op == 0)
+      n = C == 1 ? (rt == 4 ? lowd::occupancy32<2, 1>() : lowd::occupancy32<1, 1>())
+                 : (C == 2 ? lowd::occupancy32<1, 2>() : (C == 3 ? lowd::occupancy32<1, 3>() : lowd::occupancy32<1, 4>()));
     else n = rt == 4 ? lowd::occupancy32_lse<2>() : lowd::occupancy32_lse<1>();
-    cache32[op][rt].store(n, std::memory_order_relaxed);
+    cache32[op][rt][cc].store(n, std::memory_order_relaxed);
     return n;
   }
   std::atomic<int>& slot = cache[wide][C][rt];
@@ -1829,8 +1854,14 @@ hipError_t launch_mf_sum(const float* rscale, float* dst, void* region, int64_t 
   using namespace lowd;
   char* r = static_cast<char*>(region);
   const MfLayout L = mf_layout(M, N, D, C);
-  if (mf_sum_square(D, C, p.mf_rt))
-    return p.mf_rt == 4 ? sweep32<2>(r, L, dst, rscale, M, N, p, s) : sweep32<1>(r, L, dst, rscale, M, N, p, s);
+  if (mf_sum_square(D, C, p.mf_rt)) {
+    switch (C) {
+      case 1: return p.mf_rt == 4 ? sweep32<2, 1>(r, L, dst, rscale, M, N, p, s) : sweep32<1, 1>(r, L, dst, rscale, M, N, p, s);
+      case 2: return sweep32<1, 2>(r, L, dst, rscale, M, N, p, s);
+      case 3: return sweep32<1, 3>(r, L, dst, rscale, M, N, p, s);
+      case 4: return sweep32<1, 4>(r, L, dst, rscale, M, N, p, s);
+    }
+  }
 #define KEOPS_MF_C(Cv) sweep_c<Cv>(r, L, dst, rscale, M, N, p, s)
   KEOPS_SWITCH_C(C, KEOPS_MF_C)
 #undef KEOPS_MF_C
