@@ -63,6 +63,8 @@ GAUSS_SHAPES = [
     (1, 1, 3, 1, 0.1), (1, 37, 3, 1, 0.3), (257, 1000, 3, 1, 0.1), (1025, 513, 1, 1, 0.05),
     (700, 2000, 2, 3, 0.2), (513, 1500, 8, 8, 0.5), (2000, 300, 5, 4, 0.3), (300, 4099, 4, 2, 0.07),
     (100, 100_003, 3, 2, 0.02), (50_001, 777, 3, 1, 0.1), (1500, 1500, 6, 5, 0.4), (999, 2500, 7, 7, 0.6),
+    # 32x32 tiles with 2-4 channels (one 32-row tile per wave), ragged tails and column splits
+    (4000, 5001, 3, 4, 0.05), (33, 40_000, 1, 3, 0.1), (1999, 3333, 2, 2, 0.08),
 ]
 
 

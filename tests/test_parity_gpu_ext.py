@@ -340,6 +340,8 @@ ODD_WIDTHS = [
     ("float16", 2, 700, 2000, 9, 1, 0.6), ("float16", 1, 513, 1500, 12, 32, 0.8), ("float16", 3, 400, 1200, 20, 4, 1.0),
     ("float16", 1, 257, 999, 50, 17, 1.2), ("float16", 2, 200, 777, 100, 64, 1.5), ("float16", 1, 300, 900, 3, 2, 0.3),
     ("bfloat16", 1, 700, 2000, 9, 1, 0.6), ("bfloat16", 2, 400, 1200, 20, 4, 1.0), ("bfloat16", 1, 257, 999, 100, 8, 1.5),
+    # 32x32 forward tiles (D <= 32, 17 <= C <= 32): ragged rows and keys, several stages and splits
+    ("float16", 3, 1025, 777, 32, 31, 0.9), ("bfloat16", 1, 513, 1500, 24, 20, 1.1), ("float16", 2, 100, 9000, 7, 24, 0.7),
 ]
 
 
