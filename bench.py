@@ -211,7 +211,7 @@ def bench_fp16_secondary(reps, warmup):
         "pairs_per_s": pairs / t, "ms_per_call": t * 1e3, "step_stats": _stats(per_step),
         "roofline": {"bound": "mfma", "achieved": mflops / kernel_s / 1e12, "peak": PEAK_FP16_MFMA_TFLOPS,
                      "unit": "TFLOP/s", "frac": mflops / kernel_s / 1e12 / PEAK_FP16_MFMA_TFLOPS,
-                     "kernel": "fwd_kernel<_Float16,32,32,...>", "flop_per_pair": 2 * (D + C),
+                     "kernel": "fwd32_kernel<_Float16,4,128,8>", "flop_per_pair": 2 * (D + C),
                      "kernel_ms": kernel_s * 1e3,
                      "kernel_timing": "events around each launch" if sweeps.value == reps else "whole call",
                      "call_frac": mflops / t / 1e12 / PEAK_FP16_MFMA_TFLOPS},
