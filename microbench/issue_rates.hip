@@ -176,6 +176,62 @@ __global__ void __launch_bounds__(256) unit_kernel(float* out, float seed) {
   out[blockIdx.x * 256 + threadIdx.x] = s;
 }
 
+// The fp16 forward's unit structure on 32x32x16 MFMAs: per iteration a 32-key subtile against
+// 4 query tiles of 32; for each tile the scores of the next one are issued (2 MFMAs, K = 16 each
+// for 32 features), then P = fp16(2^(cs S + alpha)) of the current one (16 values per lane),
+// then O += V P (2 MFMAs for 32 channels, K = 16 keys each). One iteration is 8 units of 512
+// pairs, as in unit_kernel.
+__global__ void __launch_bounds__(256) unit32_kernel(float* out, float seed) {
+  half8 k0, k1, v0, v1, q0[4], q1[4];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    k0[s] = (_Float16)(seed * 0.01f * s);
+    k1[s] = (_Float16)(seed * 0.02f * s);
+    v0[s] = (_Float16)(seed * 0.03f);
+    v1[s] = (_Float16)(seed * 0.04f);
+  }
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    q0[t] = k0 * (_Float16)(0.1f * t);
+    q1[t] = k1 * (_Float16)(0.1f * t);
+  }
+  f32x16 beta;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) beta[i] = -1.0f - 0.1f * i;
+  float alpha[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) alpha[t] = -0.5f - 0.01f * t;
+  f32x16 O[4] = {};
+  const float cs = 1.4427f;
+  for (int it = 0; it < kIters / 8; ++it) {
+    asm volatile("" : "+v"(k0), "+v"(k1), "+v"(v0), "+v"(v1));
+    f32x16 S[2];
+    S[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(k0, q0[0], beta, 0, 0, 0);
+    S[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(k1, q1[0], S[0], 0, 0, 0);
+#pragma unroll
+    for (int qt = 0; qt < 4; ++qt) {
+      if (qt + 1 < 4) {
+        S[(qt + 1) & 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(k0, q0[qt + 1], beta, 0, 0, 0);
+        S[(qt + 1) & 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(k1, q1[qt + 1], S[(qt + 1) & 1], 0, 0, 0);
+      }
+      half8 pa, pb;
+#pragma unroll
+      for (int s = 0; s < 16; ++s) {
+        const float e = fmaf(S[qt & 1][s], cs, alpha[qt]);
+        const _Float16 h = (_Float16)__builtin_amdgcn_exp2f(e);
+        if (s < 8) pa[s] = h;
+        else pb[s - 8] = h;
+      }
+      O[qt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(v0, pa, O[qt], 0, 0, 0);
+      O[qt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(v1, pb, O[qt], 0, 0, 0);
+    }
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) s += O[t][0] + O[t][5];
+  out[blockIdx.x * 256 + threadIdx.x] = s;
+}
+
 // The float32 Gauss sum's tile structure without memory, per 1024 pairs: a high-part MFMA whose
 // result feeds the low-part MFMA as its accumulator, then per output one exp2 and one FMA into
 // a per-row partial sum. kWide = false: 16x16x32 MFMAs, 4 row tiles of 16 (8 MFMAs per 1024
@@ -262,7 +318,7 @@ int main() {
   int cus = 0;
   check(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, 0), "hipDeviceGetAttribute");
   std::printf("%-40s %12s %12s %12s\n", "ns per iteration per wave", "1 wave/SIMD", "2 waves/SIMD", "4 waves/SIMD");
-  double t[3][kKinds + 4];
+  double t[3][kKinds + 5];
   for (int w = 0; w < 3; ++w) {
     const int wps = 1 << w;
     const int blocks = cus * wps;  // 4 waves per workgroup: wps waves on every SIMD
@@ -273,9 +329,10 @@ int main() {
     t[w][kKinds + 1] = time_ms([&] { unit_kernel<false><<<blocks, 256>>>(out, 1.0f); }, 5);
     t[w][kKinds + 2] = time_ms([&] { sum_tile_kernel<false><<<blocks, 256>>>(out, 1.0f); }, 5);
     t[w][kKinds + 3] = time_ms([&] { sum_tile_kernel<true><<<blocks, 256>>>(out, 1.0f); }, 5) / 2.0;
+    t[w][kKinds + 4] = time_ms([&] { unit32_kernel<<<blocks, 256>>>(out, 1.0f); }, 5);
     check(hipGetLastError(), "launch");
     check(hipFree(out), "hipFree");
-    for (int k = 0; k < kKinds + 4; ++k) t[w][k] = t[w][k] * 1e6 / kIters / wps;
+    for (int k = 0; k < kKinds + 5; ++k) t[w][k] = t[w][k] * 1e6 / kIters / wps;
   }
   for (int k = 0; k < kKinds; ++k)
     std::printf("%-40s %12.2f %12.2f %12.2f\n", kNames[k], t[0][k], t[1][k], t[2][k]);
@@ -283,6 +340,8 @@ int main() {
               t[1][kKinds], t[2][kKinds]);
   std::printf("%-40s %12.2f %12.2f %12.2f   (per 512-pair unit)\n", "fp16 forward unit, no FMA", t[0][kKinds + 1],
               t[1][kKinds + 1], t[2][kKinds + 1]);
+  std::printf("%-40s %12.2f %12.2f %12.2f   (per 512-pair unit)\n", "fp16 forward unit on 32x32x16 tiles",
+              t[0][kKinds + 4], t[1][kKinds + 4], t[2][kKinds + 4]);
   std::printf("%-40s %12.2f %12.2f %12.2f   (per 1024 pairs)\n", "Gauss-sum tile, 16x16x32, 4 row tiles",
               t[0][kKinds + 2] * 8, t[1][kKinds + 2] * 8, t[2][kKinds + 2] * 8);
   std::printf("%-40s %12.2f %12.2f %12.2f   (per 1024 pairs)\n", "Gauss-sum tile, 32x32x16, 2 row tiles",
