@@ -34,11 +34,12 @@ constexpr int64_t kSplitCols = 32768;
 // resident slot; with only a round or two the launch ends with the slowest CU, so more and
 // shorter workgroups let the dispatcher even the load out, at the price of more partial
 // results (splits x M x C floats) and of each split's own start-up. Measured at 100k x 100k
-// and N = 2^17: the sum gains 6-8 % from 8 to 32, the gradient 4 % at 16; the log-sum-exp
-// (whose splits each re-establish their running shift) and argKmin (K-entry partial lists)
-// are fastest at 8. Wide outputs keep 8 so the partials stay small.
-constexpr int64_t wg_per_cu(int op, int C) {
-  return C > 4 ? 8 : (op == 0 ? 32 : (op == 3 ? 16 : 8));
+// and N = 2^17: the sum gains 6-8 % from 8 to 32, the gradient 4 % at 16; the log-sum-exp on
+// 32 x 32 tiles (D <= 3, no running shift) 8 % at 16 (1.05 -> 0.97 ms), while the one with a
+// running shift (whose splits each re-establish it) and argKmin (K-entry partial lists) are
+// fastest at 8. Wide outputs keep 8 so the partials stay small.
+constexpr int64_t wg_per_cu(int op, int C, int D) {
+  return C > 4 ? 8 : (op == 0 ? 32 : (op == 3 || (op == 1 && D <= 3) ? 16 : 8));
 }
 
 inline int argk_bucket(int K) {
