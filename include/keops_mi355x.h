@@ -26,8 +26,10 @@
  *   - Kernel-execution faults surface at the caller's next synchronisation, as for any HIP
  *     launch. No C++ exception crosses this boundary.
  *   - M = 0 is a no-op. Results are deterministic: the same inputs on the same device give
- *     bit-identical outputs (every sum runs in a fixed order; the only atomics take maxima,
- *     whose result does not depend on the order).
+ *     bit-identical outputs (every sum runs in a fixed order; floating-point atomics only
+ *     take maxima, whose result does not depend on the order; integer atomics count and place
+ *     points when argKmin orders them in space, which decides only which columns are
+ *     screened out, never the result).
  *   - sigma is the Gaussian bandwidth: k(x, y) = exp(-||x - y||^2 / (2 sigma^2)). The
  *     flash-attention page's Phi_tau = exp(-tau/2 ||q - k||^2) is sigma = 1/sqrt(tau).
  */
@@ -118,7 +120,9 @@ KEOPS_API int keops_gauss_sum_noalloc(const void* x, const void* y, const void* 
  * Log-sum-exp reduction ("Kernel matrix reduction", Overview, list of reductions):
  *   out[i] = log sum_j exp(-||x_i - y_j||^2 / (2 sigma^2))
  * Shapes: x (M, D), y (N, D) float32, out (M,) float32. Requires 1 <= D <= 8.
- * Evaluated with a running row maximum, so rows far from every column stay finite.
+ * Rows far from every column stay finite: their terms are taken relative to the row's
+ * largest one (a running maximum, or a float64 recomputation of rows whose plain sum came
+ * out below 2^-64).
  * N = 0 writes -inf.
  */
 KEOPS_API int keops_lse(const float* x, const float* y, float* out, int64_t M, int64_t N, int32_t D,
