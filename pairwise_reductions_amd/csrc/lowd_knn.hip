@@ -104,11 +104,10 @@ constexpr double kScreenMargin = 1.4210854715202004e-14;  // 2^-46
 // |t_j| + 2 sum_d |x_d y_d| <= 2B with B = |x|^2 + max_j(|y_j|^2 + |w_j|), so a32 differs from
 // the exact d^2 - w - |x|^2 by at most (2D + 1) 2^-24 B; the float64 threshold (key_K - |x|^2)
 // is rounded up to float32, and 2^-19 B covers both for D <= 8. The float32 FMA issues about
-// 1.6 times as fast as the float64 one on this chip, and a tile's column records take half the
-// scalar registers, so the next tile's records are loaded while the current one is screened.
+// 1.6 times as fast as the float64 one on this chip.
 constexpr double kScreenMargin32 = 0x1p-19;
 // Floats per record of the float32 screening table: D coordinates and the column term, rounded
-// up to a multiple of 4 (16-byte records for the scalar loads).
+// up to a multiple of 4 (whole 16-byte chunks for the vector loads and LDS reads).
 __host__ __device__ constexpr int screen_stride(int D) { return (D + 1 + 3) & ~3; }
 
 // The smallest float32 value >= v (v finite or +inf): the rounded value, moved one step up
@@ -508,44 +507,62 @@ knn_kernel(const float* __restrict__ x, const int32_t* __restrict__ order, const
 
   const int64_t nfull = (j1 - j0) / U;  // whole tiles of the split
   if constexpr (!LSE) {
-    // float32 records through the scalar unit, two tiles per trip in two alternating register
-    // sets; p walks the split's records. Every split but the last holds an even number of whole
-    // tiles (its column count is a multiple of 8); the last one's tiles past its end (the second
-    // tile of its last trip and the loads two tiles ahead) fall in the table's padding, whose
-    // records no row takes.
-    ConstPtr<float> p = (ConstPtr<float>)scr + j0 * S32;
+    // float32 records staged through a wave-private LDS slab: a block of kRecs records is read
+    // with one 16-byte vector load per lane a whole block ahead (vector loads complete in
+    // order, so the wait for one block never waits for a later one), written to the slab once
+    // the block before it is screened, and read back with broadcast LDS reads (every lane the
+    // same address). Every split but the last holds whole tile pairs; the last one's columns
+    // past its end read the table's (0, +inf) padding.
+    constexpr int C4 = S32 / 4;                                  // 16-byte chunks per record
+    constexpr int kRecs = (64 / C4) / (2 * U) * (2 * U);         // records per block
+    static_assert(kRecs >= 2 * U, "a block holds a tile pair");
+    __shared__ float4 slab[kBlock / 64][2][64];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t ntab = N + kScreenPad;
+    const float4* tab = reinterpret_cast<const float4*>(scr);
+    auto stage_load = [&](int64_t jb) -> float4 {
+      float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      if (lane < kRecs * C4) {
+        int64_t rec = jb + lane / C4;
+        rec = rec < ntab ? rec : ntab - 1;
+        v = tab[rec * C4 + lane % C4];
+      }
+      return v;
+    };
     struct Recs {
       float y[U][D], t[U];
     };
-    auto load = [&](ConstPtr<float> q, Recs& o) {
+    auto read = [&](int buf, int k0, Recs& o) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
+        float f[S32];
 #pragma unroll
-        for (int d = 0; d < D; ++d) o.y[u][d] = q[u * S32 + d];
-        o.t[u] = q[u * S32 + D];
+        for (int c = 0; c < C4; ++c) {
+          const float4 q = slab[wave][buf][(k0 + u) * C4 + c];
+          f[4 * c] = q.x;
+          f[4 * c + 1] = q.y;
+          f[4 * c + 2] = q.z;
+          f[4 * c + 3] = q.w;
+        }
+#pragma unroll
+        for (int d = 0; d < D; ++d) o.y[u][d] = f[d];
+        o.t[u] = f[D];
       }
     };
-    // Scalar loads complete out of order, so a wait for one set waits for every load in flight.
-    // ready() makes the wait for a set happen before the next set's load is issued: its result
-    // (always 0) depends on the set and the next load's address depends on it, so that load gets
-    // a whole tile's screening as cover.
-    auto ready = [&](const Recs& o) -> int {
-      int z;
-      asm("s_mov_b32 %0, 0" : "=s"(z) : "s"(__float_as_int(o.t[0])));
-      return z;
-    };
     const int ntiles = j1 > j0 ? (int)((j1 - j0 + U - 1) / U) : 0;  // fewer than 2^31 columns
-    Recs ra, rb;
-    if (ntiles > 0) load(p, ra);
+    int buf = 0, k0 = 0;
+    float4 stg = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    if (ntiles > 0) {
+      slab[wave][0][lane] = stage_load(j0);
+      stg = stage_load(j0 + kRecs);
+    }
     int64_t j = j0;
     for (int t = 0; t < ntiles; t += 2) {
-      load(p + ready(ra) + U * S32, rb);
-      __builtin_amdgcn_sched_barrier(0);
+      Recs ra, rb;
+      read(buf, k0, ra);
+      read(buf, k0 + U, rb);
       float aa[R][U], ab[R][U];
       const bool ha = screen32(ra.y, ra.t, aa);
-      __builtin_amdgcn_sched_barrier(0);
-      load(p + ready(rb) + 2 * U * S32, ra);
-      __builtin_amdgcn_sched_barrier(0);
       const bool hb = screen32(rb.y, rb.t, ab);
       if (__builtin_expect(__any(ha || hb), 0)) {
         queue32(j, aa);
@@ -557,8 +574,14 @@ knn_kernel(const float* __restrict__ x, const int32_t* __restrict__ order, const
           need = false;
         }
       }
-      p += 2 * U * S32;
       j += 2 * U;
+      k0 += 2 * U;
+      if (k0 == kRecs) {
+        k0 = 0;
+        buf ^= 1;
+        slab[wave][buf][lane] = stg;
+        stg = stage_load(j + kRecs);
+      }
     }
   }
   // The column records are the same for every lane: with two rows per lane they are read
