@@ -24,6 +24,7 @@ SOURCES = ["abi.hip", "lowd.hip", "lowd_sum.hip", "lowd_mfma.hip", "lowd_lse.hip
 EXTRA_FLAGS = {src: ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mno-amdgpu-ieee", "-fno-honor-nans"]
                for src in HIGHD_SOURCES}
 EXTRA_FLAGS["lowd_mfma.hip"] = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+EXTRA_FLAGS["lowd_knn.hip"] = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
 ARCH = os.environ.get("KEOPS_OFFLOAD_ARCH", "gfx950")
 
 # Packed-FP32 instruction selection is switched off: every float32 op is a plain VALU op.

@@ -112,11 +112,15 @@ struct KnnLse {
 size_t knn_screen_bytes(int64_t N, int D);
 // argKmin sweeps take their rows in spatial order, and start each row's screen from the K-th
 // smallest key over a few nearby columns, from this many rows on; the workspace (a bounding
-// box, cell counts, the row and column orders and the M starting thresholds) is
-// knn_order_bytes(M, N).
+// box, cell counts, the row and column orders, the M starting thresholds and, for the
+// matrix-core screen, its pieces) is knn_order_bytes(M, N, D, K).
 constexpr int64_t kKnnOrderMinRows = 16384;
 bool knn_orders_rows(int64_t M);
-size_t knn_order_bytes(int64_t M, int64_t N);
+size_t knn_order_bytes(int64_t M, int64_t N, int D, int K);
+// Whether the argKmin workspace holds the matrix-core screen (rows in spatial order, D <= 3,
+// K <= 16): its pieces, and partials for two lists per column split (also with one split).
+// The plain sweep (no weights, fewer than 65000 columns per split) then runs on it.
+bool knn_screens_on_matrix_cores(int64_t M, int64_t N, int D, int K);
 hipError_t launch_knn_lowd(const float* x, const float* y, const float* w, double* cols, float* scr, void* order_ws,
                            double* ymax,
                            int32_t* idx, float* dist, void* partial, float* lse_out,

@@ -145,6 +145,8 @@ Plan plan_lowd(int op, int64_t M, int64_t N, int D, int C, int K, int num_cus) {
     lead_blocks = p.mf_row_blocks;
     granule = 32;
   }
+  // argKmin's matrix-core screen halves each split into runs of 16-column tiles
+  if ((op == 2 || op == 6) && knn_screens_on_matrix_cores(M, N, D, K)) granule = 32;
   // Split the columns so that (a) there are at least lowd::wg_per_cu(op, C, D) workgroups per
   // compute unit over the launch, and (b) one split's column table stays within
   // lowd::kSplitCols columns, a working set that fits one XCD's L2 while the resident

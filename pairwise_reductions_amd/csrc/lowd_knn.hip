@@ -351,7 +351,7 @@ knn_kernel(const float* __restrict__ x, const int32_t* __restrict__ order, const
            const float* __restrict__ w, const double* __restrict__ ymax, int32_t* __restrict__ idx,
            float* __restrict__ dist, KeyIdx* __restrict__ partial, float* __restrict__ lse_out,
            LsePartial* __restrict__ lse_partial, int64_t M, int64_t N, int64_t cps, int Kout, double c2,
-           const int* __restrict__ mf, int run_if_mf) {
+           const int* __restrict__ mf, int run_if_mf, int dual) {
   if (mf && mf_admits(mf) != run_if_mf) return;  // the other form takes these inputs
   constexpr int P = (D + 2) & ~1;
   constexpr int U = D <= 4 ? 4 : 2;  // columns per screened tile
@@ -622,7 +622,18 @@ knn_kernel(const float* __restrict__ x, const int32_t* __restrict__ order, const
     int64_t i = row0 + (int64_t)r * kBlock;
     if (i >= M) continue;
     if (order) i = order[i];
-    if (gridDim.y == 1) {
+    if constexpr (LSE) {
+      if (gridDim.y == 1) {
+        lse_out[i] = (float)((mref[r] + (double)log2f(l[r])) * M_LN2);
+      } else {
+        LsePartial p;
+        p.m = mref[r];
+        p.l = l[r];
+        p.pad = 0.0f;
+        lse_partial[split * M + i] = p;
+      }
+    }
+    if (gridDim.y == 1 && !dual) {
 #pragma unroll
       for (int k = 0; k < K; ++k) {
         if (k < Kout) {
@@ -630,23 +641,265 @@ knn_kernel(const float* __restrict__ x, const int32_t* __restrict__ order, const
           if (dist) dist[i * Kout + k] = (float)keys[r][k];
         }
       }
-      if constexpr (LSE) lse_out[i] = (float)((mref[r] + (double)log2f(l[r])) * M_LN2);
     } else {
+      // with dual, the list takes list 2 split of the merge and list 2 split + 1 is left empty
+      // (the layout of the matrix-core screen, which keeps two lists per split)
+      const int64_t sub = dual ? 2 * split : split;
 #pragma unroll
       for (int k = 0; k < K; ++k) {
         KeyIdx p;
         p.key = keys[r][k];
         p.idx = ids[r][k];
         p.pad = 0;
-        partial[(split * M + i) * K + k] = p;
+        partial[(sub * M + i) * K + k] = p;
+        if (dual) {
+          p.key = INFINITY;
+          p.idx = -1;
+          partial[((sub + 1) * M + i) * K + k] = p;
+        }
       }
-      if constexpr (LSE) {
-        LsePartial p;
-        p.m = mref[r];
-        p.l = l[r];
-        p.pad = 0.0f;
-        lse_partial[split * M + i] = p;
+    }
+  }
+}
+
+// ---- The screen on the matrix cores (plain argKmin, D <= 3, K <= 16, no weights, rows in
+// spatial order). In the frame u = s (x - o), v = s (y - o) (o the centre of the bounding box
+// of rows and columns, s a power of two with |u_d|, |v_d| < 1) the key of a pair is
+// d^2_ij = (|u_i|^2 + a_ij) / s^2 with a_ij = |v_j|^2 - 2 u_i.v_j, so a column can enter row
+// i's K smallest keys only if a_ij < s^2 key_K - |u_i|^2, key_K any upper bound on the row's
+// K-th key. a_ij is a rank-(D + 1) product: one v_mfma_f32_32x32x16_f16 gives it for 1024
+// pairs from fp16 pieces (u = uh + ul + ru, v = vh + vl + rv, t = |v|^2 = th + tl + rt, each
+// hi piece the fp16 rounding of the value and each lo piece that of the rest):
+//   a'_ij = sum_d (-2 uh_d vh_d - 2 uh_d vl_d - 2 ul_d vh_d) + th_j + tl_j   (3D + 2 products).
+// Error bound: |ru|, |rv| <= 2^-22 + 2^-25 (fp16 keeps 11 bits, subnormals to 2^-24, which the
+// matrix cores take exactly) and |ul|, |vl| <= 2^-11, so the dropped products
+// 2 (uh rv + ul vl + ul rv + ru v) are below 2^-18.5 per dimension, the dropped rt below
+// 2^-22 D; the products themselves are exact in float32 and their sum, at most 3.04 D in
+// magnitude, rounds by at most (3D + 2) 2^-24 3.04 D < 2^-19 D for D <= 3. So
+// |a'_ij - a_ij| < 2^-17.5 D, and the screen compares a'_ij with the threshold
+// s^2 key_K - |u_i|^2 + 2^-16 D (float64, rounded up to float32). What the screen admits is
+// only queued: the kept columns get their exact float64 keys as in knn_kernel, so the result
+// is that of the exact keys. A non-finite frame (a point at infinity or NaN) admits every
+// column.
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+constexpr int kScreenQueue = 32;     // queued column offsets (16-bit) per lane and row
+constexpr int kScreenPieces = 64;    // piece records past the last column
+constexpr int kScreenRows = kBlock / 64 * 64;  // rows per workgroup of the screen (64 per wave)
+
+struct ScreenFrame {
+  double o[3], s;
+  bool finite;
+};
+__device__ __forceinline__ ScreenFrame screen_frame(const unsigned int* __restrict__ box, int D) {
+  ScreenFrame F;
+  double h = 0.0;
+  F.o[0] = F.o[1] = F.o[2] = 0.0;
+  for (int d = 0; d < D; ++d) {
+    const double lo = (double)f_of_ord(box[d]), hi = (double)f_of_ord(box[3 + d]);
+    F.o[d] = 0.5 * (lo + hi);
+    h = fmax(h, fmax(hi - F.o[d], F.o[d] - lo));
+  }
+  F.finite = isfinite(h);
+  int ex = 0;
+  if (F.finite && h > 0.0) frexp(h, &ex);  // h = m 2^ex, m in [0.5, 1): s h < 1
+  F.s = F.finite && h > 0.0 ? ldexp(1.0, -ex) : 1.0;
+  return F;
+}
+
+// The pieces, 16 fp16 slots per record, the row and column sides of each product:
+//   slot d: -2 uh_d | vh_d    slot D + d: -2 uh_d | vl_d    slot 2D + d: -2 ul_d | vh_d
+//   slot 3D: 1 | th           slot 3D + 1: 1 | tl           other slots 0.
+// A record past the last column has th = 65504 and nothing else, a screen value above every
+// threshold. Threads [0, M): row records rpc[i]; [M, M + N + kScreenPieces): column records,
+// from the float64 column table (y_j at cols[j P], the float32 inputs widened exactly).
+template <int D>
+__global__ void __launch_bounds__(256)
+screen_prep_kernel(const float* __restrict__ x, int64_t M, const double* __restrict__ cols, int64_t N,
+                   const unsigned int* __restrict__ box, half8* __restrict__ rpc, half8* __restrict__ cpc) {
+  constexpr int P = (D + 2) & ~1;
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= M + N + kScreenPieces) return;
+  const ScreenFrame F = screen_frame(box, D);
+  half8 lo = {0, 0, 0, 0, 0, 0, 0, 0}, hi = lo;
+  _Float16 sl[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) sl[k] = (_Float16)0.0f;
+  if (t < M) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const double u = ((double)x[t * D + d] - F.o[d]) * F.s;
+      const _Float16 uh = (_Float16)u;
+      const _Float16 ul = (_Float16)(u - (double)uh);
+      sl[d] = (_Float16)(-2.0f * (float)uh);
+      sl[D + d] = sl[d];
+      sl[2 * D + d] = (_Float16)(-2.0f * (float)ul);
+    }
+    sl[3 * D] = (_Float16)1.0f;
+    sl[3 * D + 1] = (_Float16)1.0f;
+  } else {
+    const int64_t j = t - M;
+    if (j < N) {
+      double tt = 0.0;
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        const double v = (cols[j * P + d] - F.o[d]) * F.s;
+        const _Float16 vh = (_Float16)v;
+        sl[d] = vh;
+        sl[D + d] = (_Float16)(v - (double)vh);
+        sl[2 * D + d] = vh;
+        tt = fma(v, v, tt);
       }
+      const _Float16 th = (_Float16)tt;
+      sl[3 * D] = th;
+      sl[3 * D + 1] = (_Float16)(tt - (double)th);
+    } else {
+      sl[3 * D] = (_Float16)65504.0f;
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    lo[k] = sl[k];
+    hi[k] = sl[8 + k];
+  }
+  half8* dst = t < M ? rpc + 2 * t : cpc + 2 * (t - M);
+  dst[0] = lo;
+  dst[1] = hi;
+}
+
+// The sweep. A wave takes two tiles of 32 rows (in spatial order); lane (g, l) (g = lane / 32,
+// l = lane % 32) keeps row l of each tile and screens half g of the split's columns: the split
+// [j0, j1) is cut into halves of H columns (H a multiple of 16) and the 32-column MFMA tile t
+// takes columns j0 + g H + 16 t + q, q < 16, for lane group g. With the column of A-operand row
+// m chosen so, lane (g, l) gets back exactly its 16 columns, in increasing order (MFMA output
+// item q of lane (g, l) is row 8 (q / 4) + 4 g + q % 4 of the tile). Each lane keeps its own
+// list of its half's K smallest keys; the row's threshold takes the smaller of the two lanes'
+// K-th keys (each bounds the row's K-th key from above). The lists go to partial list
+// 2 split + g, so the merge sees them in column order.
+template <int D, int K>
+__global__ void __launch_bounds__(kBlock)
+knn_screen_kernel(const float* __restrict__ x, const int32_t* __restrict__ order, const double* __restrict__ seed,
+                  const double* __restrict__ cols, const half8* __restrict__ rpc, const half8* __restrict__ cpc,
+                  const unsigned int* __restrict__ box, KeyIdx* __restrict__ partial, int64_t M, int64_t N,
+                  int64_t cps, const int* __restrict__ mf, int run_if_mf) {
+  if (mf && mf_admits(mf) != run_if_mf) return;  // the fused sweep takes these inputs
+  constexpr int RT = 2;
+  constexpr int P = (D + 2) & ~1;
+  __shared__ uint16_t queue[RT][kScreenQueue][kBlock];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 5, l32 = lane & 31;
+  const int64_t split = blockIdx.y;
+  const int64_t j0 = split * cps;
+  const int64_t j1 = (j0 + cps < N) ? j0 + cps : N;
+  const int64_t ncols = j1 > j0 ? j1 - j0 : 0;
+  const int64_t H = ((ncols + 1) / 2 + 15) / 16 * 16;
+  const ScreenFrame F = screen_frame(box, D);
+  const double s2 = F.s * F.s;
+  const double marg = 0x1p-16 * (double)D;
+
+  half8 brow[RT];
+  double xd[RT][D], au[RT], kb[RT];
+  float thr32[RT];
+  double keys[RT][K];
+  int32_t ids[RT][K];
+  int cnt[RT];
+  int64_t irow[RT];
+  bool valid[RT];
+  auto thr_of = [&](double k, double a) -> float {
+    if (!F.finite) return INFINITY;
+    const float t = round_up_f32(fma(s2, k, -a) + marg);
+    return t < 60000.0f ? t : 60000.0f;  // below the padding records' 65504
+  };
+#pragma unroll
+  for (int r = 0; r < RT; ++r) {
+    const int64_t pos = ((int64_t)blockIdx.x * (kBlock / 64) + wave) * (32 * RT) + r * 32 + l32;
+    valid[r] = pos < M;
+    const int64_t i = order[pos < M ? pos : M - 1];
+    irow[r] = i;
+    brow[r] = rpc[2 * i + g];
+    double a = 0.0;
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      xd[r][d] = (double)x[i * D + d];
+      const double u = (xd[r][d] - F.o[d]) * F.s;
+      a = fma(u, u, a);
+    }
+    au[r] = a;
+    kb[r] = seed[i];
+    thr32[r] = thr_of(kb[r], a);
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      keys[r][k] = INFINITY;
+      ids[r][k] = -1;
+    }
+    cnt[r] = 0;
+  }
+
+  // Exact keys of this lane's queued columns (in column order), then the row's bound.
+  auto flush = [&](int r) {
+    for (int e = 0; e < cnt[r]; ++e) {
+      const int64_t jj = j0 + (int64_t)queue[r][e][threadIdx.x];
+      const double key = sq_dist_key<D>(xd[r], cols + jj * P);
+      if (key < keys[r][K - 1]) topk_insert<K>(keys[r], ids[r], key, (int32_t)jj);
+    }
+    cnt[r] = 0;
+    double kth = keys[r][K - 1];
+    const double other = __shfl_xor(kth, 32);
+    kth = other < kth ? other : kth;
+    if (kth < kb[r]) kb[r] = kth;
+    thr32[r] = thr_of(kb[r], au[r]);
+  };
+
+  // A-operand row m = l32 of tile t holds column j0 + ((m >> 2) & 1) H + 16 t + 4 (m >> 3) + (m & 3)
+  const int64_t acol = j0 + (int64_t)((l32 >> 2) & 1) * H + 4 * (l32 >> 3) + (l32 & 3);
+  const int64_t ntile = H / 16;
+  const f32x16 zero16 = {};
+  // column records one, two and three tiles ahead (vector loads complete in order)
+  half8 a0 = ntile > 0 ? cpc[2 * acol + g] : half8{}, a1 = ntile > 1 ? cpc[2 * (acol + 16) + g] : half8{};
+  for (int64_t t = 0; t < ntile; ++t) {
+    const half8 a2 = t + 2 < ntile ? cpc[2 * (acol + 16 * (t + 2)) + g] : a1;
+    f32x16 e[RT];
+    bool hit = false;
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+      e[r] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, brow[r], zero16, 0, 0, 0);
+      float mn = e[r][0];
+#pragma unroll
+      for (int q = 1; q < 16; ++q) mn = fminf(mn, e[r][q]);
+      hit = hit || !(mn >= thr32[r]);
+    }
+    if (__builtin_expect(__any(hit), 0)) {
+      const int64_t off0 = (int64_t)g * H + 16 * t;  // this lane's first column, from j0
+#pragma unroll
+      for (int r = 0; r < RT; ++r) {
+        // at most kScreenQueue - 16 entries on entry, so the 16 writes stay inside the queue
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          queue[r][cnt[r]][threadIdx.x] = (uint16_t)(off0 + q);  // kept only when the count advances
+          cnt[r] += (off0 + q < ncols && !(e[r][q] >= thr32[r])) ? 1 : 0;
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < RT; ++r)
+        if (__any(cnt[r] > kScreenQueue - 16)) flush(r);
+    }
+    a0 = a1;
+    a1 = a2;
+  }
+#pragma unroll
+  for (int r = 0; r < RT; ++r) flush(r);
+
+  const int64_t sub = 2 * split + g;
+#pragma unroll
+  for (int r = 0; r < RT; ++r) {
+    if (!valid[r]) continue;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      KeyIdx p;
+      p.key = keys[r][k];
+      p.idx = ids[r][k];
+      p.pad = 0;
+      partial[(sub * M + irow[r]) * K + k] = p;
     }
   }
 }
@@ -694,6 +947,8 @@ struct Order {
   const unsigned int* cend = nullptr;
   const unsigned int* box = nullptr;
   double* seed = nullptr;
+  half8* rpc = nullptr;  // the matrix-core screen's row and column pieces (null: no such screen)
+  half8* cpc = nullptr;
 };
 
 template <int D, int K>
@@ -710,15 +965,32 @@ hipError_t knn_dk(const float* x, const Order& o, const double* cols, const floa
   dim3 grid((unsigned)p.row_blocks, (unsigned)p.splits);
   KeyIdx* part = reinterpret_cast<KeyIdx*>(partial);
   LsePartial* lpart = reinterpret_cast<LsePartial*>(lse_partial);
+  // the matrix-core screen takes the plain sweep's place (two lists per split)
+  bool screen = false;
+  // (column offsets within a split are queued as 16-bit values)
+  if constexpr (D <= 3 && K <= 16) screen = !w && o.rpc && o.cpc && o.box && o.seed && p.cols_per_split <= 65000;
+  const int dual = screen ? 1 : 0;
+  if (screen) {
+    screen_prep_kernel<D><<<(unsigned)ceil_div(M + N + kScreenPieces, 256), 256, 0, s>>>(x, M, cols, N, o.box, o.rpc,
+                                                                                         o.cpc);
+  }
   if (with_lse)
     knn_kernel<D, K, R, true><<<grid, kBlock, 0, s>>>(x, o.rows, o.seed, cols, scr, w, ymax, idx, dist, part, lse_out, lpart,
-                                                       M, N, p.cols_per_split, Kout, c2, mf, 0);
-  if (!with_lse || mf)
+                                                       M, N, p.cols_per_split, Kout, c2, mf, 0, dual);
+  if ((!with_lse || mf) && !screen)
     knn_kernel<D, K, R, false><<<grid, kBlock, 0, s>>>(x, o.rows, o.seed, cols, scr, w, ymax, idx, dist, part, lse_out, lpart,
-                                                        M, N, p.cols_per_split, Kout, c2, mf, 1);
+                                                        M, N, p.cols_per_split, Kout, c2, mf, 1, 0);
+  if constexpr (D <= 3 && K <= 16) {
+    if ((!with_lse || mf) && screen) {
+      const dim3 sgrid((unsigned)ceil_div(M, (int64_t)kScreenRows), (unsigned)p.splits);
+      knn_screen_kernel<D, K><<<sgrid, kBlock, 0, s>>>(x, o.rows, o.seed, cols, o.rpc, o.cpc, o.box, part, M, N,
+                                                        p.cols_per_split, mf, 1);
+    }
+  }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.splits == 1) return e;
-  merge_topk_kernel<K><<<(unsigned)ceil_div(M, kBlock), kBlock, 0, s>>>(part, idx, dist, M, p.splits, Kout);
+  const int64_t lists = dual ? 2 * p.splits : p.splits;
+  if (e != hipSuccess || lists == 1) return e;
+  merge_topk_kernel<K><<<(unsigned)ceil_div(M, kBlock), kBlock, 0, s>>>(part, idx, dist, M, lists, Kout);
   e = hipGetLastError();
   if (e != hipSuccess || !with_lse) return e;
   return launch_combine_lse(lpart, lse_out, M, p.splits, s, mf, 0);
@@ -817,11 +1089,12 @@ bool knn_orders_rows(int64_t M) { return M >= kKnnOrderMinRows; }
 
 namespace {
 // The order workspace: box | row cell counts | column cell counts | row order (M) | column
-// order (N) | starting thresholds (M doubles).
+// order (N) | starting thresholds (M doubles) | with the matrix-core screen, its row (M) and
+// column (N + kScreenPieces) pieces of 32 bytes.
 struct OrderLayout {
-  size_t box, counts, ccounts, rows, cols, seed, total;
+  size_t box, counts, ccounts, rows, cols, seed, rpc, cpc, total;
 };
-OrderLayout order_layout(int64_t M, int64_t N) {
+OrderLayout order_layout(int64_t M, int64_t N, int D, int K) {
   OrderLayout L;
   const size_t cells = align_up((size_t)lowd::kOrderCells * sizeof(unsigned int));
   L.box = 0;
@@ -830,14 +1103,22 @@ OrderLayout order_layout(int64_t M, int64_t N) {
   L.rows = L.ccounts + cells;
   L.cols = L.rows + align_up((size_t)M * sizeof(int32_t));
   L.seed = L.cols + align_up((size_t)N * sizeof(int32_t));
-  L.total = L.seed + align_up((size_t)M * sizeof(double));
+  L.rpc = L.seed + align_up((size_t)M * sizeof(double));
+  const bool screen = knn_screens_on_matrix_cores(M, N, D, K);
+  L.cpc = L.rpc + (screen ? align_up((size_t)M * 32) : 0);
+  L.total = L.cpc + (screen ? align_up((size_t)(N + lowd::kScreenPieces) * 32) : 0);
   return L;
 }
 }  // namespace
 
-size_t knn_order_bytes(int64_t M, int64_t N) {
+bool knn_screens_on_matrix_cores(int64_t M, int64_t N, int D, int K) {
+  (void)N;
+  return knn_orders_rows(M) && D >= 1 && D <= 3 && K >= 1 && lowd::argk_bucket(K) <= 16;
+}
+
+size_t knn_order_bytes(int64_t M, int64_t N, int D, int K) {
   if (!knn_orders_rows(M)) return 0;
-  return order_layout(M, N).total;
+  return order_layout(M, N, D, K).total;
 }
 
 hipError_t launch_knn_lowd(const float* x, const float* y, const float* w, double* cols, float* scr, void* order_ws,
@@ -859,7 +1140,7 @@ hipError_t launch_knn_lowd(const float* x, const float* y, const float* w, doubl
   lowd::Order order;
   if (knn_orders_rows(M)) {
     char* ow = static_cast<char*>(order_ws);
-    const OrderLayout L = order_layout(M, N);
+    const OrderLayout L = order_layout(M, N, D, K);
     unsigned int* box = reinterpret_cast<unsigned int*>(ow + L.box);
     unsigned int* counts = reinterpret_cast<unsigned int*>(ow + L.counts);
     unsigned int* ccounts = reinterpret_cast<unsigned int*>(ow + L.ccounts);
@@ -878,6 +1159,10 @@ hipError_t launch_knn_lowd(const float* x, const float* y, const float* w, doubl
     order.cend = ccounts;  // after the scatter: the end of each cell in the column order
     order.box = box;
     order.seed = reinterpret_cast<double*>(ow + L.seed);
+    if (knn_screens_on_matrix_cores(M, N, D, K)) {
+      order.rpc = reinterpret_cast<lowd::half8*>(ow + L.rpc);
+      order.cpc = reinterpret_cast<lowd::half8*>(ow + L.cpc);
+    }
   }
   const int Kb = lowd::argk_bucket(K);
   // With the log-sum-exp and a matrix-core region: the matrix-core log-sum-exp sweep and the
