@@ -805,7 +805,7 @@ knn_screen_kernel(const float* __restrict__ x, const int32_t* __restrict__ order
   int cnt[RT];
   int64_t irow[RT];
   bool valid[RT];
-  auto thr_of = [&](double k, double a) -> float {
+  auto thr_of = [&](double k, double a) __attribute__((always_inline)) -> float {
     if (!F.finite) return INFINITY;
     const float t = round_up_f32(fma(s2, k, -a) + marg);
     return t < 60000.0f ? t : 60000.0f;  // below the padding records' 65504
@@ -836,7 +836,7 @@ knn_screen_kernel(const float* __restrict__ x, const int32_t* __restrict__ order
   }
 
   // Exact keys of this lane's queued columns (in column order), then the row's bound.
-  auto flush = [&](int r) {
+  auto flush = [&](int r) __attribute__((always_inline)) {
     for (int e = 0; e < cnt[r]; ++e) {
       const int64_t jj = j0 + (int64_t)queue[r][e][threadIdx.x];
       const double key = sq_dist_key<D>(xd[r], cols + jj * P);
@@ -851,40 +851,65 @@ knn_screen_kernel(const float* __restrict__ x, const int32_t* __restrict__ order
   };
 
   // A-operand row m = l32 of tile t holds column j0 + ((m >> 2) & 1) H + 16 t + 4 (m >> 3) + (m & 3)
-  const int64_t acol = j0 + (int64_t)((l32 >> 2) & 1) * H + 4 * (l32 >> 3) + (l32 & 3);
-  const int64_t ntile = H / 16;
+  // (column offsets from j0 fit 16 bits: the split holds fewer than 65000 columns)
+  const int aoff = ((l32 >> 2) & 1) * (int)H + 4 * (l32 >> 3) + (l32 & 3);
+  const half8* abase = cpc + 2 * (j0 + aoff) + g;
+  const int ntile = (int)(H / 16), ncol = (int)ncols, goff = g * (int)H;
   const f32x16 zero16 = {};
-  // column records one, two and three tiles ahead (vector loads complete in order)
-  half8 a0 = ntile > 0 ? cpc[2 * acol + g] : half8{}, a1 = ntile > 1 ? cpc[2 * (acol + 16) + g] : half8{};
-  for (int64_t t = 0; t < ntile; ++t) {
-    const half8 a2 = t + 2 < ntile ? cpc[2 * (acol + 16 * (t + 2)) + g] : a1;
+  auto step = [&](int t, const half8& a) __attribute__((always_inline)) {
     f32x16 e[RT];
     bool hit = false;
 #pragma unroll
     for (int r = 0; r < RT; ++r) {
-      e[r] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, brow[r], zero16, 0, 0, 0);
+      e[r] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, brow[r], zero16, 0, 0, 0);
       float mn = e[r][0];
 #pragma unroll
       for (int q = 1; q < 16; ++q) mn = fminf(mn, e[r][q]);
-      hit = hit || !(mn >= thr32[r]);
+      hit = hit | (mn < thr32[r]);
     }
     if (__builtin_expect(__any(hit), 0)) {
-      const int64_t off0 = (int64_t)g * H + 16 * t;  // this lane's first column, from j0
+      const int off0 = goff + 16 * t;  // this lane's first column, from j0
 #pragma unroll
       for (int r = 0; r < RT; ++r) {
         // at most kScreenQueue - 16 entries on entry, so the 16 writes stay inside the queue
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
           queue[r][cnt[r]][threadIdx.x] = (uint16_t)(off0 + q);  // kept only when the count advances
-          cnt[r] += (off0 + q < ncols && !(e[r][q] >= thr32[r])) ? 1 : 0;
+          cnt[r] += (off0 + q < ncol && e[r][q] < thr32[r]) ? 1 : 0;
         }
       }
 #pragma unroll
       for (int r = 0; r < RT; ++r)
         if (__any(cnt[r] > kScreenQueue - 16)) flush(r);
     }
-    a0 = a1;
-    a1 = a2;
+  };
+  auto load = [&](int t) __attribute__((always_inline)) -> half8 { return t < ntile ? abase[32 * t] : half8{}; };
+  if (!F.finite) {
+    // no usable frame: every column of the lane's half is queued and gets its exact key
+    for (int t = 0; t < ntile; ++t)
+#pragma unroll
+      for (int r = 0; r < RT; ++r) {
+        for (int q = 0; q < 16; ++q) {
+          const int off = goff + 16 * t + q;
+          queue[r][cnt[r]][threadIdx.x] = (uint16_t)off;
+          cnt[r] += off < ncol ? 1 : 0;
+        }
+        flush(r);
+      }
+  } else {
+    // three operand sets in a ring, each loaded two tiles before its use (vector loads complete
+    // in order, so each wait is for the oldest load only)
+    half8 a0 = load(0), a1 = load(1), a2;
+    for (int t = 0; t < ntile; t += 3) {
+      a2 = load(t + 2);
+      step(t, a0);
+      if (t + 1 >= ntile) break;
+      a0 = load(t + 3);
+      step(t + 1, a1);
+      if (t + 2 >= ntile) break;
+      a1 = load(t + 4);
+      step(t + 2, a2);
+    }
   }
 #pragma unroll
   for (int r = 0; r < RT; ++r) flush(r);
