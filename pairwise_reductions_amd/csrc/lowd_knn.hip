@@ -781,14 +781,21 @@ __global__ void __launch_bounds__(kBlock)
 knn_screen_kernel(const float* __restrict__ x, const int32_t* __restrict__ order, const double* __restrict__ seed,
                   const double* __restrict__ cols, const half8* __restrict__ rpc, const half8* __restrict__ cpc,
                   const unsigned int* __restrict__ box, KeyIdx* __restrict__ partial, int64_t M, int64_t N,
-                  int64_t cps, const int* __restrict__ mf, int run_if_mf) {
+                  int64_t cps, int64_t row_blocks, const int* __restrict__ mf, int run_if_mf) {
   if (mf && mf_admits(mf) != run_if_mf) return;  // the fused sweep takes these inputs
   constexpr int RT = 2;
   constexpr int P = (D + 2) & ~1;
+  constexpr uint32_t kXcds = 8;  // accelerator complexes (each with its own L2) on the chip
   __shared__ uint16_t queue[RT][kScreenQueue][kBlock];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 5, l32 = lane & 31;
-  const int64_t split = blockIdx.y;
+  // Workgroups go to the XCDs round-robin by id; renumbered, each XCD takes a contiguous run of
+  // (split, row block) pairs, split-major, so its resident workgroups read the same split's
+  // pieces, which stay in that XCD's L2.
+  const uint32_t wg = blockIdx.x, total = gridDim.x;
+  const uint32_t per = total / kXcds, extra = total % kXcds, xcd = wg % kXcds;
+  const int64_t pair = (int64_t)xcd * per + (xcd < extra ? xcd : extra) + wg / kXcds;
+  const int64_t split = pair / row_blocks, rblock = pair % row_blocks;
   const int64_t j0 = split * cps;
   const int64_t j1 = (j0 + cps < N) ? j0 + cps : N;
   const int64_t ncols = j1 > j0 ? j1 - j0 : 0;
@@ -812,7 +819,7 @@ knn_screen_kernel(const float* __restrict__ x, const int32_t* __restrict__ order
   };
 #pragma unroll
   for (int r = 0; r < RT; ++r) {
-    const int64_t pos = ((int64_t)blockIdx.x * (kBlock / 64) + wave) * (32 * RT) + r * 32 + l32;
+    const int64_t pos = (rblock * (kBlock / 64) + wave) * (32 * RT) + r * 32 + l32;
     valid[r] = pos < M;
     const int64_t i = order[pos < M ? pos : M - 1];
     irow[r] = i;
@@ -1007,9 +1014,9 @@ hipError_t knn_dk(const float* x, const Order& o, const double* cols, const floa
                                                         M, N, p.cols_per_split, Kout, c2, mf, 1, 0);
   if constexpr (D <= 3 && K <= 16) {
     if ((!with_lse || mf) && screen) {
-      const dim3 sgrid((unsigned)ceil_div(M, (int64_t)kScreenRows), (unsigned)p.splits);
-      knn_screen_kernel<D, K><<<sgrid, kBlock, 0, s>>>(x, o.rows, o.seed, cols, o.rpc, o.cpc, o.box, part, M, N,
-                                                        p.cols_per_split, mf, 1);
+      const int64_t rblocks = ceil_div(M, (int64_t)kScreenRows);
+      knn_screen_kernel<D, K><<<(unsigned)(rblocks * p.splits), kBlock, 0, s>>>(
+          x, o.rows, o.seed, cols, o.rpc, o.cpc, o.box, part, M, N, p.cols_per_split, rblocks, mf, 1);
     }
   }
   hipError_t e = hipGetLastError();
