@@ -123,13 +123,16 @@ LowdLayout lowd_layout(int op, int64_t M, int64_t N, int D, int C, int K) {
   const size_t order_bytes = knn ? keops::align_up(keops::knn_order_bytes(M, N, D, K)) : 0;
   L.part_off = L.order_off + order_bytes;
   size_t lse_bytes = 0;
-  // argKmin on the matrix-core screen keeps two lists per split
-  const size_t lists = knn && keops::knn_screens_on_matrix_cores(M, N, D, K) ? 2 * S : S;
-  L.part_bytes = 0;
-  if (knn && lists > 1) L.part_bytes = keops::align_up(lists * Mz * keops::partial_bytes_per_row(KEOPS_OP_ARGKMIN, D, C, K));
-  if (knn && S > 1 && op == KEOPS_OP_ARGKMIN_LSE)
-    lse_bytes = keops::align_up(S * Mz * keops::partial_bytes_per_row(KEOPS_OP_LSE, D, C, K));
-  if (!knn && S > 1) L.part_bytes = keops::align_up(S * Mz * keops::partial_bytes_per_row(op, D, C, K));
+  if (S > 1) {
+    if (knn) {
+      L.part_bytes = keops::align_up(S * Mz * keops::partial_bytes_per_row(KEOPS_OP_ARGKMIN, D, C, K));
+      if (op == KEOPS_OP_ARGKMIN_LSE) lse_bytes = keops::align_up(S * Mz * keops::partial_bytes_per_row(KEOPS_OP_LSE, D, C, K));
+    } else {
+      L.part_bytes = keops::align_up(S * Mz * keops::partial_bytes_per_row(op, D, C, K));
+    }
+  } else {
+    L.part_bytes = 0;
+  }
   L.lse_off = L.part_off + L.part_bytes;
   L.mf_off = L.lse_off + lse_bytes;
   size_t mf = 0;

@@ -117,9 +117,9 @@ size_t knn_screen_bytes(int64_t N, int D);
 constexpr int64_t kKnnOrderMinRows = 16384;
 bool knn_orders_rows(int64_t M);
 size_t knn_order_bytes(int64_t M, int64_t N, int D, int K);
-// Whether the argKmin workspace holds the matrix-core screen (rows in spatial order, D <= 3,
-// K <= 16): its pieces, and partials for two lists per column split (also with one split).
-// The plain sweep (no weights, fewer than 65000 columns per split) then runs on it.
+// Whether the argKmin workspace holds the pieces of the matrix-core screen (rows in spatial
+// order, D <= 3, K <= 16); the plain sweep (no weights, fewer than 65000 columns per split)
+// then runs on it.
 bool knn_screens_on_matrix_cores(int64_t M, int64_t N, int D, int K);
 hipError_t launch_knn_lowd(const float* x, const float* y, const float* w, double* cols, float* scr, void* order_ws,
                            double* ymax,

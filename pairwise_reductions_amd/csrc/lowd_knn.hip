@@ -351,7 +351,7 @@ knn_kernel(const float* __restrict__ x, const int32_t* __restrict__ order, const
            const float* __restrict__ w, const double* __restrict__ ymax, int32_t* __restrict__ idx,
            float* __restrict__ dist, KeyIdx* __restrict__ partial, float* __restrict__ lse_out,
            LsePartial* __restrict__ lse_partial, int64_t M, int64_t N, int64_t cps, int Kout, double c2,
-           const int* __restrict__ mf, int run_if_mf, int dual) {
+           const int* __restrict__ mf, int run_if_mf) {
   if (mf && mf_admits(mf) != run_if_mf) return;  // the other form takes these inputs
   constexpr int P = (D + 2) & ~1;
   constexpr int U = D <= 4 ? 4 : 2;  // columns per screened tile
@@ -633,7 +633,7 @@ knn_kernel(const float* __restrict__ x, const int32_t* __restrict__ order, const
         lse_partial[split * M + i] = p;
       }
     }
-    if (gridDim.y == 1 && !dual) {
+    if (gridDim.y == 1) {
 #pragma unroll
       for (int k = 0; k < K; ++k) {
         if (k < Kout) {
@@ -642,21 +642,13 @@ knn_kernel(const float* __restrict__ x, const int32_t* __restrict__ order, const
         }
       }
     } else {
-      // with dual, the list takes list 2 split of the merge and list 2 split + 1 is left empty
-      // (the layout of the matrix-core screen, which keeps two lists per split)
-      const int64_t sub = dual ? 2 * split : split;
 #pragma unroll
       for (int k = 0; k < K; ++k) {
         KeyIdx p;
         p.key = keys[r][k];
         p.idx = ids[r][k];
         p.pad = 0;
-        partial[(sub * M + i) * K + k] = p;
-        if (dual) {
-          p.key = INFINITY;
-          p.idx = -1;
-          partial[((sub + 1) * M + i) * K + k] = p;
-        }
+        partial[(split * M + i) * K + k] = p;
       }
     }
   }
@@ -685,7 +677,10 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int kScreenQueue = 32;     // queued column offsets (16-bit) per lane and row
 constexpr int kScreenPieces = 64;    // piece records past the last column
-constexpr int kScreenRows = kBlock / 64 * 64;  // rows per workgroup of the screen (64 per wave)
+// Row tiles of 32 per wave: one (more resident waves, 92 VGPRs) measured 5 % faster than two
+// (168 VGPRs), which share each column operand between two MFMAs.
+constexpr int kScreenRT = 1;
+constexpr int kScreenRows = kBlock / 64 * 32 * kScreenRT;  // rows per workgroup of the screen
 
 struct ScreenFrame {
   double o[3], s;
@@ -767,23 +762,24 @@ screen_prep_kernel(const float* __restrict__ x, int64_t M, const double* __restr
   dst[1] = hi;
 }
 
-// The sweep. A wave takes two tiles of 32 rows (in spatial order); lane (g, l) (g = lane / 32,
+// The sweep. A wave takes kScreenRT tiles of 32 rows (in spatial order); lane (g, l) (g = lane / 32,
 // l = lane % 32) keeps row l of each tile and screens half g of the split's columns: the split
 // [j0, j1) is cut into halves of H columns (H a multiple of 16) and the 32-column MFMA tile t
 // takes columns j0 + g H + 16 t + q, q < 16, for lane group g. With the column of A-operand row
 // m chosen so, lane (g, l) gets back exactly its 16 columns, in increasing order (MFMA output
 // item q of lane (g, l) is row 8 (q / 4) + 4 g + q % 4 of the tile). Each lane keeps its own
 // list of its half's K smallest keys; the row's threshold takes the smaller of the two lanes'
-// K-th keys (each bounds the row's K-th key from above). The lists go to partial list
-// 2 split + g, so the merge sees them in column order.
+// K-th keys (each bounds the row's K-th key from above). At the end the two lists are merged
+// into the row's list of the split.
 template <int D, int K>
 __global__ void __launch_bounds__(kBlock)
 knn_screen_kernel(const float* __restrict__ x, const int32_t* __restrict__ order, const double* __restrict__ seed,
                   const double* __restrict__ cols, const half8* __restrict__ rpc, const half8* __restrict__ cpc,
-                  const unsigned int* __restrict__ box, KeyIdx* __restrict__ partial, int64_t M, int64_t N,
-                  int64_t cps, int64_t row_blocks, const int* __restrict__ mf, int run_if_mf) {
+                  const unsigned int* __restrict__ box, int32_t* __restrict__ idx, float* __restrict__ dist,
+                  KeyIdx* __restrict__ partial, int64_t M, int64_t N, int64_t cps, int64_t row_blocks, int64_t splits,
+                  int Kout, const int* __restrict__ mf, int run_if_mf) {
   if (mf && mf_admits(mf) != run_if_mf) return;  // the fused sweep takes these inputs
-  constexpr int RT = 2;
+  constexpr int RT = kScreenRT;
   constexpr int P = (D + 2) & ~1;
   constexpr uint32_t kXcds = 8;  // accelerator complexes (each with its own L2) on the chip
   __shared__ uint16_t queue[RT][kScreenQueue][kBlock];
@@ -921,17 +917,36 @@ knn_screen_kernel(const float* __restrict__ x, const int32_t* __restrict__ order
 #pragma unroll
   for (int r = 0; r < RT; ++r) flush(r);
 
-  const int64_t sub = 2 * split + g;
+  // The two lanes of a row hold the lists of the split's two halves; lane g = 0 takes in the
+  // second half's entries (higher columns: on equal keys they go after its own) and writes the
+  // row's list of the split.
 #pragma unroll
   for (int r = 0; r < RT; ++r) {
-    if (!valid[r]) continue;
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-      KeyIdx p;
-      p.key = keys[r][k];
-      p.idx = ids[r][k];
-      p.pad = 0;
-      partial[(sub * M + irow[r]) * K + k] = p;
+      const double ok = __shfl_xor(keys[r][k], 32);
+      const int32_t oi = __shfl_xor(ids[r][k], 32);
+      if (g == 0 && oi >= 0 && ok < keys[r][K - 1]) topk_insert<K>(keys[r], ids[r], ok, oi);
+    }
+    if (g != 0 || !valid[r]) continue;
+    const int64_t i = irow[r];
+    if (splits == 1) {
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        if (k < Kout) {
+          idx[i * Kout + k] = ids[r][k];
+          if (dist) dist[i * Kout + k] = (float)keys[r][k];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        KeyIdx p;
+        p.key = keys[r][k];
+        p.idx = ids[r][k];
+        p.pad = 0;
+        partial[(split * M + i) * K + k] = p;
+      }
     }
   }
 }
@@ -997,32 +1012,31 @@ hipError_t knn_dk(const float* x, const Order& o, const double* cols, const floa
   dim3 grid((unsigned)p.row_blocks, (unsigned)p.splits);
   KeyIdx* part = reinterpret_cast<KeyIdx*>(partial);
   LsePartial* lpart = reinterpret_cast<LsePartial*>(lse_partial);
-  // the matrix-core screen takes the plain sweep's place (two lists per split)
+  // the matrix-core screen takes the plain sweep's place
   bool screen = false;
   // (column offsets within a split are queued as 16-bit values)
   if constexpr (D <= 3 && K <= 16) screen = !w && o.rpc && o.cpc && o.box && o.seed && p.cols_per_split <= 65000;
-  const int dual = screen ? 1 : 0;
   if (screen) {
     screen_prep_kernel<D><<<(unsigned)ceil_div(M + N + kScreenPieces, 256), 256, 0, s>>>(x, M, cols, N, o.box, o.rpc,
                                                                                          o.cpc);
   }
   if (with_lse)
     knn_kernel<D, K, R, true><<<grid, kBlock, 0, s>>>(x, o.rows, o.seed, cols, scr, w, ymax, idx, dist, part, lse_out, lpart,
-                                                       M, N, p.cols_per_split, Kout, c2, mf, 0, dual);
+                                                       M, N, p.cols_per_split, Kout, c2, mf, 0);
   if ((!with_lse || mf) && !screen)
     knn_kernel<D, K, R, false><<<grid, kBlock, 0, s>>>(x, o.rows, o.seed, cols, scr, w, ymax, idx, dist, part, lse_out, lpart,
-                                                        M, N, p.cols_per_split, Kout, c2, mf, 1, 0);
+                                                        M, N, p.cols_per_split, Kout, c2, mf, 1);
   if constexpr (D <= 3 && K <= 16) {
     if ((!with_lse || mf) && screen) {
       const int64_t rblocks = ceil_div(M, (int64_t)kScreenRows);
       knn_screen_kernel<D, K><<<(unsigned)(rblocks * p.splits), kBlock, 0, s>>>(
-          x, o.rows, o.seed, cols, o.rpc, o.cpc, o.box, part, M, N, p.cols_per_split, rblocks, mf, 1);
+          x, o.rows, o.seed, cols, o.rpc, o.cpc, o.box, idx, dist, part, M, N, p.cols_per_split, rblocks, p.splits,
+          Kout, mf, 1);
     }
   }
   hipError_t e = hipGetLastError();
-  const int64_t lists = dual ? 2 * p.splits : p.splits;
-  if (e != hipSuccess || lists == 1) return e;
-  merge_topk_kernel<K><<<(unsigned)ceil_div(M, kBlock), kBlock, 0, s>>>(part, idx, dist, M, lists, Kout);
+  if (e != hipSuccess || p.splits == 1) return e;
+  merge_topk_kernel<K><<<(unsigned)ceil_div(M, kBlock), kBlock, 0, s>>>(part, idx, dist, M, p.splits, Kout);
   e = hipGetLastError();
   if (e != hipSuccess || !with_lse) return e;
   return launch_combine_lse(lpart, lse_out, M, p.splits, s, mf, 0);
