@@ -596,6 +596,56 @@ def test_argkmin_lse_exponent_regimes(D, sigma, lo, hi, outlier):
     assert np.all(err <= lse_bound(want_lse)), f"argkmin_lse regime: max LSE error {err.max():.3e}"
 
 
+# From 16384 rows on, argKmin without weights at D <= 3, K <= 16 screens on the matrix cores in
+# the frame of the points' bounding box (fp16 pieces, a proven margin, exact float64 keys for
+# the kept columns). Frames that stress it: a narrow box far from the origin, one far outlier
+# that makes the box huge (so the margin admits nearly every column), plain float32 values,
+# coarse grids with many equal keys, every D and K bucket it takes.
+SCREEN_CASES = [
+    # (name, M, N, D, K)
+    ("far narrow box, coarse grid", 20_000, 3000, 3, 10),
+    ("one far outlier", 17_000, 1500, 3, 4),
+    ("plain float32 normals", 20_000, 4000, 3, 16),
+    ("D = 2, coarse grid", 18_000, 2500, 2, 8),
+    ("D = 1, duplicates", 16_384, 2000, 1, 2),
+    ("K = 1", 16_500, 3333, 3, 1),
+]
+
+
+@pytest.mark.parametrize("name,M,N,D,K", SCREEN_CASES, ids=[c[0] for c in SCREEN_CASES])
+def test_argkmin_matrix_core_screen_frames(name, M, N, D, K):
+    import pairwise_reductions_amd as pr
+    _announce("argkmin_screen", case=name, M=M, N=N, D=D, K=K)
+    rng = np.random.default_rng(M + N + D + K)
+    if name.startswith("far"):
+        x = (1000.0 + rng.integers(0, 16, size=(M, D)) / 16.0).astype(np.float32)
+        y = (1000.0 + rng.integers(0, 16, size=(N, D)) / 16.0).astype(np.float32)
+    elif name.startswith("one far"):
+        x = workloads.grid24(rng, (M, D))
+        y = workloads.grid24(rng, (N, D))
+        y[N // 2] = 1.0e6
+    elif name.startswith("plain"):
+        x = (rng.standard_normal((M, D)) * 3.0).astype(np.float32)
+        y = (rng.standard_normal((N, D)) * 3.0).astype(np.float32)
+    elif name.startswith("D = 2"):
+        x = (rng.integers(0, 12, size=(M, D)) / 12.0).astype(np.float32)
+        y = (rng.integers(0, 12, size=(N, D)) / 12.0).astype(np.float32)
+    elif name.startswith("D = 1"):
+        x = workloads.grid24(rng, (M, D))
+        y = workloads.grid24(rng, (N, D))
+        y[300:400] = y[7]
+    else:
+        x = workloads.grid24(rng, (M, D))
+        y = workloads.grid24(rng, (N, D))
+    idx, dist = pr.argkmin(_dev(x), _dev(y), K, with_dist=True)
+    want_idx, want_d2 = oracle.argkmin(x, y, K, workers=8)
+    assert np.array_equal(_host(idx).astype(np.int64), want_idx)
+    assert np.allclose(_host(dist), want_d2, rtol=1e-6, atol=0)
+    sig = float(np.float32(0.1))
+    fidx = _host(pr.argkmin_lse(_dev(x), _dev(y), K, sig)[0]).astype(np.int64)
+    assert np.array_equal(fidx, want_idx)
+
+
 def test_argkmin_screening_far_from_origin_and_unaligned_values():
     """The screening bound grows with |x|^2 + max|y|^2: points near 1000 on a coarse grid
     (many exact ties) and plain float32 values (keys not exact) must still give the oracle's
