@@ -13,6 +13,17 @@
 // (v < 16) of column l: keys of query l, and channels of query l. Its values v < 8 and v >= 8
 // are then exactly its B operands of the two P^T products when each 32-key subtile's weights
 // are stored in the slot32_key() order, so P never moves between lanes.
+//
+// Folded form (fp16 inputs). Once a wave's rows are settled, the per-value FMA cs S' + alpha
+// can go: with the query operands replaced by qs = fp16(cs q) and the accumulator starting from
+// cs beta (stored so in LDS beside beta), the MFMA returns the unshifted exponent itself. Each
+// row's own shift alpha_i moves into its output scale (O_i is multiplied by 2^-alpha_i once).
+// That needs alpha_i in [-kFoldLow, kFoldHigh]: later terms, at most 2^kSlack under the row
+// shift, stay below 2^(kSlack + kFoldLow) = 2^15 (fp16 holds up to 65504), and no row's terms
+// move more than kFoldHigh binades towards the fp16 subnormals. The rounding of cs q moves each
+// exponent by e_ij = sum_d (qs_d - cs q_d) k_jd, |e_ij| <= |qs_i - cs q_i| |k_j|; a wave takes
+// the folded form only where that bound, with the largest |k_j| of its column split, is at most
+// 2^-10 (a relative change of each term below 6.8e-4). Otherwise it keeps the FMA.
 #pragma once
 
 #include "highd_common.h"
@@ -46,6 +57,12 @@ __device__ __forceinline__ f32x16 mfma32_s(const typename Raw8Of<TIn>::type& a, 
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// Range of the row shifts of a wave that takes the folded form (binades).
+constexpr float kFoldLow = 7.0f, kFoldHigh = 4.0f;
+// Largest |qs - cs q|^2 |k|^2 of the folded form: (2^-10)^2, less 2^-8 of it for the float32
+// rounding of the quantities it is computed from.
+constexpr float kFoldErr2 = 9.5367431640625e-07f * (1.0f - 0.00390625f);
+
 template <typename TIn, int QT, int kStage, int kW>
 __global__ void __launch_bounds__(64 * kW, 1)
 fwd32_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const float* __restrict__ beta,
@@ -62,7 +79,10 @@ fwd32_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const float* 
   using Raw8 = typename Raw8Of<TIn>::type;
   __shared__ __attribute__((aligned(16))) Raw sK[2][kStage][KP];
   __shared__ __attribute__((aligned(16))) _Float16 sV[2][NSUB][C][VP];
+  constexpr bool kFoldable = std::is_same<TIn, _Float16>::value;
   __shared__ __attribute__((aligned(16))) float sB[2][kStage];
+  __shared__ __attribute__((aligned(16))) float sBs[kFoldable ? 2 : 1][kFoldable ? kStage : 4];  // cs beta
+  __shared__ float sKn[kW];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31;
@@ -144,7 +164,10 @@ fwd32_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const float* 
       const int t = c / (C * 4), rem = c % (C * 4);
       if (c < kVChunks) *reinterpret_cast<half8*>(&sV[buf][t][rem / 4][(rem % 4) * 8]) = rv[r];
     }
-    if (tid < kStage / 4) *reinterpret_cast<f32x4*>(&sB[buf][4 * tid]) = rb;
+    if (tid < kStage / 4) {
+      *reinterpret_cast<f32x4*>(&sB[buf][4 * tid]) = rb;
+      if constexpr (kFoldable) *reinterpret_cast<f32x4*>(&sBs[buf][4 * tid]) = rb * cs;
+    }
   };
 
   // Operands of one 32-key subtile: key l's features (two K = 16 slices), beta of the lane's 16
@@ -154,12 +177,13 @@ fwd32_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const float* 
     f32x16 b;
     half8 v[2];
   };
-  auto read_operands = [&](int buf, int sub, Operands& o) {
+  auto read_operands = [&](int buf, int sub, Operands& o, auto folded) {
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) o.k[kk] = *reinterpret_cast<const Raw8*>(&sK[buf][sub * 32 + l32][16 * kk + 8 * g]);
+    const float* srcb = decltype(folded)::value ? &sBs[buf][0] : &sB[buf][0];
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const f32x4 b4 = *reinterpret_cast<const f32x4*>(&sB[buf][sub * 32 + 8 * w + 4 * g]);
+      const f32x4 b4 = *reinterpret_cast<const f32x4*>(srcb + sub * 32 + 8 * w + 4 * g);
 #pragma unroll
       for (int u = 0; u < 4; ++u) o.b[4 * w + u] = b4[u];
     }
@@ -170,11 +194,11 @@ fwd32_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const float* 
     f32x16 S = mfma32_s<TIn>(o.k[0], qop[qt][0], o.b);
     return mfma32_s<TIn>(o.k[1], qop[qt][1], S);
   };
-  auto use = [&](const Operands& o, int qt, const f32x16& S) {
+  auto use = [&](const Operands& o, int qt, const f32x16& S, auto folded) {
     half8 pa, pb;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const _Float16 h = (_Float16)exp2_hw(fmaf(S[v], cs, alpha[qt]));
+      const _Float16 h = (_Float16)exp2_hw(decltype(folded)::value ? S[v] : fmaf(S[v], cs, alpha[qt]));
       if (v < 8) pa[v] = h;
       else pb[v - 8] = h;
     }
@@ -192,7 +216,7 @@ fwd32_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const float* 
 #pragma unroll 1
     for (int sub = 0; sub < NSUB; ++sub) {
       Operands o;
-      read_operands(buf, sub, o);
+      read_operands(buf, sub, o, std::false_type{});
       bool all_settled = true;
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) {
@@ -208,7 +232,7 @@ fwd32_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const float* 
         const float sc = (first || delta == 0.0f) ? 1.0f : exp2_hw(-delta);
         O[qt] *= sc;
         all_settled = all_settled && (mrow[qt] >= -kSlack);
-        use(o, qt, S);
+        use(o, qt, S, std::false_type{});
       }
       settled = __all(all_settled);
       first = false;
@@ -219,36 +243,95 @@ fwd32_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const float* 
   // Settled stages, software-pipelined over the stage's (subtile, query tile) units: the scores
   // of the next unit are issued before the exponentials of the current one, and the next
   // subtile's operands are read one subtile ahead (two sets alternate).
-  auto stage_pipe = [&](int64_t st) {
+  auto stage_pipe = [&](int64_t st, auto folded) {
     const int buf = (int)(st & 1);
     if (st + 1 < nstages) fetch(st + 1);
     Operands ops[2];
-    read_operands(buf, 0, ops[0]);
+    read_operands(buf, 0, ops[0], folded);
     f32x16 Sbuf[2];
     Sbuf[0] = score_with(ops[0], 0);
 #pragma unroll
     for (int u = 0; u < NSUB * QT; ++u) {
       const int sub = u / QT, qt = u % QT;
       const Operands& cur = ops[sub & 1];
-      if (qt == 0 && sub + 1 < NSUB) read_operands(buf, sub + 1, ops[(sub + 1) & 1]);
+      if (qt == 0 && sub + 1 < NSUB) read_operands(buf, sub + 1, ops[(sub + 1) & 1], folded);
       if (u + 1 < NSUB * QT) {
         if (qt + 1 < QT)
           Sbuf[(u + 1) & 1] = score_with(cur, qt + 1);
         else
           Sbuf[(u + 1) & 1] = score_with(ops[(sub + 1) & 1], 0);
       }
-      use(cur, qt, Sbuf[u & 1]);
+      use(cur, qt, Sbuf[u & 1], folded);
     }
     if (st + 1 < nstages) commit(buf ^ 1);
     __syncthreads();
   };
 
+  // Largest squared key norm of the split (beta_j <= -|k_j|^2 / 2 for every key in it).
+  if constexpr (kFoldable) {
+    float kn = 0.0f;
+    for (int64_t j = j0 + tid; j < j1; j += kThreads) kn = fmaxf(kn, -2.0f * bb[j]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) kn = fmaxf(kn, __shfl_xor(kn, o));
+    if (lane == 0) sKn[wave] = kn;
+  }
   fetch(0);
   commit(0);
   __syncthreads();
   int64_t st = 0;
   for (; st < nstages && !settled; ++st) stage_track(st);
-  for (; st < nstages; ++st) stage_pipe(st);
+  bool folded = false;
+  if constexpr (kFoldable) {
+    if (settled && st < nstages) {
+      float kn2 = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kW; ++w) kn2 = fmaxf(kn2, sKn[w]);
+      float amin = alpha[0], amax = alpha[0], d2 = 0.0f;
+      bool fits = true;  // every cs q_d rounds to a finite fp16 value
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        amin = fminf(amin, alpha[qt]);
+        amax = fmaxf(amax, alpha[qt]);
+        float dq = 0.0f;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float cq = cs * (float)qop[qt][kk][e];
+            fits = fits && fabsf(cq) < 65504.0f;
+            const float dd = fits ? (float)(_Float16)cq - cq : 0.0f;
+            dq = fmaf(dd, dd, dq);
+          }
+        dq += __shfl_xor(dq, 32);
+        d2 = fmaxf(d2, dq);
+      }
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) {
+        amin = fminf(amin, __shfl_xor(amin, o));
+        amax = fmaxf(amax, __shfl_xor(amax, o));
+        d2 = fmaxf(d2, __shfl_xor(d2, o));
+      }
+      folded = __all(fits) && (amin >= -kFoldLow) && (amax <= kFoldHigh) && (d2 * kn2 <= kFoldErr2);
+      if (folded) {
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) {
+          O[qt] *= exp2_hw(-alpha[qt]);
+          mrow[qt] += alpha[qt];
+          alpha[qt] = 0.0f;
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qop[qt][kk][e] = (Raw)(cs * (float)qop[qt][kk][e]);
+        }
+      }
+    }
+  }
+  for (; st < nstages; ++st) {
+    if (folded)
+      stage_pipe(st, std::true_type{});
+    else
+      stage_pipe(st, std::false_type{});
+  }
 
   // Store the first Cout channels: lane (g, l) holds channels 8w + 4g .. 8w + 4g + 3 of query l.
   const int64_t BMC = (int64_t)gridDim.z * M * Cout;

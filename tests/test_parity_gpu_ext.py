@@ -40,6 +40,49 @@ def test_gauss_sum_fp16_feature_widths(B, M, N, D, C, sigma):
     assert_normalised(got, want, norm, TOL_F16, "fp16 width")
 
 
+# ------------------------------------------------- fp16 32x32 forward: folded and FMA waves
+def _norm_ramp_inputs(seed, B, M, N, D, C, rmax):
+    """Keys ~ N(0, I/D); queries in random directions with norms rising linearly from 0 to rmax
+    along the row index, so the waves of one launch go from small to large |q| (the folded form
+    of the 32x32 forward is open to the first and closed to the last); weights ~ N(0, 1)."""
+    rng = np.random.default_rng(seed)
+    u = rng.standard_normal((B, M, D))
+    u /= np.linalg.norm(u, axis=-1, keepdims=True)
+    r = np.linspace(0.0, rmax, M)[None, :, None]
+    q = (u * r).astype(np.float16)
+    k = (rng.standard_normal((B, N, D)) / np.sqrt(D)).astype(np.float16)
+    v = rng.standard_normal((B, N, C)).astype(np.float16)
+    return q, k, v
+
+
+FOLD_CASES = [
+    # (kind, B, M, N, D, C, sigma): "plain" N(0, I/D) points, "ramp" query norms 0..4, "offset"
+    # every point moved by +1.5 per feature (|q| ~ 8: no wave folds)
+    ("plain", 2, 2100, 6000, 32, 32, 1.0), ("ramp", 2, 2100, 6000, 32, 32, 1.0), ("ramp", 1, 3000, 4100, 24, 20, 0.8),
+    ("offset", 1, 1100, 3000, 32, 32, 1.0), ("plain", 1, 1025, 20000, 32, 32, 0.6),
+]
+
+
+@pytest.mark.parametrize("kind,B,M,N,D,C,sigma", FOLD_CASES)
+def test_gauss_sum_fp16_32x32_folded_and_fma_waves(kind, B, M, N, D, C, sigma):
+    """The 32x32 fp16 forward keeps cs S + alpha per value or, per wave, folds cs into the query
+    operands with one shift for the wave's rows; both forms, mixed in one launch, against the
+    oracle."""
+    import pairwise_reductions_amd as pr
+    _announce("fp16_32x32_fold", kind=kind, B=B, M=M, N=N, D=D, C=C, sigma=sigma)
+    if kind == "ramp":
+        q, k, v = _norm_ramp_inputs(B * 11 + M + N, B, M, N, D, C, 4.0)
+    else:
+        q, k, v = _highd_inputs(B * 13 + M + N, B, M, N, D, C)
+        if kind == "offset":
+            q = (q.astype(np.float32) + 1.5).astype(np.float16)
+            k = (k.astype(np.float32) + 1.5).astype(np.float16)
+    sig = float(np.float32(sigma))
+    got = _host(pr.gauss_sum(_dev(q), _dev(k), _dev(v), sig))
+    want, norm = oracle.gauss_sum_batched(q, k, v, 1.0 / (sig * sig), workers=8)
+    assert_normalised(got, want, norm, TOL_F16, f"32x32 fp16 {kind}")
+
+
 # ------------------------------------------------------------------ fp16 backward
 BWD_SHAPES = [
     # (B, M, N, D, C, sigma)
