@@ -60,6 +60,66 @@ constexpr int padded_k_channels(int C) { return C <= 32 ? 32 : 64; }
 
 __device__ __forceinline__ float exp2_hw(float v) { return __builtin_amdgcn_exp2f(v); }
 
+// Folded form of the fp16 forward sweeps. Once a wave's rows are settled, the per-value FMA
+// cs S' + alpha can go: with the query operands replaced by qs = fp16(cs q) and the accumulator
+// starting from cs beta (kept in LDS beside beta), the MFMA returns the unshifted exponent
+// itself, and each row's own shift alpha_i moves into its output scale (O_i is multiplied by
+// 2^-alpha_i once). That needs alpha_i in [-kFoldLow, kFoldHigh]: later terms, at most 2^kSlack
+// under the row shift, stay below 2^(kSlack + kFoldLow) = 2^15 (fp16 holds up to 65504), and no
+// row's terms move more than kFoldHigh binades towards the fp16 subnormals. The rounding of cs q
+// moves each exponent by e_ij = sum_d (qs_d - cs q_d) k_jd, |e_ij| <= |qs_i - cs q_i| |k_j|; a
+// wave takes the folded form only where that bound, with the largest |k_j| of its column split,
+// is at most 2^-9.5: each term then changes by a factor within 2^(+-2^-9.5), i.e. by less than
+// 9.6e-4, and with the fp16 rounding of P (2^-11) by less than 1.45e-3 in all, inside the fp16
+// path's 2e-3. Otherwise it keeps the FMA.
+constexpr float kFoldLow = 7.0f, kFoldHigh = 4.0f;
+// Largest |qs - cs q|^2 |k|^2 of the folded form: (2^-9.5)^2, less 2^-8 of it for the float32
+// rounding of the quantities it is computed from.
+constexpr float kFoldErr2 = 1.9073486328125e-06f * (1.0f - 0.00390625f);
+
+// Largest squared key norm over the keys [j0, j1) of a column split, from beta_j <= -|k_j|^2/2,
+// left by every wave in red[wave] (read after the next barrier).
+__device__ __forceinline__ void fold_key_norm(const float* bb, int64_t j0, int64_t j1, int tid, int nthreads,
+                                              int lane, int wave, float* red) {
+  float kn = 0.0f;
+  for (int64_t j = j0 + tid; j < j1; j += nthreads) kn = fmaxf(kn, -2.0f * bb[j]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) kn = fmaxf(kn, __shfl_xor(kn, o));
+  if (lane == 0) red[wave] = kn;
+}
+
+// Squared rounding error of fp16(cs x) over the 8 features of one operand, accumulated into d2;
+// fits turns false where a product leaves the fp16 range.
+__device__ __forceinline__ void fold_rounding(const half8& x, float cs, float& d2, bool& fits) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float cq = cs * (float)x[e];
+    fits = fits && fabsf(cq) < 65504.0f;
+    const float dd = fits ? (float)(_Float16)cq - cq : 0.0f;
+    d2 = fmaf(dd, dd, d2);
+  }
+}
+
+// The wave's decision: shifts in range, every product finite, and the rounding bound met
+// (amin, amax over the lane's rows; d2 the largest full-row squared rounding error of its rows;
+// kn2 the split's largest squared key norm).
+__device__ __forceinline__ bool fold_decide(float amin, float amax, float d2, bool fits, float kn2) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    amin = fminf(amin, __shfl_xor(amin, o));
+    amax = fmaxf(amax, __shfl_xor(amax, o));
+    d2 = fmaxf(d2, __shfl_xor(d2, o));
+  }
+  return __all(fits) && (amin >= -kFoldLow) && (amax <= kFoldHigh) && (d2 * kn2 <= kFoldErr2);
+}
+
+__device__ __forceinline__ half8 fold_scale(const half8& x, float cs) {
+  half8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = (_Float16)(cs * (float)x[e]);
+  return r;
+}
+
 __host__ __device__ inline int64_t hd_ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline int64_t padded_keys(int64_t N) { return hd_ceil_div(N, kKeyPad) * kKeyPad; }
 

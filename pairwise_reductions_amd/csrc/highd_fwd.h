@@ -131,6 +131,11 @@ fwd_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const float* __
   __shared__ __attribute__((aligned(16))) Raw sK[NP][2][kStage][KP];
   __shared__ __attribute__((aligned(16))) _Float16 sV[NP][2][NSUB][C][VP];
   __shared__ __attribute__((aligned(16))) float sB[2][kStage];
+  // fp16 inputs take the folded form of highd_common.h once a wave's rows are settled; cs beta
+  // is kept beside beta for it
+  constexpr bool kFoldable = std::is_same<TIn, _Float16>::value;
+  __shared__ __attribute__((aligned(16))) float sBs[2][kFoldable ? kStage : 4];
+  __shared__ float sKn[kW];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, l16 = lane & 15;
@@ -218,11 +223,15 @@ fwd_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const float* __
         if (c < kVChunks) *reinterpret_cast<half8*>(&sV[p][buf][t][rem / 4][(rem % 4) * 8]) = rv[p][r];
       }
     }
-    if (tid < kStage / 4) *reinterpret_cast<f32x4*>(&sB[buf][4 * tid]) = rb;
+    if (tid < kStage / 4) {
+      *reinterpret_cast<f32x4*>(&sB[buf][4 * tid]) = rb;
+      if constexpr (kFoldable) *reinterpret_cast<f32x4*>(&sBs[buf][4 * tid]) = rb * cs;
+    }
   };
 
   // S'^T of one 32-key subtile for every query tile: S[qt][half] holds keys 16*half + 4g + v.
-  auto scores = [&](int buf, int sub, f32x4 (&S)[QT][2]) {
+  auto scores = [&](int buf, int sub, f32x4 (&S)[QT][2], auto folded) {
+    const float* srcb = decltype(folded)::value ? &sBs[buf][0] : &sB[buf][0];
     Op<TIn> kop[2][DS];
     f32x4 bc[2];
 #pragma unroll
@@ -233,7 +242,7 @@ fwd_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const float* __
         kop[hh][ds].h = *reinterpret_cast<const Raw8*>(&sK[0][buf][key][col]);
         if constexpr (SPLIT) kop[hh][ds].l = *reinterpret_cast<const half8*>(&sK[NP - 1][buf][key][col]);
       }
-      bc[hh] = *reinterpret_cast<const f32x4*>(&sB[buf][sub * 32 + 16 * hh + 4 * g]);
+      bc[hh] = *reinterpret_cast<const f32x4*>(srcb + sub * 32 + 16 * hh + 4 * g);
     }
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt)
@@ -244,8 +253,9 @@ fwd_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const float* __
         for (int ds = 1; ds < DS; ++ds) S[qt][hh] = s_mfma<TIn>(kop[hh][ds], qop[qt][ds], S[qt][hh]);
       }
   };
-  // P = 2^(c S' + alpha) in fp16 (hi and lo parts when split) and O^T += V^T P^T.
-  auto accumulate = [&](int buf, int sub, const f32x4 (&S)[QT][2]) {
+  // P = 2^(c S' + alpha) in fp16 (hi and lo parts when split; 2^S' in the folded form) and
+  // O^T += V^T P^T.
+  auto accumulate = [&](int buf, int sub, const f32x4 (&S)[QT][2], auto folded) {
     half8 vop[NP][CT];
 #pragma unroll
     for (int p = 0; p < NP; ++p)
@@ -257,7 +267,8 @@ fwd_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const float* __
       half8 ph, pl;
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
-        const float pv = exp2_hw(fmaf(S[qt][s >> 2][s & 3], cs, alpha[qt]));
+        const float e = S[qt][s >> 2][s & 3];
+        const float pv = exp2_hw(decltype(folded)::value ? e : fmaf(e, cs, alpha[qt]));
         ph[s] = (_Float16)pv;
         if constexpr (SPLIT) pl[s] = (_Float16)(pv - (float)ph[s]);
       }
@@ -298,16 +309,16 @@ fwd_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const float* __
   };
   // One stage, scores of every query tile first; both phases execute one barrier per stage,
   // so the workgroup stays in step.
-  auto stage_batched = [&](int64_t st, auto track) {
+  auto stage_batched = [&](int64_t st, auto track, auto folded) {
     constexpr bool kTrack = decltype(track)::value;
     const int buf = (int)(st & 1);
     if (st + 1 < nstages) fetch(st + 1);
 #pragma unroll
     for (int sub = 0; sub < NSUB; ++sub) {
       f32x4 S[QT][2];
-      scores(buf, sub, S);
+      scores(buf, sub, S, folded);
       if constexpr (kTrack) track_rows(S);
-      accumulate(buf, sub, S);
+      accumulate(buf, sub, S, folded);
     }
     if (st + 1 < nstages) commit(buf ^ 1);
     __syncthreads();
@@ -401,7 +412,8 @@ fwd_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const float* __
     f32x4 b[2];
     half8 v[NP][CT];
   };
-  auto read_operands = [&](int buf, int sub, Operands& o) {
+  auto read_operands = [&](int buf, int sub, Operands& o, auto folded) {
+    const float* srcb = decltype(folded)::value ? &sBs[buf][0] : &sB[buf][0];
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll
@@ -410,7 +422,7 @@ fwd_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const float* __
         o.k[hh][ds].h = *reinterpret_cast<const Raw8*>(&sK[0][buf][key][col]);
         if constexpr (SPLIT) o.k[hh][ds].l = *reinterpret_cast<const half8*>(&sK[NP - 1][buf][key][col]);
       }
-      o.b[hh] = *reinterpret_cast<const f32x4*>(&sB[buf][sub * 32 + 16 * hh + 4 * g]);
+      o.b[hh] = *reinterpret_cast<const f32x4*>(srcb + sub * 32 + 16 * hh + 4 * g);
     }
 #pragma unroll
     for (int p = 0; p < NP; ++p)
@@ -426,18 +438,18 @@ fwd_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const float* __
       for (int ds = 1; ds < DS; ++ds) S[hh] = s_mfma<TIn>(o.k[hh][ds], qop[qt][ds], S[hh]);
     }
   };
-  auto stage_pipe = [&](int64_t st) {
+  auto stage_pipe = [&](int64_t st, auto folded) {
     const int buf = (int)(st & 1);
     if (st + 1 < nstages) fetch(st + 1);
     Operands ops[2];
-    read_operands(buf, 0, ops[0]);
+    read_operands(buf, 0, ops[0], folded);
     f32x4 Sbuf[2][2];
     score_with(ops[0], 0, Sbuf[0]);
 #pragma unroll
     for (int u = 0; u < NSUB * QT; ++u) {
       const int sub = u / QT, qt = u % QT;
       const Operands& cur = ops[sub & 1];
-      if (qt == 0 && sub + 1 < NSUB) read_operands(buf, sub + 1, ops[(sub + 1) & 1]);
+      if (qt == 0 && sub + 1 < NSUB) read_operands(buf, sub + 1, ops[(sub + 1) & 1], folded);
       if (u + 1 < NSUB * QT) {
         if (qt + 1 < QT)
           score_with(cur, qt + 1, Sbuf[(u + 1) & 1]);
@@ -448,7 +460,8 @@ fwd_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const float* __
       half8 ph, pl;
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
-        const float pv = exp2_hw(fmaf(S[s >> 2][s & 3], cs, alpha[qt]));
+        const float e = S[s >> 2][s & 3];
+        const float pv = exp2_hw(decltype(folded)::value ? e : fmaf(e, cs, alpha[qt]));
         ph[s] = (_Float16)pv;
         if constexpr (SPLIT) pl[s] = (_Float16)(pv - (float)ph[s]);
       }
@@ -465,16 +478,61 @@ fwd_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const float* __
     __syncthreads();
   };
 
+  if constexpr (kFoldable) fold_key_norm(bb, j0, j1, tid, kThreads, lane, wave, sKn);
   fetch(0);
   commit(0);
   __syncthreads();
   int64_t st = 0;
   if constexpr (kFused) {
     for (; st < nstages && !settled; ++st) stage_fused(st, std::true_type{});
-    for (; st < nstages; ++st) stage_pipe(st);
   } else {
-    for (; st < nstages && !settled; ++st) stage_batched(st, std::true_type{});
-    for (; st < nstages; ++st) stage_batched(st, std::false_type{});
+    for (; st < nstages && !settled; ++st) stage_batched(st, std::true_type{}, std::false_type{});
+  }
+  bool folded = false;
+  if constexpr (kFoldable) {
+    if (settled && st < nstages) {
+      float kn2 = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kW; ++w) kn2 = fmaxf(kn2, sKn[w]);
+      float amin = alpha[0], amax = alpha[0], d2 = 0.0f;
+      bool fits = true;  // every cs q_d rounds to a finite fp16 value
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        amin = fminf(amin, alpha[qt]);
+        amax = fmaxf(amax, alpha[qt]);
+        float dq = 0.0f;
+#pragma unroll
+        for (int ds = 0; ds < DS; ++ds) fold_rounding(qop[qt][ds].h, cs, dq, fits);
+        dq += __shfl_xor(dq, 16);
+        dq += __shfl_xor(dq, 32);
+        d2 = fmaxf(d2, dq);
+      }
+      folded = fold_decide(amin, amax, d2, fits, kn2);
+      if (folded) {
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) {
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) O[qt][ct] *= exp2_hw(-alpha[qt]);
+          mrow[qt] += alpha[qt];
+          alpha[qt] = 0.0f;
+#pragma unroll
+          for (int ds = 0; ds < DS; ++ds) qop[qt][ds].h = fold_scale(qop[qt][ds].h, cs);
+        }
+      }
+    }
+  }
+  for (; st < nstages; ++st) {
+    if constexpr (kFused) {
+      if (kFoldable && folded)
+        stage_pipe(st, std::true_type{});
+      else
+        stage_pipe(st, std::false_type{});
+    } else {
+      if (kFoldable && folded)
+        stage_batched(st, std::false_type{}, std::true_type{});
+      else
+        stage_batched(st, std::false_type{}, std::false_type{});
+    }
   }
 
   // Store the first Cout channels (C here is Cout rounded up to a multiple of 16).
@@ -516,9 +574,15 @@ hipError_t fwd_launch(const FwdArgs& a) {
              fwd_waves(Dp, Cv, kSplit<TIn>)>                                                                       \
       <<<a.grid, 64 * fwd_waves(Dp, Cv, kSplit<TIn>), 0, a.stream>>>(                                             \
       q, k, a.beta, a.vp, a.vpl, a.out, a.rscale, a.oscale, a.M, a.N, a.Npad, a.kps, a.cs, a.D, a.C)
-  if (Cp == 16) KEOPS_FWD(16);
-  else if (Cp == 32) KEOPS_FWD(32);
-  else KEOPS_FWD(64);
+  if (Cp == 16) {
+    KEOPS_FWD(16);
+  } else if (Cp == 32) {
+    // fp16 and bf16 at D = C = 32 (padded) run as fwd32_kernel
+    if constexpr (!kSplit<TIn> && Dp == 32) return hipErrorInvalidValue;
+    else KEOPS_FWD(32);
+  } else {
+    KEOPS_FWD(64);
+  }
 #undef KEOPS_FWD
   return hipGetLastError();
 }

@@ -14,16 +14,7 @@
 // are then exactly its B operands of the two P^T products when each 32-key subtile's weights
 // are stored in the slot32_key() order, so P never moves between lanes.
 //
-// Folded form (fp16 inputs). Once a wave's rows are settled, the per-value FMA cs S' + alpha
-// can go: with the query operands replaced by qs = fp16(cs q) and the accumulator starting from
-// cs beta (stored so in LDS beside beta), the MFMA returns the unshifted exponent itself. Each
-// row's own shift alpha_i moves into its output scale (O_i is multiplied by 2^-alpha_i once).
-// That needs alpha_i in [-kFoldLow, kFoldHigh]: later terms, at most 2^kSlack under the row
-// shift, stay below 2^(kSlack + kFoldLow) = 2^15 (fp16 holds up to 65504), and no row's terms
-// move more than kFoldHigh binades towards the fp16 subnormals. The rounding of cs q moves each
-// exponent by e_ij = sum_d (qs_d - cs q_d) k_jd, |e_ij| <= |qs_i - cs q_i| |k_j|; a wave takes
-// the folded form only where that bound, with the largest |k_j| of its column split, is at most
-// 2^-10 (a relative change of each term below 6.8e-4). Otherwise it keeps the FMA.
+// fp16 inputs take the folded form of highd_common.h once a wave's rows are settled.
 #pragma once
 
 #include "highd_common.h"
@@ -57,12 +48,6 @@ __device__ __forceinline__ f32x16 mfma32_s(const typename Raw8Of<TIn>::type& a, 
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// Range of the row shifts of a wave that takes the folded form (binades).
-constexpr float kFoldLow = 7.0f, kFoldHigh = 4.0f;
-// Largest |qs - cs q|^2 |k|^2 of the folded form: (2^-10)^2, less 2^-8 of it for the float32
-// rounding of the quantities it is computed from.
-constexpr float kFoldErr2 = 9.5367431640625e-07f * (1.0f - 0.00390625f);
-
 template <typename TIn, int QT, int kStage, int kW>
 __global__ void __launch_bounds__(64 * kW, 1)
 fwd32_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const float* __restrict__ beta,
@@ -81,7 +66,7 @@ fwd32_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const float* 
   __shared__ __attribute__((aligned(16))) _Float16 sV[2][NSUB][C][VP];
   constexpr bool kFoldable = std::is_same<TIn, _Float16>::value;
   __shared__ __attribute__((aligned(16))) float sB[2][kStage];
-  __shared__ __attribute__((aligned(16))) float sBs[kFoldable ? 2 : 1][kFoldable ? kStage : 4];  // cs beta
+  __shared__ __attribute__((aligned(16))) float sBs[2][kFoldable ? kStage : 4];  // cs beta
   __shared__ float sKn[kW];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -267,14 +252,7 @@ fwd32_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const float* 
     __syncthreads();
   };
 
-  // Largest squared key norm of the split (beta_j <= -|k_j|^2 / 2 for every key in it).
-  if constexpr (kFoldable) {
-    float kn = 0.0f;
-    for (int64_t j = j0 + tid; j < j1; j += kThreads) kn = fmaxf(kn, -2.0f * bb[j]);
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) kn = fmaxf(kn, __shfl_xor(kn, o));
-    if (lane == 0) sKn[wave] = kn;
-  }
+  if constexpr (kFoldable) fold_key_norm(bb, j0, j1, tid, kThreads, lane, wave, sKn);
   fetch(0);
   commit(0);
   __syncthreads();
@@ -294,24 +272,11 @@ fwd32_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const float* 
         amax = fmaxf(amax, alpha[qt]);
         float dq = 0.0f;
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float cq = cs * (float)qop[qt][kk][e];
-            fits = fits && fabsf(cq) < 65504.0f;
-            const float dd = fits ? (float)(_Float16)cq - cq : 0.0f;
-            dq = fmaf(dd, dd, dq);
-          }
+        for (int kk = 0; kk < 2; ++kk) fold_rounding(qop[qt][kk], cs, dq, fits);
         dq += __shfl_xor(dq, 32);
         d2 = fmaxf(d2, dq);
       }
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) {
-        amin = fminf(amin, __shfl_xor(amin, o));
-        amax = fmaxf(amax, __shfl_xor(amax, o));
-        d2 = fmaxf(d2, __shfl_xor(d2, o));
-      }
-      folded = __all(fits) && (amin >= -kFoldLow) && (amax <= kFoldHigh) && (d2 * kn2 <= kFoldErr2);
+      folded = fold_decide(amin, amax, d2, fits, kn2);
       if (folded) {
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) {
@@ -319,15 +284,13 @@ fwd32_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const float* 
           mrow[qt] += alpha[qt];
           alpha[qt] = 0.0f;
 #pragma unroll
-          for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) qop[qt][kk][e] = (Raw)(cs * (float)qop[qt][kk][e]);
+          for (int kk = 0; kk < 2; ++kk) qop[qt][kk] = fold_scale(qop[qt][kk], cs);
         }
       }
     }
   }
   for (; st < nstages; ++st) {
-    if (folded)
+    if (kFoldable && folded)
       stage_pipe(st, std::true_type{});
     else
       stage_pipe(st, std::false_type{});

@@ -40,11 +40,11 @@ def test_gauss_sum_fp16_feature_widths(B, M, N, D, C, sigma):
     assert_normalised(got, want, norm, TOL_F16, "fp16 width")
 
 
-# ------------------------------------------------- fp16 32x32 forward: folded and FMA waves
+# ---------------------------------------------------- fp16 forward: folded and FMA waves
 def _norm_ramp_inputs(seed, B, M, N, D, C, rmax):
     """Keys ~ N(0, I/D); queries in random directions with norms rising linearly from 0 to rmax
     along the row index, so the waves of one launch go from small to large |q| (the folded form
-    of the 32x32 forward is open to the first and closed to the last); weights ~ N(0, 1)."""
+    of the fp16 forward is open to the first and closed to the last); weights ~ N(0, 1)."""
     rng = np.random.default_rng(seed)
     u = rng.standard_normal((B, M, D))
     u /= np.linalg.norm(u, axis=-1, keepdims=True)
@@ -60,16 +60,19 @@ FOLD_CASES = [
     # every point moved by +1.5 per feature (|q| ~ 8: no wave folds)
     ("plain", 2, 2100, 6000, 32, 32, 1.0), ("ramp", 2, 2100, 6000, 32, 32, 1.0), ("ramp", 1, 3000, 4100, 24, 20, 0.8),
     ("offset", 1, 1100, 3000, 32, 32, 1.0), ("plain", 1, 1025, 20000, 32, 32, 0.6),
+    # the 16x16x32 forward (C <= 16, or D > 32): the same two forms
+    ("plain", 2, 2100, 6000, 32, 1, 1.0), ("ramp", 1, 3000, 4100, 64, 8, 0.8), ("ramp", 2, 1500, 3000, 128, 64, 1.2),
+    ("plain", 1, 1025, 9000, 96, 16, 1.0), ("offset", 1, 1100, 3000, 64, 3, 1.0), ("plain", 3, 700, 2500, 20, 2, 0.7),
 ]
 
 
 @pytest.mark.parametrize("kind,B,M,N,D,C,sigma", FOLD_CASES)
-def test_gauss_sum_fp16_32x32_folded_and_fma_waves(kind, B, M, N, D, C, sigma):
-    """The 32x32 fp16 forward keeps cs S + alpha per value or, per wave, folds cs into the query
-    operands with one shift for the wave's rows; both forms, mixed in one launch, against the
-    oracle."""
+def test_gauss_sum_fp16_folded_and_fma_waves(kind, B, M, N, D, C, sigma):
+    """The fp16 forward sweeps (32x32x16 and 16x16x32 tiles) keep cs S + alpha per value or, per
+    wave, fold cs into the query operands and move the row shifts into the output scale; both
+    forms, mixed in one launch, against the oracle."""
     import pairwise_reductions_amd as pr
-    _announce("fp16_32x32_fold", kind=kind, B=B, M=M, N=N, D=D, C=C, sigma=sigma)
+    _announce("fp16_fold", kind=kind, B=B, M=M, N=N, D=D, C=C, sigma=sigma)
     if kind == "ramp":
         q, k, v = _norm_ramp_inputs(B * 11 + M + N, B, M, N, D, C, 4.0)
     else:
@@ -80,7 +83,7 @@ def test_gauss_sum_fp16_32x32_folded_and_fma_waves(kind, B, M, N, D, C, sigma):
     sig = float(np.float32(sigma))
     got = _host(pr.gauss_sum(_dev(q), _dev(k), _dev(v), sig))
     want, norm = oracle.gauss_sum_batched(q, k, v, 1.0 / (sig * sig), workers=8)
-    assert_normalised(got, want, norm, TOL_F16, f"32x32 fp16 {kind}")
+    assert_normalised(got, want, norm, TOL_F16, f"fp16 forward {kind}")
 
 
 # ------------------------------------------------------------------ fp16 backward
