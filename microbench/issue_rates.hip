@@ -180,7 +180,11 @@ __global__ void __launch_bounds__(256) unit_kernel(float* out, float seed) {
 // 4 query tiles of 32; for each tile the scores of the next one are issued (2 MFMAs, K = 16 each
 // for 32 features), then P = fp16(2^(cs S + alpha)) of the current one (16 values per lane),
 // then O += V P (2 MFMAs for 32 channels, K = 16 keys each). One iteration is 8 units of 512
-// pairs, as in unit_kernel.
+// pairs, as in unit_kernel. kMode 0: as described. kMode 1: the scale is in the query operand
+// and one shift serves the wave, so the accumulator starts from beta + u (16 adds per subtile,
+// shared by the 4 tiles) and P = fp16(2^S) needs no FMA. kMode 2: as 1 with the scaled query
+// in two fp16 parts (hi + lo), i.e. 4 MFMAs for the scores.
+template <int kMode>
 __global__ void __launch_bounds__(256) unit32_kernel(float* out, float seed) {
   half8 k0, k1, v0, v1, q0[4], q1[4];
 #pragma unroll
@@ -203,21 +207,33 @@ __global__ void __launch_bounds__(256) unit32_kernel(float* out, float seed) {
   for (int t = 0; t < 4; ++t) alpha[t] = -0.5f - 0.01f * t;
   f32x16 O[4] = {};
   const float cs = 1.4427f;
+  float u = -0.75f;
   for (int it = 0; it < kIters / 8; ++it) {
-    asm volatile("" : "+v"(k0), "+v"(k1), "+v"(v0), "+v"(v1));
+    asm volatile("" : "+v"(k0), "+v"(k1), "+v"(v0), "+v"(v1), "+v"(beta), "+s"(u));
+    f32x16 bu = beta;
+    if constexpr (kMode > 0) {
+#pragma unroll
+      for (int s = 0; s < 16; ++s) bu[s] = beta[s] + u;
+    }
+    auto score = [&](int qt) {
+      f32x16 S = __builtin_amdgcn_mfma_f32_32x32x16_f16(k0, q0[qt], bu, 0, 0, 0);
+      S = __builtin_amdgcn_mfma_f32_32x32x16_f16(k1, q1[qt], S, 0, 0, 0);
+      if constexpr (kMode == 2) {
+        S = __builtin_amdgcn_mfma_f32_32x32x16_f16(k0, q1[qt], S, 0, 0, 0);
+        S = __builtin_amdgcn_mfma_f32_32x32x16_f16(k1, q0[qt], S, 0, 0, 0);
+      }
+      return S;
+    };
     f32x16 S[2];
-    S[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(k0, q0[0], beta, 0, 0, 0);
-    S[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(k1, q1[0], S[0], 0, 0, 0);
+    S[0] = score(0);
 #pragma unroll
     for (int qt = 0; qt < 4; ++qt) {
-      if (qt + 1 < 4) {
-        S[(qt + 1) & 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(k0, q0[qt + 1], beta, 0, 0, 0);
-        S[(qt + 1) & 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(k1, q1[qt + 1], S[(qt + 1) & 1], 0, 0, 0);
-      }
+      if (qt + 1 < 4) S[(qt + 1) & 1] = score(qt + 1);
       half8 pa, pb;
 #pragma unroll
       for (int s = 0; s < 16; ++s) {
-        const float e = fmaf(S[qt & 1][s], cs, alpha[qt]);
+        float e = S[qt & 1][s];
+        if constexpr (kMode == 0) e = fmaf(e, cs, alpha[qt]);
         const _Float16 h = (_Float16)__builtin_amdgcn_exp2f(e);
         if (s < 8) pa[s] = h;
         else pb[s - 8] = h;
@@ -318,7 +334,7 @@ int main() {
   int cus = 0;
   check(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, 0), "hipDeviceGetAttribute");
   std::printf("%-40s %12s %12s %12s\n", "ns per iteration per wave", "1 wave/SIMD", "2 waves/SIMD", "4 waves/SIMD");
-  double t[3][kKinds + 5];
+  double t[3][kKinds + 7];
   for (int w = 0; w < 3; ++w) {
     const int wps = 1 << w;
     const int blocks = cus * wps;  // 4 waves per workgroup: wps waves on every SIMD
@@ -329,10 +345,12 @@ int main() {
     t[w][kKinds + 1] = time_ms([&] { unit_kernel<false><<<blocks, 256>>>(out, 1.0f); }, 5);
     t[w][kKinds + 2] = time_ms([&] { sum_tile_kernel<false><<<blocks, 256>>>(out, 1.0f); }, 5);
     t[w][kKinds + 3] = time_ms([&] { sum_tile_kernel<true><<<blocks, 256>>>(out, 1.0f); }, 5) / 2.0;
-    t[w][kKinds + 4] = time_ms([&] { unit32_kernel<<<blocks, 256>>>(out, 1.0f); }, 5);
+    t[w][kKinds + 4] = time_ms([&] { unit32_kernel<0><<<blocks, 256>>>(out, 1.0f); }, 5);
+    t[w][kKinds + 5] = time_ms([&] { unit32_kernel<1><<<blocks, 256>>>(out, 1.0f); }, 5);
+    t[w][kKinds + 6] = time_ms([&] { unit32_kernel<2><<<blocks, 256>>>(out, 1.0f); }, 5);
     check(hipGetLastError(), "launch");
     check(hipFree(out), "hipFree");
-    for (int k = 0; k < kKinds + 5; ++k) t[w][k] = t[w][k] * 1e6 / kIters / wps;
+    for (int k = 0; k < kKinds + 7; ++k) t[w][k] = t[w][k] * 1e6 / kIters / wps;
   }
   for (int k = 0; k < kKinds; ++k)
     std::printf("%-40s %12.2f %12.2f %12.2f\n", kNames[k], t[0][k], t[1][k], t[2][k]);
@@ -342,6 +360,10 @@ int main() {
               t[1][kKinds + 1], t[2][kKinds + 1]);
   std::printf("%-40s %12.2f %12.2f %12.2f   (per 512-pair unit)\n", "fp16 forward unit on 32x32x16 tiles",
               t[0][kKinds + 4], t[1][kKinds + 4], t[2][kKinds + 4]);
+  std::printf("%-40s %12.2f %12.2f %12.2f   (per 512-pair unit)\n", "fp16 unit, 32x32, wave shift, no FMA",
+              t[0][kKinds + 5], t[1][kKinds + 5], t[2][kKinds + 5]);
+  std::printf("%-40s %12.2f %12.2f %12.2f   (per 512-pair unit)\n", "fp16 unit, 32x32, wave shift, hi+lo q",
+              t[0][kKinds + 6], t[1][kKinds + 6], t[2][kKinds + 6]);
   std::printf("%-40s %12.2f %12.2f %12.2f   (per 1024 pairs)\n", "Gauss-sum tile, 16x16x32, 4 row tiles",
               t[0][kKinds + 2] * 8, t[1][kKinds + 2] * 8, t[2][kKinds + 2] * 8);
   std::printf("%-40s %12.2f %12.2f %12.2f   (per 1024 pairs)\n", "Gauss-sum tile, 32x32x16, 2 row tiles",
