@@ -86,6 +86,34 @@ def test_gauss_sum_fp16_folded_and_fma_waves(kind, B, M, N, D, C, sigma):
     assert_normalised(got, want, norm, TOL_F16, f"fp16 forward {kind}")
 
 
+BWD_RAMP_CASES = [
+    # (kind, B, M, N, D, C, sigma): query norms rising along the rows, plain and offset points
+    ("ramp", 2, 2100, 3000, 32, 1, 1.0), ("ramp", 1, 1500, 2000, 64, 3, 0.8), ("plain", 1, 1100, 2500, 32, 16, 1.0),
+    ("offset", 1, 700, 1500, 32, 2, 1.0),
+]
+
+
+@pytest.mark.parametrize("kind,B,M,N,D,C,sigma", BWD_RAMP_CASES)
+def test_gauss_sum_backward_fp16_norm_ramp_and_offset(kind, B, M, N, D, C, sigma):
+    """x, y and b gradients for queries whose norms rise from 0 to 4 along the rows (row shifts
+    of every size in one launch), plain N(0, I/D) points and points moved far from the origin."""
+    import pairwise_reductions_amd as pr
+    _announce("backward_fp16_ramp", kind=kind, B=B, M=M, N=N, D=D, C=C, sigma=sigma)
+    if kind == "ramp":
+        q, k, v = _norm_ramp_inputs(B * 17 + M + N, B, M, N, D, C, 4.0)
+    else:
+        q, k, v = _highd_inputs(B * 19 + M + N, B, M, N, D, C)
+        if kind == "offset":
+            q = (q.astype(np.float32) + 1.5).astype(np.float16)
+            k = (k.astype(np.float32) + 1.5).astype(np.float16)
+    g = workloads.upstream_gradient(M, C, seed=M + N + D, B=B)
+    sig = float(np.float32(sigma))
+    got = pr.gauss_sum_backward(_dev(q), _dev(k), _dev(v), _dev(g), sig)
+    want = _oracle_backward(q, k, v, g, sig)
+    for key in ("x", "y", "b"):
+        assert_normalised(_host(got[key]), want[key][0], want[key][1], TOL_F16, f"backward {kind} {key}")
+
+
 # ------------------------------------------------------------------ fp16 backward
 BWD_SHAPES = [
     # (B, M, N, D, C, sigma)
