@@ -14,6 +14,8 @@
 // copies the weights unchanged.
 #include "highd_common.h"
 
+#include <type_traits>
+
 #include <math.h>
 
 namespace keops {
@@ -101,15 +103,30 @@ col_prep_kernel(const TK* __restrict__ k, const T* __restrict__ w, const float* 
 #pragma unroll
     for (int u = 0; u < EV; ++u) sk[key][d + u] = to_f32(v[u]);
   }
-  // weights, times the column scale
-  for (int e = tid; e < 32 * C; e += 256) {
-    const int key = e / C, c = e % C;
-    float v = 0.0f;
-    if (key < live) {
-      v = to_f32(w[(t * N + j0) * C + e]);
-      if (cscale) v *= cscale[t * N + j0 + key];
+  // weights, times the column scale (fp16 rows of a multiple of 8 channels in 16-byte vectors)
+  if (std::is_same<T, _Float16>::value && C % 8 == 0) {
+    typedef T t8 __attribute__((ext_vector_type(8)));
+    for (int c8 = tid; c8 < 32 * C / 8; c8 += 256) {
+      const int key = (8 * c8) / C, c = (8 * c8) % C;
+      t8 v = t8{};
+      float sc = 1.0f;
+      if (key < live) {
+        v = *reinterpret_cast<const t8*>(w + (t * N + j0) * C + 8 * c8);
+        if (cscale) sc = cscale[t * N + j0 + key];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) sw[key][c + u] = to_f32(v[u]) * sc;
     }
-    sw[key][c] = v;
+  } else {
+    for (int e = tid; e < 32 * C; e += 256) {
+      const int key = e / C, c = e % C;
+      float v = 0.0f;
+      if (key < live) {
+        v = to_f32(w[(t * N + j0) * C + e]);
+        if (cscale) v *= cscale[t * N + j0 + key];
+      }
+      sw[key][c] = v;
+    }
   }
   __syncthreads();
 
@@ -167,15 +184,22 @@ col_prep_kernel(const TK* __restrict__ k, const T* __restrict__ w, const float* 
       yd[e] = v;
     }
   } else {
-    // forward layout; with wpl the fp16 lo parts of float32 weights as well
+    // forward layout, 8 slots per 16-byte store; with wpl the fp16 lo parts of float32 weights
+    // as well
     _Float16* dst = wp + (t * Npad + j0) * Cw;
     _Float16* dsl = wpl ? wpl + (t * Npad + j0) * Cw : nullptr;
-    for (int e = tid; e < 32 * Cw; e += 256) {
-      const int c = e / 32, key = perm32 ? hd::slot32_key(e % 32) : slot_key(e % 32);
-      const float v = c < C ? sw[key][c] * sinv[key] : 0.0f;
-      const _Float16 h = (_Float16)v;
-      dst[e] = h;
-      if (dsl) dsl[e] = (_Float16)(v - (float)h);
+    for (int e8 = tid; e8 < 4 * Cw; e8 += 256) {
+      const int c = e8 / 4, s0 = (e8 % 4) * 8;
+      hd::half8 h8, l8;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int key = perm32 ? hd::slot32_key(s0 + u) : slot_key(s0 + u);
+        const float v = c < C ? sw[key][c] * sinv[key] : 0.0f;
+        h8[u] = (_Float16)v;
+        l8[u] = (_Float16)(v - (float)h8[u]);
+      }
+      *reinterpret_cast<hd::half8*>(dst + 8 * e8) = h8;
+      if (dsl) *reinterpret_cast<hd::half8*>(dsl + 8 * e8) = l8;
     }
   }
 }
