@@ -84,7 +84,10 @@ typedef enum {
  *   - KEOPS_F16, KEOPS_BF16 (any 1 <= D <= 128), and KEOPS_F32 with 9 <= D <= 128: the
  *     matrix-core path, any B >= 1, 1 <= C <= 64. x, y, b are of the dtype; fp32
  *     accumulation. fp16 and bf16 inputs: the kernel values are rounded to fp16 before they
- *     multiply b. float32 inputs are split into fp16 high and low parts (three products per
+ *     multiply b. With fp16 inputs a block of rows may also take tau log2(e) into its rounded
+ *     fp16 query operands, but only where the resulting change of every kernel value is proven
+ *     below 9.6e-4 relative (from the rows' and the keys' norms); otherwise the scale is applied
+ *     in float32. float32 inputs are split into fp16 high and low parts (three products per
  *     step, float32 accuracy). Features run in steps of 32 and channels in tiles of 16 (both
  *     read as zero past D and C). When D is a multiple of 16, x and y must be 16-byte aligned
  *     and are read in place; any other D is first copied, zero-padded to the next multiple of
