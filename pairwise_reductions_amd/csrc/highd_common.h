@@ -113,6 +113,8 @@ __device__ __forceinline__ bool fold_decide(float amin, float amax, float d2, bo
   return __all(fits) && (amin >= -kFoldLow) && (amax <= kFoldHigh) && (d2 * kn2 <= kFoldErr2);
 }
 
+// The folded query operand: each feature times cs, rounded to fp16 (the rounding fold_rounding
+// measured).
 __device__ __forceinline__ half8 fold_scale(const half8& x, float cs) {
   half8 r;
 #pragma unroll
