@@ -63,6 +63,9 @@ FOLD_CASES = [
     # the 16x16x32 forward (C <= 16, or D > 32): the same two forms
     ("plain", 2, 2100, 6000, 32, 1, 1.0), ("ramp", 1, 3000, 4100, 64, 8, 0.8), ("ramp", 2, 1500, 3000, 128, 64, 1.2),
     ("plain", 1, 1025, 9000, 96, 16, 1.0), ("offset", 1, 1100, 3000, 64, 3, 1.0), ("plain", 3, 700, 2500, 20, 2, 0.7),
+    # the decision right before a last stage holding one key, or a ragged one; tiny row counts
+    ("plain", 1, 33, 129, 32, 32, 1.0), ("ramp", 2, 1025, 257, 32, 17, 1.0), ("plain", 1, 17, 130, 32, 1, 1.0),
+    ("plain", 2, 100, 200, 64, 8, 0.9), ("ramp", 1, 5, 65, 128, 3, 1.1),
 ]
 
 
