@@ -35,16 +35,17 @@ constexpr int fwd_query_tiles(int D, int C, bool split) {
 // keeps two waves per SIMD; elsewhere the tile-batched order runs faster (more independent
 // products in flight). Measured on the register counts of the compiled kernels.
 constexpr bool fwd_fused(int D, int C, bool split) {
-  return split ? (C == 64 && D >= 64) : ((D == 32 && C == 32) || (D == 64 && C == 64));
+  return split ? (C == 64 && D >= 64) : ((D == 32 && C <= 32) || (D == 64 && C == 64));
 }
-// Keys per LDS stage and waves per workgroup of the forward kernel. At D = C = 32 (fp16 or
+// Keys per LDS stage and waves per workgroup of the forward kernel. At D = 32, C <= 32 (fp16 or
 // bf16) eight waves (two per SIMD) share one stage of 128 keys: fewer stage barriers per key,
-// and the barrier keeps the two waves of a SIMD in step. Measured at B = 4, 16384^2: the sweep
-// took 186 us with four waves and 64-key stages, 175 us like this.
+// and the barrier keeps the two waves of a SIMD in step. Measured at B = 4, 16384^2: the
+// C = 32 sweep took 186 us with four waves and 64-key stages, 175 us like this; the C = 1
+// forward 0.167 -> 0.157 ms per call (with the software-pipelined stages of fwd_fused).
 constexpr int fwd_stage(int D, int C, bool split) {
-  return split ? 32 : ((D == 32 && C == 32) ? 128 : kStageKeys);
+  return split ? 32 : ((D == 32 && C <= 32) ? 128 : kStageKeys);
 }
-constexpr int fwd_waves(int D, int C, bool split) { return (!split && D == 32 && C == 32) ? 8 : kWaves; }
+constexpr int fwd_waves(int D, int C, bool split) { return (!split && D == 32 && C <= 32) ? 8 : kWaves; }
 // The gradient kernel holds three products per subtile, so it takes fewer.
 // (Sizes chosen so every instantiation fits 256 VGPRs, i.e. two waves per SIMD.)
 constexpr int grad_query_tiles(int D, int CK, int CB) { return D <= 32 ? (CK <= 32 && CB == 0 ? 4 : 2) : 1; }
