@@ -30,22 +30,25 @@ constexpr int fwd_query_tiles(int D, int C, bool split) {
   return split ? ((D <= 64 && C <= 32) || D == 32 ? 4 : (D > 64 && C == 64 ? 1 : 2))
                : ((D == 32 && C <= 32) ? 8 : (D <= 64 ? 4 : 2));
 }
-// Where scoring every query tile of a subtile before using them needs more than 256 VGPRs
-// (one wave per SIMD), the forward kernel scores and uses one tile at a time instead, which
-// keeps two waves per SIMD; elsewhere the tile-batched order runs faster (more independent
-// products in flight). Measured on the register counts of the compiled kernels.
+// The fused form scores and uses one query tile at a time while rows are tracked and runs
+// software-pipelined settled stages (fwd_kernel's stage_fused / stage_pipe); the other form
+// scores every tile of a subtile first. The fused form is taken with C <= 32 (measured faster
+// at every D with eight-wave, 128-key stages) and wherever the batched order would need more
+// than 256 VGPRs (one wave per SIMD), as at D = C = 64.
 constexpr bool fwd_fused(int D, int C, bool split) {
-  return split ? (C == 64 && D >= 64) : ((D == 32 && C <= 32) || (D == 64 && C == 64));
+  return split ? (C == 64 && D >= 64) : (C <= 32 || (D == 64 && C == 64));
 }
-// Keys per LDS stage and waves per workgroup of the forward kernel. At D = 32, C <= 32 (fp16 or
-// bf16) eight waves (two per SIMD) share one stage of 128 keys: fewer stage barriers per key,
-// and the barrier keeps the two waves of a SIMD in step. Measured at B = 4, 16384^2: the
-// C = 32 sweep took 186 us with four waves and 64-key stages, 175 us like this; the C = 1
-// forward 0.167 -> 0.157 ms per call (with the software-pipelined stages of fwd_fused).
+// Keys per LDS stage and waves per workgroup of the forward kernel. With C <= 32 (fp16 or bf16)
+// eight waves (two per SIMD) share one stage of 128 keys: fewer stage barriers per key, and the
+// barrier keeps the two waves of a SIMD in step (at D = 128 the stage takes 92 KB of LDS: one
+// such workgroup per CU, still two waves per SIMD). Measured at B = 4, 16384^2: the D = C = 32
+// sweep took 186 us with four waves and 64-key stages, 175 us like this; with the
+// software-pipelined stages of fwd_fused the C = 1 forward went 0.167 -> 0.157 ms per call, and
+// at B = 64, C = 1 the D = 64 / 128 sweeps 2.94 -> 2.71 / 5.54 -> 4.84 ms.
 constexpr int fwd_stage(int D, int C, bool split) {
-  return split ? 32 : ((D == 32 && C <= 32) ? 128 : kStageKeys);
+  return split ? 32 : (C <= 32 ? 128 : kStageKeys);
 }
-constexpr int fwd_waves(int D, int C, bool split) { return (!split && D == 32 && C <= 32) ? 8 : kWaves; }
+constexpr int fwd_waves(int D, int C, bool split) { return (!split && C <= 32) ? 8 : kWaves; }
 // The gradient kernel holds three products per subtile, so it takes fewer.
 // (Sizes chosen so every instantiation fits 256 VGPRs, i.e. two waves per SIMD.)
 constexpr int grad_query_tiles(int D, int CK, int CB) { return D <= 32 ? (CK <= 32 && CB == 0 ? 4 : 2) : 1; }
