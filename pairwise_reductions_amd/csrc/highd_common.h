@@ -44,11 +44,15 @@ constexpr bool fwd_fused(int D, int C, bool split) {
 // such workgroup per CU, still two waves per SIMD). Measured at B = 4, 16384^2: the D = C = 32
 // sweep took 186 us with four waves and 64-key stages, 175 us like this; with the
 // software-pipelined stages of fwd_fused the C = 1 forward went 0.167 -> 0.157 ms per call, and
-// at B = 64, C = 1 the D = 64 / 128 sweeps 2.94 -> 2.71 / 5.54 -> 4.84 ms.
+// at B = 64, C = 1 the D = 64 / 128 sweeps 2.94 -> 2.71 / 5.54 -> 4.84 ms. Float32 inputs (two
+// operand parts in LDS) take eight waves too, with 64-key stages at C <= 16 and at D = 32 (32
+// elsewhere, where 64 would spill): the B = 4, 16384^2, D = C = 32 sweep 0.558 -> 0.490 ms and the B = 64,
+// C = 1 D sweep 6.16 / 6.21 / 7.90 / 17.6 -> 5.44 / 5.48 / 7.47 / 14.7 ms at D = 16 / 32 / 64 /
+// 128, against four waves and 32-key stages.
 constexpr int fwd_stage(int D, int C, bool split) {
-  return split ? 32 : (C <= 32 ? 128 : kStageKeys);
+  return split ? ((C <= 16 || (D == 32 && C <= 32)) ? 64 : 32) : (C <= 32 ? 128 : kStageKeys);
 }
-constexpr int fwd_waves(int D, int C, bool split) { return (!split && C <= 32) ? 8 : kWaves; }
+constexpr int fwd_waves(int D, int C, bool split) { return (split || C <= 32) ? 8 : kWaves; }
 // The gradient kernel holds three products per subtile, so it takes fewer.
 // (Sizes chosen so every instantiation fits 256 VGPRs, i.e. two waves per SIMD.)
 constexpr int grad_query_tiles(int D, int CK, int CB) { return D <= 32 ? (CK <= 32 && CB == 0 ? 4 : 2) : 1; }
