@@ -56,6 +56,9 @@ constexpr int fwd_waves(int D, int C, bool split) { return (split || C <= 32) ? 
 // The gradient kernel holds three products per subtile, so it takes fewer.
 // (Sizes chosen so every instantiation fits 256 VGPRs, i.e. two waves per SIMD.)
 constexpr int grad_query_tiles(int D, int CK, int CB) { return D <= 32 ? (CK <= 32 && CB == 0 ? 4 : 2) : 1; }
+// Waves per workgroup and keys per LDS stage of the gradient sweep.
+constexpr int grad_waves(int D) { return D <= 32 ? 8 : kWaves; }
+constexpr int grad_stage(int D) { return D <= 64 ? kStageKeys : 32; }
 // The gradient sweep can also produce the weights' gradient (a second output of at most
 // kFusedWeightChannels channels) from the same kernel values.
 constexpr int kFusedWeightChannels = 16;

@@ -34,8 +34,8 @@ namespace keops {
 namespace hd {
 namespace {
 
-template <int D, int CK, int QT, int kStage, int CB>
-__global__ void __launch_bounds__(256, 1)
+template <int D, int CK, int QT, int kStage, int CB, int kW>
+__global__ void __launch_bounds__(64 * kW, 1)
 grad_kernel(const _Float16* __restrict__ x, const _Float16* __restrict__ y, const _Float16* __restrict__ ap,
             const float* __restrict__ rho, const float* __restrict__ beta, const _Float16* __restrict__ bvp,
             const _Float16* __restrict__ yp, const _Float16* __restrict__ gp, const float* __restrict__ oscale,
@@ -49,7 +49,8 @@ grad_kernel(const _Float16* __restrict__ x, const _Float16* __restrict__ y, cons
   constexpr int AP = CK + 8;
   constexpr int VP = 32 + 8;
   constexpr int NSUB = kStage / 32;
-  constexpr int kRowsPerBlock = kWaves * QT * 16;
+  constexpr int kRowsPerBlock = kW * QT * 16;
+  constexpr int kThreads = 64 * kW;
   __shared__ __attribute__((aligned(16))) _Float16 sK[2][kStage][KP];
   __shared__ __attribute__((aligned(16))) _Float16 sA[2][kStage][AP];
   __shared__ __attribute__((aligned(16))) _Float16 sY[2][NSUB][YC][VP];
@@ -108,19 +109,19 @@ grad_kernel(const _Float16* __restrict__ x, const _Float16* __restrict__ y, cons
   }
 
   // Stage loads, global -> registers before the current stage is computed, registers -> LDS
-  // after it. Each table is cut into 16-byte chunks dealt round-robin to the 256 threads.
-  constexpr int kKChunks = kStage * D / 8, KCH = (kKChunks + 255) / 256;
-  constexpr int kAChunks = kStage * CK / 8, ACH = (kAChunks + 255) / 256;
-  constexpr int kYChunks = NSUB * YC * 4, YCH = (kYChunks + 255) / 256;
-  constexpr int kGChunks = CB > 0 ? NSUB * CB * 4 : 0, GCH = kGChunks > 0 ? (kGChunks + 255) / 256 : 1;
-  static_assert(kStage / 4 <= 256 && kStage % 32 == 0, "tile shapes");
+  // after it. Each table is cut into 16-byte chunks dealt round-robin to the workgroup's threads.
+  constexpr int kKChunks = kStage * D / 8, KCH = (kKChunks + kThreads - 1) / kThreads;
+  constexpr int kAChunks = kStage * CK / 8, ACH = (kAChunks + kThreads - 1) / kThreads;
+  constexpr int kYChunks = NSUB * YC * 4, YCH = (kYChunks + kThreads - 1) / kThreads;
+  constexpr int kGChunks = CB > 0 ? NSUB * CB * 4 : 0, GCH = kGChunks > 0 ? (kGChunks + kThreads - 1) / kThreads : 1;
+  static_assert(kStage / 4 <= kThreads && kStage % 32 == 0, "tile shapes");
   half8 rk[KCH], ra[ACH], ry[YCH], rg[GCH];
   f32x4 rb = {};
   auto fetch = [&](int64_t st) {
     const int64_t jb = j0 + st * kStage;
 #pragma unroll
     for (int r = 0; r < KCH; ++r) {
-      const int c = tid + 256 * r;
+      const int c = tid + kThreads * r;
       const int row = c / (D / 8), col = (c % (D / 8)) * 8;
       const int64_t j = jb + row;
       rk[r] = half8{};
@@ -128,20 +129,20 @@ grad_kernel(const _Float16* __restrict__ x, const _Float16* __restrict__ y, cons
     }
 #pragma unroll
     for (int r = 0; r < ACH; ++r) {
-      const int c = tid + 256 * r;
+      const int c = tid + kThreads * r;
       const int row = c / (CK / 8), col = (c % (CK / 8)) * 8;
       if (c < kAChunks) ra[r] = *reinterpret_cast<const half8*>(vb + (jb + row) * CK + col);
     }
 #pragma unroll
     for (int r = 0; r < YCH; ++r) {
-      const int c = tid + 256 * r;
+      const int c = tid + kThreads * r;
       const int t = c / (YC * 4), rem = c % (YC * 4), ch = rem / 4, part = (rem % 4) * 8;
       if (c < kYChunks) ry[r] = *reinterpret_cast<const half8*>(pb + ((jb / 32 + t) * YC + ch) * 32 + part);
     }
     if constexpr (CB > 0) {
 #pragma unroll
       for (int r = 0; r < GCH; ++r) {
-        const int c = tid + 256 * r;
+        const int c = tid + kThreads * r;
         const int t = c / (CB * 4), rem = c % (CB * 4), ch = rem / 4, part = (rem % 4) * 8;
         if (c < kGChunks) rg[r] = *reinterpret_cast<const half8*>(gb + ((jb / 32 + t) * CB + ch) * 32 + part);
       }
@@ -151,24 +152,24 @@ grad_kernel(const _Float16* __restrict__ x, const _Float16* __restrict__ y, cons
   auto commit = [&](int buf) {
 #pragma unroll
     for (int r = 0; r < KCH; ++r) {
-      const int c = tid + 256 * r;
+      const int c = tid + kThreads * r;
       if (c < kKChunks) *reinterpret_cast<half8*>(&sK[buf][c / (D / 8)][(c % (D / 8)) * 8]) = rk[r];
     }
 #pragma unroll
     for (int r = 0; r < ACH; ++r) {
-      const int c = tid + 256 * r;
+      const int c = tid + kThreads * r;
       if (c < kAChunks) *reinterpret_cast<half8*>(&sA[buf][c / (CK / 8)][(c % (CK / 8)) * 8]) = ra[r];
     }
 #pragma unroll
     for (int r = 0; r < YCH; ++r) {
-      const int c = tid + 256 * r;
+      const int c = tid + kThreads * r;
       const int t = c / (YC * 4), rem = c % (YC * 4);
       if (c < kYChunks) *reinterpret_cast<half8*>(&sY[buf][t][rem / 4][(rem % 4) * 8]) = ry[r];
     }
     if constexpr (CB > 0) {
 #pragma unroll
       for (int r = 0; r < GCH; ++r) {
-        const int c = tid + 256 * r;
+        const int c = tid + kThreads * r;
         const int t = c / (CB * 4), rem = c % (CB * 4);
         if (c < kGChunks) *reinterpret_cast<half8*>(&sG[buf][t][rem / 4][(rem % 4) * 8]) = rg[r];
       }
@@ -321,9 +322,9 @@ grad_kernel(const _Float16* __restrict__ x, const _Float16* __restrict__ y, cons
 
 template <int Dp>
 hipError_t grad_launch(const GradArgs& a) {
-  constexpr int kStage = Dp <= 64 ? kStageKeys : 32;
+  constexpr int kStage = grad_stage(Dp), kW = grad_waves(Dp);
 #define KEOPS_GRAD(CKv, CBv)                                                                                     \
-  grad_kernel<Dp, CKv, grad_query_tiles(Dp, CKv, CBv), kStage, CBv><<<a.grid, 256, 0, a.stream>>>(               \
+  grad_kernel<Dp, CKv, grad_query_tiles(Dp, CKv, CBv), kStage, CBv, kW><<<a.grid, 64 * kW, 0, a.stream>>>(       \
       a.x, a.y, a.ap, a.rho, a.beta, a.bvp, a.yp, a.gp, a.oscale, a.out, a.out2, a.M, a.N, a.Npad, a.kps, a.cs, \
       a.tau, a.D, a.C2)
   if (a.out2) {
